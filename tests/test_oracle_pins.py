@@ -1,0 +1,323 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test checks the oracle against something other than itself: the E4M3FN
+and bf16 definitions worked by hand (tests/golden/), brute force over all codes
+or all bf16 bit patterns, an exact-rational re-implementation on tiny shapes
+(oracle/exact.py), closed forms and invariants of the layer
+out = bf16((q(x) W_q^T) s_act s_w[n]).
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import exact
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f32(s):
+    return np.float32(float.fromhex(s) if s not in ("inf", "-inf", "nan") else float(s))
+
+
+# ------------------------------------------------------------------ E4M3 ---
+
+def test_e4m3_table_structure():
+    t = oracle.e4m3_table()
+    finite = [c for c in range(256) if not np.isnan(t[c])]
+    assert len(finite) == 254
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x08] == 2.0 ** -6 and t[0x01] == 2.0 ** -9
+    mags = t[:0x7F]
+    assert np.all(np.diff(mags) > 0), "codes 0x00..0x7E must be strictly increasing"
+    assert len(set(mags.tolist())) == 127
+    for c in range(0x7F):
+        assert t[c | 0x80] == -t[c]
+    assert np.signbit(t[0x80]) and t[0x80] == 0.0
+
+
+def test_e4m3_table_matches_exact_enumeration():
+    # exact.py enumerates sign/exponent/mantissa independently with Fractions
+    t = oracle.e4m3_table()
+    for c in exact.FINITE_CODES:
+        assert Fraction(t[c]) == exact.e4m3_value(c), hex(c)
+
+
+def test_e4m3_roundtrip_all_finite_codes():
+    t = oracle.e4m3_table()
+    codes = np.array(exact.FINITE_CODES, np.uint8)
+    enc = oracle.e4m3_encode(t[codes].astype(np.float32))
+    assert np.array_equal(enc, codes)
+
+
+def test_e4m3_hand_values():
+    g = _golden("e4m3_encode_hand.json")
+    xs = np.array([_f32(c["x"]) for c in g["cases"]], np.float32)
+    want = np.array([int(c["code"], 16) for c in g["cases"]], np.uint8)
+    got = oracle.e4m3_encode(xs)
+    bad = [(c["x"], c["code"], hex(v)) for c, v, w in zip(g["cases"], got, want) if v != w]
+    assert not bad, bad
+
+
+def _brute_force_encode(t32: np.ndarray) -> np.ndarray:
+    """Nearest of the 127 non-negative magnitudes by exhaustive distance, ties to
+    the even code, saturation at 448, NaN -> 0x7F, sign bit copied."""
+    tab = oracle.e4m3_table()[:0x7F]
+    a = np.abs(t32.astype(np.float64))
+    out = np.zeros(t32.shape, np.uint8)
+    fin = ~np.isnan(a)
+    d = np.abs(a[fin, None] - tab[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    # among tied candidates choose the even code
+    idx = np.arange(0x7F)[None, :]
+    even_pref = np.where(cand & (idx % 2 == 0), idx, 10_000).min(axis=1)
+    any_pref = np.where(cand, idx, 10_000).min(axis=1)
+    code = np.where(even_pref < 10_000, even_pref, any_pref)
+    code = np.where(a[fin] >= 448.0, 0x7E, code)
+    out[fin] = code.astype(np.uint8)
+    out[~fin] = 0x7F
+    out |= np.where(np.signbit(t32), 0x80, 0).astype(np.uint8)
+    return out
+
+
+@pytest.mark.parametrize("s_act", [1.0, 0.5, 3.0, 1.0 / 7.0, 0.2])
+def test_quant_encoder_exhaustive_bf16(s_act):
+    """All 65536 bf16 patterns: x / s_act in IEEE fp32 (numpy), then brute force."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    xf = oracle.bf16_bits_to_f32(bits)
+    with np.errstate(all="ignore"):
+        t = (xf / np.float32(s_act)).astype(np.float32)
+    want = _brute_force_encode(t)
+    got = oracle.quant_act(bits.reshape(1, -1), s_act).reshape(-1)
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:10]
+
+
+def test_encoder_random_fp32_vs_brute_force():
+    g = np.random.Generator(np.random.PCG64(1234))
+    t = np.concatenate([
+        g.standard_normal(20000).astype(np.float32) * np.float32(40),
+        (g.random(20000) * 2 - 1).astype(np.float32) * np.float32(2 ** -6),
+        (g.random(2000) * 1000).astype(np.float32),
+    ])
+    assert np.array_equal(oracle.e4m3_encode(t), _brute_force_encode(t))
+
+
+# ------------------------------------------------------------------ bf16 ---
+
+def test_bf16_rounding_against_exact_and_torch():
+    import torch
+    g = np.random.Generator(np.random.PCG64(7))
+    vals = list(g.standard_normal(3000) * 10.0 ** g.integers(-40, 38, 3000))
+    # exact ties between adjacent bf16 values and subnormal-range values
+    vals += [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(2.0 + 2 ** -7), 2 ** -130 * 1.5, 2 ** -133 * 0.5,
+             2 ** -133 * 1.5, 3.0 * 2 ** -134]
+    for v in vals:
+        want_val = exact.bf16(Fraction(v))
+        got = oracle.f64_to_bf16(v)
+        if want_val == 0:
+            assert got & 0x7FFF == 0
+        else:
+            assert got == exact.bf16_bits(want_val), (v, hex(got))
+    # fp32 inputs: the library cast (round to nearest even) is a second reference
+    f = (g.standard_normal(20000) * 10.0 ** g.integers(-30, 30, 20000)).astype(np.float32)
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.f32_to_bf16(x) for x in f], np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------- the layer ---
+
+def test_tiny_product_hand_worked():
+    g = _golden("tiny_product.json")
+    xq = np.array([[int(c, 16) for c in g["x_q"]]], np.uint8)
+    wq = np.array([[int(c, 16) for c in r] for r in g["W_q"]], np.uint8)
+    s_act = float.fromhex(g["s_act"])
+    s_w = np.array([float.fromhex(s) for s in g["s_w"]], np.float32)
+    acc = oracle.exact_acc(xq, wq)[0]
+    assert [Fraction(a) for a in acc] == [Fraction(s) for s in g["acc_exact"]]
+    out, v = oracle.scaled_mm(xq, wq, s_act, s_w, want_v=True)
+    assert [Fraction(x) for x in v[0]] == [Fraction(s) for s in g["v_exact"]]
+    assert [hex(b) for b in out[0]] == g["out_bf16"]
+
+
+def test_brute_force_2x3x4_against_exact_rationals():
+    """Whole pipeline (quant -> exact GEMM -> bf16) in Fractions vs the oracle."""
+    g = np.random.Generator(np.random.PCG64(99))
+    t = oracle.e4m3_table()
+    for it in range(400):
+        x = wl.to_bf16_bits(g.standard_normal((2, 4)).astype(np.float32) * np.float32(g.choice([0.01, 1, 30])))
+        s_act = float(np.float32(g.choice([1.0, 0.5, 1 / 7, 0.0123, 3.7])))
+        codes = wl.FINITE_CODE_VALUES[g.integers(0, 254, (3, 4))]
+        if it % 5 == 0:  # restrict to a small code set to hit ties and cancellations
+            codes = np.array([0x38, 0xB8, 0x40, 0x01, 0x81, 0x7E, 0xFE], np.uint8)[g.integers(0, 7, (3, 4))]
+        s_w = (g.random(3) * 0.01 + 1e-4).astype(np.float32)
+        xq = oracle.quant_act(x, s_act)
+        xq_exact = np.array(exact.quant(x.tolist(), s_act), np.uint8)
+        assert np.array_equal(xq, xq_exact), (x, s_act)
+        out = oracle.scaled_mm(xq, codes, s_act, s_w)
+        out_exact, _ = exact.scaled_mm(xq_exact.tolist(), codes.tolist(), s_act, s_w.tolist())
+        assert np.array_equal(out, np.array(out_exact, np.uint16)), (it, out, out_exact)
+        assert not np.isnan(t[xq]).any()
+
+
+def test_gemm_exact_accumulation_closed_form():
+    """Every E4M3 value is a multiple of 2^-9: the integer sum in units of 2^-18
+    must equal the fp64 accumulator, and any K permutation gives the same bits."""
+    g = np.random.Generator(np.random.PCG64(5))
+    M, N, K = 3, 40, 17408
+    xq = wl.FINITE_CODE_VALUES[g.integers(0, 254, (M, K))]
+    wq = wl.FINITE_CODE_VALUES[g.integers(0, 254, (N, K))]
+    t = oracle.e4m3_table()
+    xi = np.rint(t[xq] * 512).astype(np.int64)
+    wi = np.rint(t[wq] * 512).astype(np.int64)
+    acc_int = xi @ wi.T                                  # units of 2^-18, exact in int64
+    acc = oracle.exact_acc(xq, wq)
+    assert np.array_equal(acc * 2.0 ** 18, acc_int.astype(np.float64))
+    assert np.all(np.abs(acc_int) < 2 ** 50)
+    perm = g.permutation(K)
+    assert np.array_equal(oracle.exact_acc(xq[:, perm], wq[:, perm]), acc)
+
+
+def test_invariants_scale_zero_identity_sign_merge():
+    g = np.random.Generator(np.random.PCG64(11))
+    M, N, K = 5, 48, 512
+    x = wl.to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    s_act = oracle.act_scale(x)
+    xq = oracle.quant_act(x, s_act)
+    w = g.standard_normal((N, K)).astype(np.float32) * np.float32(0.02)
+    wq, sw = oracle.quant_weight(w)
+    out, v = oracle.scaled_mm(xq, wq, s_act, sw, want_v=True)
+    # linearity in s_w: a power of two scales the result bit-exactly
+    for j in (-3, 1, 4):
+        out2 = oracle.scaled_mm(xq, wq, s_act, (sw * np.float32(2.0 ** j)).astype(np.float32))
+        want = wl.to_bf16_bits(oracle.bf16_bits_to_f32(out) * np.float32(2.0 ** j))
+        assert np.array_equal(out2, want)
+    # general scale: within one bf16 rounding of the scaled exact value
+    c = np.float32(1.37)
+    out3 = oracle.scaled_mm(xq, wq, s_act, (sw * c).astype(np.float32))
+    vc = v * np.float64(c)
+    err = np.abs(oracle.bf16_bits_to_f32(out3).astype(np.float64) - vc)
+    assert np.all(err <= 2.0 ** -8 * np.abs(vc) + 1e-30)
+    # zero row -> +0 row
+    xz = xq.copy()
+    xz[2] = 0
+    oz = oracle.scaled_mm(xz, wq, s_act, sw)
+    assert np.all(oz[2] == 0)
+    # identity weight with power-of-two s_act: out = bf16(dec(x_q) * s_act) exactly
+    Ki = 256
+    ident = np.where(np.eye(Ki, dtype=bool), 0x38, 0).astype(np.uint8)
+    xi = xq[:, :Ki]
+    oi = oracle.scaled_mm(xi, ident, 0.25, np.ones(Ki, np.float32))
+    dec = oracle.e4m3_table()[xi] * 0.25
+    assert np.array_equal(oracle.bf16_bits_to_f32(oi).astype(np.float64), dec)
+    # flipping every W sign bit negates the output exactly
+    on = oracle.scaled_mm(xq, wq ^ np.uint8(0x80), s_act, sw)
+    nz = (out & 0x7FFF) != 0
+    assert np.array_equal(on[nz], out[nz] ^ np.uint16(0x8000))
+    # merged == split: concatenated shards equal separate products
+    wa, wb = wq[:20], wq[20:]
+    oa = oracle.scaled_mm(xq, wa, s_act, sw[:20])
+    ob = oracle.scaled_mm(xq, wb, s_act, sw[20:])
+    assert np.array_equal(np.concatenate([oa, ob], axis=1), out)
+
+
+# --------------------------------------------------------------- RMSNorm ---
+
+def test_rmsnorm_closed_forms():
+    K = 5120
+    eps = 1e-6
+    ones = np.ones(K, np.float32)
+    gamma1 = wl.to_bf16_bits(ones)
+    # rows of +-1: r = fl32(1/sqrt(1 + eps)) rounds y to exactly bf16 1.0
+    row = np.where(np.arange(K) % 3 == 0, -1.0, 1.0).astype(np.float32)
+    x = wl.to_bf16_bits(row[None, :])
+    y = oracle.rmsnorm(x, gamma1, eps)
+    assert np.array_equal(oracle.bf16_bits_to_f32(y)[0], row)
+    q = oracle.quant_rmsnorm(x, gamma1, eps, np.float32(1.0 / 448.0))
+    assert np.array_equal(q[0], np.where(row < 0, 0xFE, 0x7E).astype(np.uint8))
+    # constant row c: y = gamma * c / sqrt(c^2 + eps), then rounded
+    for c in (0.5, -3.0, 1e-3):
+        x = wl.to_bf16_bits(np.full((1, K), c, np.float32))
+        cb = float(oracle.bf16_bits_to_f32(x)[0, 0])
+        r = np.float32(1.0 / np.sqrt(cb * cb + np.float64(np.float32(eps))))
+        want = wl.to_bf16_bits(np.float32(np.float32(cb) * r) * np.float32(1.0))
+        assert np.all(oracle.rmsnorm(x, gamma1, eps)[0] == want)
+    # a single nonzero entry a at position j: y_j = gamma_j * a / sqrt(a^2/K + eps)
+    a, j = np.float32(2.0), 17
+    row = np.zeros(K, np.float32)
+    row[j] = a
+    x = wl.to_bf16_bits(row[None, :])
+    g = wl.gamma_bf16(3, K)
+    y = oracle.bf16_bits_to_f32(oracle.rmsnorm(x, g, eps))[0]
+    r = np.float32(1.0 / np.sqrt(4.0 / K + np.float64(np.float32(eps))))
+    want = wl.to_bf16_bits(np.float32(a * r) * oracle.bf16_bits_to_f32(g)[j])
+    assert y[j] == oracle.bf16_bits_to_f32(want) and np.all(np.delete(y, j) == 0)
+
+
+def test_rmsnorm_against_numpy_formula():
+    """Independent restatement with numpy (pairwise fp64 sum, fp32 products,
+    torch's bf16 cast) on the decode-MLP input distribution."""
+    K = 5120
+    x = wl.activation_bf16(3, 32, K, outliers=True)
+    g = wl.gamma_bf16(3, K)
+    xf = oracle.bf16_bits_to_f32(x)
+    ss = np.sum(xf.astype(np.float64) ** 2, axis=1)
+    r = (1.0 / np.sqrt(ss / K + np.float64(np.float32(1e-6)))).astype(np.float32)
+    y = (xf * r[:, None]).astype(np.float32) * oracle.bf16_bits_to_f32(g)[None, :]
+    want = wl.to_bf16_bits(y.astype(np.float32))
+    assert np.array_equal(oracle.rmsnorm(x, g, 1e-6), want)
+
+
+@pytest.mark.parametrize("wid,M", [(3, 32), (5, 64)])
+def test_fused_quant_is_byte_exact_against_unfused(wid, M):
+    """The fused RMSNorm->quant must equal quant(rmsnorm(x)) byte for byte."""
+    K = 5120
+    x = wl.activation_bf16(wid, M, K, outliers=(wid == 3))
+    g = wl.gamma_bf16(wid, K)
+    s = oracle.act_scale(x, g, 1e-6)
+    fused = oracle.quant_rmsnorm(x, g, 1e-6, s)
+    unfused = oracle.quant_act(oracle.rmsnorm(x, g, 1e-6), s)
+    assert np.array_equal(fused, unfused)
+    # the calibrated scale is amax over the tensor actually quantized
+    y = oracle.bf16_bits_to_f32(oracle.rmsnorm(x, g, 1e-6))
+    assert s == np.float32(np.abs(y).max() / np.float32(448.0))
+    assert np.abs(oracle.e4m3_table()[fused]).max() == 448.0
+
+
+# ------------------------------------------------------- scales and weights --
+
+def test_act_scale_and_weight_quant_definitions():
+    x = wl.activation_bf16(2, 8, 5120, outliers=True)
+    xf = oracle.bf16_bits_to_f32(x)
+    assert oracle.act_scale(x) == np.float32(np.abs(xf).max()) / np.float32(448.0)
+    assert oracle.act_scale(np.zeros((2, 16), np.uint16)) == 1.0
+    w = wl.weight_f32(1, 384, 256)
+    w[7] = 0.0
+    wq, sw = oracle.quant_weight(w)
+    amax = np.abs(w).max(axis=1)
+    want_sw = np.where(amax == 0, np.float32(1), amax / np.float32(448.0)).astype(np.float32)
+    assert np.array_equal(sw, want_sw)
+    t = (w / sw[:, None]).astype(np.float32)
+    assert np.array_equal(wq, _brute_force_encode(t))
+    assert (wq[np.arange(384) != 7] & 0x7F).max(axis=1).min() == 0x7E  # every row reaches +-448
+
+
+def test_double_rounding_trap():
+    """The bf16 output is ONE rounding of the exact value (never through fp32)."""
+    g = _golden("tiny_product.json")["double_rounding_trap"]
+    xq = np.array([[int(c, 16) for c in g["x_q"]]], np.uint8)
+    wq = np.array([[int(c, 16) for c in r] for r in g["W_q"]], np.uint8)
+    s_w = np.array([float.fromhex(s) for s in g["s_w"]], np.float32)
+    out = oracle.scaled_mm(xq, wq, float.fromhex(g["s_act"]), s_w)
+    assert hex(out[0, 0]) == g["out_bf16"]
