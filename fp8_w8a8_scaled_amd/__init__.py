@@ -1,0 +1,260 @@
+"""fp8_w8a8_scaled_amd -- MI355X (gfx950) FP8 E4M3 W8A8 scaled-matmul layer.
+
+Thin ctypes binding over ``libfp8mm.so`` (C ABI in ``include/fp8mm.h``).  This
+module only marshals arguments: it checks dtypes, devices and strides, allocates
+outputs with ``torch.empty`` and passes raw device pointers plus the current HIP
+stream.  Every step of the layer runs in the library's HIP kernels; there is no
+fallback.  If the library is missing, importing this package raises.
+
+The layer:  out[m,n] = bf16((sum_k x_q[m,k] w_q[n,k]) * s_act * s_w[n]),
+x_q = saturating RNE E4M3(x / s_act) -- bmm_fp8 with a per-tensor activation
+scale and per-channel weight scales, bf16 output (vllm.cpp #252 "CORRECTION";
+vllm.cpp #417 Finding 1).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8mm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python fp8_w8a8_scaled_amd/build.py` "
+                      "(the package has no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
+SMALL_M_MAX = 64
+THRESHOLD_MIN = 16
+MAX_SHARDS = 8
+
+_P, _I64, _F32, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+
+
+class Shard(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64)]
+
+
+def _decl(name, args, res=ctypes.c_int):
+    f = getattr(_lib, name)
+    f.argtypes = args
+    f.restype = res
+    return f
+
+
+_quant_rmsnorm = _decl("fp8_quant_rmsnorm", [_P, _I64, _P, _F32, _F32, _P, _I64, _I64, _P])
+_scaled_mm = _decl("fp8_scaled_mm", [_P, _P, _F32, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P])
+_scaled_mm_arm = _decl("fp8_scaled_mm_arm", [_P, _P, _F32, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _SZ, _P])
+_scaled_mm_merged = _decl("fp8_scaled_mm_merged", [_P, _P, _F32, _P, ctypes.POINTER(Shard), _I32, _I64, _I64, _P, _SZ, _P])
+_workspace_bytes = _decl("fp8_scaled_mm_workspace_bytes", [_I64, _I64, _I64], _SZ)
+_select = _decl("fp8_scaled_mm_select", [_I64, _I64, _I64])
+_set_threshold = _decl("fp8_set_large_m_threshold", [_I64])
+_get_threshold = _decl("fp8_get_large_m_threshold", [], _I64)
+_scales_equal = _decl("fp8_scales_bitwise_equal", [_P, _I32])
+_strerror = _decl("fp8mm_strerror", [_I32], ctypes.c_char_p)
+_quant_weight = _decl("fp8_quant_weight", [_P, _I64, _I64, _P, _P, _P])
+_act_scale_ws = _decl("fp8_act_scale_workspace_bytes", [_I64, _I64], _SZ)
+_act_scale = _decl("fp8_act_scale", [_P, _I64, _P, _F32, _I64, _I64, _P, _P, _SZ, _P])
+
+
+class Fp8mmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+def strerror(status: int) -> str:
+    return _strerror(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise Fp8mmError(status, what)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _codes(t: torch.Tensor, name: str) -> torch.Tensor:
+    """E4M3 tensors travel as raw bytes: accept uint8 or float8_e4m3fn."""
+    if t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be uint8 E4M3 codes or float8_e4m3fn, got {t.dtype}")
+    return t
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _row_major(t: torch.Tensor, name: str) -> int:
+    _need(t.dim() == 2 and t.stride(1) == 1, f"{name} must be 2-D with unit column stride")
+    return t.stride(0)
+
+
+# ------------------------------------------------------------- activations --
+
+def quant_rmsnorm(x: torch.Tensor, gamma: Optional[torch.Tensor], s_act: float, eps: float = 1e-6,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fused RMSNorm -> static E4M3 quant (gamma given) or plain static quant
+    (gamma None) of bf16 x [M, K]; returns uint8 codes [M, K]."""
+    _need(x.is_cuda and x.dtype == torch.bfloat16, "x must be a bf16 CUDA tensor")
+    ldx = _row_major(x, "x")
+    M, K = x.shape
+    if gamma is not None:
+        _need(gamma.is_cuda and gamma.dtype == torch.bfloat16 and gamma.is_contiguous()
+              and gamma.numel() == K, "gamma must be a contiguous bf16 CUDA tensor of K elements")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    out = _codes(out, "out")
+    _need(out.is_contiguous() and tuple(out.shape) == (M, K), "out must be contiguous uint8 [M, K]")
+    _check(_quant_rmsnorm(_ptr(x), ldx, _ptr(gamma), float(eps), float(s_act), _ptr(out), M, K, _stream(x)),
+           "fp8_quant_rmsnorm")
+    return out
+
+
+def quant(x: torch.Tensor, s_act: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Plain static per-tensor E4M3 quant of bf16 x [M, K]."""
+    return quant_rmsnorm(x, None, s_act, 0.0, out)
+
+
+def act_scale(x: torch.Tensor, gamma: Optional[torch.Tensor] = None, eps: float = 1e-6) -> torch.Tensor:
+    """Static scale calibration: device f32 [1] = fl32(amax / 448) of the tensor
+    quant_rmsnorm(x, gamma, ., eps) would quantize (1 if amax == 0)."""
+    _need(x.is_cuda and x.dtype == torch.bfloat16, "x must be a bf16 CUDA tensor")
+    ldx = _row_major(x, "x")
+    M, K = x.shape
+    if gamma is not None:
+        _need(gamma.is_cuda and gamma.dtype == torch.bfloat16 and gamma.is_contiguous() and gamma.numel() == K,
+              "gamma must be a contiguous bf16 CUDA tensor of K elements")
+    s = torch.empty(1, dtype=torch.float32, device=x.device)
+    nbytes = int(_act_scale_ws(M, K))
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check(_act_scale(_ptr(x), ldx, _ptr(gamma), float(eps), M, K, _ptr(s), _ptr(ws), ws.numel(), _stream(x)),
+           "fp8_act_scale")
+    return s
+
+
+# ------------------------------------------------------------------ weights --
+
+def quant_weight(w: torch.Tensor):
+    """Per-output-channel E4M3 quant of f32 w [N, K] -> (w_q uint8 [N, K], s_w f32 [N])."""
+    _need(w.is_cuda and w.dtype == torch.float32 and w.dim() == 2 and w.is_contiguous(),
+          "w must be a contiguous 2-D f32 CUDA tensor")
+    N, K = w.shape
+    wq = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    sw = torch.empty(N, dtype=torch.float32, device=w.device)
+    _check(_quant_weight(_ptr(w), N, K, _ptr(wq), _ptr(sw), _stream(w)), "fp8_quant_weight")
+    return wq, sw
+
+
+# --------------------------------------------------------------------- GEMM --
+
+def _gemm_args(x_q, w_q, s_w):
+    x_q = _codes(x_q, "x_q")
+    w_q = _codes(w_q, "w_q")
+    _need(x_q.is_cuda and x_q.dim() == 2 and x_q.is_contiguous(), "x_q must be contiguous [M, K]")
+    _need(w_q.is_cuda and w_q.dim() == 2 and w_q.is_contiguous(), "w_q must be contiguous [N, K]")
+    _need(x_q.shape[1] == w_q.shape[1], "x_q and w_q must share K")
+    _need(s_w.is_cuda and s_w.dtype == torch.float32 and s_w.is_contiguous() and s_w.numel() == w_q.shape[0],
+          "s_w must be a contiguous f32 CUDA tensor of N elements")
+    return x_q, w_q
+
+
+def workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(_workspace_bytes(M, N, K))
+
+
+def _workspace(M, N, K, device, workspace):
+    nbytes = workspace_bytes(M, N, K)
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def scaled_mm(x_q: torch.Tensor, w_q: torch.Tensor, s_act: float, s_w: torch.Tensor,
+              out: Optional[torch.Tensor] = None, arm: Optional[int] = None,
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [M, N] = bf16((x_q . w_q^T) * s_act * s_w).  arm None = dispatcher,
+    0 = force the small-M kernel, 1 = force the large-M kernel."""
+    x_q, w_q = _gemm_args(x_q, w_q, s_w)
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x_q.device)
+    _need(out.dtype == torch.bfloat16 and out.is_cuda and out.shape == (M, N), "out must be bf16 [M, N]")
+    ldo = _row_major(out, "out")
+    ws, wsb = _workspace(M, N, K, x_q.device, workspace)
+    if arm is None:
+        st = _scaled_mm(_ptr(x_q), _ptr(w_q), float(s_act), _ptr(s_w), _ptr(out), ldo, M, N, K,
+                        _ptr(ws), wsb, _stream(x_q))
+    else:
+        st = _scaled_mm_arm(_ptr(x_q), _ptr(w_q), float(s_act), _ptr(s_w), _ptr(out), ldo, M, N, K, int(arm),
+                            _ptr(ws), wsb, _stream(x_q))
+    _check(st, "fp8_scaled_mm")
+    return out
+
+
+def scaled_mm_merged(x_q: torch.Tensor, w_q: torch.Tensor, s_act: float, s_w: torch.Tensor,
+                     shard_sizes: Sequence[int], outs: Optional[Sequence[torch.Tensor]] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """One launch over a concatenated weight [sum n_i, K]; returns the list of
+    bf16 [M, n_i] shard outputs (or fills ``outs``)."""
+    x_q, w_q = _gemm_args(x_q, w_q, s_w)
+    M, K = x_q.shape
+    _need(sum(shard_sizes) == w_q.shape[0], "shard sizes must sum to the weight rows")
+    _need(1 <= len(shard_sizes) <= MAX_SHARDS, f"1..{MAX_SHARDS} shards")
+    if outs is None:
+        outs = [torch.empty((M, n), dtype=torch.bfloat16, device=x_q.device) for n in shard_sizes]
+    arr = (Shard * len(shard_sizes))()
+    for i, (n, o) in enumerate(zip(shard_sizes, outs)):
+        _need(o.dtype == torch.bfloat16 and o.is_cuda and o.shape == (M, n), "shard outputs must be bf16 [M, n_i]")
+        arr[i] = Shard(int(n), o.data_ptr(), _row_major(o, "out"))
+    ws, wsb = _workspace(M, w_q.shape[0], K, x_q.device, workspace)
+    _check(_scaled_mm_merged(_ptr(x_q), _ptr(w_q), float(s_act), _ptr(s_w), arr, len(shard_sizes), M, K,
+                             _ptr(ws), wsb, _stream(x_q)), "fp8_scaled_mm_merged")
+    return list(outs)
+
+
+# --------------------------------------------------------------- dispatcher --
+
+def select(M: int, N: int, K: int) -> int:
+    """0 = small-M kernel, 1 = large-M kernel (pure function of M and T)."""
+    return int(_select(M, N, K))
+
+
+def set_large_m_threshold(t: int) -> None:
+    _check(_set_threshold(int(t)), "fp8_set_large_m_threshold")
+
+
+def get_large_m_threshold() -> int:
+    return int(_get_threshold())
+
+
+def scales_bitwise_equal(scales: Sequence[float]) -> bool:
+    """Merge predicate: all f32 input scales have the same bit pattern."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(scales, dtype=np.float32))
+    st = _scales_equal(a.ctypes.data, a.size)
+    if st < 0:
+        raise Fp8mmError(st, "fp8_scales_bitwise_equal")
+    return bool(st)
+
+
+def raw_lib() -> ctypes.CDLL:
+    """The loaded C library (for direct C-ABI calls)."""
+    return _lib

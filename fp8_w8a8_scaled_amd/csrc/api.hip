@@ -1,0 +1,231 @@
+// api.hip -- the C ABI of libfp8mm (declared in include/fp8mm.h): argument
+// validation (fail closed), the M-threshold dispatcher, the merge predicate and
+// the launches.  No call allocates, synchronizes or throws.
+//
+// Dispatcher: the small-M arm serves M <= T, the large-M arm M > T.  The branch
+// is a pure function of M (and T), re-decided on every call, so a captured
+// graph freezes the same branch an eager call takes; thresholds in [2,16) are
+// rejected so that decode / speculative-verify batches (M <= 8) never leave the
+// memory-bound arm (vLLM PR #53014, Marlin large-M commit message).
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "internal.h"
+
+namespace {
+
+// Default threshold: largest M served by the small-M arm.  Chosen from the
+// measured crossover of the two arms on MI355X.
+constexpr int64_t kDefaultThreshold = 32;
+
+int64_t initial_threshold()
+{
+    const char* e = std::getenv("FP8MM_LARGE_M_THRESHOLD");
+    if (e && *e) {
+        char* end = nullptr;
+        const long long v = std::strtoll(e, &end, 10);
+        if (end && *end == '\0' && v >= FP8MM_THRESHOLD_MIN && v <= FP8MM_SMALL_M_MAX) return (int64_t)v;
+    }
+    return kDefaultThreshold;
+}
+
+std::atomic<int64_t> g_threshold{initial_threshold()};
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
+
+int launch_status()
+{
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? FP8MM_OK : FP8MM_ELAUNCH;
+}
+
+// Shared validation of the GEMM operands; fills the shard table.
+int check_gemm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,
+               const fp8_shard_t* shards, int num_shards, int64_t M, int64_t K,
+               fp8mm::ShardTable* tab, int64_t* N_out)
+{
+    // Sizes and scalars first; an empty product (M == 0 or N == 0) is a no-op
+    // that may come with null pointers (empty tensors).
+    if (!shards || M < 0 || K < 0 || num_shards < 1 || num_shards > FP8MM_MAX_SHARDS) return FP8MM_EINVAL;
+    if (!good_scale(s_act)) return FP8MM_EINVAL;
+    int64_t N = 0;
+    tab->num = num_shards;
+    for (int i = 0; i < num_shards; ++i) {
+        const fp8_shard_t& s = shards[i];
+        if (s.n < 0 || s.ldo < s.n) return FP8MM_EINVAL;
+        if (M > 0 && s.n > 0 && !s.out) return FP8MM_EINVAL;
+        if (s.n % 16 != 0 || s.ldo % 8 != 0 || !aligned16(s.out)) return FP8MM_EUNSUPPORTED;
+        tab->start[i] = N;
+        tab->out[i] = s.out;
+        tab->ldo[i] = s.ldo;
+        N += s.n;
+    }
+    tab->start[num_shards] = N;
+    if (K % 16 != 0) return FP8MM_EUNSUPPORTED;
+    *N_out = N;
+    if (M == 0 || N == 0) return FP8MM_OK;
+    if (!x_q || !w_q || !s_w) return FP8MM_EINVAL;
+    if (K == 0) return FP8MM_EUNSUPPORTED;
+    if (!aligned16(x_q) || !aligned16(w_q) || !aligned16(s_w)) return FP8MM_EUNSUPPORTED;
+    if (M > (int64_t)65535 * 128 || N / 16 > (int64_t)0x7fffffff) return FP8MM_EUNSUPPORTED;
+    *N_out = N;
+    return FP8MM_OK;
+}
+
+int run_gemm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,
+             const fp8_shard_t* shards, int num_shards, int64_t M, int64_t K, int arm,
+             void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    fp8mm::ShardTable tab{};
+    int64_t N = 0;
+    int st = check_gemm(x_q, w_q, s_act, s_w, shards, num_shards, M, K, &tab, &N);
+    if (st != FP8MM_OK) return st;
+    if (workspace_bytes < fp8_scaled_mm_workspace_bytes(M, N, K)) return FP8MM_EWORKSPACE;
+    (void)workspace;
+    if (M == 0 || N == 0) return FP8MM_OK;
+    if (arm < 0) arm = fp8_scaled_mm_select(M, N, K);
+    if (arm == 0) {
+        if (M > FP8MM_SMALL_M_MAX) return FP8MM_EINVAL;
+        fp8mm::launch_gemm_small_m(x_q, w_q, s_act, s_w, tab, M, N, K, stream);
+    } else if (arm == 1) {
+        fp8mm::launch_gemm_large_m(x_q, w_q, s_act, s_w, tab, M, N, K, stream);
+    } else {
+        return FP8MM_EINVAL;
+    }
+    return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_quant_rmsnorm(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, float s_act,
+                      uint8_t* x_q, int64_t M, int64_t K, hipStream_t stream)
+{
+    if (M < 0 || K < 0 || ldx < K) return FP8MM_EINVAL;
+    if (!good_scale(s_act)) return FP8MM_EINVAL;
+    if (gamma && !(std::isfinite(eps) && eps >= 0.0f)) return FP8MM_EINVAL;
+    if (K % 16 != 0 || ldx % 8 != 0) return FP8MM_EUNSUPPORTED;
+    if (M == 0 || K == 0) return FP8MM_OK;
+    if (!x || !x_q) return FP8MM_EINVAL;
+    if (!aligned16(x) || !aligned16(x_q) || (gamma && !aligned16(gamma))) return FP8MM_EUNSUPPORTED;
+    if (gamma && M > (int64_t)0x7fffffff) return FP8MM_EUNSUPPORTED;
+    // x_q must not overlap x
+    const uintptr_t xb = reinterpret_cast<uintptr_t>(x), xe = xb + (uintptr_t)((M - 1) * ldx + K) * 2;
+    const uintptr_t qb = reinterpret_cast<uintptr_t>(x_q), qe = qb + (uintptr_t)(M * K);
+    if (qb < xe && xb < qe) return FP8MM_EINVAL;
+    fp8mm::launch_quant(x, ldx, gamma, eps, s_act, x_q, M, K, stream);
+    return launch_status();
+}
+
+int fp8_scaled_mm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,
+                  uint16_t* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (N < 0) return FP8MM_EINVAL;
+    const fp8_shard_t one{N, out, ldo};
+    return run_gemm(x_q, w_q, s_act, s_w, &one, 1, M, K, -1, workspace, workspace_bytes, stream);
+}
+
+int fp8_scaled_mm_arm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,
+                      uint16_t* out, int64_t ldo, int64_t M, int64_t N, int64_t K, int arm,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (N < 0 || (arm != 0 && arm != 1)) return FP8MM_EINVAL;
+    if (arm == 0 && M > FP8MM_SMALL_M_MAX) return FP8MM_EINVAL;
+    const fp8_shard_t one{N, out, ldo};
+    return run_gemm(x_q, w_q, s_act, s_w, &one, 1, M, K, arm, workspace, workspace_bytes, stream);
+}
+
+int fp8_scaled_mm_merged(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,
+                         const fp8_shard_t* shards, int num_shards, int64_t M, int64_t K,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return run_gemm(x_q, w_q, s_act, s_w, shards, num_shards, M, K, -1, workspace, workspace_bytes, stream);
+}
+
+size_t fp8_scaled_mm_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    (void)M; (void)N; (void)K;
+    return 0;   // both arms reduce on chip: no split-K partials leave the workgroup
+}
+
+int fp8_scaled_mm_select(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0) return FP8MM_EINVAL;
+    return M <= g_threshold.load(std::memory_order_relaxed) ? 0 : 1;
+}
+
+int fp8_set_large_m_threshold(int64_t t)
+{
+    if (t < FP8MM_THRESHOLD_MIN || t > FP8MM_SMALL_M_MAX) return FP8MM_EINVAL;
+    g_threshold.store(t, std::memory_order_relaxed);
+    return FP8MM_OK;
+}
+
+int64_t fp8_get_large_m_threshold(void) { return g_threshold.load(std::memory_order_relaxed); }
+
+int fp8_scales_bitwise_equal(const float* s, int n)
+{
+    if (!s || n < 1) return FP8MM_EINVAL;
+    uint32_t first;
+    std::memcpy(&first, &s[0], 4);
+    for (int i = 1; i < n; ++i) {
+        uint32_t b;
+        std::memcpy(&b, &s[i], 4);
+        if (b != first) return 0;
+    }
+    return 1;
+}
+
+const char* fp8mm_strerror(int status)
+{
+    switch (status) {
+    case FP8MM_OK: return "ok";
+    case FP8MM_EINVAL: return "invalid argument (null pointer, negative size, bad scale or out-of-range value)";
+    case FP8MM_EUNSUPPORTED: return "unsupported shape or alignment (K%16, N%16, ld%8, 16-byte pointers)";
+    case FP8MM_EWORKSPACE: return "workspace too small";
+    case FP8MM_ELAUNCH: return "HIP kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int fp8_quant_weight(const float* w, int64_t N, int64_t K, uint8_t* w_q, float* s_w, hipStream_t stream)
+{
+    if (N < 0 || K < 0) return FP8MM_EINVAL;
+    if (K % 16 != 0) return FP8MM_EUNSUPPORTED;
+    if (N == 0) return FP8MM_OK;
+    if (!s_w || (K > 0 && (!w || !w_q))) return FP8MM_EINVAL;
+    if (!aligned16(w) || !aligned16(w_q) || !aligned16(s_w)) return FP8MM_EUNSUPPORTED;
+    if (N > (int64_t)0x7fffffff) return FP8MM_EUNSUPPORTED;
+    if (K == 0) return FP8MM_EUNSUPPORTED;   // no row to take a scale from
+    fp8mm::launch_quant_weight(w, N, K, w_q, s_w, stream);
+    return launch_status();
+}
+
+size_t fp8_act_scale_workspace_bytes(int64_t M, int64_t K)
+{
+    if (M <= 0 || K <= 0) return 0;
+    const size_t a = fp8mm::act_scale_partials(M, K, true), b = fp8mm::act_scale_partials(M, K, false);
+    return (a > b ? a : b) * sizeof(float);
+}
+
+int fp8_act_scale(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, int64_t M, int64_t K,
+                  float* s_act, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!x || !s_act || M < 0 || K < 0 || ldx < K) return FP8MM_EINVAL;
+    if (gamma && !(std::isfinite(eps) && eps >= 0.0f)) return FP8MM_EINVAL;
+    if (K % 16 != 0 || ldx % 8 != 0 || !aligned16(x) || (gamma && !aligned16(gamma))) return FP8MM_EUNSUPPORTED;
+    if (gamma && M > (int64_t)0x7fffffff) return FP8MM_EUNSUPPORTED;
+    if (M == 0 || K == 0) return FP8MM_EINVAL;   // no tensor to calibrate on
+    if (!workspace || workspace_bytes < fp8_act_scale_workspace_bytes(M, K)) return FP8MM_EWORKSPACE;
+    if (!aligned16(workspace)) return FP8MM_EUNSUPPORTED;
+    fp8mm::launch_act_scale(x, ldx, gamma, eps, M, K, s_act, static_cast<float*>(workspace), stream);
+    return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// internal.h -- launcher interface between the C ABI (api.hip) and the kernels.
+// Callers have already validated shapes, strides and alignment.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp8mm.h"
+
+namespace fp8mm {
+
+// Output placement of a (possibly merged) projection, passed by value in the
+// kernel arguments: weight rows [start[i], start[i+1]) go to out[i] with row
+// stride ldo[i].  Every start[i] is a multiple of 16.
+struct ShardTable {
+    int num;
+    int64_t start[FP8MM_MAX_SHARDS + 1];
+    uint16_t* out[FP8MM_MAX_SHARDS];
+    int64_t ldo[FP8MM_MAX_SHARDS];
+};
+
+// quant.hip
+void launch_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, float s_act,
+                  uint8_t* xq, int64_t M, int64_t K, hipStream_t stream);
+size_t act_scale_partials(int64_t M, int64_t K, bool rms);
+void launch_act_scale(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
+                      int64_t M, int64_t K, float* s_act, float* partial, hipStream_t stream);
+void launch_quant_weight(const float* w, int64_t N, int64_t K, uint8_t* wq, float* s_w,
+                         hipStream_t stream);
+
+// gemm_small_m.hip: memory-bound arm, M <= FP8MM_SMALL_M_MAX.
+void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
+                         const ShardTable& shards, int64_t M, int64_t N, int64_t K,
+                         hipStream_t stream);
+
+// gemm_large_m.hip: compute-bound MFMA-tiled arm, any M.
+void launch_gemm_large_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
+                         const ShardTable& shards, int64_t M, int64_t N, int64_t K,
+                         hipStream_t stream);
+
+}  // namespace fp8mm

@@ -1,0 +1,217 @@
+/*
+ * fp8mm.h -- C ABI of the MI355X (gfx950) FP8 E4M3 W8A8 scaled-matmul layer.
+ *
+ * The layer (one linear projection of a quantized LLM's decode or prefill step):
+ *
+ *     out[m,n] = bf16( (sum_k x_q[m,k] * W_q[n,k]) * s_act * s_w[n] )
+ *     x_q      = saturating round-to-nearest-even E4M3( x / s_act )
+ *
+ * Sources (web pages):
+ *   - bmm_fp8(a, b, scale_a, scale_b, out_dtype, backend): vllm.cpp issue #252
+ *     ("FP8 tower's cuBLASLt default rests on a false premise"), "CORRECTION".
+ *   - bf16 (model dtype) output instead of F32: vllm.cpp issue #417 ("We emit F32
+ *     where vLLM emits bf16"), Finding 1; vllm.cpp issue #213 ("Qwen3.6 NVFP4
+ *     baselines must reach vLLM speed parity"), original post, instance 2.
+ *   - static per-tensor activation scale, quantize-once and the fused
+ *     RMSNorm->fp8 quant (byte-exact against the unfused path): vllm.cpp #417,
+ *     ranked follow-ons; vllm.cpp #213, "The GDN fp8 merge predicate FIRES".
+ *   - merged projections (qkvz, qkv, gate_up) and merging only on bitwise-equal
+ *     input scales: vllm.cpp #252, "SETTLED BY PAIRED TRACE"; vllm.cpp #213,
+ *     "merge predicate FIRES"; vllm.cpp #417, ranked follow-ons.
+ *   - an M-threshold dispatch between a memory-bound small-M kernel and a
+ *     compute-bound large-M kernel, decided per call as a pure function of M,
+ *     thresholds in [2,16) rejected, workspaces never allocated in the forward:
+ *     vLLM PR #53014 ("[Kernel] add Flashinfer cutedsl w4a16 linear"), the
+ *     Marlin large-M commit message.
+ *   - per-output-channel weight scales ("FP8 channelwise"): same commit message.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns every
+ *     buffer (inputs, outputs, weights, scales, workspaces); the library keeps
+ *     no device allocation and never calls hipMalloc/hipFree.
+ *   - Every GPU call is asynchronous on `stream` (0 = the null stream), never
+ *     synchronizes and returns an int status (enum below).  No C++ exception
+ *     crosses the ABI.
+ *   - M == 0 (or N == 0) is a no-op returning FP8MM_OK.
+ *   - Layouts are row-major.  E4M3 is OCP E4M3FN (bias 7, max 448, S.1111.111 =
+ *     NaN, no infinity), one byte per value.  bf16 is passed as uint16_t bits.
+ *   - Fail closed: a shape or alignment the kernels do not cover returns
+ *     FP8MM_EUNSUPPORTED (there is no silent slow path):
+ *       K % 16 == 0, N % 16 == 0 (each merged shard too), ldx % 8 == 0,
+ *       ldo % 8 == 0, and every pointer 16-byte aligned.
+ *   - FP8MM_EINVAL: a null pointer, a negative size, a leading dimension smaller
+ *     than the row, a non-finite or non-positive scale, an out-of-range
+ *     argument.
+ *   - FP8MM_ELAUNCH: the HIP runtime reported an error for the launch.
+ *   - Kernel choice depends only on (M, N, K) and the threshold, so a stream
+ *     capture into a HIP graph freezes exactly the branch an eager call takes.
+ *   - Results are bitwise deterministic run to run (no floating-point atomics),
+ *     and column n of a merged call is bitwise equal to the same column of a
+ *     separate call on that shard.
+ */
+#ifndef FP8MM_H
+#define FP8MM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fp8mm_status {
+    FP8MM_OK = 0,
+    FP8MM_EINVAL = -1,
+    FP8MM_EUNSUPPORTED = -2,
+    FP8MM_EWORKSPACE = -3,
+    FP8MM_ELAUNCH = -4
+};
+
+/* Largest M the small-M (memory-bound) kernel serves; the threshold may not
+ * exceed it. */
+#define FP8MM_SMALL_M_MAX 64
+/* Smallest threshold accepted: M <= 8 (decode and speculative-verify batches)
+ * must always stay on the small-M kernel. */
+#define FP8MM_THRESHOLD_MIN 16
+/* Most shards one merged call takes. */
+#define FP8MM_MAX_SHARDS 8
+
+/* ------------------------------------------------------------------------
+ * Activation quantization (quantize-once): vllm.cpp #417, ranked follow-ons
+ * (InputLayernormFp8 / QuantFp8Static, "byte-exact quant fusion").
+ *
+ * gamma != NULL -- fused RMSNorm -> FP8, per row m:
+ *     r      = fl32( 1 / sqrt( (sum_k x[m,k]^2) / K + eps ) )   (sum and sqrt in fp64)
+ *     y      = bf16_RNE( fl32( fl32(x[m,k] * r) * gamma[k] ) )
+ *     x_q    = satRNE_E4M3( fl32( y / s_act ) )
+ * gamma == NULL -- plain static quant: x_q = satRNE_E4M3( fl32( x / s_act ) );
+ *     eps is ignored.
+ * Division is IEEE fp32 division.  Values >= 448 in magnitude (inf included)
+ * saturate to +-448, NaN gives 0x7F/0xFF, and a negative value that rounds to
+ * zero gives 0x80.
+ *
+ * x     : bf16 [M, K], row stride ldx (elements, ldx >= K).
+ * gamma : bf16 [K] or NULL.
+ * s_act : static per-tensor scale, finite and > 0 (FP8MM_EINVAL otherwise).
+ * x_q   : E4M3 [M, K], contiguous (row stride K); must not overlap x.
+ * ---------------------------------------------------------------------- */
+int fp8_quant_rmsnorm(const uint16_t* x, int64_t ldx,
+                      const uint16_t* gamma, float eps,
+                      float s_act,
+                      uint8_t* x_q,
+                      int64_t M, int64_t K, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Scaled FP8 GEMM with bf16 output (bmm_fp8 with scale_a = s_act, scale_b =
+ * s_w, out_dtype = bf16): vllm.cpp #252 "CORRECTION"; vllm.cpp #417 Finding 1.
+ *
+ *     out[m,n] = bf16_RNE( fl32( fl32(acc[m,n] * s_act) * s_w[n] ) ),
+ *     acc[m,n] = sum_k dec(x_q[m,k]) * dec(w_q[n,k])   (fp32 accumulation)
+ *
+ * x_q  : E4M3 [M, K], contiguous.
+ * w_q  : E4M3 [N, K], row-major, K contiguous ([out, in], as checkpoints store it).
+ * s_act: per-tensor activation scale (by value), finite and > 0.
+ * s_w  : f32 [N] per-output-channel weight scales.
+ * out  : bf16 [M, N], row stride ldo >= N.
+ * workspace / workspace_bytes: caller-provided scratch of at least
+ *     fp8_scaled_mm_workspace_bytes(M, N, K) bytes (may be NULL/0 when that is
+ *     0); FP8MM_EWORKSPACE if too small.
+ * The kernel is chosen by fp8_scaled_mm_select(M, N, K).
+ * ---------------------------------------------------------------------- */
+int fp8_scaled_mm(const uint8_t* x_q, const uint8_t* w_q,
+                  float s_act, const float* s_w,
+                  uint16_t* out, int64_t ldo,
+                  int64_t M, int64_t N, int64_t K,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Same as fp8_scaled_mm but with the kernel forced: arm 0 = small-M
+ * (memory-bound, M <= FP8MM_SMALL_M_MAX), arm 1 = large-M (MFMA-tiled, any M).
+ * For tests of both arms against each other and for threshold sweeps.
+ * FP8MM_EINVAL for another arm or for arm 0 with M > FP8MM_SMALL_M_MAX. */
+int fp8_scaled_mm_arm(const uint8_t* x_q, const uint8_t* w_q,
+                      float s_act, const float* s_w,
+                      uint16_t* out, int64_t ldo,
+                      int64_t M, int64_t N, int64_t K, int arm,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Merged projection: ONE launch over the physically concatenated weight of
+ * several projections that share x_q and s_act (GDN qkv+z -> qkvz, attention
+ * q/k/v -> qkv, MLP gate/up -> gate_up): vllm.cpp #252 "SETTLED BY PAIRED
+ * TRACE" (merging is the lever: shape and fusion, not library).
+ *
+ * w_q  : E4M3 [sum n_i, K]; s_w: f32 [sum n_i].
+ * shards (HOST array, read during the call only): shard i covers weight rows
+ *     [sum_{j<i} n_j, sum_{j<=i} n_j) and writes bf16 [M, n_i] to out_i with
+ *     row stride ldo_i >= n_i.  n_i % 16 == 0.  1 <= num_shards <= 8.
+ * Merge admission is the caller's: merge only shards whose input scales are
+ * bitwise equal (fp8_scales_bitwise_equal); otherwise call fp8_scaled_mm per
+ * shard.  Column n of shard i is bitwise equal to the same column of a
+ * separate fp8_scaled_mm call on that shard.
+ * ---------------------------------------------------------------------- */
+typedef struct fp8_shard {
+    int64_t n;        /* output columns (weight rows) of this shard */
+    uint16_t* out;    /* device, bf16 [M, n] */
+    int64_t ldo;      /* row stride of out, elements */
+} fp8_shard_t;
+
+int fp8_scaled_mm_merged(const uint8_t* x_q, const uint8_t* w_q,
+                         float s_act, const float* s_w,
+                         const fp8_shard_t* shards, int num_shards,
+                         int64_t M, int64_t K,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes fp8_scaled_mm / _merged need for (M, N, K) (N = sum n_i).
+ * 0 when the chosen kernel needs none.  Pure host function. */
+size_t fp8_scaled_mm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Dispatcher (pure host function of M and the threshold T):
+ * returns 0 (small-M kernel) when M <= T, 1 (large-M kernel) otherwise.
+ * M <= 8 always returns 0 because T >= 16.  Negative sizes -> FP8MM_EINVAL. */
+int fp8_scaled_mm_select(int64_t M, int64_t N, int64_t K);
+
+/* Set the threshold T.  Accepts FP8MM_THRESHOLD_MIN <= t <= FP8MM_SMALL_M_MAX;
+ * anything else (including t in [2,16)) returns FP8MM_EINVAL and leaves T
+ * unchanged.  The initial T is the built-in default unless the environment
+ * variable FP8MM_LARGE_M_THRESHOLD holds a valid value when the library loads.
+ * Set T at start-up: a call that races with a concurrent GEMM call on another
+ * thread may take either value. */
+int fp8_set_large_m_threshold(int64_t t);
+int64_t fp8_get_large_m_threshold(void);
+
+/* Merge predicate (host): 1 iff all n f32 values in the HOST array s have the
+ * same bit pattern (so 0.0 != -0.0 and NaN == NaN only with equal payloads),
+ * 0 otherwise, FP8MM_EINVAL for s == NULL or n < 1. */
+int fp8_scales_bitwise_equal(const float* s, int n);
+
+/* Static string for a status code. */
+const char* fp8mm_strerror(int status);
+
+/* ------------------------------------------------------------------------
+ * Load-time helpers (not on the per-step path).
+ * ---------------------------------------------------------------------- */
+
+/* Per-output-channel weight quantization:
+ *     s_w[n]   = fl32( max_k |w[n,k]| / 448 )   (1 for an all-zero row)
+ *     w_q[n,k] = satRNE_E4M3( fl32( w[n,k] / s_w[n] ) )
+ * w: f32 [N, K] row-major; w_q: E4M3 [N, K]; s_w: f32 [N]. */
+int fp8_quant_weight(const float* w, int64_t N, int64_t K,
+                     uint8_t* w_q, float* s_w, hipStream_t stream);
+
+/* Static activation scale calibration: *s_act = fl32(amax / 448) where amax is
+ * the largest finite |value| of the tensor that fp8_quant_rmsnorm with the same
+ * (x, ldx, gamma, eps, M, K) would quantize (x itself when gamma == NULL, the
+ * bf16 RMSNorm output otherwise); 1 when amax == 0.  s_act is a DEVICE f32.
+ * workspace must hold fp8_act_scale_workspace_bytes(M, K) bytes. */
+size_t fp8_act_scale_workspace_bytes(int64_t M, int64_t K);
+int fp8_act_scale(const uint16_t* x, int64_t ldx,
+                  const uint16_t* gamma, float eps,
+                  int64_t M, int64_t K, float* s_act,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8MM_H */

@@ -137,7 +137,9 @@ uint16_t oracle_f32_to_bf16(float f) { return oracle_f64_to_bf16((double)f); }
 /* ------------------------------------------------------ activation quant --- */
 
 /* Plain static per-tensor quant: x_q = satRNE_E4M3( fl32(f32(x) / s_act) ).
- * One IEEE fp32 division, then the E4M3 rounding (QuantFp8Static). */
+ * One IEEE fp32 division, then the E4M3 rounding (QuantFp8Static).  A NaN input
+ * skips the division so that its own sign bit is the one encoded (IEEE leaves
+ * the sign of a NaN result unspecified). */
 void oracle_quant_act(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
                       float s_act, unsigned char* xq)
 {
@@ -145,7 +147,7 @@ void oracle_quant_act(const uint16_t* x, int64_t ldx, int64_t M, int64_t K,
     for (int64_t m = 0; m < M; ++m)
         for (int64_t k = 0; k < K; ++k) {
             float v = oracle_bf16_to_f32(x[m * ldx + k]);
-            float t = v / s_act;
+            float t = isnan(v) ? v : v / s_act;
             xq[m * K + k] = oracle_e4m3_encode(t);
         }
 }

@@ -1,0 +1,198 @@
+"""The C-ABI library on the host (CPU only, no GPU calls).
+
+Checks that libfp8mm.so loads, exports every function include/fp8mm.h declares,
+and that the pure host logic behaves as documented: the M-threshold dispatcher
+(a pure function of M; M <= 8 always takes the small-M kernel; thresholds in
+[2,16) rejected -- vLLM PR #53014, Marlin large-M commit message), the
+bitwise merge predicate (vllm.cpp #213, "merge predicate FIRES"), status
+strings, workspace queries, and the fail-closed argument validation that
+returns before any HIP call.
+"""
+import ctypes
+import os
+import re
+import struct
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8mm.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+(fp8\w*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def fp8():
+    import fp8_w8a8_scaled_amd as m
+    return m
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("fp8_quant_rmsnorm", "fp8_scaled_mm", "fp8_scaled_mm_merged", "fp8_scaled_mm_select",
+                     "fp8_set_large_m_threshold", "fp8_scales_bitwise_equal", "fp8mm_strerror",
+                     "fp8_scaled_mm_workspace_bytes", "fp8_quant_weight", "fp8_act_scale"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(fp8):
+    lib = ctypes.CDLL(fp8.LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    out = subprocess.run(["nm", "-D", "--defined-only", fp8.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(_declared_functions()) <= exported
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-fsyntax-only", "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__",
+                        "-x", "c", HEADER], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_dispatcher_is_pure_in_m_and_guards_decode(fp8):
+    t0 = fp8.get_large_m_threshold()
+    try:
+        for t in (16, 32, 64):
+            fp8.set_large_m_threshold(t)
+            assert fp8.get_large_m_threshold() == t
+            for M in range(0, 300):
+                want = 0 if M <= t else 1
+                assert fp8.select(M, 10240, 5120) == want
+                assert fp8.select(M, 16, 16) == want          # N and K do not matter
+            for M in range(0, 9):
+                assert fp8.select(M, 5120, 17408) == 0
+        for bad in (-1, 0, 1, 2, 8, 15, 65, 512, 4096):
+            with pytest.raises(fp8.Fp8mmError) as e:
+                fp8.set_large_m_threshold(bad)
+            assert e.value.status == fp8.EINVAL
+            assert fp8.get_large_m_threshold() == 64            # unchanged
+        assert fp8.select(-1, 1, 1) == fp8.EINVAL
+    finally:
+        fp8.set_large_m_threshold(t0)
+
+
+def test_threshold_env_read_at_load():
+    code = ("import fp8_w8a8_scaled_amd as m; print(m.get_large_m_threshold())")
+    env = dict(os.environ, FP8MM_LARGE_M_THRESHOLD="48", PYTHONPATH=ROOT)
+    assert subprocess.run(["python", "-c", code], env=env, capture_output=True, text=True).stdout.strip() == "48"
+    env["FP8MM_LARGE_M_THRESHOLD"] = "4"     # rejected -> built-in default
+    r = subprocess.run(["python", "-c", code], env=env, capture_output=True, text=True).stdout.strip()
+    assert 16 <= int(r) <= 64 and r != "4"
+
+
+def test_scales_bitwise_equal(fp8):
+    assert fp8.scales_bitwise_equal([0.0123, 0.0123, 0.0123])
+    a = np.float32(0.0123)
+    b = np.frombuffer(struct.pack("<I", struct.unpack("<I", struct.pack("<f", a))[0] + 1), np.float32)[0]
+    assert not fp8.scales_bitwise_equal([a, b])                 # one ulp apart
+    assert not fp8.scales_bitwise_equal([0.0, -0.0])            # equal values, different bits
+    assert fp8.scales_bitwise_equal([1.5])
+    with pytest.raises(fp8.Fp8mmError):
+        fp8.scales_bitwise_equal([])
+
+
+def test_status_strings_and_workspace(fp8):
+    for s in (fp8.OK, fp8.EINVAL, fp8.EUNSUPPORTED, fp8.EWORKSPACE, fp8.ELAUNCH):
+        assert fp8.strerror(s) and fp8.strerror(s) != "unknown status"
+    assert fp8.strerror(12345) == "unknown status"
+    assert fp8.workspace_bytes(8, 10240, 5120) == 0
+    lib = fp8.raw_lib()
+    assert lib.fp8_act_scale_workspace_bytes(6576, 5120) >= 6576 * 4
+
+
+# Fake, never-dereferenced device addresses: every call below must be rejected
+# (or be an M == 0 no-op) by host validation before any HIP call -- never add a
+# case here that passes validation with M > 0: it would launch on fake pointers.
+A = 0x10000000
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+
+
+def _mm(lib, xq=A, wq=B, s_act=0.5, sw=C, out=D, ldo=10240, M=8, N=10240, K=5120, ws=None, wsb=0):
+    f = lib.fp8_scaled_mm
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    return f(xq, wq, s_act, sw, out, ldo, M, N, K, ws, wsb, None)
+
+
+def test_gemm_validation_fails_closed(fp8):
+    lib = fp8.raw_lib()
+    E, U = fp8.EINVAL, fp8.EUNSUPPORTED
+    assert _mm(lib, xq=None) == E
+    assert _mm(lib, out=None) == E
+    assert _mm(lib, M=-1) == E
+    assert _mm(lib, N=-16) == E
+    assert _mm(lib, ldo=16) == E                                # ldo < N
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert _mm(lib, s_act=bad) == E
+    assert _mm(lib, K=5121) == U                                # K % 16
+    assert _mm(lib, K=5128) == U
+    assert _mm(lib, N=10248, ldo=10248) == U                    # N % 16
+    assert _mm(lib, ldo=10244) == U                             # ldo % 8
+    assert _mm(lib, xq=A + 8) == U                              # 16-byte alignment
+    assert _mm(lib, wq=B + 1) == U
+    assert _mm(lib, sw=C + 4) == U
+    assert _mm(lib, out=D + 2) == U
+    assert _mm(lib, M=0) == fp8.OK                              # no-op, no launch
+    f = lib.fp8_scaled_mm_arm
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert f(A, B, 0.5, C, D, 16, 65, 16, 16, 0, None, 0, None) == E   # small-M arm beyond its M
+    assert f(A, B, 0.5, C, D, 16, 8, 16, 16, 2, None, 0, None) == E    # no such arm
+    assert f(A, B, 0.5, C, D, 16, 0, 16, 16, 1, None, 0, None) == fp8.OK
+
+
+def test_merged_validation_fails_closed(fp8):
+    lib = fp8.raw_lib()
+    Shard = fp8.Shard
+    f = lib.fp8_scaled_mm_merged
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(Shard),
+                  ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+
+    def call(shards, n=None, M=0):
+        arr = (Shard * max(1, len(shards)))(*shards)
+        return f(A, B, 0.5, C, arr, len(shards) if n is None else n, M, 5120, None, 0, None)
+
+    good = [Shard(17408, D, 17408), Shard(17408, D + 0x1000000, 17408)]
+    assert call(good) == fp8.OK                                  # M == 0 no-op
+    assert call(good, n=0) == fp8.EINVAL
+    assert call(good * 5, n=9) == fp8.EINVAL                     # > 8 shards
+    assert call([Shard(17400, D, 17408)]) == fp8.EUNSUPPORTED    # shard n % 16
+    assert call([Shard(17408, D + 8, 17408)]) == fp8.EUNSUPPORTED
+    assert call([Shard(17408, None, 17408)], M=1) == fp8.EINVAL   # rejected before any launch
+    assert call([Shard(17408, None, 17408)]) == fp8.OK           # empty product: null output allowed
+    assert call([Shard(17408, D, 16)]) == fp8.EINVAL             # ldo < n
+
+
+def test_quant_validation_fails_closed(fp8):
+    lib = fp8.raw_lib()
+    f = lib.fp8_quant_rmsnorm
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    E, U = fp8.EINVAL, fp8.EUNSUPPORTED
+    assert f(None, 5120, C, 1e-6, 0.1, B, 8, 5120, None) == E
+    assert f(A, 5000, C, 1e-6, 0.1, B, 8, 5120, None) == E       # ldx < K
+    assert f(A, 5120, C, 1e-6, 0.0, B, 8, 5120, None) == E
+    assert f(A, 5120, C, float("nan"), 0.1, B, 8, 5120, None) == E
+    assert f(A, 5120, C, 1e-6, 0.1, B, 8, 5112 + 4, None) == U   # K % 16
+    assert f(A, 5124, C, 1e-6, 0.1, B, 8, 5120, None) == U       # ldx % 8
+    assert f(A + 2, 5120, C, 1e-6, 0.1, B, 8, 5120, None) == U
+    assert f(A, 5120, C + 2, 1e-6, 0.1, B, 8, 5120, None) == U
+    assert f(A, 5120, C, 1e-6, 0.1, A + 16, 8, 5120, None) == E  # x_q overlaps x
+    assert f(A, 5120, C, 1e-6, 0.1, B, 0, 5120, None) == fp8.OK
+    g = lib.fp8_quant_weight
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert g(A, 16, 24, B, C, None) == U
+    assert g(A, 0, 32, B, C, None) == fp8.OK
+    assert g(None, 16, 32, B, C, None) == E

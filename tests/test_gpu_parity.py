@@ -1,0 +1,337 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Bar: E4M3 activation and weight bytes and the static scales bit-exact; bf16
+outputs within max(2 bf16 ulp, 1e-3 * ||row||_2) per element of the oracle
+(tests/helpers.py).  Inputs are the seeded synthetic workloads of workloads/.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from helpers import (assert_within_tolerance, bf16_dev, f32_dev, host_u16, host_u8, u8_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fp8():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import fp8_w8a8_scaled_amd as m
+    return m
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ quantization --
+
+@pytest.mark.parametrize("s_act", [1.0, 0.5, 3.0, 1.0 / 7.0, 0.2])
+def test_quant_all_bf16_patterns_bit_exact(fp8, s_act):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(1, -1)
+    got = host_u8(fp8.quant(bf16_dev(bits), s_act))
+    want = oracle.quant_act(bits, np.float32(s_act))
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:10]
+
+
+@pytest.mark.parametrize("wid,M,K", [(1, 4, 256), (2, 1, 5120), (2, 2, 5120), (2, 4, 5120), (2, 8, 5120),
+                                     (3, 1, 17408), (3, 8, 17408), (3, 32, 17408), (5, 6576, 17408)])
+def test_plain_quant_and_scale_bit_exact(fp8, wid, M, K):
+    x = wl.activation_bf16(wid, M, K, outliers=wid in (2, 3, 4), tensor=wl.T_DOWN_X if K == 17408 else wl.T_X)
+    xd = bf16_dev(x)
+    s_gpu = fp8.act_scale(xd)
+    s_ref = oracle.act_scale(x)
+    assert np.float32(s_gpu.item()).view(np.uint32) == np.float32(s_ref).view(np.uint32)
+    got = host_u8(fp8.quant(xd, s_ref))
+    assert np.array_equal(got, oracle.quant_act(x, s_ref))
+
+
+@pytest.mark.parametrize("wid,M", [(3, 1), (3, 4), (3, 8), (3, 16), (3, 32), (5, 6576)])
+def test_fused_rmsnorm_quant_bit_exact(fp8, wid, M):
+    K = 5120
+    x = wl.activation_bf16(wid, M, K, outliers=(wid == 3))
+    g = wl.gamma_bf16(wid, K)
+    xd, gd = bf16_dev(x), bf16_dev(g)
+    s_gpu = fp8.act_scale(xd, gd, wl.EPS)
+    s_ref = oracle.act_scale(x, g, wl.EPS)
+    assert np.float32(s_gpu.item()).view(np.uint32) == np.float32(s_ref).view(np.uint32)
+    got = host_u8(fp8.quant_rmsnorm(xd, gd, s_ref, wl.EPS))
+    want = oracle.quant_rmsnorm(x, g, wl.EPS, s_ref)
+    assert np.array_equal(got, want), f"{int((got != want).sum())} bytes differ"
+
+
+def _strided(x, ld):
+    big = np.zeros((x.shape[0], ld), np.uint16)
+    big[:, :x.shape[1]] = x
+    xd = bf16_dev(big)[:, :x.shape[1]]
+    assert xd.stride(0) == ld
+    return xd
+
+
+def test_quant_strided_input_and_special_rows(fp8):
+    M, K, ld = 5, 5120, 5136
+    s = np.float32(0.0137)
+    x = wl.activation_bf16(3, M, K, outliers=True)
+    x[1] = 0                                   # all-zero row: r = 1/sqrt(eps)
+    x[2] = 0x8000                              # -0 row
+    x[3, :5] = np.array([0x0001, 0x8001, 0x7F7F, 0xFF7F, 0x0080], np.uint16)   # subnormal, +-max, min normal
+    g = wl.gamma_bf16(3, K)
+    got = host_u8(fp8.quant_rmsnorm(_strided(x, ld), bf16_dev(g), float(s), wl.EPS))
+    assert np.array_equal(got, oracle.quant_rmsnorm(x, g, wl.EPS, s))
+    # plain quant also takes non-finite inputs: inf saturates, NaN keeps its sign
+    x[4, :4] = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC1], np.uint16)
+    got = host_u8(fp8.quant(_strided(x, ld), float(s)))
+    assert np.array_equal(got, oracle.quant_act(x, s))
+    assert list(got[4, :4]) == [0x7E, 0xFE, 0x7F, 0xFF]
+
+
+@pytest.mark.parametrize("N,K", [(384, 256), (10240, 5120), (48, 17408)])
+def test_weight_quant_bit_exact(fp8, N, K):
+    w = wl.weight_f32(1 if K == 256 else 2, N, K)
+    w[3] = 0.0                                  # zero row -> s_w = 1, codes 0
+    w[5, 7] = np.float32(3.0e38)                # a huge element sets that row's scale
+    wq, sw = fp8.quant_weight(f32_dev(w))
+    owq, osw = oracle.quant_weight(w)
+    assert np.array_equal(sw.cpu().numpy().view(np.uint32), osw.view(np.uint32))
+    assert np.array_equal(host_u8(wq), owq)
+
+
+# -------------------------------------------------------------------- GEMM --
+
+def _prepare(wid, M, N, K, outliers, w_tensor=wl.T_W, x_tensor=wl.T_X):
+    """Oracle-side inputs: quantized activation, weight, scales."""
+    x = wl.activation_bf16(wid, M, K, outliers=outliers, tensor=x_tensor)
+    s_act = oracle.act_scale(x)
+    xq = oracle.quant_act(x, s_act)
+    wq, sw = oracle.quant_weight(wl.weight_f32(wid, N, K, tensor=w_tensor))
+    return xq, wq, s_act, sw
+
+
+def _run_arm(fp8, xq, wq, s_act, sw, arm):
+    out = fp8.scaled_mm(u8_dev(xq), u8_dev(wq), s_act, f32_dev(sw), arm=arm)
+    return host_u16(out)
+
+
+@pytest.mark.parametrize("arm", [0, 1])
+def test_tiny_all_elements_both_arms(fp8, arm):
+    xq, wq, s_act, sw = _prepare(1, 4, 384, 256, outliers=False)
+    ref, v = oracle.scaled_mm(xq, wq, s_act, sw, want_v=True)
+    assert_within_tolerance(_run_arm(fp8, xq, wq, s_act, sw, arm), ref, v, f"tiny arm {arm}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_decode_projection_all_elements(fp8, M):
+    xq, wq, s_act, sw = _prepare(2, M, 10240, 5120, outliers=True)
+    ref, v = oracle.scaled_mm(xq, wq, s_act, sw, want_v=True)
+    got = host_u16(fp8.scaled_mm(u8_dev(xq), u8_dev(wq), s_act, f32_dev(sw)))
+    assert fp8.select(M, 10240, 5120) == 0
+    assert_within_tolerance(got, ref, v, f"decode proj M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 8, 16, 32])
+def test_decode_mlp_merged_gate_up_and_down(fp8, M):
+    """Config of the decode MLP: fused RMSNorm quant -> merged gate_up (two
+    17408-column shards, one launch) -> down projection (K = 17408)."""
+    K, N = 5120, 34816
+    x = wl.activation_bf16(3, M, K, outliers=True)
+    g = wl.gamma_bf16(3, K)
+    s1 = oracle.act_scale(x, g, wl.EPS)
+    xq = oracle.quant_rmsnorm(x, g, wl.EPS, s1)
+    xq_gpu = fp8.quant_rmsnorm(bf16_dev(x), bf16_dev(g), s1, wl.EPS)
+    assert np.array_equal(host_u8(xq_gpu), xq)
+    wq, sw = oracle.quant_weight(wl.weight_f32(3, N, K))
+    outs = fp8.scaled_mm_merged(xq_gpu, u8_dev(wq), s1, f32_dev(sw), [17408, 17408])
+    ref, v = oracle.scaled_mm(xq, wq, s1, sw, want_v=True)
+    got = np.concatenate([host_u16(o) for o in outs], axis=1)
+    assert_within_tolerance(got, ref, v, f"gate_up M={M}")
+    # down projection on its own seeded input
+    xd = wl.activation_bf16(3, M, 17408, outliers=True, tensor=wl.T_DOWN_X)
+    s2 = oracle.act_scale(xd)
+    xq2 = oracle.quant_act(xd, s2)
+    wq2, sw2 = oracle.quant_weight(wl.weight_f32(3, 5120, 17408, tensor=wl.T_DOWN_W))
+    got2 = host_u16(fp8.scaled_mm(u8_dev(xq2), u8_dev(wq2), s2, f32_dev(sw2)))
+    ref2, v2 = oracle.scaled_mm(xq2, wq2, s2, sw2, want_v=True)
+    assert_within_tolerance(got2, ref2, v2, f"down M={M}")
+
+
+def test_prefill_sampled_rows(fp8):
+    """Prefill chunk, M = 6576 (large-M arm): the whole GEMM on the GPU, checked
+    on sampled rows (tile edges, the ragged tail, random rows) against the oracle."""
+    M, K, N = 6576, 5120, 34816
+    x = wl.activation_bf16(5, M, K, outliers=False)
+    g = wl.gamma_bf16(5, K)
+    s1 = oracle.act_scale(x, g, wl.EPS)
+    xq_gpu = fp8.quant_rmsnorm(bf16_dev(x), bf16_dev(g), s1, wl.EPS)
+    xq = host_u8(xq_gpu)
+    w = wl.weight_f32(5, N, K)
+    wq_gpu, sw_gpu = fp8.quant_weight(f32_dev(w))
+    del w
+    assert fp8.select(M, N, K) == 1
+    outs = fp8.scaled_mm_merged(xq_gpu, wq_gpu, s1, sw_gpu, [17408, 17408])
+    _sync()
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 4095, 4096, 6399, 6400, 6527, 6528, 6575],
+                                     np.random.Generator(np.random.PCG64(3)).integers(0, M, 19)]))
+    wq, sw = host_u8(wq_gpu), sw_gpu.cpu().numpy()
+    got = np.concatenate([host_u16(o) for o in outs], axis=1)[rows]
+    ref, v = oracle.scaled_mm(xq[rows], wq, s1, sw, want_v=True)
+    assert_within_tolerance(got, ref, v, "prefill gate_up")
+    # down projection K = 17408
+    xd = wl.activation_bf16(5, M, 17408, outliers=False, tensor=wl.T_DOWN_X)
+    s2 = oracle.act_scale(xd)
+    xq2_gpu = fp8.quant(bf16_dev(xd), s2)
+    wd = wl.weight_f32(5, 5120, 17408, tensor=wl.T_DOWN_W)
+    wq2_gpu, sw2_gpu = fp8.quant_weight(f32_dev(wd))
+    out2 = fp8.scaled_mm(xq2_gpu, wq2_gpu, s2, sw2_gpu)
+    _sync()
+    ref2, v2 = oracle.scaled_mm(host_u8(xq2_gpu)[rows], host_u8(wq2_gpu), s2, sw2_gpu.cpu().numpy(), want_v=True)
+    assert_within_tolerance(host_u16(out2)[rows], ref2, v2, "prefill down")
+
+
+@pytest.mark.parametrize("arm", [0, 1])
+def test_every_e4m3_code_through_mfma(fp8, arm):
+    """One-hot GEMM: x_q = e_k with code 0x38 (1.0), s_act = s_w = 1, so out[0, n]
+    = dec(w_q[n, k]) exactly; w_q[:, k] runs over all 254 finite codes.  Pins the
+    matrix cores' FP8 decoding (OCP E4M3FN, not FNUZ) and the operand layouts."""
+    K, N = 256, 256
+    codes = wl.FINITE_CODE_VALUES
+    tab = oracle.e4m3_table()
+    for k in (0, 77, 255):
+        wq = wl.random_codes(1, N, K, m=k)
+        wq[:254, k] = codes
+        wq[254:, k] = 0
+        xq = np.zeros((2, K), np.uint8)
+        xq[0, k] = 0x38
+        xq[1, k] = 0xB8                        # -1.0 in row 1
+        out = _run_arm(fp8, xq, wq, 1.0, np.ones(N, np.float32), arm)
+        want = tab[wq[:, k]]
+        got0 = (out[0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        got1 = (out[1].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert np.array_equal(got0, want) and np.array_equal(got1, -want)
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 32, 64])
+def test_both_arms_agree_with_oracle(fp8, M):
+    xq, wq, s_act, sw = _prepare(2, M, 2048, 5120, outliers=True)
+    ref, v = oracle.scaled_mm(xq, wq, s_act, sw, want_v=True)
+    a0 = _run_arm(fp8, xq, wq, s_act, sw, 0)
+    a1 = _run_arm(fp8, xq, wq, s_act, sw, 1)
+    assert_within_tolerance(a0, ref, v, f"small-M arm M={M}")
+    assert_within_tolerance(a1, ref, v, f"large-M arm M={M}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (3, 48, 48), (17, 32, 272), (33, 64, 400), (65, 80, 144),
+                                   (129, 144, 1040), (257, 272, 2064), (300, 1040, 17408)])
+def test_ragged_shapes_both_arms(fp8, M, N, K):
+    g = np.random.Generator(np.random.PCG64(M * 1000 + N + K))
+    xq = wl.random_codes(9, M, K, m=M)
+    wq = wl.random_codes(9, N, K, tensor=wl.T_W, m=N)
+    s_act = float(np.float32(0.0071))
+    sw = (g.random(N) * 1e-3 + 1e-4).astype(np.float32)
+    ref, v = oracle.scaled_mm(xq, wq, s_act, sw, want_v=True)
+    arms = [1] if M > 64 else [0, 1]
+    for arm in arms:
+        assert_within_tolerance(_run_arm(fp8, xq, wq, s_act, sw, arm), ref, v, f"{M}x{N}x{K} arm {arm}")
+
+
+def test_strided_output_and_zero_m(fp8):
+    import torch
+    xq, wq, s_act, sw = _prepare(1, 4, 384, 256, outliers=False)
+    big = torch.full((4, 400), -7.0, dtype=torch.bfloat16, device="cuda")
+    view = big[:, 8:392]
+    fp8.scaled_mm(u8_dev(xq), u8_dev(wq), s_act, f32_dev(sw), out=view)
+    ref, v = oracle.scaled_mm(xq, wq, s_act, sw, want_v=True)
+    assert_within_tolerance(host_u16(view), ref, v, "strided out")
+    assert torch.all(big[:, :8] == -7) and torch.all(big[:, 392:] == -7)
+    empty = fp8.scaled_mm(u8_dev(xq[:0]), u8_dev(wq), s_act, f32_dev(sw))
+    assert empty.shape == (0, 384)
+
+
+# ------------------------------------------------- merge and determinism ----
+
+@pytest.mark.parametrize("M", [1, 8, 32, 300])
+def test_merged_equals_split_bitwise(fp8, M):
+    K = 5120
+    xq = wl.random_codes(4, M, K, m=M)
+    wq = wl.random_codes(4, 1040, K, tensor=wl.T_W)
+    sw = (np.random.Generator(np.random.PCG64(1)).random(1040) * 1e-3 + 1e-5).astype(np.float32)
+    s_act = 0.013
+    shards = [512, 16, 512]
+    xd, wd, swd = u8_dev(xq), u8_dev(wq), f32_dev(sw)
+    merged = [host_u16(o) for o in fp8.scaled_mm_merged(xd, wd, s_act, swd, shards)]
+    start = 0
+    for n, mo in zip(shards, merged):
+        split = host_u16(fp8.scaled_mm(xd, wd[start:start + n], s_act, swd[start:start + n]))
+        assert np.array_equal(split, mo), f"shard at {start} differs"
+        start += n
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_run_to_run_and_graph_capture_bitwise(fp8, M):
+    import torch
+    xq, wq, s_act, sw = _prepare(2, M, 10240, 5120, outliers=True)
+    x = wl.activation_bf16(2, M, 5120, outliers=True)
+    xd, wd, swd = bf16_dev(x), u8_dev(wq), f32_dev(sw)
+    s = oracle.act_scale(x)
+    xq_d = fp8.quant(xd, s)
+    eager = fp8.scaled_mm(xq_d, wd, s, swd)
+    first = host_u16(eager)
+    for _ in range(3):
+        assert np.array_equal(host_u16(fp8.scaled_mm(xq_d, wd, s, swd)), first)
+    # capture quant + GEMM into a HIP graph; replay several times with eager work between
+    xq_g = torch.empty_like(xq_d)
+    out_g = torch.empty_like(eager)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        fp8.quant(xd, s, out=xq_g)
+        fp8.scaled_mm(xq_g, wd, s, swd, out=out_g)
+    torch.cuda.current_stream().wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fp8.quant(xd, s, out=xq_g)
+        fp8.scaled_mm(xq_g, wd, s, swd, out=out_g)
+    for i in range(4):
+        out_g.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u16(out_g), first), f"replay {i}"
+        assert np.array_equal(host_u8(xq_g), host_u8(xq_d))
+        _ = fp8.scaled_mm(xq_d, wd, s, swd)          # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_dispatcher_routes_to_the_selected_arm(fp8):
+    t0 = fp8.get_large_m_threshold()
+    try:
+        for t in (16, 32, 64):
+            fp8.set_large_m_threshold(t)
+            for M in (1, 8, t, t + 1):
+                xq, wq, s_act, sw = _prepare(2, M, 512, 1024, outliers=True)
+                auto = _run_arm(fp8, xq, wq, s_act, sw, None)
+                arm = fp8.select(M, 512, 1024)
+                assert arm == (0 if M <= t else 1)
+                assert np.array_equal(auto, _run_arm(fp8, xq, wq, s_act, sw, arm))
+    finally:
+        fp8.set_large_m_threshold(t0)
+
+
+def test_fail_closed_on_device_tensors(fp8):
+    import torch
+    xq, wq, s_act, sw = _prepare(1, 4, 384, 256, outliers=False)
+    xd, wd, swd = u8_dev(xq), u8_dev(wq), f32_dev(sw)
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(fp8.Fp8mmError) as e:
+            fp8.scaled_mm(xd, wd, bad, swd)
+        assert e.value.status == fp8.EINVAL
+    raw = torch.zeros(4 * 256 + 1, dtype=torch.uint8, device="cuda")
+    mis = raw[1:].view(4, 256)                      # 1-byte misaligned x_q
+    with pytest.raises(fp8.Fp8mmError) as e:
+        fp8.scaled_mm(mis, wd, s_act, swd)
+    assert e.value.status == fp8.EUNSUPPORTED
+    x = torch.zeros((4, 24), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fp8.Fp8mmError) as e:
+        fp8.quant(x, 1.0)
+    assert e.value.status == fp8.EUNSUPPORTED

@@ -30,7 +30,7 @@ MUTATIONS = {
                         "if (e == 0u) mag = ldexp((double)m, -10);"),
     "fnuz_bias": ("else mag = ldexp(1.0 + (double)m / 8.0, (int)e - 7);",
                   "else mag = ldexp(1.0 + (double)m / 8.0, (int)e - 8);"),
-    "reciprocal_not_division": ("float t = v / s_act;", "float t = v * (1.0f / s_act);"),
+    "reciprocal_not_division": ("float t = isnan(v) ? v : v / s_act;", "float t = isnan(v) ? v : v * (1.0f / s_act);"),
     "transposed_operand": ("const unsigned char* b = wq + n * K;", "const unsigned char* b = wq + m * K;"),
     "dropped_weight_scale": ("val = (acc * (double)s_act) * (double)s_w[n];", "val = acc * (double)s_act;"),
     "epilogue_through_fp32": ("out[m * ldo + n] = oracle_f64_to_bf16(val);",
