@@ -10,33 +10,90 @@
 // vllm.cpp #213 "+0.0532 splitK reduce").
 //
 // Design (MI355X-first, not a port of those tiles):
-//  * one workgroup owns a 16-row slice of W (one MFMA A tile) and the whole K;
-//    its W waves split K into 128-byte chunks, wave w taking chunks w, w+W, ...
-//    so that the workgroup sweeps each weight row front to back;
-//  * every lane streams its 2 x 16 B of W per chunk straight from HBM into
-//    registers (each weight byte is used by one MFMA only, so no LDS staging),
-//    batched four chunks deep (fewer when x_q needs two or four M tiles);
-//    x_q (at most 64 x K bytes) is re-read from L2;
-//  * v_mfma_f32_16x16x128_f8f6f4 with x_q as the B operand, M padded to 16 (or
-//    two / four M tiles for M <= 32 / 64): MFMA keeps the fp32 work off the VALU;
-//  * the W partial sums are reduced in LDS in a fixed order (no atomics), then
-//    the scale epilogue and the bf16 store happen in registers.
-//  W depends on K only, so every column's summation order is the same for a
-//  merged call and a per-shard call: results are bitwise identical.
+//  * a workgroup owns NT x 16 rows of W (NT MFMA A tiles) and the whole K; its
+//    W waves split K into 128-byte chunks, wave w taking chunks w, w+W, ..., so
+//    the workgroup sweeps each weight row front to back;
+//  * every lane streams 2 x 16 B of each of its rows per chunk straight from
+//    HBM into registers: bytes [16g, 16g+16) and [64+16g, 80+16g) of the chunk
+//    for lane group g, so one load instruction covers 64 contiguous bytes of
+//    each of 16 rows.  Each weight byte feeds one MFMA only, so there is no LDS
+//    staging.  Loads run a batch of chunks ahead of the MFMAs (double buffer);
+//  * v_mfma_f32_16x16x128_f8f6f4 with x_q as the B operand, M padded to 16
+//    (MT = 2 or 4 M tiles for M <= 32 / 64).  x_q (at most 64 x K bytes) is read
+//    from L2 with the same K mapping as W, which is all the MFMA needs;
+//  * the W per-wave partial sums are reduced in LDS in a fixed order (no
+//    atomics), then the scale epilogue and the bf16 store happen in registers.
+//  W and the chunk assignment depend on K only, so every column's summation
+//  order is the same for a merged call and a per-shard call: bitwise identical.
 #include "device_common.h"
 #include "internal.h"
+
+// Tuning knobs (build-time).  Target chunks per wave -> waves per workgroup.
+#ifndef FP8MM_SMALLM_CPW
+#define FP8MM_SMALLM_CPW 5
+#endif
+// Chunk fragments (x N tiles x M tiles) in flight per wave per batch.
+#ifndef FP8MM_SMALLM_BATCH
+#define FP8MM_SMALLM_BATCH 2
+#endif
+// 1: issue the next batch's loads before the current batch's MFMAs.
+#ifndef FP8MM_SMALLM_PIPE
+#define FP8MM_SMALLM_PIPE 1
+#endif
+// 16-row N tiles per workgroup (each wave covers all of them; x_q is reused).
+#ifndef FP8MM_SMALLM_NT
+#define FP8MM_SMALLM_NT 1
+#endif
+// 1: weight loads marked non-temporal (streamed once).
+#ifndef FP8MM_SMALLM_NTLOAD
+#define FP8MM_SMALLM_NTLOAD 0
+#endif
+
+// Largest LDS footprint (x_q rows + reduction) of the all-in-flight variant;
+// 0 disables it.  Three workgroups of this size fit in a 160 KB CU.
+#ifndef FP8MM_SMALLM_XLDS_MAX
+#define FP8MM_SMALLM_XLDS_MAX (52 * 1024)
+#endif
+// 16-row weight tiles per workgroup of the all-in-flight variant (x_q reuse).
+#ifndef FP8MM_SMALLM_XLDS_NT
+#define FP8MM_SMALLM_XLDS_NT 1
+#endif
 
 namespace fp8mm {
 
 namespace {
 
+constexpr int kXldsMaxCpw = 8;   // weight chunks per wave held in registers
+constexpr int kXldsNT = FP8MM_SMALLM_XLDS_NT;   // 16-row tiles per workgroup
 constexpr int kChunk = 128;     // K bytes per MFMA (16x16x128)
-constexpr int kBatchRegs = 4;   // chunk x M-tile fragments in flight per wave per batch
 constexpr int kMaxWaves = 16;
+constexpr int kNT = FP8MM_SMALLM_NT;
 
-__device__ __forceinline__ uint4 ld16(const uint8_t* p)
+__device__ __forceinline__ uint4 ld16_stream(const uint8_t* p)
 {
+#if FP8MM_SMALLM_NTLOAD
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+#else
     return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+
+// Branch-free masked 16-byte load: the address is always an in-bounds one (the
+// caller passes a fallback), and invalid lanes get zeros through a select.  A
+// conditional load would become a branch, after which the compiler waits for
+// all outstanding loads -- serializing the stream.
+__device__ __forceinline__ uint4 ld16_masked(const uint8_t* p, const uint8_t* safe, bool ok)
+{
+    const uint4 v = *reinterpret_cast<const uint4*>(ok ? p : safe);
+    return ok ? v : make_uint4(0u, 0u, 0u, 0u);
+}
+
+__device__ __forceinline__ uint4 ld16_stream_masked(const uint8_t* p, const uint8_t* safe, bool ok)
+{
+    const uint4 v = ld16_stream(ok ? p : safe);
+    return ok ? v : make_uint4(0u, 0u, 0u, 0u);
 }
 
 __device__ __forceinline__ v8i pack(const uint4 lo, const uint4 hi)
@@ -47,96 +104,266 @@ __device__ __forceinline__ v8i pack(const uint4 lo, const uint4 hi)
     return r;
 }
 
+template <int MT, int B>
+struct Frags {
+    uint4 a[B][kNT][2];
+    uint4 b[B][MT][2];
+};
+
+template <int MT, int B>
+__device__ __forceinline__ void load_batch(Frags<MT, B>& f, int i0, int nc, int wave, int W, int g, int64_t K,
+                                           const uint8_t* const (&wrow)[kNT], const bool (&wv)[kNT],
+                                           const uint8_t* const (&xrow)[MT], const bool (&xv)[MT])
+{
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+        const int64_t c = (int64_t)wave + (int64_t)(i0 + j) * W;
+        const int64_t k0 = c * kChunk + g * 16;          // this lane's two 16-byte pieces
+        const bool cv = (i0 + j) < nc;
+        const bool v0 = cv && k0 < K, v1 = cv && k0 + 64 < K;
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) {
+            f.a[j][t][0] = ld16_stream_masked(wrow[t] + k0, wrow[t], v0 && wv[t]);
+            f.a[j][t][1] = ld16_stream_masked(wrow[t] + k0 + 64, wrow[t], v1 && wv[t]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            f.b[j][mt][0] = ld16_masked(xrow[mt] + k0, xrow[mt], v0 && xv[mt]);
+            f.b[j][mt][1] = ld16_masked(xrow[mt] + k0 + 64, xrow[mt], v1 && xv[mt]);
+        }
+    }
+}
+
+template <int MT, int B>
+__device__ __forceinline__ void mfma_batch(const Frags<MT, B>& f, v4f (&acc)[kNT][MT])
+{
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) {
+            const v8i A = pack(f.a[j][t][0], f.a[j][t][1]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[t][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    A, pack(f.b[j][mt][0], f.b[j][mt][1]), acc[t][mt], 0, 0, 0, 0, 0, 0);
+        }
+}
+
+// Sum the W per-wave partials red[W][NTt][MT][64] in wave order (fixed, no
+// atomics), apply the scales in fp32 and store bf16.  16x16 MFMA C layout:
+// lane l holds rows 4*(l/16)+v (= n) of column l%16 (= m).
+template <int MT, int NTt>
+__device__ __forceinline__ void reduce_store(const v4f* red, int W, int64_t n0, float s_act,
+                                             const float* __restrict__ s_w, const ShardTable& sh,
+                                             int M, int64_t N)
+{
+    for (int idx = threadIdx.x; idx < NTt * MT * 64; idx += blockDim.x) {   // blocks may be narrower
+        const int t = idx / (MT * 64), mt = (idx >> 6) % MT, l = idx & 63;
+        const int64_t nt0 = n0 + 16 * t;
+        const int m = mt * 16 + (l & 15);
+        if (nt0 >= N || m >= M) continue;
+        v4f s = red[(t * MT + mt) * 64 + l];
+        for (int w = 1; w < W; ++w) {
+            const v4f p = red[((w * NTt + t) * MT + mt) * 64 + l];
+            s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+        }
+        const int64_t n = nt0 + 4 * (l >> 4);
+        int i = 0;
+        while (i + 1 < sh.num && nt0 >= sh.start[i + 1]) ++i;
+        const float4 sw = *reinterpret_cast<const float4*>(s_w + n);
+        const uint32_t o0 = f32_to_bf16_rne((s.x * s_act) * sw.x) | (f32_to_bf16_rne((s.y * s_act) * sw.y) << 16);
+        const uint32_t o1 = f32_to_bf16_rne((s.z * s_act) * sw.z) | (f32_to_bf16_rne((s.w * s_act) * sw.w) << 16);
+        *reinterpret_cast<uint2*>(sh.out[i] + (int64_t)m * sh.ldo[i] + (n - sh.start[i])) = make_uint2(o0, o1);
+    }
+}
+
 template <int MT>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act,
-    const float* __restrict__ s_w, ShardTable sh, int M, int64_t K, int nchunks)
+    const float* __restrict__ s_w, ShardTable sh, int M, int64_t N, int64_t K, int nchunks)
 {
-    extern __shared__ v4f red[];                       // [W][MT][64]
+    extern __shared__ v4f red[];                       // [W][kNT][MT][64]
+    constexpr int B = FP8MM_SMALLM_BATCH / (MT * kNT) > 0 ? FP8MM_SMALLM_BATCH / (MT * kNT) : 1;
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * kNT);
 
-    const uint8_t* wrow = wq + (n0 + r) * K + g * 32;
+    const uint8_t* wrow[kNT];
+    bool wv[kNT];
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+        wv[t] = n0 + 16 * t < N;                        // a ragged last workgroup may hold fewer tiles
+        wrow[t] = wq + (wv[t] ? n0 + 16 * t + r : r) * K;
+    }
     const uint8_t* xrow[MT];
     bool xv[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int m = mt * 16 + r;
         xv[mt] = m < M;
-        xrow[mt] = xq + (int64_t)(xv[mt] ? m : 0) * K + g * 32;
+        xrow[mt] = xq + (int64_t)(xv[mt] ? m : 0) * K;
     }
 
-    v4f acc[MT];
+    v4f acc[kNT][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kNT; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int kBatch = kBatchRegs / MT > 0 ? kBatchRegs / MT : 1;   // chunks per batch
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
     const int nc = (nchunks - wave + W - 1) / W;       // chunks owned by this wave
-    for (int i0 = 0; i0 < nc; i0 += kBatch) {
-        uint4 a[kBatch][2];
-        uint4 b[kBatch][MT][2];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int64_t c = (int64_t)wave + (int64_t)(i0 + j) * W;
-            const int64_t kb = c * kChunk + g * 32;    // this lane's first K byte
-            const bool cv = (i0 + j) < nc;
-            const bool v0 = cv && kb < K, v1 = cv && kb + 16 < K;
-            a[j][0] = v0 ? ld16(wrow + c * kChunk) : z;
-            a[j][1] = v1 ? ld16(wrow + c * kChunk + 16) : z;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                b[j][mt][0] = (v0 && xv[mt]) ? ld16(xrow[mt] + c * kChunk) : z;
-                b[j][mt][1] = (v1 && xv[mt]) ? ld16(xrow[mt] + c * kChunk + 16) : z;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const v8i A = pack(a[j][0], a[j][1]);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    A, pack(b[j][mt][0], b[j][mt][1]), acc[mt], 0, 0, 0, 0, 0, 0);
-        }
+#if FP8MM_SMALLM_PIPE
+    Frags<MT, B> cur;
+    load_batch<MT, B>(cur, 0, nc, wave, W, g, K, wrow, wv, xrow, xv);
+    for (int i0 = 0; i0 < nc; i0 += B) {
+        Frags<MT, B> nxt;
+        const bool more = i0 + B < nc;
+        if (more) load_batch<MT, B>(nxt, i0 + B, nc, wave, W, g, K, wrow, wv, xrow, xv);
+        mfma_batch<MT, B>(cur, acc);
+        if (more) cur = nxt;
     }
+#else
+    for (int i0 = 0; i0 < nc; i0 += B) {
+        Frags<MT, B> cur;
+        load_batch<MT, B>(cur, i0, nc, wave, W, g, K, wrow, wv, xrow, xv);
+        mfma_batch<MT, B>(cur, acc);
+    }
+#endif
 
     // Fixed-order reduction of the W per-wave partials.
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = acc[mt];
+    for (int t = 0; t < kNT; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) red[((wave * kNT + t) * MT + mt) * 64 + lane] = acc[t][mt];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < MT * 64; idx += blockDim.x) {   // blocks may be narrower than MT*64
-        const int mt = idx >> 6, l = idx & 63;
-        v4f s = red[mt * 64 + l];
-        for (int w = 1; w < W; ++w) {
-            const v4f p = red[(w * MT + mt) * 64 + l];
-            s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
-        }
-        // C layout of 16x16 MFMA: lane l holds rows 4*(l/16)+v (= n) of column l%16 (= m).
-        const int m = mt * 16 + (l & 15);
-        if (m < M) {
-            const int64_t n = n0 + 4 * (l >> 4);
-            int i = 0;
-            while (i + 1 < sh.num && n0 >= sh.start[i + 1]) ++i;
-            const float4 sw = *reinterpret_cast<const float4*>(s_w + n);
-            const uint32_t o0 = f32_to_bf16_rne((s.x * s_act) * sw.x) | (f32_to_bf16_rne((s.y * s_act) * sw.y) << 16);
-            const uint32_t o1 = f32_to_bf16_rne((s.z * s_act) * sw.z) | (f32_to_bf16_rne((s.w * s_act) * sw.w) << 16);
-            *reinterpret_cast<uint2*>(sh.out[i] + (int64_t)m * sh.ldo[i] + (n - sh.start[i])) = make_uint2(o0, o1);
-        }
-    }
+    reduce_store<MT, kNT>(red, W, n0, s_act, s_w, sh, M, N);
 }
 
-}  // namespace
+
+// All-in-flight variant for M <= 16 and K % 1024 == 0 when x_q fits in LDS:
+// every wave issues the loads of ALL its weight chunks at once (CPW x 2 x 16 B
+// per lane, into registers); the workgroup then copies x_q[0:M, :] into LDS
+// with direct global->LDS loads (no registers; rows padded to K + 16 bytes so
+// the 16 fragment rows of an MFMA fall in distinct banks), waits once, and the
+// MFMAs read their B fragments from LDS.  With every workgroup resident, the
+// whole weight is requested up front, which is what a 50-200 MB stream needs
+// to reach the HBM rate.  Same chunk assignment and reduction order as
+// k_gemm_small_m, so both kernels give identical bits.
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int CPW, int NTX>
+__global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_xlds(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act,
+    const float* __restrict__ s_w, ShardTable sh, int M, int64_t N, int64_t K, int nchunks)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * NTX);
+    const int64_t ldsx = K + 16;
+    uint8_t* xs = smem;
+    v4f* red = reinterpret_cast<v4f*>(smem + ((M * ldsx + 15) & ~(int64_t)15));
+
+    // every weight chunk of this wave (for each of its NTX row tiles), all in flight
+    const uint8_t* wrow[NTX];
+    bool wok[NTX];
+#pragma unroll
+    for (int t = 0; t < NTX; ++t) {
+        wok[t] = n0 + 16 * t < N;                          // a ragged last workgroup holds fewer tiles
+        wrow[t] = wq + (wok[t] ? n0 + 16 * t + r : r) * K;
+    }
+    uint4 a[CPW][NTX][2];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int64_t c = (int64_t)wave + (int64_t)i * W;
+        const int64_t k0 = c * kChunk + g * 16;
+        const bool cv = c < nchunks;
+#pragma unroll
+        for (int t = 0; t < NTX; ++t) {
+            a[i][t][0] = ld16_stream_masked(wrow[t] + k0, wrow[t], wok[t] && cv && k0 < K);
+            a[i][t][1] = ld16_stream_masked(wrow[t] + k0 + 64, wrow[t], wok[t] && cv && k0 + 64 < K);
+        }
+    }
+    // x_q -> LDS: each wave moves 64 consecutive 16-byte pieces (1 KB, inside
+    // one row because K/16 is a multiple of 64) per instruction.
+    const int64_t kp = K >> 4, np = (int64_t)M * kp;
+    for (int64_t p0 = (int64_t)wave * 64; p0 < np; p0 += blockDim.x) {
+        const int64_t row = p0 / kp, col0 = p0 - row * kp;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(xq + (p0 + lane) * 16),
+                                         (lds_void*)(xs + row * ldsx + col0 * 16), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);                      // all loads, weight and x_q, have landed
+    __syncthreads();
+
+    v4f acc[NTX];
+#pragma unroll
+    for (int t = 0; t < NTX; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    const bool xr = r < M;
+    const uint8_t* xrow = xs + (xr ? r : 0) * ldsx;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int64_t c = (int64_t)wave + (int64_t)i * W;
+        if (c >= nchunks) break;                          // wave-uniform
+        const int64_t k0 = c * kChunk + g * 16;
+        const v8i B = pack(ld16_masked(xrow + k0, xrow, xr && k0 < K), ld16_masked(xrow + k0 + 64, xrow, xr && k0 + 64 < K));
+#pragma unroll
+        for (int t = 0; t < NTX; ++t)
+            acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pack(a[i][t][0], a[i][t][1]), B, acc[t],
+                                                                     0, 0, 0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NTX; ++t) red[(wave * NTX + t) * 64 + lane] = acc[t];
+    __syncthreads();
+    reduce_store<1, NTX>(red, W, n0, s_act, s_w, sh, M, N);
+}
 
 // Waves per workgroup: a function of K only (it fixes the summation order).
 int small_m_waves(int64_t K)
 {
     const int64_t nchunks = (K + kChunk - 1) / kChunk;
-    int64_t w = (nchunks + 7) / 8;
+    int64_t w = (nchunks + FP8MM_SMALLM_CPW - 1) / FP8MM_SMALLM_CPW;
     if (w < 1) w = 1;
     if (w > kMaxWaves) w = kMaxWaves;
     return (int)w;
+}
+
+}  // namespace
+
+// The reduction buffer can exceed the default 64 KB dynamic-LDS limit (W = 16
+// waves x 4 M tiles x NT tiles); allow up to the 160 KB a gfx950 CU has.
+template <int MT>
+void allow_large_lds()
+{
+    static const bool done = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m<MT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        return true;
+    }();
+    (void)done;
+}
+
+// LDS bytes of the all-in-flight variant, or 0 if it does not apply.
+size_t xlds_bytes(int64_t M, int64_t K, int W)
+{
+    if (M > 16 || K % 1024 != 0 || K > (int64_t)kChunk * kXldsMaxCpw * W) return 0;
+    const size_t b = (size_t)((M * (K + 16) + 15) & ~(int64_t)15) + (size_t)W * kXldsNT * 64 * sizeof(v4f);
+    return b <= (size_t)FP8MM_SMALLM_XLDS_MAX ? b : 0;
+}
+
+template <int CPW>
+void launch_xlds(const dim3& grid, const dim3& block, size_t lds, hipStream_t stream, const uint8_t* xq,
+                 const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh, int M, int64_t N,
+                 int64_t K, int nchunks)
+{
+    static const bool attr = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_xlds<CPW, kXldsNT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        return true;
+    }();
+    (void)attr;
+    hipLaunchKernelGGL((k_gemm_small_m_xlds<CPW, kXldsNT>), grid, block, lds, stream, xq, wq, s_act, s_w, sh,
+                       M, N, K, nchunks);
 }
 
 void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
@@ -144,15 +371,35 @@ void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, cons
 {
     const int W = small_m_waves(K);
     const int nchunks = (int)((K + kChunk - 1) / kChunk);
-    const dim3 grid((uint32_t)(N / 16)), block(64 * W);
+    const size_t xl = xlds_bytes(M, K, W);
+    if (xl) {
+        const int cpw = (nchunks + W - 1) / W;
+        const dim3 grid((uint32_t)((N + 16 * kXldsNT - 1) / (16 * kXldsNT))), block(64 * W);
+        switch (cpw) {
+        case 1: launch_xlds<1>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
+        case 2: launch_xlds<2>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
+        case 3: launch_xlds<3>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
+        case 4: launch_xlds<4>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
+        case 5: launch_xlds<5>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
+        case 6: launch_xlds<6>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
+        case 7: launch_xlds<7>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
+        default: launch_xlds<8>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
+        }
+    }
     const int MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    const size_t lds = (size_t)W * MT * 64 * sizeof(v4f);
+    const size_t lds = (size_t)W * kNT * MT * 64 * sizeof(v4f);
+    const dim3 grid((uint32_t)((N + 16 * kNT - 1) / (16 * kNT))), block(64 * W);
+    if (lds > 64 * 1024) {
+        if (MT == 1) allow_large_lds<1>();
+        else if (MT == 2) allow_large_lds<2>();
+        else allow_large_lds<4>();
+    }
     if (MT == 1)
-        hipLaunchKernelGGL(k_gemm_small_m<1>, grid, block, lds, stream, xq, wq, s_act, s_w, shards, (int)M, K, nchunks);
+        hipLaunchKernelGGL(k_gemm_small_m<1>, grid, block, lds, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks);
     else if (MT == 2)
-        hipLaunchKernelGGL(k_gemm_small_m<2>, grid, block, lds, stream, xq, wq, s_act, s_w, shards, (int)M, K, nchunks);
+        hipLaunchKernelGGL(k_gemm_small_m<2>, grid, block, lds, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks);
     else
-        hipLaunchKernelGGL(k_gemm_small_m<4>, grid, block, lds, stream, xq, wq, s_act, s_w, shards, (int)M, K, nchunks);
+        hipLaunchKernelGGL(k_gemm_small_m<4>, grid, block, lds, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks);
 }
 
 }  // namespace fp8mm
