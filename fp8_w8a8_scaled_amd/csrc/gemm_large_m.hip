@@ -126,11 +126,329 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Tiled kernel for K % 64 == 0 (every prefill shape of the layer).
+//
+// 256x256 output tile per 256-thread workgroup; wave (wn, wm) owns 128 rows of
+// W (n) x 128 rows of x_q (m) as 4x4 v_mfma_f32_32x32x64_f8f6f4 tiles with W
+// as the A operand (accumulators live in AGPRs).  K advances 64 bytes (one
+// MFMA depth) per stage through NSTAGE LDS stages filled by direct
+// global->LDS loads (global_load_lds_dwordx4: no staging registers, no LDS
+// store instructions), issued NSTAGE-1 stages ahead.  Fragment registers are
+// double-buffered: the 16 ds_read_b128 of stage k+1 are interleaved one-to-one
+// with the 16 MFMAs of stage k, so neither the LDS latency nor the barrier
+// leaves the matrix pipe idle.  LDS rows are 64 bytes with their four 16-byte
+// pieces XOR-swizzled by row (skipping one row bit: gfx950 LDS serves 16
+// lanes x 16 B per cycle) so fragment reads are bank-conflict free.
+// Workgroups are renumbered so that each XCD (blocks are dealt to the 8 XCDs
+// round-robin) walks a contiguous range of tiles, in groups of GM row-tiles
+// that share W column tiles through L2.  The epilogue scales in fp32, stages
+// the bf16 tile in LDS and writes it with row-contiguous 16-byte stores.
+// Rows past M or N load a clamped (real) row and are never stored.
+// ---------------------------------------------------------------------------
+#ifndef FP8MM_LARGEM_TK
+#define FP8MM_LARGEM_TK 128
+#endif
+#ifndef FP8MM_LARGEM_NSTAGE
+#define FP8MM_LARGEM_NSTAGE 2
+#endif
+#ifndef FP8MM_LARGEM_SWZ
+#define FP8MM_LARGEM_SWZ 1          // row bits skipped by the XOR swizzle
+#endif
+#ifndef FP8MM_LARGEM_GM
+#define FP8MM_LARGEM_GM 8
+#endif
+#ifndef FP8MM_LARGEM_INTERLEAVE
+#define FP8MM_LARGEM_INTERLEAVE 1
+#endif
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int T2 = 256;                      // tile rows of W and of x_q
+constexpr int TK = FP8MM_LARGEM_TK;          // K bytes per stage (S MFMA depths)
+constexpr int S_SUB = TK / 64;               // MFMA sub-steps per stage
+constexpr int NSTAGE = FP8MM_LARGEM_NSTAGE;
+constexpr int PPR = TK / 16;                 // 16-byte pieces per LDS row
+constexpr int STAGE_BYTES = 2 * T2 * TK;     // W tile + x_q tile
+constexpr int ROWS_PER_INST = 64 / PPR;      // rows one direct-to-LDS instruction fills
+constexpr int LOADS_PER_STAGE = 2 * (T2 / ROWS_PER_INST) / 4;   // per wave
+constexpr int C_ROW = T2 * 2 + 16;           // padded bf16 C-tile row, bytes
+constexpr int C_BYTES = T2 * C_ROW;
+constexpr int LM_LDS = (NSTAGE * STAGE_BYTES > C_BYTES) ? NSTAGE * STAGE_BYTES : C_BYTES;
+
+__device__ __forceinline__ int swz(int row, int piece)
+{
+    return piece ^ ((row >> FP8MM_LARGEM_SWZ) & (PPR - 1));
+}
+
+__device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// s_waitcnt with only vmcnt constrained (expcnt = 7, lgkmcnt = 15: no wait).
+// The count must be a compile-time constant.
+#define FP8MM_VMCNT_IMM(n) ((((n) & 15) | ((((n) >> 4) & 3) << 14)) | (7 << 4) | (15 << 8))
+#define vmcnt_wait(n) __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_IMM(n))
+// same, and lgkmcnt(0): every LDS read of this wave has returned
+#define FP8MM_VMCNT_LGKM0_IMM(n) ((((n) & 15) | ((((n) >> 4) & 3) << 14)) | (7 << 4))
+
+// Per-lane byte offsets (row * K + piece * 16, 32-bit) of the rows this lane
+// moves for each of its NQ/4 direct-to-LDS instructions per operand; rows past
+// N or M are clamped to the last real row.  Fixed for a whole tile.
+constexpr int NQ = T2 / ROWS_PER_INST;               // instructions per operand tile
+struct RowOffsets {
+    uint32_t w[NQ / 4], x[NQ / 4];
+};
+
+__device__ __forceinline__ void row_offsets(RowOffsets& o, int64_t n0, int64_t m0, int64_t N, int64_t M,
+                                            int64_t K, int wave, int lane)
+{
+    const int lr = lane / PPR, lp = lane % PPR;       // row within instruction, physical piece
+#pragma unroll
+    for (int i = 0; i < NQ / 4; ++i) {
+        const int row = (wave + 4 * i) * ROWS_PER_INST + lr;
+        const int piece = swz(row, lp);               // logical piece stored at physical lp
+        const int64_t gn = n0 + row < N ? n0 + row : N - 1;
+        const int64_t gm = m0 + row < M ? m0 + row : M - 1;
+        o.w[i] = (uint32_t)(gn * K + piece * 16);
+        o.x[i] = (uint32_t)(gm * K + piece * 16);
+    }
+}
+
+// Issue one stage (K bytes [k0, k0+TK) of the W and x_q tiles).  Instruction
+// q = wave + 4i fills LDS rows q*ROWS_PER_INST.. of one operand.
+__device__ __forceinline__ void load_stage(uint8_t* st, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ xq,
+                                           const RowOffsets& o, int64_t k0, int wave)
+{
+    const uint8_t* wk = wq + k0;
+    const uint8_t* xk = xq + k0;
+#pragma unroll
+    for (int i = 0; i < NQ / 4; ++i) {
+        const int q = wave + 4 * i;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wk + o.w[i]), (lds_void_t*)(st + q * 1024),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(xk + o.x[i]),
+                                         (lds_void_t*)(st + T2 * TK + q * 1024), 16, 0, 0);
+    }
+}
+
+struct Frags {
+    v8i a[4], b[4];
+};
+
+__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* __restrict__ st, int sub, int lane, int wn,
+                                           int wm)
+{
+    const int fr = lane & 31, p0 = sub * 4 + (lane >> 5) * 2;
+    const uint8_t* sW = st;
+    const uint8_t* sX = st + T2 * TK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = wn * 128 + i * 32 + fr;
+        f.a[i] = pack(lds16(sW + row * TK + swz(row, p0) * 16), lds16(sW + row * TK + swz(row, p0 + 1) * 16));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = wm * 128 + j * 32 + fr;
+        f.b[j] = pack(lds16(sX + row * TK + swz(row, p0) * 16), lds16(sX + row * TK + swz(row, p0 + 1) * 16));
+    }
+}
+
+__device__ __forceinline__ void mfma_frags(const Frags& f, v16f (&acc)[4][4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+}
+
+// Stage boundary, before the first fragment read of stage kt+1: wait until
+// stage kt+1 has landed for this wave (only its NSTAGE-2 newer stages may stay
+// in flight) and until this wave's fragment reads of stage kt are done, then
+// a barrier extends both to the workgroup, so stage kt's buffer can be
+// refilled with stage kt+NSTAGE.  A bare barrier: __syncthreads() would also
+// drain the stages that are meant to stay in flight.
+__device__ __forceinline__ void stage_boundary(uint8_t* fill, const uint8_t* __restrict__ wq,
+                                               const uint8_t* __restrict__ xq, const RowOffsets& ro,
+                                               int64_t k_fill, int wave)
+{
+    __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_LGKM0_IMM((NSTAGE - 2) * LOADS_PER_STAGE));
+    __builtin_amdgcn_s_barrier();
+    load_stage(fill, wq, xq, ro, k_fill, wave);
+}
+
+// One MFMA sub-step: read the next sub-step's fragments into `fn` while the
+// 16 MFMAs of `fc` run, one fragment read per MFMA.  The two LDS pointers are
+// restrict-qualified: the fragment reads never touch the stage being filled,
+// which lets the compiler see they do not wait for those loads (the explicit
+// s_waitcnt and barrier order them after the loads of earlier stages).
+__device__ __forceinline__ void substep(const uint8_t* __restrict__ frag_src, int sub_next, int lane, int wn,
+                                        int wm, const Frags& fc, Frags& fn, v16f (&acc)[4][4])
+{
+    read_frags(fn, frag_src, sub_next, lane, wn, wm);
+    mfma_frags(fc, acc);
+#if FP8MM_LARGEM_INTERLEAVE
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#endif
+}
+
+__global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act,
+    const float* __restrict__ s_w, ShardTable sh, int64_t M, int64_t N, int64_t K)
+{
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+
+    // Persistent schedule.  Workgroups are dealt to the 8 XCDs round-robin, so
+    // the ones with bid % 8 == x share XCD x's L2: give that XCD a contiguous
+    // range of tiles and let its workgroups walk it in lockstep rounds (round
+    // r = tiles r*nbx .. r*nbx+nbx-1 of the range).  Tiles are numbered in
+    // groups of GM row-tiles per W column-tile, so one round covers a few
+    // x_q row-tiles and W column-tiles whose K slices the concurrent
+    // workgroups fetch at about the same time -- they meet in L2.
+    const int nb = gridDim.x, bid = blockIdx.x;
+    const int num_m = (int)((M + T2 - 1) / T2), num_n = (int)((N + T2 - 1) / T2);
+    const int ntiles = num_m * num_n;
+    const int xcd = bid & 7;
+    const int nbx = (nb >> 3) + (xcd < (nb & 7) ? 1 : 0);
+    const int tiles_x = (ntiles >> 3) + (xcd < (ntiles & 7) ? 1 : 0);
+    const int start_x = xcd * (ntiles >> 3) + (xcd < (ntiles & 7) ? xcd : (ntiles & 7));
+    const int GM = FP8MM_LARGEM_GM;
+    const int in_group = GM * num_n;
+    for (int u = bid >> 3; u < tiles_x; u += nbx) {
+    const int t = start_x + u;
+    const int first_m = (t / in_group) * GM;
+    const int gsz = (num_m - first_m) < GM ? (num_m - first_m) : GM;
+    const int tm = first_m + (t % in_group) % gsz;
+    const int tn = (t % in_group) / gsz;
+    const int64_t m0 = (int64_t)tm * T2, n0 = (int64_t)tn * T2;
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const int nk = (int)(K / TK);
+    const int64_t k_last = (int64_t)(nk - 1) * TK;
+    auto kof = [&](int st) { const int64_t k = (int64_t)st * TK; return k < k_last ? k : k_last; };
+    RowOffsets ro;
+    row_offsets(ro, n0, m0, N, M, K, wave, lane);
+#pragma unroll
+    for (int s = 0; s < NSTAGE; ++s)
+        load_stage(smem + s * STAGE_BYTES, wq, xq, ro, kof(s), wave);
+    vmcnt_wait((NSTAGE - 1) * LOADS_PER_STAGE);        // stage 0 landed for this wave
+    __builtin_amdgcn_s_barrier();
+
+    // Sub-steps run in order (stage kt, sub-step s); fragments alternate
+    // between fa and fb, so the loop is unrolled over two sub-steps.
+    Frags fa, fb;
+    read_frags(fa, smem, 0, lane, wn, wm);
+    const int nsub = nk * S_SUB;
+    auto one = [&](int g, const Frags& fc, Frags& fn) {
+        const int kt = g / S_SUB, sub = g % S_SUB;
+        if (sub == S_SUB - 1) {                        // next fragments come from stage kt+1
+            stage_boundary(smem + (kt % NSTAGE) * STAGE_BYTES, wq, xq, ro, kof(kt + NSTAGE), wave);
+            substep(smem + ((kt + 1) % NSTAGE) * STAGE_BYTES, 0, lane, wn, wm, fc, fn, acc);
+        } else {
+            substep(smem + (kt % NSTAGE) * STAGE_BYTES, sub + 1, lane, wn, wm, fc, fn, acc);
+        }
+    };
+    int g = 0;
+    for (; g + 2 <= nsub; g += 2) {
+        one(g, fa, fb);
+        one(g + 1, fb, fa);
+    }
+    if (g < nsub) one(g, fa, fb);                      // odd number of sub-steps
+
+    // Epilogue: scale, round to bf16, stage the 256x256 tile in LDS (rows of
+    // m, padded), then store rows with 16-byte, row-contiguous writes.
+    __builtin_amdgcn_s_waitcnt(0);                     // retire the trailing (unused) stage loads
+    __syncthreads();                                   // every stage read by every wave
+    const int fr = lane & 31, fh = lane >> 5;
+    // 32x32 C layout with W as A: lane l holds column l%32 (= m) and rows
+    // 8*(v/4) + 4*(l/32) + v%4 (= n): four consecutive n per v/4.
+    float4 swv[4][4];                                  // all weight scales first, one wait
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wn * 128 + i * 32 + 8 * q + 4 * fh;
+            swv[i][q] = *reinterpret_cast<const float4*>(s_w + (n < N ? n : 0));
+        }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int nl = wn * 128 + i * 32 + 8 * q + 4 * fh;
+            const float4 sw = swv[i][q];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int ml = wm * 128 + j * 32 + fr;
+                const v16f& c = acc[i][j];
+                const uint32_t lo = f32_to_bf16_rne((c[4 * q + 0] * s_act) * sw.x) |
+                                    (f32_to_bf16_rne((c[4 * q + 1] * s_act) * sw.y) << 16);
+                const uint32_t hi = f32_to_bf16_rne((c[4 * q + 2] * s_act) * sw.z) |
+                                    (f32_to_bf16_rne((c[4 * q + 3] * s_act) * sw.w) << 16);
+                *reinterpret_cast<uint2*>(smem + ml * C_ROW + nl * 2) = make_uint2(lo, hi);
+            }
+        }
+    __syncthreads();
+    constexpr int CHUNKS = T2 * T2 * 2 / 16;           // 16-byte pieces of the tile
+#pragma unroll 4
+    for (int c = threadIdx.x; c < CHUNKS; c += 256) {
+        const int ml = c >> 5, nl = (c & 31) * 8;
+        const int64_t m = m0 + ml, n = n0 + nl;
+        if (m >= M || n >= N) continue;
+        int si = 0;
+        while (si + 1 < sh.num && n >= sh.start[si + 1]) ++si;
+        *reinterpret_cast<uint4*>(sh.out[si] + m * sh.ldo[si] + (n - sh.start[si])) =
+            *reinterpret_cast<const uint4*>(smem + ml * C_ROW + nl * 2);
+    }
+    __syncthreads();                                   // the next tile reuses the LDS
+    }
+}
+
 }  // namespace
+
+// Compute units of the current device (cached per device ordinal).
+int num_cus()
+{
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
 
 void launch_gemm_large_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
                          const ShardTable& shards, int64_t M, int64_t N, int64_t K, hipStream_t stream)
 {
+    // the tiled kernel addresses operands with 32-bit row offsets
+    if (K % TK == 0 && N * K < ((int64_t)1 << 32) && M * K < ((int64_t)1 << 32)) {
+        static const bool attr = [] {
+            (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_large_m_tiled),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            return true;
+        }();
+        (void)attr;
+        const int64_t tiles = ((M + T2 - 1) / T2) * ((N + T2 - 1) / T2);
+        const int64_t grid = tiles < num_cus() ? tiles : num_cus();   // one resident workgroup per CU
+        hipLaunchKernelGGL(k_gemm_large_m_tiled, dim3((uint32_t)grid), dim3(256), (size_t)LM_LDS,
+                           stream, xq, wq, s_act, s_w, shards, M, N, K);
+        return;
+    }
     const dim3 grid((uint32_t)((N + BN - 1) / BN), (uint32_t)((M + BM - 1) / BM));
     hipLaunchKernelGGL(k_gemm_large_m, grid, dim3(kThreads), 0, stream, xq, wq, s_act, s_w, shards, M, N, K);
 }
