@@ -2,27 +2,42 @@
 
     python bench.py [--steps K] [--warmup W] [--M 8] [--no-prefill] [--no-cpu-baseline]
 
-Prints ONE JSON line.  The headline (`value`) is the decode projection: a step
-is one pass of the layer's decode path over one batch -- static quant of the
-bf16 activation [M, 5120] to E4M3, then the scaled GEMM against a 10240 x 5120
-E4M3 weight with per-channel scales, bf16 output, the kernel picked by the
-M-threshold dispatcher (the small-M arm at M <= 8).  `value` is algorithmic HBM
-bytes per step / step time, in GB/s (inputs resident in HBM; weight copies are
-rotated so that no step finds its weight in the 256 MB last-level cache).
+Prints ONE JSON line.  The headline (`value`) is the decode projection (M = 8,
+K = 5120, N = 10240): a step is one pass of the layer's decode path over one
+batch -- static quant of the bf16 activation [M, 5120] to E4M3, then the scaled
+GEMM against a 10240 x 5120 E4M3 weight with per-channel scales and a bf16
+output, the kernel picked by the M-threshold dispatcher (the small-M arm).
+`value` is algorithmic bytes per step / step time in GB/s, with inputs resident
+in HBM; weight copies are rotated so that no step finds its weight in the
+256 MB Infinity Cache.  Steps are captured into a HIP graph and replayed (the
+decode steps of a served model are graph replays), timed with HIP events on
+the replay stream.
 
-`prefill` reports the prefill chunk (M = 6576: fused RMSNorm->quant, merged
-gate_up 34816 x 5120, plain quant of the down input, down 5120 x 17408, large-M
-arm) in TFLOP/s.  `roofline` objects use each path's dominant kernel timed with
-HIP events around every launch in the timed region.  `cpu_baseline` is the CPU
-oracle timed on a bounded sample of the same workload.
+`roofline` is for the dominant kernel (the small-M GEMM): algorithmic bytes per
+launch over its average launch duration, timed live in a graph of back-to-back
+GEMM launches on the same stream.  `traffic` comes from a rocprofv3 FETCH_SIZE /
+WRITE_SIZE summary committed under profiles/ (null if absent or if the kernel
+sources changed since it was taken).  `prefill` reports the prefill chunk
+(M = 6576: fused RMSNorm->quant, merged gate_up 34816 x 5120, plain quant of the
+down input, down 5120 x 17408 -- the large-M arm) in TFLOP/s, with its own
+roofline for the gate_up GEMM.  `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the decode workload.
 
 Inputs are seeded synthetic tensors from workloads/ (no datasets, no weights).
+
+Other modes (no GPU work):
+    python bench.py --summarize-trace DIR  --name NAME --cmd "..."   # kernel-trace stats -> profiles/NAME.md
+    python bench.py --summarize-pmc DIR --name NAME --cmd "..."      # FETCH/WRITE_SIZE -> profiles/NAME.md
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -33,19 +48,36 @@ METRIC = "FP8 scaled-MM: HBM GB/s at M≤8 (decode), FP8 TFLOPS at prefill M, % 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published (no sparsity)
 LLC_BYTES = 256 * 2 ** 20      # Infinity Cache to defeat
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "fp8_w8a8_scaled_amd", "csrc")
 
 
 def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=240)
+    p.add_argument("--warmup", type=int, default=20, help="untimed eager steps before the timed graph")
     p.add_argument("--M", type=int, default=8)
-    p.add_argument("--prefill-steps", type=int, default=20)
+    p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--summarize-trace", metavar="DIR")
+    p.add_argument("--summarize-pmc", metavar="DIR")
+    p.add_argument("--pmc-driver", choices=["decode", "prefill"],
+                   help="run a known-size copy, then a few launches of one GEMM (for rocprofv3 --pmc)")
+    p.add_argument("--meta-out", metavar="DIR")
+    p.add_argument("--name")
+    p.add_argument("--cmd", default="")
     return p.parse_args()
+
+
+def kernel_sources_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
 
 
 def bf16_dev(a_u16):
@@ -60,20 +92,50 @@ def f32_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
-class Timer:
-    """HIP events around individual launches on the current stream."""
+def graph_time_ms(fn, n, warmup):
+    """Run `warmup` untimed eager calls of fn(i), capture n calls into one HIP
+    graph, replay it once untimed, then time exactly one replay (n calls) with
+    HIP events on the capture stream, bracketed by device synchronizations.
+    Returns ms per call."""
+    import torch
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for i in range(max(1, warmup)):
+            fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
 
-    def __init__(self, n):
-        import torch
-        self.s = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        self.e = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
-    def mean_ms(self, n):
-        return sum(self.s[i].elapsed_time(self.e[i]) for i in range(n)) / n
+def load_traffic(name: str):
+    """Bytes per launch from a committed FETCH_SIZE/WRITE_SIZE summary, or None
+    if it is missing or was taken from other kernel sources."""
+    path = os.path.join(PROFILES, f"{name}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_h = re.search(r"kernel_sources_sha256_16:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_h or not m_b or m_h.group(1) != kernel_sources_hash():
+        return None
+    return float(m_b.group(1))
 
 
 def bench_decode(fp8, M, steps, warmup):
-    import numpy as np
     import torch
     import workloads as wl
 
@@ -93,36 +155,27 @@ def bench_decode(fp8, M, steps, warmup):
     quant_bytes = 2 * M * K + M * K
     assert fp8.select(M, N, K) == 0
 
-    def step(i, timer=None):
+    def step(i):
         fp8.quant(xd, s_act, out=xq)
-        if timer is not None:
-            timer.s[i].record()
         fp8.scaled_mm(xq, ws[i % copies], s_act, sw, out=out)
-        if timer is not None:
-            timer.e[i].record()
 
-    for i in range(warmup):
-        step(i)
-    timer = Timer(steps)
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(steps):
-        step(i, timer)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    gemm_ms = timer.mean_ms(steps)
+    def gemm(i):
+        fp8.scaled_mm(xq, ws[i % copies], s_act, sw, out=out)
+
+    ms = graph_time_ms(step, steps, warmup)
+    gemm_ms = graph_time_ms(gemm, steps, warmup)
     step_bytes = gemm_bytes + quant_bytes
     achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+    traffic = load_traffic("decode_gemm_M8_K5120_N10240_pmc")
     return {
         "ms_per_step": ms,
         "value": step_bytes / (ms * 1e-3) / 1e9,
         "config": {"workload": f"decode_proj_M{M}_K{K}_N{N}", "M": M, "K": K, "N": N,
-                   "weight_copies_rotated": copies, "step": "static quant [M,K] + scaled GEMM (small-M arm)",
+                   "weight_copies_rotated": copies,
+                   "step": "static quant [M,K] + scaled GEMM via dispatcher (small-M arm), graph-replayed",
                    "algorithmic_bytes_per_step": step_bytes},
-        "roofline": {"bound": "hbm", "kernel": "k_gemm_small_m", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+        "roofline": {"bound": "hbm", "kernel": "k_gemm_small_m_xlds", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_us": gemm_ms * 1e3},
     }
 
@@ -149,40 +202,25 @@ def bench_prefill(fp8, steps, warmup):
     assert fp8.select(M, N1, K1) == 1
     flops1, flops2 = 2 * M * N1 * K1, 2 * M * N2 * K2
 
-    def step(i, t_gu=None, t_dn=None):
+    def step(i):
         fp8.quant_rmsnorm(xd, gd, s1, wl.EPS, out=xq1)
-        if t_gu is not None:
-            t_gu.s[i].record()
         fp8.scaled_mm_merged(xq1, wq1, s1, sw1, [N1 // 2, N1 // 2], outs=[gate, up])
-        if t_gu is not None:
-            t_gu.e[i].record()
         fp8.quant(xdd, s2, out=xq2)
-        if t_dn is not None:
-            t_dn.s[i].record()
         fp8.scaled_mm(xq2, wq2, s2, sw2, out=down)
-        if t_dn is not None:
-            t_dn.e[i].record()
 
-    for i in range(warmup):
-        step(i)
-    t_gu, t_dn = Timer(steps), Timer(steps)
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(steps):
-        step(i, t_gu, t_dn)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    gu_ms, dn_ms = t_gu.mean_ms(steps), t_dn.mean_ms(steps)
+    ms = graph_time_ms(step, steps, warmup)
+    gu_ms = graph_time_ms(lambda i: fp8.scaled_mm_merged(xq1, wq1, s1, sw1, [N1 // 2, N1 // 2], outs=[gate, up]),
+                          steps, warmup)
+    dn_ms = graph_time_ms(lambda i: fp8.scaled_mm(xq2, wq2, s2, sw2, out=down), steps, warmup)
     ach = flops1 / (gu_ms * 1e-3) / 1e12
     return {
         "workload": f"prefill_M{M}_gateup_K{K1}_N{N1}_down_K{K2}_N{N2}",
         "value": (flops1 + flops2) / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_step": ms,
-        "step": "fused RMSNorm quant + merged gate_up GEMM + static quant + down GEMM (large-M arm)",
+        "step": "fused RMSNorm quant + merged gate_up GEMM + static quant + down GEMM (large-M arm), graph-replayed",
         "gemm_tflops": {"gate_up": ach, "down": flops2 / (dn_ms * 1e-3) / 1e12},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm_large_m (gate_up)", "achieved": ach,
-                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / FP8_PEAK_TFLOPS, "traffic": None,
+        "roofline": {"bound": "mfma", "kernel": "k_gemm_large_m_tiled (gate_up)", "achieved": ach,
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / FP8_PEAK_TFLOPS,
+                     "traffic": load_traffic("prefill_gateup_M6576_K5120_N34816_pmc"),
                      "algorithmic_flops_per_launch": flops1, "avg_launch_us": gu_ms * 1e3},
     }
 
@@ -191,7 +229,6 @@ def cpu_baseline(M, seconds):
     """The CPU oracle (as it stands) on a bounded sample of the decode step:
     static quant of [M, 5120] + exact GEMM against the full 10240 x 5120 weight,
     repeated for about `seconds`; reported in the metric's unit (GB/s)."""
-    import numpy as np
     import oracle
     import workloads as wl
     K, N = 5120, 10240
@@ -212,8 +249,118 @@ def cpu_baseline(M, seconds):
             "sample": f"{reps} full decode steps (quant [{M},{K}] + GEMM vs the whole {N}x{K} weight) in {el:.1f} s"}
 
 
+# ------------------------------------------------------- profile summaries --
+
+def _short(name: str) -> str:
+    name = name.replace("fp8mm::(anonymous namespace)::", "").replace("void ", "")
+    return re.sub(r"\(.*", "", name)
+
+
+def summarize_trace(d, name, cmd):
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    assert files, f"no *kernel_stats.csv under {d}"
+    rows = list(csv.DictReader(open(files[0])))
+    lines = [f"# {name}", "", "rocprofv3 kernel trace, `--stats` summary (times in microseconds).", "",
+             f"Command: `{cmd}`", "", f"kernel_sources_sha256_16: {kernel_sources_hash()}", "",
+             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    out = os.path.join(PROFILES, f"{name}.md")
+    os.makedirs(PROFILES, exist_ok=True)
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
+def summarize_pmc(d, name, cmd):
+    """FETCH_SIZE / WRITE_SIZE per dispatch of the target kernel, scaled by the
+    same counters on the plain copy the driver runs first (an elementwise
+    read-N-bytes / write-N-bytes kernel of known size)."""
+    per = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            per.setdefault((r["Counter_Name"], r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    meta = json.load(open(os.path.join(d, "pmc_meta.json")))
+    copy_k = meta["copy_kernel"]
+    target = meta["kernel"]
+    res = {}
+    for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+        tv = [v for (cn, kn), vals in per.items() if cn == cname and target in kn for v in vals]
+        cv = [v for (cn, kn), vals in per.items() if cn == cname and copy_k in kn for v in vals]
+        if not tv or not cv:
+            raise SystemExit(f"missing {cname} samples for {target} or {copy_k}: {sorted(set(per))}")
+        kib = sum(tv) / len(tv)
+        copy_kib = max(cv)
+        factor = meta["copy_bytes"] / (copy_kib * 1024.0)
+        res[cname] = (kib, copy_kib, factor, kib * 1024.0 * factor, len(tv))
+    traffic = res["FETCH_SIZE"][3] + res["WRITE_SIZE"][3]
+    lines = [f"# {name}", "", "rocprofv3 `--pmc` (one counter per run): HBM traffic of one launch of "
+             f"`{target}`, calibrated on a plain copy of {meta['copy_bytes']} bytes "
+             f"(`{copy_k}`, read {meta['copy_bytes']} and written {meta['copy_bytes']}).", "",
+             f"Commands: `{cmd}`", "", f"kernel_sources_sha256_16: {kernel_sources_hash()}", "",
+             "| counter | KiB per launch | copy KiB | scale = copy bytes / copy KiB·1024 | bytes per launch |",
+             "|---|---|---|---|---|"]
+    for cname, (kib, ck, fac, b, n) in res.items():
+        lines.append(f"| {cname} | {kib:.1f} (mean of {n}) | {ck:.1f} | {fac:.4f} | {b:.0f} |")
+    lines += ["", f"algorithmic_bytes_per_launch: {meta['algorithmic_bytes']}",
+              f"traffic_bytes_per_launch: {traffic:.0f}",
+              f"traffic / algorithmic: {traffic / meta['algorithmic_bytes']:.3f}"]
+    out = os.path.join(PROFILES, f"{name}.md")
+    os.makedirs(PROFILES, exist_ok=True)
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
+def pmc_driver(fp8, which, meta_dir):
+    """Launches profiled by the FETCH_SIZE / WRITE_SIZE passes: first one
+    elementwise kernel that reads 256 MiB and writes 256 MiB (the calibration
+    copy: torch.neg on float32), then 3 launches of the decode GEMM (on 3
+    different weight copies, so each launch finds its weight cache-cold) or of
+    the prefill gate_up GEMM, on the bench's inputs."""
+    import torch
+    import workloads as wl
+    nbytes = 256 * 2 ** 20
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.neg(src)
+    torch.cuda.synchronize()
+    del dst
+    if which == "decode":
+        M, K, N = 8, 5120, 10240
+        xd = bf16_dev(wl.activation_bf16(wl.DECODE_PROJ.wid, M, K, outliers=True))
+        s_act = float(fp8.act_scale(xd).item())
+        wq, sw = fp8.quant_weight(f32_dev(wl.weight_f32(wl.DECODE_PROJ.wid, N, K)))
+        copies = [wq] + [wq.clone() for _ in range(11)]
+        xq = fp8.quant(xd, s_act)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        for i in range(3):
+            fp8.scaled_mm(xq, copies[4 * i + 1], s_act, sw, out=out)
+        kernel = "k_gemm_small_m_xlds"
+    else:
+        M, K, N = 6576, 5120, 34816
+        xd = bf16_dev(wl.activation_bf16(wl.PREFILL.wid, M, K, outliers=False))
+        gd = bf16_dev(wl.gamma_bf16(wl.PREFILL.wid, K))
+        s1 = float(fp8.act_scale(xd, gd, wl.EPS).item())
+        wq, sw = fp8.quant_weight(f32_dev(wl.weight_f32(wl.PREFILL.wid, N, K)))
+        xq = fp8.quant_rmsnorm(xd, gd, s1, wl.EPS)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            fp8.scaled_mm_merged(xq, wq, s1, sw, [N // 2, N // 2])
+        kernel = "k_gemm_large_m_tiled"
+    torch.cuda.synchronize()
+    alg = N * K + 4 * N + M * K + 2 * M * N
+    os.makedirs(meta_dir, exist_ok=True)
+    json.dump({"kernel": kernel, "copy_kernel": "elementwise_kernel", "copy_bytes": nbytes, "algorithmic_bytes": alg},
+              open(os.path.join(meta_dir, "pmc_meta.json"), "w"))
+    print("pmc driver done", which, flush=True)
+
+
 def main():
     a = _args()
+    if a.summarize_trace:
+        return summarize_trace(a.summarize_trace, a.name, a.cmd)
+    if a.summarize_pmc:
+        return summarize_pmc(a.summarize_pmc, a.name, a.cmd)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}); "
@@ -223,6 +370,8 @@ def main():
     import fp8_w8a8_scaled_amd as fp8
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     torch.cuda.set_device(0)
+    if a.pmc_driver:
+        return pmc_driver(fp8, a.pmc_driver, a.meta_out)
     res = bench_decode(fp8, a.M, a.steps, a.warmup)
     line = {
         "metric": METRIC, "value": res["value"], "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
@@ -231,10 +380,10 @@ def main():
         "config": res["config"], "roofline": res["roofline"],
     }
     if not a.no_prefill:
-        line["prefill"] = bench_prefill(fp8, a.prefill_steps, 3)
+        line["prefill"] = bench_prefill(fp8, a.prefill_steps, a.warmup)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a.M, a.cpu_seconds)
-    line["device"] = torch.cuda.get_device_name(0)
+    line["kernel_sources_sha256_16"] = kernel_sources_hash()
     print(json.dumps(line), flush=True)
 
 

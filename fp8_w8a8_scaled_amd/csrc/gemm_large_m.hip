@@ -162,6 +162,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
 #ifndef FP8MM_LARGEM_INTERLEAVE
 #define FP8MM_LARGEM_INTERLEAVE 1
 #endif
+// L2 prefetch distance in stages (0: off).  Each stage load is followed by two
+// 4-byte-per-lane direct-to-LDS loads that touch every 128-byte line of the
+// stage PF stages further on, so that its real loads hit L2.
+#ifndef FP8MM_LARGEM_PREFETCH
+#define FP8MM_LARGEM_PREFETCH 4
+#endif
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -175,7 +181,7 @@ constexpr int ROWS_PER_INST = 64 / PPR;      // rows one direct-to-LDS instructi
 constexpr int LOADS_PER_STAGE = 2 * (T2 / ROWS_PER_INST) / 4;   // per wave
 constexpr int C_ROW = T2 * 2 + 16;           // padded bf16 C-tile row, bytes
 constexpr int C_BYTES = T2 * C_ROW;
-constexpr int LM_LDS = (NSTAGE * STAGE_BYTES > C_BYTES) ? NSTAGE * STAGE_BYTES : C_BYTES;
+constexpr int LM_LDS = (NSTAGE * STAGE_BYTES + 2048 > C_BYTES) ? NSTAGE * STAGE_BYTES + 2048 : C_BYTES;
 
 __device__ __forceinline__ int swz(int row, int piece)
 {
@@ -197,7 +203,11 @@ __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_c
 constexpr int NQ = T2 / ROWS_PER_INST;               // instructions per operand tile
 struct RowOffsets {
     uint32_t w[NQ / 4], x[NQ / 4];
+    uint32_t pw, px;                                  // prefetch: row wave*64 + lane, piece 0
 };
+constexpr int PF_STAGES = FP8MM_LARGEM_PREFETCH;
+constexpr int PF_LOADS = PF_STAGES > 0 ? 2 : 0;      // prefetch loads per stage per wave
+constexpr int PF_JUNK = NSTAGE * STAGE_BYTES;        // LDS offset of the prefetch landing area
 
 __device__ __forceinline__ void row_offsets(RowOffsets& o, int64_t n0, int64_t m0, int64_t N, int64_t M,
                                             int64_t K, int wave, int lane)
@@ -211,6 +221,25 @@ __device__ __forceinline__ void row_offsets(RowOffsets& o, int64_t n0, int64_t m
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
         o.w[i] = (uint32_t)(gn * K + piece * 16);
         o.x[i] = (uint32_t)(gm * K + piece * 16);
+    }
+    const int prow = wave * 64 + lane;                // 4 waves x 64 lanes = the 256 tile rows
+    const int64_t pn = n0 + prow < N ? n0 + prow : N - 1;
+    const int64_t pm = m0 + prow < M ? m0 + prow : M - 1;
+    o.pw = (uint32_t)(pn * K);
+    o.px = (uint32_t)(pm * K);
+}
+
+// Touch every 128-byte line of the W and x_q tile rows at K offset k (4 bytes
+// per row, landing in a scratch LDS area nobody reads).
+__device__ __forceinline__ void prefetch_stage(uint8_t* junk, const uint8_t* __restrict__ wq,
+                                               const uint8_t* __restrict__ xq, const RowOffsets& o, int64_t k,
+                                               int wave)
+{
+    if (PF_STAGES > 0) {
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wq + k + o.pw), (lds_void_t*)(junk + wave * 512),
+                                         4, 0, 0);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(xq + k + o.px),
+                                         (lds_void_t*)(junk + wave * 512 + 256), 4, 0, 0);
     }
 }
 
@@ -268,13 +297,15 @@ __device__ __forceinline__ void mfma_frags(const Frags& f, v16f (&acc)[4][4])
 // a barrier extends both to the workgroup, so stage kt's buffer can be
 // refilled with stage kt+NSTAGE.  A bare barrier: __syncthreads() would also
 // drain the stages that are meant to stay in flight.
-__device__ __forceinline__ void stage_boundary(uint8_t* fill, const uint8_t* __restrict__ wq,
+__device__ __forceinline__ void stage_boundary(uint8_t* fill, uint8_t* junk, const uint8_t* __restrict__ wq,
                                                const uint8_t* __restrict__ xq, const RowOffsets& ro,
-                                               int64_t k_fill, int wave)
+                                               int64_t k_fill, int64_t k_pref, int wave)
 {
-    __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_LGKM0_IMM((NSTAGE - 2) * LOADS_PER_STAGE));
+    // issued after stage kt+1's loads: its prefetch, then NSTAGE-2 newer stages with theirs
+    __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_LGKM0_IMM(PF_LOADS + (NSTAGE - 2) * (LOADS_PER_STAGE + PF_LOADS)));
     __builtin_amdgcn_s_barrier();
     load_stage(fill, wq, xq, ro, k_fill, wave);
+    prefetch_stage(junk, wq, xq, ro, k_pref, wave);
 }
 
 // One MFMA sub-step: read the next sub-step's fragments into `fn` while the
@@ -342,9 +373,11 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     RowOffsets ro;
     row_offsets(ro, n0, m0, N, M, K, wave, lane);
 #pragma unroll
-    for (int s = 0; s < NSTAGE; ++s)
+    for (int s = 0; s < NSTAGE; ++s) {                 // every stage load is followed by its prefetch
         load_stage(smem + s * STAGE_BYTES, wq, xq, ro, kof(s), wave);
-    vmcnt_wait((NSTAGE - 1) * LOADS_PER_STAGE);        // stage 0 landed for this wave
+        prefetch_stage(smem + PF_JUNK, wq, xq, ro, kof(s + PF_STAGES), wave);
+    }
+    vmcnt_wait(PF_LOADS + (NSTAGE - 1) * (LOADS_PER_STAGE + PF_LOADS));   // stage 0 landed for this wave
     __builtin_amdgcn_s_barrier();
 
     // Sub-steps run in order (stage kt, sub-step s); fragments alternate
@@ -355,7 +388,8 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     auto one = [&](int g, const Frags& fc, Frags& fn) {
         const int kt = g / S_SUB, sub = g % S_SUB;
         if (sub == S_SUB - 1) {                        // next fragments come from stage kt+1
-            stage_boundary(smem + (kt % NSTAGE) * STAGE_BYTES, wq, xq, ro, kof(kt + NSTAGE), wave);
+            stage_boundary(smem + (kt % NSTAGE) * STAGE_BYTES, smem + PF_JUNK, wq, xq, ro, kof(kt + NSTAGE),
+                           kof(kt + NSTAGE + PF_STAGES), wave);
             substep(smem + ((kt + 1) % NSTAGE) * STAGE_BYTES, 0, lane, wn, wm, fc, fn, acc);
         } else {
             substep(smem + (kt % NSTAGE) * STAGE_BYTES, sub + 1, lane, wn, wm, fc, fn, acc);
