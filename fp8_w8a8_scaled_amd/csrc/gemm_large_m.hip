@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
 // 4-byte-per-lane direct-to-LDS loads that touch every 128-byte line of the
 // stage PF stages further on, so that its real loads hit L2.
 #ifndef FP8MM_LARGEM_PREFETCH
-#define FP8MM_LARGEM_PREFETCH 4
+#define FP8MM_LARGEM_PREFETCH 0
 #endif
 
 typedef __attribute__((address_space(3))) void lds_void_t;

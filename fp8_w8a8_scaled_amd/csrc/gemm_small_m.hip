@@ -59,6 +59,21 @@
 #define FP8MM_SMALLM_XLDS_NT 1
 #endif
 
+// Persistent variant (one workgroup per CU walking its weight tiles): 1 = on.
+#ifndef FP8MM_SMALLM_PERSIST
+#define FP8MM_SMALLM_PERSIST 1
+#endif
+
+// Persistent variant: reduce every tile once, at the end (1), when the
+// partials of all of a workgroup's tiles fit in LDS; else tile by tile.
+#ifndef FP8MM_SMALLM_DEFER
+#define FP8MM_SMALLM_DEFER 1
+#endif
+
+// s_waitcnt with only vmcnt constrained (expcnt = 7, lgkmcnt = 15: no wait);
+// a compile-time count.
+#define FP8MM_SM_VMCNT(n) ((((n) & 15) | ((((n) >> 4) & 3) << 14)) | (7 << 4) | (15 << 8))
+
 namespace fp8mm {
 
 namespace {
@@ -318,6 +333,168 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_xlds(
     reduce_store<1, NTX>(red, W, n0, s_act, s_w, sh, M, N);
 }
 
+// Persistent variant for M <= 16 and K % 1024 == 0 when x_q fits in LDS next
+// to the reduction buffers: one workgroup per CU walks the 16-row weight
+// tiles bid, bid + G, bid + 2G, ... (G workgroups).  x_q[0:M, :] is copied
+// into LDS once per workgroup (not once per tile), and the weight loads of
+// the next D tiles are always in flight: each wave keeps a ring of D tiles x
+// CPW chunks of registers, refilling a slot as soon as its MFMAs have read
+// it.  Weight loads are raw buffer loads over the whole weight; a chunk or
+// tile that does not exist loads from an offset past the end of the buffer,
+// which returns zeros without a memory access, so every wave issues the same
+// instruction stream and the wait counts stay static.  The per-tile
+// reduction of the W wave partials is the fixed-order one of the other two
+// kernels (same chunk -> wave assignment), so all three give identical bits.
+constexpr uint32_t kOob = 0x80000000u;   // > any weight byte offset served here (N*K < 2^31)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const uint8_t* p, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// The CPW chunks of one weight tile this wave owns: 2 x 16 bytes per lane and
+// chunk ([16g, 16g+16) and [64+16g, 80+16g) of the chunk, row r of the tile).
+template <int CPW>
+__device__ __forceinline__ void issue_tile(u32x4_t (&a)[CPW][2], __amdgpu_buffer_rsrc_t rw, uint32_t tile_off,
+                                           bool tile_ok, int wave, int W, int nchunks)
+{
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const int chunk = wave + c * W;
+        const uint32_t v = (tile_ok && chunk < nchunks) ? tile_off + (uint32_t)chunk * kChunk : kOob;
+        a[c][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)v, 0, 0);
+        a[c][1] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(v + 64), 0, 0);
+    }
+}
+
+// MFMAs of one tile; B fragments (x_q) from LDS.  A chunk past K reads the
+// last real chunk of x_q (its weight fragment is zero, and x_q is finite
+// there, so it adds exact zeros).
+template <int CPW>
+__device__ __forceinline__ v4f tile_mfma(const u32x4_t (&a)[CPW][2], const uint8_t* __restrict__ xrow, int wave,
+                                         int W, int nchunks, int g)
+{
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        int chunk = wave + c * W;
+        chunk = chunk < nchunks ? chunk : nchunks - 1;
+        const uint8_t* p = xrow + chunk * kChunk + g * 16;
+        const uint4 b0 = *reinterpret_cast<const uint4*>(p), b1 = *reinterpret_cast<const uint4*>(p + 64);
+        v8i A, B;
+        A[0] = (int)a[c][0][0]; A[1] = (int)a[c][0][1]; A[2] = (int)a[c][0][2]; A[3] = (int)a[c][0][3];
+        A[4] = (int)a[c][1][0]; A[5] = (int)a[c][1][1]; A[6] = (int)a[c][1][2]; A[7] = (int)a[c][1][3];
+        B = pack(b0, b1);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 0, 0, 0, 0, 0, 0);
+    }
+    return acc;
+}
+
+// Wave 0: sum the W partials of one tile in wave order, scale (weight scales
+// preloaded in sw: n = n0 + 4*(lane/16) .. +3) and store bf16.
+__device__ __forceinline__ void reduce_tile(const v4f* red, int W, int64_t n0, float s_act, const float4 sw,
+                                            const ShardTable& sh, int M, int lane)
+{
+    const int m = lane & 15;
+    if (m >= M) return;
+    v4f s = red[lane];
+    for (int w = 1; w < W; ++w) {
+        const v4f p = red[w * 64 + lane];
+        s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+    }
+    const int64_t n = n0 + 4 * (lane >> 4);
+    int i = 0;
+    while (i + 1 < sh.num && n0 >= sh.start[i + 1]) ++i;
+    const uint32_t o0 = f32_to_bf16_rne((s.x * s_act) * sw.x) | (f32_to_bf16_rne((s.y * s_act) * sw.y) << 16);
+    const uint32_t o1 = f32_to_bf16_rne((s.z * s_act) * sw.z) | (f32_to_bf16_rne((s.w * s_act) * sw.w) << 16);
+    *reinterpret_cast<uint2*>(sh.out[i] + (int64_t)m * sh.ldo[i] + (n - sh.start[i])) = make_uint2(o0, o1);
+}
+
+template <int CPW, int D, int WMAX, bool DEFER>
+__global__ __launch_bounds__(64 * WMAX) void k_gemm_small_m_persist(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act,
+    const float* __restrict__ s_w, ShardTable sh, int M, int64_t N, int64_t K, int nchunks)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int ntiles = (int)(N >> 4);
+    const int my_tiles = (ntiles - bid + G - 1) / G;
+    __builtin_assume(my_tiles >= 1);                    // G <= ntiles
+    const int64_t ldsx = K + 16;
+    uint8_t* xs = smem;
+    // W partials: [2][W][64], or with DEFER [my_tiles][W][64] (reduced once, at the end)
+    v4f* red = reinterpret_cast<v4f*>(smem + ((M * ldsx + 15) & ~(int64_t)15));
+    const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
+    const uint32_t lane_off = (uint32_t)(r * K + g * 16);
+    auto tile_off = [&](int u) { return (uint32_t)((int64_t)(bid + u * G) * 16 * K) + lane_off; };
+    // weight scales of tile u for this lane's four rows (zeros past the last tile)
+    auto tile_sw = [&](int u) {
+        const uint32_t o = u < my_tiles ? (uint32_t)((bid + u * G) * 64 + g * 16) : kOob;
+        return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, 0, 0);
+    };
+
+    // x_q -> LDS first: each wave moves 64 consecutive 16-byte pieces (1 KB,
+    // inside one row because K/16 is a multiple of 64) per instruction.
+    const int64_t kp = K >> 4, np = (int64_t)M * kp;
+    for (int64_t p0 = (int64_t)wave * 64; p0 < np; p0 += blockDim.x) {
+        const int64_t row = p0 / kp, col0 = p0 - row * kp;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(xq + (p0 + lane) * 16),
+                                         (lds_void*)(xs + row * ldsx + col0 * 16), 16, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4_t a[D][CPW][2], sws[D];
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+        issue_tile<CPW>(a[s], rw, tile_off(s), s < my_tiles, wave, W, nchunks);
+        if constexpr (!DEFER) sws[s] = tile_sw(s);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // x_q landed: only the D tiles' weight (and scale) loads, issued after it,
+    // may be in flight (for this wave; the barrier extends it to the workgroup)
+    __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT(D * (2 * CPW + (DEFER ? 0 : 1))));
+    __builtin_amdgcn_s_barrier();
+
+    const uint8_t* xrow = xs + (r < M ? r : M - 1) * ldsx;
+    for (int u0 = 0; u0 < my_tiles; u0 += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            const int u = u0 + s;
+            if (u >= my_tiles) break;                    // workgroup-uniform
+            const v4f acc = tile_mfma<CPW>(a[s], xrow, wave, W, nchunks, g);
+            issue_tile<CPW>(a[s], rw, tile_off(u + D), u + D < my_tiles, wave, W, nchunks);
+            if constexpr (DEFER) {
+                red[(u * W + wave) * 64 + lane] = acc;
+            } else {
+                const u32x4_t swu = sws[s];
+                sws[s] = tile_sw(u + D);
+                v4f* rb = red + (u & 1) * W * 64;
+                rb[wave * 64 + lane] = acc;
+                __syncthreads();
+                if (wave == 0)
+                    reduce_tile(rb, W, (int64_t)(bid + u * G) * 16, s_act,
+                                make_float4(__uint_as_float(swu[0]), __uint_as_float(swu[1]),
+                                            __uint_as_float(swu[2]), __uint_as_float(swu[3])),
+                                sh, M, lane);
+            }
+        }
+    }
+    if constexpr (DEFER) {                               // one barrier, then every wave reduces
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < my_tiles * 64; idx += blockDim.x) {
+            const int u = idx >> 6, l = idx & 63;
+            const int64_t n0 = (int64_t)(bid + u * G) * 16;
+            reduce_tile(red + u * W * 64, W, n0, s_act, *reinterpret_cast<const float4*>(s_w + n0 + 4 * (l >> 4)),
+                        sh, M, l);
+        }
+    }
+}
+
 // Waves per workgroup: a function of K only (it fixes the summation order).
 int small_m_waves(int64_t K)
 {
@@ -366,11 +543,75 @@ void launch_xlds(const dim3& grid, const dim3& block, size_t lds, hipStream_t st
                        M, N, K, nchunks);
 }
 
+// LDS bytes of the persistent variant (x_q rows + reduction buffers for
+// `tiles` tiles), or 0 if it does not apply.
+size_t persist_bytes(int64_t M, int64_t N, int64_t K, int W, int64_t tiles)
+{
+    if (!FP8MM_SMALLM_PERSIST || M > 16 || K % 1024 != 0 || N * K >= ((int64_t)1 << 31)) return 0;
+    const size_t b = (size_t)((M * (K + 16) + 15) & ~(int64_t)15) + (size_t)tiles * W * 64 * sizeof(v4f);
+    return b <= (size_t)160 * 1024 ? b : 0;
+}
+
+template <int CPW, int D, int WMAX, bool DEFER>
+void launch_persist(const dim3& grid, const dim3& block, size_t lds, hipStream_t stream, const uint8_t* xq,
+                    const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh, int M, int64_t N,
+                    int64_t K, int nchunks)
+{
+    static const bool attr = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_persist<CPW, D, WMAX, DEFER>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        return true;
+    }();
+    (void)attr;
+    hipLaunchKernelGGL((k_gemm_small_m_persist<CPW, D, WMAX, DEFER>), grid, block, lds, stream, xq, wq, s_act, s_w, sh,
+                       M, N, K, nchunks);
+}
+
 void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
                          const ShardTable& shards, int64_t M, int64_t N, int64_t K, hipStream_t stream)
 {
     const int W = small_m_waves(K);
     const int nchunks = (int)((K + kChunk - 1) / kChunk);
+    const int64_t G = N / 16 < num_cus() ? N / 16 : num_cus();
+    const int64_t tiles_max = (N / 16 + G - 1) / G;            // tiles of the busiest workgroup
+    // (deferring needs registers too: only with up to 8 waves, 256 VGPRs each)
+    const size_t pl_defer = FP8MM_SMALLM_DEFER && W <= 8 ? persist_bytes(M, N, K, W, tiles_max) : 0;
+    const size_t pl = pl_defer ? pl_defer : persist_bytes(M, N, K, W, 2);
+    const bool defer = pl_defer != 0;
+    if (pl) {
+        // Ring depth: as many tiles in flight as the registers allow (<= 3).
+        // Up to 8 waves: 2 waves per SIMD, 256 VGPRs each; more: 4, 128 VGPRs.
+        const int cpw = (nchunks + W - 1) / W;
+        const dim3 grid((uint32_t)G), block(64 * W);
+        const int budget = (W <= 8 ? 256 : 128) - 72;
+        int d = budget / (cpw * 8);
+        d = d < 1 ? 1 : (d > 3 ? 3 : d);
+#define FP8MM_PERSIST_ARGS grid, block, pl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks
+#define FP8MM_PERSIST_DISPATCH(C, DF)                                                         \
+        if (W > 8) launch_persist<C, 1, 16, DF>(FP8MM_PERSIST_ARGS);                           \
+        else if (d == 1) launch_persist<C, 1, 8, DF>(FP8MM_PERSIST_ARGS);                      \
+        else if (d == 2) launch_persist<C, 2, 8, DF>(FP8MM_PERSIST_ARGS);                      \
+        else launch_persist<C, 3, 8, DF>(FP8MM_PERSIST_ARGS);
+#define FP8MM_PERSIST_CASE(C)                                                                 \
+    case C:                                                                                   \
+        if (defer) { FP8MM_PERSIST_DISPATCH(C, true) } else { FP8MM_PERSIST_DISPATCH(C, false) } \
+        return;
+        switch (cpw) {
+            FP8MM_PERSIST_CASE(1)
+            FP8MM_PERSIST_CASE(2)
+            FP8MM_PERSIST_CASE(3)
+            FP8MM_PERSIST_CASE(4)
+            FP8MM_PERSIST_CASE(5)
+            FP8MM_PERSIST_CASE(6)
+            FP8MM_PERSIST_CASE(7)
+            FP8MM_PERSIST_CASE(8)
+            FP8MM_PERSIST_CASE(9)
+        default: break;                                  // more chunks per wave: the kernels below
+        }
+#undef FP8MM_PERSIST_ARGS
+#undef FP8MM_PERSIST_DISPATCH
+#undef FP8MM_PERSIST_CASE
+    }
     const size_t xl = xlds_bytes(M, K, W);
     if (xl) {
         const int cpw = (nchunks + W - 1) / W;

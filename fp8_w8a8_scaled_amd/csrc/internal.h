@@ -33,6 +33,9 @@ void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, cons
                          const ShardTable& shards, int64_t M, int64_t N, int64_t K,
                          hipStream_t stream);
 
+// gemm_large_m.hip: compute units of the current device (cached).
+int num_cus();
+
 // gemm_large_m.hip: compute-bound MFMA-tiled arm, any M.
 void launch_gemm_large_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
                          const ShardTable& shards, int64_t M, int64_t N, int64_t K,
