@@ -64,6 +64,11 @@
 #define FP8MM_SMALLM_PERSIST 1
 #endif
 
+// Persistent variant with the weight staged through per-wave LDS rings: 1 = on.
+#ifndef FP8MM_SMALLM_RING
+#define FP8MM_SMALLM_RING 1
+#endif
+
 // Persistent variant: reduce every tile once, at the end (1), when the
 // partials of all of a workgroup's tiles fit in LDS; else tile by tile.
 #ifndef FP8MM_SMALLM_DEFER
@@ -73,6 +78,8 @@
 // s_waitcnt with only vmcnt constrained (expcnt = 7, lgkmcnt = 15: no wait);
 // a compile-time count.
 #define FP8MM_SM_VMCNT(n) ((((n) & 15) | ((((n) >> 4) & 3) << 14)) | (7 << 4) | (15 << 8))
+// lgkmcnt(0) only (vmcnt = 63, expcnt = 7: no wait)
+#define FP8MM_SM_LGKM0 (15 | (3 << 14) | (7 << 4))
 
 namespace fp8mm {
 
@@ -392,16 +399,17 @@ __device__ __forceinline__ v4f tile_mfma(const u32x4_t (&a)[CPW][2], const uint8
     return acc;
 }
 
-// Wave 0: sum the W partials of one tile in wave order, scale (weight scales
-// preloaded in sw: n = n0 + 4*(lane/16) .. +3) and store bf16.
-__device__ __forceinline__ void reduce_tile(const v4f* red, int W, int64_t n0, float s_act, const float4 sw,
-                                            const ShardTable& sh, int M, int lane)
+// Sum the W partials of one tile in wave order (partial of wave w for MFMA
+// lane `lane` at red[w * stride + slot]), scale (weight scales in sw: n = n0 +
+// 4*(lane/16) .. +3) and store bf16.
+__device__ __forceinline__ void reduce_tile(const v4f* red, int stride, int slot, int W, int64_t n0, float s_act,
+                                            const float4 sw, const ShardTable& sh, int M, int lane)
 {
     const int m = lane & 15;
     if (m >= M) return;
-    v4f s = red[lane];
+    v4f s = red[slot];
     for (int w = 1; w < W; ++w) {
-        const v4f p = red[w * 64 + lane];
+        const v4f p = red[w * stride + slot];
         s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
     }
     const int64_t n = n0 + 4 * (lane >> 4);
@@ -477,7 +485,7 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemm_small_m_persist(
                 rb[wave * 64 + lane] = acc;
                 __syncthreads();
                 if (wave == 0)
-                    reduce_tile(rb, W, (int64_t)(bid + u * G) * 16, s_act,
+                    reduce_tile(rb, 64, lane, W, (int64_t)(bid + u * G) * 16, s_act,
                                 make_float4(__uint_as_float(swu[0]), __uint_as_float(swu[1]),
                                             __uint_as_float(swu[2]), __uint_as_float(swu[3])),
                                 sh, M, lane);
@@ -489,8 +497,157 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemm_small_m_persist(
         for (int idx = threadIdx.x; idx < my_tiles * 64; idx += blockDim.x) {
             const int u = idx >> 6, l = idx & 63;
             const int64_t n0 = (int64_t)(bid + u * G) * 16;
-            reduce_tile(red + u * W * 64, W, n0, s_act, *reinterpret_cast<const float4*>(s_w + n0 + 4 * (l >> 4)),
-                        sh, M, l);
+            reduce_tile(red + u * W * 64, 64, l, W, n0, s_act,
+                        *reinterpret_cast<const float4*>(s_w + n0 + 4 * (l >> 4)), sh, M, l);
+        }
+    }
+}
+
+// Weight staging through LDS for the persistent variant.  A weight load
+// instruction in which each lane takes 16 bytes of a 16-row fragment in the
+// MFMA operand layout (lane -> row) touches 16 half cache lines; one in which 8
+// lanes cover a row's 128-byte chunk (8 rows per instruction) touches 8 whole
+// lines, and the memory pipeline streams the latter markedly faster at decode
+// sizes.  So each wave moves its chunks with whole-line direct-to-LDS loads
+// into a private ring of S 2 KB slots and reads its A fragments back from
+// there (no barrier: the wave that loads a slot is the only one reading it).
+// Within a slot row n holds its 16-byte pieces XOR-swizzled by row (skipping
+// one row bit), so the fragment reads are bank-conflict free.
+__device__ __forceinline__ int wswz(int row, int piece) { return piece ^ ((row >> 1) & 7); }
+
+// Chunk `chunk` of tile rows n0..n0+15 into an LDS slot: instruction i covers
+// rows 8i..8i+7; lane -> row 8i + lane/8, physical piece lane%8.  `ok` false:
+// an offset past the end of the buffer (zeros, no memory access).
+__device__ __forceinline__ void dma_wchunk(__amdgpu_buffer_rsrc_t rw, uint8_t* slot, uint32_t row_off0,
+                                           uint32_t row_off1, int chunk, bool ok)
+{
+    const uint32_t c = (uint32_t)chunk * kChunk;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)slot, 16, (int)(ok ? row_off0 + c : kOob), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(slot + 1024), 16, (int)(ok ? row_off1 + c : kOob), 0,
+                                             0, 0);
+}
+
+// The A fragment (row r, logical pieces g and g+4) of a staged chunk, and the
+// matching B fragment of x_q.  Both pointers are restrict-qualified: these LDS
+// reads never touch a slot with loads in flight (the explicit waits order
+// them), which keeps the compiler from waiting for every outstanding load.
+__device__ __forceinline__ v4f chunk_mfma(const uint8_t* __restrict__ slot, const uint8_t* __restrict__ xrow,
+                                          int chunk, int r, int g, v4f acc)
+{
+    const uint8_t* ws = slot + r * kChunk;
+    const v8i A = pack(*reinterpret_cast<const uint4*>(ws + wswz(r, g) * 16),
+                       *reinterpret_cast<const uint4*>(ws + wswz(r, g + 4) * 16));
+    const uint8_t* xp = xrow + chunk * kChunk + g * 16;
+    const v8i B = pack(*reinterpret_cast<const uint4*>(xp), *reinterpret_cast<const uint4*>(xp + 64));
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 0, 0, 0, 0, 0, 0);
+}
+
+template <int S, bool DEFER>
+__global__ __launch_bounds__(64 * 8) void k_gemm_small_m_ring(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act,
+    const float* __restrict__ s_w, ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int ntiles = (int)(N >> 4);
+    const int my_tiles = (ntiles - bid + G - 1) / G;
+    __builtin_assume(my_tiles >= 1);                    // G <= ntiles
+    const int tiles_max = (ntiles + G - 1) / G;
+    const int64_t ldsx = K + 16;
+    uint8_t* xs = smem;
+    const int64_t xbytes = (M * ldsx + 15) & ~(int64_t)15;
+    // W partials: [2][W][64], or with DEFER [tiles_max][W][mp] (reduced once, at
+    // the end; for M <= 8 only the 32 lanes holding columns m < 8 are kept)
+    const int mp = M <= 8 ? 32 : 64;
+    const int pslot = mp == 64 ? lane : (lane >> 4) * 8 + (lane & 7);
+    v4f* red = reinterpret_cast<v4f*>(smem + xbytes);
+    uint8_t* ring = smem + xbytes + (DEFER ? (int64_t)tiles_max * W * mp : (int64_t)2 * W * 64) * sizeof(v4f) +
+                    wave * S * 2048;
+    const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
+    // this lane's two rows of a chunk (instruction i: row 8i + lane/8), logical piece
+    const int lrow = lane >> 3;
+    const uint32_t pieceoff0 = (uint32_t)(lrow * K + wswz(lrow, lane & 7) * 16);
+    const uint32_t pieceoff1 = (uint32_t)((lrow + 8) * K + wswz(lrow + 8, lane & 7) * 16);
+    const int total = my_tiles * cpw;                   // this wave's chunks, tile-major
+    auto issue = [&](int j, int slot) {                 // chunk j of the sequence into a ring slot
+        const int u = j / cpw, c = j - u * cpw;
+        const int chunk = wave + c * W;
+        const uint32_t t0 = (uint32_t)((int64_t)(bid + u * G) * 16 * K);
+        dma_wchunk(rw, ring + slot * 2048, t0 + pieceoff0, t0 + pieceoff1, chunk, j < total && chunk < nchunks);
+    };
+
+    // x_q -> LDS first: each wave moves 64 consecutive 16-byte pieces (1 KB,
+    // inside one row because K/16 is a multiple of 64) per instruction.
+    const int64_t kp = K >> 4, np = (int64_t)M * kp;
+    for (int64_t p0 = (int64_t)wave * 64; p0 < np; p0 += blockDim.x) {
+        const int64_t row = p0 / kp, col0 = p0 - row * kp;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(xq + (p0 + lane) * 16),
+                                         (lds_void*)(xs + row * ldsx + col0 * 16), 16, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) issue(s, s);
+    __builtin_amdgcn_sched_barrier(0);
+    // x_q landed: only the S chunks issued after it may be in flight (for this
+    // wave; the barrier extends it to the workgroup)
+    __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT(2 * S));
+    __builtin_amdgcn_s_barrier();
+
+    const uint8_t* xrow = xs + (r < M ? r : M - 1) * ldsx;
+    // weight scales of tile u for this lane's four rows (tile-by-tile reduction only)
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
+    auto tile_sw = [&](int t) {
+        const uint32_t o = t < my_tiles ? (uint32_t)((bid + t * G) * 64 + g * 16) : kOob;
+        return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, 0, 0);
+    };
+    u32x4_t swu{0u, 0u, 0u, 0u};
+    if constexpr (!DEFER) swu = tile_sw(0);
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    int u = 0, c = 0;                                   // tile and chunk of sequence position j
+    for (int j0 = 0; j0 < total; j0 += S) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int j = j0 + s;
+            if (j >= total) break;                       // wave-uniform
+            // chunk j landed: only the S-1 chunks after it may be in flight
+            __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT(2 * (S - 1)));
+            int chunk = wave + c * W;
+            chunk = chunk < nchunks ? chunk : nchunks - 1;   // (a zero slot: adds exact zeros)
+            acc = chunk_mfma(ring + s * 2048, xrow, chunk, r, g, acc);
+            __builtin_amdgcn_s_waitcnt(FP8MM_SM_LGKM0);  // the slot's reads have returned
+            issue(j + S, s);
+            if (++c == cpw) {                            // tile u complete
+                if constexpr (DEFER) {
+                    if (mp == 64 || (lane & 15) < 8) red[(u * W + wave) * mp + pslot] = acc;
+                } else {
+                    v4f* rb = red + (u & 1) * W * 64;
+                    rb[wave * 64 + lane] = acc;
+                    __syncthreads();
+                    if (wave == 0)
+                        reduce_tile(rb, 64, lane, W, (int64_t)(bid + u * G) * 16, s_act,
+                                    make_float4(__uint_as_float(swu[0]), __uint_as_float(swu[1]),
+                                                __uint_as_float(swu[2]), __uint_as_float(swu[3])),
+                                    sh, M, lane);
+                    swu = tile_sw(u + 1);                // scales of the next tile
+                }
+                acc = v4f{0.f, 0.f, 0.f, 0.f};
+                c = 0;
+                ++u;
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);                      // no direct-to-LDS load outlives the workgroup
+    if constexpr (DEFER) {                               // one barrier, then every wave reduces
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < my_tiles * mp; idx += blockDim.x) {
+            const int uu = idx / mp, ps = idx - uu * mp;
+            const int l = mp == 64 ? ps : (ps >> 3) * 16 + (ps & 7);
+            const int64_t n0 = (int64_t)(bid + uu * G) * 16;
+            reduce_tile(red + uu * W * mp, mp, ps, W, n0, s_act,
+                        *reinterpret_cast<const float4*>(s_w + n0 + 4 * (l >> 4)), sh, M, l);
         }
     }
 }
@@ -567,11 +724,57 @@ void launch_persist(const dim3& grid, const dim3& block, size_t lds, hipStream_t
                        M, N, K, nchunks);
 }
 
+template <int S, bool DEFER>
+void launch_ring(const dim3& grid, const dim3& block, size_t lds, hipStream_t stream, const uint8_t* xq,
+                 const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh, int M, int64_t N, int64_t K,
+                 int nchunks, int cpw)
+{
+    static const bool attr = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_ring<S, DEFER>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        return true;
+    }();
+    (void)attr;
+    hipLaunchKernelGGL((k_gemm_small_m_ring<S, DEFER>), grid, block, lds, stream, xq, wq, s_act, s_w, sh, M, N, K,
+                       nchunks, cpw);
+}
+
+// The LDS-ring persistent kernel, if it applies (M <= 16, K % 1024 == 0, up to
+// 8 waves, x_q + partials + rings within 160 KB): deepest ring that fits,
+// deferred reduction preferred.
+bool try_ring(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh,
+              int64_t M, int64_t N, int64_t K, int W, int nchunks, hipStream_t stream)
+{
+    if (!FP8MM_SMALLM_RING || M > 16 || K % 1024 != 0 || W > 8 || N * K >= ((int64_t)1 << 31)) return false;
+    const int64_t G = N / 16 < num_cus() ? N / 16 : num_cus();
+    const int64_t tiles_max = (N / 16 + G - 1) / G;
+    const size_t xb = (size_t)((M * (K + 16) + 15) & ~(int64_t)15);
+    const size_t part = (size_t)W * 64 * sizeof(v4f);               // one tile's partials
+    const size_t dpart = (size_t)W * (M <= 8 ? 32 : 64) * sizeof(v4f);   // ... as the deferred buffer keeps them
+    const int cpw = (nchunks + W - 1) / W;
+    const dim3 grid((uint32_t)G), block(64 * W);
+    auto bytes = [&](int S, bool df) { return xb + (df ? tiles_max * dpart : 2 * part) + (size_t)W * S * 2048; };
+#define FP8MM_RING_TRY(S, DF)                                                                          \
+    if (bytes(S, DF) <= 160 * 1024) {                                                                  \
+        launch_ring<S, DF>(grid, block, bytes(S, DF), stream, xq, wq, s_act, s_w, sh, (int)M, N, K, nchunks, cpw); \
+        return true;                                                                                   \
+    }
+    FP8MM_RING_TRY(6, true)
+    FP8MM_RING_TRY(5, true)
+    FP8MM_RING_TRY(6, false)
+    FP8MM_RING_TRY(4, true)
+    FP8MM_RING_TRY(4, false)
+    FP8MM_RING_TRY(3, false)
+#undef FP8MM_RING_TRY
+    return false;
+}
+
 void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
                          const ShardTable& shards, int64_t M, int64_t N, int64_t K, hipStream_t stream)
 {
     const int W = small_m_waves(K);
     const int nchunks = (int)((K + kChunk - 1) / kChunk);
+    if (try_ring(xq, wq, s_act, s_w, shards, M, N, K, W, nchunks, stream)) return;
     const int64_t G = N / 16 < num_cus() ? N / 16 : num_cus();
     const int64_t tiles_max = (N / 16 + G - 1) / G;            // tiles of the busiest workgroup
     // (deferring needs registers too: only with up to 8 waves, 256 VGPRs each)
