@@ -542,8 +542,21 @@ __device__ __forceinline__ v4f chunk_mfma(const uint8_t* __restrict__ slot, cons
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 0, 0, 0, 0, 0, 0);
 }
 
-template <int S, bool DEFER>
-__global__ __launch_bounds__(64 * 8) void k_gemm_small_m_ring(
+// Same, with the x_q chunk staged in the slot too (at +2048, rows swizzled
+// like the weight's).  A missing chunk is all zeros in both operands.
+__device__ __forceinline__ v4f chunk_mfma_x(const uint8_t* __restrict__ slot, int r, int g, int xr, v4f acc)
+{
+    const uint8_t* ws = slot + r * kChunk;
+    const v8i A = pack(*reinterpret_cast<const uint4*>(ws + wswz(r, g) * 16),
+                       *reinterpret_cast<const uint4*>(ws + wswz(r, g + 4) * 16));
+    const uint8_t* xs = slot + 2048 + xr * kChunk;
+    const v8i B = pack(*reinterpret_cast<const uint4*>(xs + wswz(xr, g) * 16),
+                       *reinterpret_cast<const uint4*>(xs + wswz(xr, g + 4) * 16));
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 0, 0, 0, 0, 0, 0);
+}
+
+template <int S, bool DEFER, int XI>
+__global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act,
     const float* __restrict__ s_w, ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw)
 {
@@ -556,47 +569,68 @@ __global__ __launch_bounds__(64 * 8) void k_gemm_small_m_ring(
     const int my_tiles = (ntiles - bid + G - 1) / G;
     __builtin_assume(my_tiles >= 1);                    // G <= ntiles
     const int tiles_max = (ntiles + G - 1) / G;
+    constexpr int SB = 2048 + 1024 * XI;                // ring slot: W chunk (+ x_q chunk)
+    constexpr int LPC = 2 + XI;                          // direct-to-LDS loads per chunk
     const int64_t ldsx = K + 16;
     uint8_t* xs = smem;
-    const int64_t xbytes = (M * ldsx + 15) & ~(int64_t)15;
+    const int64_t xbytes = XI ? 0 : (M * ldsx + 15) & ~(int64_t)15;
     // W partials: [2][W][64], or with DEFER [tiles_max][W][mp] (reduced once, at
     // the end; for M <= 8 only the 32 lanes holding columns m < 8 are kept)
     const int mp = M <= 8 ? 32 : 64;
     const int pslot = mp == 64 ? lane : (lane >> 4) * 8 + (lane & 7);
     v4f* red = reinterpret_cast<v4f*>(smem + xbytes);
     uint8_t* ring = smem + xbytes + (DEFER ? (int64_t)tiles_max * W * mp : (int64_t)2 * W * 64) * sizeof(v4f) +
-                    wave * S * 2048;
+                    wave * S * SB;
     const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
+    const __amdgpu_buffer_rsrc_t rx = weight_rsrc(xq, M * K);
     // this lane's two rows of a chunk (instruction i: row 8i + lane/8), logical piece
     const int lrow = lane >> 3;
     const uint32_t pieceoff0 = (uint32_t)(lrow * K + wswz(lrow, lane & 7) * 16);
     const uint32_t pieceoff1 = (uint32_t)((lrow + 8) * K + wswz(lrow + 8, lane & 7) * 16);
+    // streamed x_q: rows past M repeat row M-1 (their columns are never stored)
+    const int xr0 = lrow < M ? lrow : M - 1, xr1 = lrow + 8 < M ? lrow + 8 : M - 1;
+    const uint32_t xoff0 = (uint32_t)(xr0 * K + wswz(lrow, lane & 7) * 16);
+    const uint32_t xoff1 = (uint32_t)(xr1 * K + wswz(lrow + 8, lane & 7) * 16);
     const int total = my_tiles * cpw;                   // this wave's chunks, tile-major
     auto issue = [&](int j, int slot) {                 // chunk j of the sequence into a ring slot
         const int u = j / cpw, c = j - u * cpw;
         const int chunk = wave + c * W;
+        const bool ok = j < total && chunk < nchunks;
         const uint32_t t0 = (uint32_t)((int64_t)(bid + u * G) * 16 * K);
-        dma_wchunk(rw, ring + slot * 2048, t0 + pieceoff0, t0 + pieceoff1, chunk, j < total && chunk < nchunks);
+        uint8_t* sl = ring + slot * SB;
+        dma_wchunk(rw, sl, t0 + pieceoff0, t0 + pieceoff1, chunk, ok);
+        const uint32_t cx = (uint32_t)chunk * kChunk;
+        if (XI >= 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sl + 2048), 16, (int)(ok ? xoff0 + cx : kOob),
+                                                     0, 0, 0);
+        if (XI >= 2)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sl + 3072), 16, (int)(ok ? xoff1 + cx : kOob),
+                                                     0, 0, 0);
     };
 
-    // x_q -> LDS first: each wave moves 64 consecutive 16-byte pieces (1 KB,
-    // inside one row because K/16 is a multiple of 64) per instruction.
-    const int64_t kp = K >> 4, np = (int64_t)M * kp;
-    for (int64_t p0 = (int64_t)wave * 64; p0 < np; p0 += blockDim.x) {
-        const int64_t row = p0 / kp, col0 = p0 - row * kp;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(xq + (p0 + lane) * 16),
-                                         (lds_void*)(xs + row * ldsx + col0 * 16), 16, 0, 0);
+    if (XI == 0) {
+        // x_q -> LDS first: each wave moves 64 consecutive 16-byte pieces (1 KB,
+        // inside one row because K/16 is a multiple of 64) per instruction.
+        const int64_t kp = K >> 4, np = (int64_t)M * kp;
+        for (int64_t p0 = (int64_t)wave * 64; p0 < np; p0 += blockDim.x) {
+            const int64_t row = p0 / kp, col0 = p0 - row * kp;
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(xq + (p0 + lane) * 16),
+                                             (lds_void*)(xs + row * ldsx + col0 * 16), 16, 0, 0);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < S; ++s) issue(s, s);
     __builtin_amdgcn_sched_barrier(0);
-    // x_q landed: only the S chunks issued after it may be in flight (for this
-    // wave; the barrier extends it to the workgroup)
-    __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT(2 * S));
-    __builtin_amdgcn_s_barrier();
+    if (XI == 0) {
+        // x_q landed: only the S chunks issued after it may be in flight (for
+        // this wave; the barrier extends it to the workgroup)
+        __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT(LPC * S));
+        __builtin_amdgcn_s_barrier();
+    }
 
     const uint8_t* xrow = xs + (r < M ? r : M - 1) * ldsx;
+    const int xsr = XI == 1 ? (r < 8 ? r : 7) : r;      // streamed x_q: row of the slot's x part
     // weight scales of tile u for this lane's four rows (tile-by-tile reduction only)
     const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
     auto tile_sw = [&](int t) {
@@ -613,10 +647,14 @@ __global__ __launch_bounds__(64 * 8) void k_gemm_small_m_ring(
             const int j = j0 + s;
             if (j >= total) break;                       // wave-uniform
             // chunk j landed: only the S-1 chunks after it may be in flight
-            __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT(2 * (S - 1)));
-            int chunk = wave + c * W;
-            chunk = chunk < nchunks ? chunk : nchunks - 1;   // (a zero slot: adds exact zeros)
-            acc = chunk_mfma(ring + s * 2048, xrow, chunk, r, g, acc);
+            __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT(LPC * (S - 1)));
+            if (XI == 0) {
+                int chunk = wave + c * W;
+                chunk = chunk < nchunks ? chunk : nchunks - 1;   // (a zero slot: adds exact zeros)
+                acc = chunk_mfma(ring + s * SB, xrow, chunk, r, g, acc);
+            } else {
+                acc = chunk_mfma_x(ring + s * SB, r, g, xsr, acc);
+            }
             __builtin_amdgcn_s_waitcnt(FP8MM_SM_LGKM0);  // the slot's reads have returned
             issue(j + S, s);
             if (++c == cpw) {                            // tile u complete
@@ -724,28 +762,28 @@ void launch_persist(const dim3& grid, const dim3& block, size_t lds, hipStream_t
                        M, N, K, nchunks);
 }
 
-template <int S, bool DEFER>
+template <int S, bool DEFER, int XI>
 void launch_ring(const dim3& grid, const dim3& block, size_t lds, hipStream_t stream, const uint8_t* xq,
                  const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh, int M, int64_t N, int64_t K,
                  int nchunks, int cpw)
 {
     static const bool attr = [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_ring<S, DEFER>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_ring<S, DEFER, XI>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         return true;
     }();
     (void)attr;
-    hipLaunchKernelGGL((k_gemm_small_m_ring<S, DEFER>), grid, block, lds, stream, xq, wq, s_act, s_w, sh, M, N, K,
+    hipLaunchKernelGGL((k_gemm_small_m_ring<S, DEFER, XI>), grid, block, lds, stream, xq, wq, s_act, s_w, sh, M, N, K,
                        nchunks, cpw);
 }
 
-// The LDS-ring persistent kernel, if it applies (M <= 16, K % 1024 == 0, up to
-// 8 waves, x_q + partials + rings within 160 KB): deepest ring that fits,
-// deferred reduction preferred.
+// The LDS-ring persistent kernel, if it applies (M <= 16, K % 1024 == 0,
+// x_q + partials + rings within 160 KB): deepest ring that fits, deferred
+// reduction preferred.
 bool try_ring(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh,
               int64_t M, int64_t N, int64_t K, int W, int nchunks, hipStream_t stream)
 {
-    if (!FP8MM_SMALLM_RING || M > 16 || K % 1024 != 0 || W > 8 || N * K >= ((int64_t)1 << 31)) return false;
+    if (!FP8MM_SMALLM_RING || M > 16 || K % 1024 != 0 || N * K >= ((int64_t)1 << 31)) return false;
     const int64_t G = N / 16 < num_cus() ? N / 16 : num_cus();
     const int64_t tiles_max = (N / 16 + G - 1) / G;
     const size_t xb = (size_t)((M * (K + 16) + 15) & ~(int64_t)15);
@@ -753,18 +791,30 @@ bool try_ring(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_
     const size_t dpart = (size_t)W * (M <= 8 ? 32 : 64) * sizeof(v4f);   // ... as the deferred buffer keeps them
     const int cpw = (nchunks + W - 1) / W;
     const dim3 grid((uint32_t)G), block(64 * W);
-    auto bytes = [&](int S, bool df) { return xb + (df ? tiles_max * dpart : 2 * part) + (size_t)W * S * 2048; };
-#define FP8MM_RING_TRY(S, DF)                                                                          \
-    if (bytes(S, DF) <= 160 * 1024) {                                                                  \
-        launch_ring<S, DF>(grid, block, bytes(S, DF), stream, xq, wq, s_act, s_w, sh, (int)M, N, K, nchunks, cpw); \
+    // x_q in LDS (XI = 0), else streamed with each chunk (1 KB for M <= 8, 2 KB for M <= 16)
+    auto bytes = [&](int S, bool df, int xi) {
+        return (xi ? 0 : xb) + (df ? tiles_max * dpart : 2 * part) + (size_t)W * S * (2048 + 1024 * xi);
+    };
+#define FP8MM_RING_TRY(S, DF, XI)                                                                      \
+    if (bytes(S, DF, XI) <= 160 * 1024) {                                                              \
+        launch_ring<S, DF, XI>(grid, block, bytes(S, DF, XI), stream, xq, wq, s_act, s_w, sh, (int)M, N, K, nchunks, \
+                               cpw);                                                                   \
         return true;                                                                                   \
     }
-    FP8MM_RING_TRY(6, true)
-    FP8MM_RING_TRY(5, true)
-    FP8MM_RING_TRY(6, false)
-    FP8MM_RING_TRY(4, true)
-    FP8MM_RING_TRY(4, false)
-    FP8MM_RING_TRY(3, false)
+    FP8MM_RING_TRY(6, true, 0)
+    FP8MM_RING_TRY(5, true, 0)
+    FP8MM_RING_TRY(6, false, 0)
+    FP8MM_RING_TRY(4, true, 0)
+    FP8MM_RING_TRY(4, false, 0)
+    FP8MM_RING_TRY(3, false, 0)
+    if (M <= 8) {
+        FP8MM_RING_TRY(4, true, 1)
+        FP8MM_RING_TRY(3, true, 1)
+        FP8MM_RING_TRY(2, true, 1)
+    } else {
+        FP8MM_RING_TRY(3, true, 2)
+        FP8MM_RING_TRY(2, true, 2)
+    }
 #undef FP8MM_RING_TRY
     return false;
 }
