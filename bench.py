@@ -60,6 +60,7 @@ def _args():
     p.add_argument("--M", type=int, default=8)
     p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-sweep", action="store_true", help="skip the 64-layer decode-step weight sweep")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--summarize-trace", metavar="DIR")
@@ -166,7 +167,7 @@ def bench_decode(fp8, M, steps, warmup):
     gemm_ms = graph_time_ms(gemm, steps, warmup)
     step_bytes = gemm_bytes + quant_bytes
     achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
-    traffic = load_traffic("decode_gemm_M8_K5120_N10240_pmc")
+    traffic = load_traffic(f"decode_gemm_M{M}_K{K}_N{N}_pmc")
     return {
         "ms_per_step": ms,
         "value": step_bytes / (ms * 1e-3) / 1e9,
@@ -174,7 +175,7 @@ def bench_decode(fp8, M, steps, warmup):
                    "weight_copies_rotated": copies,
                    "step": "static quant [M,K] + scaled GEMM via dispatcher (small-M arm), graph-replayed",
                    "algorithmic_bytes_per_step": step_bytes},
-        "roofline": {"bound": "hbm", "kernel": "k_gemm_small_m_xlds", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "k_gemm_small_m_ring", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_us": gemm_ms * 1e3},
     }
@@ -223,6 +224,66 @@ def bench_prefill(fp8, steps, warmup):
                      "traffic": load_traffic("prefill_gateup_M6576_K5120_N34816_pmc"),
                      "algorithmic_flops_per_launch": flops1, "avg_launch_us": gu_ms * 1e3},
     }
+
+
+def bench_sweep(fp8, layers, M, steps, warmup, wid=4):
+    """Decode-step weight sweep: `layers` = ((count, projections), ...).  The
+    distinct projections of each layer group get their own seeded weights
+    (quantized on the GPU); every other layer holds device copies, so a step
+    streams count x bytes from HBM (far past the Infinity Cache).  A step is,
+    per layer and projection, the static quant of its bf16 input (fused
+    RMSNorm quant for the projections a norm feeds: qkv(z) and gate_up) and
+    its GEMM, at M tokens."""
+    import torch
+    import workloads as wl
+    plan, src, step_bytes, gemm_bytes = [], {}, 0, 0
+    for gi, (count, projs) in enumerate(layers):
+        srcs = []
+        for pi, p in enumerate(projs):
+            t = wl.T_LAYER0 + 16 * gi + pi
+            norm = p.name.startswith(("qkv", "in_proj", "gate_up"))
+            x = bf16_dev(wl.activation_bf16(wid, M, p.K, outliers=True, tensor=t))
+            gam = bf16_dev(wl.gamma_bf16(wid, p.K)) if norm else None
+            s = float((fp8.act_scale(x, gam, wl.EPS) if norm else fp8.act_scale(x)).item())
+            wq, sw = fp8.quant_weight(f32_dev(wl.weight_f32(wid, p.N, p.K, tensor=t)))
+            xq = torch.empty((M, p.K), dtype=torch.uint8, device="cuda")
+            outs = [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for n in (p.shards or (p.N,))]
+            srcs.append((p, x, gam, s, wq, sw, xq, outs))
+        for li in range(count):
+            for (p, x, gam, s, wq, sw, xq, outs) in srcs:
+                plan.append((p, x, gam, s, wq if li == 0 else wq.clone(), sw, xq, outs))
+                step_bytes += p.N * p.K + 4 * p.N + M * p.K + 2 * M * p.N + 3 * M * p.K + (2 * p.K if gam is not None else 0)
+                gemm_bytes += p.N * p.K + 4 * p.N + M * p.K + 2 * M * p.N
+    torch.cuda.synchronize()
+
+    def step(i):
+        for (p, x, gam, s, wq, sw, xq, outs) in plan:
+            if gam is not None:
+                fp8.quant_rmsnorm(x, gam, s, wl.EPS, out=xq)
+            else:
+                fp8.quant(x, s, out=xq)
+            if p.shards:
+                fp8.scaled_mm_merged(xq, wq, s, sw, list(p.shards), outs=outs)
+            else:
+                fp8.scaled_mm(xq, wq, s, sw, out=outs[0])
+
+    def gemms(i):
+        for (p, x, gam, s, wq, sw, xq, outs) in plan:
+            if p.shards:
+                fp8.scaled_mm_merged(xq, wq, s, sw, list(p.shards), outs=outs)
+            else:
+                fp8.scaled_mm(xq, wq, s, sw, out=outs[0])
+
+    ms = graph_time_ms(step, steps, warmup)
+    gms = graph_time_ms(gemms, steps, warmup)
+    n_launch = len(plan)
+    res = {"layers": sum(c for c, _ in layers), "launches_per_step": 2 * n_launch, "gemm_launches": n_launch,
+           "weight_bytes": sum(p.N * p.K for (p, *_r) in plan), "ms_per_step": ms,
+           "value": step_bytes / (ms * 1e-3) / 1e9, "unit": "GB/s",
+           "gemm_only": {"ms": gms, "GBs": gemm_bytes / (gms * 1e-3) / 1e9}}
+    del plan
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(M, seconds):
@@ -335,7 +396,7 @@ def pmc_driver(fp8, which, meta_dir):
         torch.cuda.synchronize()
         for i in range(3):
             fp8.scaled_mm(xq, copies[4 * i + 1], s_act, sw, out=out)
-        kernel = "k_gemm_small_m_xlds"
+        kernel = "k_gemm_small_m_ring"
     else:
         M, K, N = 6576, 5120, 34816
         xd = bf16_dev(wl.activation_bf16(wl.PREFILL.wid, M, K, outliers=False))
@@ -381,6 +442,12 @@ def main():
     }
     if not a.no_prefill:
         line["prefill"] = bench_prefill(fp8, a.prefill_steps, a.warmup)
+    if not a.no_sweep:
+        import workloads as wl
+        line["decode_step_sweep"] = {
+            "4A_64_layers": bench_sweep(fp8, ((wl.DECODE_STEP_LAYERS, wl.DECODE_STEP_LAYER),), a.M, 3, 1),
+            "4B_pages_tower": bench_sweep(fp8, wl.DECODE_STEP_4B, a.M, 3, 1),
+        }
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a.M, a.cpu_seconds)
     line["kernel_sources_sha256_16"] = kernel_sources_hash()

@@ -158,36 +158,86 @@ def test_decode_mlp_merged_gate_up_and_down(fp8, M):
 
 
 def test_prefill_sampled_rows(fp8):
-    """Prefill chunk, M = 6576 (large-M arm): the whole GEMM on the GPU, checked
-    on sampled rows (tile edges, the ragged tail, random rows) against the oracle."""
+    """Prefill chunk, M = 6576 (large-M arm): the whole GEMM on the GPU from the
+    oracle's quantized inputs, checked on sampled rows (tile edges, the ragged
+    tail, random rows) against the oracle; the GPU's own quantization of the
+    same inputs is checked bit-exact on the side."""
     M, K, N = 6576, 5120, 34816
     x = wl.activation_bf16(5, M, K, outliers=False)
     g = wl.gamma_bf16(5, K)
     s1 = oracle.act_scale(x, g, wl.EPS)
-    xq_gpu = fp8.quant_rmsnorm(bf16_dev(x), bf16_dev(g), s1, wl.EPS)
-    xq = host_u8(xq_gpu)
+    xq = oracle.quant_rmsnorm(x, g, wl.EPS, s1)
+    assert np.array_equal(host_u8(fp8.quant_rmsnorm(bf16_dev(x), bf16_dev(g), s1, wl.EPS)), xq)
     w = wl.weight_f32(5, N, K)
+    wq, sw = oracle.quant_weight(w)
     wq_gpu, sw_gpu = fp8.quant_weight(f32_dev(w))
     del w
+    assert np.array_equal(host_u8(wq_gpu), wq) and np.array_equal(sw_gpu.cpu().numpy().view(np.uint32),
+                                                                  sw.view(np.uint32))
+    del wq_gpu, sw_gpu
     assert fp8.select(M, N, K) == 1
-    outs = fp8.scaled_mm_merged(xq_gpu, wq_gpu, s1, sw_gpu, [17408, 17408])
+    outs = fp8.scaled_mm_merged(u8_dev(xq), u8_dev(wq), s1, f32_dev(sw), [17408, 17408])
     _sync()
     rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 4095, 4096, 6399, 6400, 6527, 6528, 6575],
                                      np.random.Generator(np.random.PCG64(3)).integers(0, M, 19)]))
-    wq, sw = host_u8(wq_gpu), sw_gpu.cpu().numpy()
     got = np.concatenate([host_u16(o) for o in outs], axis=1)[rows]
     ref, v = oracle.scaled_mm(xq[rows], wq, s1, sw, want_v=True)
     assert_within_tolerance(got, ref, v, "prefill gate_up")
     # down projection K = 17408
     xd = wl.activation_bf16(5, M, 17408, outliers=False, tensor=wl.T_DOWN_X)
     s2 = oracle.act_scale(xd)
-    xq2_gpu = fp8.quant(bf16_dev(xd), s2)
-    wd = wl.weight_f32(5, 5120, 17408, tensor=wl.T_DOWN_W)
-    wq2_gpu, sw2_gpu = fp8.quant_weight(f32_dev(wd))
-    out2 = fp8.scaled_mm(xq2_gpu, wq2_gpu, s2, sw2_gpu)
+    xq2 = oracle.quant_act(xd, s2)
+    assert np.array_equal(host_u8(fp8.quant(bf16_dev(xd), s2)), xq2)
+    wq2, sw2 = oracle.quant_weight(wl.weight_f32(5, 5120, 17408, tensor=wl.T_DOWN_W))
+    out2 = fp8.scaled_mm(u8_dev(xq2), u8_dev(wq2), s2, f32_dev(sw2))
     _sync()
-    ref2, v2 = oracle.scaled_mm(host_u8(xq2_gpu)[rows], host_u8(wq2_gpu), s2, sw2_gpu.cpu().numpy(), want_v=True)
+    ref2, v2 = oracle.scaled_mm(xq2[rows], wq2, s2, sw2, want_v=True)
     assert_within_tolerance(host_u16(out2)[rows], ref2, v2, "prefill down")
+
+
+def test_decode_step_sweep_64_layers(fp8):
+    """Decode-step weight sweep at M = 8: 64 layers x {qkvz 12288x5120, out_proj
+    5120x6144, merged gate_up 34816x5120, down 5120x17408} (23.15 GB of E4M3,
+    far beyond on-chip caches), run as one step of 256 launches; layers 0, 31
+    and 63 have their own seeded weights and inputs and are checked in full
+    against the oracle, the other layers hold device copies of them."""
+    import torch
+    M = 8
+    checked = (0, 31, 63)
+    src = {}
+    for l in checked:
+        layer = []
+        for pi, p in enumerate(wl.DECODE_STEP_LAYER):
+            x = wl.activation_bf16(4, M, p.K, outliers=True, tensor=wl.T_LAYER0 + 4 * l + pi)
+            s = oracle.act_scale(x)
+            xq = oracle.quant_act(x, s)
+            wq, sw = oracle.quant_weight(wl.weight_f32(4, p.N, p.K, tensor=wl.T_LAYER0 + 4 * l + pi))
+            layer.append((xq, wq, s, sw))
+        src[l] = layer
+    dev = {l: [(u8_dev(xq), u8_dev(wq), s, f32_dev(sw)) for xq, wq, s, sw in src[l]] for l in checked}
+    layers = []
+    for l in range(wl.DECODE_STEP_LAYERS):
+        if l in dev:
+            layers.append(dev[l])
+        else:
+            base = dev[checked[l % 3]]
+            layers.append([(xq, wq.clone(), s, sw) for xq, wq, s, sw in base])
+    outs = {}
+    for l, layer in enumerate(layers):
+        res = []
+        for (xq, wq, s, sw), p in zip(layer, wl.DECODE_STEP_LAYER):
+            assert fp8.select(M, p.N, p.K) == 0
+            if p.shards:
+                res.append(torch.cat(fp8.scaled_mm_merged(xq, wq, s, sw, list(p.shards)), dim=1))
+            else:
+                res.append(fp8.scaled_mm(xq, wq, s, sw))
+        if l in checked:
+            outs[l] = res
+    _sync()
+    for l in checked:
+        for (xq, wq, s, sw), got, p in zip(src[l], outs[l], wl.DECODE_STEP_LAYER):
+            ref, v = oracle.scaled_mm(xq, wq, s, sw, want_v=True)
+            assert_within_tolerance(host_u16(got), ref, v, f"layer {l} {p.name}")
 
 
 @pytest.mark.parametrize("arm", [0, 1])
@@ -335,3 +385,4 @@ def test_fail_closed_on_device_tensors(fp8):
     with pytest.raises(fp8.Fp8mmError) as e:
         fp8.quant(x, 1.0)
     assert e.value.status == fp8.EUNSUPPORTED
+

@@ -60,3 +60,13 @@ def test_workload_table():
     assert sum(wl.PREFILL.projections[0].shards) == wl.PREFILL.projections[0].N
     layer_bytes = sum(p.N * p.K for p in wl.DECODE_STEP_LAYER)
     assert layer_bytes * wl.DECODE_STEP_LAYERS == 23_152_558_080
+    # the pages' tower as merged launches: its projections read exactly the
+    # printed bytes/step, plus the MLP pair's ~0.996 GiB; 136 launches
+    g = json.load(open(os.path.join(GOLDEN, "tower_bytes.json")))
+    tower = sum(n * sum(p.N * p.K for p in ps) for n, ps in wl.DECODE_STEP_4B)
+    mlp = 4 * (34816 * 5120 + 5120 * 17408)
+    assert tower - mlp == g["bytes_per_step"]
+    assert round(mlp / 2 ** 30, 3) == 0.996
+    assert tower == 8_283_750_400
+    assert sum(n * len(ps) for n, ps in wl.DECODE_STEP_4B) == 136
+    assert 48 * 2 + 16 * 2 == g["vllm_merged_launches"]["total"]

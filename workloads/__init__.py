@@ -125,6 +125,12 @@ DECODE_STEP_LAYER = (Projection("qkvz", 12288, 5120),
                      Projection("down", 5120, 17408))
 DECODE_STEP = Workload(4, "decode_step_64_layers_M8", (8,), DECODE_STEP_LAYER, False, True)
 DECODE_STEP_LAYERS = 64
+# The pages' own tower (the 7.7 GiB of E4M3 a decode step reads), as (layers,
+# projections): 48 GDN layers with a merged qkvz and out_proj, 16 attention
+# layers with a merged qkv and o_proj, and the MLP pair; 136 launches.
+DECODE_STEP_4B = ((48, (Projection("in_proj_qkvz", 16384, 5120), Projection("out_proj", 5120, 6144))),
+                  (16, (Projection("qkv", 14336, 5120), Projection("o_proj", 5120, 6144))),
+                  (4, (Projection("gate_up", 34816, 5120, (17408, 17408)), Projection("down", 5120, 17408))))
 PREFILL = Workload(5, "prefill_M6576_gateup_K5120_N34816_down_K17408_N5120", (6576,),
                    (Projection("gate_up", 34816, 5120, (17408, 17408)),
                     Projection("down", 5120, 17408)), True, False)
