@@ -165,6 +165,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
 // L2 prefetch distance in stages (0: off).  Each stage load is followed by two
 // 4-byte-per-lane direct-to-LDS loads that touch every 128-byte line of the
 // stage PF stages further on, so that its real loads hit L2.
+// 1: C tile stores marked non-temporal.  The workgroups finish their tiles at
+// about the same time, and the C tiles they write (4 MB per XCD per round)
+// would otherwise displace from L2 the operand panels the next round reads;
+// measured 13% faster on the prefill gate_up shape.
+#ifndef FP8MM_LARGEM_NTSTORE
+#define FP8MM_LARGEM_NTSTORE 1
+#endif
 #ifndef FP8MM_LARGEM_PREFETCH
 #define FP8MM_LARGEM_PREFETCH 0
 #endif
@@ -443,8 +450,14 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
         if (m >= M || n >= N) continue;
         int si = 0;
         while (si + 1 < sh.num && n >= sh.start[si + 1]) ++si;
-        *reinterpret_cast<uint4*>(sh.out[si] + m * sh.ldo[si] + (n - sh.start[si])) =
-            *reinterpret_cast<const uint4*>(smem + ml * C_ROW + nl * 2);
+        const uint4 v = *reinterpret_cast<const uint4*>(smem + ml * C_ROW + nl * 2);
+        uint16_t* dst = sh.out[si] + m * sh.ldo[si] + (n - sh.start[si]);
+#if FP8MM_LARGEM_NTSTORE
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+#else
+        *reinterpret_cast<uint4*>(dst) = v;
+#endif
     }
     __syncthreads();                                   // the next tile reuses the LDS
     }

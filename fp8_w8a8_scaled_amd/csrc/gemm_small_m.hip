@@ -64,6 +64,12 @@
 #define FP8MM_SMALLM_PERSIST 1
 #endif
 
+// Cache-policy bits of the streamed weight loads: 2 = nt (streamed once,
+// non-temporal; measured faster than the default on every decode shape).
+#ifndef FP8MM_SMALLM_CPOL
+#define FP8MM_SMALLM_CPOL 2
+#endif
+
 // Persistent variant with the weight staged through per-wave LDS rings: 1 = on.
 #ifndef FP8MM_SMALLM_RING
 #define FP8MM_SMALLM_RING 1
@@ -522,9 +528,10 @@ __device__ __forceinline__ void dma_wchunk(__amdgpu_buffer_rsrc_t rw, uint8_t* s
                                            uint32_t row_off1, int chunk, bool ok)
 {
     const uint32_t c = (uint32_t)chunk * kChunk;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)slot, 16, (int)(ok ? row_off0 + c : kOob), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)slot, 16, (int)(ok ? row_off0 + c : kOob), 0, 0,
+                                             FP8MM_SMALLM_CPOL);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(slot + 1024), 16, (int)(ok ? row_off1 + c : kOob), 0,
-                                             0, 0);
+                                             0, FP8MM_SMALLM_CPOL);
 }
 
 // The A fragment (row r, logical pieces g and g+4) of a staged chunk, and the
