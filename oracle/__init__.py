@@ -71,6 +71,8 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_quant_weight.argtypes = [P, I64, I64, P, P]
     L.oracle_scaled_mm.argtypes = [P, P, F32, P, I64, I64, I64, P, I64, P]
     L.oracle_exact_acc.argtypes = [P, P, I64, I64, I64, P]
+    L.oracle_silu_mul.argtypes = [P, I64, P, I64, I64, I64, P]
+    L.oracle_silu_mul_quant.argtypes = [P, I64, P, I64, F32, I64, I64, P]
     L.oracle_num_threads.restype = ctypes.c_int
     return L
 
@@ -151,6 +153,28 @@ def act_scale(x_bf16: np.ndarray, gamma_bf16: np.ndarray | None = None, eps: flo
     M, K = x.shape
     g = None if gamma_bf16 is None else _c(gamma_bf16, np.uint16)
     return float(np.float32(lib().oracle_act_scale(_ptr(x), K, _ptr(g), float(eps), M, K)))
+
+
+def silu_mul(gate_bf16: np.ndarray, up_bf16: np.ndarray) -> np.ndarray:
+    """Unfused MLP activation: bf16 bits of fl32(silu(gate) * up), [M, I]."""
+    g = _c(gate_bf16, np.uint16)
+    u = _c(up_bf16, np.uint16)
+    M, I = g.shape
+    assert u.shape == (M, I)
+    h = np.empty((M, I), np.uint16)
+    lib().oracle_silu_mul(_ptr(g), I, _ptr(u), I, M, I, _ptr(h))
+    return h
+
+
+def silu_mul_quant(gate_bf16: np.ndarray, up_bf16: np.ndarray, s_act: float) -> np.ndarray:
+    """Fused SiLU*mul -> static E4M3 quant (one pass), uint8 codes [M, I]."""
+    g = _c(gate_bf16, np.uint16)
+    u = _c(up_bf16, np.uint16)
+    M, I = g.shape
+    assert u.shape == (M, I)
+    out = np.empty((M, I), np.uint8)
+    lib().oracle_silu_mul_quant(_ptr(g), I, _ptr(u), I, float(s_act), M, I, _ptr(out))
+    return out
 
 
 # ---------------------------------------------------------------- weights ---

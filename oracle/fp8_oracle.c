@@ -227,6 +227,52 @@ float oracle_act_scale(const uint16_t* x, int64_t ldx, const uint16_t* gamma, fl
     return amax / 448.0f;                 /* one IEEE fp32 division */
 }
 
+/* ------------------------------------------------ SiLU*mul -> FP8 ------- */
+
+/* The MLP activation between the merged gate_up projection and the down
+ * projection, quantized once for the down GEMM: h = silu(gate) * up with
+ * silu(g) = g * sigmoid(g) = g / (1 + exp(-g)).  The merged gate_up launch and
+ * its two shards: vllm.cpp #252 "SETTLED BY PAIRED TRACE" (the MLP pair), the
+ * quantize-once input of the next GEMM: vllm.cpp #417, ranked follow-ons.
+ * The pages fix no precision; the reading taken (like the RMSNorm one): silu
+ * evaluated in fp64 and rounded once to fp32, the product in fp32, the
+ * unfused activation emitting the model dtype, h_b = bf16_RNE(h), and then the
+ * static quant x_q = satRNE_E4M3(fl32(h_b / s_act)). */
+static float silu_f32(float g)
+{
+    double d = (double)g;
+    return (float)(d / (1.0 + exp(-d)));
+}
+
+/* Unfused: h_b[m,i] = bf16_RNE( fl32( silu(gate[m,i]) * up[m,i] ) ). */
+void oracle_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu,
+                     int64_t M, int64_t I, uint16_t* h)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t i = 0; i < I; ++i) {
+            float s = silu_f32(oracle_bf16_to_f32(gate[m * ldg + i]));
+            float hf = s * oracle_bf16_to_f32(up[m * ldu + i]);
+            h[m * I + i] = oracle_f32_to_bf16(hf);
+        }
+}
+
+/* Fused SiLU*mul -> static FP8 quant, written as one pass; its bytes must equal
+ * quant(silu_mul(gate, up)). */
+void oracle_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu,
+                           float s_act, int64_t M, int64_t I, unsigned char* xq)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t i = 0; i < I; ++i) {
+            double g = (double)oracle_bf16_to_f32(gate[m * ldg + i]);
+            float sig_g = (float)(g / (1.0 + exp(-g)));
+            float u = oracle_bf16_to_f32(up[m * ldu + i]);
+            float hb = oracle_bf16_to_f32(oracle_f32_to_bf16(sig_g * u));
+            xq[m * I + i] = oracle_e4m3_encode(isnan(hb) ? hb : hb / s_act);
+        }
+}
+
 /* ------------------------------------------------------- weight prep ------ */
 
 /* Per-output-channel weight quant (load time): s_w[n] = fl32(amax_k |W[n,k]| / 448)

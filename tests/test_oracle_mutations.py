@@ -43,6 +43,11 @@ MUTATIONS = {
     "weight_scale_fnuz_max": ("s = (amax == 0.0f) ? 1.0f : amax / 448.0f;", "s = (amax == 0.0f) ? 1.0f : amax / 240.0f;"),
     "bf16_truncates": ("r = nearbyint(q);\n        res = ldexp(r, ex - 8);", "r = floor(q);\n        res = ldexp(r, ex - 8);"),
     "gamma_ignored": ("float yk = xn * oracle_bf16_to_f32(gamma[k]);", "float yk = xn;"),
+    "silu_sigmoid_sign": ("return (float)(d / (1.0 + exp(-d)));", "return (float)(d / (1.0 + exp(d)));"),
+    "silu_mul_skips_bf16": ("float hb = oracle_bf16_to_f32(oracle_f32_to_bf16(sig_g * u));", "float hb = sig_g * u;"),
+    "silu_in_fp32": ("return (float)(d / (1.0 + exp(-d)));", "return (float)g / (1.0f + expf(-g));"),
+    "silu_mul_swapped": ("float hf = s * oracle_bf16_to_f32(up[m * ldu + i]);",
+                         "float hf = silu_f32(oracle_bf16_to_f32(up[m * ldu + i])) * oracle_bf16_to_f32(gate[m * ldg + i]);"),
 }
 
 PIN_TESTS = [
@@ -61,6 +66,10 @@ PIN_TESTS = [
     pins.test_rmsnorm_against_numpy_formula,
     lambda: pins.test_fused_quant_is_byte_exact_against_unfused(3, 32),
     pins.test_act_scale_and_weight_quant_definitions,
+    pins.test_silu_against_scipy_expit_all_bf16,
+    pins.test_silu_closed_forms_and_identities,
+    pins.test_silu_mul_product_and_power_of_two_scaling,
+    lambda: pins.test_silu_mul_quant_is_byte_exact_against_unfused(1),
 ]
 
 

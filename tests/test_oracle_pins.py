@@ -321,3 +321,75 @@ def test_double_rounding_trap():
     s_w = np.array([float.fromhex(s) for s in g["s_w"]], np.float32)
     out = oracle.scaled_mm(xq, wq, float.fromhex(g["s_act"]), s_w)
     assert hex(out[0, 0]) == g["out_bf16"]
+
+
+# ------------------------------------------------------ SiLU*mul -> quant --
+
+def _all_finite_bf16():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = oracle.bf16_bits_to_f32(b)
+    return b[np.isfinite(f)]
+
+
+def test_silu_against_scipy_expit_all_bf16():
+    """silu(g) for every finite bf16 g against a different routine: g * expit(g)
+    (scipy's logistic function) in fp64, rounded to fp32, then to bf16 (up = 1)."""
+    from scipy.special import expit
+    g = _all_finite_bf16().reshape(1, -1)
+    one = np.full_like(g, 0x3F80)                     # bf16 1.0
+    got = oracle.silu_mul(g, one)
+    gd = oracle.bf16_bits_to_f32(g).astype(np.float64)
+    with np.errstate(over="ignore"):
+        want = wl.to_bf16_bits((gd * expit(gd)).astype(np.float32))
+    assert np.array_equal(got, want)
+
+
+def test_silu_closed_forms_and_identities():
+    def silu(vals):
+        g = wl.to_bf16_bits(np.asarray(vals, np.float32)).reshape(1, -1)
+        return oracle.bf16_bits_to_f32(oracle.silu_mul(g, np.full_like(g, 0x3F80)))[0]
+    z = silu([0.0, -0.0])
+    assert z[0] == 0 and not np.signbit(z[0]) and z[1] == 0 and np.signbit(z[1])
+    big = np.array([32.0, 100.0, 3.0e38], np.float32)          # exp(-g) below half an ulp: silu(g) = g
+    assert np.array_equal(silu(big), oracle.bf16_bits_to_f32(wl.to_bf16_bits(big)))
+    assert np.all(silu([-100.0, -1000.0, -3.0e38]) == 0)       # g / (1 + huge) -> 0 (sign kept)
+    assert silu([1.0])[0] == np.float32(oracle.bf16_bits_to_f32(wl.to_bf16_bits(np.float32(1.0 / (1.0 + np.exp(-1.0))))))
+    # silu(g) - silu(-g) = g (sigmoid(g) + sigmoid(-g) = 1), checked in fp32 before the bf16 rounding
+    gd = np.random.Generator(np.random.PCG64(11)).normal(0, 3, 4096)
+    g = oracle.bf16_bits_to_f32(wl.to_bf16_bits(gd.astype(np.float32))).astype(np.float64)
+    sp, sm = g / (1 + np.exp(-g)), (-g) / (1 + np.exp(g))
+    assert np.allclose(sp - sm, g, rtol=0, atol=4e-16 * np.maximum(1, np.abs(g)))
+    # the minimum of silu is -0.27846454... (at g = -1.27846...): over all bf16 g
+    # the smallest bf16 output is that value rounded to bf16
+    allg = _all_finite_bf16().reshape(1, -1)
+    vals = oracle.bf16_bits_to_f32(oracle.silu_mul(allg, np.full_like(allg, 0x3F80)))
+    assert np.nanmin(vals) == oracle.bf16_bits_to_f32(wl.to_bf16_bits(np.float32(-0.2784645428)))
+
+
+def test_silu_mul_product_and_power_of_two_scaling():
+    """h = fl32(silu(g) * u): u = 2^j scales h exactly; u = -u flips its sign."""
+    g = wl.activation_bf16(3, 4, 512, outliers=True, tensor=wl.T_LAYER0 + 90)
+    u = wl.activation_bf16(3, 4, 512, outliers=False, tensor=wl.T_LAYER0 + 91)
+    h = oracle.bf16_bits_to_f32(oracle.silu_mul(g, u))
+    u4 = wl.to_bf16_bits(oracle.bf16_bits_to_f32(u) * np.float32(4.0))
+    assert np.array_equal(oracle.bf16_bits_to_f32(oracle.silu_mul(g, u4)), h * np.float32(4.0))
+    assert np.array_equal(oracle.silu_mul(g, u ^ np.uint16(0x8000)), oracle.silu_mul(g, u) ^ np.uint16(0x8000))
+    # against a numpy restatement: silu via expit (a different routine), product in fp32
+    from scipy.special import expit
+    gd = oracle.bf16_bits_to_f32(g).astype(np.float64)
+    s32 = (gd * expit(gd)).astype(np.float32)
+    assert np.array_equal(oracle.silu_mul(g, u), wl.to_bf16_bits(s32 * oracle.bf16_bits_to_f32(u)))
+
+
+@pytest.mark.parametrize("M", [1, 32])
+def test_silu_mul_quant_is_byte_exact_against_unfused(M):
+    """Fused SiLU*mul -> quant equals quant(silu_mul(gate, up)) byte for byte,
+    and the calibrated scale puts the largest |h| at +-448."""
+    I = 17408
+    g = wl.activation_bf16(3, M, I, outliers=True, tensor=wl.T_LAYER0 + 92)
+    u = wl.activation_bf16(3, M, I, outliers=True, tensor=wl.T_LAYER0 + 93)
+    h = oracle.silu_mul(g, u)
+    s = oracle.act_scale(h)
+    fused = oracle.silu_mul_quant(g, u, s)
+    assert np.array_equal(fused, oracle.quant_act(h, s))
+    assert np.abs(oracle.e4m3_table()[fused]).max() == 448.0
