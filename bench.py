@@ -73,9 +73,23 @@ def _args():
     return p.parse_args()
 
 
-def kernel_sources_hash() -> str:
+# The sources each profiled kernel is compiled from (its own file and the
+# shared device header); a traffic figure is valid only for these bytes.
+KERNEL_SOURCES = {"k_gemm_small_m": ("gemm_small_m.hip", "device_common.h"),
+                  "k_gemm_large_m": ("gemm_large_m.hip", "device_common.h"),
+                  "k_silu_mul_quant": ("quant.hip", "device_common.h")}
+
+
+def kernel_sources_hash(kernel: str | None = None) -> str:
+    """sha256 (16 hex digits) of every kernel source, or of those `kernel` is
+    built from (matched by name prefix)."""
+    if kernel is None:
+        files = sorted(glob.glob(os.path.join(CSRC, "*")))
+    else:
+        key = next(k for k in KERNEL_SOURCES if kernel.startswith(k))
+        files = [os.path.join(CSRC, f) for f in KERNEL_SOURCES[key]]
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+    for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + fh.read())
     return h.hexdigest()[:16]
@@ -122,16 +136,16 @@ def graph_time_ms(fn, n, warmup):
     return e0.elapsed_time(e1) / n
 
 
-def load_traffic(name: str):
+def load_traffic(name: str, kernel: str):
     """Bytes per launch from a committed FETCH_SIZE/WRITE_SIZE summary, or None
-    if it is missing or was taken from other kernel sources."""
+    if it is missing or was taken from other sources of `kernel`."""
     path = os.path.join(PROFILES, f"{name}.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
-    m_h = re.search(r"kernel_sources_sha256_16:\s*([0-9a-f]+)", txt)
+    m_h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_h or not m_b or m_h.group(1) != kernel_sources_hash():
+    if not m_h or not m_b or m_h.group(1) != kernel_sources_hash(kernel):
         return None
     return float(m_b.group(1))
 
@@ -167,7 +181,7 @@ def bench_decode(fp8, M, steps, warmup):
     gemm_ms = graph_time_ms(gemm, steps, warmup)
     step_bytes = gemm_bytes + quant_bytes
     achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
-    traffic = load_traffic(f"decode_gemm_M{M}_K{K}_N{N}_pmc")
+    traffic = load_traffic(f"decode_gemm_M{M}_K{K}_N{N}_pmc", "k_gemm_small_m_ring")
     return {
         "ms_per_step": ms,
         "value": step_bytes / (ms * 1e-3) / 1e9,
@@ -189,10 +203,8 @@ def bench_prefill(fp8, steps, warmup):
     wid = wl.PREFILL.wid
     x = wl.activation_bf16(wid, M, K1, outliers=False)
     g = wl.gamma_bf16(wid, K1)
-    xdn = wl.activation_bf16(wid, M, K2, outliers=False, tensor=wl.T_DOWN_X)
-    xd, gd, xdd = bf16_dev(x), bf16_dev(g), bf16_dev(xdn)
+    xd, gd = bf16_dev(x), bf16_dev(g)
     s1 = float(fp8.act_scale(xd, gd, wl.EPS).item())
-    s2 = float(fp8.act_scale(xdd).item())
     wq1, sw1 = fp8.quant_weight(f32_dev(wl.weight_f32(wid, N1, K1)))
     wq2, sw2 = fp8.quant_weight(f32_dev(wl.weight_f32(wid, N2, K2, tensor=wl.T_DOWN_W)))
     xq1 = torch.empty((M, K1), dtype=torch.uint8, device="cuda")
@@ -202,26 +214,34 @@ def bench_prefill(fp8, steps, warmup):
     down = torch.empty((M, N2), dtype=torch.bfloat16, device="cuda")
     assert fp8.select(M, N1, K1) == 1
     flops1, flops2 = 2 * M * N1 * K1, 2 * M * N2 * K2
+    # the down projection's static scale, calibrated on this input's activation
+    fp8.quant_rmsnorm(xd, gd, s1, wl.EPS, out=xq1)
+    fp8.scaled_mm_merged(xq1, wq1, s1, sw1, [N1 // 2, N1 // 2], outs=[gate, up])
+    s2 = float(fp8.act_scale_silu_mul(gate, up).item())
 
     def step(i):
         fp8.quant_rmsnorm(xd, gd, s1, wl.EPS, out=xq1)
         fp8.scaled_mm_merged(xq1, wq1, s1, sw1, [N1 // 2, N1 // 2], outs=[gate, up])
-        fp8.quant(xdd, s2, out=xq2)
+        fp8.silu_mul_quant(gate, up, s2, out=xq2)
         fp8.scaled_mm(xq2, wq2, s2, sw2, out=down)
 
     ms = graph_time_ms(step, steps, warmup)
     gu_ms = graph_time_ms(lambda i: fp8.scaled_mm_merged(xq1, wq1, s1, sw1, [N1 // 2, N1 // 2], outs=[gate, up]),
                           steps, warmup)
     dn_ms = graph_time_ms(lambda i: fp8.scaled_mm(xq2, wq2, s2, sw2, out=down), steps, warmup)
+    sq_ms = graph_time_ms(lambda i: fp8.silu_mul_quant(gate, up, s2, out=xq2), steps, warmup)
+    sq_bytes = 5 * M * K2
     ach = flops1 / (gu_ms * 1e-3) / 1e12
     return {
         "workload": f"prefill_M{M}_gateup_K{K1}_N{N1}_down_K{K2}_N{N2}",
         "value": (flops1 + flops2) / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_step": ms,
-        "step": "fused RMSNorm quant + merged gate_up GEMM + static quant + down GEMM (large-M arm), graph-replayed",
+        "step": "fused RMSNorm quant + merged gate_up GEMM + fused SiLU*mul quant + down GEMM (large-M arm), "
+                "graph-replayed",
         "gemm_tflops": {"gate_up": ach, "down": flops2 / (dn_ms * 1e-3) / 1e12},
+        "silu_mul_quant": {"us": sq_ms * 1e3, "GBs": sq_bytes / (sq_ms * 1e-3) / 1e9},
         "roofline": {"bound": "mfma", "kernel": "k_gemm_large_m_tiled (gate_up)", "achieved": ach,
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / FP8_PEAK_TFLOPS,
-                     "traffic": load_traffic("prefill_gateup_M6576_K5120_N34816_pmc"),
+                     "traffic": load_traffic("prefill_gateup_M6576_K5120_N34816_pmc", "k_gemm_large_m_tiled"),
                      "algorithmic_flops_per_launch": flops1, "avg_launch_us": gu_ms * 1e3},
     }
 
@@ -232,8 +252,9 @@ def bench_sweep(fp8, layers, M, steps, warmup, wid=4):
     (quantized on the GPU); every other layer holds device copies, so a step
     streams count x bytes from HBM (far past the Infinity Cache).  A step is,
     per layer and projection, the static quant of its bf16 input (fused
-    RMSNorm quant for the projections a norm feeds: qkv(z) and gate_up) and
-    its GEMM, at M tokens."""
+    RMSNorm quant for the projections a norm feeds: qkv(z) and gate_up; the
+    fused SiLU*mul quant of the gate_up output for down) and its GEMM, at M
+    tokens."""
     import torch
     import workloads as wl
     plan, src, step_bytes, gemm_bytes = [], {}, 0, 0
@@ -242,23 +263,35 @@ def bench_sweep(fp8, layers, M, steps, warmup, wid=4):
         for pi, p in enumerate(projs):
             t = wl.T_LAYER0 + 16 * gi + pi
             norm = p.name.startswith(("qkv", "in_proj", "gate_up"))
-            x = bf16_dev(wl.activation_bf16(wid, M, p.K, outliers=True, tensor=t))
-            gam = bf16_dev(wl.gamma_bf16(wid, p.K)) if norm else None
-            s = float((fp8.act_scale(x, gam, wl.EPS) if norm else fp8.act_scale(x)).item())
             wq, sw = fp8.quant_weight(f32_dev(wl.weight_f32(wid, p.N, p.K, tensor=t)))
             xq = torch.empty((M, p.K), dtype=torch.uint8, device="cuda")
             outs = [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for n in (p.shards or (p.N,))]
+            if p.name == "down":
+                # input: SiLU*mul of the gate_up outputs just produced
+                gu = srcs[-1]
+                assert gu[0].name == "gate_up"
+                fp8.quant_rmsnorm(gu[1], gu[2], gu[3], wl.EPS, out=gu[6])
+                fp8.scaled_mm_merged(gu[6], gu[4], gu[3], gu[5], list(gu[0].shards), outs=gu[7])
+                x, gam = tuple(gu[7]), None
+                s = float(fp8.act_scale_silu_mul(*x).item())
+            else:
+                x = bf16_dev(wl.activation_bf16(wid, M, p.K, outliers=True, tensor=t))
+                gam = bf16_dev(wl.gamma_bf16(wid, p.K)) if norm else None
+                s = float((fp8.act_scale(x, gam, wl.EPS) if norm else fp8.act_scale(x)).item())
             srcs.append((p, x, gam, s, wq, sw, xq, outs))
         for li in range(count):
             for (p, x, gam, s, wq, sw, xq, outs) in srcs:
                 plan.append((p, x, gam, s, wq if li == 0 else wq.clone(), sw, xq, outs))
-                step_bytes += p.N * p.K + 4 * p.N + M * p.K + 2 * M * p.N + 3 * M * p.K + (2 * p.K if gam is not None else 0)
+                qb = 5 * M * p.K if isinstance(x, tuple) else 3 * M * p.K + (2 * p.K if gam is not None else 0)
+                step_bytes += p.N * p.K + 4 * p.N + M * p.K + 2 * M * p.N + qb
                 gemm_bytes += p.N * p.K + 4 * p.N + M * p.K + 2 * M * p.N
     torch.cuda.synchronize()
 
     def step(i):
         for (p, x, gam, s, wq, sw, xq, outs) in plan:
-            if gam is not None:
+            if isinstance(x, tuple):
+                fp8.silu_mul_quant(x[0], x[1], s, out=xq)
+            elif gam is not None:
                 fp8.quant_rmsnorm(x, gam, s, wl.EPS, out=xq)
             else:
                 fp8.quant(x, s, out=xq)
@@ -358,7 +391,8 @@ def summarize_pmc(d, name, cmd):
     lines = [f"# {name}", "", "rocprofv3 `--pmc` (one counter per run): HBM traffic of one launch of "
              f"`{target}`, calibrated on a plain copy of {meta['copy_bytes']} bytes "
              f"(`{copy_k}`, read {meta['copy_bytes']} and written {meta['copy_bytes']}).", "",
-             f"Commands: `{cmd}`", "", f"kernel_sources_sha256_16: {kernel_sources_hash()}", "",
+             f"Commands: `{cmd}`", "", f"kernel_source_sha256_16: {kernel_sources_hash(target)} "
+             f"({', '.join(KERNEL_SOURCES[next(k for k in KERNEL_SOURCES if target.startswith(k))])})", "",
              "| counter | KiB per launch | copy KiB | scale = copy bytes / copy KiB·1024 | bytes per launch |",
              "|---|---|---|---|---|"]
     for cname, (kib, ck, fac, b, n) in res.items():

@@ -60,6 +60,8 @@ _strerror = _decl("fp8mm_strerror", [_I32], ctypes.c_char_p)
 _quant_weight = _decl("fp8_quant_weight", [_P, _I64, _I64, _P, _P, _P])
 _act_scale_ws = _decl("fp8_act_scale_workspace_bytes", [_I64, _I64], _SZ)
 _act_scale = _decl("fp8_act_scale", [_P, _I64, _P, _F32, _I64, _I64, _P, _P, _SZ, _P])
+_silu_mul_quant = _decl("fp8_silu_mul_quant", [_P, _I64, _P, _I64, _F32, _P, _I64, _I64, _P])
+_act_scale_silu_mul = _decl("fp8_act_scale_silu_mul", [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _SZ, _P])
 
 
 class Fp8mmError(RuntimeError):
@@ -144,6 +146,42 @@ def act_scale(x: torch.Tensor, gamma: Optional[torch.Tensor] = None, eps: float 
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
     _check(_act_scale(_ptr(x), ldx, _ptr(gamma), float(eps), M, K, _ptr(s), _ptr(ws), ws.numel(), _stream(x)),
            "fp8_act_scale")
+    return s
+
+
+def _gate_up(gate: torch.Tensor, up: torch.Tensor):
+    _need(gate.is_cuda and gate.dtype == torch.bfloat16 and up.is_cuda and up.dtype == torch.bfloat16,
+          "gate and up must be bf16 CUDA tensors")
+    _need(tuple(gate.shape) == tuple(up.shape) and gate.dim() == 2, "gate and up must be 2-D of equal shape")
+    return _row_major(gate, "gate"), _row_major(up, "up")
+
+
+def silu_mul_quant(gate: torch.Tensor, up: torch.Tensor, s_act: float,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """E4M3 codes [M, I] of silu(gate) * up (the bf16 MLP activation) quantized
+    with the static scale s_act; gate/up may be strided views (the two halves of
+    a merged gate_up output)."""
+    ldg, ldu = _gate_up(gate, up)
+    M, I = gate.shape
+    if out is None:
+        out = torch.empty((M, I), dtype=torch.uint8, device=gate.device)
+    out = _codes(out, "out")
+    _need(out.is_contiguous() and tuple(out.shape) == (M, I), "out must be contiguous uint8 [M, I]")
+    _check(_silu_mul_quant(_ptr(gate), ldg, _ptr(up), ldu, float(s_act), _ptr(out), M, I, _stream(gate)),
+           "fp8_silu_mul_quant")
+    return out
+
+
+def act_scale_silu_mul(gate: torch.Tensor, up: torch.Tensor) -> torch.Tensor:
+    """Static scale calibration for silu_mul_quant: device f32 [1] =
+    fl32(amax / 448) of the bf16 activation silu(gate) * up (1 if amax == 0)."""
+    ldg, ldu = _gate_up(gate, up)
+    M, I = gate.shape
+    s = torch.empty(1, dtype=torch.float32, device=gate.device)
+    nbytes = int(_act_scale_ws(M, I))
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=gate.device)
+    _check(_act_scale_silu_mul(_ptr(gate), ldg, _ptr(up), ldu, M, I, _ptr(s), _ptr(ws), ws.numel(), _stream(gate)),
+           "fp8_act_scale_silu_mul")
     return s
 
 

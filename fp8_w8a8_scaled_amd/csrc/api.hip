@@ -207,6 +207,61 @@ int fp8_quant_weight(const float* w, int64_t N, int64_t K, uint8_t* w_q, float* 
     return launch_status();
 }
 
+namespace {
+
+// Validation shared by the SiLU*mul entry points.
+int check_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, int64_t M, int64_t I,
+                   bool* empty)
+{
+    *empty = false;
+    if (M < 0 || I < 0 || ldg < I || ldu < I) return FP8MM_EINVAL;
+    if (I % 16 != 0 || ldg % 8 != 0 || ldu % 8 != 0) return FP8MM_EUNSUPPORTED;
+    if (M == 0 || I == 0) {
+        *empty = true;
+        return FP8MM_OK;
+    }
+    if (!gate || !up) return FP8MM_EINVAL;
+    if (!aligned16(gate) || !aligned16(up)) return FP8MM_EUNSUPPORTED;
+    return FP8MM_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t ab = reinterpret_cast<uintptr_t>(a), bb = reinterpret_cast<uintptr_t>(b);
+    return ab < bb + nb && bb < ab + na;
+}
+
+}  // namespace
+
+int fp8_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, float s_act,
+                       uint8_t* x_q, int64_t M, int64_t I, hipStream_t stream)
+{
+    bool empty = false;
+    const int st = check_silu_mul(gate, ldg, up, ldu, M, I, &empty);
+    if (st != FP8MM_OK) return st;
+    if (!good_scale(s_act)) return FP8MM_EINVAL;
+    if (empty) return FP8MM_OK;
+    if (!x_q) return FP8MM_EINVAL;
+    if (!aligned16(x_q)) return FP8MM_EUNSUPPORTED;
+    const size_t gb = (size_t)((M - 1) * ldg + I) * 2, ub = (size_t)((M - 1) * ldu + I) * 2, qb = (size_t)(M * I);
+    if (overlaps(x_q, qb, gate, gb) || overlaps(x_q, qb, up, ub)) return FP8MM_EINVAL;
+    fp8mm::launch_silu_mul_quant(gate, ldg, up, ldu, s_act, x_q, M, I, stream);
+    return launch_status();
+}
+
+int fp8_act_scale_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, int64_t M,
+                           int64_t I, float* s_act, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    bool empty = false;
+    const int st = check_silu_mul(gate, ldg, up, ldu, M, I, &empty);
+    if (st != FP8MM_OK) return st;
+    if (empty || !s_act) return FP8MM_EINVAL;           // no tensor to calibrate on
+    if (!workspace || workspace_bytes < fp8_act_scale_workspace_bytes(M, I)) return FP8MM_EWORKSPACE;
+    if (!aligned16(workspace)) return FP8MM_EUNSUPPORTED;
+    fp8mm::launch_act_scale_silu_mul(gate, ldg, up, ldu, M, I, s_act, static_cast<float*>(workspace), stream);
+    return launch_status();
+}
+
 size_t fp8_act_scale_workspace_bytes(int64_t M, int64_t K)
 {
     if (M <= 0 || K <= 0) return 0;

@@ -27,6 +27,10 @@ void launch_act_scale(const uint16_t* x, int64_t ldx, const uint16_t* gamma, flo
                       int64_t M, int64_t K, float* s_act, float* partial, hipStream_t stream);
 void launch_quant_weight(const float* w, int64_t N, int64_t K, uint8_t* wq, float* s_w,
                          hipStream_t stream);
+void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, float s_act,
+                           uint8_t* xq, int64_t M, int64_t I, hipStream_t stream);
+void launch_act_scale_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, int64_t M,
+                               int64_t I, float* s_act, float* partial, hipStream_t stream);
 
 // gemm_small_m.hip: memory-bound arm, M <= FP8MM_SMALL_M_MAX.
 void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,

@@ -174,6 +174,68 @@ __global__ __launch_bounds__(kQuantThreads) void k_absmax_final(
     if (threadIdx.x == 0) *s_act = (amax == 0.0f) ? 1.0f : amax / 448.0f;
 }
 
+// ---- SiLU*mul -> E4M3 (the MLP activation feeding the down projection) -----
+
+// h_b = bf16(fl32(silu(g) * u)) for 8 values (silu(g) = g / (1 + exp(-g)) in
+// fp64, rounded once to fp32), returned as fp32.
+__device__ __forceinline__ void silu_mul8(const uint4 g, const uint4 u, float h[8])
+{
+    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+    const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const double d = (double)bf16_to_f32((gw[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
+        const float s = (float)(d / (1.0 + exp(-d)));
+        const float uv = bf16_to_f32((uw[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
+        h[i] = bf16_to_f32(f32_to_bf16_rne(s * uv));
+    }
+}
+
+__global__ __launch_bounds__(kQuantThreads) void k_silu_mul_quant(
+    const uint16_t* __restrict__ gate, int64_t ldg, const uint16_t* __restrict__ up, int64_t ldu, float s_act,
+    uint8_t* __restrict__ xq, int64_t M, int64_t I)
+{
+    const int64_t nv = I >> 3, total = M * nv;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = i / nv, v = i - m * nv;
+        const uint4 g = *reinterpret_cast<const uint4*>(gate + m * ldg + v * 8);
+        const uint4 u = *reinterpret_cast<const uint4*>(up + m * ldu + v * 8);
+        float h[8];
+        silu_mul8(g, u, h);
+        uint32_t o[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t hb;
+            __builtin_memcpy(&hb, &h[j], 4);
+            // a NaN is encoded with its own sign (as the plain quant does)
+            const uint32_t c = isnan(h[j]) ? (0x7fu | ((hb >> 24) & 0x80u)) : f32_to_e4m3_sat(h[j] / s_act);
+            o[j >> 2] |= c << ((j & 3) * 8);
+        }
+        *reinterpret_cast<uint2*>(xq + m * I + v * 8) = make_uint2(o[0], o[1]);
+    }
+}
+
+__global__ __launch_bounds__(kQuantThreads) void k_absmax_silu_mul(
+    const uint16_t* __restrict__ gate, int64_t ldg, const uint16_t* __restrict__ up, int64_t ldu, int64_t M,
+    int64_t I, float* __restrict__ partial)
+{
+    __shared__ float lds[kQuantThreads / 64];
+    const int64_t nv = I >> 3, total = M * nv;
+    float amax = 0.0f;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = i / nv, v = i - m * nv;
+        float h[8];
+        silu_mul8(*reinterpret_cast<const uint4*>(gate + m * ldg + v * 8),
+                  *reinterpret_cast<const uint4*>(up + m * ldu + v * 8), h);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = finite_abs_max(amax, h[j]);
+    }
+    amax = block_max_f32(amax, lds);
+    if (threadIdx.x == 0) partial[blockIdx.x] = amax;
+}
+
 // ---- load-time per-output-channel weight quant ----------------------------
 
 __global__ __launch_bounds__(kQuantThreads) void k_quant_weight(
@@ -245,6 +307,22 @@ void launch_act_scale(const uint16_t* x, int64_t ldx, const uint16_t* gamma, flo
         hipLaunchKernelGGL(k_absmax_plain, dim3((uint32_t)np), dim3(kQuantThreads), 0, stream,
                            x, ldx, M, K, partial);
     }
+    hipLaunchKernelGGL(k_absmax_final, dim3(1), dim3(kQuantThreads), 0, stream, partial, np, s_act);
+}
+
+void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, float s_act,
+                           uint8_t* xq, int64_t M, int64_t I, hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_silu_mul_quant, dim3((uint32_t)plain_grid(M, I)), dim3(kQuantThreads), 0, stream, gate, ldg,
+                       up, ldu, s_act, xq, M, I);
+}
+
+void launch_act_scale_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, int64_t M,
+                               int64_t I, float* s_act, float* partial, hipStream_t stream)
+{
+    const int64_t np = plain_grid(M, I);
+    hipLaunchKernelGGL(k_absmax_silu_mul, dim3((uint32_t)np), dim3(kQuantThreads), 0, stream, gate, ldg, up, ldu, M,
+                       I, partial);
     hipLaunchKernelGGL(k_absmax_final, dim3(1), dim3(kQuantThreads), 0, stream, partial, np, s_act);
 }
 

@@ -103,6 +103,39 @@ int fp8_quant_rmsnorm(const uint16_t* x, int64_t ldx,
                       int64_t M, int64_t K, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * SiLU*mul -> FP8: the MLP activation between the merged gate_up projection and
+ * the down projection, quantized once for the down GEMM (the gate/up pair of
+ * the tower: vllm.cpp #252, "SETTLED BY PAIRED TRACE"; quantize-once input of
+ * the next GEMM: vllm.cpp #417, ranked follow-ons).  Per element:
+ *     s    = fl32( g / (1 + exp(-g)) )            (evaluated in fp64)
+ *     h    = bf16_RNE( fl32( s * u ) )             (the unfused activation's bf16)
+ *     x_q  = satRNE_E4M3( fl32( h / s_act ) )      (NaN h: 0x7F/0xFF)
+ * so the bytes equal fp8_quant_rmsnorm(gamma = NULL) applied to the bf16
+ * activation an unfused silu_and_mul would write.  The sign of a NaN that the
+ * arithmetic itself creates (g = -inf, 0 * inf) is not specified.
+ *
+ * gate, up : bf16 [M, I], row strides ldg, ldu (elements, >= I, multiples of
+ *            8); typically the two halves of the gate_up output (up = gate + I,
+ *            ldg = ldu = 2 I).
+ * s_act    : static per-tensor scale of the down projection's input, finite > 0.
+ * x_q      : E4M3 [M, I], contiguous; must not overlap gate or up.
+ * I % 16 == 0 and 16-byte aligned pointers (FP8MM_EUNSUPPORTED otherwise).
+ * ---------------------------------------------------------------------- */
+int fp8_silu_mul_quant(const uint16_t* gate, int64_t ldg,
+                       const uint16_t* up, int64_t ldu,
+                       float s_act, uint8_t* x_q,
+                       int64_t M, int64_t I, hipStream_t stream);
+
+/* Static scale calibration for fp8_silu_mul_quant: *s_act (DEVICE f32) =
+ * fl32(amax / 448), amax the largest finite |h| over the [M, I] activation
+ * (1 when amax == 0).  workspace: at least fp8_act_scale_workspace_bytes(M, I)
+ * bytes.  M == 0 or I == 0 is FP8MM_EINVAL (nothing to calibrate on). */
+int fp8_act_scale_silu_mul(const uint16_t* gate, int64_t ldg,
+                           const uint16_t* up, int64_t ldu,
+                           int64_t M, int64_t I, float* s_act,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Scaled FP8 GEMM with bf16 output (bmm_fp8 with scale_a = s_act, scale_b =
  * s_w, out_dtype = bf16): vllm.cpp #252 "CORRECTION"; vllm.cpp #417 Finding 1.
  *

@@ -196,3 +196,41 @@ def test_quant_validation_fails_closed(fp8):
     assert g(A, 16, 24, B, C, None) == U
     assert g(A, 0, 32, B, C, None) == fp8.OK
     assert g(None, 16, 32, B, C, None) == E
+
+
+def test_silu_mul_validation_fails_closed(fp8):
+    lib = fp8.raw_lib()
+    f = lib.fp8_silu_mul_quant
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    E, U = fp8.EINVAL, fp8.EUNSUPPORTED
+    I, L = 17408, 2 * 17408                                      # gate/up halves of a gate_up row
+    assert f(None, L, A + 2 * I, L, 0.1, B, 8, I, None) == E
+    assert f(A, L, None, L, 0.1, B, 8, I, None) == E
+    assert f(A, L, A + 2 * I, L, 0.1, None, 8, I, None) == E
+    assert f(A, I - 8, A + 2 * I, L, 0.1, B, 8, I, None) == E    # ldg < I
+    assert f(A, L, A + 2 * I, I - 8, 0.1, B, 8, I, None) == E    # ldu < I
+    assert f(A, L, A + 2 * I, L, 0.1, B, -1, I, None) == E
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        assert f(A, L, A + 2 * I, L, s, B, 8, I, None) == E
+    assert f(A, L, A + 2 * I, L, 0.1, B, 8, I - 8, None) == U    # I % 16
+    assert f(A, L + 4, A + 2 * I, L, 0.1, B, 8, I, None) == U    # ldg % 8
+    assert f(A + 2, L, A + 2 * I, L, 0.1, B, 8, I, None) == U
+    assert f(A, L, A + 2 * I + 2, L, 0.1, B, 8, I, None) == U
+    assert f(A, L, A + 2 * I, L, 0.1, B + 8, 8, I, None) == U
+    assert f(A, L, A + 2 * I, L, 0.1, A + 64, 8, I, None) == E   # x_q overlaps gate
+    assert f(A, L, A + 2 * I, L, 0.1, A + 7 * L * 2 + 2 * I, 8, I, None) == E  # x_q overlaps up's last row
+    assert f(A, L, A + 2 * I, L, 0.1, B, 0, I, None) == fp8.OK
+    assert f(A, L, A + 2 * I, L, 0.1, None, 0, I, None) == fp8.OK   # empty: nothing written
+    g = lib.fp8_act_scale_silu_mul
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    ws = int(lib.fp8_act_scale_workspace_bytes(ctypes.c_int64(8), ctypes.c_int64(I)))
+    assert ws > 0
+    assert g(A, L, A + 2 * I, L, 0, I, C, D, ws, None) == E      # nothing to calibrate on
+    assert g(A, L, A + 2 * I, L, 8, I, None, D, ws, None) == E
+    assert g(A, L, A + 2 * I, L, 8, I, C, None, ws, None) == fp8.EWORKSPACE
+    assert g(A, L, A + 2 * I, L, 8, I, C, D, ws - 4, None) == fp8.EWORKSPACE
+    assert g(A, L, A + 2 * I, L, 8, I - 8, C, D, ws, None) == U
+    assert g(A + 2, L, A + 2 * I, L, 8, I, C, D, ws, None) == U
+    assert g(A, L, A + 2 * I, L, 8, I, C, D + 8, ws, None) == U

@@ -99,6 +99,66 @@ def test_weight_quant_bit_exact(fp8, N, K):
     assert np.array_equal(host_u8(wq), owq)
 
 
+# ------------------------------------------------------ SiLU*mul -> E4M3 --
+
+def _assert_codes_equal(got, want, what=""):
+    """E4M3 codes bit-exact, except that the sign bit of a NaN code is free: the
+    sign of a NaN that the arithmetic creates (g = -inf, 0 * inf) or passes on is
+    not fixed by IEEE 754, so only the NaN positions must agree."""
+    nan_w = (want & 0x7F) == 0x7F
+    assert np.array_equal(nan_w, (got & 0x7F) == 0x7F), f"{what}: NaN positions differ"
+    diff = (got != want) & ~nan_w
+    assert not diff.any(), f"{what}: {int(diff.sum())} codes differ, first at {np.argwhere(diff)[:5].tolist()}"
+
+
+def _silu_scale_bit_exact(fp8, gate_d, up_d, gate, up):
+    s_gpu = fp8.act_scale_silu_mul(gate_d, up_d)
+    s_ref = oracle.act_scale(oracle.silu_mul(gate, up))
+    assert np.float32(s_gpu.item()).view(np.uint32) == np.float32(s_ref).view(np.uint32)
+    return s_ref
+
+
+@pytest.mark.parametrize("s_act", [1.0, 0.37, 1.0 / 448.0])
+def test_silu_mul_quant_all_bf16_patterns(fp8, s_act):
+    """Every bf16 gate pattern (inf, NaN, subnormals, the huge negatives where
+    silu underflows to -0) against unit, random and every up pattern, and every
+    up pattern against random gates."""
+    every = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    rnd = wl.activation_bf16(1, 2, 65536, outliers=True, tensor=wl.T_GATE_UP)
+    gate = np.stack([every, every, rnd[0], every])
+    up = np.stack([np.full(65536, 0x3F80, np.uint16), rnd[1], every, every[::-1]])
+    got = host_u8(fp8.silu_mul_quant(bf16_dev(gate), bf16_dev(up), s_act))
+    _assert_codes_equal(got, oracle.silu_mul_quant(gate, up, np.float32(s_act)), "all patterns")
+    _silu_scale_bit_exact(fp8, bf16_dev(gate), bf16_dev(up), gate, up)
+
+
+@pytest.mark.parametrize("wid,M,I", [(1, 3, 48), (1, 7, 208), (3, 1, 17408), (3, 8, 17408), (3, 32, 17408),
+                                     (5, 6576, 17408)])
+def test_silu_mul_quant_gate_up_halves(fp8, wid, M, I):
+    """The two halves of a merged gate_up output [M, 2I] as strided views
+    (ldg = ldu = 2I); the static scale calibrated on the GPU bit-exact."""
+    gu = wl.activation_bf16(wid, M, 2 * I, outliers=True, tensor=wl.T_GATE_UP)
+    gud = bf16_dev(gu)
+    gate_d, up_d = gud[:, :I], gud[:, I:]
+    assert gate_d.stride(0) == 2 * I
+    s = _silu_scale_bit_exact(fp8, gate_d, up_d, gu[:, :I], gu[:, I:])
+    got = host_u8(fp8.silu_mul_quant(gate_d, up_d, s))
+    _assert_codes_equal(got, oracle.silu_mul_quant(gu[:, :I], gu[:, I:], s), f"M={M} I={I}")
+
+
+def test_silu_mul_quant_zero_m_and_separate_buffers(fp8):
+    import torch
+    I = 17408
+    g = wl.activation_bf16(2, 4, I, outliers=False, tensor=wl.T_GATE_UP)
+    u = wl.activation_bf16(2, 4, I, outliers=False, tensor=wl.T_DOWN_X)
+    out = torch.full((4, I), 0xA5, dtype=torch.uint8, device="cuda")
+    fp8.silu_mul_quant(bf16_dev(g)[:0], bf16_dev(u)[:0], 0.5, out=out[:0])
+    _sync()
+    assert int((out != 0xA5).sum().item()) == 0
+    fp8.silu_mul_quant(bf16_dev(g), bf16_dev(u), 0.5, out=out)
+    _assert_codes_equal(host_u8(out), oracle.silu_mul_quant(g, u, np.float32(0.5)), "separate buffers")
+
+
 # -------------------------------------------------------------------- GEMM --
 
 def _prepare(wid, M, N, K, outliers, w_tensor=wl.T_W, x_tensor=wl.T_X):
@@ -147,10 +207,14 @@ def test_decode_mlp_merged_gate_up_and_down(fp8, M):
     ref, v = oracle.scaled_mm(xq, wq, s1, sw, want_v=True)
     got = np.concatenate([host_u16(o) for o in outs], axis=1)
     assert_within_tolerance(got, ref, v, f"gate_up M={M}")
-    # down projection on its own seeded input
-    xd = wl.activation_bf16(3, M, 17408, outliers=True, tensor=wl.T_DOWN_X)
-    s2 = oracle.act_scale(xd)
-    xq2 = oracle.quant_act(xd, s2)
+    # SiLU*mul -> E4M3 of the oracle's gate_up output (identical bytes uploaded),
+    # then the down projection on those codes
+    gate, up = ref[:, :17408], ref[:, 17408:]
+    refd = bf16_dev(ref)
+    s2 = _silu_scale_bit_exact(fp8, refd[:, :17408], refd[:, 17408:], gate, up)
+    xq2 = oracle.silu_mul_quant(gate, up, s2)
+    xq2_gpu = fp8.silu_mul_quant(refd[:, :17408], refd[:, 17408:], s2)
+    _assert_codes_equal(host_u8(xq2_gpu), xq2, f"silu_mul M={M}")
     wq2, sw2 = oracle.quant_weight(wl.weight_f32(3, 5120, 17408, tensor=wl.T_DOWN_W))
     got2 = host_u16(fp8.scaled_mm(u8_dev(xq2), u8_dev(wq2), s2, f32_dev(sw2)))
     ref2, v2 = oracle.scaled_mm(xq2, wq2, s2, sw2, want_v=True)
