@@ -1,0 +1,121 @@
+// act_tables.h -- small per-workgroup tables that replace per-element fp64 and
+// IEEE-division work in the activation quant kernels, with results identical
+// to the per-element evaluation (host-checked over every bf16 input).
+//
+// Both tables exist because the quantities are functions of one bf16 value:
+// SiLU of a bf16 gate, and the E4M3 code of a bf16 activation h under a fixed
+// static scale.  Building them costs a few thousand evaluations per
+// workgroup; the per-element path then needs one LDS read each.
+#pragma once
+
+#include "device_common.h"
+
+namespace fp8mm {
+
+// SiLU of a gate value, s = fl32( g / (1 + exp(-g)) ) with the expression in
+// fp64 (the same reading as the RMSNorm scale: wide arithmetic, one rounding).
+__device__ __host__ __forceinline__ float silu_f64(float g)
+{
+    const double d = (double)g;
+    return (float)(d / (1.0 + exp(-d)));
+}
+
+// silu_f64 of every bf16 gate as s = fma(g, m, t) with the pair (m, t) read
+// from a table.  Outside a band of magnitudes s is exact in closed form:
+//   |g| < 2^-25           s = g / 2  (g^2/4 is below half an fp32 ulp of g/2)
+//   g >= 109, +inf, +NaN  s = g      (exp(-g) < 2^-157)
+//   g <= -109, -inf, -NaN s = g * 0  (-0: |g| e^g is below half the least fp32
+//                                     subnormal; -inf / inf and NaN give NaN)
+// so the table holds, per sign, a below-band entry (0.5, -0), the band entries
+// (0, silu_f64(g)) for magnitudes [2^-25, 109) (bf16 patterns 0x3300 ..
+// 0x42D9), and an above-band entry ((1 or 0), -0).  fma(g, 0, t) = t exactly
+// (no band value is zero) and fma(g, m, -0) = g * m exactly.
+constexpr uint32_t kSiluLo = 0x3300u, kSiluBand = 0x42DAu - 0x3300u;
+constexpr int kSiluHalf = (int)kSiluBand + 2;
+constexpr int kSiluTableSize = 2 * kSiluHalf;       // (m, t) pairs
+
+__device__ __host__ __forceinline__ float2 silu_table_entry(int j)
+{
+    const uint32_t neg = j >= kSiluHalf ? 1u : 0u;
+    const int k = j - (int)neg * kSiluHalf;
+    if (k == 0) return make_float2(0.5f, -0.0f);
+    if (k == kSiluHalf - 1) return make_float2(neg ? 0.0f : 1.0f, -0.0f);
+    return make_float2(0.0f, silu_f64(bf16_to_f32((neg << 15) | (kSiluLo + (uint32_t)k - 1u))));
+}
+
+__device__ __host__ __forceinline__ uint32_t silu_table_index(uint32_t b)
+{
+    const int d = (int)(b & 0x7fffu) - (int)kSiluLo;
+    const int k = d < -1 ? -1 : (d > (int)kSiluBand ? (int)kSiluBand : d);      // a med3
+    return (uint32_t)(k + 1) + (b >> 15) * (uint32_t)kSiluHalf;
+}
+
+__device__ __host__ __forceinline__ float silu_finish(uint32_t b, float2 mt)
+{
+    return __builtin_fmaf(bf16_to_f32(b), mt.x, mt.y);
+}
+
+__device__ __host__ __forceinline__ float silu_from_table(uint32_t b, const float2* tab)
+{
+    return silu_finish(b, tab[silu_table_index(b)]);
+}
+
+// One E4M3 code of the bf16-valued h / s; a NaN h is encoded with its own sign
+// (it is not divided: the sign of a NaN out of a division is not fixed).
+__device__ __host__ __forceinline__ uint32_t quant_value(float h, float s_act)
+{
+    return f32_to_e4m3_sat(h != h ? h : h / s_act);
+}
+
+// E4M3 code of h / s_act for every bf16 pattern h: a 65,536-byte table.  Only
+// the 2 x 2560 patterns of one band of magnitudes need the division: with lo
+// the smallest bf16 magnitude >= s * 2^-11, |h| < lo gives |h/s| < 2^-11, a
+// signed zero, and |h| >= 2^20 lo (pattern lo + 2560) gives |h/s| >= 512,
+// saturated (inf too); NaN -> 0x7F | sign.  Valid for 2^-100 <= s <= 2^100
+// (lo normal, the band below inf).
+constexpr uint32_t kCodeBand = 20u * 128u;
+
+__device__ __host__ __forceinline__ bool code_table_ok(float s_act)
+{
+    return s_act >= 0x1p-100f && s_act <= 0x1p100f;
+}
+
+__device__ __host__ __forceinline__ uint32_t code_band_lo(float s_act)
+{
+    const float f = s_act * 0x1p-11f;              // exact for s >= 2^-100
+    uint32_t u;
+    __builtin_memcpy(&u, &f, 4);
+    return (u + 0xffffu) >> 16;                    // round the magnitude up to bf16
+}
+
+__device__ __host__ __forceinline__ uint32_t code_table_entry(uint32_t h, uint32_t lo, float s_act)
+{
+    const uint32_t a = h & 0x7fffu, sg = (h >> 8) & 0x80u;
+    if (a < lo) return sg;
+    if (a - lo < kCodeBand) return quant_value(bf16_to_f32(h), s_act);
+    return sg | (a > 0x7f80u ? 0x7fu : 0x7eu);
+}
+
+// fp32 -> bf16 bits, round to nearest even, NaN -> quiet NaN with its sign,
+// written without branches (same results as f32_to_bf16_rne).
+__device__ __host__ __forceinline__ uint32_t f32_to_bf16_rne_sel(float f)
+{
+    uint32_t u;
+    __builtin_memcpy(&u, &f, 4);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t q = ((u >> 16) & 0x8000u) | 0x7fc0u;
+    return (u & 0x7fffffffu) > 0x7f800000u ? q : r;
+}
+
+// fp32 -> bf16 bits, round to nearest even, NaN stays NaN: gfx950's
+// v_cvt_pk_bf16_f32 on the device, the integer form above on the host.
+__device__ __host__ __forceinline__ uint32_t f32_to_bf16_cvt(float f)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+#else
+    return f32_to_bf16_rne_sel(f);
+#endif
+}
+
+}  // namespace fp8mm

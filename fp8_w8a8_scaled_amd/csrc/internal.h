@@ -29,6 +29,21 @@ void launch_quant_weight(const float* w, int64_t N, int64_t K, uint8_t* wq, floa
                          hipStream_t stream);
 void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, float s_act,
                            uint8_t* xq, int64_t M, int64_t I, hipStream_t stream);
+// Table-based SiLU*mul quant: workgroups per CU, 16-byte pieces per thread
+// and step, next-step prefetch, non-temporal loads.
+#ifndef FP8MM_SILU_LUT_BPC
+#define FP8MM_SILU_LUT_BPC 1
+#endif
+#ifndef FP8MM_SILU_NP
+#define FP8MM_SILU_NP 2
+#endif
+#ifndef FP8MM_SILU_PF
+#define FP8MM_SILU_PF 0
+#endif
+#ifndef FP8MM_SILU_NT
+#define FP8MM_SILU_NT 0
+#endif
+bool silu_mul_uses_table(int64_t M, int64_t I, float s_act);
 void launch_act_scale_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, int64_t M,
                                int64_t I, float* s_act, float* partial, hipStream_t stream);
 

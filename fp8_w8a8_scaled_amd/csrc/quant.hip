@@ -10,6 +10,7 @@
 //
 // All kernels are memory-bound streaming passes: 16-byte bf16 loads, 8-byte
 // E4M3 stores, no LDS except for block reductions.
+#include "act_tables.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -176,21 +177,42 @@ __global__ __launch_bounds__(kQuantThreads) void k_absmax_final(
 
 // ---- SiLU*mul -> E4M3 (the MLP activation feeding the down projection) -----
 
-// h_b = bf16(fl32(silu(g) * u)) for 8 values (silu(g) = g / (1 + exp(-g)) in
-// fp64, rounded once to fp32), returned as fp32.
-__device__ __forceinline__ void silu_mul8(const uint4 g, const uint4 u, float h[8])
+// h_b = bf16(fl32(s * u)) (bits), s = silu(g) from `silu` (silu_f64 itself, or
+// its table), for the 8 gate / up values of one 16-byte load each.
+template <class Silu>
+__device__ __forceinline__ void silu_mul8(const uint4 g, const uint4 u, uint32_t hb[8], Silu silu)
 {
     const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
     const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const double d = (double)bf16_to_f32((gw[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
-        const float s = (float)(d / (1.0 + exp(-d)));
+        const float sg = silu((gw[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
         const float uv = bf16_to_f32((uw[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
-        h[i] = bf16_to_f32(f32_to_bf16_rne(s * uv));
+        hb[i] = f32_to_bf16_rne(sg * uv);
     }
 }
 
+struct SiluDirect {
+    __device__ float operator()(uint32_t b) const { return silu_f64(bf16_to_f32(b)); }
+};
+
+struct CodeDirect {
+    float s_act;
+    __device__ uint32_t operator()(uint32_t hb) const { return quant_value(bf16_to_f32(hb), s_act); }
+};
+
+template <class Silu, class Code>
+__device__ __forceinline__ uint2 silu_mul_quant8(const uint4 g, const uint4 u, Silu silu, Code code)
+{
+    uint32_t hb[8];
+    silu_mul8(g, u, hb, silu);
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j >> 2] |= code(hb[j]) << ((j & 3) * 8);
+    return make_uint2(o[0], o[1]);
+}
+
+// Few rows (decode): silu in fp64 and the IEEE division per element.
 __global__ __launch_bounds__(kQuantThreads) void k_silu_mul_quant(
     const uint16_t* __restrict__ gate, int64_t ldg, const uint16_t* __restrict__ up, int64_t ldu, float s_act,
     uint8_t* __restrict__ xq, int64_t M, int64_t I)
@@ -201,18 +223,150 @@ __global__ __launch_bounds__(kQuantThreads) void k_silu_mul_quant(
         const int64_t m = i / nv, v = i - m * nv;
         const uint4 g = *reinterpret_cast<const uint4*>(gate + m * ldg + v * 8);
         const uint4 u = *reinterpret_cast<const uint4*>(up + m * ldu + v * 8);
-        float h[8];
-        silu_mul8(g, u, h);
+        *reinterpret_cast<uint2*>(xq + m * I + v * 8) = silu_mul_quant8(g, u, SiluDirect{}, CodeDirect{s_act});
+    }
+}
+
+// Table path for NP 16-byte pieces of gate and up: every SiLU table read is
+// issued before any is used, then every code table read, so one LDS latency
+// covers 8 * NP values; nothing branches.
+template <int NP>
+__device__ __forceinline__ void silu_mul_quant_tables(const uint4 (&g)[NP], const uint4 (&u)[NP], const float2* stab,
+                                                      const uint8_t* ctab, uint2 (&out)[NP])
+{
+    constexpr int E = 8 * NP;
+    uint32_t gb[E], hb[E], c[E];
+    float2 mt[E];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const uint32_t w[4] = {g[p].x, g[p].y, g[p].z, g[p].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gb[8 * p + i] = (w[i >> 1] >> ((i & 1) * 16)) & 0xffffu;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) mt[e] = stab[silu_table_index(gb[e])];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const uint32_t w[4] = {u[p].x, u[p].y, u[p].z, u[p].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = 8 * p + i;
+            const float uv = bf16_to_f32((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
+            hb[e] = f32_to_bf16_cvt(silu_finish(gb[e], mt[e]) * uv);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) c[e] = ctab[hb[e]];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
         uint32_t o[2] = {0u, 0u};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t hb;
-            __builtin_memcpy(&hb, &h[j], 4);
-            // a NaN is encoded with its own sign (as the plain quant does)
-            const uint32_t c = isnan(h[j]) ? (0x7fu | ((hb >> 24) & 0x80u)) : f32_to_e4m3_sat(h[j] / s_act);
-            o[j >> 2] |= c << ((j & 3) * 8);
+        for (int i = 0; i < 8; ++i) o[i >> 2] |= c[8 * p + i] << ((i & 3) * 8);
+        out[p] = make_uint2(o[0], o[1]);
+    }
+}
+
+// Many rows (prefill).  Each workgroup first fills two LDS tables: the SiLU
+// (m, t) pairs (8116 fp64 evaluations) and the E4M3 code of every bf16 value
+// under s_act (65,536 bytes, 5120 of them by division).  It then streams a
+// contiguous share of the [M, I] pieces, NP per thread per step (kSiluLutThreads
+// apart, so each load instruction of a wave covers 1 KB), stepping the row and
+// column instead of dividing; with PF the next step's loads are issued before
+// this step's arithmetic.  total = M * I / 8 < 2^31.
+constexpr int kSiluLutThreads = 1024;
+
+__device__ __forceinline__ uint4 load_piece(const uint16_t* p)
+{
+#if FP8MM_SILU_NT
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(r.x, r.y, r.z, r.w);
+#else
+    return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+
+template <int NP, bool PF>
+__global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
+    const uint16_t* __restrict__ gate, int64_t ldg, const uint16_t* __restrict__ up, int64_t ldu, float s_act,
+    uint8_t* __restrict__ xq, uint32_t nv, uint32_t total, int64_t I)
+{
+    __shared__ float2 stab[kSiluTableSize];
+    __shared__ uint32_t ctab4[16384];
+    const uint32_t lo = code_band_lo(s_act);
+    for (int j = threadIdx.x; j < kSiluTableSize; j += blockDim.x) stab[j] = silu_table_entry(j);
+    for (int j = threadIdx.x; j < 16384; j += blockDim.x) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w |= code_table_entry(4u * j + k, lo, s_act) << (8 * k);
+        ctab4[j] = w;
+    }
+    __syncthreads();
+    const uint8_t* ctab = reinterpret_cast<const uint8_t*>(ctab4);
+    // this workgroup's pieces: [begin, end), a multiple of kStep long
+    constexpr uint32_t kStep = (uint32_t)NP * kSiluLutThreads;
+    const uint32_t per = ((total + gridDim.x - 1) / gridDim.x + kStep - 1) / kStep * kStep;
+    const uint32_t begin = blockIdx.x * per;
+    const uint32_t end = begin + per < total ? begin + per : total;
+    uint32_t i = begin + threadIdx.x;
+    if (i >= end) return;
+    const uint32_t dm = kStep / nv, dv = kStep - dm * nv;     // one step = dm rows + dv pieces
+    uint32_t m[NP], v[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const uint32_t ip = i + (uint32_t)p * kSiluLutThreads;
+        m[p] = ip / nv;
+        v[p] = ip - m[p] * nv;
+    }
+    // a piece at or past `end` is loaded from piece 0's address instead (a
+    // valid location), so no load needs a branch
+    uint4 g[NP], u[NP];
+    auto load_step = [&](uint32_t i_, const uint32_t (&m_)[NP], const uint32_t (&v_)[NP], uint4 (&g_)[NP],
+                         uint4 (&u_)[NP]) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const bool ok = i_ + (uint32_t)p * kSiluLutThreads < end;
+            const uint32_t mm = ok ? m_[p] : m_[0], vv = ok ? v_[p] : v_[0];
+            g_[p] = load_piece(gate + mm * ldg + vv * 8);
+            u_[p] = load_piece(up + mm * ldu + vv * 8);
         }
-        *reinterpret_cast<uint2*>(xq + m * I + v * 8) = make_uint2(o[0], o[1]);
+    };
+    auto advance = [&](uint32_t (&m_)[NP], uint32_t (&v_)[NP]) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            v_[p] += dv;
+            m_[p] += dm + (v_[p] >= nv ? 1u : 0u);
+            v_[p] -= v_[p] >= nv ? nv : 0u;
+        }
+    };
+    if (PF) load_step(i, m, v, g, u);
+    for (;;) {
+        uint32_t mn[NP], vn[NP];
+        uint4 gn[NP], un[NP];
+        const uint32_t in = i + kStep;
+        const bool more = in < end;
+        if (PF) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) mn[p] = m[p], vn[p] = v[p];
+            advance(mn, vn);
+            load_step(more ? in : i, more ? mn : m, more ? vn : v, gn, un);
+        } else {
+            load_step(i, m, v, g, u);
+        }
+        uint2 o[NP];
+        silu_mul_quant_tables<NP>(g, u, stab, ctab, o);
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            if (i + (uint32_t)p * kSiluLutThreads < end)
+                *reinterpret_cast<uint2*>(xq + (int64_t)m[p] * I + v[p] * 8) = o[p];
+        if (!more) break;
+        i = in;
+        if (PF) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) m[p] = mn[p], v[p] = vn[p], g[p] = gn[p], u[p] = un[p];
+        } else {
+            advance(m, v);
+        }
     }
 }
 
@@ -226,11 +380,11 @@ __global__ __launch_bounds__(kQuantThreads) void k_absmax_silu_mul(
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t m = i / nv, v = i - m * nv;
-        float h[8];
+        uint32_t hb[8];
         silu_mul8(*reinterpret_cast<const uint4*>(gate + m * ldg + v * 8),
-                  *reinterpret_cast<const uint4*>(up + m * ldu + v * 8), h);
+                  *reinterpret_cast<const uint4*>(up + m * ldu + v * 8), hb, SiluDirect{});
 #pragma unroll
-        for (int j = 0; j < 8; ++j) amax = finite_abs_max(amax, h[j]);
+        for (int j = 0; j < 8; ++j) amax = finite_abs_max(amax, bf16_to_f32(hb[j]));
     }
     amax = block_max_f32(amax, lds);
     if (threadIdx.x == 0) partial[blockIdx.x] = amax;
@@ -313,8 +467,22 @@ void launch_act_scale(const uint16_t* x, int64_t ldx, const uint16_t* gamma, flo
 void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, float s_act,
                            uint8_t* xq, int64_t M, int64_t I, hipStream_t stream)
 {
-    hipLaunchKernelGGL(k_silu_mul_quant, dim3((uint32_t)plain_grid(M, I)), dim3(kQuantThreads), 0, stream, gate, ldg,
-                       up, ldu, s_act, xq, M, I);
+    const int64_t total = M * (I >> 3);
+    if (silu_mul_uses_table(M, I, s_act)) {
+        const int64_t grid = (int64_t)num_cus() * FP8MM_SILU_LUT_BPC;
+        hipLaunchKernelGGL((k_silu_mul_quant_lut<FP8MM_SILU_NP, FP8MM_SILU_PF != 0>), dim3((uint32_t)grid),
+                           dim3(kSiluLutThreads), 0, stream, gate, ldg,
+                           up, ldu, s_act, xq, (uint32_t)(I >> 3), (uint32_t)total, I);
+    } else {
+        hipLaunchKernelGGL(k_silu_mul_quant, dim3((uint32_t)plain_grid(M, I)), dim3(kQuantThreads), 0, stream, gate,
+                           ldg, up, ldu, s_act, xq, M, I);
+    }
+}
+
+bool silu_mul_uses_table(int64_t M, int64_t I, float s_act)
+{
+    const int64_t total = M * (I >> 3);
+    return total >= FP8MM_SILU_TABLE_MIN_ELEMS / 8 && total < ((int64_t)1 << 31) && code_table_ok(s_act);
 }
 
 void launch_act_scale_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, int64_t M,

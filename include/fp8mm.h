@@ -120,7 +120,12 @@ int fp8_quant_rmsnorm(const uint16_t* x, int64_t ldx,
  * s_act    : static per-tensor scale of the down projection's input, finite > 0.
  * x_q      : E4M3 [M, I], contiguous; must not overlap gate or up.
  * I % 16 == 0 and 16-byte aligned pointers (FP8MM_EUNSUPPORTED otherwise).
+ * From FP8MM_SILU_TABLE_MIN_ELEMS elements on (M * I below 2^34, and
+ * 2^-100 <= s_act <= 2^100) the kernel takes silu and the E4M3 code from
+ * per-workgroup tables of the same evaluations instead of evaluating them per
+ * element; the bytes are the same.
  * ---------------------------------------------------------------------- */
+#define FP8MM_SILU_TABLE_MIN_ELEMS (1LL << 22)
 int fp8_silu_mul_quant(const uint16_t* gate, int64_t ldg,
                        const uint16_t* up, int64_t ldu,
                        float s_act, uint8_t* x_q,

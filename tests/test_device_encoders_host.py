@@ -20,12 +20,48 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 DRIVER = r"""
-#include "device_common.h"
+#include "act_tables.h"
 extern "C" void enc(const float* t, long n, unsigned char* o) {
     for (long i = 0; i < n; ++i) o[i] = (unsigned char)fp8mm::f32_to_e4m3_sat(t[i]);
 }
 extern "C" void bf(const float* t, long n, unsigned short* o) {
     for (long i = 0; i < n; ++i) o[i] = (unsigned short)fp8mm::f32_to_bf16_rne(t[i]);
+}
+extern "C" long bf_sel_mismatches_all(void) {
+    long bad = 0;
+    for (unsigned long long i = 0; i < (1ull << 32); ++i) {
+        const unsigned u = (unsigned)i;
+        float f;
+        __builtin_memcpy(&f, &u, 4);
+        bad += fp8mm::f32_to_bf16_rne_sel(f) != fp8mm::f32_to_bf16_rne(f);
+    }
+    return bad;
+}
+static float2 g_stab[fp8mm::kSiluTableSize];
+extern "C" int silu_lut_build(void) {
+    for (int j = 0; j < fp8mm::kSiluTableSize; ++j) g_stab[j] = fp8mm::silu_table_entry(j);
+    return fp8mm::kSiluTableSize;
+}
+extern "C" void silu_both(const unsigned short* b, long n, float* from_lut, float* direct) {
+    for (long i = 0; i < n; ++i) {
+        from_lut[i] = fp8mm::silu_from_table(b[i], g_stab);
+        direct[i] = fp8mm::silu_f64(fp8mm::bf16_to_f32(b[i]));
+    }
+}
+static unsigned char g_codes[65536];
+extern "C" int code_table_build(float s) {
+    if (!fp8mm::code_table_ok(s)) return -1;
+    const unsigned lo = fp8mm::code_band_lo(s);
+    for (unsigned h = 0; h < 65536; ++h) g_codes[h] = (unsigned char)fp8mm::code_table_entry(h, lo, s);
+    return (int)lo;
+}
+extern "C" void codes_from_table(const unsigned short* h, long n, unsigned char* o) {
+    for (long i = 0; i < n; ++i) o[i] = g_codes[h[i]];
+}
+extern "C" void silu_mul_codes(const unsigned short* g, const unsigned short* u, long n, float s, unsigned char* o) {
+    code_table_build(s);
+    for (long i = 0; i < n; ++i)
+        o[i] = g_codes[fp8mm::f32_to_bf16_cvt(fp8mm::silu_from_table(g[i], g_stab) * fp8mm::bf16_to_f32(u[i]))];
 }
 """
 
@@ -43,6 +79,12 @@ def dev():
     lib = ctypes.CDLL(so)
     lib.enc.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p]
     lib.bf.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p]
+    lib.silu_both.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p]
+    lib.silu_mul_codes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_float, ctypes.c_void_p]
+    lib.bf_sel_mismatches_all.restype = ctypes.c_long
+    lib.code_table_build.argtypes = [ctypes.c_float]
+    lib.codes_from_table.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p]
+    lib.silu_lut_build()
     return lib
 
 
@@ -90,3 +132,70 @@ def test_gpu_bf16_rounding_matches_oracle(dev):
     dev.bf(np.ascontiguousarray(f).ctypes.data, f.size, o.ctypes.data)
     want = np.array([oracle.f32_to_bf16(v) for v in f], np.uint16)
     assert np.array_equal(o, want)
+
+
+@pytest.mark.parametrize("s", [1.0, 0.37, 1.0 / 448.0, 0.0137, 3.0e-5, 1234.5, 2.0 ** -100, 2.0 ** 100,
+                               float(np.nextafter(np.float32(2.0 ** -100), np.float32(1))), 1.0e-30, 7.0e29])
+def test_code_table_equals_plain_quant_for_every_bf16(dev, s):
+    """The GPU's E4M3 code table (divisions only for one band of bf16
+    magnitudes, signed zero below it, saturation above) against the oracle's
+    static quant of all 65,536 bf16 patterns: bit-exact, NaN signs included."""
+    s = np.float32(s)
+    assert dev.code_table_build(s) > 0
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = np.empty(65536, np.uint8)
+    dev.codes_from_table(h.ctypes.data, h.size, got.ctypes.data)
+    want = oracle.quant_act(h[None], s)[0]
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(hex(h[i]), hex(got[i]), hex(want[i])) for i in bad[:8]]
+
+
+def test_code_table_refuses_scales_outside_its_range(dev):
+    for s in (2.0 ** -101, 2.0 ** 101, 1e-40):
+        assert dev.code_table_build(np.float32(s)) == -1
+
+
+def bf16_value(b):
+    return float(np.array([b << 16], np.uint32).view(np.float32)[0])
+
+
+def test_silu_table_equals_direct_fp64_for_every_bf16_gate(dev):
+    """The GPU's SiLU table, s = fma(g, m, t) with (m, t) from the table, gives
+    the same fp32 bits as the direct fp64 evaluation for all 65,536 gates."""
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    lut, direct = np.empty(65536, np.float32), np.empty(65536, np.float32)
+    dev.silu_both(b.ctypes.data, b.size, lut.ctypes.data, direct.ctypes.data)
+    nan = np.isnan(direct)
+    assert np.array_equal(nan, np.isnan(lut))
+    assert np.array_equal(lut.view(np.uint32)[~nan], direct.view(np.uint32)[~nan])
+    # the closed-form regions are exercised: -0 from -109 down, g itself from 109
+    # on, g/2 below 2^-25 (signed zeros kept)
+    assert lut[0xC2DA].view(np.uint32) == 0x80000000 and lut[0x42DA] == np.float32(109.0)
+    assert np.isnan(lut[0xFF80]) and lut[0x7F80] == np.inf
+    assert lut[0x8000].view(np.uint32) == 0x80000000 and lut[0x0000].view(np.uint32) == 0
+    assert lut[0x32FF] == np.float32(bf16_value(0x32FF) / 2)
+
+
+def test_silu_mul_quant_device_logic_matches_oracle(dev):
+    """The table-based SiLU*mul -> E4M3 of the GPU, run on the host, against the
+    oracle's fused function for every gate pattern times unit, random and every
+    up pattern (NaN codes compared up to their sign)."""
+    every = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    rnd = np.random.Generator(np.random.PCG64(11)).standard_normal(65536).astype(np.float32)
+    rnd_b = (rnd.view(np.uint32) >> 16).astype(np.uint16)        # truncation is fine: any bf16 pattern will do
+    gate = np.concatenate([every, every, every, rnd_b])
+    up = np.concatenate([np.full(65536, 0x3F80, np.uint16), rnd_b, every[::-1].copy(), every])
+    for s in (1.0, 0.37, 1.0 / 448.0):
+        got = np.empty(gate.size, np.uint8)
+        dev.silu_mul_codes(gate.ctypes.data, up.ctypes.data, gate.size, s, got.ctypes.data)
+        want = oracle.silu_mul_quant(gate[None], up[None], np.float32(s))[0]
+        nan_w = (want & 0x7F) == 0x7F
+        assert np.array_equal(nan_w, (got & 0x7F) == 0x7F)
+        bad = np.flatnonzero((got != want) & ~nan_w)
+        assert bad.size == 0, [(hex(gate[i]), hex(up[i]), hex(got[i]), hex(want[i])) for i in bad[:8]]
+
+
+def test_branch_free_bf16_rounding_equals_the_plain_one_on_every_fp32(dev):
+    """f32_to_bf16_rne_sel (the select form the table kernel uses) against
+    f32_to_bf16_rne on all 2^32 fp32 patterns."""
+    assert dev.bf_sel_mismatches_all() == 0

@@ -118,18 +118,29 @@ def _silu_scale_bit_exact(fp8, gate_d, up_d, gate, up):
     return s_ref
 
 
+def _silu_table_min_elems():
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fp8mm.h")).read()
+    return int(eval(re.search(r"#define FP8MM_SILU_TABLE_MIN_ELEMS \((.*)\)", hdr).group(1).replace("LL", "")))
+
+
 @pytest.mark.parametrize("s_act", [1.0, 0.37, 1.0 / 448.0])
-def test_silu_mul_quant_all_bf16_patterns(fp8, s_act):
+@pytest.mark.parametrize("rows", [4, 64])
+def test_silu_mul_quant_all_bf16_patterns(fp8, s_act, rows):
     """Every bf16 gate pattern (inf, NaN, subnormals, the huge negatives where
     silu underflows to -0) against unit, random and every up pattern, and every
-    up pattern against random gates."""
+    up pattern against random gates; 4 rows take the per-element fp64 silu, 64
+    rows (2^22 elements) the table path."""
     every = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     rnd = wl.activation_bf16(1, 2, 65536, outliers=True, tensor=wl.T_GATE_UP)
-    gate = np.stack([every, every, rnd[0], every])
-    up = np.stack([np.full(65536, 0x3F80, np.uint16), rnd[1], every, every[::-1]])
+    gate = np.tile(np.stack([every, every, rnd[0], every]), (rows // 4, 1))
+    up = np.tile(np.stack([np.full(65536, 0x3F80, np.uint16), rnd[1], every, every[::-1]]), (rows // 4, 1))
+    assert (rows * 65536 >= _silu_table_min_elems()) == (rows == 64)
     got = host_u8(fp8.silu_mul_quant(bf16_dev(gate), bf16_dev(up), s_act))
-    _assert_codes_equal(got, oracle.silu_mul_quant(gate, up, np.float32(s_act)), "all patterns")
-    _silu_scale_bit_exact(fp8, bf16_dev(gate), bf16_dev(up), gate, up)
+    _assert_codes_equal(got, oracle.silu_mul_quant(gate, up, np.float32(s_act)), f"all patterns, {rows} rows")
+    if rows == 4:
+        _silu_scale_bit_exact(fp8, bf16_dev(gate), bf16_dev(up), gate, up)
 
 
 @pytest.mark.parametrize("wid,M,I", [(1, 3, 48), (1, 7, 208), (3, 1, 17408), (3, 8, 17408), (3, 32, 17408),
