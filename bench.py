@@ -65,7 +65,7 @@ def _args():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--summarize-trace", metavar="DIR")
     p.add_argument("--summarize-pmc", metavar="DIR")
-    p.add_argument("--pmc-driver", choices=["decode", "prefill"],
+    p.add_argument("--pmc-driver", choices=["decode", "prefill", "prefill_f32"],
                    help="run a known-size copy, then a few launches of one GEMM (for rocprofv3 --pmc)")
     p.add_argument("--meta-out", metavar="DIR")
     p.add_argument("--name")
@@ -75,9 +75,9 @@ def _args():
 
 # The sources each profiled kernel is compiled from (its own file and the
 # shared device header); a traffic figure is valid only for these bytes.
-KERNEL_SOURCES = {"k_gemm_small_m": ("gemm_small_m.hip", "device_common.h"),
-                  "k_gemm_large_m": ("gemm_large_m.hip", "device_common.h"),
-                  "k_silu_mul_quant": ("quant.hip", "device_common.h")}
+KERNEL_SOURCES = {"k_gemm_small_m": ("gemm_small_m.hip", "device_common.h", "out_store.h", "internal.h"),
+                  "k_gemm_large_m": ("gemm_large_m.hip", "device_common.h", "out_store.h", "internal.h"),
+                  "k_silu_mul_quant": ("quant.hip", "device_common.h", "act_tables.h", "internal.h")}
 
 
 def kernel_sources_hash(kernel: str | None = None) -> str:
@@ -229,6 +229,12 @@ def bench_prefill(fp8, steps, warmup):
     gu_ms = graph_time_ms(lambda i: fp8.scaled_mm_merged(xq1, wq1, s1, sw1, [N1 // 2, N1 // 2], outs=[gate, up]),
                           steps, warmup)
     dn_ms = graph_time_ms(lambda i: fp8.scaled_mm(xq2, wq2, s2, sw2, out=down), steps, warmup)
+    # A/B: the same merged gate_up launch with F32 outputs (twice the output bytes)
+    gate32 = torch.empty((M, N1 // 2), dtype=torch.float32, device="cuda")
+    up32 = torch.empty((M, N1 // 2), dtype=torch.float32, device="cuda")
+    gu32_ms = graph_time_ms(lambda i: fp8.scaled_mm_merged(xq1, wq1, s1, sw1, [N1 // 2, N1 // 2],
+                                                           outs=[gate32, up32]), steps, warmup)
+    del gate32, up32
     sq_ms = graph_time_ms(lambda i: fp8.silu_mul_quant(gate, up, s2, out=xq2), steps, warmup)
     sq_bytes = 5 * M * K2
     ach = flops1 / (gu_ms * 1e-3) / 1e12
@@ -239,6 +245,12 @@ def bench_prefill(fp8, steps, warmup):
                 "graph-replayed",
         "gemm_tflops": {"gate_up": ach, "down": flops2 / (dn_ms * 1e-3) / 1e12},
         "silu_mul_quant": {"us": sq_ms * 1e3, "GBs": sq_bytes / (sq_ms * 1e-3) / 1e9},
+        "f32_out_ab": {"gate_up_bf16_us": gu_ms * 1e3, "gate_up_f32_us": gu32_ms * 1e3,
+                       "out_bytes_bf16": 2 * M * N1, "out_bytes_f32": 4 * M * N1,
+                       "f32_over_bf16_time": gu32_ms / gu_ms,
+                       "traffic_bf16": load_traffic("prefill_gateup_M6576_K5120_N34816_pmc", "k_gemm_large_m_tiled"),
+                       "traffic_f32": load_traffic("prefill_gateup_f32out_M6576_K5120_N34816_pmc",
+                                                   "k_gemm_large_m_tiled")},
         "roofline": {"bound": "mfma", "kernel": "k_gemm_large_m_tiled (gate_up)", "achieved": ach,
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / FP8_PEAK_TFLOPS,
                      "traffic": load_traffic("prefill_gateup_M6576_K5120_N34816_pmc", "k_gemm_large_m_tiled"),
@@ -438,12 +450,14 @@ def pmc_driver(fp8, which, meta_dir):
         s1 = float(fp8.act_scale(xd, gd, wl.EPS).item())
         wq, sw = fp8.quant_weight(f32_dev(wl.weight_f32(wl.PREFILL.wid, N, K)))
         xq = fp8.quant_rmsnorm(xd, gd, s1, wl.EPS)
+        odt = torch.float32 if which == "prefill_f32" else torch.bfloat16
+        outs = [torch.empty((M, N // 2), dtype=odt, device="cuda") for _ in range(2)]
         torch.cuda.synchronize()
         for _ in range(3):
-            fp8.scaled_mm_merged(xq, wq, s1, sw, [N // 2, N // 2])
+            fp8.scaled_mm_merged(xq, wq, s1, sw, [N // 2, N // 2], outs=outs)
         kernel = "k_gemm_large_m_tiled"
     torch.cuda.synchronize()
-    alg = N * K + 4 * N + M * K + 2 * M * N
+    alg = N * K + 4 * N + M * K + (4 if which == "prefill_f32" else 2) * M * N
     os.makedirs(meta_dir, exist_ok=True)
     json.dump({"kernel": kernel, "copy_kernel": "elementwise_kernel", "copy_bytes": nbytes, "algorithmic_bytes": alg},
               open(os.path.join(meta_dir, "pmc_meta.json"), "w"))

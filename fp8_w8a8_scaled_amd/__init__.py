@@ -51,6 +51,9 @@ _quant_rmsnorm = _decl("fp8_quant_rmsnorm", [_P, _I64, _P, _F32, _F32, _P, _I64,
 _scaled_mm = _decl("fp8_scaled_mm", [_P, _P, _F32, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P])
 _scaled_mm_arm = _decl("fp8_scaled_mm_arm", [_P, _P, _F32, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _SZ, _P])
 _scaled_mm_merged = _decl("fp8_scaled_mm_merged", [_P, _P, _F32, _P, ctypes.POINTER(Shard), _I32, _I64, _I64, _P, _SZ, _P])
+_scaled_mm_f32 = _decl("fp8_scaled_mm_f32", [_P, _P, _F32, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P])
+_scaled_mm_merged_f32 = _decl("fp8_scaled_mm_merged_f32",
+                              [_P, _P, _F32, _P, ctypes.POINTER(Shard), _I32, _I64, _I64, _P, _SZ, _P])
 _workspace_bytes = _decl("fp8_scaled_mm_workspace_bytes", [_I64, _I64, _I64], _SZ)
 _select = _decl("fp8_scaled_mm_select", [_I64, _I64, _I64])
 _set_threshold = _decl("fp8_set_large_m_threshold", [_I64])
@@ -224,20 +227,31 @@ def _workspace(M, N, K, device, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+def _out_dtype(out_dtype):
+    _need(out_dtype in (torch.bfloat16, torch.float32), "out_dtype must be torch.bfloat16 or torch.float32")
+    return out_dtype
+
+
 def scaled_mm(x_q: torch.Tensor, w_q: torch.Tensor, s_act: float, s_w: torch.Tensor,
               out: Optional[torch.Tensor] = None, arm: Optional[int] = None,
-              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """bf16 [M, N] = bf16((x_q . w_q^T) * s_act * s_w).  arm None = dispatcher,
-    0 = force the small-M kernel, 1 = force the large-M kernel."""
+              workspace: Optional[torch.Tensor] = None, out_dtype=None) -> torch.Tensor:
+    """[M, N] = (x_q . w_q^T) * s_act * s_w, as bf16 (default) or f32
+    (out_dtype=torch.float32, or an f32 ``out``).  arm None = dispatcher,
+    0 = force the small-M kernel, 1 = force the large-M kernel (bf16 only)."""
     x_q, w_q = _gemm_args(x_q, w_q, s_w)
     M, K = x_q.shape
     N = w_q.shape[0]
+    dt = _out_dtype(out_dtype or (out.dtype if out is not None else torch.bfloat16))
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=x_q.device)
-    _need(out.dtype == torch.bfloat16 and out.is_cuda and out.shape == (M, N), "out must be bf16 [M, N]")
+        out = torch.empty((M, N), dtype=dt, device=x_q.device)
+    _need(out.dtype == dt and out.is_cuda and out.shape == (M, N), f"out must be {dt} [M, N]")
     ldo = _row_major(out, "out")
     ws, wsb = _workspace(M, N, K, x_q.device, workspace)
-    if arm is None:
+    if dt == torch.float32:
+        _need(arm is None, "arm forcing is bf16-only")
+        st = _scaled_mm_f32(_ptr(x_q), _ptr(w_q), float(s_act), _ptr(s_w), _ptr(out), ldo, M, N, K,
+                            _ptr(ws), wsb, _stream(x_q))
+    elif arm is None:
         st = _scaled_mm(_ptr(x_q), _ptr(w_q), float(s_act), _ptr(s_w), _ptr(out), ldo, M, N, K,
                         _ptr(ws), wsb, _stream(x_q))
     else:
@@ -249,22 +263,24 @@ def scaled_mm(x_q: torch.Tensor, w_q: torch.Tensor, s_act: float, s_w: torch.Ten
 
 def scaled_mm_merged(x_q: torch.Tensor, w_q: torch.Tensor, s_act: float, s_w: torch.Tensor,
                      shard_sizes: Sequence[int], outs: Optional[Sequence[torch.Tensor]] = None,
-                     workspace: Optional[torch.Tensor] = None):
+                     workspace: Optional[torch.Tensor] = None, out_dtype=None):
     """One launch over a concatenated weight [sum n_i, K]; returns the list of
-    bf16 [M, n_i] shard outputs (or fills ``outs``)."""
+    [M, n_i] shard outputs, bf16 (default) or f32 (or fills ``outs``)."""
     x_q, w_q = _gemm_args(x_q, w_q, s_w)
     M, K = x_q.shape
     _need(sum(shard_sizes) == w_q.shape[0], "shard sizes must sum to the weight rows")
     _need(1 <= len(shard_sizes) <= MAX_SHARDS, f"1..{MAX_SHARDS} shards")
+    dt = _out_dtype(out_dtype or (outs[0].dtype if outs else torch.bfloat16))
     if outs is None:
-        outs = [torch.empty((M, n), dtype=torch.bfloat16, device=x_q.device) for n in shard_sizes]
+        outs = [torch.empty((M, n), dtype=dt, device=x_q.device) for n in shard_sizes]
     arr = (Shard * len(shard_sizes))()
     for i, (n, o) in enumerate(zip(shard_sizes, outs)):
-        _need(o.dtype == torch.bfloat16 and o.is_cuda and o.shape == (M, n), "shard outputs must be bf16 [M, n_i]")
+        _need(o.dtype == dt and o.is_cuda and o.shape == (M, n), f"shard outputs must be {dt} [M, n_i]")
         arr[i] = Shard(int(n), o.data_ptr(), _row_major(o, "out"))
     ws, wsb = _workspace(M, w_q.shape[0], K, x_q.device, workspace)
-    _check(_scaled_mm_merged(_ptr(x_q), _ptr(w_q), float(s_act), _ptr(s_w), arr, len(shard_sizes), M, K,
-                             _ptr(ws), wsb, _stream(x_q)), "fp8_scaled_mm_merged")
+    fn = _scaled_mm_merged_f32 if dt == torch.float32 else _scaled_mm_merged
+    _check(fn(_ptr(x_q), _ptr(w_q), float(s_act), _ptr(s_w), arr, len(shard_sizes), M, K,
+              _ptr(ws), wsb, _stream(x_q)), "fp8_scaled_mm_merged")
     return list(outs)
 
 

@@ -43,9 +43,17 @@ int launch_status()
     return e == hipSuccess ? FP8MM_OK : FP8MM_ELAUNCH;
 }
 
-// Shared validation of the GEMM operands; fills the shard table.
+// One output shard of either output type.
+struct OutShard {
+    int64_t n;
+    void* out;
+    int64_t ldo;
+};
+
+// Shared validation of the GEMM operands; fills the shard table.  Rows of an
+// output start 16-byte aligned: ldo a multiple of 8 (bf16) or 4 (f32).
 int check_gemm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,
-               const fp8_shard_t* shards, int num_shards, int64_t M, int64_t K,
+               const OutShard* shards, int num_shards, bool f32, int64_t M, int64_t K,
                fp8mm::ShardTable* tab, int64_t* N_out)
 {
     // Sizes and scalars first; an empty product (M == 0 or N == 0) is a no-op
@@ -54,11 +62,12 @@ int check_gemm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float*
     if (!good_scale(s_act)) return FP8MM_EINVAL;
     int64_t N = 0;
     tab->num = num_shards;
+    tab->f32 = f32 ? 1 : 0;
     for (int i = 0; i < num_shards; ++i) {
-        const fp8_shard_t& s = shards[i];
+        const OutShard& s = shards[i];
         if (s.n < 0 || s.ldo < s.n) return FP8MM_EINVAL;
         if (M > 0 && s.n > 0 && !s.out) return FP8MM_EINVAL;
-        if (s.n % 16 != 0 || s.ldo % 8 != 0 || !aligned16(s.out)) return FP8MM_EUNSUPPORTED;
+        if (s.n % 16 != 0 || s.ldo % (f32 ? 4 : 8) != 0 || !aligned16(s.out)) return FP8MM_EUNSUPPORTED;
         tab->start[i] = N;
         tab->out[i] = s.out;
         tab->ldo[i] = s.ldo;
@@ -77,12 +86,12 @@ int check_gemm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float*
 }
 
 int run_gemm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,
-             const fp8_shard_t* shards, int num_shards, int64_t M, int64_t K, int arm,
+             const OutShard* shards, int num_shards, bool f32, int64_t M, int64_t K, int arm,
              void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     fp8mm::ShardTable tab{};
     int64_t N = 0;
-    int st = check_gemm(x_q, w_q, s_act, s_w, shards, num_shards, M, K, &tab, &N);
+    int st = check_gemm(x_q, w_q, s_act, s_w, shards, num_shards, f32, M, K, &tab, &N);
     if (st != FP8MM_OK) return st;
     if (workspace_bytes < fp8_scaled_mm_workspace_bytes(M, N, K)) return FP8MM_EWORKSPACE;
     (void)workspace;
@@ -127,8 +136,8 @@ int fp8_scaled_mm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const flo
                   void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (N < 0) return FP8MM_EINVAL;
-    const fp8_shard_t one{N, out, ldo};
-    return run_gemm(x_q, w_q, s_act, s_w, &one, 1, M, K, -1, workspace, workspace_bytes, stream);
+    const OutShard one{N, out, ldo};
+    return run_gemm(x_q, w_q, s_act, s_w, &one, 1, false, M, K, -1, workspace, workspace_bytes, stream);
 }
 
 int fp8_scaled_mm_arm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,
@@ -137,15 +146,37 @@ int fp8_scaled_mm_arm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const
 {
     if (N < 0 || (arm != 0 && arm != 1)) return FP8MM_EINVAL;
     if (arm == 0 && M > FP8MM_SMALL_M_MAX) return FP8MM_EINVAL;
-    const fp8_shard_t one{N, out, ldo};
-    return run_gemm(x_q, w_q, s_act, s_w, &one, 1, M, K, arm, workspace, workspace_bytes, stream);
+    const OutShard one{N, out, ldo};
+    return run_gemm(x_q, w_q, s_act, s_w, &one, 1, false, M, K, arm, workspace, workspace_bytes, stream);
 }
 
 int fp8_scaled_mm_merged(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,
                          const fp8_shard_t* shards, int num_shards, int64_t M, int64_t K,
                          void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    return run_gemm(x_q, w_q, s_act, s_w, shards, num_shards, M, K, -1, workspace, workspace_bytes, stream);
+    if (!shards || num_shards < 1 || num_shards > FP8MM_MAX_SHARDS) return FP8MM_EINVAL;
+    OutShard tab[FP8MM_MAX_SHARDS];
+    for (int i = 0; i < num_shards; ++i) tab[i] = OutShard{shards[i].n, shards[i].out, shards[i].ldo};
+    return run_gemm(x_q, w_q, s_act, s_w, tab, num_shards, false, M, K, -1, workspace, workspace_bytes, stream);
+}
+
+int fp8_scaled_mm_f32(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,
+                      float* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (N < 0) return FP8MM_EINVAL;
+    const OutShard one{N, out, ldo};
+    return run_gemm(x_q, w_q, s_act, s_w, &one, 1, true, M, K, -1, workspace, workspace_bytes, stream);
+}
+
+int fp8_scaled_mm_merged_f32(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,
+                             const fp8_shard_f32_t* shards, int num_shards, int64_t M, int64_t K,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!shards || num_shards < 1 || num_shards > FP8MM_MAX_SHARDS) return FP8MM_EINVAL;
+    OutShard tab[FP8MM_MAX_SHARDS];
+    for (int i = 0; i < num_shards; ++i) tab[i] = OutShard{shards[i].n, shards[i].out, shards[i].ldo};
+    return run_gemm(x_q, w_q, s_act, s_w, tab, num_shards, true, M, K, -1, workspace, workspace_bytes, stream);
 }
 
 size_t fp8_scaled_mm_workspace_bytes(int64_t M, int64_t N, int64_t K)

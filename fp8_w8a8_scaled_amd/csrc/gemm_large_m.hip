@@ -15,6 +15,7 @@
 // on store.  The epilogue scales in fp32 and stores bf16.
 #include "device_common.h"
 #include "internal.h"
+#include "out_store.h"
 
 namespace fp8mm {
 
@@ -111,17 +112,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
     for (int j = 0; j < 2; ++j) {
         const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
         if (n >= N) continue;
-        int si = 0;
-        while (si + 1 < sh.num && n >= sh.start[si + 1]) ++si;
-        uint16_t* o = sh.out[si] + (n - sh.start[si]);
-        const int64_t ldo = sh.ldo[si];
+        const int si = shard_of(sh, n);
         const float swn = s_w[n];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (m < M) o[m * ldo] = (uint16_t)f32_to_bf16_rne((acc[i][j][v] * s_act) * swn);
+                if (m < M) store_out1(sh, si, m, n, (acc[i][j][v] * s_act) * swn);
             }
     }
 }
@@ -410,7 +408,8 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     if (g < nsub) one(g, fa, fb);                      // odd number of sub-steps
 
     // Epilogue: scale, round to bf16, stage the 256x256 tile in LDS (rows of
-    // m, padded), then store rows with 16-byte, row-contiguous writes.
+    // m, padded), then store rows with 16-byte, row-contiguous writes (an f32
+    // output in two halves: a whole f32 tile would not fit in LDS).
     __builtin_amdgcn_s_waitcnt(0);                     // retire the trailing (unused) stage loads
     __syncthreads();                                   // every stage read by every wave
     const int fr = lane & 31, fh = lane >> 5;
@@ -424,6 +423,48 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
             const int64_t n = n0 + wn * 128 + i * 32 + 8 * q + 4 * fh;
             swv[i][q] = *reinterpret_cast<const float4*>(s_w + (n < N ? n : 0));
         }
+    if (sh.f32) {
+        // f32: the tile in two halves of 128 rows (the waves with wm == h hold
+        // half h), each staged in LDS and stored with row-contiguous 16-byte writes
+        constexpr int C_ROW32 = T2 * 4 + 16;
+        static_assert(T2 / 2 * C_ROW32 <= LM_LDS, "f32 half tile must fit the LDS");
+        for (int h = 0; h < 2; ++h) {
+            if (wm == h) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int nl = wn * 128 + i * 32 + 8 * q + 4 * fh;
+                        const float4 sw = swv[i][q];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const v16f& c = acc[i][j];
+                            *reinterpret_cast<float4*>(smem + (j * 32 + fr) * C_ROW32 + nl * 4) =
+                                make_float4((c[4 * q + 0] * s_act) * sw.x, (c[4 * q + 1] * s_act) * sw.y,
+                                            (c[4 * q + 2] * s_act) * sw.z, (c[4 * q + 3] * s_act) * sw.w);
+                        }
+                    }
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int c = threadIdx.x; c < T2 / 2 * T2 / 4; c += 256) {
+                const int ml = c >> 6, nl = (c & 63) * 4;
+                const int64_t m = m0 + h * (T2 / 2) + ml, n = n0 + nl;
+                if (m >= M || n >= N) continue;
+                const int si = shard_of(sh, n);
+                const uint4 v = *reinterpret_cast<const uint4*>(smem + ml * C_ROW32 + nl * 4);
+                float* dst = static_cast<float*>(sh.out[si]) + m * sh.ldo[si] + (n - sh.start[si]);
+#if FP8MM_LARGEM_NTSTORE
+                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+#else
+                *reinterpret_cast<uint4*>(dst) = v;
+#endif
+            }
+            __syncthreads();                           // the LDS is reused (next half, next tile)
+        }
+        continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -448,10 +489,9 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
         const int ml = c >> 5, nl = (c & 31) * 8;
         const int64_t m = m0 + ml, n = n0 + nl;
         if (m >= M || n >= N) continue;
-        int si = 0;
-        while (si + 1 < sh.num && n >= sh.start[si + 1]) ++si;
+        const int si = shard_of(sh, n);
         const uint4 v = *reinterpret_cast<const uint4*>(smem + ml * C_ROW + nl * 2);
-        uint16_t* dst = sh.out[si] + m * sh.ldo[si] + (n - sh.start[si]);
+        uint16_t* dst = static_cast<uint16_t*>(sh.out[si]) + m * sh.ldo[si] + (n - sh.start[si]);
 #if FP8MM_LARGEM_NTSTORE
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
         __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));

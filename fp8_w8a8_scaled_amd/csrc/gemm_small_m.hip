@@ -27,6 +27,7 @@
 //  order is the same for a merged call and a per-shard call: bitwise identical.
 #include "device_common.h"
 #include "internal.h"
+#include "out_store.h"
 
 // Tuning knobs (build-time).  Target chunks per wave -> waves per workgroup.
 #ifndef FP8MM_SMALLM_CPW
@@ -196,12 +197,9 @@ __device__ __forceinline__ void reduce_store(const v4f* red, int W, int64_t n0, 
             s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
         }
         const int64_t n = nt0 + 4 * (l >> 4);
-        int i = 0;
-        while (i + 1 < sh.num && nt0 >= sh.start[i + 1]) ++i;
         const float4 sw = *reinterpret_cast<const float4*>(s_w + n);
-        const uint32_t o0 = f32_to_bf16_rne((s.x * s_act) * sw.x) | (f32_to_bf16_rne((s.y * s_act) * sw.y) << 16);
-        const uint32_t o1 = f32_to_bf16_rne((s.z * s_act) * sw.z) | (f32_to_bf16_rne((s.w * s_act) * sw.w) << 16);
-        *reinterpret_cast<uint2*>(sh.out[i] + (int64_t)m * sh.ldo[i] + (n - sh.start[i])) = make_uint2(o0, o1);
+        store_out4(sh, shard_of(sh, nt0), m, n, (s.x * s_act) * sw.x, (s.y * s_act) * sw.y, (s.z * s_act) * sw.z,
+                   (s.w * s_act) * sw.w);
     }
 }
 
@@ -419,11 +417,8 @@ __device__ __forceinline__ void reduce_tile(const v4f* red, int stride, int slot
         s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
     }
     const int64_t n = n0 + 4 * (lane >> 4);
-    int i = 0;
-    while (i + 1 < sh.num && n0 >= sh.start[i + 1]) ++i;
-    const uint32_t o0 = f32_to_bf16_rne((s.x * s_act) * sw.x) | (f32_to_bf16_rne((s.y * s_act) * sw.y) << 16);
-    const uint32_t o1 = f32_to_bf16_rne((s.z * s_act) * sw.z) | (f32_to_bf16_rne((s.w * s_act) * sw.w) << 16);
-    *reinterpret_cast<uint2*>(sh.out[i] + (int64_t)m * sh.ldo[i] + (n - sh.start[i])) = make_uint2(o0, o1);
+    store_out4(sh, shard_of(sh, n0), m, n, (s.x * s_act) * sw.x, (s.y * s_act) * sw.y, (s.z * s_act) * sw.z,
+               (s.w * s_act) * sw.w);
 }
 
 template <int CPW, int D, int WMAX, bool DEFER>

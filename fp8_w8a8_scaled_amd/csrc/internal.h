@@ -11,11 +11,14 @@ namespace fp8mm {
 
 // Output placement of a (possibly merged) projection, passed by value in the
 // kernel arguments: weight rows [start[i], start[i+1]) go to out[i] with row
-// stride ldo[i].  Every start[i] is a multiple of 16.
+// stride ldo[i] (elements).  Every start[i] is a multiple of 16.  f32 selects
+// the output type for every shard: 0 bf16 (RNE), 1 f32 (the scaled fp32 value
+// itself).
 struct ShardTable {
     int num;
+    int f32;
     int64_t start[FP8MM_MAX_SHARDS + 1];
-    uint16_t* out[FP8MM_MAX_SHARDS];
+    void* out[FP8MM_MAX_SHARDS];
     int64_t ldo[FP8MM_MAX_SHARDS];
 };
 

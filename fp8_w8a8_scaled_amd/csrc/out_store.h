@@ -1,0 +1,44 @@
+// out_store.h -- the GEMM output stores: scaled fp32 values to bf16 (RNE) or
+// to f32, for the output type a ShardTable selects.
+#pragma once
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace fp8mm {
+
+// Shard of output column n (n0 of a 16-column tile works for the whole tile:
+// shard boundaries are multiples of 16).
+__device__ __forceinline__ int shard_of(const ShardTable& sh, int64_t n)
+{
+    int i = 0;
+    while (i + 1 < sh.num && n >= sh.start[i + 1]) ++i;
+    return i;
+}
+
+// Four consecutive columns n..n+3 (n % 4 == 0) of row m in shard i: 8 bytes of
+// bf16 or 16 bytes of f32.
+__device__ __forceinline__ void store_out4(const ShardTable& sh, int i, int64_t m, int64_t n, float a, float b,
+                                           float c, float d)
+{
+    const int64_t off = m * sh.ldo[i] + (n - sh.start[i]);
+    if (sh.f32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(sh.out[i]) + off) = make_float4(a, b, c, d);
+    } else {
+        const uint32_t lo = f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+        const uint32_t hi = f32_to_bf16_rne(c) | (f32_to_bf16_rne(d) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(sh.out[i]) + off) = make_uint2(lo, hi);
+    }
+}
+
+// One element.
+__device__ __forceinline__ void store_out1(const ShardTable& sh, int i, int64_t m, int64_t n, float v)
+{
+    const int64_t off = m * sh.ldo[i] + (n - sh.start[i]);
+    if (sh.f32)
+        static_cast<float*>(sh.out[i])[off] = v;
+    else
+        static_cast<uint16_t*>(sh.out[i])[off] = (uint16_t)f32_to_bf16_rne(v);
+}
+
+}  // namespace fp8mm

@@ -200,6 +200,35 @@ int fp8_scaled_mm_merged(const uint8_t* x_q, const uint8_t* w_q,
                          int64_t M, int64_t K,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * F32-output variants (the A/B of vllm.cpp #417 Finding 1: an F32 output
+ * doubles the bytes of the largest activation buffers against the model's
+ * bf16).  Same kernels, same arithmetic and kernel choice; the epilogue stores
+ *
+ *     out[m,n] = fl32( fl32(acc[m,n] * s_act) * s_w[n] )
+ *
+ * instead of its bf16 rounding, so bf16_RNE of an F32 result equals the bf16
+ * entry point's result bit for bit.  out: f32 [M, N] (shard i: f32 [M, n_i]),
+ * row stride ldo a multiple of 4 (16-byte rows), 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+typedef struct fp8_shard_f32 {
+    int64_t n;        /* output columns (weight rows) of this shard */
+    float* out;       /* device, f32 [M, n] */
+    int64_t ldo;      /* row stride of out, elements */
+} fp8_shard_f32_t;
+
+int fp8_scaled_mm_f32(const uint8_t* x_q, const uint8_t* w_q,
+                      float s_act, const float* s_w,
+                      float* out, int64_t ldo,
+                      int64_t M, int64_t N, int64_t K,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int fp8_scaled_mm_merged_f32(const uint8_t* x_q, const uint8_t* w_q,
+                             float s_act, const float* s_w,
+                             const fp8_shard_f32_t* shards, int num_shards,
+                             int64_t M, int64_t K,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes fp8_scaled_mm / _merged need for (M, N, K) (N = sum n_i).
  * 0 when the chosen kernel needs none.  Pure host function. */
 size_t fp8_scaled_mm_workspace_bytes(int64_t M, int64_t N, int64_t K);

@@ -234,3 +234,32 @@ def test_silu_mul_validation_fails_closed(fp8):
     assert g(A, L, A + 2 * I, L, 8, I - 8, C, D, ws, None) == U
     assert g(A + 2, L, A + 2 * I, L, 8, I, C, D, ws, None) == U
     assert g(A, L, A + 2 * I, L, 8, I, C, D + 8, ws, None) == U
+
+
+def test_f32_output_validation_fails_closed(fp8):
+    lib = fp8.raw_lib()
+    f = lib.fp8_scaled_mm_f32
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    E, U = fp8.EINVAL, fp8.EUNSUPPORTED
+    assert f(A, B, 0.5, C, D, 10240, 0, 10240, 5120, None, 0, None) == fp8.OK     # M == 0
+    assert f(A, B, 0.5, C, D, 10244, 0, 10240, 5120, None, 0, None) == fp8.OK     # f32 rows: ldo % 4 suffices
+    assert f(A, B, 0.5, C, D, 10242, 8, 10240, 5120, None, 0, None) == U          # ldo % 4
+    assert f(A, B, 0.5, C, D + 8, 10240, 8, 10240, 5120, None, 0, None) == U      # 16-byte rows
+    assert f(A, B, 0.5, C, None, 10240, 8, 10240, 5120, None, 0, None) == E
+    assert f(A, B, 0.0, C, D, 10240, 8, 10240, 5120, None, 0, None) == E
+    assert f(A, B, 0.5, C, D, 10000, 8, 10240, 5120, None, 0, None) == E          # ldo < N
+    g = lib.fp8_scaled_mm_merged_f32
+    Shard = fp8.Shard
+    g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(Shard),
+                  ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+
+    def call(shards, n=None, M=0):
+        arr = (Shard * max(1, len(shards)))(*shards)
+        return g(A, B, 0.5, C, arr, len(shards) if n is None else n, M, 5120, None, 0, None)
+
+    assert call([Shard(17408, D, 17412), Shard(17408, D + 0x2000000, 17408)]) == fp8.OK
+    assert call([Shard(17408, D, 17410)]) == U                   # ldo % 4
+    assert call([Shard(17408, None, 17408)], M=1) == E
+    assert call([Shard(16, D, 16)] * 9, n=9) == E
+    assert g(A, B, 0.5, C, None, 1, 0, 5120, None, 0, None) == E

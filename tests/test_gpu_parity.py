@@ -374,6 +374,53 @@ def test_strided_output_and_zero_m(fp8):
     assert empty.shape == (0, 384)
 
 
+# ------------------------------------------------------------ F32 output ----
+
+def _f32_bits_to_bf16_rne(a):
+    """bf16 RNE of finite f32 values (bit arithmetic on the host)."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 10240, 5120), (8, 10240, 5120), (16, 384, 256), (17, 32, 272),
+                                   (65, 80, 144), (300, 1040, 5120), (600, 544, 1088)])
+def test_f32_output_rounds_to_the_bf16_output(fp8, M, N, K):
+    """The F32 variant stores the same scaled fp32 value the bf16 variant
+    rounds: bf16_RNE(f32 out) equals the bf16 out bit for bit, on both arms
+    (M <= 64: small-M; larger M: large-M), and the f32 values meet the
+    oracle's tolerance."""
+    xq, wq, s_act, sw = _prepare(2, M, N, K, outliers=True)
+    xd, wd, swd = u8_dev(xq), u8_dev(wq), f32_dev(sw)
+    o16 = host_u16(fp8.scaled_mm(xd, wd, s_act, swd))
+    o32 = fp8.scaled_mm(xd, wd, s_act, swd, out_dtype=__import__("torch").float32).cpu().numpy()
+    assert np.all(np.isfinite(o32))
+    assert np.array_equal(_f32_bits_to_bf16_rne(o32), o16)
+    rows = np.unique(np.linspace(0, M - 1, min(M, 24)).astype(int))
+    _, v = oracle.scaled_mm(xq[rows], wq, s_act, sw, want_v=True)
+    tol = np.maximum(2.0 * np.abs(v) * 2.0 ** -23, 1e-3 * np.sqrt(np.sum(v * v, axis=1, keepdims=True)))
+    assert np.all(np.abs(o32[rows].astype(np.float64) - v) <= tol)
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_f32_merged_equals_split_and_strided(fp8, M):
+    import torch
+    K = 5120
+    xq = wl.random_codes(4, M, K, m=M)
+    wq = wl.random_codes(4, 1040, K, tensor=wl.T_W)
+    sw = (np.random.Generator(np.random.PCG64(1)).random(1040) * 1e-3 + 1e-5).astype(np.float32)
+    xd, wd, swd = u8_dev(xq), u8_dev(wq), f32_dev(sw)
+    shards = [512, 16, 512]
+    big = torch.full((M, 1100), -7.0, dtype=torch.float32, device="cuda")
+    outs = [big[:, 4:516], big[:, 520:536], big[:, 540:1052]]
+    fp8.scaled_mm_merged(xd, wd, 0.013, swd, shards, outs=outs)
+    start = 0
+    for n, mo in zip(shards, outs):
+        split = fp8.scaled_mm(xd, wd[start:start + n], 0.013, swd[start:start + n], out_dtype=torch.float32)
+        assert torch.equal(split, mo), f"shard at {start} differs"
+        start += n
+    assert torch.all(big[:, :4] == -7) and torch.all(big[:, 516:520] == -7) and torch.all(big[:, 1052:] == -7)
+
+
 # ------------------------------------------------- merge and determinism ----
 
 @pytest.mark.parametrize("M", [1, 8, 32, 300])
