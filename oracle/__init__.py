@@ -73,6 +73,8 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_exact_acc.argtypes = [P, P, I64, I64, I64, P]
     L.oracle_silu_mul.argtypes = [P, I64, P, I64, I64, I64, P]
     L.oracle_silu_mul_quant.argtypes = [P, I64, P, I64, F32, I64, I64, P]
+    L.oracle_quant_per_token.argtypes = [P, I64, P, F32, I64, I64, P, P]
+    L.oracle_scaled_mm_rows.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P]
     L.oracle_num_threads.restype = ctypes.c_int
     return L
 
@@ -202,6 +204,33 @@ def scaled_mm(xq: np.ndarray, wq: np.ndarray, s_act: float, s_w: np.ndarray, wan
     out = np.empty((M, N), np.uint16)
     v = np.empty((M, N), np.float64) if want_v else None
     lib().oracle_scaled_mm(_ptr(a), _ptr(b), float(s_act), _ptr(sw), M, N, K, _ptr(out), N, _ptr(v))
+    return (out, v) if want_v else out
+
+
+def quant_per_token(x_bf16: np.ndarray, gamma_bf16: np.ndarray | None = None, eps: float = 1e-6):
+    """Per-token dynamic quant: (codes uint8 [M, K], scales float32 [M]); each
+    row quantized with its own amax / 448 (RMSNorm first when gamma is given)."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    g = None if gamma_bf16 is None else _c(gamma_bf16, np.uint16)
+    xq = np.empty((M, K), np.uint8)
+    s = np.empty(M, np.float32)
+    lib().oracle_quant_per_token(_ptr(x), K, _ptr(g), float(eps), M, K, _ptr(xq), _ptr(s))
+    return xq, s
+
+
+def scaled_mm_rows(xq: np.ndarray, wq: np.ndarray, s_rows: np.ndarray, s_w: np.ndarray, want_v: bool = False):
+    """Per-row activation scales: out bf16 bits [M, N] (and the fp64 v)."""
+    a = _c(xq, np.uint8)
+    b = _c(wq, np.uint8)
+    sr = _c(s_rows, np.float32)
+    sw = _c(s_w, np.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K and sr.shape == (M,) and sw.shape == (N,)
+    out = np.empty((M, N), np.uint16)
+    v = np.empty((M, N), np.float64) if want_v else None
+    lib().oracle_scaled_mm_rows(_ptr(a), _ptr(b), _ptr(sr), _ptr(sw), M, N, K, _ptr(out), N, _ptr(v))
     return (out, v) if want_v else out
 
 

@@ -119,8 +119,11 @@ def quant(x_bits, s_act: float):
     for row in x_bits:
         r = []
         for b in row:
-            xv = bf16_bits_value(b)
             neg = bool(b & 0x8000)
+            if (b & 0x7FFF) >= 0x7F80:                    # inf saturates, NaN stays NaN
+                r.append((0x80 if neg else 0) | (0x7E if (b & 0x7FFF) == 0x7F80 else 0x7F))
+                continue
+            xv = bf16_bits_value(b)
             t = fl32(xv / s)
             r.append(e4m3_encode_exact(t, neg))
         out.append(r)
@@ -142,3 +145,35 @@ def scaled_mm(xq, wq, s_act: float, s_w):
         bits.append(rb)
         vals.append(rv)
     return bits, vals
+
+
+# ------------------------------------------------------- per-token scales ---
+
+def act_scale(row_bits) -> float:
+    """fl32(amax / 448) over the finite values of bf16 patterns (1 when 0)."""
+    amax = Fraction(0)
+    for b in row_bits:
+        if (b & 0x7F80) == 0x7F80:
+            continue                                      # inf / NaN
+        amax = max(amax, abs(bf16_bits_value(b)))
+    if amax == 0:
+        return 1.0
+    return float(fl32(amax / 448))
+
+
+def quant_per_token(x_bits):
+    """(codes, scales): every row quantized with its own act_scale."""
+    codes, scales = [], []
+    for row in x_bits:
+        s = act_scale(row)
+        scales.append(s)
+        codes.append(quant([row], s)[0])
+    return codes, scales
+
+
+def scaled_mm_rows(xq, wq, s_rows, s_w):
+    """bf16 patterns of (acc[m,n] * s_rows[m]) * s_w[n], one rounding."""
+    bits = []
+    for a, s in zip(xq, s_rows):
+        bits.append(scaled_mm([a], wq, s, s_w)[0][0])
+    return bits

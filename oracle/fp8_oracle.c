@@ -319,6 +319,39 @@ void oracle_scaled_mm(const unsigned char* xq, const unsigned char* wq, float s_
         }
 }
 
+/* ------------------------------------------ per-token dynamic scales --- */
+
+/* Per-token dynamic activation scales: the scale granularity vllm.cpp #252
+ * leaves open ("What is owed", item 2: per-tensor vs per-channel vs per-token
+ * scaling).  Reading taken: every row is quantized as a tensor of its own, with
+ * the static quant's calibration rule applied to that row alone:
+ *     s[m]     = fl32( amax_k |y[m,k]| / 448 )    (finite values; 1 when 0)
+ *     x_q[m,k] = satRNE_E4M3( fl32( y[m,k] / s[m] ) )
+ * y is x (gamma == NULL) or the bf16 RMSNorm output of the row. */
+void oracle_quant_per_token(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
+                            int64_t M, int64_t K, unsigned char* xq, float* s_rows)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* row = x + m * ldx;
+        const float s = oracle_act_scale(row, ldx, gamma, eps, 1, K);
+        s_rows[m] = s;
+        if (gamma)
+            oracle_quant_rmsnorm(row, ldx, gamma, eps, s, 1, K, xq + m * K);
+        else
+            oracle_quant_act(row, ldx, 1, K, s, xq + m * K);
+    }
+}
+
+/* The GEMM with a per-row activation scale: v[m,n] = (acc[m,n] * s[m]) * s_w[n]
+ * in fp64, out = bf16_RNE(v) (the per-tensor epilogue with s_act -> s[m]). */
+void oracle_scaled_mm_rows(const unsigned char* xq, const unsigned char* wq, const float* s_rows,
+                           const float* s_w, int64_t M, int64_t N, int64_t K,
+                           uint16_t* out, int64_t ldo, double* v)
+{
+    for (int64_t m = 0; m < M; ++m)
+        oracle_scaled_mm(xq + m * K, wq, s_rows[m], s_w, 1, N, K, out + m * ldo, ldo, v ? v + m * N : NULL);
+}
+
 /* Only the exact accumulator (fp64), for the closed-form pins. */
 void oracle_exact_acc(const unsigned char* xq, const unsigned char* wq,
                       int64_t M, int64_t N, int64_t K, double* acc)

@@ -48,6 +48,10 @@ MUTATIONS = {
     "silu_in_fp32": ("return (float)(d / (1.0 + exp(-d)));", "return (float)g / (1.0f + expf(-g));"),
     "silu_mul_swapped": ("float hf = s * oracle_bf16_to_f32(up[m * ldu + i]);",
                          "float hf = silu_f32(oracle_bf16_to_f32(up[m * ldu + i])) * oracle_bf16_to_f32(gate[m * ldg + i]);"),
+    "per_token_tensor_amax": ("const float s = oracle_act_scale(row, ldx, gamma, eps, 1, K);",
+                              "const float s = oracle_act_scale(x, ldx, gamma, eps, M, K);"),
+    "rows_scale_first_row": ("oracle_scaled_mm(xq + m * K, wq, s_rows[m], s_w,",
+                             "oracle_scaled_mm(xq + m * K, wq, s_rows[0], s_w,"),
 }
 
 PIN_TESTS = [
@@ -70,6 +74,10 @@ PIN_TESTS = [
     pins.test_silu_closed_forms_and_identities,
     pins.test_silu_mul_product_and_power_of_two_scaling,
     lambda: pins.test_silu_mul_quant_is_byte_exact_against_unfused(1),
+    pins.test_per_token_brute_force_against_exact_rationals,
+    pins.test_per_token_rows_are_independent_and_scale_covariant,
+    pins.test_per_token_rmsnorm_row_is_the_static_quant_of_that_row,
+    pins.test_rows_gemm_with_equal_scales_is_the_per_tensor_gemm,
 ]
 
 

@@ -393,3 +393,69 @@ def test_silu_mul_quant_is_byte_exact_against_unfused(M):
     fused = oracle.silu_mul_quant(g, u, s)
     assert np.array_equal(fused, oracle.quant_act(h, s))
     assert np.abs(oracle.e4m3_table()[fused]).max() == 448.0
+
+
+# ----------------------------------------------------- per-token scales ----
+
+def test_per_token_brute_force_against_exact_rationals():
+    """Per-row dynamic quant (each row: fl32(amax/448), then the static quant)
+    and the GEMM with per-row scales, in Fractions vs the oracle; rows of very
+    different magnitude, a zero row and non-finite entries included."""
+    g = np.random.Generator(np.random.PCG64(314))
+    for it in range(150):
+        mags = np.array([g.choice([1e-3, 1.0, 50.0]) for _ in range(3)], np.float32)[:, None]
+        x = wl.to_bf16_bits(g.standard_normal((3, 8)).astype(np.float32) * mags)
+        if it % 7 == 0:
+            x[1] = 0x8000 if it % 2 else 0                 # a zero row: scale 1
+        if it % 11 == 0:
+            x[2, 3] = 0x7F80                               # inf is skipped by the amax, saturates
+        xq, s = oracle.quant_per_token(x)
+        xq_e, s_e = exact.quant_per_token(x.tolist())
+        assert [float(v) for v in s] == s_e, (it, s, s_e)
+        assert np.array_equal(xq, np.array(xq_e, np.uint8)), it
+        codes = wl.FINITE_CODE_VALUES[g.integers(0, 254, (4, 8))]
+        s_w = (g.random(4) * 0.01 + 1e-4).astype(np.float32)
+        out = oracle.scaled_mm_rows(xq, codes, s, s_w)
+        assert np.array_equal(out, np.array(exact.scaled_mm_rows(xq.tolist(), codes.tolist(), s.tolist(),
+                                                                 s_w.tolist()), np.uint16)), it
+
+
+def test_per_token_rows_are_independent_and_scale_covariant():
+    """Multiplying one row by 2^k (exact in bf16) multiplies its scale by 2^k
+    and leaves every code of every row unchanged; the other rows' scales do not
+    move; a constant row quantizes to +-448 everywhere."""
+    x = wl.activation_bf16(2, 6, 5120, outliers=True)
+    q0, s0 = oracle.quant_per_token(x)
+    for k in (-3, 5):
+        y = x.copy()
+        f = (y[2].astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** k)
+        y[2] = (f.view(np.uint32) >> 16).astype(np.uint16)
+        q1, s1 = oracle.quant_per_token(y)
+        assert np.array_equal(q0, q1)
+        assert s1[2] == np.float32(s0[2] * 2.0 ** k)
+        assert np.array_equal(np.delete(s1, 2), np.delete(s0, 2))
+    c = np.full((1, 64), 0xC040, np.uint16)               # -3.0
+    qc, sc = oracle.quant_per_token(c)
+    assert sc[0] == np.float32(3.0) / np.float32(448.0) and np.all(qc == 0xFE)
+
+
+def test_per_token_rmsnorm_row_is_the_static_quant_of_that_row():
+    """With gamma, row m's codes and scale equal the static fused RMSNorm quant
+    of that row alone, calibrated on that row alone."""
+    x = wl.activation_bf16(3, 5, 5120, outliers=True)
+    gm = wl.gamma_bf16(3, 5120)
+    q, s = oracle.quant_per_token(x, gm, wl.EPS)
+    for m in range(5):
+        sm = oracle.act_scale(x[m:m + 1], gm, wl.EPS)
+        assert s[m] == np.float32(sm)
+        assert np.array_equal(q[m:m + 1], oracle.quant_rmsnorm(x[m:m + 1], gm, wl.EPS, sm))
+
+
+def test_rows_gemm_with_equal_scales_is_the_per_tensor_gemm():
+    g = np.random.Generator(np.random.PCG64(8))
+    xq = wl.random_codes(2, 7, 640)
+    wq = wl.random_codes(2, 48, 640, tensor=wl.T_W)
+    sw = (g.random(48) * 1e-3 + 1e-5).astype(np.float32)
+    a, va = oracle.scaled_mm(xq, wq, 0.0123, sw, want_v=True)
+    b, vb = oracle.scaled_mm_rows(xq, wq, np.full(7, 0.0123, np.float32), sw, want_v=True)
+    assert np.array_equal(a, b) and np.array_equal(va, vb)
