@@ -258,6 +258,45 @@ def bench_prefill(fp8, steps, warmup):
     }
 
 
+def bench_per_token(fp8, M, steps, warmup):
+    """Per-token dynamic scales beside the per-tensor numbers: the decode step
+    (per-token quant [M,5120] + GEMM 10240x5120 with per-row scales, weights
+    rotated as in the main line) and the prefill gate_up (per-token fused
+    RMSNorm quant [6576,5120] + merged gate_up with per-row scales)."""
+    import torch
+    import workloads as wl
+    K, N = 5120, 10240
+    xd = bf16_dev(wl.activation_bf16(wl.DECODE_PROJ.wid, M, K, outliers=True))
+    wq, sw = fp8.quant_weight(f32_dev(wl.weight_f32(wl.DECODE_PROJ.wid, N, K)))
+    copies = max(2, -(-2 * LLC_BYTES // (N * K)) + 1)
+    ws = [wq] + [wq.clone() for _ in range(copies - 1)]
+    xq, sr = fp8.quant_per_token(xd)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        fp8.quant_per_token(xd, out=xq, scales=sr)
+        fp8.scaled_mm_per_token(xq, ws[i % copies], sr, sw, out=out)
+
+    ms = graph_time_ms(step, steps, warmup)
+    gms = graph_time_ms(lambda i: fp8.scaled_mm_per_token(xq, ws[i % copies], sr, sw, out=out), steps, warmup)
+    step_bytes = N * K + 4 * N + M * K + 2 * M * N + 3 * M * K + 4 * M
+    del ws
+    Mp, N1 = 6576, 34816
+    wid = wl.PREFILL.wid
+    xp = bf16_dev(wl.activation_bf16(wid, Mp, K, outliers=False))
+    gp = bf16_dev(wl.gamma_bf16(wid, K))
+    wq1, sw1 = fp8.quant_weight(f32_dev(wl.weight_f32(wid, N1, K)))
+    xq1, sr1 = fp8.quant_per_token(xp, gp, wl.EPS)
+    outs = [torch.empty((Mp, N1 // 2), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    pq_ms = graph_time_ms(lambda i: fp8.quant_per_token(xp, gp, wl.EPS, out=xq1, scales=sr1), 10, 2)
+    pg_ms = graph_time_ms(lambda i: fp8.scaled_mm_merged_per_token(xq1, wq1, sr1, sw1, [N1 // 2, N1 // 2],
+                                                                   outs=outs), 10, 2)
+    return {"decode_step": {"workload": f"decode_proj_M{M}_K{K}_N{N}", "us": ms * 1e3,
+                            "GBs": step_bytes / (ms * 1e-3) / 1e9, "gemm_us": gms * 1e3},
+            "prefill": {"quant_rmsnorm_per_token_us": pq_ms * 1e3,
+                        "gate_up_us": pg_ms * 1e3, "gate_up_TFLOPs": 2 * Mp * N1 * K / (pg_ms * 1e-3) / 1e12}}
+
+
 def bench_sweep(fp8, layers, M, steps, warmup, wid=4):
     """Decode-step weight sweep: `layers` = ((count, projections), ...).  The
     distinct projections of each layer group get their own seeded weights
@@ -490,6 +529,7 @@ def main():
     }
     if not a.no_prefill:
         line["prefill"] = bench_prefill(fp8, a.prefill_steps, a.warmup)
+        line["per_token_scales"] = bench_per_token(fp8, a.M, a.steps, a.warmup)
     if not a.no_sweep:
         import workloads as wl
         line["decode_step_sweep"] = {

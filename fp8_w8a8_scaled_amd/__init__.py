@@ -51,6 +51,10 @@ _quant_rmsnorm = _decl("fp8_quant_rmsnorm", [_P, _I64, _P, _F32, _F32, _P, _I64,
 _scaled_mm = _decl("fp8_scaled_mm", [_P, _P, _F32, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P])
 _scaled_mm_arm = _decl("fp8_scaled_mm_arm", [_P, _P, _F32, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _SZ, _P])
 _scaled_mm_merged = _decl("fp8_scaled_mm_merged", [_P, _P, _F32, _P, ctypes.POINTER(Shard), _I32, _I64, _I64, _P, _SZ, _P])
+_quant_per_token = _decl("fp8_quant_per_token", [_P, _I64, _P, _F32, _P, _P, _I64, _I64, _P])
+_scaled_mm_per_token = _decl("fp8_scaled_mm_per_token", [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P])
+_scaled_mm_merged_per_token = _decl("fp8_scaled_mm_merged_per_token",
+                                    [_P, _P, _P, _P, ctypes.POINTER(Shard), _I32, _I64, _I64, _P, _SZ, _P])
 _scaled_mm_f32 = _decl("fp8_scaled_mm_f32", [_P, _P, _F32, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P])
 _scaled_mm_merged_f32 = _decl("fp8_scaled_mm_merged_f32",
                               [_P, _P, _F32, _P, ctypes.POINTER(Shard), _I32, _I64, _I64, _P, _SZ, _P])
@@ -281,6 +285,68 @@ def scaled_mm_merged(x_q: torch.Tensor, w_q: torch.Tensor, s_act: float, s_w: to
     fn = _scaled_mm_merged_f32 if dt == torch.float32 else _scaled_mm_merged
     _check(fn(_ptr(x_q), _ptr(w_q), float(s_act), _ptr(s_w), arr, len(shard_sizes), M, K,
               _ptr(ws), wsb, _stream(x_q)), "fp8_scaled_mm_merged")
+    return list(outs)
+
+
+# ------------------------------------------------------ per-token scales --
+
+def quant_per_token(x: torch.Tensor, gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                    out: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):
+    """Per-token dynamic E4M3 quant of bf16 x [M, K] (RMSNorm first when gamma
+    is given): returns (codes uint8 [M, K], scales f32 [M])."""
+    _need(x.is_cuda and x.dtype == torch.bfloat16, "x must be a bf16 CUDA tensor")
+    ldx = _row_major(x, "x")
+    M, K = x.shape
+    if gamma is not None:
+        _need(gamma.is_cuda and gamma.dtype == torch.bfloat16 and gamma.is_contiguous() and gamma.numel() == K,
+              "gamma must be a contiguous bf16 CUDA tensor of K elements")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(M, dtype=torch.float32, device=x.device)
+    out = _codes(out, "out")
+    _need(out.is_contiguous() and tuple(out.shape) == (M, K), "out must be contiguous uint8 [M, K]")
+    _need(scales.dtype == torch.float32 and scales.is_contiguous() and scales.numel() == M, "scales must be f32 [M]")
+    _check(_quant_per_token(_ptr(x), ldx, _ptr(gamma), float(eps), _ptr(out), _ptr(scales), M, K, _stream(x)),
+           "fp8_quant_per_token")
+    return out, scales
+
+
+def scaled_mm_per_token(x_q: torch.Tensor, w_q: torch.Tensor, s_rows: torch.Tensor, s_w: torch.Tensor,
+                        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [M, N] = bf16((x_q . w_q^T) * s_rows[m] * s_w[n])."""
+    x_q, w_q = _gemm_args(x_q, w_q, s_w)
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    _need(s_rows.is_cuda and s_rows.dtype == torch.float32 and s_rows.is_contiguous() and s_rows.numel() == M,
+          "s_rows must be a contiguous f32 CUDA tensor of M elements")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x_q.device)
+    _need(out.dtype == torch.bfloat16 and out.is_cuda and out.shape == (M, N), "out must be bf16 [M, N]")
+    ws, wsb = _workspace(M, N, K, x_q.device, workspace)
+    _check(_scaled_mm_per_token(_ptr(x_q), _ptr(w_q), _ptr(s_rows), _ptr(s_w), _ptr(out), _row_major(out, "out"),
+                                M, N, K, _ptr(ws), wsb, _stream(x_q)), "fp8_scaled_mm_per_token")
+    return out
+
+
+def scaled_mm_merged_per_token(x_q: torch.Tensor, w_q: torch.Tensor, s_rows: torch.Tensor, s_w: torch.Tensor,
+                               shard_sizes: Sequence[int], outs: Optional[Sequence[torch.Tensor]] = None,
+                               workspace: Optional[torch.Tensor] = None):
+    x_q, w_q = _gemm_args(x_q, w_q, s_w)
+    M, K = x_q.shape
+    _need(sum(shard_sizes) == w_q.shape[0], "shard sizes must sum to the weight rows")
+    _need(1 <= len(shard_sizes) <= MAX_SHARDS, f"1..{MAX_SHARDS} shards")
+    _need(s_rows.is_cuda and s_rows.dtype == torch.float32 and s_rows.is_contiguous() and s_rows.numel() == M,
+          "s_rows must be a contiguous f32 CUDA tensor of M elements")
+    if outs is None:
+        outs = [torch.empty((M, n), dtype=torch.bfloat16, device=x_q.device) for n in shard_sizes]
+    arr = (Shard * len(shard_sizes))()
+    for i, (n, o) in enumerate(zip(shard_sizes, outs)):
+        _need(o.dtype == torch.bfloat16 and o.is_cuda and o.shape == (M, n), "shard outputs must be bf16 [M, n_i]")
+        arr[i] = Shard(int(n), o.data_ptr(), _row_major(o, "out"))
+    ws, wsb = _workspace(M, w_q.shape[0], K, x_q.device, workspace)
+    _check(_scaled_mm_merged_per_token(_ptr(x_q), _ptr(w_q), _ptr(s_rows), _ptr(s_w), arr, len(shard_sizes), M, K,
+                                       _ptr(ws), wsb, _stream(x_q)), "fp8_scaled_mm_merged_per_token")
     return list(outs)
 
 

@@ -56,6 +56,7 @@ int check_gemm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float*
                const OutShard* shards, int num_shards, bool f32, int64_t M, int64_t K,
                fp8mm::ShardTable* tab, int64_t* N_out)
 {
+    tab->s_rows = nullptr;
     // Sizes and scalars first; an empty product (M == 0 or N == 0) is a no-op
     // that may come with null pointers (empty tensors).
     if (!shards || M < 0 || K < 0 || num_shards < 1 || num_shards > FP8MM_MAX_SHARDS) return FP8MM_EINVAL;
@@ -87,12 +88,18 @@ int check_gemm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float*
 
 int run_gemm(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,
              const OutShard* shards, int num_shards, bool f32, int64_t M, int64_t K, int arm,
-             void* workspace, size_t workspace_bytes, hipStream_t stream)
+             void* workspace, size_t workspace_bytes, hipStream_t stream, bool per_row = false,
+             const float* s_rows = nullptr)
 {
     fp8mm::ShardTable tab{};
     int64_t N = 0;
     int st = check_gemm(x_q, w_q, s_act, s_w, shards, num_shards, f32, M, K, &tab, &N);
     if (st != FP8MM_OK) return st;
+    if (per_row) {                                       // s_act is unused: device per-row scales instead
+        if (M > 0 && N > 0 && !s_rows) return FP8MM_EINVAL;
+        if (reinterpret_cast<uintptr_t>(s_rows) & 3u) return FP8MM_EUNSUPPORTED;
+        tab.s_rows = s_rows;
+    }
     if (workspace_bytes < fp8_scaled_mm_workspace_bytes(M, N, K)) return FP8MM_EWORKSPACE;
     (void)workspace;
     if (M == 0 || N == 0) return FP8MM_OK;
@@ -177,6 +184,48 @@ int fp8_scaled_mm_merged_f32(const uint8_t* x_q, const uint8_t* w_q, float s_act
     OutShard tab[FP8MM_MAX_SHARDS];
     for (int i = 0; i < num_shards; ++i) tab[i] = OutShard{shards[i].n, shards[i].out, shards[i].ldo};
     return run_gemm(x_q, w_q, s_act, s_w, tab, num_shards, true, M, K, -1, workspace, workspace_bytes, stream);
+}
+
+int fp8_quant_per_token(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, uint8_t* x_q,
+                        float* s_rows, int64_t M, int64_t K, hipStream_t stream)
+{
+    if (M < 0 || K < 0 || ldx < K) return FP8MM_EINVAL;
+    if (gamma && !(std::isfinite(eps) && eps >= 0.0f)) return FP8MM_EINVAL;
+    if (K % 16 != 0 || ldx % 8 != 0) return FP8MM_EUNSUPPORTED;
+    if (M == 0) return FP8MM_OK;
+    if (!x || !x_q || !s_rows) return FP8MM_EINVAL;
+    if (K == 0) return FP8MM_EUNSUPPORTED;               // a row with no values has no scale
+    if (!aligned16(x) || !aligned16(x_q) || (gamma && !aligned16(gamma)) ||
+        (reinterpret_cast<uintptr_t>(s_rows) & 3u))
+        return FP8MM_EUNSUPPORTED;
+    if (M > (int64_t)0x7fffffff) return FP8MM_EUNSUPPORTED;
+    const uintptr_t xb = reinterpret_cast<uintptr_t>(x), xe = xb + (uintptr_t)((M - 1) * ldx + K) * 2;
+    const uintptr_t qb = reinterpret_cast<uintptr_t>(x_q), qe = qb + (uintptr_t)(M * K);
+    const uintptr_t sb = reinterpret_cast<uintptr_t>(s_rows), se = sb + (uintptr_t)M * 4;
+    if ((qb < xe && xb < qe) || (sb < xe && xb < se) || (sb < qe && qb < se)) return FP8MM_EINVAL;
+    fp8mm::launch_quant_per_token(x, ldx, gamma, eps, x_q, s_rows, M, K, stream);
+    return launch_status();
+}
+
+int fp8_scaled_mm_per_token(const uint8_t* x_q, const uint8_t* w_q, const float* s_rows, const float* s_w,
+                            uint16_t* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (N < 0) return FP8MM_EINVAL;
+    const OutShard one{N, out, ldo};
+    return run_gemm(x_q, w_q, 1.0f, s_w, &one, 1, false, M, K, -1, workspace, workspace_bytes, stream, true,
+                    s_rows);
+}
+
+int fp8_scaled_mm_merged_per_token(const uint8_t* x_q, const uint8_t* w_q, const float* s_rows, const float* s_w,
+                                   const fp8_shard_t* shards, int num_shards, int64_t M, int64_t K,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!shards || num_shards < 1 || num_shards > FP8MM_MAX_SHARDS) return FP8MM_EINVAL;
+    OutShard tab[FP8MM_MAX_SHARDS];
+    for (int i = 0; i < num_shards; ++i) tab[i] = OutShard{shards[i].n, shards[i].out, shards[i].ldo};
+    return run_gemm(x_q, w_q, 1.0f, s_w, tab, num_shards, false, M, K, -1, workspace, workspace_bytes, stream, true,
+                    s_rows);
 }
 
 size_t fp8_scaled_mm_workspace_bytes(int64_t M, int64_t N, int64_t K)

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (m < M) store_out1(sh, si, m, n, (acc[i][j][v] * s_act) * swn);
+                if (m < M) store_out1(sh, si, m, n, (acc[i][j][v] * row_scale(sh, m, s_act)) * swn);
             }
     }
 }
@@ -423,6 +423,8 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
             const int64_t n = n0 + wn * 128 + i * 32 + 8 * q + 4 * fh;
             swv[i][q] = *reinterpret_cast<const float4*>(s_w + (n < N ? n : 0));
         }
+    // The loops below run row group j outermost, so only one activation scale
+    // (per-tensor, or this lane's row's) is live at a time.
     if (sh.f32) {
         // f32: the tile in two halves of 128 rows (the waves with wm == h hold
         // half h), each staged in LDS and stored with row-contiguous 16-byte writes
@@ -431,19 +433,20 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
         for (int h = 0; h < 2; ++h) {
             if (wm == h) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < 4; ++j) {
+                    const float sa = row_scale(sh, min(m0 + wm * 128 + j * 32 + fr, M - 1), s_act);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int nl = wn * 128 + i * 32 + 8 * q + 4 * fh;
-                        const float4 sw = swv[i][q];
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
+                        for (int q = 0; q < 4; ++q) {
+                            const int nl = wn * 128 + i * 32 + 8 * q + 4 * fh;
+                            const float4 sw = swv[i][q];
                             const v16f& c = acc[i][j];
                             *reinterpret_cast<float4*>(smem + (j * 32 + fr) * C_ROW32 + nl * 4) =
-                                make_float4((c[4 * q + 0] * s_act) * sw.x, (c[4 * q + 1] * s_act) * sw.y,
-                                            (c[4 * q + 2] * s_act) * sw.z, (c[4 * q + 3] * s_act) * sw.w);
+                                make_float4((c[4 * q + 0] * sa) * sw.x, (c[4 * q + 1] * sa) * sw.y,
+                                            (c[4 * q + 2] * sa) * sw.z, (c[4 * q + 3] * sa) * sw.w);
                         }
-                    }
+                }
             }
             __syncthreads();
 #pragma unroll 4
@@ -466,22 +469,23 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
         continue;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) {
+        const float sa = row_scale(sh, min(m0 + wm * 128 + j * 32 + fr, M - 1), s_act);
+        const int ml = wm * 128 + j * 32 + fr;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int nl = wn * 128 + i * 32 + 8 * q + 4 * fh;
-            const float4 sw = swv[i][q];
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int ml = wm * 128 + j * 32 + fr;
+            for (int q = 0; q < 4; ++q) {
+                const int nl = wn * 128 + i * 32 + 8 * q + 4 * fh;
+                const float4 sw = swv[i][q];
                 const v16f& c = acc[i][j];
-                const uint32_t lo = f32_to_bf16_rne((c[4 * q + 0] * s_act) * sw.x) |
-                                    (f32_to_bf16_rne((c[4 * q + 1] * s_act) * sw.y) << 16);
-                const uint32_t hi = f32_to_bf16_rne((c[4 * q + 2] * s_act) * sw.z) |
-                                    (f32_to_bf16_rne((c[4 * q + 3] * s_act) * sw.w) << 16);
+                const uint32_t lo = f32_to_bf16_rne((c[4 * q + 0] * sa) * sw.x) |
+                                    (f32_to_bf16_rne((c[4 * q + 1] * sa) * sw.y) << 16);
+                const uint32_t hi = f32_to_bf16_rne((c[4 * q + 2] * sa) * sw.z) |
+                                    (f32_to_bf16_rne((c[4 * q + 3] * sa) * sw.w) << 16);
                 *reinterpret_cast<uint2*>(smem + ml * C_ROW + nl * 2) = make_uint2(lo, hi);
             }
-        }
+    }
     __syncthreads();
     constexpr int CHUNKS = T2 * T2 * 2 / 16;           // 16-byte pieces of the tile
 #pragma unroll 4

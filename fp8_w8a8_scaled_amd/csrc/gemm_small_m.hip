@@ -198,8 +198,9 @@ __device__ __forceinline__ void reduce_store(const v4f* red, int W, int64_t n0, 
         }
         const int64_t n = nt0 + 4 * (l >> 4);
         const float4 sw = *reinterpret_cast<const float4*>(s_w + n);
-        store_out4(sh, shard_of(sh, nt0), m, n, (s.x * s_act) * sw.x, (s.y * s_act) * sw.y, (s.z * s_act) * sw.z,
-                   (s.w * s_act) * sw.w);
+        const float sa = row_scale(sh, m, s_act);
+        store_out4(sh, shard_of(sh, nt0), m, n, (s.x * sa) * sw.x, (s.y * sa) * sw.y, (s.z * sa) * sw.z,
+                   (s.w * sa) * sw.w);
     }
 }
 
@@ -417,8 +418,9 @@ __device__ __forceinline__ void reduce_tile(const v4f* red, int stride, int slot
         s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
     }
     const int64_t n = n0 + 4 * (lane >> 4);
-    store_out4(sh, shard_of(sh, n0), m, n, (s.x * s_act) * sw.x, (s.y * s_act) * sw.y, (s.z * s_act) * sw.z,
-               (s.w * s_act) * sw.w);
+    const float sa = row_scale(sh, m, s_act);
+    store_out4(sh, shard_of(sh, n0), m, n, (s.x * sa) * sw.x, (s.y * sa) * sw.y, (s.z * sa) * sw.z,
+               (s.w * sa) * sw.w);
 }
 
 template <int CPW, int D, int WMAX, bool DEFER>

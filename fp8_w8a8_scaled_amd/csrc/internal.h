@@ -13,10 +13,12 @@ namespace fp8mm {
 // kernel arguments: weight rows [start[i], start[i+1]) go to out[i] with row
 // stride ldo[i] (elements).  Every start[i] is a multiple of 16.  f32 selects
 // the output type for every shard: 0 bf16 (RNE), 1 f32 (the scaled fp32 value
-// itself).
+// itself).  s_rows, when not null, holds per-row activation scales (device f32
+// [M]) that replace the per-tensor s_act in the epilogue.
 struct ShardTable {
     int num;
     int f32;
+    const float* s_rows;
     int64_t start[FP8MM_MAX_SHARDS + 1];
     void* out[FP8MM_MAX_SHARDS];
     int64_t ldo[FP8MM_MAX_SHARDS];
@@ -30,6 +32,8 @@ void launch_act_scale(const uint16_t* x, int64_t ldx, const uint16_t* gamma, flo
                       int64_t M, int64_t K, float* s_act, float* partial, hipStream_t stream);
 void launch_quant_weight(const float* w, int64_t N, int64_t K, uint8_t* wq, float* s_w,
                          hipStream_t stream);
+void launch_quant_per_token(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, uint8_t* xq,
+                            float* s_rows, int64_t M, int64_t K, hipStream_t stream);
 void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, float s_act,
                            uint8_t* xq, int64_t M, int64_t I, hipStream_t stream);
 // Table-based SiLU*mul quant: workgroups per CU, 16-byte pieces per thread

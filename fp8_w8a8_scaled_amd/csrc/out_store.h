@@ -16,6 +16,12 @@ __device__ __forceinline__ int shard_of(const ShardTable& sh, int64_t n)
     return i;
 }
 
+// Activation scale of output row m (m < M): per-row when the table has them.
+__device__ __forceinline__ float row_scale(const ShardTable& sh, int64_t m, float s_act)
+{
+    return sh.s_rows ? sh.s_rows[m] : s_act;
+}
+
 // Four consecutive columns n..n+3 (n % 4 == 0) of row m in shard i: 8 bytes of
 // bf16 or 16 bytes of f32.
 __device__ __forceinline__ void store_out4(const ShardTable& sh, int i, int64_t m, int64_t n, float a, float b,

@@ -116,6 +116,122 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_rmsnorm(
     }
 }
 
+// ---- per-token dynamic quant: every row with its own scale ------------------
+
+__device__ __forceinline__ float finite_abs_max(float acc, float v);
+
+// The 8 values of piece v of a row that get quantized: x itself, or the bf16
+// RMSNorm output (r the row's scale).
+__device__ __forceinline__ void row_values8(const uint16_t* __restrict__ row, const uint16_t* __restrict__ gamma,
+                                           float r, int64_t v, float y[8])
+{
+    const uint4 in = *reinterpret_cast<const uint4*>(row + v * 8);
+    if (gamma) {
+        rms_apply8(in, *reinterpret_cast<const uint4*>(gamma + v * 8), r, y);
+    } else {
+        const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = bf16_to_f32((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
+    }
+}
+
+// One workgroup per row: s_rows[m] = fl32(amax / 448) over the row's finite
+// values (1 when 0), then the codes of fl32(y / s_rows[m]) (a NaN keeps its own
+// sign, as in the static quant).  The row is re-read from L2 for each pass.
+__global__ __launch_bounds__(kQuantThreads) void k_quant_per_token(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma, float eps,
+    uint8_t* __restrict__ xq, float* __restrict__ s_rows, int64_t K)
+{
+    __shared__ double lds[kQuantThreads / 64];
+    __shared__ float ldsf[kQuantThreads / 64];
+    const int64_t m = blockIdx.x;
+    const uint16_t* row = x + m * ldx;
+    const float r = gamma ? row_rms_inv(row, K, eps, lds) : 1.0f;
+    const int64_t nv = K >> 3;
+    float amax = 0.0f;
+    for (int64_t v = threadIdx.x; v < nv; v += blockDim.x) {
+        float y[8];
+        row_values8(row, gamma, r, v, y);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = finite_abs_max(amax, y[j]);
+    }
+    amax = block_max_f32(amax, ldsf);
+    const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+    if (threadIdx.x == 0) s_rows[m] = s;
+    for (int64_t v = threadIdx.x; v < nv; v += blockDim.x) {
+        float y[8];
+        row_values8(row, gamma, r, v, y);
+        uint32_t o[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j >> 2] |= quant_value(y[j], s) << ((j & 3) * 8);
+        *reinterpret_cast<uint2*>(xq + m * K + v * 8) = make_uint2(o[0], o[1]);
+    }
+}
+
+// The same with the row held in registers (K <= 8 * 256 * PPT): one read of
+// x, and the fp64 sum of squares taken in the generic kernel's order (each
+// thread's pieces in turn, then the block reduction).
+template <int PPT>
+__global__ __launch_bounds__(kQuantThreads) void k_quant_per_token_reg(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma, float eps,
+    uint8_t* __restrict__ xq, float* __restrict__ s_rows, int64_t K)
+{
+    __shared__ double lds[kQuantThreads / 64];
+    __shared__ float ldsf[kQuantThreads / 64];
+    const int64_t m = blockIdx.x;
+    const uint16_t* row = x + m * ldx;
+    const int nv = (int)(K >> 3);
+    uint4 in[PPT];
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+        const int v = threadIdx.x + p * kQuantThreads;
+        in[p] = v < nv ? *reinterpret_cast<const uint4*>(row + (int64_t)v * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float r = 1.0f;
+    if (gamma) {
+        double ss = 0.0;
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            const uint32_t w[4] = {in[p].x, in[p].y, in[p].z, in[p].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const double f = (double)bf16_to_f32((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
+                ss += f * f;                  // zero pieces past the row add exact zeros
+            }
+        }
+        ss = block_sum_f64(ss, lds);
+        r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+    }
+    float y[PPT][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+        const int v = threadIdx.x + p * kQuantThreads;
+        if (gamma) {
+            const uint4 g = v < nv ? *reinterpret_cast<const uint4*>(gamma + (int64_t)v * 8) : make_uint4(0u, 0u, 0u, 0u);
+            rms_apply8(in[p], g, r, y[p]);
+        } else {
+            const uint32_t w[4] = {in[p].x, in[p].y, in[p].z, in[p].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[p][i] = bf16_to_f32((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = finite_abs_max(amax, y[p][j]);   // zero pieces: no effect
+    }
+    amax = block_max_f32(amax, ldsf);
+    const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+    if (threadIdx.x == 0) s_rows[m] = s;
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+        const int v = threadIdx.x + p * kQuantThreads;
+        if (v >= nv) break;
+        uint32_t o[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j >> 2] |= quant_value(y[p][j], s) << ((j & 3) * 8);
+        *reinterpret_cast<uint2*>(xq + m * K + (int64_t)v * 8) = make_uint2(o[0], o[1]);
+    }
+}
+
 // ---- calibration: amax of the tensor that gets quantized -> s_act ----------
 
 __device__ __forceinline__ float finite_abs_max(float acc, float v)
@@ -462,6 +578,23 @@ void launch_act_scale(const uint16_t* x, int64_t ldx, const uint16_t* gamma, flo
                            x, ldx, M, K, partial);
     }
     hipLaunchKernelGGL(k_absmax_final, dim3(1), dim3(kQuantThreads), 0, stream, partial, np, s_act);
+}
+
+void launch_quant_per_token(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, uint8_t* xq,
+                            float* s_rows, int64_t M, int64_t K, hipStream_t stream)
+{
+    const int64_t ppt = ((K >> 3) + kQuantThreads - 1) / kQuantThreads;   // 16-byte pieces per thread
+    const dim3 grid((uint32_t)M), block(kQuantThreads);
+    if (ppt <= 1)
+        hipLaunchKernelGGL(k_quant_per_token_reg<1>, grid, block, 0, stream, x, ldx, gamma, eps, xq, s_rows, K);
+    else if (ppt <= 2)
+        hipLaunchKernelGGL(k_quant_per_token_reg<2>, grid, block, 0, stream, x, ldx, gamma, eps, xq, s_rows, K);
+    else if (ppt <= 4)
+        hipLaunchKernelGGL(k_quant_per_token_reg<4>, grid, block, 0, stream, x, ldx, gamma, eps, xq, s_rows, K);
+    else if (ppt <= 9)
+        hipLaunchKernelGGL(k_quant_per_token_reg<9>, grid, block, 0, stream, x, ldx, gamma, eps, xq, s_rows, K);
+    else
+        hipLaunchKernelGGL(k_quant_per_token, grid, block, 0, stream, x, ldx, gamma, eps, xq, s_rows, K);
 }
 
 void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, float s_act,

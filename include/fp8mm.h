@@ -229,6 +229,39 @@ int fp8_scaled_mm_merged_f32(const uint8_t* x_q, const uint8_t* w_q,
                              int64_t M, int64_t K,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Per-token dynamic activation scales: the scale granularity vllm.cpp #252
+ * leaves open ("What is owed", item 2: per-tensor vs per-channel vs
+ * per-token).  Each row is quantized as a tensor of its own:
+ *
+ *     s_rows[m] = fl32( amax_k |y[m,k]| / 448 )   (finite values; 1 when 0)
+ *     x_q[m,k]  = satRNE_E4M3( fl32( y[m,k] / s_rows[m] ) )
+ *
+ * with y = x (gamma == NULL) or the bf16 RMSNorm output of fp8_quant_rmsnorm.
+ * s_rows: DEVICE f32 [M] (4-byte aligned), written by the quant; it must not
+ * overlap x or x_q.  Other arguments and checks as fp8_quant_rmsnorm.
+ * ---------------------------------------------------------------------- */
+int fp8_quant_per_token(const uint16_t* x, int64_t ldx,
+                        const uint16_t* gamma, float eps,
+                        uint8_t* x_q, float* s_rows,
+                        int64_t M, int64_t K, hipStream_t stream);
+
+/* The GEMM with per-row activation scales (device s_rows [M], as written by
+ * fp8_quant_per_token):
+ *     out[m,n] = bf16_RNE( fl32( fl32(acc[m,n] * s_rows[m]) * s_w[n] ) )
+ * Same kernels, dispatcher and checks as fp8_scaled_mm / _merged. */
+int fp8_scaled_mm_per_token(const uint8_t* x_q, const uint8_t* w_q,
+                            const float* s_rows, const float* s_w,
+                            uint16_t* out, int64_t ldo,
+                            int64_t M, int64_t N, int64_t K,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int fp8_scaled_mm_merged_per_token(const uint8_t* x_q, const uint8_t* w_q,
+                                   const float* s_rows, const float* s_w,
+                                   const fp8_shard_t* shards, int num_shards,
+                                   int64_t M, int64_t K,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes fp8_scaled_mm / _merged need for (M, N, K) (N = sum n_i).
  * 0 when the chosen kernel needs none.  Pure host function. */
 size_t fp8_scaled_mm_workspace_bytes(int64_t M, int64_t N, int64_t K);

@@ -263,3 +263,27 @@ def test_f32_output_validation_fails_closed(fp8):
     assert call([Shard(17408, None, 17408)], M=1) == E
     assert call([Shard(16, D, 16)] * 9, n=9) == E
     assert g(A, B, 0.5, C, None, 1, 0, 5120, None, 0, None) == E
+
+
+def test_per_token_validation_fails_closed(fp8):
+    lib = fp8.raw_lib()
+    f = lib.fp8_quant_per_token
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    E, U = fp8.EINVAL, fp8.EUNSUPPORTED
+    assert f(A, 5120, None, 0.0, B, C, 0, 5120, None) == fp8.OK
+    assert f(A, 5120, None, 0.0, B, None, 8, 5120, None) == E          # no scale output
+    assert f(None, 5120, None, 0.0, B, C, 8, 5120, None) == E
+    assert f(A, 5000, None, 0.0, B, C, 8, 5120, None) == E             # ldx < K
+    assert f(A, 5120, C, float("nan"), B, C + 0x100000, 8, 5120, None) == E
+    assert f(A, 5120, None, 0.0, B, C + 2, 8, 5120, None) == U         # s_rows alignment
+    assert f(A, 5120, None, 0.0, B, C, 8, 5112 + 4, None) == U         # K % 16
+    assert f(A, 5120, None, 0.0, B, A + 64, 8, 5120, None) == E        # s_rows overlaps x
+    assert f(A, 5120, None, 0.0, B, B + 64, 8, 5120, None) == E        # s_rows overlaps x_q
+    g = lib.fp8_scaled_mm_per_token
+    g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert g(A, B, None, C, D, 10240, 0, 10240, 5120, None, 0, None) == fp8.OK
+    assert g(A, B, None, C, D, 10240, 8, 10240, 5120, None, 0, None) == E   # no per-row scales
+    assert g(A, B, C + 2, C, D, 10240, 8, 10240, 5120, None, 0, None) == U
+    assert g(A, B, C, C, D, 10244, 8, 10240, 5120, None, 0, None) == U      # bf16 rows: ldo % 8

@@ -421,6 +421,60 @@ def test_f32_merged_equals_split_and_strided(fp8, M):
     assert torch.all(big[:, :4] == -7) and torch.all(big[:, 516:520] == -7) and torch.all(big[:, 1052:] == -7)
 
 
+# ------------------------------------------------------ per-token scales ----
+
+@pytest.mark.parametrize("wid,M,K,rms", [(2, 8, 5120, False), (3, 1, 5120, True), (3, 32, 5120, True),
+                                         (3, 7, 17408, False), (5, 6576, 5120, True)])
+def test_per_token_quant_bit_exact(fp8, wid, M, K, rms):
+    x = wl.activation_bf16(wid, M, K, outliers=wid != 5)
+    if M >= 7:
+        x[1] = 0                                   # zero row: scale 1, codes 0
+        x[2] = 0xC040                              # constant row: +-448 everywhere
+        x[3, :4] = np.array([0x7F80, 0xFF80, 0x7FC0, 0x0001], np.uint16) if not rms else x[3, :4]
+    g = wl.gamma_bf16(wid, K) if rms else None
+    q, s = fp8.quant_per_token(bf16_dev(x), None if g is None else bf16_dev(g), wl.EPS)
+    q_ref, s_ref = oracle.quant_per_token(x, g, wl.EPS)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host_u8(q), q_ref), f"{int((host_u8(q) != q_ref).sum())} codes differ"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 10240, 5120), (8, 10240, 5120), (8, 5120, 17408), (33, 64, 400),
+                                   (300, 1040, 5120)])
+def test_per_token_gemm_against_oracle(fp8, M, N, K):
+    """Per-row scales in the epilogue, on both arms; with every row scale equal
+    the result is the per-tensor GEMM bit for bit."""
+    x = wl.activation_bf16(2, M, K, outliers=True)
+    q, s = oracle.quant_per_token(x)
+    wq, sw = oracle.quant_weight(wl.weight_f32(2, N, K))
+    qd, sd, wd, swd = u8_dev(q), f32_dev(s), u8_dev(wq), f32_dev(sw)
+    got = host_u16(fp8.scaled_mm_per_token(qd, wd, sd, swd))
+    rows = np.unique(np.linspace(0, M - 1, min(M, 24)).astype(int))
+    ref, v = oracle.scaled_mm_rows(q[rows], wq, s[rows], sw, want_v=True)
+    assert_within_tolerance(got[rows], ref, v, f"per-token M={M} N={N} K={K}")
+    same = np.full(M, s[0], np.float32)
+    a = host_u16(fp8.scaled_mm_per_token(qd, wd, f32_dev(same), swd))
+    b = host_u16(fp8.scaled_mm(qd, wd, float(s[0]), swd))
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_per_token_merged_equals_split(fp8, M):
+    K = 5120
+    xq = wl.random_codes(4, M, K, m=M)
+    wq = wl.random_codes(4, 1040, K, tensor=wl.T_W)
+    g = np.random.Generator(np.random.PCG64(2))
+    sw = (g.random(1040) * 1e-3 + 1e-5).astype(np.float32)
+    sr = (g.random(M) * 1e-2 + 1e-4).astype(np.float32)
+    xd, wd, swd, srd = u8_dev(xq), u8_dev(wq), f32_dev(sw), f32_dev(sr)
+    shards = [512, 16, 512]
+    merged = [host_u16(o) for o in fp8.scaled_mm_merged_per_token(xd, wd, srd, swd, shards)]
+    start = 0
+    for n, mo in zip(shards, merged):
+        split = host_u16(fp8.scaled_mm_per_token(xd, wd[start:start + n], srd, swd[start:start + n]))
+        assert np.array_equal(split, mo), f"shard at {start} differs"
+        start += n
+
+
 # ------------------------------------------------- merge and determinism ----
 
 @pytest.mark.parametrize("M", [1, 8, 32, 300])
