@@ -75,6 +75,8 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_silu_mul_quant.argtypes = [P, I64, P, I64, F32, I64, I64, P]
     L.oracle_quant_per_token.argtypes = [P, I64, P, F32, I64, I64, P, P]
     L.oracle_scaled_mm_rows.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P]
+    L.oracle_quant_weight_per_tensor.argtypes = [P, I64, I64, P, P]
+    L.oracle_requant_max_scale.argtypes = [P, P, P, ctypes.c_int, I64, P, P]
     L.oracle_num_threads.restype = ctypes.c_int
     return L
 
@@ -189,6 +191,45 @@ def quant_weight(w_f32: np.ndarray):
     sw = np.empty(N, np.float32)
     lib().oracle_quant_weight(_ptr(w), N, K, _ptr(wq), _ptr(sw))
     return wq, sw
+
+
+def quant_weight_per_tensor(w_f32: np.ndarray):
+    """Per-tensor E4M3 quant: returns (W_q uint8 [N,K], s float32 scalar)."""
+    w = _c(w_f32, np.float32)
+    N, K = w.shape
+    wq = np.empty((N, K), np.uint8)
+    s = np.empty(1, np.float32)
+    lib().oracle_quant_weight_per_tensor(_ptr(w), N, K, _ptr(wq), _ptr(s))
+    return wq, s[0]
+
+
+def requant_max_scale(wq: np.ndarray, rows, scales):
+    """Requantize the shards (``rows[i]`` weight rows with per-tensor scale
+    ``scales[i]``) of a merged [sum rows, K] weight to the largest scale:
+    returns (W_q' uint8 [sum rows, K], s_max float32)."""
+    w = _c(wq, np.uint8)
+    r = np.ascontiguousarray(rows, np.int64)
+    sc = np.ascontiguousarray(scales, np.float32)
+    assert r.shape == sc.shape and r.size >= 1 and int(r.sum()) == w.shape[0]
+    out = np.empty_like(w)
+    s = np.empty(1, np.float32)
+    lib().oracle_requant_max_scale(_ptr(w), _ptr(r), _ptr(sc), int(r.size), w.shape[1], _ptr(out), _ptr(s))
+    return out, s[0]
+
+
+def merged_max_scale_layer(x_bf16: np.ndarray, wq_shards, w_scales, in_scales, want_v: bool = False):
+    """One merged projection built the lossy way from shards that each carry a
+    per-tensor weight scale and a static input scale: the input is quantized
+    once at the largest input scale, the weight is requantized to the largest
+    weight scale, and one GEMM with that scale on every column runs.  Returns
+    (x_q, W_q', s_act, s_max, out[, v])."""
+    s_act = np.float32(max(np.float32(s) for s in in_scales))
+    xq = quant_act(x_bf16, float(s_act))
+    wq_cat = np.concatenate([_c(w, np.uint8) for w in wq_shards], axis=0)
+    wq2, s_max = requant_max_scale(wq_cat, [w.shape[0] for w in wq_shards], w_scales)
+    sw = np.full(wq2.shape[0], s_max, np.float32)
+    res = scaled_mm(xq, wq2, float(s_act), sw, want_v=want_v)
+    return (xq, wq2, s_act, s_max) + (res if want_v else (res,))
 
 
 # ------------------------------------------------------------------- GEMM ---

@@ -177,3 +177,29 @@ def scaled_mm_rows(xq, wq, s_rows, s_w):
     for a, s in zip(xq, s_rows):
         bits.append(scaled_mm([a], wq, s, s_w)[0][0])
     return bits
+
+
+# ------------------------------------------------- merged-shard requant ----
+
+def requant_max_scale(codes_by_shard, scales):
+    """Exact-rational requant of shards with per-tensor scales to the largest:
+    w = fl32(dec(c) * s_i), c' = nearest E4M3 (ties even, saturating) of
+    fl32(w / s_max), the sign of zero taken from c.  Returns (shards of codes,
+    s_max)."""
+    s_max = max(Fraction(s) for s in scales)
+    out = []
+    for rows, s in zip(codes_by_shard, scales):
+        si = Fraction(s)
+        o = []
+        for row in rows:
+            r = []
+            for c in row:
+                if (c & 0x7F) == 0x7F:
+                    r.append(c)                                   # NaN kept
+                    continue
+                w = fl32(e4m3_value(c) * si)
+                t = fl32(w / s_max)
+                r.append(e4m3_encode_exact(t, bool(c & 0x80)))
+            o.append(r)
+        out.append(o)
+    return out, float(s_max)

@@ -293,6 +293,51 @@ void oracle_quant_weight(const float* W, int64_t N, int64_t K, unsigned char* wq
     }
 }
 
+/* Per-tensor weight quant (one scale for the whole [N,K] weight, the scale
+ * form a checkpoint's q/k/v shards carry one each): s = fl32(amax |W| / 448)
+ * over every element (1 for an all-zero weight), W_q = satRNE_E4M3(fl32(W / s)).
+ * The same rule as the per-channel quant above, applied to the whole tensor. */
+void oracle_quant_weight_per_tensor(const float* W, int64_t N, int64_t K, unsigned char* wq, float* s_out)
+{
+    float amax = 0.0f, s;
+    for (int64_t i = 0; i < N * K; ++i) {
+        float a = fabsf(W[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) s = 1.0f; else s = amax / 448.0f;
+    *s_out = s;
+    for (int64_t i = 0; i < N * K; ++i) wq[i] = oracle_e4m3_encode(W[i] / s);
+}
+
+/* Requantize a merged weight whose shards carry different per-tensor scales to
+ * the largest of them, so that one per-tensor scale serves the whole merged
+ * projection (the lossy alternative to declining the merge that vllm.cpp #417,
+ * ranked follow-ons, contrasts with the exact split path).  Shard i holds rows
+ * [r_i, r_i + rows[i]) of the [sum rows, K] weight and has scale scales[i]:
+ *     s_max = max_i scales[i]
+ *     w     = fl32( dec(c) * scales[i] )          (the shard's f32 weight value)
+ *     c'    = satRNE_E4M3( fl32( w / s_max ) )    (the per-tensor quant of w at s_max)
+ * A NaN code is kept as it is.  Scales are finite and > 0. */
+void oracle_requant_max_scale(const unsigned char* wq, const int64_t* rows, const float* scales,
+                              int num_shards, int64_t K, unsigned char* out, float* s_max_out)
+{
+    float s_max = scales[0];
+    int64_t r0 = 0;
+    for (int i = 1; i < num_shards; ++i)
+        if (scales[i] > s_max) s_max = scales[i];
+    *s_max_out = s_max;
+    for (int i = 0; i < num_shards; ++i) {
+        for (int64_t e = r0 * K; e < (r0 + rows[i]) * K; ++e) {
+            double d = e4m3_value(wq[e]);
+            float w;
+            if (isnan(d)) { out[e] = wq[e]; continue; }
+            w = (float)d * scales[i];
+            out[e] = oracle_e4m3_encode(w / s_max);
+        }
+        r0 += rows[i];
+    }
+}
+
 /* ------------------------------------------------------------- GEMM ------- */
 
 /* out[m,n] = bf16_RNE( (acc * s_act) * s_w[n] ) with

@@ -50,6 +50,12 @@ MUTATIONS = {
                          "float hf = silu_f32(oracle_bf16_to_f32(up[m * ldu + i])) * oracle_bf16_to_f32(gate[m * ldg + i]);"),
     "per_token_tensor_amax": ("const float s = oracle_act_scale(row, ldx, gamma, eps, 1, K);",
                               "const float s = oracle_act_scale(x, ldx, gamma, eps, M, K);"),
+    "requant_to_min_scale": ("if (scales[i] > s_max) s_max = scales[i];", "if (scales[i] < s_max) s_max = scales[i];"),
+    "requant_drops_shard_scale": ("w = (float)d * scales[i];", "w = (float)d;"),
+    "requant_shard_offset": ("r0 += rows[i];", "r0 += rows[0];"),
+    "requant_reciprocal": ("out[e] = oracle_e4m3_encode(w / s_max);", "out[e] = oracle_e4m3_encode(w * (1.0f / s_max));"),
+    "per_tensor_amax_first_row": ("for (int64_t i = 0; i < N * K; ++i) {\n        float a = fabsf(W[i]);",
+                                  "for (int64_t i = 0; i < K; ++i) {\n        float a = fabsf(W[i]);"),
     "rows_scale_first_row": ("oracle_scaled_mm(xq + m * K, wq, s_rows[m], s_w,",
                              "oracle_scaled_mm(xq + m * K, wq, s_rows[0], s_w,"),
 }
@@ -78,6 +84,13 @@ PIN_TESTS = [
     pins.test_per_token_rows_are_independent_and_scale_covariant,
     pins.test_per_token_rmsnorm_row_is_the_static_quant_of_that_row,
     pins.test_rows_gemm_with_equal_scales_is_the_per_tensor_gemm,
+    pins.test_requant_brute_force_against_exact_rationals,
+    pins.test_requant_matches_ieee_steps_and_nearest_search,
+    pins.test_requant_equal_scales_is_the_identity,
+    pins.test_requant_power_of_two_ratio_closed_form,
+    pins.test_requant_sign_symmetry_and_monotone_in_the_ratio,
+    pins.test_weight_per_tensor_definition,
+    pins.test_max_scale_layer_with_equal_scales_is_the_exact_merge,
 ]
 
 

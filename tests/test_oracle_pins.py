@@ -459,3 +459,130 @@ def test_rows_gemm_with_equal_scales_is_the_per_tensor_gemm():
     a, va = oracle.scaled_mm(xq, wq, 0.0123, sw, want_v=True)
     b, vb = oracle.scaled_mm_rows(xq, wq, np.full(7, 0.0123, np.float32), sw, want_v=True)
     assert np.array_equal(a, b) and np.array_equal(va, vb)
+
+
+# ------------------------------------- merged shards, per-tensor scales ----
+# A merged projection whose shards carry one per-tensor weight scale each can
+# either keep every shard exact (expand the scales to per-channel form, or
+# decline the merge) or requantize every shard to the largest scale (lossy);
+# vllm.cpp #417, ranked follow-ons, contrasts the two.
+
+def _shard_rows_scales(g, rows):
+    """Per-tensor scales for shards: arbitrary fp32 values, one repeated (an
+    exact tie for the max), and a power-of-two ratio."""
+    sc = (g.random(len(rows)) * 1e-3 + 1e-5).astype(np.float32)
+    if len(rows) >= 3:
+        sc[2] = sc[0]
+    if len(rows) >= 4:
+        sc[3] = np.float32(sc[1] * np.float32(0.25))
+    return sc
+
+
+def test_requant_brute_force_against_exact_rationals():
+    g = np.random.Generator(np.random.PCG64(2718))
+    for it in range(60):
+        rows = [int(r) for r in g.integers(1, 4, size=int(g.integers(1, 5)))]
+        K = 6
+        codes = [wl.FINITE_CODE_VALUES[g.integers(0, 254, (r, K))] for r in rows]
+        if it % 5 == 0:
+            codes[0][0, :2] = (0x7F, 0xFF)                       # NaN codes are kept
+        sc = _shard_rows_scales(g, rows)
+        got, s_max = oracle.requant_max_scale(np.concatenate(codes), rows, sc)
+        want, s_max_e = exact.requant_max_scale([c.tolist() for c in codes], sc.tolist())
+        assert float(s_max) == s_max_e == float(sc.max())
+        assert np.array_equal(got, np.concatenate([np.array(w, np.uint8) for w in want])), it
+
+
+def test_requant_matches_ieee_steps_and_nearest_search():
+    """Large random case: numpy's IEEE fp32 multiply and divide, then the
+    exhaustive nearest search, give the oracle's bytes."""
+    g = np.random.Generator(np.random.PCG64(99))
+    rows = [96, 16, 16, 48]
+    K = 256
+    wq = wl.random_codes(3, sum(rows), K)
+    sc = _shard_rows_scales(g, rows)
+    got, s_max = oracle.requant_max_scale(wq, rows, sc)
+    per_row = np.repeat(sc, rows).astype(np.float32)
+    w = (oracle.e4m3_table()[wq].astype(np.float32) * per_row[:, None]).astype(np.float32)
+    t = (w / np.float32(sc.max())).astype(np.float32)
+    assert np.array_equal(got, _brute_force_encode(t))
+
+
+def test_requant_equal_scales_is_the_identity():
+    """Every finite code survives dequantize-then-requantize at its own scale
+    (the fp32 steps err by 2^-23 relative, far inside half an E4M3 step); the
+    shard that holds the largest scale is unchanged inside any merge."""
+    codes = wl.FINITE_CODE_VALUES.reshape(2, 127)
+    for s in (1.0, 0.02 / 448, 3.7e-5, 0.1234567, 7.5):
+        out, s_max = oracle.requant_max_scale(codes, [1, 1], [s, s])
+        assert np.array_equal(out, codes) and s_max == np.float32(s)
+    g = np.random.Generator(np.random.PCG64(5))
+    wq = wl.random_codes(3, 64, 128)
+    sc = np.array([3e-4, 9e-4, 1e-4], np.float32)
+    out, _ = oracle.requant_max_scale(wq, [16, 32, 16], sc)
+    assert np.array_equal(out[16:48], wq[16:48])
+    assert not np.array_equal(out[:16], wq[:16])
+
+
+def test_requant_power_of_two_ratio_closed_form():
+    """Scales 2^-7 and 2^(-7-j): the requantized value is dec(c) / 2^j exactly
+    before the E4M3 rounding.  Written on the bit fields: a normal result lowers
+    the exponent field by j; a subnormal result is round-half-even of
+    (value * 2^9) / 2^j on the integer grid m * 2^-9 (grid value 8 = code 0x08)."""
+    codes = wl.FINITE_CODE_VALUES
+    for j in (1, 2, 3, 5):
+        out, s_max = oracle.requant_max_scale(np.stack([codes, codes]), [1, 1], [2.0 ** -7, 2.0 ** (-7 - j)])
+        assert s_max == np.float32(2.0 ** -7)
+        assert np.array_equal(out[0], codes)
+        for c, got in zip(codes.tolist(), out[1].tolist()):
+            sgn, e, m = c & 0x80, (c >> 3) & 15, c & 7
+            if e > j:
+                want = sgn | ((c & 0x7F) - (j << 3))
+            else:
+                v9 = m if e == 0 else (8 + m) << (e - 1)           # value * 2^9, an integer
+                q, r = divmod(v9, 1 << j)
+                half = 1 << (j - 1)
+                q += 1 if (r > half or (r == half and q % 2 == 1)) else 0
+                want = sgn | q
+            assert got == want, (j, hex(c), hex(got), hex(want))
+
+
+def test_requant_sign_symmetry_and_monotone_in_the_ratio():
+    wq = wl.random_codes(3, 40, 96)
+    rows, sc = [8, 32], np.array([1e-3, 4.3e-4], np.float32)
+    a, _ = oracle.requant_max_scale(wq, rows, sc)
+    b, _ = oracle.requant_max_scale(wq ^ np.uint8(0x80), rows, sc)
+    assert np.array_equal(b, a ^ np.uint8(0x80))
+    # A smaller shard scale never gives a larger magnitude.
+    c, _ = oracle.requant_max_scale(wq, rows, np.array([1e-3, 2.1e-4], np.float32))
+    tab = oracle.e4m3_table()
+    assert np.all(np.abs(tab[c[8:]]) <= np.abs(tab[a[8:]]))
+
+
+def test_weight_per_tensor_definition():
+    w = wl.weight_f32(1, 96, 256)
+    w[40, 17] = np.float32(0.5)                                  # the tensor max, not in row 0
+    wq, s = oracle.quant_weight_per_tensor(w)
+    assert s == np.float32(0.5) / np.float32(448.0)
+    assert np.array_equal(wq, _brute_force_encode((w / s).astype(np.float32)))
+    assert oracle.quant_weight_per_tensor(np.zeros((4, 16), np.float32))[1] == 1.0
+    # Rows with equal amax: per-tensor == per-channel.
+    v = np.abs(wl.weight_f32(1, 8, 64))
+    v[:, 0] = np.float32(0.25)
+    q1, s1 = oracle.quant_weight_per_tensor(v)
+    q2, s2 = oracle.quant_weight(v)
+    assert np.array_equal(q1, q2) and np.all(s2 == s1)
+
+
+def test_max_scale_layer_with_equal_scales_is_the_exact_merge():
+    """Equal input and weight scales: the requantizing merge loses nothing, so
+    its output is the exact merged (and split) layer bit for bit."""
+    x = wl.activation_bf16(2, 4, 512, outliers=True)
+    shards = [wl.random_codes(3, n, 512, m=i) for i, n in enumerate((64, 16, 16))]
+    s_in = oracle.act_scale(x)
+    xq, wq2, s_act, s_max, out = oracle.merged_max_scale_layer(x, shards, [2e-4] * 3, [s_in] * 3)
+    assert s_act == np.float32(s_in) and s_max == np.float32(2e-4)
+    want = np.concatenate([oracle.scaled_mm(oracle.quant_act(x, s_in), w, s_in, np.full(w.shape[0], 2e-4,
+                                                                                          np.float32))
+                           for w in shards], axis=1)
+    assert np.array_equal(out, want)
