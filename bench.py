@@ -297,6 +297,72 @@ def bench_per_token(fp8, M, steps, warmup):
                         "gate_up_us": pg_ms * 1e3, "gate_up_TFLOPs": 2 * Mp * N1 * K / (pg_ms * 1e-3) / 1e12}}
 
 
+def bench_merge_policies(fp8, M, steps, warmup):
+    """Attention q/k/v (12288 | 1024 | 1024 rows, K=5120) whose shards carry
+    per-tensor weight scales and mismatched static input scales, at decode M:
+    the exact policy (merge declined: quant + GEMM per shard, 6 launches)
+    against the max-scale policy (one quant at the largest input scale, weights
+    requantized to the largest weight scale, one merged GEMM: 2 launches), with
+    the accuracy the max-scale merge gives up, measured against the exact split
+    outputs.  Weights rotate as in the main line."""
+    import numpy as np
+    import torch
+    import workloads as wl
+    shards, K = (12288, 1024, 1024), 5120
+    x = wl.activation_bf16(4, M, K, outliers=True)
+    xd = bf16_dev(x)
+    s_cal = float(fp8.act_scale(xd).item())
+    s_in = [float(np.float32(s_cal * f)) for f in (1.0, 1.5, 0.75)]
+    wqs, sws = [], []
+    for i, n in enumerate(shards):
+        w = wl.weight_f32(4, n, K, tensor=wl.T_SHARD0 + i) * np.float32((1.0, 0.5, 2.0)[i])
+        wq, s = fp8.quant_weight_per_tensor(f32_dev(w))
+        wqs.append(wq)
+        sws.append(float(s.item()))
+    merge, _ = fp8.merge_admit(s_in, fp8.MERGE_EXACT)
+    assert not merge
+    _, s_mx = fp8.merge_admit(s_in, fp8.MERGE_MAX_SCALE)
+    w_cat = torch.cat(wqs)
+    w_mx, sw_mx, _ = fp8.requant_max_scale(w_cat, shards, sws)
+    N = sum(shards)
+    copies = max(2, -(-2 * LLC_BYTES // (N * K)) + 1)
+    split_w = [[w] + [w.clone() for _ in range(copies - 1)] for w in wqs]
+    split_sw = [torch.full((n,), s, dtype=torch.float32, device="cuda") for n, s in zip(shards, sws)]
+    merged_w = [w_mx] + [w_mx.clone() for _ in range(copies - 1)]
+    xq_s = [torch.empty((M, K), dtype=torch.uint8, device="cuda") for _ in shards]
+    xq_m = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    out_s = [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for n in shards]
+    out_m = [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for n in shards]
+
+    def split(i):
+        for j in range(len(shards)):
+            fp8.quant(xd, s_in[j], out=xq_s[j])
+            fp8.scaled_mm(xq_s[j], split_w[j][i % copies], s_in[j], split_sw[j], out=out_s[j])
+
+    def merged(i):
+        fp8.quant(xd, s_mx, out=xq_m)
+        fp8.scaled_mm_merged(xq_m, merged_w[i % copies], s_mx, sw_mx, list(shards), outs=out_m)
+
+    split_ms = graph_time_ms(split, steps, warmup)
+    merged_ms = graph_time_ms(merged, steps, warmup)
+    split(0)
+    merged(0)
+    torch.cuda.synchronize()
+    ex = torch.cat(out_s, dim=1).float().cpu().numpy().astype(np.float64)
+    mx = torch.cat(out_m, dim=1).float().cpu().numpy().astype(np.float64)
+    row = np.sqrt((ex * ex).sum(axis=1, keepdims=True))
+    rel = np.abs(mx - ex) / row
+    wbytes = N * K
+    return {"workload": f"attn_qkv_M{M}_K{K}_N{N}_shards_12288_1024_1024",
+            "split_exact_us": split_ms * 1e3, "split_launches": 6,
+            "merged_max_scale_us": merged_ms * 1e3, "merged_launches": 2,
+            "split_over_merged_time": split_ms / merged_ms,
+            "weight_GBs": {"split": wbytes / (split_ms * 1e-3) / 1e9, "merged": wbytes / (merged_ms * 1e-3) / 1e9},
+            "max_scale_error_vs_exact": {"max_abs_over_row_norm": float(rel.max()),
+                                         "mean_abs_over_row_norm": float(rel.mean())},
+            "input_scales": s_in, "weight_scales": sws}
+
+
 def bench_sweep(fp8, layers, M, steps, warmup, wid=4):
     """Decode-step weight sweep: `layers` = ((count, projections), ...).  The
     distinct projections of each layer group get their own seeded weights
@@ -530,6 +596,7 @@ def main():
     if not a.no_prefill:
         line["prefill"] = bench_prefill(fp8, a.prefill_steps, a.warmup)
         line["per_token_scales"] = bench_per_token(fp8, a.M, a.steps, a.warmup)
+        line["merge_policies"] = bench_merge_policies(fp8, a.M, a.steps, a.warmup)
     if not a.no_sweep:
         import workloads as wl
         line["decode_step_sweep"] = {

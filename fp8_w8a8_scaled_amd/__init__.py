@@ -69,6 +69,12 @@ _act_scale_ws = _decl("fp8_act_scale_workspace_bytes", [_I64, _I64], _SZ)
 _act_scale = _decl("fp8_act_scale", [_P, _I64, _P, _F32, _I64, _I64, _P, _P, _SZ, _P])
 _silu_mul_quant = _decl("fp8_silu_mul_quant", [_P, _I64, _P, _I64, _F32, _P, _I64, _I64, _P])
 _act_scale_silu_mul = _decl("fp8_act_scale_silu_mul", [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _SZ, _P])
+_qw_tensor_ws = _decl("fp8_quant_weight_per_tensor_workspace_bytes", [_I64, _I64], _SZ)
+_qw_tensor = _decl("fp8_quant_weight_per_tensor", [_P, _I64, _I64, _P, _P, _P, _SZ, _P])
+_expand_scales = _decl("fp8_expand_shard_scales", [_P, _P, _I32, _P, _P])
+_requant_max = _decl("fp8_requant_max_scale", [_P, _P, _I64, _P, _P, _I32, _P, _P, _P])
+_merge_admit = _decl("fp8_merge_admit", [_P, _I32, _I32, _P])
+MERGE_EXACT, MERGE_MAX_SCALE = 0, 1
 
 
 class Fp8mmError(RuntimeError):
@@ -203,6 +209,69 @@ def quant_weight(w: torch.Tensor):
     sw = torch.empty(N, dtype=torch.float32, device=w.device)
     _check(_quant_weight(_ptr(w), N, K, _ptr(wq), _ptr(sw), _stream(w)), "fp8_quant_weight")
     return wq, sw
+
+
+# ------------------------------------- merged shards with per-tensor scales --
+
+def quant_weight_per_tensor(w: torch.Tensor):
+    """Per-tensor E4M3 quant of f32 w [N, K] -> (w_q uint8 [N, K], s f32 [1] on the device)."""
+    _need(w.is_cuda and w.dtype == torch.float32 and w.dim() == 2 and w.is_contiguous(),
+          "w must be a contiguous 2-D f32 CUDA tensor")
+    N, K = w.shape
+    wq = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws = torch.empty(max(int(_qw_tensor_ws(N, K)), 16), dtype=torch.uint8, device=w.device)
+    _check(_qw_tensor(_ptr(w), N, K, _ptr(wq), _ptr(s), _ptr(ws), ws.numel(), _stream(w)),
+           "fp8_quant_weight_per_tensor")
+    return wq, s
+
+
+def _host_shards(shard_rows: Sequence[int], shard_scales: Sequence[float]):
+    import numpy as np
+    r = np.ascontiguousarray(np.asarray(shard_rows, dtype=np.int64))
+    s = np.ascontiguousarray(np.asarray(shard_scales, dtype=np.float32))
+    _need(r.ndim == 1 and r.shape == s.shape and 1 <= r.size <= MAX_SHARDS, f"1..{MAX_SHARDS} shards")
+    return r, s
+
+
+def expand_shard_scales(shard_rows: Sequence[int], shard_scales: Sequence[float], device="cuda") -> torch.Tensor:
+    """Per-channel s_w f32 [sum rows] holding each shard's per-tensor scale (exact merge)."""
+    r, s = _host_shards(shard_rows, shard_scales)
+    sw = torch.empty(int(r.sum()), dtype=torch.float32, device=device)
+    _check(_expand_scales(r.ctypes.data, s.ctypes.data, r.size, _ptr(sw), _stream(sw)), "fp8_expand_shard_scales")
+    return sw
+
+
+def requant_max_scale(w_q: torch.Tensor, shard_rows: Sequence[int], shard_scales: Sequence[float],
+                      out: Optional[torch.Tensor] = None):
+    """Requantize the shards of a merged weight [sum rows, K] to the largest
+    shard scale (lossy merge): returns (w_q' uint8, s_w f32 [sum rows] filled
+    with s_max, s_max as a Python float).  ``out`` may be ``w_q`` (in place)."""
+    w_q = _codes(w_q, "w_q")
+    _need(w_q.is_cuda and w_q.dim() == 2 and w_q.is_contiguous(), "w_q must be contiguous [rows, K]")
+    r, s = _host_shards(shard_rows, shard_scales)
+    _need(int(r.sum()) == w_q.shape[0], "shard rows must sum to the weight rows")
+    if out is None:
+        out = torch.empty_like(w_q)
+    out = _codes(out, "out")
+    _need(out.is_contiguous() and out.shape == w_q.shape, "out must be contiguous like w_q")
+    sw = torch.empty(w_q.shape[0], dtype=torch.float32, device=w_q.device)
+    smax = ctypes.c_float(0.0)
+    _check(_requant_max(_ptr(w_q), _ptr(out), w_q.shape[1], r.ctypes.data, s.ctypes.data, r.size, _ptr(sw),
+                        ctypes.byref(smax), _stream(w_q)), "fp8_requant_max_scale")
+    return out, sw, float(smax.value)
+
+
+def merge_admit(input_scales: Sequence[float], policy: int = MERGE_EXACT):
+    """(merge?, s_act): whether projections with these static input scales run
+    as one merged launch under ``policy``, and the one input scale it uses."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(input_scales, dtype=np.float32))
+    s = ctypes.c_float(0.0)
+    st = _merge_admit(a.ctypes.data, a.size, int(policy), ctypes.byref(s))
+    if st < 0:
+        raise Fp8mmError(st, "fp8_merge_admit")
+    return bool(st), (float(s.value) if st == 1 else None)
 
 
 # --------------------------------------------------------------------- GEMM --

@@ -363,4 +363,120 @@ int fp8_act_scale(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float e
     return launch_status();
 }
 
+size_t fp8_quant_weight_per_tensor_workspace_bytes(int64_t N, int64_t K)
+{
+    if (N <= 0 || K <= 0) return 0;
+    return fp8mm::weight_absmax_partials(N, K) * sizeof(float);
+}
+
+int fp8_quant_weight_per_tensor(const float* w, int64_t N, int64_t K, uint8_t* w_q, float* s_w, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream)
+{
+    if (N < 0 || K < 0) return FP8MM_EINVAL;
+    if (K % 16 != 0) return FP8MM_EUNSUPPORTED;
+    if (N == 0 || K == 0) return FP8MM_EINVAL;           // no value to take a scale from
+    if (!w || !w_q || !s_w) return FP8MM_EINVAL;
+    if (N > ((int64_t)1 << 40) / K) return FP8MM_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < fp8_quant_weight_per_tensor_workspace_bytes(N, K)) return FP8MM_EWORKSPACE;
+    if (!aligned16(w) || !aligned16(w_q) || !aligned16(workspace) || (reinterpret_cast<uintptr_t>(s_w) & 3u))
+        return FP8MM_EUNSUPPORTED;
+    const size_t wb = (size_t)(N * K) * 4, qb = (size_t)(N * K), pb = workspace_bytes;
+    if (overlaps(w_q, qb, w, wb) || overlaps(s_w, 4, w, wb) || overlaps(s_w, 4, w_q, qb) ||
+        overlaps(workspace, pb, w, wb) || overlaps(workspace, pb, w_q, qb) || overlaps(workspace, pb, s_w, 4))
+        return FP8MM_EINVAL;
+    fp8mm::launch_quant_weight_per_tensor(w, N, K, w_q, s_w, static_cast<float*>(workspace), stream);
+    return launch_status();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Host shard table of per-tensor scales; rows and scales validated.
+int shard_scales_table(const int64_t* shard_rows, const float* shard_scales, int num_shards,
+                       fp8mm::ShardScales* tab)
+{
+    if (!shard_rows || !shard_scales || num_shards < 1 || num_shards > FP8MM_MAX_SHARDS) return FP8MM_EINVAL;
+    tab->num = num_shards;
+    int64_t r = 0;
+    for (int i = 0; i < num_shards; ++i) {
+        if (shard_rows[i] < 0 || !good_scale(shard_scales[i])) return FP8MM_EINVAL;
+        if (shard_rows[i] > ((int64_t)1 << 40)) return FP8MM_EUNSUPPORTED;
+        tab->start[i] = r;
+        tab->scale[i] = shard_scales[i];
+        r += shard_rows[i];
+    }
+    tab->start[num_shards] = r;
+    return FP8MM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_expand_shard_scales(const int64_t* shard_rows, const float* shard_scales, int num_shards, float* s_w,
+                            hipStream_t stream)
+{
+    fp8mm::ShardScales tab{};
+    const int st = shard_scales_table(shard_rows, shard_scales, num_shards, &tab);
+    if (st != FP8MM_OK) return st;
+    if (tab.start[num_shards] == 0) return FP8MM_OK;
+    if (!s_w) return FP8MM_EINVAL;
+    if (reinterpret_cast<uintptr_t>(s_w) & 3u) return FP8MM_EUNSUPPORTED;
+    fp8mm::launch_expand_shard_scales(tab, s_w, stream);
+    return launch_status();
+}
+
+int fp8_requant_max_scale(const uint8_t* w_q, uint8_t* w_out, int64_t K, const int64_t* shard_rows,
+                          const float* shard_scales, int num_shards, float* s_w, float* s_max_out,
+                          hipStream_t stream)
+{
+    fp8mm::ShardScales tab{};
+    const int st = shard_scales_table(shard_rows, shard_scales, num_shards, &tab);
+    if (st != FP8MM_OK) return st;
+    if (K < 0) return FP8MM_EINVAL;
+    if (K % 16 != 0) return FP8MM_EUNSUPPORTED;
+    float s_max = shard_scales[0];
+    for (int i = 1; i < num_shards; ++i) s_max = shard_scales[i] > s_max ? shard_scales[i] : s_max;
+    const int64_t rows = tab.start[num_shards];
+    if (rows > ((int64_t)1 << 40) / (K > 0 ? K : 1)) return FP8MM_EUNSUPPORTED;
+    if (rows > 0) {
+        if (!s_w || (K > 0 && (!w_q || !w_out))) return FP8MM_EINVAL;
+        if ((K > 0 && (!aligned16(w_q) || !aligned16(w_out))) || (reinterpret_cast<uintptr_t>(s_w) & 3u))
+            return FP8MM_EUNSUPPORTED;
+        const size_t wb = (size_t)(rows * K), sb = (size_t)rows * 4;
+        if (K > 0 && w_out != w_q && overlaps(w_out, wb, w_q, wb)) return FP8MM_EINVAL;
+        if (K > 0 && (overlaps(s_w, sb, w_q, wb) || overlaps(s_w, sb, w_out, wb))) return FP8MM_EINVAL;
+        if (K > 0) {
+            fp8mm::launch_requant_max_scale(w_q, w_out, tab, s_max, K, s_w, stream);
+        } else {
+            fp8mm::ShardScales one = tab;                  // no weight bytes: only the scale vector
+            for (int i = 0; i < num_shards; ++i) one.scale[i] = s_max;
+            fp8mm::launch_expand_shard_scales(one, s_w, stream);
+        }
+        const int ls = launch_status();
+        if (ls != FP8MM_OK) return ls;
+    }
+    if (s_max_out) *s_max_out = s_max;
+    return FP8MM_OK;
+}
+
+int fp8_merge_admit(const float* input_scales, int num_shards, int policy, float* s_act_out)
+{
+    if (!input_scales || !s_act_out || num_shards < 1 || num_shards > FP8MM_MAX_SHARDS) return FP8MM_EINVAL;
+    if (policy != FP8MM_MERGE_EXACT && policy != FP8MM_MERGE_MAX_SCALE) return FP8MM_EINVAL;
+    float s_max = input_scales[0];
+    for (int i = 0; i < num_shards; ++i) {
+        if (!good_scale(input_scales[i])) return FP8MM_EINVAL;
+        s_max = input_scales[i] > s_max ? input_scales[i] : s_max;
+    }
+    if (policy == FP8MM_MERGE_MAX_SCALE) {
+        *s_act_out = s_max;
+        return 1;
+    }
+    if (fp8_scales_bitwise_equal(input_scales, num_shards) != 1) return 0;
+    *s_act_out = input_scales[0];
+    return 1;
+}
+
 }  // extern "C"

@@ -54,6 +54,21 @@ bool silu_mul_uses_table(int64_t M, int64_t I, float s_act);
 void launch_act_scale_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, int64_t M,
                                int64_t I, float* s_act, float* partial, hipStream_t stream);
 
+// merge.hip: load-time weight preparation for merged shards with per-tensor
+// scales.  Shard i holds weight rows [start[i], start[i+1]) and has the
+// per-tensor scale scale[i].
+struct ShardScales {
+    int num;
+    float scale[FP8MM_MAX_SHARDS];
+    int64_t start[FP8MM_MAX_SHARDS + 1];
+};
+size_t weight_absmax_partials(int64_t N, int64_t K);
+void launch_quant_weight_per_tensor(const float* w, int64_t N, int64_t K, uint8_t* wq, float* s,
+                                    float* partial, hipStream_t stream);
+void launch_expand_shard_scales(const ShardScales& tab, float* s_w, hipStream_t stream);
+void launch_requant_max_scale(const uint8_t* in, uint8_t* out, const ShardScales& tab, float s_max, int64_t K,
+                              float* s_w, hipStream_t stream);
+
 // gemm_small_m.hip: memory-bound arm, M <= FP8MM_SMALL_M_MAX.
 void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
                          const ShardTable& shards, int64_t M, int64_t N, int64_t K,

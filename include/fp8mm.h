@@ -310,6 +310,65 @@ int fp8_act_scale(const uint16_t* x, int64_t ldx,
                   int64_t M, int64_t K, float* s_act,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Merged projections whose shards carry per-tensor scales (the q/k/v shards
+ * of an attention projection, or qkv and z): vllm.cpp #417, ranked follow-ons
+ * (one implementation keeps q/k/v apart unless their input scales are bitwise
+ * equal; another always merges and requantizes mismatched shards to the
+ * largest weight scale, which is lossy); vllm.cpp #213, "The GDN fp8 merge
+ * predicate FIRES".  All load-time calls except fp8_merge_admit (host only).
+ * ---------------------------------------------------------------------- */
+
+/* Per-tensor weight quantization (one scale for the whole weight):
+ *     *s_w     = fl32( max |w| / 448 )   over all N*K values (1 when all zero;
+ *                a NaN is skipped, an inf makes the scale inf)
+ *     w_q[n,k] = satRNE_E4M3( fl32( w[n,k] / *s_w ) )
+ * w: f32 [N, K]; w_q: E4M3 [N, K]; s_w: DEVICE f32 [1] (4-byte aligned).
+ * workspace: at least fp8_quant_weight_per_tensor_workspace_bytes(N, K) bytes,
+ * 16-byte aligned.  N == 0 or K == 0 is FP8MM_EINVAL (no value to take a scale
+ * from); K % 16 != 0 is FP8MM_EUNSUPPORTED. */
+size_t fp8_quant_weight_per_tensor_workspace_bytes(int64_t N, int64_t K);
+int fp8_quant_weight_per_tensor(const float* w, int64_t N, int64_t K,
+                                uint8_t* w_q, float* s_w,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Exact merge: expand per-tensor shard scales into the per-channel vector the
+ * GEMMs take, s_w[r] = shard_scales[i] for every weight row r of shard i.  A
+ * merged call with this s_w gives, column for column, the bits of a separate
+ * call per shard with that shard's scale.
+ * shard_rows, shard_scales: HOST arrays of num_shards (1..8) entries; rows >= 0,
+ * scales finite and > 0.  s_w: DEVICE f32 [sum shard_rows], 4-byte aligned. */
+int fp8_expand_shard_scales(const int64_t* shard_rows, const float* shard_scales, int num_shards,
+                            float* s_w, hipStream_t stream);
+
+/* Lossy merge: requantize every shard to the largest shard scale so that one
+ * per-tensor scale serves the whole merged weight:
+ *     s_max      = max_i shard_scales[i]
+ *     w_out[r,k] = satRNE_E4M3( fl32( fl32( dec(w_q[r,k]) * shard_scales[i] ) / s_max ) )
+ * for row r of shard i (NaN codes are copied).  Shards whose scale equals s_max
+ * come out unchanged; the others lose the low bits their smaller scale held.
+ * w_q, w_out: E4M3 [sum shard_rows, K] (w_out == w_q requantizes in place; any
+ * other overlap is FP8MM_EINVAL).  s_w: DEVICE f32 [sum shard_rows], filled with
+ * s_max (the per-channel form of the one scale).  *s_max_out (HOST, may be
+ * NULL) receives s_max.  K % 16 == 0, 16-byte aligned w_q / w_out. */
+int fp8_requant_max_scale(const uint8_t* w_q, uint8_t* w_out, int64_t K,
+                          const int64_t* shard_rows, const float* shard_scales, int num_shards,
+                          float* s_w, float* s_max_out, hipStream_t stream);
+
+/* Merge admission (host).  Projections that share one input each carry a
+ * static input scale; a merged launch quantizes the input once, so it needs one.
+ *   FP8MM_MERGE_EXACT: merge only when all input scales are bitwise equal
+ *     (returns 1, *s_act_out = that scale); otherwise returns 0: run each shard
+ *     as its own quant + GEMM at its own scale (exact).
+ *   FP8MM_MERGE_MAX_SCALE: always merge (returns 1) with *s_act_out = the
+ *     largest input scale (lossy for the shards with smaller scales: their
+ *     inputs are quantized on a coarser grid; none saturates).
+ * input_scales: HOST array of num_shards (1..8) finite scales > 0.
+ * FP8MM_EINVAL for a null pointer, a bad count or scale, another policy. */
+#define FP8MM_MERGE_EXACT 0
+#define FP8MM_MERGE_MAX_SCALE 1
+int fp8_merge_admit(const float* input_scales, int num_shards, int policy, float* s_act_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -306,6 +306,7 @@ void oracle_quant_weight_per_tensor(const float* W, int64_t N, int64_t K, unsign
     }
     if (amax == 0.0f) s = 1.0f; else s = amax / 448.0f;
     *s_out = s;
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < N * K; ++i) wq[i] = oracle_e4m3_encode(W[i] / s);
 }
 
@@ -327,6 +328,7 @@ void oracle_requant_max_scale(const unsigned char* wq, const int64_t* rows, cons
         if (scales[i] > s_max) s_max = scales[i];
     *s_max_out = s_max;
     for (int i = 0; i < num_shards; ++i) {
+#pragma omp parallel for schedule(static)
         for (int64_t e = r0 * K; e < (r0 + rows[i]) * K; ++e) {
             double d = e4m3_value(wq[e]);
             float w;

@@ -287,3 +287,72 @@ def test_per_token_validation_fails_closed(fp8):
     assert g(A, B, None, C, D, 10240, 8, 10240, 5120, None, 0, None) == E   # no per-row scales
     assert g(A, B, C + 2, C, D, 10240, 8, 10240, 5120, None, 0, None) == U
     assert g(A, B, C, C, D, 10244, 8, 10240, 5120, None, 0, None) == U      # bf16 rows: ldo % 8
+
+
+def test_merge_admit_policies(fp8):
+    """Exact policy: merge only on bitwise-equal input scales (vllm.cpp #213,
+    "merge predicate FIRES"); max-scale policy: always merge at the largest
+    input scale (vllm.cpp #417, ranked follow-ons)."""
+    a = np.float32(0.0123)
+    b = np.frombuffer(struct.pack("<I", struct.unpack("<I", struct.pack("<f", a))[0] + 1), np.float32)[0]
+    assert fp8.merge_admit([a, a, a]) == (True, float(a))
+    assert fp8.merge_admit([a, b, a]) == (False, None)                   # one ulp apart: split
+    assert fp8.merge_admit([a, b, a], fp8.MERGE_MAX_SCALE) == (True, float(b))
+    assert fp8.merge_admit([0.5, 2.0, 1.0], fp8.MERGE_MAX_SCALE) == (True, 2.0)
+    assert fp8.merge_admit([3.0]) == (True, 3.0)
+    for bad in ([], [0.0, 1.0], [1.0, -1.0], [float("nan")], [float("inf"), 1.0], [1.0] * 9):
+        for pol in (fp8.MERGE_EXACT, fp8.MERGE_MAX_SCALE):
+            with pytest.raises(fp8.Fp8mmError):
+                fp8.merge_admit(bad, pol)
+    with pytest.raises(fp8.Fp8mmError):
+        fp8.merge_admit([1.0, 1.0], 7)
+
+
+def test_shard_scale_calls_fail_closed(fp8):
+    lib = fp8.raw_lib()
+    E, U = fp8.EINVAL, fp8.EUNSUPPORTED
+    P = ctypes.c_void_p
+
+    def arr(vals, t):
+        a = np.ascontiguousarray(np.asarray(vals, dtype=t))
+        return a, a.ctypes.data
+
+    rows, pr = arr([64, 16, 16], np.int64)
+    sc, ps = arr([1e-3, 2e-3, 5e-4], np.float32)
+    zr, pz = arr([0, 0, 0], np.int64)
+    bad_sc, pbs = arr([1e-3, 0.0, 5e-4], np.float32)
+    neg, pn = arr([64, -16, 16], np.int64)
+    ex = lib.fp8_expand_shard_scales
+    ex.argtypes = [P, P, ctypes.c_int, P, P]
+    assert ex(pz, ps, 3, None, None) == fp8.OK                          # no rows: no-op
+    assert ex(pr, ps, 3, None, None) == E                                # no output
+    assert ex(pr, ps, 0, C, None) == E and ex(pr, ps, 9, C, None) == E   # shard count
+    assert ex(pr, pbs, 3, C, None) == E and ex(pn, ps, 3, C, None) == E
+    assert ex(None, ps, 3, C, None) == E and ex(pr, None, 3, C, None) == E
+    assert ex(pr, ps, 3, C + 2, None) == U                               # 4-byte alignment
+    rq = lib.fp8_requant_max_scale
+    rq.argtypes = [P, P, ctypes.c_int64, P, P, ctypes.c_int, P, P, P]
+    smax = ctypes.c_float(0.0)
+    assert rq(A, A, 5120, pz, ps, 3, C, ctypes.byref(smax), None) == fp8.OK   # no rows: only s_max
+    assert smax.value == np.float32(2e-3)
+    assert rq(A, B, 5120, pr, ps, 3, None, None, None) == E              # no s_w
+    assert rq(None, B, 5120, pr, ps, 3, C, None, None) == E
+    assert rq(A, B, 5120, pr, pbs, 3, C, None, None) == E
+    assert rq(A, B, 5112 + 4, pr, ps, 3, C, None, None) == U             # K % 16
+    assert rq(A, B + 8, 5120, pr, ps, 3, C, None, None) == U             # alignment
+    assert rq(A, A + 5120, 5120, pr, ps, 3, C, None, None) == E          # partial overlap in/out
+    assert rq(A, B, 5120, pr, ps, 3, A + 64, None, None) == E            # s_w overlaps the weight
+    assert rq(A, B, -16, pr, ps, 3, C, None, None) == E
+    qt = lib.fp8_quant_weight_per_tensor
+    qt.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P, P, ctypes.c_size_t, P]
+    wsb = lib.fp8_quant_weight_per_tensor_workspace_bytes
+    wsb.argtypes, wsb.restype = [ctypes.c_int64, ctypes.c_int64], ctypes.c_size_t
+    need = wsb(1024, 5120)
+    assert need >= 4 and wsb(0, 5120) == 0
+    assert qt(A, 0, 5120, B, C, D, need, None) == E                      # nothing to take a scale from
+    assert qt(A, 1024, 5112 + 4, B, C, D, need, None) == U
+    assert qt(None, 1024, 5120, B, C, D, need, None) == E
+    assert qt(A, 1024, 5120, B, C, D, need - 4, None) == fp8.EWORKSPACE
+    assert qt(A, 1024, 5120, B, C, None, need, None) == fp8.EWORKSPACE
+    assert qt(A, 1024, 5120, B, C + 2, D, need, None) == U
+    assert qt(A, 1024, 5120, A + 16, C, D, need, None) == E              # w_q overlaps w

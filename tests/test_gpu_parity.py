@@ -562,3 +562,132 @@ def test_fail_closed_on_device_tensors(fp8):
         fp8.quant(x, 1.0)
     assert e.value.status == fp8.EUNSUPPORTED
 
+
+
+# ------------------------------------- merged shards, per-tensor scales ----
+# Attention q/k/v of the pages' tower: one merged qkv of 14336 x 5120 rows,
+# split 12288 | 1024 | 1024, each shard with a per-tensor weight scale and its
+# own static input scale (vllm.cpp #417, ranked follow-ons).
+QKV_SHARDS = (12288, 1024, 1024)
+QKV_K = 5120
+IN_SCALE_FACTORS = (1.0, 1.5, 0.75)      # synthetic per-shard input scales around the calibrated one
+
+
+def _qkv_shard_f32(i):
+    return wl.weight_f32(4, QKV_SHARDS[i], QKV_K, tensor=wl.T_SHARD0 + i) * np.float32((1.0, 0.5, 2.0)[i])
+
+
+_QKV_REF = {}
+
+
+def _qkv_weights(fp8):
+    """Seeded f32 shards (N(0, 0.02), scaled by 1, 0.5 and 2 so their per-tensor
+    scales differ), quantized per tensor on the GPU and checked against the
+    oracle byte for byte; returns the oracle's codes and scales."""
+    codes, scales, devs = [], [], []
+    for i in range(len(QKV_SHARDS)):
+        w = _qkv_shard_f32(i)
+        wq_d, s_d = fp8.quant_weight_per_tensor(f32_dev(w))
+        if i not in _QKV_REF:
+            _QKV_REF[i] = oracle.quant_weight_per_tensor(w)
+        wq_ref, s_ref = _QKV_REF[i]
+        assert np.float32(s_d.item()).view(np.uint32) == np.float32(s_ref).view(np.uint32), i
+        assert np.array_equal(host_u8(wq_d), wq_ref), f"shard {i}: per-tensor codes differ"
+        codes.append(wq_ref)
+        scales.append(np.float32(s_ref))
+        devs.append(wq_d)
+    return codes, np.array(scales, np.float32), devs
+
+
+def test_quant_weight_per_tensor_bit_exact(fp8):
+    _qkv_weights(fp8)
+    # The tensor max in the last row, an all-zero weight and inf/NaN entries.
+    w = wl.weight_f32(4, 48, 256)
+    w[47, 255] = np.float32(-0.75)
+    for ww in (w, np.zeros((16, 64), np.float32)):
+        wq_d, s_d = fp8.quant_weight_per_tensor(f32_dev(ww))
+        wq_ref, s_ref = oracle.quant_weight_per_tensor(ww)
+        assert np.float32(s_d.item()) == s_ref and np.array_equal(host_u8(wq_d), wq_ref)
+    w2 = w.copy()
+    w2[3, 5] = np.nan                                              # skipped by the amax
+    wq_d, s_d = fp8.quant_weight_per_tensor(f32_dev(w2))
+    wq_ref, s_ref = oracle.quant_weight_per_tensor(w2)
+    assert np.float32(s_d.item()) == s_ref
+    ok = ~np.isnan(w2)
+    assert np.array_equal(host_u8(wq_d)[ok], wq_ref[ok]) and (host_u8(wq_d)[3, 5] & 0x7F) == 0x7F
+
+
+def test_requant_max_scale_bit_exact(fp8):
+    codes, scales, _ = _qkv_weights(fp8)
+    cat = np.concatenate(codes)
+    want, s_max = oracle.requant_max_scale(cat, QKV_SHARDS, scales)
+    d = u8_dev(cat)
+    got, sw, s_max_d = fp8.requant_max_scale(d, QKV_SHARDS, scales)
+    assert np.float32(s_max_d) == s_max == scales.max()
+    assert np.array_equal(host_u8(got), want), f"{int((host_u8(got) != want).sum())} codes differ"
+    assert np.all(sw.cpu().numpy() == s_max)
+    assert np.array_equal(host_u8(got)[:QKV_SHARDS[0]], cat[:QKV_SHARDS[0]]) or scales[0] != s_max
+    # In place gives the same bytes.
+    fp8.requant_max_scale(d, QKV_SHARDS, scales, out=d)
+    assert np.array_equal(host_u8(d), want)
+    # Every code (NaN codes included) under arbitrary and power-of-two scale ratios.
+    allc = np.tile(np.arange(256, dtype=np.uint8), 4).reshape(16, 64)
+    for sc in ([1e-3, 3.3e-4, 1e-3, 2.5e-4], [2.0 ** -7, 2.0 ** -9, 2.0 ** -8, 2.0 ** -12]):
+        want, _ = oracle.requant_max_scale(allc, [4, 4, 4, 4], sc)
+        got, _, _ = fp8.requant_max_scale(u8_dev(allc), [4, 4, 4, 4], sc)
+        assert np.array_equal(host_u8(got), want)
+
+
+@pytest.mark.parametrize("M", [1, 8, 96])
+def test_expanded_scales_merged_equals_split(fp8, M):
+    """Exact merge: per-tensor shard scales expanded to per-channel form give,
+    column for column, the bits of one GEMM per shard (both arms: M = 96 takes
+    the large-M kernel), and match the oracle."""
+    codes, scales, devs = _qkv_weights(fp8)
+    x = wl.activation_bf16(4, M, QKV_K, outliers=True)
+    s_in = oracle.act_scale(x)
+    xq = fp8.quant(bf16_dev(x), s_in)
+    sw = fp8.expand_shard_scales(QKV_SHARDS, scales)
+    assert np.array_equal(sw.cpu().numpy(), np.repeat(scales, QKV_SHARDS))
+    w_cat = u8_dev(np.concatenate(codes))
+    outs = fp8.scaled_mm_merged(xq, w_cat, s_in, sw, QKV_SHARDS)
+    xq_ref = oracle.quant_act(x, s_in)
+    for i, (n, o) in enumerate(zip(QKV_SHARDS, outs)):
+        one = fp8.scaled_mm(xq, devs[i], s_in, f32_dev(np.full(n, scales[i], np.float32)))
+        assert np.array_equal(host_u16(o), host_u16(one)), f"shard {i}: merged != split"
+        ref, v = oracle.scaled_mm(xq_ref, codes[i], s_in, np.full(n, scales[i], np.float32), want_v=True)
+        assert_within_tolerance(host_u16(o), ref, v, f"qkv shard {i} M={M}")
+
+
+@pytest.mark.parametrize("M", [8, 64])
+def test_merge_policies_end_to_end(fp8, M):
+    """Mismatched input scales.  Exact policy: the merge is declined and each
+    shard runs its own quant + GEMM at its own scale.  Max-scale policy: one
+    quant at the largest input scale, weights requantized to the largest weight
+    scale, one merged GEMM; quant and requant bytes bit-exact and outputs within
+    tolerance of the oracle's max-scale layer."""
+    codes, scales, devs = _qkv_weights(fp8)
+    x = wl.activation_bf16(4, M, QKV_K, outliers=True)
+    s_cal = oracle.act_scale(x)
+    s_in = [np.float32(s_cal * f) for f in IN_SCALE_FACTORS]
+    xd = bf16_dev(x)
+    merge, _ = fp8.merge_admit(s_in, fp8.MERGE_EXACT)
+    assert not merge
+    for i, n in enumerate(QKV_SHARDS):
+        xq = fp8.quant(xd, float(s_in[i]))
+        xq_ref = oracle.quant_act(x, s_in[i])
+        assert np.array_equal(host_u8(xq), xq_ref)
+        out = fp8.scaled_mm(xq, devs[i], float(s_in[i]), f32_dev(np.full(n, scales[i], np.float32)))
+        ref, v = oracle.scaled_mm(xq_ref, codes[i], s_in[i], np.full(n, scales[i], np.float32), want_v=True)
+        assert_within_tolerance(host_u16(out), ref, v, f"split shard {i} M={M}")
+    merge, s_act = fp8.merge_admit(s_in, fp8.MERGE_MAX_SCALE)
+    assert merge and np.float32(s_act) == max(s_in)
+    xq = fp8.quant(xd, s_act)
+    w2, sw, s_max = fp8.requant_max_scale(u8_dev(np.concatenate(codes)), QKV_SHARDS, scales)
+    outs = fp8.scaled_mm_merged(xq, w2, s_act, sw, QKV_SHARDS)
+    xq_ref, w2_ref, s_act_ref, s_max_ref, ref, v = oracle.merged_max_scale_layer(x, codes, scales, s_in,
+                                                                                 want_v=True)
+    assert np.float32(s_act) == s_act_ref and np.float32(s_max) == s_max_ref
+    assert np.array_equal(host_u8(xq), xq_ref) and np.array_equal(host_u8(w2), w2_ref)
+    got = np.concatenate([host_u16(o) for o in outs], axis=1)
+    assert_within_tolerance(got, ref, v, f"max-scale merged qkv M={M}")

@@ -17,7 +17,8 @@ Generator: numpy PCG64 seeded with the entropy list
 ``[0x5EED0000, workload_id, tensor_id, M]`` so every tensor is reproducible on
 its own.  Tensor ids: 0 weight, 1 activation, 2 gamma, 3 outlier positions,
 4 down-projection weight, 5 down-projection activation, 6 random codes,
-7 gate_up output (the SiLU*mul input), 64 + layer for the decode-step sweep.
+7 gate_up output (the SiLU*mul input), 32 + i for shard i of a merged weight
+whose shards are quantized per tensor, 64 + layer for the decode-step sweep.
 """
 from __future__ import annotations
 
@@ -28,6 +29,7 @@ import numpy as np
 
 SEED_BASE = 0x5EED0000
 T_W, T_X, T_GAMMA, T_OUTLIER, T_DOWN_W, T_DOWN_X, T_CODES, T_GATE_UP = 0, 1, 2, 3, 4, 5, 6, 7
+T_SHARD0 = 32
 T_LAYER0 = 64
 
 EPS = 1e-6
