@@ -126,43 +126,36 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
 
 
 // ---------------------------------------------------------------------------
-// Tiled kernel for K % 64 == 0 (every prefill shape of the layer).
+// Tiled kernel for K % 128 == 0 (every prefill shape of the layer).
 //
 // 256x256 output tile per 256-thread workgroup; wave (wn, wm) owns 128 rows of
 // W (n) x 128 rows of x_q (m) as 4x4 v_mfma_f32_32x32x64_f8f6f4 tiles with W
-// as the A operand (accumulators live in AGPRs).  K advances 64 bytes (one
-// MFMA depth) per stage through NSTAGE LDS stages filled by direct
-// global->LDS loads (global_load_lds_dwordx4: no staging registers, no LDS
-// store instructions), issued NSTAGE-1 stages ahead.  Fragment registers are
-// double-buffered: the 16 ds_read_b128 of stage k+1 are interleaved one-to-one
-// with the 16 MFMAs of stage k, so neither the LDS latency nor the barrier
-// leaves the matrix pipe idle.  LDS rows are 64 bytes with their four 16-byte
-// pieces XOR-swizzled by row (skipping one row bit: gfx950 LDS serves 16
-// lanes x 16 B per cycle) so fragment reads are bank-conflict free.
+// as the A operand (accumulators live in AGPRs).  K advances 128 bytes per
+// stage through two LDS stages of 64 KB filled by direct global->LDS loads
+// (global_load_lds_dwordx4: whole 128-byte lines, no staging registers).  A
+// stage is two sub-steps of 16 MFMAs (one 64-byte MFMA depth each); fragment
+// registers are double-buffered, so the 16 ds_read_b128 of the next sub-step
+// are interleaved one-to-one with the 16 MFMAs of the current one.
+// Stage boundary (before the last sub-step of stage kt reads stage kt+1):
+// wait until stage kt+1 has landed and this wave's reads of stage kt are
+// done, then a bare barrier; stage kt's buffer then takes stage kt+2, whose
+// 16 loads are issued one per MFMA of the following sub-step.  Issued as one
+// burst, those loads queue on the CU's one address unit and hold up every
+// wave's matrix pipe behind them (in-order issue); spread out they overlap
+// the MFMAs (measured 10% faster on the prefill gate_up shape).
+// sched_barrier fences keep each MFMA with its fragment read and its load.
+// LDS rows are 128 bytes with their eight 16-byte pieces XOR-swizzled by row
+// (skipping one row bit: gfx950 LDS serves 16 lanes x 16 B per cycle) so the
+// fragment reads are bank-conflict free.
 // Workgroups are renumbered so that each XCD (blocks are dealt to the 8 XCDs
 // round-robin) walks a contiguous range of tiles, in groups of GM row-tiles
 // that share W column tiles through L2.  The epilogue scales in fp32, stages
 // the bf16 tile in LDS and writes it with row-contiguous 16-byte stores.
 // Rows past M or N load a clamped (real) row and are never stored.
 // ---------------------------------------------------------------------------
-#ifndef FP8MM_LARGEM_TK
-#define FP8MM_LARGEM_TK 128
-#endif
-#ifndef FP8MM_LARGEM_NSTAGE
-#define FP8MM_LARGEM_NSTAGE 2
-#endif
-#ifndef FP8MM_LARGEM_SWZ
-#define FP8MM_LARGEM_SWZ 1          // row bits skipped by the XOR swizzle
-#endif
 #ifndef FP8MM_LARGEM_GM
 #define FP8MM_LARGEM_GM 8
 #endif
-#ifndef FP8MM_LARGEM_INTERLEAVE
-#define FP8MM_LARGEM_INTERLEAVE 1
-#endif
-// L2 prefetch distance in stages (0: off).  Each stage load is followed by two
-// 4-byte-per-lane direct-to-LDS loads that touch every 128-byte line of the
-// stage PF stages further on, so that its real loads hit L2.
 // 1: C tile stores marked non-temporal.  The workgroups finish their tiles at
 // about the same time, and the C tiles they write (4 MB per XCD per round)
 // would otherwise displace from L2 the operand panels the next round reads;
@@ -170,27 +163,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
 #ifndef FP8MM_LARGEM_NTSTORE
 #define FP8MM_LARGEM_NTSTORE 1
 #endif
-#ifndef FP8MM_LARGEM_PREFETCH
-#define FP8MM_LARGEM_PREFETCH 0
-#endif
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int T2 = 256;                      // tile rows of W and of x_q
-constexpr int TK = FP8MM_LARGEM_TK;          // K bytes per stage (S MFMA depths)
+constexpr int TK = 128;                      // K bytes per stage (two MFMA depths)
 constexpr int S_SUB = TK / 64;               // MFMA sub-steps per stage
-constexpr int NSTAGE = FP8MM_LARGEM_NSTAGE;
+constexpr int NSTAGE = 2;
 constexpr int PPR = TK / 16;                 // 16-byte pieces per LDS row
 constexpr int STAGE_BYTES = 2 * T2 * TK;     // W tile + x_q tile
 constexpr int ROWS_PER_INST = 64 / PPR;      // rows one direct-to-LDS instruction fills
-constexpr int LOADS_PER_STAGE = 2 * (T2 / ROWS_PER_INST) / 4;   // per wave
+constexpr int NQ = T2 / ROWS_PER_INST;       // instructions per operand tile
+constexpr int LOADS_PER_STAGE = 2 * NQ / 4;  // per wave
 constexpr int C_ROW = T2 * 2 + 16;           // padded bf16 C-tile row, bytes
 constexpr int C_BYTES = T2 * C_ROW;
-constexpr int LM_LDS = (NSTAGE * STAGE_BYTES + 2048 > C_BYTES) ? NSTAGE * STAGE_BYTES + 2048 : C_BYTES;
+constexpr int LM_LDS = (NSTAGE * STAGE_BYTES > C_BYTES) ? NSTAGE * STAGE_BYTES : C_BYTES;
+static_assert(S_SUB == 2 && LOADS_PER_STAGE == 16, "one stage load per MFMA of one sub-step");
+static_assert(LM_LDS <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ int swz(int row, int piece)
 {
-    return piece ^ ((row >> FP8MM_LARGEM_SWZ) & (PPR - 1));
+    return piece ^ ((row >> 1) & (PPR - 1));
 }
 
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -198,21 +191,15 @@ __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_c
 // s_waitcnt with only vmcnt constrained (expcnt = 7, lgkmcnt = 15: no wait).
 // The count must be a compile-time constant.
 #define FP8MM_VMCNT_IMM(n) ((((n) & 15) | ((((n) >> 4) & 3) << 14)) | (7 << 4) | (15 << 8))
-#define vmcnt_wait(n) __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_IMM(n))
 // same, and lgkmcnt(0): every LDS read of this wave has returned
 #define FP8MM_VMCNT_LGKM0_IMM(n) ((((n) & 15) | ((((n) >> 4) & 3) << 14)) | (7 << 4))
 
 // Per-lane byte offsets (row * K + piece * 16, 32-bit) of the rows this lane
 // moves for each of its NQ/4 direct-to-LDS instructions per operand; rows past
 // N or M are clamped to the last real row.  Fixed for a whole tile.
-constexpr int NQ = T2 / ROWS_PER_INST;               // instructions per operand tile
 struct RowOffsets {
     uint32_t w[NQ / 4], x[NQ / 4];
-    uint32_t pw, px;                                  // prefetch: row wave*64 + lane, piece 0
 };
-constexpr int PF_STAGES = FP8MM_LARGEM_PREFETCH;
-constexpr int PF_LOADS = PF_STAGES > 0 ? 2 : 0;      // prefetch loads per stage per wave
-constexpr int PF_JUNK = NSTAGE * STAGE_BYTES;        // LDS offset of the prefetch landing area
 
 __device__ __forceinline__ void row_offsets(RowOffsets& o, int64_t n0, int64_t m0, int64_t N, int64_t M,
                                             int64_t K, int wave, int lane)
@@ -227,109 +214,61 @@ __device__ __forceinline__ void row_offsets(RowOffsets& o, int64_t n0, int64_t m
         o.w[i] = (uint32_t)(gn * K + piece * 16);
         o.x[i] = (uint32_t)(gm * K + piece * 16);
     }
-    const int prow = wave * 64 + lane;                // 4 waves x 64 lanes = the 256 tile rows
-    const int64_t pn = n0 + prow < N ? n0 + prow : N - 1;
-    const int64_t pm = m0 + prow < M ? m0 + prow : M - 1;
-    o.pw = (uint32_t)(pn * K);
-    o.px = (uint32_t)(pm * K);
 }
 
-// Touch every 128-byte line of the W and x_q tile rows at K offset k (4 bytes
-// per row, landing in a scratch LDS area nobody reads).
-__device__ __forceinline__ void prefetch_stage(uint8_t* junk, const uint8_t* __restrict__ wq,
-                                               const uint8_t* __restrict__ xq, const RowOffsets& o, int64_t k,
-                                               int wave)
+// Load li (0..15) of the stage at K offset k0: even li fill W rows, odd li
+// x_q rows; instruction q = wave + 4 (li / 2) fills LDS rows q*ROWS_PER_INST..
+__device__ __forceinline__ void stage_load(int li, uint8_t* st, const uint8_t* __restrict__ wk,
+                                           const uint8_t* __restrict__ xk, const RowOffsets& o, int wave)
 {
-    if (PF_STAGES > 0) {
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wq + k + o.pw), (lds_void_t*)(junk + wave * 512),
-                                         4, 0, 0);
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(xq + k + o.px),
-                                         (lds_void_t*)(junk + wave * 512 + 256), 4, 0, 0);
-    }
-}
-
-// Issue one stage (K bytes [k0, k0+TK) of the W and x_q tiles).  Instruction
-// q = wave + 4i fills LDS rows q*ROWS_PER_INST.. of one operand.
-__device__ __forceinline__ void load_stage(uint8_t* st, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ xq,
-                                           const RowOffsets& o, int64_t k0, int wave)
-{
-    const uint8_t* wk = wq + k0;
-    const uint8_t* xk = xq + k0;
-#pragma unroll
-    for (int i = 0; i < NQ / 4; ++i) {
-        const int q = wave + 4 * i;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wk + o.w[i]), (lds_void_t*)(st + q * 1024),
-                                         16, 0, 0);
+    const int i = li >> 1, q = wave + 4 * i;
+    if ((li & 1) == 0)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wk + o.w[i]), (lds_void_t*)(st + q * 1024), 16,
+                                         0, 0);
+    else
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(xk + o.x[i]),
                                          (lds_void_t*)(st + T2 * TK + q * 1024), 16, 0, 0);
-    }
 }
 
 struct Frags {
     v8i a[4], b[4];
 };
 
-__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* __restrict__ st, int sub, int lane, int wn,
+// Fragment half h of MFMA operand f (0-3: W rows, 4-7: x_q rows) for
+// sub-step `sub` of a stage: lane l supplies row l % 32 and K bytes
+// [32 (l / 32), 32 (l / 32) + 32) of the 64-byte depth.
+__device__ __forceinline__ uint4 frag_half(const uint8_t* __restrict__ st, int f, int h, int sub, int lane, int wn,
                                            int wm)
 {
-    const int fr = lane & 31, p0 = sub * 4 + (lane >> 5) * 2;
-    const uint8_t* sW = st;
-    const uint8_t* sX = st + T2 * TK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = wn * 128 + i * 32 + fr;
-        f.a[i] = pack(lds16(sW + row * TK + swz(row, p0) * 16), lds16(sW + row * TK + swz(row, p0 + 1) * 16));
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = wm * 128 + j * 32 + fr;
-        f.b[j] = pack(lds16(sX + row * TK + swz(row, p0) * 16), lds16(sX + row * TK + swz(row, p0 + 1) * 16));
-    }
+    const int fr = lane & 31, p = sub * 4 + (lane >> 5) * 2 + h;
+    const int row = f < 4 ? wn * 128 + f * 32 + fr : wm * 128 + (f - 4) * 32 + fr;
+    const uint8_t* base = f < 4 ? st : st + T2 * TK;
+    return lds16(base + row * TK + swz(row, p) * 16);
 }
 
-__device__ __forceinline__ void mfma_frags(const Frags& f, v16f (&acc)[4][4])
+// One sub-step: the 16 MFMAs of `fc`, each followed by one 16-byte read of
+// the next sub-step's fragments (into `fn`) and, when `ld` is set, by one
+// load of the stage at K offset k_fill into `fill`.
+template <bool LD>
+__device__ __forceinline__ void substep(const uint8_t* __restrict__ frag_src, int sub_next, int lane, int wn, int wm,
+                                        const Frags& fc, Frags& fn, v16f (&acc)[4][4], uint8_t* fill,
+                                        const uint8_t* __restrict__ wk, const uint8_t* __restrict__ xk,
+                                        const RowOffsets& ro, int wave)
 {
+    uint4 t[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-}
-
-// Stage boundary, before the first fragment read of stage kt+1: wait until
-// stage kt+1 has landed for this wave (only its NSTAGE-2 newer stages may stay
-// in flight) and until this wave's fragment reads of stage kt are done, then
-// a barrier extends both to the workgroup, so stage kt's buffer can be
-// refilled with stage kt+NSTAGE.  A bare barrier: __syncthreads() would also
-// drain the stages that are meant to stay in flight.
-__device__ __forceinline__ void stage_boundary(uint8_t* fill, uint8_t* junk, const uint8_t* __restrict__ wq,
-                                               const uint8_t* __restrict__ xq, const RowOffsets& ro,
-                                               int64_t k_fill, int64_t k_pref, int wave)
-{
-    // issued after stage kt+1's loads: its prefetch, then NSTAGE-2 newer stages with theirs
-    __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_LGKM0_IMM(PF_LOADS + (NSTAGE - 2) * (LOADS_PER_STAGE + PF_LOADS)));
-    __builtin_amdgcn_s_barrier();
-    load_stage(fill, wq, xq, ro, k_fill, wave);
-    prefetch_stage(junk, wq, xq, ro, k_pref, wave);
-}
-
-// One MFMA sub-step: read the next sub-step's fragments into `fn` while the
-// 16 MFMAs of `fc` run, one fragment read per MFMA.  The two LDS pointers are
-// restrict-qualified: the fragment reads never touch the stage being filled,
-// which lets the compiler see they do not wait for those loads (the explicit
-// s_waitcnt and barrier order them after the loads of earlier stages).
-__device__ __forceinline__ void substep(const uint8_t* __restrict__ frag_src, int sub_next, int lane, int wn,
-                                        int wm, const Frags& fc, Frags& fn, v16f (&acc)[4][4])
-{
-    read_frags(fn, frag_src, sub_next, lane, wn, wm);
-    mfma_frags(fc, acc);
-#if FP8MM_LARGEM_INTERLEAVE
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int s = 0; s < 16; ++s) {
+        const int i = s >> 2, j = s & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+        t[s] = frag_half(frag_src, s >> 1, s & 1, sub_next, lane, wn, wm);
+        if (LD) stage_load(s, fill, wk, xk, ro, wave);
+        __builtin_amdgcn_sched_barrier(0);
     }
-#endif
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        fn.a[f] = pack(t[2 * f], t[2 * f + 1]);
+        fn.b[f] = pack(t[8 + 2 * f], t[8 + 2 * f + 1]);
+    }
 }
 
 __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
@@ -378,34 +317,33 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     RowOffsets ro;
     row_offsets(ro, n0, m0, N, M, K, wave, lane);
 #pragma unroll
-    for (int s = 0; s < NSTAGE; ++s) {                 // every stage load is followed by its prefetch
-        load_stage(smem + s * STAGE_BYTES, wq, xq, ro, kof(s), wave);
-        prefetch_stage(smem + PF_JUNK, wq, xq, ro, kof(s + PF_STAGES), wave);
-    }
-    vmcnt_wait(PF_LOADS + (NSTAGE - 1) * (LOADS_PER_STAGE + PF_LOADS));   // stage 0 landed for this wave
+    for (int s = 0; s < NSTAGE; ++s)
+#pragma unroll
+        for (int li = 0; li < LOADS_PER_STAGE; ++li)
+            stage_load(li, smem + s * STAGE_BYTES, wq + kof(s), xq + kof(s), ro, wave);
+    __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_IMM(LOADS_PER_STAGE));   // stage 0 landed for this wave
     __builtin_amdgcn_s_barrier();
 
-    // Sub-steps run in order (stage kt, sub-step s); fragments alternate
-    // between fa and fb, so the loop is unrolled over two sub-steps.
+    // Sub-steps run in order (stage kt: sub-step 0, boundary, sub-step 1);
+    // fragments alternate between fa and fb.
     Frags fa, fb;
-    read_frags(fa, smem, 0, lane, wn, wm);
-    const int nsub = nk * S_SUB;
-    auto one = [&](int g, const Frags& fc, Frags& fn) {
-        const int kt = g / S_SUB, sub = g % S_SUB;
-        if (sub == S_SUB - 1) {                        // next fragments come from stage kt+1
-            stage_boundary(smem + (kt % NSTAGE) * STAGE_BYTES, smem + PF_JUNK, wq, xq, ro, kof(kt + NSTAGE),
-                           kof(kt + NSTAGE + PF_STAGES), wave);
-            substep(smem + ((kt + 1) % NSTAGE) * STAGE_BYTES, 0, lane, wn, wm, fc, fn, acc);
-        } else {
-            substep(smem + (kt % NSTAGE) * STAGE_BYTES, sub + 1, lane, wn, wm, fc, fn, acc);
-        }
-    };
-    int g = 0;
-    for (; g + 2 <= nsub; g += 2) {
-        one(g, fa, fb);
-        one(g + 1, fb, fa);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        fa.a[f] = pack(frag_half(smem, f, 0, 0, lane, wn, wm), frag_half(smem, f, 1, 0, lane, wn, wm));
+        fa.b[f] = pack(frag_half(smem, 4 + f, 0, 0, lane, wn, wm), frag_half(smem, 4 + f, 1, 0, lane, wn, wm));
     }
-    if (g < nsub) one(g, fa, fb);                      // odd number of sub-steps
+    for (int kt = 0; kt < nk; ++kt) {
+        uint8_t* cur = smem + (kt & 1) * STAGE_BYTES;
+        uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE_BYTES;
+        // sub-step 0 of stage kt (its sub-step 1 fragments come from the same stage)
+        substep<false>(cur, 1, lane, wn, wm, fa, fb, acc, nullptr, nullptr, nullptr, ro, wave);
+        // boundary: stage kt+1 landed (the only stage in flight), stage kt fully read
+        __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_LGKM0_IMM(0));
+        __builtin_amdgcn_s_barrier();
+        // sub-step 1 of stage kt: fragments of stage kt+1, and the loads of stage kt+2 into stage kt's buffer
+        const int64_t k2 = kof(kt + 2);
+        substep<true>(nxt, 0, lane, wn, wm, fb, fa, acc, cur, wq + k2, xq + k2, ro, wave);
+    }
 
     // Epilogue: scale, round to bf16, stage the 256x256 tile in LDS (rows of
     // m, padded), then store rows with 16-byte, row-contiguous writes (an f32
