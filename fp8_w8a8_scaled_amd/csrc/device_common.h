@@ -64,6 +64,17 @@ __device__ __host__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two fp32 -> packed bf16 bits (lo in bits 0-15), round to nearest even, with
+// one gfx950 v_cvt_pk_bf16_f32.  Same bits as f32_to_bf16_rne for every
+// non-NaN input (a NaN stays a NaN of its sign).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
 // 8 bf16 values (one 16-byte load) -> 8 E4M3 codes of x / s (one 8-byte store).
 // A NaN input is encoded with its own sign bit (the sign of a NaN produced by a
 // division is not fixed by IEEE 754).

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
 // (global_load_lds_dwordx4: whole 128-byte lines, no staging registers).  A
 // stage is two sub-steps of 16 MFMAs (one 64-byte MFMA depth each); fragment
 // registers are double-buffered, so the 16 ds_read_b128 of the next sub-step
-// are interleaved one-to-one with the 16 MFMAs of the current one.
+// are interleaved with the first 8 MFMAs of the current one.
 // Stage boundary (before the last sub-step of stage kt reads stage kt+1):
 // wait until stage kt+1 has landed and this wave's reads of stage kt are
 // done, then a bare barrier; stage kt's buffer then takes stage kt+2, whose
@@ -149,13 +149,15 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
 // fragment reads are bank-conflict free.
 // Workgroups are renumbered so that each XCD (blocks are dealt to the 8 XCDs
 // round-robin) walks a contiguous range of tiles, in groups of GM row-tiles
-// that share W column tiles through L2.  The epilogue scales in fp32, stages
-// the bf16 tile in LDS and writes it with row-contiguous 16-byte stores.
+// that share W column tiles through L2.  The epilogue scales in fp32, rounds
+// pairs to bf16 with v_cvt_pk_bf16_f32, stages the tile in LDS and writes it
+// with row-contiguous 16-byte stores.
 // Rows past M or N load a clamped (real) row and are never stored.
 // ---------------------------------------------------------------------------
 #ifndef FP8MM_LARGEM_GM
 #define FP8MM_LARGEM_GM 8
 #endif
+
 // 1: C tile stores marked non-temporal.  The workgroups finish their tiles at
 // about the same time, and the C tiles they write (4 MB per XCD per round)
 // would otherwise displace from L2 the operand panels the next round reads;
@@ -246,8 +248,9 @@ __device__ __forceinline__ uint4 frag_half(const uint8_t* __restrict__ st, int f
     return lds16(base + row * TK + swz(row, p) * 16);
 }
 
-// One sub-step: the 16 MFMAs of `fc`, each followed by one 16-byte read of
-// the next sub-step's fragments (into `fn`) and, when `ld` is set, by one
+// One sub-step: the 16 MFMAs of `fc`; the first 8 are each followed by the two
+// 16-byte reads of one fragment of the next sub-step (into `fn`), so the reads
+// have landed before the sub-step ends, and, when LD is set, every MFMA by one
 // load of the stage at K offset k_fill into `fill`.
 template <bool LD>
 __device__ __forceinline__ void substep(const uint8_t* __restrict__ frag_src, int sub_next, int lane, int wn, int wm,
@@ -260,7 +263,10 @@ __device__ __forceinline__ void substep(const uint8_t* __restrict__ frag_src, in
     for (int s = 0; s < 16; ++s) {
         const int i = s >> 2, j = s & 3;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-        t[s] = frag_half(frag_src, s >> 1, s & 1, sub_next, lane, wn, wm);
+        if (s < 8) {
+            t[2 * s] = frag_half(frag_src, s, 0, sub_next, lane, wn, wm);
+            t[2 * s + 1] = frag_half(frag_src, s, 1, sub_next, lane, wn, wm);
+        }
         if (LD) stage_load(s, fill, wk, xk, ro, wave);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -417,10 +423,8 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
                 const int nl = wn * 128 + i * 32 + 8 * q + 4 * fh;
                 const float4 sw = swv[i][q];
                 const v16f& c = acc[i][j];
-                const uint32_t lo = f32_to_bf16_rne((c[4 * q + 0] * sa) * sw.x) |
-                                    (f32_to_bf16_rne((c[4 * q + 1] * sa) * sw.y) << 16);
-                const uint32_t hi = f32_to_bf16_rne((c[4 * q + 2] * sa) * sw.z) |
-                                    (f32_to_bf16_rne((c[4 * q + 3] * sa) * sw.w) << 16);
+                const uint32_t lo = pack_bf16x2((c[4 * q + 0] * sa) * sw.x, (c[4 * q + 1] * sa) * sw.y);
+                const uint32_t hi = pack_bf16x2((c[4 * q + 2] * sa) * sw.z, (c[4 * q + 3] * sa) * sw.w);
                 *reinterpret_cast<uint2*>(smem + ml * C_ROW + nl * 2) = make_uint2(lo, hi);
             }
     }
