@@ -168,20 +168,31 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int T2 = 256;                      // tile rows of W and of x_q
+constexpr int TW = 256;                      // tile rows of W (2 waves x 128)
 constexpr int TK = 128;                      // K bytes per stage (two MFMA depths)
-constexpr int S_SUB = TK / 64;               // MFMA sub-steps per stage
 constexpr int NSTAGE = 2;
 constexpr int PPR = TK / 16;                 // 16-byte pieces per LDS row
-constexpr int STAGE_BYTES = 2 * T2 * TK;     // W tile + x_q tile
 constexpr int ROWS_PER_INST = 64 / PPR;      // rows one direct-to-LDS instruction fills
-constexpr int NQ = T2 / ROWS_PER_INST;       // instructions per operand tile
-constexpr int LOADS_PER_STAGE = 2 * NQ / 4;  // per wave
-constexpr int C_ROW = T2 * 2 + 16;           // padded bf16 C-tile row, bytes
-constexpr int C_BYTES = T2 * C_ROW;
-constexpr int LM_LDS = (NSTAGE * STAGE_BYTES > C_BYTES) ? NSTAGE * STAGE_BYTES : C_BYTES;
-static_assert(S_SUB == 2 && LOADS_PER_STAGE == 16, "one stage load per MFMA of one sub-step");
-static_assert(LM_LDS <= 160 * 1024, "LDS budget");
+constexpr int WQ = TW / ROWS_PER_INST / 4;   // W loads per wave and stage
+
+// Tile shapes: NJ 32-row blocks of x_q per wave, so TX = 64 NJ rows of x_q per
+// tile (NJ = 4: 256x256 tiles; NJ = 3: 256x192, for shapes whose 256x256 tile
+// count leaves the last round of the persistent grid nearly empty).
+template <int NJ>
+struct Cfg {
+    static constexpr int TX = 64 * NJ;                        // tile rows of x_q
+    static constexpr int XQ = TX / ROWS_PER_INST / 4;         // x_q loads per wave and stage
+    static constexpr int LOADS = WQ + XQ;                     // loads per wave and stage
+    static constexpr int MF = 4 * NJ;                         // MFMAs per sub-step
+    static constexpr int NF = 4 + NJ;                         // fragments per sub-step
+    static constexpr int STAGE_BYTES = (TW + TX) * TK;        // W tile + x_q tile
+    static constexpr int C_ROW = TW * 2 + 16;                 // padded bf16 C row (one m), bytes
+    static constexpr int C_ROW32 = TW * 4 + 16;               // padded f32 C row, bytes
+    static constexpr int A = NSTAGE * STAGE_BYTES, B = TX * C_ROW, C = TX / 2 * C_ROW32;
+    static constexpr int LDS = A > B ? (A > C ? A : C) : (B > C ? B : C);
+    static_assert(NF <= MF && LOADS <= 2 * MF, "reads and loads fit the sub-step's MFMA slots");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
 
 __device__ __forceinline__ int swz(int row, int piece)
 {
@@ -197,90 +208,108 @@ __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_c
 #define FP8MM_VMCNT_LGKM0_IMM(n) ((((n) & 15) | ((((n) >> 4) & 3) << 14)) | (7 << 4))
 
 // Per-lane byte offsets (row * K + piece * 16, 32-bit) of the rows this lane
-// moves for each of its NQ/4 direct-to-LDS instructions per operand; rows past
-// N or M are clamped to the last real row.  Fixed for a whole tile.
+// moves for each of its direct-to-LDS instructions per operand; rows past N or
+// M are clamped to the last real row.  Fixed for a whole tile.
+template <int NJ>
 struct RowOffsets {
-    uint32_t w[NQ / 4], x[NQ / 4];
+    uint32_t w[WQ], x[Cfg<NJ>::XQ];
 };
 
-__device__ __forceinline__ void row_offsets(RowOffsets& o, int64_t n0, int64_t m0, int64_t N, int64_t M,
+template <int NJ>
+__device__ __forceinline__ void row_offsets(RowOffsets<NJ>& o, int64_t n0, int64_t m0, int64_t N, int64_t M,
                                             int64_t K, int wave, int lane)
 {
     const int lr = lane / PPR, lp = lane % PPR;       // row within instruction, physical piece
 #pragma unroll
-    for (int i = 0; i < NQ / 4; ++i) {
+    for (int i = 0; i < WQ; ++i) {
         const int row = (wave + 4 * i) * ROWS_PER_INST + lr;
-        const int piece = swz(row, lp);               // logical piece stored at physical lp
         const int64_t gn = n0 + row < N ? n0 + row : N - 1;
+        o.w[i] = (uint32_t)(gn * K + swz(row, lp) * 16);   // logical piece stored at physical lp
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg<NJ>::XQ; ++i) {
+        const int row = (wave + 4 * i) * ROWS_PER_INST + lr;
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
-        o.w[i] = (uint32_t)(gn * K + piece * 16);
-        o.x[i] = (uint32_t)(gm * K + piece * 16);
+        o.x[i] = (uint32_t)(gm * K + swz(row, lp) * 16);
     }
 }
 
-// Load li (0..15) of the stage at K offset k0: even li fill W rows, odd li
-// x_q rows; instruction q = wave + 4 (li / 2) fills LDS rows q*ROWS_PER_INST..
+// Load li of the stage at K offset k0 (wk = w_q + k0, xk = x_q + k0): li < WQ
+// fill W rows, the rest x_q rows; instruction q = wave + 4 i fills the LDS rows
+// q * ROWS_PER_INST.. of its operand tile.
+template <int NJ>
 __device__ __forceinline__ void stage_load(int li, uint8_t* st, const uint8_t* __restrict__ wk,
-                                           const uint8_t* __restrict__ xk, const RowOffsets& o, int wave)
+                                           const uint8_t* __restrict__ xk, const RowOffsets<NJ>& o, int wave)
 {
-    const int i = li >> 1, q = wave + 4 * i;
-    if ((li & 1) == 0)
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wk + o.w[i]), (lds_void_t*)(st + q * 1024), 16,
+    if (li < WQ) {
+        const int q = wave + 4 * li;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wk + o.w[li]), (lds_void_t*)(st + q * 1024), 16,
                                          0, 0);
-    else
+    } else {
+        const int i = li - WQ, q = wave + 4 * i;
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(xk + o.x[i]),
-                                         (lds_void_t*)(st + T2 * TK + q * 1024), 16, 0, 0);
+                                         (lds_void_t*)(st + TW * TK + q * 1024), 16, 0, 0);
+    }
 }
 
+template <int NJ>
 struct Frags {
-    v8i a[4], b[4];
+    v8i a[4], b[NJ];
 };
 
-// Fragment half h of MFMA operand f (0-3: W rows, 4-7: x_q rows) for
-// sub-step `sub` of a stage: lane l supplies row l % 32 and K bytes
-// [32 (l / 32), 32 (l / 32) + 32) of the 64-byte depth.
+// Fragment half h of MFMA operand f (0-3: W rows, 4..: x_q rows) for sub-step
+// `sub` of a stage: lane l supplies row l % 32 and K bytes [32 (l / 32),
+// 32 (l / 32) + 32) of the 64-byte depth.
+template <int NJ>
 __device__ __forceinline__ uint4 frag_half(const uint8_t* __restrict__ st, int f, int h, int sub, int lane, int wn,
                                            int wm)
 {
     const int fr = lane & 31, p = sub * 4 + (lane >> 5) * 2 + h;
-    const int row = f < 4 ? wn * 128 + f * 32 + fr : wm * 128 + (f - 4) * 32 + fr;
-    const uint8_t* base = f < 4 ? st : st + T2 * TK;
+    const int row = f < 4 ? wn * 128 + f * 32 + fr : wm * (32 * NJ) + (f - 4) * 32 + fr;
+    const uint8_t* base = f < 4 ? st : st + TW * TK;
     return lds16(base + row * TK + swz(row, p) * 16);
 }
 
-// One sub-step: the 16 MFMAs of `fc`; the first 8 are each followed by the two
-// 16-byte reads of one fragment of the next sub-step (into `fn`), so the reads
-// have landed before the sub-step ends, and, when LD is set, every MFMA by one
-// load of the stage at K offset k_fill into `fill`.
-template <bool LD>
+// One sub-step: the MF MFMAs of `fc`; the first NF are each followed by the
+// two 16-byte reads of one fragment of the next sub-step (into `fn`), so the
+// reads have landed before the sub-step ends, and, when LD is set, the
+// stage's LOADS loads (into `fill`) are spread over all MF MFMAs.
+template <int NJ, bool LD>
 __device__ __forceinline__ void substep(const uint8_t* __restrict__ frag_src, int sub_next, int lane, int wn, int wm,
-                                        const Frags& fc, Frags& fn, v16f (&acc)[4][4], uint8_t* fill,
+                                        const Frags<NJ>& fc, Frags<NJ>& fn, v16f (&acc)[4][NJ], uint8_t* fill,
                                         const uint8_t* __restrict__ wk, const uint8_t* __restrict__ xk,
-                                        const RowOffsets& ro, int wave)
+                                        const RowOffsets<NJ>& ro, int wave)
 {
-    uint4 t[16];
+    using C = Cfg<NJ>;
+    uint4 t[2 * C::NF];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-        const int i = s >> 2, j = s & 3;
+    for (int s = 0; s < C::MF; ++s) {
+        const int i = s / NJ, j = s % NJ;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-        if (s < 8) {
-            t[2 * s] = frag_half(frag_src, s, 0, sub_next, lane, wn, wm);
-            t[2 * s + 1] = frag_half(frag_src, s, 1, sub_next, lane, wn, wm);
+        if (s < C::NF) {
+            t[2 * s] = frag_half<NJ>(frag_src, s, 0, sub_next, lane, wn, wm);
+            t[2 * s + 1] = frag_half<NJ>(frag_src, s, 1, sub_next, lane, wn, wm);
         }
-        if (LD) stage_load(s, fill, wk, xk, ro, wave);
+        if (LD) {
+#pragma unroll
+            for (int li = s * C::LOADS / C::MF; li < (s + 1) * C::LOADS / C::MF; ++li)
+                stage_load<NJ>(li, fill, wk, xk, ro, wave);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        fn.a[f] = pack(t[2 * f], t[2 * f + 1]);
-        fn.b[f] = pack(t[8 + 2 * f], t[8 + 2 * f + 1]);
-    }
+    for (int f = 0; f < 4; ++f) fn.a[f] = pack(t[2 * f], t[2 * f + 1]);
+#pragma unroll
+    for (int f = 0; f < NJ; ++f) fn.b[f] = pack(t[8 + 2 * f], t[8 + 2 * f + 1]);
 }
 
+template <int NJ>
 __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act,
     const float* __restrict__ s_w, ShardTable sh, int64_t M, int64_t N, int64_t K)
 {
+    using C = Cfg<NJ>;
+    constexpr int TX = C::TX, HX = TX / 2;             // x_q rows per tile and per wave
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave & 1, wm = wave >> 1;
@@ -293,7 +322,7 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     // x_q row-tiles and W column-tiles whose K slices the concurrent
     // workgroups fetch at about the same time -- they meet in L2.
     const int nb = gridDim.x, bid = blockIdx.x;
-    const int num_m = (int)((M + T2 - 1) / T2), num_n = (int)((N + T2 - 1) / T2);
+    const int num_m = (int)((M + TX - 1) / TX), num_n = (int)((N + TW - 1) / TW);
     const int ntiles = num_m * num_n;
     const int xcd = bid & 7;
     const int nbx = (nb >> 3) + (xcd < (nb & 7) ? 1 : 0);
@@ -307,51 +336,52 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     const int gsz = (num_m - first_m) < GM ? (num_m - first_m) : GM;
     const int tm = first_m + (t % in_group) % gsz;
     const int tn = (t % in_group) / gsz;
-    const int64_t m0 = (int64_t)tm * T2, n0 = (int64_t)tn * T2;
+    const int64_t m0 = (int64_t)tm * TX, n0 = (int64_t)tn * TW;
 
-    v16f acc[4][4];
+    v16f acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int nk = (int)(K / TK);
     const int64_t k_last = (int64_t)(nk - 1) * TK;
     auto kof = [&](int st) { const int64_t k = (int64_t)st * TK; return k < k_last ? k : k_last; };
-    RowOffsets ro;
-    row_offsets(ro, n0, m0, N, M, K, wave, lane);
+    RowOffsets<NJ> ro;
+    row_offsets<NJ>(ro, n0, m0, N, M, K, wave, lane);
 #pragma unroll
     for (int s = 0; s < NSTAGE; ++s)
 #pragma unroll
-        for (int li = 0; li < LOADS_PER_STAGE; ++li)
-            stage_load(li, smem + s * STAGE_BYTES, wq + kof(s), xq + kof(s), ro, wave);
-    __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_IMM(LOADS_PER_STAGE));   // stage 0 landed for this wave
+        for (int li = 0; li < C::LOADS; ++li)
+            stage_load<NJ>(li, smem + s * C::STAGE_BYTES, wq + kof(s), xq + kof(s), ro, wave);
+    __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_IMM(C::LOADS));   // stage 0 landed for this wave
     __builtin_amdgcn_s_barrier();
 
     // Sub-steps run in order (stage kt: sub-step 0, boundary, sub-step 1);
     // fragments alternate between fa and fb.
-    Frags fa, fb;
+    Frags<NJ> fa, fb;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        fa.a[f] = pack(frag_half(smem, f, 0, 0, lane, wn, wm), frag_half(smem, f, 1, 0, lane, wn, wm));
-        fa.b[f] = pack(frag_half(smem, 4 + f, 0, 0, lane, wn, wm), frag_half(smem, 4 + f, 1, 0, lane, wn, wm));
-    }
+    for (int f = 0; f < 4; ++f)
+        fa.a[f] = pack(frag_half<NJ>(smem, f, 0, 0, lane, wn, wm), frag_half<NJ>(smem, f, 1, 0, lane, wn, wm));
+#pragma unroll
+    for (int f = 0; f < NJ; ++f)
+        fa.b[f] = pack(frag_half<NJ>(smem, 4 + f, 0, 0, lane, wn, wm), frag_half<NJ>(smem, 4 + f, 1, 0, lane, wn, wm));
     for (int kt = 0; kt < nk; ++kt) {
-        uint8_t* cur = smem + (kt & 1) * STAGE_BYTES;
-        uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE_BYTES;
+        uint8_t* cur = smem + (kt & 1) * C::STAGE_BYTES;
+        uint8_t* nxt = smem + ((kt + 1) & 1) * C::STAGE_BYTES;
         // sub-step 0 of stage kt (its sub-step 1 fragments come from the same stage)
-        substep<false>(cur, 1, lane, wn, wm, fa, fb, acc, nullptr, nullptr, nullptr, ro, wave);
+        substep<NJ, false>(cur, 1, lane, wn, wm, fa, fb, acc, nullptr, nullptr, nullptr, ro, wave);
         // boundary: stage kt+1 landed (the only stage in flight), stage kt fully read
         __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_LGKM0_IMM(0));
         __builtin_amdgcn_s_barrier();
         // sub-step 1 of stage kt: fragments of stage kt+1, and the loads of stage kt+2 into stage kt's buffer
         const int64_t k2 = kof(kt + 2);
-        substep<true>(nxt, 0, lane, wn, wm, fb, fa, acc, cur, wq + k2, xq + k2, ro, wave);
+        substep<NJ, true>(nxt, 0, lane, wn, wm, fb, fa, acc, cur, wq + k2, xq + k2, ro, wave);
     }
 
-    // Epilogue: scale, round to bf16, stage the 256x256 tile in LDS (rows of
+    // Epilogue: scale, round to bf16, stage the TX x 256 tile in LDS (rows of
     // m, padded), then store rows with 16-byte, row-contiguous writes (an f32
     // output in two halves: a whole f32 tile would not fit in LDS).
     __builtin_amdgcn_s_waitcnt(0);                     // retire the trailing (unused) stage loads
@@ -370,15 +400,13 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     // The loops below run row group j outermost, so only one activation scale
     // (per-tensor, or this lane's row's) is live at a time.
     if (sh.f32) {
-        // f32: the tile in two halves of 128 rows (the waves with wm == h hold
+        // f32: the tile in two halves of HX rows (the waves with wm == h hold
         // half h), each staged in LDS and stored with row-contiguous 16-byte writes
-        constexpr int C_ROW32 = T2 * 4 + 16;
-        static_assert(T2 / 2 * C_ROW32 <= LM_LDS, "f32 half tile must fit the LDS");
         for (int h = 0; h < 2; ++h) {
             if (wm == h) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float sa = row_scale(sh, min(m0 + wm * 128 + j * 32 + fr, M - 1), s_act);
+                for (int j = 0; j < NJ; ++j) {
+                    const float sa = row_scale(sh, min(m0 + wm * HX + j * 32 + fr, M - 1), s_act);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -386,7 +414,7 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
                             const int nl = wn * 128 + i * 32 + 8 * q + 4 * fh;
                             const float4 sw = swv[i][q];
                             const v16f& c = acc[i][j];
-                            *reinterpret_cast<float4*>(smem + (j * 32 + fr) * C_ROW32 + nl * 4) =
+                            *reinterpret_cast<float4*>(smem + (j * 32 + fr) * C::C_ROW32 + nl * 4) =
                                 make_float4((c[4 * q + 0] * sa) * sw.x, (c[4 * q + 1] * sa) * sw.y,
                                             (c[4 * q + 2] * sa) * sw.z, (c[4 * q + 3] * sa) * sw.w);
                         }
@@ -394,12 +422,12 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
             }
             __syncthreads();
 #pragma unroll 4
-            for (int c = threadIdx.x; c < T2 / 2 * T2 / 4; c += 256) {
+            for (int c = threadIdx.x; c < HX * TW / 4; c += 256) {
                 const int ml = c >> 6, nl = (c & 63) * 4;
-                const int64_t m = m0 + h * (T2 / 2) + ml, n = n0 + nl;
+                const int64_t m = m0 + h * HX + ml, n = n0 + nl;
                 if (m >= M || n >= N) continue;
                 const int si = shard_of(sh, n);
-                const uint4 v = *reinterpret_cast<const uint4*>(smem + ml * C_ROW32 + nl * 4);
+                const uint4 v = *reinterpret_cast<const uint4*>(smem + ml * C::C_ROW32 + nl * 4);
                 float* dst = static_cast<float*>(sh.out[si]) + m * sh.ldo[si] + (n - sh.start[si]);
 #if FP8MM_LARGEM_NTSTORE
                 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -413,9 +441,9 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
         continue;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float sa = row_scale(sh, min(m0 + wm * 128 + j * 32 + fr, M - 1), s_act);
-        const int ml = wm * 128 + j * 32 + fr;
+    for (int j = 0; j < NJ; ++j) {
+        const float sa = row_scale(sh, min(m0 + wm * HX + j * 32 + fr, M - 1), s_act);
+        const int ml = wm * HX + j * 32 + fr;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -425,18 +453,18 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
                 const v16f& c = acc[i][j];
                 const uint32_t lo = pack_bf16x2((c[4 * q + 0] * sa) * sw.x, (c[4 * q + 1] * sa) * sw.y);
                 const uint32_t hi = pack_bf16x2((c[4 * q + 2] * sa) * sw.z, (c[4 * q + 3] * sa) * sw.w);
-                *reinterpret_cast<uint2*>(smem + ml * C_ROW + nl * 2) = make_uint2(lo, hi);
+                *reinterpret_cast<uint2*>(smem + ml * C::C_ROW + nl * 2) = make_uint2(lo, hi);
             }
     }
     __syncthreads();
-    constexpr int CHUNKS = T2 * T2 * 2 / 16;           // 16-byte pieces of the tile
+    constexpr int CHUNKS = TX * TW * 2 / 16;           // 16-byte pieces of the tile
 #pragma unroll 4
     for (int c = threadIdx.x; c < CHUNKS; c += 256) {
         const int ml = c >> 5, nl = (c & 31) * 8;
         const int64_t m = m0 + ml, n = n0 + nl;
         if (m >= M || n >= N) continue;
         const int si = shard_of(sh, n);
-        const uint4 v = *reinterpret_cast<const uint4*>(smem + ml * C_ROW + nl * 2);
+        const uint4 v = *reinterpret_cast<const uint4*>(smem + ml * C::C_ROW + nl * 2);
         uint16_t* dst = static_cast<uint16_t*>(sh.out[si]) + m * sh.ldo[si] + (n - sh.start[si]);
 #if FP8MM_LARGEM_NTSTORE
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -465,21 +493,46 @@ int num_cus()
     return cache[dev];
 }
 
+// Rounds of the persistent grid times x_q rows per tile, for a tile of 64 nj
+// rows of x_q: the time the grid takes, in units of one 256x64 strip.
+static int64_t tiled_cost(int64_t M, int64_t N, int nj, int64_t cus)
+{
+    const int64_t tiles = ((M + 64 * nj - 1) / (64 * nj)) * ((N + TW - 1) / TW);
+    const int64_t grid = tiles < cus ? tiles : cus;
+    return ((tiles + grid - 1) / grid) * nj;
+}
+
+template <int NJ>
+static void launch_tiled(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
+                         const ShardTable& shards, int64_t M, int64_t N, int64_t K, int64_t cus, hipStream_t stream)
+{
+    static const bool attr = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_large_m_tiled<NJ>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        return true;
+    }();
+    (void)attr;
+    const int64_t tiles = ((M + Cfg<NJ>::TX - 1) / Cfg<NJ>::TX) * ((N + TW - 1) / TW);
+    const int64_t grid = tiles < cus ? tiles : cus;   // one resident workgroup per CU
+    hipLaunchKernelGGL(k_gemm_large_m_tiled<NJ>, dim3((uint32_t)grid), dim3(256), (size_t)Cfg<NJ>::LDS, stream, xq,
+                       wq, s_act, s_w, shards, M, N, K);
+}
+
 void launch_gemm_large_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
                          const ShardTable& shards, int64_t M, int64_t N, int64_t K, hipStream_t stream)
 {
     // the tiled kernel addresses operands with 32-bit row offsets
     if (K % TK == 0 && N * K < ((int64_t)1 << 32) && M * K < ((int64_t)1 << 32)) {
-        static const bool attr = [] {
-            (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_large_m_tiled),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-            return true;
-        }();
-        (void)attr;
-        const int64_t tiles = ((M + T2 - 1) / T2) * ((N + T2 - 1) / T2);
-        const int64_t grid = tiles < num_cus() ? tiles : num_cus();   // one resident workgroup per CU
-        hipLaunchKernelGGL(k_gemm_large_m_tiled, dim3((uint32_t)grid), dim3(256), (size_t)LM_LDS,
-                           stream, xq, wq, s_act, s_w, shards, M, N, K);
+        // 256x192 tiles when they cut the grid's time by at least 10% (their
+        // operand traffic per flop is about 17% higher): e.g. the prefill down
+        // projection, 26 x 20 = 520 tiles of 256x256 (2 full rounds and 8
+        // tiles on 256 CUs) against 35 x 20 = 700 of 256x192 (3 rounds of
+        // three-quarter tiles).
+        const int64_t cus = num_cus();
+        if (10 * tiled_cost(M, N, 3, cus) <= 9 * tiled_cost(M, N, 4, cus))
+            launch_tiled<3>(xq, wq, s_act, s_w, shards, M, N, K, cus, stream);
+        else
+            launch_tiled<4>(xq, wq, s_act, s_w, shards, M, N, K, cus, stream);
         return;
     }
     const dim3 grid((uint32_t)((N + BN - 1) / BN), (uint32_t)((M + BM - 1) / BM));
