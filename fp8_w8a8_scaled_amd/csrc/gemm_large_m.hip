@@ -191,6 +191,7 @@ struct Cfg {
     static constexpr int A = NSTAGE * STAGE_BYTES, B = TX * C_ROW, C = TX / 2 * C_ROW32;
     static constexpr int LDS = A > B ? (A > C ? A : C) : (B > C ? B : C);
     static_assert(NF <= MF && LOADS <= 2 * MF, "reads and loads fit the sub-step's MFMA slots");
+    static_assert((TX / 8) % 4 == 0 && (TX / 2 / 4) % 4 == 0, "epilogue rows per thread come in groups of 4");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -421,20 +422,38 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
                 }
             }
             __syncthreads();
-#pragma unroll 4
-            for (int c = threadIdx.x; c < HX * TW / 4; c += 256) {
-                const int ml = c >> 6, nl = (c & 63) * 4;
-                const int64_t m = m0 + h * HX + ml, n = n0 + nl;
-                if (m >= M || n >= N) continue;
+            // This thread's 4 columns are the same in every row it stores:
+            // shard, destination column and row stride are fixed per tile.
+            const int nl = (threadIdx.x & 63) * 4;
+            const int64_t n = n0 + nl;
+            if (n < N) {
                 const int si = shard_of(sh, n);
-                const uint4 v = *reinterpret_cast<const uint4*>(smem + ml * C::C_ROW32 + nl * 4);
-                float* dst = static_cast<float*>(sh.out[si]) + m * sh.ldo[si] + (n - sh.start[si]);
+                float* col = static_cast<float*>(sh.out[si]) + (n - sh.start[si]);
+                const int64_t ldo = sh.ldo[si];
+                // rows ml = threadIdx/64 + 4 r: four LDS reads, then their stores
+                // (rows past M are read but not stored)
+#pragma unroll
+                for (int g = 0; g < HX / 4; g += 4) {
+                    uint4 v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] = *reinterpret_cast<const uint4*>(smem + ((threadIdx.x >> 6) + 4 * (g + r)) * C::C_ROW32 +
+                                                               nl * 4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int64_t m = m0 + h * HX + (threadIdx.x >> 6) + 4 * (g + r);
+                        if (m < M) {
+                            float* dst = col + m * ldo;
 #if FP8MM_LARGEM_NTSTORE
-                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-                __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+                            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                            __builtin_nontemporal_store(u32x4{v[r].x, v[r].y, v[r].z, v[r].w},
+                                                        reinterpret_cast<u32x4*>(dst));
 #else
-                *reinterpret_cast<uint4*>(dst) = v;
+                            *reinterpret_cast<uint4*>(dst) = v[r];
 #endif
+                        }
+                    }
+                }
             }
             __syncthreads();                           // the LDS is reused (next half, next tile)
         }
@@ -457,21 +476,40 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
             }
     }
     __syncthreads();
-    constexpr int CHUNKS = TX * TW * 2 / 16;           // 16-byte pieces of the tile
-#pragma unroll 4
-    for (int c = threadIdx.x; c < CHUNKS; c += 256) {
-        const int ml = c >> 5, nl = (c & 31) * 8;
-        const int64_t m = m0 + ml, n = n0 + nl;
-        if (m >= M || n >= N) continue;
-        const int si = shard_of(sh, n);
-        const uint4 v = *reinterpret_cast<const uint4*>(smem + ml * C::C_ROW + nl * 2);
-        uint16_t* dst = static_cast<uint16_t*>(sh.out[si]) + m * sh.ldo[si] + (n - sh.start[si]);
+    {
+        // This thread's 8 columns are the same in every row it stores (rows
+        // advance by 8 per 256 threads): shard, destination column and row
+        // stride are fixed per tile, so the store loop carries no table lookup.
+        const int nl = (threadIdx.x & 31) * 8;
+        const int64_t n = n0 + nl;
+        if (n < N) {
+            const int si = shard_of(sh, n);
+            uint16_t* col = static_cast<uint16_t*>(sh.out[si]) + (n - sh.start[si]);
+            const int64_t ldo = sh.ldo[si];
+            // rows ml = threadIdx/32 + 8 r: four LDS reads, then their stores
+            // (rows past M are read but not stored)
+#pragma unroll
+            for (int g = 0; g < TX / 8; g += 4) {
+                uint4 v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[r] = *reinterpret_cast<const uint4*>(smem + ((threadIdx.x >> 5) + 8 * (g + r)) * C::C_ROW + nl * 2);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t m = m0 + (threadIdx.x >> 5) + 8 * (g + r);
+                    if (m < M) {
+                        uint16_t* dst = col + m * ldo;
 #if FP8MM_LARGEM_NTSTORE
-        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+                        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                        __builtin_nontemporal_store(u32x4{v[r].x, v[r].y, v[r].z, v[r].w},
+                                                    reinterpret_cast<u32x4*>(dst));
 #else
-        *reinterpret_cast<uint4*>(dst) = v;
+                        *reinterpret_cast<uint4*>(dst) = v[r];
 #endif
+                    }
+                }
+            }
+        }
     }
     __syncthreads();                                   // the next tile reuses the LDS
     }
