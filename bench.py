@@ -477,6 +477,27 @@ def summarize_trace(d, name, cmd):
     for r in rows:
         lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    # Runs: maximal sequences of back-to-back dispatches of one kernel (a graph
+    # replay of n launches of one kernel is one run of n), so a shape-specific
+    # average can be read next to the bench line's live per-launch figure.
+    tfiles = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if tfiles:
+        disp = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short(r["Kernel_Name"]))
+                       for r in csv.DictReader(open(tfiles[0]))), key=lambda x: x[0])
+        runs = []
+        for st, en, k in disp:
+            if runs and runs[-1][0] == k:
+                runs[-1][1].append(en - st)
+            else:
+                runs.append((k, [en - st]))
+        lines += ["", "Runs of at least 8 back-to-back dispatches of one kernel, in launch order (a graph replay of "
+                  "n launches of one kernel is one run of n; the bench replays each graph twice back to back, untimed then "
+                  "timed, so such a run holds 2n):", "",
+                  "| run | kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+        for i, (k, ds) in enumerate(runs):
+            if len(ds) >= 8:
+                lines.append(f"| {i} | {k} | {len(ds)} | {sum(ds) / len(ds) / 1e3:.2f} | {min(ds) / 1e3:.2f} | "
+                             f"{max(ds) / 1e3:.2f} |")
     out = os.path.join(PROFILES, f"{name}.md")
     os.makedirs(PROFILES, exist_ok=True)
     open(out, "w").write("\n".join(lines) + "\n")
