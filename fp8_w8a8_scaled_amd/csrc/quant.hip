@@ -10,6 +10,7 @@
 //
 // All kernels are memory-bound streaming passes: 16-byte bf16 loads, 8-byte
 // E4M3 stores, no LDS except for block reductions.
+#include "act_quant.h"
 #include "act_tables.h"
 #include "device_common.h"
 #include "internal.h"
@@ -18,7 +19,7 @@ namespace fp8mm {
 
 namespace {
 
-constexpr int kQuantThreads = 256;
+constexpr int kQuantThreads = kRmsRowThreads;
 
 // Fixed-order block reduction of a double (wave butterfly, then waves in order).
 __device__ double block_sum_f64(double v, double* lds)
@@ -54,32 +55,10 @@ __device__ float row_rms_inv(const uint16_t* __restrict__ row, int64_t K, float 
 {
     const int64_t nv = K >> 3;
     double ss = 0.0;
-    for (int64_t v = threadIdx.x; v < nv; v += blockDim.x) {
-        const uint4 in = *reinterpret_cast<const uint4*>(row + v * 8);
-        const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const double f = (double)bf16_to_f32((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
-            ss += f * f;                      // exact: a bf16 square has <= 16 bits
-        }
-    }
+    for (int64_t v = threadIdx.x; v < nv; v += blockDim.x)
+        ss = sumsq8(*reinterpret_cast<const uint4*>(row + v * 8), ss);
     ss = block_sum_f64(ss, lds);
-    return (float)(1.0 / sqrt(ss / (double)K + (double)eps));
-}
-
-// y_b = bf16(fl32(fl32(x * r) * gamma)) for 8 values; returns them as fp32.
-__device__ __forceinline__ void rms_apply8(const uint4 in, const uint4 g, float r, float y[8])
-{
-    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float xv = bf16_to_f32((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
-        const float gv = bf16_to_f32((gw[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
-        const float xn = xv * r;
-        const float yf = xn * gv;
-        y[i] = bf16_to_f32(f32_to_bf16_rne(yf));
-    }
+    return rms_inv(ss, K, eps);
 }
 
 __global__ __launch_bounds__(kQuantThreads) void k_quant_plain(
@@ -107,12 +86,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_rmsnorm(
     for (int64_t v = threadIdx.x; v < nv; v += blockDim.x) {
         const uint4 in = *reinterpret_cast<const uint4*>(row + v * 8);
         const uint4 g = *reinterpret_cast<const uint4*>(gamma + v * 8);
-        float y[8];
-        rms_apply8(in, g, r, y);
-        uint32_t o[2] = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i >> 2] |= f32_to_e4m3_sat(y[i] / s_act) << ((i & 3) * 8);
-        *reinterpret_cast<uint2*>(xq + m * K + v * 8) = make_uint2(o[0], o[1]);
+        *reinterpret_cast<uint2*>(xq + m * K + v * 8) = rms_quant8(in, g, r, s_act);
     }
 }
 
