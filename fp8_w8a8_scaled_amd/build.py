@@ -23,6 +23,7 @@ HIPCC_FLAGS = [
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
+    "-Werror=uninitialized", "-Werror=sometimes-uninitialized",
     "-I", os.path.join(ROOT, "include"),
 ]
 

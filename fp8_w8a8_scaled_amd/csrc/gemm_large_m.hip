@@ -312,7 +312,8 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     using C = Cfg<NJ>;
     constexpr int TX = C::TX, HX = TX / 2;             // x_q rows per tile and per wave
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar registers
     const int wn = wave & 1, wm = wave >> 1;
 
     // Persistent schedule.  Workgroups are dealt to the 8 XCDs round-robin, so
@@ -351,7 +352,13 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     const int64_t k_last = (int64_t)(nk - 1) * TK;
     auto kof = [&](int st) { const int64_t k = (int64_t)st * TK; return k < k_last ? k : k_last; };
     RowOffsets<NJ> ro;
-    row_offsets<NJ>(ro, n0, m0, N, M, K, wave, lane);
+    // The lane index passes through an empty asm statement, so the offsets'
+    // lane arithmetic is redone per tile rather than hoisted out of the tile
+    // loop: hoisted, its values live across the main loop and get spilled
+    // (and reloaded from scratch on every tile's critical path).
+    int rlane = lane;
+    __asm__ volatile("" : "+v"(rlane));
+    row_offsets<NJ>(ro, n0, m0, N, M, K, wave, rlane);
 #pragma unroll
     for (int s = 0; s < NSTAGE; ++s)
 #pragma unroll
@@ -387,7 +394,12 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     // output in two halves: a whole f32 tile would not fit in LDS).
     __builtin_amdgcn_s_waitcnt(0);                     // retire the trailing (unused) stage loads
     __syncthreads();                                   // every stage read by every wave
-    const int fr = lane & 31, fh = lane >> 5;
+    // The same for the epilogue's thread-index arithmetic (row and column
+    // indices, LDS addresses).
+    int tid = threadIdx.x;
+    __asm__ volatile("" : "+v"(tid));
+    const int fr = tid & 31, fh = (tid & 63) >> 5;
+    const int ewn = (tid >> 6) & 1, ewm = tid >> 7;    // this wave's wn, wm
     // 32x32 C layout with W as A: lane l holds column l%32 (= m) and rows
     // 8*(v/4) + 4*(l/32) + v%4 (= n): four consecutive n per v/4.
     float4 swv[4][4];                                  // all weight scales first, one wait
@@ -395,7 +407,7 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int64_t n = n0 + wn * 128 + i * 32 + 8 * q + 4 * fh;
+            const int64_t n = n0 + ewn * 128 + i * 32 + 8 * q + 4 * fh;
             swv[i][q] = *reinterpret_cast<const float4*>(s_w + (n < N ? n : 0));
         }
     // The loops below run row group j outermost, so only one activation scale
@@ -404,15 +416,15 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
         // f32: the tile in two halves of HX rows (the waves with wm == h hold
         // half h), each staged in LDS and stored with row-contiguous 16-byte writes
         for (int h = 0; h < 2; ++h) {
-            if (wm == h) {
+            if (ewm == h) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const float sa = row_scale(sh, min(m0 + wm * HX + j * 32 + fr, M - 1), s_act);
+                    const float sa = row_scale(sh, min(m0 + ewm * HX + j * 32 + fr, M - 1), s_act);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const int nl = wn * 128 + i * 32 + 8 * q + 4 * fh;
+                            const int nl = ewn * 128 + i * 32 + 8 * q + 4 * fh;
                             const float4 sw = swv[i][q];
                             const v16f& c = acc[i][j];
                             *reinterpret_cast<float4*>(smem + (j * 32 + fr) * C::C_ROW32 + nl * 4) =
@@ -424,7 +436,7 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
             __syncthreads();
             // This thread's 4 columns are the same in every row it stores:
             // shard, destination column and row stride are fixed per tile.
-            const int nl = (threadIdx.x & 63) * 4;
+            const int nl = (tid & 63) * 4;
             const int64_t n = n0 + nl;
             if (n < N) {
                 const int si = shard_of(sh, n);
@@ -437,11 +449,11 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
                     uint4 v[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        v[r] = *reinterpret_cast<const uint4*>(smem + ((threadIdx.x >> 6) + 4 * (g + r)) * C::C_ROW32 +
+                        v[r] = *reinterpret_cast<const uint4*>(smem + ((tid >> 6) + 4 * (g + r)) * C::C_ROW32 +
                                                                nl * 4);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int64_t m = m0 + h * HX + (threadIdx.x >> 6) + 4 * (g + r);
+                        const int64_t m = m0 + h * HX + (tid >> 6) + 4 * (g + r);
                         if (m < M) {
                             float* dst = col + m * ldo;
 #if FP8MM_LARGEM_NTSTORE
@@ -461,13 +473,13 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        const float sa = row_scale(sh, min(m0 + wm * HX + j * 32 + fr, M - 1), s_act);
-        const int ml = wm * HX + j * 32 + fr;
+        const float sa = row_scale(sh, min(m0 + ewm * HX + j * 32 + fr, M - 1), s_act);
+        const int ml = ewm * HX + j * 32 + fr;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int nl = wn * 128 + i * 32 + 8 * q + 4 * fh;
+                const int nl = ewn * 128 + i * 32 + 8 * q + 4 * fh;
                 const float4 sw = swv[i][q];
                 const v16f& c = acc[i][j];
                 const uint32_t lo = pack_bf16x2((c[4 * q + 0] * sa) * sw.x, (c[4 * q + 1] * sa) * sw.y);
@@ -480,7 +492,7 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
         // This thread's 8 columns are the same in every row it stores (rows
         // advance by 8 per 256 threads): shard, destination column and row
         // stride are fixed per tile, so the store loop carries no table lookup.
-        const int nl = (threadIdx.x & 31) * 8;
+        const int nl = (tid & 31) * 8;
         const int64_t n = n0 + nl;
         if (n < N) {
             const int si = shard_of(sh, n);
@@ -493,10 +505,10 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
                 uint4 v[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    v[r] = *reinterpret_cast<const uint4*>(smem + ((threadIdx.x >> 5) + 8 * (g + r)) * C::C_ROW + nl * 2);
+                    v[r] = *reinterpret_cast<const uint4*>(smem + ((tid >> 5) + 8 * (g + r)) * C::C_ROW + nl * 2);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int64_t m = m0 + (threadIdx.x >> 5) + 8 * (g + r);
+                    const int64_t m = m0 + (tid >> 5) + 8 * (g + r);
                     if (m < M) {
                         uint16_t* dst = col + m * ldo;
 #if FP8MM_LARGEM_NTSTORE
@@ -514,6 +526,7 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     __syncthreads();                                   // the next tile reuses the LDS
     }
 }
+
 
 }  // namespace
 
