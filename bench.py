@@ -46,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP8 scaled-MM: HBM GB/s at M≤8 (decode), FP8 TFLOPS at prefill M, % roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+REPLAYS = 10          # further timed replays of the roofline kernels' graphs (median and min reported)
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published (no sparsity)
 LLC_BYTES = 256 * 2 ** 20      # Infinity Cache to defeat
 PROFILES = os.path.join(ROOT, "profiles")
@@ -107,11 +108,12 @@ def f32_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
-def graph_time_ms(fn, n, warmup):
+def graph_time_ms(fn, n, warmup, replays=0):
     """Run `warmup` untimed eager calls of fn(i), capture n calls into one HIP
     graph, replay it once untimed, then time exactly one replay (n calls) with
     HIP events on the capture stream, bracketed by device synchronizations.
-    Returns ms per call."""
+    Returns ms per call; with replays > 0 also the ms per call of that many
+    further timed replays, as (first, [each])."""
     import torch
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
@@ -133,7 +135,24 @@ def graph_time_ms(fn, n, warmup):
         g.replay()
         e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n
+    first = e0.elapsed_time(e1) / n
+    if not replays:
+        return first
+    each = []
+    for _ in range(replays):
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        each.append(e0.elapsed_time(e1) / n)
+    return first, each
+
+
+def replay_stats(each_ms):
+    """Median and min (us per launch) over further graph replays."""
+    import statistics
+    return {"replays": len(each_ms), "median_us": statistics.median(each_ms) * 1e3, "min_us": min(each_ms) * 1e3}
 
 
 def load_traffic(name: str, kernel: str):
@@ -178,7 +197,7 @@ def bench_decode(fp8, M, steps, warmup):
         fp8.scaled_mm(xq, ws[i % copies], s_act, sw, out=out)
 
     ms = graph_time_ms(step, steps, warmup)
-    gemm_ms = graph_time_ms(gemm, steps, warmup)
+    gemm_ms, gemm_each = graph_time_ms(gemm, steps, warmup, replays=REPLAYS)
     step_bytes = gemm_bytes + quant_bytes
     achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
     traffic = load_traffic(f"decode_gemm_M{M}_K{K}_N{N}_pmc", "k_gemm_small_m_ring")
@@ -191,7 +210,8 @@ def bench_decode(fp8, M, steps, warmup):
                    "algorithmic_bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "kernel": "k_gemm_small_m_ring", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_us": gemm_ms * 1e3},
+                     "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_us": gemm_ms * 1e3,
+                     "further_replays": replay_stats(gemm_each)},
     }
 
 
@@ -226,9 +246,10 @@ def bench_prefill(fp8, steps, warmup):
         fp8.scaled_mm(xq2, wq2, s2, sw2, out=down)
 
     ms = graph_time_ms(step, steps, warmup)
-    gu_ms = graph_time_ms(lambda i: fp8.scaled_mm_merged(xq1, wq1, s1, sw1, [N1 // 2, N1 // 2], outs=[gate, up]),
-                          steps, warmup)
-    dn_ms = graph_time_ms(lambda i: fp8.scaled_mm(xq2, wq2, s2, sw2, out=down), steps, warmup)
+    gu_ms, gu_each = graph_time_ms(lambda i: fp8.scaled_mm_merged(xq1, wq1, s1, sw1, [N1 // 2, N1 // 2],
+                                                                  outs=[gate, up]), steps, warmup, replays=REPLAYS)
+    dn_ms, dn_each = graph_time_ms(lambda i: fp8.scaled_mm(xq2, wq2, s2, sw2, out=down), steps, warmup,
+                                   replays=REPLAYS)
     # A/B: the same merged gate_up launch with F32 outputs (twice the output bytes)
     gate32 = torch.empty((M, N1 // 2), dtype=torch.float32, device="cuda")
     up32 = torch.empty((M, N1 // 2), dtype=torch.float32, device="cuda")
@@ -244,6 +265,7 @@ def bench_prefill(fp8, steps, warmup):
         "step": "fused RMSNorm quant + merged gate_up GEMM + fused SiLU*mul quant + down GEMM (large-M arm), "
                 "graph-replayed",
         "gemm_tflops": {"gate_up": ach, "down": flops2 / (dn_ms * 1e-3) / 1e12},
+        "down_further_replays": replay_stats(dn_each),
         "silu_mul_quant": {"us": sq_ms * 1e3, "GBs": sq_bytes / (sq_ms * 1e-3) / 1e9},
         "f32_out_ab": {"gate_up_bf16_us": gu_ms * 1e3, "gate_up_f32_us": gu32_ms * 1e3,
                        "out_bytes_bf16": 2 * M * N1, "out_bytes_f32": 4 * M * N1,
@@ -254,7 +276,8 @@ def bench_prefill(fp8, steps, warmup):
         "roofline": {"bound": "mfma", "kernel": "k_gemm_large_m_tiled (gate_up)", "achieved": ach,
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / FP8_PEAK_TFLOPS,
                      "traffic": load_traffic("prefill_gateup_M6576_K5120_N34816_pmc", "k_gemm_large_m_tiled"),
-                     "algorithmic_flops_per_launch": flops1, "avg_launch_us": gu_ms * 1e3},
+                     "algorithmic_flops_per_launch": flops1, "avg_launch_us": gu_ms * 1e3,
+                     "further_replays": replay_stats(gu_each)},
     }
 
 
