@@ -208,48 +208,49 @@ __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_c
 // same, and lgkmcnt(0): every LDS read of this wave has returned
 #define FP8MM_VMCNT_LGKM0_IMM(n) ((((n) & 15) | ((((n) >> 4) & 3) << 14)) | (7 << 4))
 
-// Per-lane byte offsets (row * K + piece * 16, 32-bit) of the rows this lane
-// moves for each of its direct-to-LDS instructions per operand; rows past N or
-// M are clamped to the last real row.  Fixed for a whole tile.
+// Operand addressing of one tile.  The lane's load i of an operand moves
+// LDS row (wave + 4 i) * ROWS_PER_INST + lane / PPR, i.e. global row
+// row0 + 32 i: byte offset w0 (x0) + i * step in the operand's buffer, plus the
+// stage's K offset.  The XOR swizzle of the piece uses row bits 1..3 only, so
+// it is the same for all i.  Rows past N (M) fall past the end of the buffer
+// resource and load zeros; their results are never stored.  Offsets are
+// 32-bit (N K, M K < 2^32); an offset that wraps around for such a row stays
+// inside the buffer, so no load leaves its buffer.
 template <int NJ>
 struct RowOffsets {
-    uint32_t w[WQ], x[Cfg<NJ>::XQ];
+    uint32_t w0, x0, step;
 };
 
-template <int NJ>
-__device__ __forceinline__ void row_offsets(RowOffsets<NJ>& o, int64_t n0, int64_t m0, int64_t N, int64_t M,
-                                            int64_t K, int wave, int lane)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const uint8_t* p, int64_t bytes)
 {
-    const int lr = lane / PPR, lp = lane % PPR;       // row within instruction, physical piece
-#pragma unroll
-    for (int i = 0; i < WQ; ++i) {
-        const int row = (wave + 4 * i) * ROWS_PER_INST + lr;
-        const int64_t gn = n0 + row < N ? n0 + row : N - 1;
-        o.w[i] = (uint32_t)(gn * K + swz(row, lp) * 16);   // logical piece stored at physical lp
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg<NJ>::XQ; ++i) {
-        const int row = (wave + 4 * i) * ROWS_PER_INST + lr;
-        const int64_t gm = m0 + row < M ? m0 + row : M - 1;
-        o.x[i] = (uint32_t)(gm * K + swz(row, lp) * 16);
-    }
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
 }
 
-// Load li of the stage at K offset k0 (wk = w_q + k0, xk = x_q + k0): li < WQ
-// fill W rows, the rest x_q rows; instruction q = wave + 4 i fills the LDS rows
-// q * ROWS_PER_INST.. of its operand tile.
 template <int NJ>
-__device__ __forceinline__ void stage_load(int li, uint8_t* st, const uint8_t* __restrict__ wk,
-                                           const uint8_t* __restrict__ xk, const RowOffsets<NJ>& o, int wave)
+__device__ __forceinline__ void row_offsets(RowOffsets<NJ>& o, int64_t n0, int64_t m0, int64_t K, int wave, int lane)
+{
+    const int lr = lane / PPR, lp = lane % PPR;       // row within instruction, physical piece
+    const int row = wave * ROWS_PER_INST + lr;
+    o.w0 = (uint32_t)((n0 + row) * K + swz(row, lp) * 16);   // logical piece stored at physical lp
+    o.x0 = (uint32_t)((m0 + row) * K + swz(row, lp) * 16);
+    o.step = (uint32_t)(4 * ROWS_PER_INST * K);
+}
+
+// Load li of the stage at K offset k: li < WQ fill W rows, the rest x_q rows;
+// instruction q = wave + 4 i fills the LDS rows q * ROWS_PER_INST.. of its
+// operand tile.
+template <int NJ>
+__device__ __forceinline__ void stage_load(int li, uint8_t* st, uint32_t k, __amdgpu_buffer_rsrc_t rw,
+                                           __amdgpu_buffer_rsrc_t rx, const RowOffsets<NJ>& o, int wave)
 {
     if (li < WQ) {
         const int q = wave + 4 * li;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(wk + o.w[li]), (lds_void_t*)(st + q * 1024), 16,
-                                         0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(st + q * 1024), 16,
+                                                 (int)(o.w0 + (uint32_t)li * o.step + k), 0, 0, 0);
     } else {
         const int i = li - WQ, q = wave + 4 * i;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(xk + o.x[i]),
-                                         (lds_void_t*)(st + TW * TK + q * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(st + TW * TK + q * 1024), 16,
+                                                 (int)(o.x0 + (uint32_t)i * o.step + k), 0, 0, 0);
     }
 }
 
@@ -278,7 +279,7 @@ __device__ __forceinline__ uint4 frag_half(const uint8_t* __restrict__ st, int f
 template <int NJ, bool LD>
 __device__ __forceinline__ void substep(const uint8_t* __restrict__ frag_src, int sub_next, int lane, int wn, int wm,
                                         const Frags<NJ>& fc, Frags<NJ>& fn, v16f (&acc)[4][NJ], uint8_t* fill,
-                                        const uint8_t* __restrict__ wk, const uint8_t* __restrict__ xk,
+                                        uint32_t k, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx,
                                         const RowOffsets<NJ>& ro, int wave)
 {
     using C = Cfg<NJ>;
@@ -294,7 +295,7 @@ __device__ __forceinline__ void substep(const uint8_t* __restrict__ frag_src, in
         if (LD) {
 #pragma unroll
             for (int li = s * C::LOADS / C::MF; li < (s + 1) * C::LOADS / C::MF; ++li)
-                stage_load<NJ>(li, fill, wk, xk, ro, wave);
+                stage_load<NJ>(li, fill, k, rw, rx, ro, wave);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -332,6 +333,8 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     const int start_x = xcd * (ntiles >> 3) + (xcd < (ntiles & 7) ? xcd : (ntiles & 7));
     const int GM = FP8MM_LARGEM_GM;
     const int in_group = GM * num_n;
+    // operand buffers: rows past N or M load zeros
+    const __amdgpu_buffer_rsrc_t rw = operand_rsrc(wq, N * K), rx = operand_rsrc(xq, M * K);
     for (int u = bid >> 3; u < tiles_x; u += nbx) {
     const int t = start_x + u;
     const int first_m = (t / in_group) * GM;
@@ -358,12 +361,12 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     // (and reloaded from scratch on every tile's critical path).
     int rlane = lane;
     __asm__ volatile("" : "+v"(rlane));
-    row_offsets<NJ>(ro, n0, m0, N, M, K, wave, rlane);
+    row_offsets<NJ>(ro, n0, m0, K, wave, rlane);
 #pragma unroll
     for (int s = 0; s < NSTAGE; ++s)
 #pragma unroll
         for (int li = 0; li < C::LOADS; ++li)
-            stage_load<NJ>(li, smem + s * C::STAGE_BYTES, wq + kof(s), xq + kof(s), ro, wave);
+            stage_load<NJ>(li, smem + s * C::STAGE_BYTES, (uint32_t)kof(s), rw, rx, ro, wave);
     __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_IMM(C::LOADS));   // stage 0 landed for this wave
     __builtin_amdgcn_s_barrier();
 
@@ -380,13 +383,13 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
         uint8_t* cur = smem + (kt & 1) * C::STAGE_BYTES;
         uint8_t* nxt = smem + ((kt + 1) & 1) * C::STAGE_BYTES;
         // sub-step 0 of stage kt (its sub-step 1 fragments come from the same stage)
-        substep<NJ, false>(cur, 1, lane, wn, wm, fa, fb, acc, nullptr, nullptr, nullptr, ro, wave);
+        substep<NJ, false>(cur, 1, lane, wn, wm, fa, fb, acc, nullptr, 0u, rw, rx, ro, wave);
         // boundary: stage kt+1 landed (the only stage in flight), stage kt fully read
         __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_LGKM0_IMM(0));
         __builtin_amdgcn_s_barrier();
         // sub-step 1 of stage kt: fragments of stage kt+1, and the loads of stage kt+2 into stage kt's buffer
         const int64_t k2 = kof(kt + 2);
-        substep<NJ, true>(nxt, 0, lane, wn, wm, fb, fa, acc, cur, wq + k2, xq + k2, ro, wave);
+        substep<NJ, true>(nxt, 0, lane, wn, wm, fb, fa, acc, cur, (uint32_t)k2, rw, rx, ro, wave);
     }
 
     // Epilogue: scale, round to bf16, stage the TX x 256 tile in LDS (rows of
