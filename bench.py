@@ -514,8 +514,9 @@ def summarize_trace(d, name, cmd):
             else:
                 runs.append((k, [en - st]))
         lines += ["", "Runs of at least 8 back-to-back dispatches of one kernel, in launch order (a graph replay of "
-                  "n launches of one kernel is one run of n; the bench replays each graph twice back to back, untimed then "
-                  "timed, so such a run holds 2n):", "",
+                  "n launches of one kernel is one run of n; the bench replays each graph back to back, untimed then timed, "
+                  "so such a run holds 2n, or 12n for the graphs of the roofline kernels, which get 10 further timed "
+                  "replays):", "",
                   "| run | kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
         for i, (k, ds) in enumerate(runs):
             if len(ds) >= 8:
