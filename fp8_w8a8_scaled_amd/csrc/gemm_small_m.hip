@@ -71,6 +71,12 @@
 #define FP8MM_SMALLM_CPOL 2
 #endif
 
+// Ring kernel: row-balanced last round where whole tiles are badly
+// unbalanced over the CUs (see k_gemm_small_m_ring): 1 = on.
+#ifndef FP8MM_SMALLM_BAL
+#define FP8MM_SMALLM_BAL 1
+#endif
+
 // Persistent variant with the weight staged through per-wave LDS rings: 1 = on.
 #ifndef FP8MM_SMALLM_RING
 #define FP8MM_SMALLM_RING 1
@@ -406,20 +412,25 @@ __device__ __forceinline__ v4f tile_mfma(const u32x4_t (&a)[CPW][2], const uint8
 
 // Sum the W partials of one tile in wave order (partial of wave w for MFMA
 // lane `lane` at red[w * stride + slot]), scale (weight scales in sw: n = n0 +
-// 4*(lane/16) .. +3) and store bf16.
-__device__ __forceinline__ void reduce_tile(const v4f* red, int stride, int slot, int W, int64_t n0, float s_act,
-                                            const float4 sw, const ShardTable& sh, int M, int lane)
+// 4*(lane/16) .. +3) and store bf16.  Rows n >= nend belong to another
+// workgroup (or do not exist) and are not stored.  The shard is that of n0
+// (one lookup for the tile: a tile starting at a multiple of 16 lies in one
+// shard), or with lane_shard that of each 4-row group (such a group never
+// straddles two shards: shard starts are multiples of 16).
+__device__ __forceinline__ void reduce_tile(const v4f* red, int stride, int slot, int W, int64_t n0, int64_t nend,
+                                            float s_act, const float4 sw, const ShardTable& sh, int M, int lane,
+                                            bool lane_shard = false)
 {
     const int m = lane & 15;
-    if (m >= M) return;
+    const int64_t n = n0 + 4 * (lane >> 4);
+    if (m >= M || n >= nend) return;
     v4f s = red[slot];
     for (int w = 1; w < W; ++w) {
         const v4f p = red[w * stride + slot];
         s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
     }
-    const int64_t n = n0 + 4 * (lane >> 4);
     const float sa = row_scale(sh, m, s_act);
-    store_out4(sh, shard_of(sh, n0), m, n, (s.x * sa) * sw.x, (s.y * sa) * sw.y, (s.z * sa) * sw.z,
+    store_out4(sh, shard_of(sh, lane_shard ? n : n0), m, n, (s.x * sa) * sw.x, (s.y * sa) * sw.y, (s.z * sa) * sw.z,
                (s.w * sa) * sw.w);
 }
 
@@ -488,7 +499,7 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemm_small_m_persist(
                 rb[wave * 64 + lane] = acc;
                 __syncthreads();
                 if (wave == 0)
-                    reduce_tile(rb, 64, lane, W, (int64_t)(bid + u * G) * 16, s_act,
+                    reduce_tile(rb, 64, lane, W, (int64_t)(bid + u * G) * 16, N, s_act,
                                 make_float4(__uint_as_float(swu[0]), __uint_as_float(swu[1]),
                                             __uint_as_float(swu[2]), __uint_as_float(swu[3])),
                                 sh, M, lane);
@@ -500,7 +511,7 @@ __global__ __launch_bounds__(64 * WMAX) void k_gemm_small_m_persist(
         for (int idx = threadIdx.x; idx < my_tiles * 64; idx += blockDim.x) {
             const int u = idx >> 6, l = idx & 63;
             const int64_t n0 = (int64_t)(bid + u * G) * 16;
-            reduce_tile(red + u * W * 64, 64, l, W, n0, s_act,
+            reduce_tile(red + u * W * 64, 64, l, W, n0, N, s_act,
                         *reinterpret_cast<const float4*>(s_w + n0 + 4 * (l >> 4)), sh, M, l);
         }
     }
@@ -559,7 +570,16 @@ __device__ __forceinline__ v4f chunk_mfma_x(const uint8_t* __restrict__ slot, in
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 0, 0, 0, 0, 0, 0);
 }
 
-template <int S, bool DEFER, int XI>
+// BAL (row-balanced last round): taken where whole tiles would leave the
+// busiest workgroup with much more weight than the average (e.g. N = 5120: 320
+// tiles on 256 CUs, 2 against 1.25).  A workgroup then runs FR full rounds of
+// 16-row tiles bid, bid + G, ... and a share of the rows left over, [R + q0,
+// R + q1): their 4-row groups split evenly (+-1 group) over the G workgroups.
+// Rows of that last tile past its end load as zeros and are not stored.  The
+// chunk -> wave assignment and the reduction order do not change: the same
+// bits.  Its refill offsets come from an incremental cursor, computed before
+// the wait for the chunk whose slot they refill.
+template <int S, bool DEFER, int XI, bool BAL>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act,
     const float* __restrict__ s_w, ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw)
@@ -570,9 +590,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
     const int r = lane & 15, g = lane >> 4;
     const int G = gridDim.x, bid = blockIdx.x;
     const int ntiles = (int)(N >> 4);
-    const int my_tiles = (ntiles - bid + G - 1) / G;
+    const int FR = BAL ? ntiles / G : 0;                // >= 1 with BAL: G <= N / 16
+    const int R = FR * G * 16, ngr = BAL ? ((int)N - R) >> 2 : 0;
+    const int q0 = 4 * (int)((int64_t)ngr * bid / G), q1 = 4 * (int)((int64_t)ngr * (bid + 1) / G);
+    const int my_tiles = BAL ? FR + (q1 > q0 ? 1 : 0) : (ntiles - bid + G - 1) / G;
     __builtin_assume(my_tiles >= 1);                    // G <= ntiles
-    const int tiles_max = (ntiles + G - 1) / G;
+    const int tiles_max = BAL ? FR + (ngr > 0 ? 1 : 0) : (ntiles + G - 1) / G;
+    auto tile_rows = [&](int u, int& rt, int& re) {     // rows [rt, re) of tile u
+        if (!BAL || u < FR) {
+            rt = (bid + u * G) * 16;
+            re = rt + 16;
+        } else {
+            rt = R + q0;
+            re = R + q1;
+        }
+    };
     constexpr int SB = 2048 + 1024 * XI;                // ring slot: W chunk (+ x_q chunk)
     constexpr int LPC = 2 + XI;                          // direct-to-LDS loads per chunk
     const int64_t ldsx = K + 16;
@@ -596,7 +628,43 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
     const uint32_t xoff0 = (uint32_t)(xr0 * K + wswz(lrow, lane & 7) * 16);
     const uint32_t xoff1 = (uint32_t)(xr1 * K + wswz(lrow + 8, lane & 7) * 16);
     const int total = my_tiles * cpw;                   // this wave's chunks, tile-major
-    auto issue = [&](int j, int slot) {                 // chunk j of the sequence into a ring slot
+    // BAL issue cursor: sequence position iq, its tile iu and chunk index ic,
+    // and the rows [irt, ire) of tile iu.  prep() returns the buffer offsets of
+    // the chunk at the cursor (past the buffer, i.e. zeros, where nothing is
+    // loaded) and advances it; fire() issues those loads into a ring slot.
+    int iq = 0, iu = 0, ic = 0, irt, ire;
+    tile_rows(0, irt, ire);
+    struct Pend {
+        uint32_t w0, w1, x0, x1;
+    };
+    [[maybe_unused]] auto prep = [&]() {
+        const int chunk = wave + ic * W;
+        const bool ok = iq < total && chunk < nchunks;
+        const uint32_t t0 = (uint32_t)((int64_t)irt * K) + (uint32_t)chunk * kChunk;
+        const uint32_t cx = (uint32_t)chunk * kChunk;
+        Pend pd;
+        pd.w0 = ok && irt + lrow < ire ? t0 + pieceoff0 : kOob;
+        pd.w1 = ok && irt + lrow + 8 < ire ? t0 + pieceoff1 : kOob;
+        pd.x0 = ok ? xoff0 + cx : kOob;
+        pd.x1 = ok ? xoff1 + cx : kOob;
+        ++iq;
+        if (++ic == cpw) {
+            ic = 0;
+            ++iu;
+            tile_rows(iu, irt, ire);
+        }
+        return pd;
+    };
+    [[maybe_unused]] auto fire = [&](const Pend& pd, int slot) {
+        uint8_t* sl = ring + slot * SB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)sl, 16, (int)pd.w0, 0, 0, FP8MM_SMALLM_CPOL);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sl + 1024), 16, (int)pd.w1, 0, 0, FP8MM_SMALLM_CPOL);
+        if (XI >= 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sl + 2048), 16, (int)pd.x0, 0, 0, 0);
+        if (XI >= 2)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sl + 3072), 16, (int)pd.x1, 0, 0, 0);
+    };
+    [[maybe_unused]] auto issue = [&](int j, int slot) {   // chunk j of the sequence into a ring slot (not BAL)
         const int u = j / cpw, c = j - u * cpw;
         const int chunk = wave + c * W;
         const bool ok = j < total && chunk < nchunks;
@@ -624,7 +692,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < S; ++s) issue(s, s);
+    for (int s = 0; s < S; ++s) {
+        if constexpr (BAL) fire(prep(), s);
+        else issue(s, s);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (XI == 0) {
         // x_q landed: only the S chunks issued after it may be in flight (for
@@ -638,7 +709,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
     // weight scales of tile u for this lane's four rows (tile-by-tile reduction only)
     const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
     auto tile_sw = [&](int t) {
-        const uint32_t o = t < my_tiles ? (uint32_t)((bid + t * G) * 64 + g * 16) : kOob;
+        int rt, re;
+        tile_rows(t, rt, re);
+        const int n = rt + 4 * g;
+        const uint32_t o = t < my_tiles && n < re ? (uint32_t)n * 4 : kOob;
         return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, 0, 0);
     };
     u32x4_t swu{0u, 0u, 0u, 0u};
@@ -650,6 +724,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
         for (int s = 0; s < S; ++s) {
             const int j = j0 + s;
             if (j >= total) break;                       // wave-uniform
+            [[maybe_unused]] Pend refill;
+            if constexpr (BAL) refill = prep();          // chunk j + S, into this slot once it is read
             // chunk j landed: only the S-1 chunks after it may be in flight
             __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT(LPC * (S - 1)));
             if (XI == 0) {
@@ -660,7 +736,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
                 acc = chunk_mfma_x(ring + s * SB, r, g, xsr, acc);
             }
             __builtin_amdgcn_s_waitcnt(FP8MM_SM_LGKM0);  // the slot's reads have returned
-            issue(j + S, s);
+            if constexpr (BAL) fire(refill, s);
+            else issue(j + S, s);
             if (++c == cpw) {                            // tile u complete
                 if constexpr (DEFER) {
                     if (mp == 64 || (lane & 15) < 8) red[(u * W + wave) * mp + pslot] = acc;
@@ -668,11 +745,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
                     v4f* rb = red + (u & 1) * W * 64;
                     rb[wave * 64 + lane] = acc;
                     __syncthreads();
+                    int rt, re;
+                    tile_rows(u, rt, re);
                     if (wave == 0)
-                        reduce_tile(rb, 64, lane, W, (int64_t)(bid + u * G) * 16, s_act,
+                        reduce_tile(rb, 64, lane, W, rt, re, s_act,
                                     make_float4(__uint_as_float(swu[0]), __uint_as_float(swu[1]),
                                                 __uint_as_float(swu[2]), __uint_as_float(swu[3])),
-                                    sh, M, lane);
+                                    sh, M, lane, BAL && u >= FR);
                     swu = tile_sw(u + 1);                // scales of the next tile
                 }
                 acc = v4f{0.f, 0.f, 0.f, 0.f};
@@ -687,9 +766,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
         for (int idx = threadIdx.x; idx < my_tiles * mp; idx += blockDim.x) {
             const int uu = idx / mp, ps = idx - uu * mp;
             const int l = mp == 64 ? ps : (ps >> 3) * 16 + (ps & 7);
-            const int64_t n0 = (int64_t)(bid + uu * G) * 16;
-            reduce_tile(red + uu * W * mp, mp, ps, W, n0, s_act,
-                        *reinterpret_cast<const float4*>(s_w + n0 + 4 * (l >> 4)), sh, M, l);
+            int n0, re;
+            tile_rows(uu, n0, re);
+            if (n0 + 4 * (l >> 4) >= re) continue;       // another workgroup's rows
+            reduce_tile(red + uu * W * mp, mp, ps, W, n0, re, s_act,
+                        *reinterpret_cast<const float4*>(s_w + n0 + 4 * (l >> 4)), sh, M, l, BAL);
         }
     }
 }
@@ -766,18 +847,18 @@ void launch_persist(const dim3& grid, const dim3& block, size_t lds, hipStream_t
                        M, N, K, nchunks);
 }
 
-template <int S, bool DEFER, int XI>
+template <int S, bool DEFER, int XI, bool BAL>
 void launch_ring(const dim3& grid, const dim3& block, size_t lds, hipStream_t stream, const uint8_t* xq,
                  const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh, int M, int64_t N, int64_t K,
                  int nchunks, int cpw)
 {
     static const bool attr = [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_ring<S, DEFER, XI>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_ring<S, DEFER, XI, BAL>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         return true;
     }();
     (void)attr;
-    hipLaunchKernelGGL((k_gemm_small_m_ring<S, DEFER, XI>), grid, block, lds, stream, xq, wq, s_act, s_w, sh, M, N, K,
+    hipLaunchKernelGGL((k_gemm_small_m_ring<S, DEFER, XI, BAL>), grid, block, lds, stream, xq, wq, s_act, s_w, sh, M, N, K,
                        nchunks, cpw);
 }
 
@@ -789,7 +870,10 @@ bool try_ring(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_
 {
     if (!FP8MM_SMALLM_RING || M > 16 || K % 1024 != 0 || N * K >= ((int64_t)1 << 31)) return false;
     const int64_t G = N / 16 < num_cus() ? N / 16 : num_cus();
-    const int64_t tiles_max = (N / 16 + G - 1) / G;
+    const int64_t tiles_max = (N / 16 + G - 1) / G;      // whole tiles, or FR + 1 with the balanced last round
+    // Balanced last round when whole tiles leave the busiest workgroup at least
+    // 1.3x the average weight bytes.
+    const bool bal = FP8MM_SMALLM_BAL && 10 * tiles_max * G >= 13 * (N / 16);
     const size_t xb = (size_t)((M * (K + 16) + 15) & ~(int64_t)15);
     const size_t part = (size_t)W * 64 * sizeof(v4f);               // one tile's partials
     const size_t dpart = (size_t)W * (M <= 8 ? 32 : 64) * sizeof(v4f);   // ... as the deferred buffer keeps them
@@ -801,8 +885,12 @@ bool try_ring(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_
     };
 #define FP8MM_RING_TRY(S, DF, XI)                                                                      \
     if (bytes(S, DF, XI) <= 160 * 1024) {                                                              \
-        launch_ring<S, DF, XI>(grid, block, bytes(S, DF, XI), stream, xq, wq, s_act, s_w, sh, (int)M, N, K, nchunks, \
-                               cpw);                                                                   \
+        if (bal)                                                                                       \
+            launch_ring<S, DF, XI, true>(grid, block, bytes(S, DF, XI), stream, xq, wq, s_act, s_w, sh, (int)M, N, K, \
+                                         nchunks, cpw);                                                \
+        else                                                                                           \
+            launch_ring<S, DF, XI, false>(grid, block, bytes(S, DF, XI), stream, xq, wq, s_act, s_w, sh, (int)M, N, K, \
+                                          nchunks, cpw);                                               \
         return true;                                                                                   \
     }
     FP8MM_RING_TRY(6, true, 0)

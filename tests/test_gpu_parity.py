@@ -691,3 +691,31 @@ def test_merge_policies_end_to_end(fp8, M):
     assert np.array_equal(host_u8(xq), xq_ref) and np.array_equal(host_u8(w2), w2_ref)
     got = np.concatenate([host_u16(o) for o in outs], axis=1)
     assert_within_tolerance(got, ref, v, f"max-scale merged qkv M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+@pytest.mark.parametrize("N,shards", [(5120, [4112, 1008]), (5632, [4384, 16, 1232])])
+def test_balanced_last_round_merged_equals_split(fp8, M, N, shards):
+    """Decode widths whose whole 16-row tiles fall unevenly on the CUs (320 or
+    352 tiles on 256) take the row-balanced last round: each workgroup's share
+    of the leftover rows starts at a multiple of 4, so a shard boundary can fall
+    inside it (4112 and 4384 here).  Merged == one call per shard, bit for bit,
+    for bf16 and f32 outputs, and within the oracle's tolerance."""
+    import torch
+    K = 2048
+    xq = wl.random_codes(4, M, K, m=M)
+    wq = wl.random_codes(4, N, K, tensor=wl.T_W)
+    sw = (np.random.Generator(np.random.PCG64(3)).random(N) * 1e-3 + 1e-5).astype(np.float32)
+    s_act = 0.011
+    xd, wd, swd = u8_dev(xq), u8_dev(wq), f32_dev(sw)
+    for dt in (torch.bfloat16, torch.float32):
+        merged = fp8.scaled_mm_merged(xd, wd, s_act, swd, shards, out_dtype=dt)
+        start = 0
+        for n, mo in zip(shards, merged):
+            split = fp8.scaled_mm(xd, wd[start:start + n], s_act, swd[start:start + n], out_dtype=dt)
+            assert torch.equal(split, mo), f"{dt} shard at {start} differs"
+            start += n
+        if dt == torch.bfloat16:
+            ref, v = oracle.scaled_mm(xq, wq, s_act, sw, want_v=True)
+            assert_within_tolerance(np.concatenate([host_u16(o) for o in merged], axis=1), ref, v,
+                                    f"balanced M={M} N={N}")
