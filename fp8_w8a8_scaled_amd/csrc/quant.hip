@@ -155,11 +155,13 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_per_token_reg(
     const int64_t m = blockIdx.x;
     const uint16_t* row = x + m * ldx;
     const int nv = (int)(K >> 3);
-    uint4 in[PPT];
+    uint4 in[PPT], gm[PPT];                             // gamma too: both loads in flight together
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
         const int v = threadIdx.x + p * kQuantThreads;
         in[p] = v < nv ? *reinterpret_cast<const uint4*>(row + (int64_t)v * 8) : make_uint4(0u, 0u, 0u, 0u);
+        gm[p] = gamma && v < nv ? *reinterpret_cast<const uint4*>(gamma + (int64_t)v * 8)
+                                : make_uint4(0u, 0u, 0u, 0u);
     }
     float r = 1.0f;
     if (gamma) {
@@ -180,10 +182,8 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_per_token_reg(
     float amax = 0.0f;
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
-        const int v = threadIdx.x + p * kQuantThreads;
         if (gamma) {
-            const uint4 g = v < nv ? *reinterpret_cast<const uint4*>(gamma + (int64_t)v * 8) : make_uint4(0u, 0u, 0u, 0u);
-            rms_apply8(in[p], g, r, y[p]);
+            rms_apply8(in[p], gm[p], r, y[p]);
         } else {
             const uint32_t w[4] = {in[p].x, in[p].y, in[p].z, in[p].w};
 #pragma unroll
