@@ -51,6 +51,18 @@ void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up
 #define FP8MM_SILU_NT 0
 #endif
 bool silu_mul_uses_table(int64_t M, int64_t I, float s_act);
+// Table-based fused RMSNorm quant (the same bytes as the per-element kernel):
+// from this many rows on, groups of 256 threads (one row each) per workgroup,
+// workgroups per CU.
+#ifndef FP8MM_RMS_LUT_MIN_ROWS
+#define FP8MM_RMS_LUT_MIN_ROWS 1
+#endif
+#ifndef FP8MM_RMS_LUT_GROUPS
+#define FP8MM_RMS_LUT_GROUPS 2
+#endif
+#ifndef FP8MM_RMS_LUT_BPC
+#define FP8MM_RMS_LUT_BPC 2
+#endif
 void launch_act_scale_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, int64_t M,
                                int64_t I, float* s_act, float* partial, hipStream_t stream);
 

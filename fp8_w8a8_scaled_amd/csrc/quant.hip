@@ -9,7 +9,8 @@
 // commit message.
 //
 // All kernels are memory-bound streaming passes: 16-byte bf16 loads, 8-byte
-// E4M3 stores, no LDS except for block reductions.
+// E4M3 stores; LDS holds block reductions and the lookup tables that replace
+// the per-element division and encode.
 #include "act_quant.h"
 #include "act_tables.h"
 #include "device_common.h"
@@ -87,6 +88,148 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_rmsnorm(
         const uint4 in = *reinterpret_cast<const uint4*>(row + v * 8);
         const uint4 g = *reinterpret_cast<const uint4*>(gamma + v * 8);
         *reinterpret_cast<uint2*>(xq + m * K + v * 8) = rms_quant8(in, g, r, s_act);
+    }
+}
+
+// The same bytes as k_quant_rmsnorm with the division and the encode replaced
+// by a lookup (K <= 2048 * PPT, 2^-100 <= s_act <= 2^100).  Once r and gamma
+// are finite, no y can be a NaN: |x * r| <= sqrt(K), so y is finite or
+// overflows to +-inf.  The code of y then depends only on the magnitude bits a
+// of y_b and its sign: a below code_band_lo(s_act) gives a signed zero, a at or
+// past lo + kCodeBand (inf included) the saturated code, and the kCodeBand
+// magnitudes between are looked up in a workgroup table filled once with the
+// exact division.  Rows with a non-finite value or r, or a non-finite gamma,
+// take the per-element path.
+//
+// A workgroup is G groups of 256 threads, persistent over rows: each group
+// takes one row at a time and sums its squares in k_quant_rmsnorm's order
+// (thread t: pieces t, t + 256, ...; xor butterfly per wave; the 4 wave sums
+// in order), so r is bitwise the same.  A thread holds its pieces of the row
+// and of gamma in registers and loads its pieces of the group's next row
+// before the row's barrier.
+template <int G>
+struct RmsLutShared {
+    uint8_t tab[kCodeBand + 2];        // [0]: below the band, [1 + i]: band entry i, [kCodeBand + 1]: above
+    double part[2][G][kRmsRowThreads / 64];
+};
+
+// A thread's PPT pieces of row m (pieces t, t + 256, ...) through a buffer
+// resource over that row: pieces past the row, and every piece of a row past
+// M (a resource of 0 bytes), read as zeros without a branch, so the loads of a
+// prefetched row stay in flight past the uses of the current one.  m is the
+// same across the wave (one group is 4 whole waves).
+template <int PPT>
+__device__ __forceinline__ void load_row_pieces(const uint16_t* __restrict__ x, int64_t ldx, int m, int64_t M,
+                                                int64_t K, int t, uint4 (&in)[PPT])
+{
+    const int mu = __builtin_amdgcn_readfirstlane(m);
+    const bool live = mu < M;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(live ? x + (int64_t)mu * ldx : x), (short)0, live ? (int)(K * 2) : 0, 0x00020000);
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, (t + p * kRmsRowThreads) * 16, 0, 0);
+        in[p] = make_uint4(r.x, r.y, r.z, r.w);
+    }
+}
+
+template <int PPT, int G>
+__global__ __launch_bounds__(G * kRmsRowThreads) void k_quant_rmsnorm_lut(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma, float eps,
+    float s_act, uint8_t* __restrict__ xq, int64_t M, int64_t K)
+{
+    __shared__ RmsLutShared<G> sh;
+    const int grp = threadIdx.x / kRmsRowThreads, t = threadIdx.x % kRmsRowThreads;
+    const int wave = t >> 6, lane = t & 63;
+    const int nv = (int)(K >> 3);
+    const int64_t stride = (int64_t)gridDim.x * G;
+    int64_t m = (int64_t)blockIdx.x * G + grp;
+    // the group's rows m, m + stride, ... alternate between two buffers, so a
+    // prefetched row is never copied (a copy would wait for its loads)
+    uint4 buf[2][PPT];
+    load_row_pieces<PPT>(x, ldx, (int)m, M, K, t, buf[0]);
+
+    // gamma as fp32, fixed per thread; the lookup needs all of it finite
+    float gf[PPT][8];
+    bool g_fin = true;
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+        const int v = t + p * kRmsRowThreads;
+        const uint4 g = v < nv ? *reinterpret_cast<const uint4*>(gamma + (int64_t)v * 8) : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t b = (gw[i >> 1] >> ((i & 1) * 16)) & 0xffffu;
+            gf[p][i] = bf16_to_f32(b);
+            g_fin = g_fin && (b & 0x7fffu) < 0x7f80u;
+        }
+    }
+    const uint32_t lo = code_band_lo(s_act);
+    const int lo1 = (int)lo - 1;                         // table index of magnitude a: clamp(a - lo1)
+    for (int j = threadIdx.x; j < (int)kCodeBand + 2; j += blockDim.x)
+        sh.tab[j] = j == 0 ? 0u : j > (int)kCodeBand ? 0x7eu : quant_value(bf16_to_f32(lo - 1u + (uint32_t)j), s_act);
+    const bool gamma_ok = __syncthreads_and(g_fin);       // also orders the table before its first read
+
+    // one row of the group: `in` holds it, `nx` receives the group's next row
+    auto row_step = [&](const uint4 (&in)[PPT], uint4 (&nx)[PPT], int it) {
+        double ss = 0.0;
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) ss = sumsq8(in[p], ss);           // zero pieces add exact zeros
+        load_row_pieces<PPT>(x, ldx, (int)(m + stride), M, K, t, nx);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        if (lane == 0) sh.part[it & 1][grp][wave] = ss;
+        __syncthreads();
+        double tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < kRmsRowThreads / 64; ++w) tot += sh.part[it & 1][grp][w];
+        const float r = rms_inv(tot, K, eps);
+        uint8_t* out = xq + m * K;
+        if (m >= M) return;
+        if (gamma_ok && __builtin_isfinite(tot) && __builtin_isfinite(r)) {
+#pragma unroll
+            for (int p = 0; p < PPT; ++p) {
+                const int v = t + p * kRmsRowThreads;
+                const uint32_t w[4] = {in[p].x, in[p].y, in[p].z, in[p].w};
+                uint32_t h[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    h[i] = pack_bf16x2(bf16_to_f32(w[i] & 0xffffu) * r * gf[p][2 * i],
+                                       bf16_to_f32(w[i] >> 16) * r * gf[p][2 * i + 1]);
+                uint32_t o[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    uint32_t c = 0u;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int a = (int)((h[2 * q + (e >> 1)] >> ((e & 1) * 16)) & 0x7fffu);
+                        c |= (uint32_t)sh.tab[min(max(a - lo1, 0), (int)kCodeBand + 1)] << (8 * e);
+                    }
+                    // the four sign bits: bit 15 and bit 31 of each packed pair
+                    o[q] = c | (__builtin_amdgcn_perm(h[2 * q + 1], h[2 * q], 0x07050301u) & 0x80808080u);
+                }
+                if (v < nv) *reinterpret_cast<uint2*>(out + (int64_t)v * 8) = make_uint2(o[0], o[1]);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < PPT; ++p) {
+                const int v = t + p * kRmsRowThreads;
+                if (v < nv)
+                    *reinterpret_cast<uint2*>(out + (int64_t)v * 8) =
+                        rms_quant8(in[p], *reinterpret_cast<const uint4*>(gamma + (int64_t)v * 8), r, s_act);
+            }
+        }
+    };
+    const int64_t first = (int64_t)blockIdx.x * G;       // the workgroup runs while its first group has a row
+    for (int it = 0; first + it * stride < M;) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (first + it * stride >= M) break;
+            row_step(buf[j], buf[j ^ 1], it);
+            m += stride;
+            ++it;
+        }
     }
 }
 
@@ -526,7 +669,20 @@ int64_t plain_grid(int64_t M, int64_t K)
 void launch_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, float s_act,
                   uint8_t* xq, int64_t M, int64_t K, hipStream_t stream)
 {
-    if (gamma) {
+    const int64_t ppt = ((K >> 3) + kRmsRowThreads - 1) / kRmsRowThreads;   // 16-byte pieces per thread
+    if (gamma && M >= FP8MM_RMS_LUT_MIN_ROWS && M < ((int64_t)1 << 30) && ppt <= 4 && code_table_ok(s_act)) {
+        constexpr int G = FP8MM_RMS_LUT_GROUPS;
+        const int64_t want = (M + G - 1) / G, cap = (int64_t)num_cus() * FP8MM_RMS_LUT_BPC;
+        const dim3 grid((uint32_t)(want < cap ? want : cap)), block(G * kRmsRowThreads);
+        if (ppt <= 1)
+            hipLaunchKernelGGL((k_quant_rmsnorm_lut<1, G>), grid, block, 0, stream, x, ldx, gamma, eps, s_act, xq, M, K);
+        else if (ppt <= 2)
+            hipLaunchKernelGGL((k_quant_rmsnorm_lut<2, G>), grid, block, 0, stream, x, ldx, gamma, eps, s_act, xq, M, K);
+        else if (ppt <= 3)
+            hipLaunchKernelGGL((k_quant_rmsnorm_lut<3, G>), grid, block, 0, stream, x, ldx, gamma, eps, s_act, xq, M, K);
+        else
+            hipLaunchKernelGGL((k_quant_rmsnorm_lut<4, G>), grid, block, 0, stream, x, ldx, gamma, eps, s_act, xq, M, K);
+    } else if (gamma) {
         hipLaunchKernelGGL(k_quant_rmsnorm, dim3((uint32_t)M), dim3(kQuantThreads), 0, stream,
                            x, ldx, gamma, eps, s_act, xq, K);
     } else {
