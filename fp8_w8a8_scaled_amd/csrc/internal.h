@@ -48,7 +48,7 @@ void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up
 #define FP8MM_SILU_PF 0
 #endif
 #ifndef FP8MM_SILU_NT
-#define FP8MM_SILU_NT 0
+#define FP8MM_SILU_NT 1
 #endif
 bool silu_mul_uses_table(int64_t M, int64_t I, float s_act);
 // Table-based fused RMSNorm quant (the same bytes as the per-element kernel):

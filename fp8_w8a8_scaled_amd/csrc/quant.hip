@@ -588,10 +588,14 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
         }
         uint2 o[NP];
         silu_mul_quant_tables<NP>(g, u, stab, ctab, o);
+        // a piece past `end` was loaded from piece 0's address, so its codes are
+        // piece 0's: it stores them there again instead of branching (a branch
+        // lets the compiler sink that piece's loads behind the other's store)
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
-            if (i + (uint32_t)p * kSiluLutThreads < end)
-                *reinterpret_cast<uint2*>(xq + (int64_t)m[p] * I + v[p] * 8) = o[p];
+        for (int p = 0; p < NP; ++p) {
+            const bool ok = i + (uint32_t)p * kSiluLutThreads < end;
+            *reinterpret_cast<uint2*>(xq + (int64_t)(ok ? m[p] : m[0]) * I + (ok ? v[p] : v[0]) * 8) = o[p];
+        }
         if (!more) break;
         i = in;
         if (PF) {
