@@ -258,6 +258,10 @@ def bench_prefill(fp8, steps, warmup):
     del gate32, up32
     sq_ms = graph_time_ms(lambda i: fp8.silu_mul_quant(gate, up, s2, out=xq2), steps, warmup)
     sq_bytes = 5 * M * K2
+    # the step's fused RMSNorm quant alone, and the plain static quant of a bf16
+    # [M, 17408] down-projection input (the gate half stands in for it)
+    rq_ms = graph_time_ms(lambda i: fp8.quant_rmsnorm(xd, gd, s1, wl.EPS, out=xq1), steps, warmup)
+    pq_ms = graph_time_ms(lambda i: fp8.quant(gate, s2, out=xq2), steps, warmup)
     ach = flops1 / (gu_ms * 1e-3) / 1e12
     return {
         "workload": f"prefill_M{M}_gateup_K{K1}_N{N1}_down_K{K2}_N{N2}",
@@ -267,6 +271,8 @@ def bench_prefill(fp8, steps, warmup):
         "gemm_tflops": {"gate_up": ach, "down": flops2 / (dn_ms * 1e-3) / 1e12},
         "down_further_replays": replay_stats(dn_each),
         "silu_mul_quant": {"us": sq_ms * 1e3, "GBs": sq_bytes / (sq_ms * 1e-3) / 1e9},
+        "quant_rmsnorm": {"us": rq_ms * 1e3, "GBs": (3 * M * K1 + 2 * K1) / (rq_ms * 1e-3) / 1e9},
+        "plain_quant_M6576_K17408": {"us": pq_ms * 1e3, "GBs": 3 * M * K2 / (pq_ms * 1e-3) / 1e9},
         "f32_out_ab": {"gate_up_bf16_us": gu_ms * 1e3, "gate_up_f32_us": gu32_ms * 1e3,
                        "out_bytes_bf16": 2 * M * N1, "out_bytes_f32": 4 * M * N1,
                        "f32_over_bf16_time": gu32_ms / gu_ms,

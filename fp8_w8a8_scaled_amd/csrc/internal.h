@@ -51,6 +51,17 @@ void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up
 #define FP8MM_SILU_NT 1
 #endif
 bool silu_mul_uses_table(int64_t M, int64_t I, float s_act);
+// Table-based plain static quant (same bytes): from this many elements on,
+// workgroups per CU, 16-byte pieces per thread and step.
+#ifndef FP8MM_PLAIN_LUT_MIN_ELEMS
+#define FP8MM_PLAIN_LUT_MIN_ELEMS (1LL << 20)
+#endif
+#ifndef FP8MM_PLAIN_LUT_BPC
+#define FP8MM_PLAIN_LUT_BPC 2
+#endif
+#ifndef FP8MM_PLAIN_LUT_NP
+#define FP8MM_PLAIN_LUT_NP 2
+#endif
 // Table-based fused RMSNorm quant (the same bytes as the per-element kernel):
 // from this many rows on, groups of 256 threads (one row each) per workgroup,
 // workgroups per CU.

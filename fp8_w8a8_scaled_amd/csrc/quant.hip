@@ -607,6 +607,81 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
     }
 }
 
+// Plain static quant of many elements: the codes of quant8 from a 2563-byte
+// table of the band of magnitudes whose code needs the division (as in
+// k_quant_rmsnorm_lut; entry kCodeBand + 2 is unused padding), a NaN keeping
+// its sign.  Each workgroup fills the table, then streams a contiguous share of
+// the [M, K] pieces, NP per thread per step, without branches: a piece past
+// the share is loaded from the thread's first piece and stores that piece's
+// codes there again.  total = M * K / 8 < 2^31.
+constexpr int kPlainLutThreads = 1024;
+
+template <int NP>
+__global__ __launch_bounds__(kPlainLutThreads) void k_quant_plain_lut(
+    const uint16_t* __restrict__ x, int64_t ldx, float s_act, uint8_t* __restrict__ xq, uint32_t nv,
+    uint32_t total, int64_t K)
+{
+    __shared__ uint8_t tab[kCodeBand + 3];
+    const uint32_t lo = code_band_lo(s_act);
+    const int lo1 = (int)lo - 1;
+    for (int j = threadIdx.x; j < (int)kCodeBand + 3; j += blockDim.x)
+        tab[j] = j == 0 ? 0u : j > (int)kCodeBand ? 0x7eu : quant_value(bf16_to_f32(lo - 1u + (uint32_t)j), s_act);
+    __syncthreads();
+    constexpr uint32_t kStep = (uint32_t)NP * kPlainLutThreads;
+    const uint32_t per = ((total + gridDim.x - 1) / gridDim.x + kStep - 1) / kStep * kStep;
+    const uint32_t begin = blockIdx.x * per;
+    const uint32_t end = begin + per < total ? begin + per : total;
+    uint32_t i = begin + threadIdx.x;
+    if (i >= end) return;
+    const uint32_t dm = kStep / nv, dv = kStep - dm * nv;      // one step = dm rows + dv pieces
+    uint32_t m[NP], v[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const uint32_t ip = i + (uint32_t)p * kPlainLutThreads;
+        m[p] = ip / nv;
+        v[p] = ip - m[p] * nv;
+    }
+    for (;;) {
+        uint4 in[NP];
+        uint32_t mm[NP], vv[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const bool ok = i + (uint32_t)p * kPlainLutThreads < end;
+            mm[p] = ok ? m[p] : m[0];
+            vv[p] = ok ? v[p] : v[0];
+            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + mm[p] * ldx + vv[p] * 8));
+            in[p] = make_uint4(r.x, r.y, r.z, r.w);
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const uint32_t w[4] = {in[p].x, in[p].y, in[p].z, in[p].w};
+            uint32_t o[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                uint32_t c = 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t a = (w[2 * q + (e >> 1)] >> ((e & 1) * 16)) & 0x7fffu;
+                    const uint32_t t = tab[min(max((int)a - lo1, 0), (int)kCodeBand + 1)];
+                    c |= (a > 0x7f80u ? 0x7fu : t) << (8 * e);
+                }
+                // the four sign bits: bit 15 and bit 31 of each pair of values
+                o[q] = c | (__builtin_amdgcn_perm(w[2 * q + 1], w[2 * q], 0x07050301u) & 0x80808080u);
+            }
+            *reinterpret_cast<uint2*>(xq + (int64_t)mm[p] * K + vv[p] * 8) = make_uint2(o[0], o[1]);
+        }
+        i += kStep;
+        if (i >= end) break;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            v[p] += dv;
+            m[p] += dm + (v[p] >= nv ? 1u : 0u);
+            v[p] -= v[p] >= nv ? nv : 0u;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kQuantThreads) void k_absmax_silu_mul(
     const uint16_t* __restrict__ gate, int64_t ldg, const uint16_t* __restrict__ up, int64_t ldu, int64_t M,
     int64_t I, float* __restrict__ partial)
@@ -689,6 +764,11 @@ void launch_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float e
     } else if (gamma) {
         hipLaunchKernelGGL(k_quant_rmsnorm, dim3((uint32_t)M), dim3(kQuantThreads), 0, stream,
                            x, ldx, gamma, eps, s_act, xq, K);
+    } else if (M * (K >> 3) >= FP8MM_PLAIN_LUT_MIN_ELEMS / 8 && M * (K >> 3) < ((int64_t)1 << 31) &&
+               code_table_ok(s_act)) {
+        const int64_t total = M * (K >> 3);
+        hipLaunchKernelGGL((k_quant_plain_lut<FP8MM_PLAIN_LUT_NP>), dim3((uint32_t)num_cus() * FP8MM_PLAIN_LUT_BPC),
+                           dim3(kPlainLutThreads), 0, stream, x, ldx, s_act, xq, (uint32_t)(K >> 3), (uint32_t)total, K);
     } else {
         hipLaunchKernelGGL(k_quant_plain, dim3((uint32_t)plain_grid(M, K)), dim3(kQuantThreads), 0, stream,
                            x, ldx, s_act, xq, M, K);

@@ -37,6 +37,19 @@ def test_quant_all_bf16_patterns_bit_exact(fp8, s_act):
     assert np.array_equal(got, want), np.flatnonzero(got != want)[:10]
 
 
+@pytest.mark.parametrize("s_act", [1.0, 3.0, 1.0 / 7.0, 2.0 ** -99, 2.0 ** 99, 2.0 ** -120])
+def test_plain_quant_table_path_all_bf16_patterns(fp8, s_act):
+    """Every bf16 pattern in 24 rows (1.5 M elements, past the table path's
+    2^20), the rows rotated so each pattern meets several column offsets and
+    the workgroups' shares end mid-row; 2^-120 is outside the table's range
+    (per-element path)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = np.stack([np.roll(bits, 977 * i) for i in range(24)])
+    got = host_u8(fp8.quant(bf16_dev(x), s_act))
+    want = oracle.quant_act(x, np.float32(s_act))
+    assert np.array_equal(got, want), np.argwhere(got != want)[:10]
+
+
 @pytest.mark.parametrize("wid,M,K", [(1, 4, 256), (2, 1, 5120), (2, 2, 5120), (2, 4, 5120), (2, 8, 5120),
                                      (3, 1, 17408), (3, 8, 17408), (3, 32, 17408), (5, 6576, 17408)])
 def test_plain_quant_and_scale_bit_exact(fp8, wid, M, K):
