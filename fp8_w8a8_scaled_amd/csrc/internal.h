@@ -62,6 +62,10 @@ bool silu_mul_uses_table(int64_t M, int64_t I, float s_act);
 #ifndef FP8MM_PLAIN_LUT_NP
 #define FP8MM_PLAIN_LUT_NP 2
 #endif
+// plain static quant with 4 values per thread below this many elements
+#ifndef FP8MM_PLAIN_HALF_MAX_ELEMS
+#define FP8MM_PLAIN_HALF_MAX_ELEMS ((1LL << 20) - 1)
+#endif
 // Table-based fused RMSNorm quant (the same bytes as the per-element kernel):
 // from this many rows on, groups of 256 threads (one row each) per workgroup,
 // workgroups per CU.

@@ -75,6 +75,29 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_plain(
     }
 }
 
+// Few elements (decode): the same codes with 4 values (8 bytes) per thread, so
+// the per-element division and encode that follow the load are half as long.
+__global__ __launch_bounds__(kQuantThreads) void k_quant_plain_half(
+    const uint16_t* __restrict__ x, int64_t ldx, float s_act, uint8_t* __restrict__ xq, int64_t M, int64_t K)
+{
+    const int64_t nh = K >> 2, total = M * nh;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = i / nh, h = i - m * nh;
+        const uint2 in = *reinterpret_cast<const uint2*>(x + m * ldx + h * 4);
+        const uint32_t w[2] = {in.x, in.y};
+        uint32_t o = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t b = (w[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+            const uint32_t c = ((b & 0x7fffu) > 0x7f80u) ? (0x7fu | ((b >> 8) & 0x80u))
+                                                         : f32_to_e4m3_sat(bf16_to_f32(b) / s_act);
+            o |= c << (8 * j);
+        }
+        *reinterpret_cast<uint32_t*>(xq + m * K + h * 4) = o;
+    }
+}
+
 __global__ __launch_bounds__(kQuantThreads) void k_quant_rmsnorm(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma, float eps,
     float s_act, uint8_t* __restrict__ xq, int64_t K)
@@ -769,6 +792,10 @@ void launch_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float e
         const int64_t total = M * (K >> 3);
         hipLaunchKernelGGL((k_quant_plain_lut<FP8MM_PLAIN_LUT_NP>), dim3((uint32_t)num_cus() * FP8MM_PLAIN_LUT_BPC),
                            dim3(kPlainLutThreads), 0, stream, x, ldx, s_act, xq, (uint32_t)(K >> 3), (uint32_t)total, K);
+    } else if (M * K <= FP8MM_PLAIN_HALF_MAX_ELEMS) {
+        const int64_t blocks = (M * (K >> 2) + kQuantThreads - 1) / kQuantThreads;
+        hipLaunchKernelGGL(k_quant_plain_half, dim3((uint32_t)(blocks < 1 ? 1 : blocks)), dim3(kQuantThreads), 0,
+                           stream, x, ldx, s_act, xq, M, K);
     } else {
         hipLaunchKernelGGL(k_quant_plain, dim3((uint32_t)plain_grid(M, K)), dim3(kQuantThreads), 0, stream,
                            x, ldx, s_act, xq, M, K);
