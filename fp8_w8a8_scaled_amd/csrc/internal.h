@@ -72,6 +72,9 @@ bool silu_mul_uses_table(int64_t M, int64_t I, float s_act);
 #ifndef FP8MM_RMS_LUT_MIN_ROWS
 #define FP8MM_RMS_LUT_MIN_ROWS 1
 #endif
+#ifndef FP8MM_RMS_LUT_MIN_K
+#define FP8MM_RMS_LUT_MIN_K 2048          // shorter rows do not repay the table
+#endif
 #ifndef FP8MM_RMS_LUT_GROUPS
 #define FP8MM_RMS_LUT_GROUPS 2
 #endif

@@ -772,7 +772,8 @@ void launch_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float e
                   uint8_t* xq, int64_t M, int64_t K, hipStream_t stream)
 {
     const int64_t ppt = ((K >> 3) + kRmsRowThreads - 1) / kRmsRowThreads;   // 16-byte pieces per thread
-    if (gamma && M >= FP8MM_RMS_LUT_MIN_ROWS && M < ((int64_t)1 << 30) && ppt <= 4 && code_table_ok(s_act)) {
+    if (gamma && M >= FP8MM_RMS_LUT_MIN_ROWS && M < ((int64_t)1 << 30) && K >= FP8MM_RMS_LUT_MIN_K && ppt <= 4 &&
+        code_table_ok(s_act)) {
         constexpr int G = FP8MM_RMS_LUT_GROUPS;
         const int64_t want = (M + G - 1) / G, cap = (int64_t)num_cus() * FP8MM_RMS_LUT_BPC;
         const dim3 grid((uint32_t)(want < cap ? want : cap)), block(G * kRmsRowThreads);

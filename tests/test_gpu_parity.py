@@ -106,7 +106,7 @@ def test_quant_strided_input_and_special_rows(fp8):
 def test_rmsnorm_quant_wide_gamma_and_special_rows(fp8, K, s_act):
     """gamma spans 2^-40 .. 2^41 with random signs, so y_b crosses both edges of
     the band of magnitudes whose code needs the division, under every scale.
-    K <= 8192 with 2^-100 <= s_act <= 2^100 takes the code lookup, the rest the
+    2048 <= K <= 8192 with 2^-100 <= s_act <= 2^100 takes the code lookup, the rest the
     per-element path; both must give the oracle's bytes.  Special rows: inf, NaN,
     all zeros with eps = 0 (r = inf), a lone subnormal; then an infinite gamma."""
     rng = np.random.default_rng(4200 + K)
