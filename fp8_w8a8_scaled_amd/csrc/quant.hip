@@ -130,6 +130,18 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_rmsnorm(
 // in order), so r is bitwise the same.  A thread holds its pieces of the row
 // and of gamma in registers and loads its pieces of the group's next row
 // before the row's barrier.
+// Entries 1 .. kCodeBand of a band table: entry 1 + e holds the code of the
+// bf16 magnitude lo + e.  Adding 128 to a finite bf16 pattern doubles its
+// value, and every quotient here is an fp32 normal in [2^-11, 2^9), where the
+// rounded quotient doubles with it: fl32(h 2^k / s) = 2^k fl32(h / s).  So one
+// division per mantissa serves all 20 binades.  blockDim.x is a multiple of 128.
+__device__ __forceinline__ void fill_band_table(uint8_t* tab, uint32_t lo, float s_act)
+{
+    const float q0 = bf16_to_f32(lo + (threadIdx.x & 127u)) / s_act;
+    for (int e = threadIdx.x; e < (int)kCodeBand; e += blockDim.x)
+        tab[1 + e] = f32_to_e4m3_sat(q0 * __uint_as_float((127u + (uint32_t)(e >> 7)) << 23));
+}
+
 template <int G>
 struct RmsLutShared {
     uint8_t tab[kCodeBand + 2];        // [0]: below the band, [1 + i]: band entry i, [kCodeBand + 1]: above
@@ -190,8 +202,8 @@ __global__ __launch_bounds__(G * kRmsRowThreads) void k_quant_rmsnorm_lut(
     }
     const uint32_t lo = code_band_lo(s_act);
     const int lo1 = (int)lo - 1;                         // table index of magnitude a: clamp(a - lo1)
-    for (int j = threadIdx.x; j < (int)kCodeBand + 2; j += blockDim.x)
-        sh.tab[j] = j == 0 ? 0u : j > (int)kCodeBand ? 0x7eu : quant_value(bf16_to_f32(lo - 1u + (uint32_t)j), s_act);
+    fill_band_table(sh.tab, lo, s_act);
+    if (threadIdx.x == 0) sh.tab[0] = 0u, sh.tab[kCodeBand + 1] = 0x7eu;
     const bool gamma_ok = __syncthreads_and(g_fin);       // also orders the table before its first read
 
     // one row of the group: `in` holds it, `nx` receives the group's next row
@@ -647,8 +659,8 @@ __global__ __launch_bounds__(kPlainLutThreads) void k_quant_plain_lut(
     __shared__ uint8_t tab[kCodeBand + 3];
     const uint32_t lo = code_band_lo(s_act);
     const int lo1 = (int)lo - 1;
-    for (int j = threadIdx.x; j < (int)kCodeBand + 3; j += blockDim.x)
-        tab[j] = j == 0 ? 0u : j > (int)kCodeBand ? 0x7eu : quant_value(bf16_to_f32(lo - 1u + (uint32_t)j), s_act);
+    fill_band_table(tab, lo, s_act);
+    if (threadIdx.x == 0) tab[0] = 0u, tab[kCodeBand + 1] = 0x7eu, tab[kCodeBand + 2] = 0x7eu;
     __syncthreads();
     constexpr uint32_t kStep = (uint32_t)NP * kPlainLutThreads;
     const uint32_t per = ((total + gridDim.x - 1) / gridDim.x + kStep - 1) / kStep * kStep;
