@@ -1,6 +1,6 @@
 // act_quant.h -- per-piece steps of the activation quant (16-byte pieces of 8
-// bf16 values), shared by the standalone quant kernels and the GEMM kernel
-// that quantizes its own input, so both produce the same bytes.
+// bf16 values), shared by the activation quant kernels so that every one of
+// them produces the same bytes.
 //
 // Fused RMSNorm -> FP8 (vllm.cpp issue #417, ranked follow-ons:
 // InputLayernormFp8, byte-exact against QuantFp8Static), per row:

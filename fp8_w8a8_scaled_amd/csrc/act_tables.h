@@ -96,6 +96,27 @@ __device__ __host__ __forceinline__ uint32_t code_table_entry(uint32_t h, uint32
     return sg | (a > 0x7f80u ? 0x7fu : 0x7eu);
 }
 
+// Entries 1 .. kCodeBand of a band table (entry 1 + e: the code of the bf16
+// magnitude lo + e; entries 0 and kCodeBand + 1 are the caller's), the share
+// of thread `tid` of `nthreads` (a multiple of 128).  Adding 128 to a finite
+// bf16 pattern doubles its value, and every quotient here is an fp32 normal
+// in [2^-11, 2^9), where the rounded quotient doubles with it: fl32(h 2^k / s)
+// = 2^k fl32(h / s).  So each thread divides once, for the mantissa lo +
+// tid % 128, and scales that quotient by 2^k for each of its entries (all of
+// the same mantissa, since nthreads is a multiple of 128).  Same bytes as
+// code_table_entry for 2^-100 <= s_act <= 2^100.
+__device__ __host__ __forceinline__ void fill_band_table(uint8_t* tab, uint32_t lo, float s_act, int tid,
+                                                         int nthreads)
+{
+    const float q0 = bf16_to_f32(lo + ((uint32_t)tid & 127u)) / s_act;
+    for (int e = tid; e < (int)kCodeBand; e += nthreads) {
+        const uint32_t pw = (127u + (uint32_t)(e >> 7)) << 23;   // 2^(e / 128)
+        float p2;
+        __builtin_memcpy(&p2, &pw, 4);
+        tab[1 + e] = (uint8_t)f32_to_e4m3_sat(q0 * p2);
+    }
+}
+
 // fp32 -> bf16 bits, round to nearest even, NaN -> quiet NaN with its sign,
 // written without branches (same results as f32_to_bf16_rne).
 __device__ __host__ __forceinline__ uint32_t f32_to_bf16_rne_sel(float f)

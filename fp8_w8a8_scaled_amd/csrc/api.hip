@@ -16,8 +16,7 @@
 
 namespace {
 
-// Default threshold: largest M served by the small-M arm.  Chosen from the
-// measured crossover of the two arms on MI355X.
+// Default threshold: the largest M served by the small-M arm.
 constexpr int64_t kDefaultThreshold = 32;
 
 int64_t initial_threshold()

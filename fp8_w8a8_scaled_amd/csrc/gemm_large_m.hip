@@ -154,17 +154,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
 // with row-contiguous 16-byte stores.
 // Rows past M or N load a clamped (real) row and are never stored.
 // ---------------------------------------------------------------------------
-#ifndef FP8MM_LARGEM_GM
-#define FP8MM_LARGEM_GM 8
-#endif
+constexpr int kGroupM = 8;                   // x_q row-tiles per tile group (L2 sharing)
 
-// 1: C tile stores marked non-temporal.  The workgroups finish their tiles at
+// The C tile stores are non-temporal.  The workgroups finish their tiles at
 // about the same time, and the C tiles they write (4 MB per XCD per round)
 // would otherwise displace from L2 the operand panels the next round reads;
 // measured 13% faster on the prefill gate_up shape.
-#ifndef FP8MM_LARGEM_NTSTORE
-#define FP8MM_LARGEM_NTSTORE 1
-#endif
+__device__ __forceinline__ void store_c16(void* dst, const uint4 v)
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     const int nbx = (nb >> 3) + (xcd < (nb & 7) ? 1 : 0);
     const int tiles_x = (ntiles >> 3) + (xcd < (ntiles & 7) ? 1 : 0);
     const int start_x = xcd * (ntiles >> 3) + (xcd < (ntiles & 7) ? xcd : (ntiles & 7));
-    const int GM = FP8MM_LARGEM_GM;
+    const int GM = kGroupM;
     const int in_group = GM * num_n;
     // operand buffers: rows past N or M load zeros
     const __amdgpu_buffer_rsrc_t rw = operand_rsrc(wq, N * K), rx = operand_rsrc(xq, M * K);
@@ -458,14 +458,7 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
                     for (int r = 0; r < 4; ++r) {
                         const int64_t m = m0 + h * HX + (tid >> 6) + 4 * (g + r);
                         if (m < M) {
-                            float* dst = col + m * ldo;
-#if FP8MM_LARGEM_NTSTORE
-                            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-                            __builtin_nontemporal_store(u32x4{v[r].x, v[r].y, v[r].z, v[r].w},
-                                                        reinterpret_cast<u32x4*>(dst));
-#else
-                            *reinterpret_cast<uint4*>(dst) = v[r];
-#endif
+                            store_c16(col + m * ldo, v[r]);
                         }
                     }
                 }
@@ -513,14 +506,7 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
                 for (int r = 0; r < 4; ++r) {
                     const int64_t m = m0 + (tid >> 5) + 8 * (g + r);
                     if (m < M) {
-                        uint16_t* dst = col + m * ldo;
-#if FP8MM_LARGEM_NTSTORE
-                        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-                        __builtin_nontemporal_store(u32x4{v[r].x, v[r].y, v[r].z, v[r].w},
-                                                    reinterpret_cast<u32x4*>(dst));
-#else
-                        *reinterpret_cast<uint4*>(dst) = v[r];
-#endif
+                        store_c16(col + m * ldo, v[r]);
                     }
                 }
             }

@@ -10,83 +10,28 @@
 // vllm.cpp #213 "+0.0532 splitK reduce").
 //
 // Design (MI355X-first, not a port of those tiles):
-//  * a workgroup owns NT x 16 rows of W (NT MFMA A tiles) and the whole K; its
-//    W waves split K into 128-byte chunks, wave w taking chunks w, w+W, ..., so
-//    the workgroup sweeps each weight row front to back;
-//  * every lane streams 2 x 16 B of each of its rows per chunk straight from
-//    HBM into registers: bytes [16g, 16g+16) and [64+16g, 80+16g) of the chunk
-//    for lane group g, so one load instruction covers 64 contiguous bytes of
-//    each of 16 rows.  Each weight byte feeds one MFMA only, so there is no LDS
-//    staging.  Loads run a batch of chunks ahead of the MFMAs (double buffer);
-//  * v_mfma_f32_16x16x128_f8f6f4 with x_q as the B operand, M padded to 16
-//    (MT = 2 or 4 M tiles for M <= 32 / 64).  x_q (at most 64 x K bytes) is read
-//    from L2 with the same K mapping as W, which is all the MFMA needs;
+//  * a 16-row weight tile is reduced over K by W waves of one workgroup: K is
+//    cut into 128-byte chunks and wave w takes chunks w, w+W, ... (W = a
+//    function of K only);
+//  * every weight byte feeds exactly one v_mfma_f32_16x16x128_f8f6f4, with
+//    x_q as the B operand (M padded to 16; MT = 2 or 4 B tiles for M <= 32 /
+//    64);
 //  * the W per-wave partial sums are reduced in LDS in a fixed order (no
-//    atomics), then the scale epilogue and the bf16 store happen in registers.
-//  W and the chunk assignment depend on K only, so every column's summation
-//  order is the same for a merged call and a per-shard call: bitwise identical.
+//    atomics, no workspace), then the scale epilogue and the store happen in
+//    registers.
+// Two kernels share that work split, so they give the same bits:
+//  * k_gemm_small_m_ring (M <= 16, K % 1024 == 0, every decode shape):
+//    persistent, one workgroup per CU walking its weight tiles; each wave
+//    streams its chunks with whole-line direct-to-LDS loads into a private
+//    ring of LDS slots, x_q staged in LDS once (or streamed with each chunk
+//    when it does not fit);
+//  * k_gemm_small_m (anything else up to M = 64): one workgroup per tile, the
+//    fragments loaded straight into registers.
+// W and the chunk assignment depend on K only, so every column's summation
+// order is the same for a merged call and a per-shard call: bitwise identical.
 #include "device_common.h"
 #include "internal.h"
 #include "out_store.h"
-
-// Tuning knobs (build-time).  Target chunks per wave -> waves per workgroup.
-#ifndef FP8MM_SMALLM_CPW
-#define FP8MM_SMALLM_CPW 5
-#endif
-// Chunk fragments (x N tiles x M tiles) in flight per wave per batch.
-#ifndef FP8MM_SMALLM_BATCH
-#define FP8MM_SMALLM_BATCH 2
-#endif
-// 1: issue the next batch's loads before the current batch's MFMAs.
-#ifndef FP8MM_SMALLM_PIPE
-#define FP8MM_SMALLM_PIPE 1
-#endif
-// 16-row N tiles per workgroup (each wave covers all of them; x_q is reused).
-#ifndef FP8MM_SMALLM_NT
-#define FP8MM_SMALLM_NT 1
-#endif
-// 1: weight loads marked non-temporal (streamed once).
-#ifndef FP8MM_SMALLM_NTLOAD
-#define FP8MM_SMALLM_NTLOAD 0
-#endif
-
-// Largest LDS footprint (x_q rows + reduction) of the all-in-flight variant;
-// 0 disables it.  Three workgroups of this size fit in a 160 KB CU.
-#ifndef FP8MM_SMALLM_XLDS_MAX
-#define FP8MM_SMALLM_XLDS_MAX (52 * 1024)
-#endif
-// 16-row weight tiles per workgroup of the all-in-flight variant (x_q reuse).
-#ifndef FP8MM_SMALLM_XLDS_NT
-#define FP8MM_SMALLM_XLDS_NT 1
-#endif
-
-// Persistent variant (one workgroup per CU walking its weight tiles): 1 = on.
-#ifndef FP8MM_SMALLM_PERSIST
-#define FP8MM_SMALLM_PERSIST 1
-#endif
-
-// Cache-policy bits of the streamed weight loads: 2 = nt (streamed once,
-// non-temporal; measured faster than the default on every decode shape).
-#ifndef FP8MM_SMALLM_CPOL
-#define FP8MM_SMALLM_CPOL 2
-#endif
-
-// Ring kernel: row-balanced last round where whole tiles are badly
-// unbalanced over the CUs (see k_gemm_small_m_ring): 1 = on.
-#ifndef FP8MM_SMALLM_BAL
-#define FP8MM_SMALLM_BAL 1
-#endif
-
-// Persistent variant with the weight staged through per-wave LDS rings: 1 = on.
-#ifndef FP8MM_SMALLM_RING
-#define FP8MM_SMALLM_RING 1
-#endif
-
-// Persistent variant: reduce every tile once, at the end (1), when the
-// partials of all of a workgroup's tiles fit in LDS; else tile by tile.
-#ifndef FP8MM_SMALLM_DEFER
-#define FP8MM_SMALLM_DEFER 1
-#endif
 
 // s_waitcnt with only vmcnt constrained (expcnt = 7, lgkmcnt = 15: no wait);
 // a compile-time count.
@@ -98,22 +43,14 @@ namespace fp8mm {
 
 namespace {
 
-constexpr int kXldsMaxCpw = 8;   // weight chunks per wave held in registers
-constexpr int kXldsNT = FP8MM_SMALLM_XLDS_NT;   // 16-row tiles per workgroup
 constexpr int kChunk = 128;     // K bytes per MFMA (16x16x128)
 constexpr int kMaxWaves = 16;
-constexpr int kNT = FP8MM_SMALLM_NT;
-
-__device__ __forceinline__ uint4 ld16_stream(const uint8_t* p)
-{
-#if FP8MM_SMALLM_NTLOAD
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v[0], v[1], v[2], v[3]);
-#else
-    return *reinterpret_cast<const uint4*>(p);
-#endif
-}
+constexpr int kCpw = 5;         // target 128-byte chunks per wave: fixes the waves per workgroup
+constexpr int kBatch = 2;       // chunk fragments (x M tiles) in flight per wave, generic kernel
+// Cache-policy bits of the streamed weight loads of the ring kernel: 2 = nt
+// (non-temporal: the weight is read once; measured faster than the default on
+// every decode shape).
+constexpr int kWeightCpol = 2;
 
 // Branch-free masked 16-byte load: the address is always an in-bounds one (the
 // caller passes a fallback), and invalid lanes get zeros through a select.  A
@@ -122,12 +59,6 @@ __device__ __forceinline__ uint4 ld16_stream(const uint8_t* p)
 __device__ __forceinline__ uint4 ld16_masked(const uint8_t* p, const uint8_t* safe, bool ok)
 {
     const uint4 v = *reinterpret_cast<const uint4*>(ok ? p : safe);
-    return ok ? v : make_uint4(0u, 0u, 0u, 0u);
-}
-
-__device__ __forceinline__ uint4 ld16_stream_masked(const uint8_t* p, const uint8_t* safe, bool ok)
-{
-    const uint4 v = ld16_stream(ok ? p : safe);
     return ok ? v : make_uint4(0u, 0u, 0u, 0u);
 }
 
@@ -141,14 +72,17 @@ __device__ __forceinline__ v8i pack(const uint4 lo, const uint4 hi)
 
 template <int MT, int B>
 struct Frags {
-    uint4 a[B][kNT][2];
+    uint4 a[B][2];
     uint4 b[B][MT][2];
 };
 
+// Chunks i0 .. i0+B-1 of this wave (chunk c = wave + i W): the weight row's
+// and the MT x_q rows' two 16-byte pieces each, zeros where a chunk, row or
+// piece does not exist.
 template <int MT, int B>
 __device__ __forceinline__ void load_batch(Frags<MT, B>& f, int i0, int nc, int wave, int W, int g, int64_t K,
-                                           const uint8_t* const (&wrow)[kNT], const bool (&wv)[kNT],
-                                           const uint8_t* const (&xrow)[MT], const bool (&xv)[MT])
+                                           const uint8_t* wrow, bool wv, const uint8_t* const (&xrow)[MT],
+                                           const bool (&xv)[MT])
 {
 #pragma unroll
     for (int j = 0; j < B; ++j) {
@@ -156,11 +90,8 @@ __device__ __forceinline__ void load_batch(Frags<MT, B>& f, int i0, int nc, int 
         const int64_t k0 = c * kChunk + g * 16;          // this lane's two 16-byte pieces
         const bool cv = (i0 + j) < nc;
         const bool v0 = cv && k0 < K, v1 = cv && k0 + 64 < K;
-#pragma unroll
-        for (int t = 0; t < kNT; ++t) {
-            f.a[j][t][0] = ld16_stream_masked(wrow[t] + k0, wrow[t], v0 && wv[t]);
-            f.a[j][t][1] = ld16_stream_masked(wrow[t] + k0 + 64, wrow[t], v1 && wv[t]);
-        }
+        f.a[j][0] = ld16_masked(wrow + k0, wrow, v0 && wv);
+        f.a[j][1] = ld16_masked(wrow + k0 + 64, wrow, v1 && wv);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             f.b[j][mt][0] = ld16_masked(xrow[mt] + k0, xrow[mt], v0 && xv[mt]);
@@ -170,65 +101,58 @@ __device__ __forceinline__ void load_batch(Frags<MT, B>& f, int i0, int nc, int 
 }
 
 template <int MT, int B>
-__device__ __forceinline__ void mfma_batch(const Frags<MT, B>& f, v4f (&acc)[kNT][MT])
+__device__ __forceinline__ void mfma_batch(const Frags<MT, B>& f, v4f (&acc)[MT])
 {
 #pragma unroll
-    for (int j = 0; j < B; ++j)
+    for (int j = 0; j < B; ++j) {
+        const v8i A = pack(f.a[j][0], f.a[j][1]);
 #pragma unroll
-        for (int t = 0; t < kNT; ++t) {
-            const v8i A = pack(f.a[j][t][0], f.a[j][t][1]);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[t][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    A, pack(f.b[j][mt][0], f.b[j][mt][1]), acc[t][mt], 0, 0, 0, 0, 0, 0);
-        }
+        for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, pack(f.b[j][mt][0], f.b[j][mt][1]), acc[mt],
+                                                                      0, 0, 0, 0, 0, 0);
+    }
 }
 
-// Sum the W per-wave partials red[W][NTt][MT][64] in wave order (fixed, no
-// atomics), apply the scales in fp32 and store bf16.  16x16 MFMA C layout:
-// lane l holds rows 4*(l/16)+v (= n) of column l%16 (= m).
-template <int MT, int NTt>
+// Sum the W per-wave partials red[W][MT][64] in wave order (fixed, no
+// atomics), apply the scales in fp32 and store.  16x16 MFMA C layout: lane l
+// holds rows 4*(l/16)+v (= n) of column l%16 (= m).
+template <int MT>
 __device__ __forceinline__ void reduce_store(const v4f* red, int W, int64_t n0, float s_act,
-                                             const float* __restrict__ s_w, const ShardTable& sh,
-                                             int M, int64_t N)
+                                             const float* __restrict__ s_w, const ShardTable& sh, int M, int64_t N)
 {
-    for (int idx = threadIdx.x; idx < NTt * MT * 64; idx += blockDim.x) {   // blocks may be narrower
-        const int t = idx / (MT * 64), mt = (idx >> 6) % MT, l = idx & 63;
-        const int64_t nt0 = n0 + 16 * t;
+    for (int idx = threadIdx.x; idx < MT * 64; idx += blockDim.x) {   // blocks may be narrower
+        const int mt = idx >> 6, l = idx & 63;
         const int m = mt * 16 + (l & 15);
-        if (nt0 >= N || m >= M) continue;
-        v4f s = red[(t * MT + mt) * 64 + l];
+        if (n0 >= N || m >= M) continue;
+        v4f s = red[mt * 64 + l];
         for (int w = 1; w < W; ++w) {
-            const v4f p = red[((w * NTt + t) * MT + mt) * 64 + l];
+            const v4f p = red[(w * MT + mt) * 64 + l];
             s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
         }
-        const int64_t n = nt0 + 4 * (l >> 4);
+        const int64_t n = n0 + 4 * (l >> 4);
         const float4 sw = *reinterpret_cast<const float4*>(s_w + n);
         const float sa = row_scale(sh, m, s_act);
-        store_out4(sh, shard_of(sh, nt0), m, n, (s.x * sa) * sw.x, (s.y * sa) * sw.y, (s.z * sa) * sw.z,
+        store_out4(sh, shard_of(sh, n0), m, n, (s.x * sa) * sw.x, (s.y * sa) * sw.y, (s.z * sa) * sw.z,
                    (s.w * sa) * sw.w);
     }
 }
 
+// Generic kernel (any M <= 64, any K % 16 == 0): one workgroup per 16-row
+// weight tile, the weight and x_q fragments loaded straight into registers
+// (MFMA operand layout), a batch of chunks ahead of the MFMAs.
 template <int MT>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act,
     const float* __restrict__ s_w, ShardTable sh, int M, int64_t N, int64_t K, int nchunks)
 {
-    extern __shared__ v4f red[];                       // [W][kNT][MT][64]
-    constexpr int B = FP8MM_SMALLM_BATCH / (MT * kNT) > 0 ? FP8MM_SMALLM_BATCH / (MT * kNT) : 1;
+    extern __shared__ v4f red[];                       // [W][MT][64]
+    constexpr int B = kBatch / MT > 0 ? kBatch / MT : 1;
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * (16 * kNT);
-
-    const uint8_t* wrow[kNT];
-    bool wv[kNT];
-#pragma unroll
-    for (int t = 0; t < kNT; ++t) {
-        wv[t] = n0 + 16 * t < N;                        // a ragged last workgroup may hold fewer tiles
-        wrow[t] = wq + (wv[t] ? n0 + 16 * t + r : r) * K;
-    }
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const bool wv = n0 < N;
+    const uint8_t* wrow = wq + (wv ? n0 + r : r) * K;
     const uint8_t* xrow[MT];
     bool xv[MT];
 #pragma unroll
@@ -238,14 +162,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m(
         xrow[mt] = xq + (int64_t)(xv[mt] ? m : 0) * K;
     }
 
-    v4f acc[kNT][MT];
+    v4f acc[MT];
 #pragma unroll
-    for (int t = 0; t < kNT; ++t)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const int nc = (nchunks - wave + W - 1) / W;       // chunks owned by this wave
-#if FP8MM_SMALLM_PIPE
     Frags<MT, B> cur;
     load_batch<MT, B>(cur, 0, nc, wave, W, g, K, wrow, wv, xrow, xv);
     for (int i0 = 0; i0 < nc; i0 += B) {
@@ -255,115 +176,29 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m(
         mfma_batch<MT, B>(cur, acc);
         if (more) cur = nxt;
     }
-#else
-    for (int i0 = 0; i0 < nc; i0 += B) {
-        Frags<MT, B> cur;
-        load_batch<MT, B>(cur, i0, nc, wave, W, g, K, wrow, wv, xrow, xv);
-        mfma_batch<MT, B>(cur, acc);
-    }
-#endif
 
     // Fixed-order reduction of the W per-wave partials.
 #pragma unroll
-    for (int t = 0; t < kNT; ++t)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) red[((wave * kNT + t) * MT + mt) * 64 + lane] = acc[t][mt];
+    for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = acc[mt];
     __syncthreads();
-    reduce_store<MT, kNT>(red, W, n0, s_act, s_w, sh, M, N);
+    reduce_store<MT>(red, W, n0, s_act, s_w, sh, M, N);
 }
 
-
-// All-in-flight variant for M <= 16 and K % 1024 == 0 when x_q fits in LDS:
-// every wave issues the loads of ALL its weight chunks at once (CPW x 2 x 16 B
-// per lane, into registers); the workgroup then copies x_q[0:M, :] into LDS
-// with direct global->LDS loads (no registers; rows padded to K + 16 bytes so
-// the 16 fragment rows of an MFMA fall in distinct banks), waits once, and the
-// MFMAs read their B fragments from LDS.  With every workgroup resident, the
-// whole weight is requested up front, which is what a 50-200 MB stream needs
-// to reach the HBM rate.  Same chunk assignment and reduction order as
-// k_gemm_small_m, so both kernels give identical bits.
+// Weight staging through LDS for the persistent ring kernel.  A weight load
+// instruction in which each lane takes 16 bytes of a 16-row fragment in the
+// MFMA operand layout (lane -> row) touches 16 half cache lines; one in which 8
+// lanes cover a row's 128-byte chunk (8 rows per instruction) touches 8 whole
+// lines, and the memory pipeline streams the latter markedly faster at decode
+// sizes.  So each wave moves its chunks with whole-line direct-to-LDS loads
+// into a private ring of S 2 KB slots and reads its A fragments back from
+// there (no barrier: the wave that loads a slot is the only one reading it).
+// Within a slot row n holds its 16-byte pieces XOR-swizzled by row (skipping
+// one row bit), so the fragment reads are bank-conflict free.
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int CPW, int NTX>
-__global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_xlds(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act,
-    const float* __restrict__ s_w, ShardTable sh, int M, int64_t N, int64_t K, int nchunks)
-{
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int W = blockDim.x >> 6;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane & 15, g = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * (16 * NTX);
-    const int64_t ldsx = K + 16;
-    uint8_t* xs = smem;
-    v4f* red = reinterpret_cast<v4f*>(smem + ((M * ldsx + 15) & ~(int64_t)15));
-
-    // every weight chunk of this wave (for each of its NTX row tiles), all in flight
-    const uint8_t* wrow[NTX];
-    bool wok[NTX];
-#pragma unroll
-    for (int t = 0; t < NTX; ++t) {
-        wok[t] = n0 + 16 * t < N;                          // a ragged last workgroup holds fewer tiles
-        wrow[t] = wq + (wok[t] ? n0 + 16 * t + r : r) * K;
-    }
-    uint4 a[CPW][NTX][2];
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-        const int64_t c = (int64_t)wave + (int64_t)i * W;
-        const int64_t k0 = c * kChunk + g * 16;
-        const bool cv = c < nchunks;
-#pragma unroll
-        for (int t = 0; t < NTX; ++t) {
-            a[i][t][0] = ld16_stream_masked(wrow[t] + k0, wrow[t], wok[t] && cv && k0 < K);
-            a[i][t][1] = ld16_stream_masked(wrow[t] + k0 + 64, wrow[t], wok[t] && cv && k0 + 64 < K);
-        }
-    }
-    // x_q -> LDS: each wave moves 64 consecutive 16-byte pieces (1 KB, inside
-    // one row because K/16 is a multiple of 64) per instruction.
-    const int64_t kp = K >> 4, np = (int64_t)M * kp;
-    for (int64_t p0 = (int64_t)wave * 64; p0 < np; p0 += blockDim.x) {
-        const int64_t row = p0 / kp, col0 = p0 - row * kp;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(xq + (p0 + lane) * 16),
-                                         (lds_void*)(xs + row * ldsx + col0 * 16), 16, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);                      // all loads, weight and x_q, have landed
-    __syncthreads();
-
-    v4f acc[NTX];
-#pragma unroll
-    for (int t = 0; t < NTX; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-    const bool xr = r < M;
-    const uint8_t* xrow = xs + (xr ? r : 0) * ldsx;
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-        const int64_t c = (int64_t)wave + (int64_t)i * W;
-        if (c >= nchunks) break;                          // wave-uniform
-        const int64_t k0 = c * kChunk + g * 16;
-        const v8i B = pack(ld16_masked(xrow + k0, xrow, xr && k0 < K), ld16_masked(xrow + k0 + 64, xrow, xr && k0 + 64 < K));
-#pragma unroll
-        for (int t = 0; t < NTX; ++t)
-            acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pack(a[i][t][0], a[i][t][1]), B, acc[t],
-                                                                     0, 0, 0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int t = 0; t < NTX; ++t) red[(wave * NTX + t) * 64 + lane] = acc[t];
-    __syncthreads();
-    reduce_store<1, NTX>(red, W, n0, s_act, s_w, sh, M, N);
-}
-
-// Persistent variant for M <= 16 and K % 1024 == 0 when x_q fits in LDS next
-// to the reduction buffers: one workgroup per CU walks the 16-row weight
-// tiles bid, bid + G, bid + 2G, ... (G workgroups).  x_q[0:M, :] is copied
-// into LDS once per workgroup (not once per tile), and the weight loads of
-// the next D tiles are always in flight: each wave keeps a ring of D tiles x
-// CPW chunks of registers, refilling a slot as soon as its MFMAs have read
-// it.  Weight loads are raw buffer loads over the whole weight; a chunk or
-// tile that does not exist loads from an offset past the end of the buffer,
-// which returns zeros without a memory access, so every wave issues the same
-// instruction stream and the wait counts stay static.  The per-tile
-// reduction of the W wave partials is the fixed-order one of the other two
-// kernels (same chunk -> wave assignment), so all three give identical bits.
-constexpr uint32_t kOob = 0x80000000u;   // > any weight byte offset served here (N*K < 2^31)
+// A tile or chunk that does not exist loads from this offset, past the end of
+// the buffer resource: zeros without a memory access (N*K < 2^31 here).
+constexpr uint32_t kOob = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const uint8_t* p, int64_t bytes)
 {
@@ -372,51 +207,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const uint8_t* p, 
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-// The CPW chunks of one weight tile this wave owns: 2 x 16 bytes per lane and
-// chunk ([16g, 16g+16) and [64+16g, 80+16g) of the chunk, row r of the tile).
-template <int CPW>
-__device__ __forceinline__ void issue_tile(u32x4_t (&a)[CPW][2], __amdgpu_buffer_rsrc_t rw, uint32_t tile_off,
-                                           bool tile_ok, int wave, int W, int nchunks)
-{
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-        const int chunk = wave + c * W;
-        const uint32_t v = (tile_ok && chunk < nchunks) ? tile_off + (uint32_t)chunk * kChunk : kOob;
-        a[c][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)v, 0, 0);
-        a[c][1] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(v + 64), 0, 0);
-    }
-}
-
-// MFMAs of one tile; B fragments (x_q) from LDS.  A chunk past K reads the
-// last real chunk of x_q (its weight fragment is zero, and x_q is finite
-// there, so it adds exact zeros).
-template <int CPW>
-__device__ __forceinline__ v4f tile_mfma(const u32x4_t (&a)[CPW][2], const uint8_t* __restrict__ xrow, int wave,
-                                         int W, int nchunks, int g)
-{
-    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-        int chunk = wave + c * W;
-        chunk = chunk < nchunks ? chunk : nchunks - 1;
-        const uint8_t* p = xrow + chunk * kChunk + g * 16;
-        const uint4 b0 = *reinterpret_cast<const uint4*>(p), b1 = *reinterpret_cast<const uint4*>(p + 64);
-        v8i A, B;
-        A[0] = (int)a[c][0][0]; A[1] = (int)a[c][0][1]; A[2] = (int)a[c][0][2]; A[3] = (int)a[c][0][3];
-        A[4] = (int)a[c][1][0]; A[5] = (int)a[c][1][1]; A[6] = (int)a[c][1][2]; A[7] = (int)a[c][1][3];
-        B = pack(b0, b1);
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 0, 0, 0, 0, 0, 0);
-    }
-    return acc;
-}
-
 // Sum the W partials of one tile in wave order (partial of wave w for MFMA
 // lane `lane` at red[w * stride + slot]), scale (weight scales in sw: n = n0 +
-// 4*(lane/16) .. +3) and store bf16.  Rows n >= nend belong to another
-// workgroup (or do not exist) and are not stored.  The shard is that of n0
-// (one lookup for the tile: a tile starting at a multiple of 16 lies in one
-// shard), or with lane_shard that of each 4-row group (such a group never
-// straddles two shards: shard starts are multiples of 16).
+// 4*(lane/16) .. +3) and store.  Rows n >= nend belong to another workgroup
+// (or do not exist) and are not stored.  The shard is that of n0 (one lookup
+// for the tile: a tile starting at a multiple of 16 lies in one shard), or
+// with lane_shard that of each 4-row group (such a group never straddles two
+// shards: shard starts are multiples of 16).
 __device__ __forceinline__ void reduce_tile(const v4f* red, int stride, int slot, int W, int64_t n0, int64_t nend,
                                             float s_act, const float4 sw, const ShardTable& sh, int M, int lane,
                                             bool lane_shard = false)
@@ -434,99 +231,6 @@ __device__ __forceinline__ void reduce_tile(const v4f* red, int stride, int slot
                (s.w * sa) * sw.w);
 }
 
-template <int CPW, int D, int WMAX, bool DEFER>
-__global__ __launch_bounds__(64 * WMAX) void k_gemm_small_m_persist(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act,
-    const float* __restrict__ s_w, ShardTable sh, int M, int64_t N, int64_t K, int nchunks)
-{
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int W = blockDim.x >> 6;
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r = lane & 15, g = lane >> 4;
-    const int G = gridDim.x, bid = blockIdx.x;
-    const int ntiles = (int)(N >> 4);
-    const int my_tiles = (ntiles - bid + G - 1) / G;
-    __builtin_assume(my_tiles >= 1);                    // G <= ntiles
-    const int64_t ldsx = K + 16;
-    uint8_t* xs = smem;
-    // W partials: [2][W][64], or with DEFER [my_tiles][W][64] (reduced once, at the end)
-    v4f* red = reinterpret_cast<v4f*>(smem + ((M * ldsx + 15) & ~(int64_t)15));
-    const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
-    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
-    const uint32_t lane_off = (uint32_t)(r * K + g * 16);
-    auto tile_off = [&](int u) { return (uint32_t)((int64_t)(bid + u * G) * 16 * K) + lane_off; };
-    // weight scales of tile u for this lane's four rows (zeros past the last tile)
-    auto tile_sw = [&](int u) {
-        const uint32_t o = u < my_tiles ? (uint32_t)((bid + u * G) * 64 + g * 16) : kOob;
-        return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, 0, 0);
-    };
-
-    // x_q -> LDS first: each wave moves 64 consecutive 16-byte pieces (1 KB,
-    // inside one row because K/16 is a multiple of 64) per instruction.
-    const int64_t kp = K >> 4, np = (int64_t)M * kp;
-    for (int64_t p0 = (int64_t)wave * 64; p0 < np; p0 += blockDim.x) {
-        const int64_t row = p0 / kp, col0 = p0 - row * kp;
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(xq + (p0 + lane) * 16),
-                                         (lds_void*)(xs + row * ldsx + col0 * 16), 16, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    u32x4_t a[D][CPW][2], sws[D];
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-        issue_tile<CPW>(a[s], rw, tile_off(s), s < my_tiles, wave, W, nchunks);
-        if constexpr (!DEFER) sws[s] = tile_sw(s);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // x_q landed: only the D tiles' weight (and scale) loads, issued after it,
-    // may be in flight (for this wave; the barrier extends it to the workgroup)
-    __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT(D * (2 * CPW + (DEFER ? 0 : 1))));
-    __builtin_amdgcn_s_barrier();
-
-    const uint8_t* xrow = xs + (r < M ? r : M - 1) * ldsx;
-    for (int u0 = 0; u0 < my_tiles; u0 += D) {
-#pragma unroll
-        for (int s = 0; s < D; ++s) {
-            const int u = u0 + s;
-            if (u >= my_tiles) break;                    // workgroup-uniform
-            const v4f acc = tile_mfma<CPW>(a[s], xrow, wave, W, nchunks, g);
-            issue_tile<CPW>(a[s], rw, tile_off(u + D), u + D < my_tiles, wave, W, nchunks);
-            if constexpr (DEFER) {
-                red[(u * W + wave) * 64 + lane] = acc;
-            } else {
-                const u32x4_t swu = sws[s];
-                sws[s] = tile_sw(u + D);
-                v4f* rb = red + (u & 1) * W * 64;
-                rb[wave * 64 + lane] = acc;
-                __syncthreads();
-                if (wave == 0)
-                    reduce_tile(rb, 64, lane, W, (int64_t)(bid + u * G) * 16, N, s_act,
-                                make_float4(__uint_as_float(swu[0]), __uint_as_float(swu[1]),
-                                            __uint_as_float(swu[2]), __uint_as_float(swu[3])),
-                                sh, M, lane);
-            }
-        }
-    }
-    if constexpr (DEFER) {                               // one barrier, then every wave reduces
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < my_tiles * 64; idx += blockDim.x) {
-            const int u = idx >> 6, l = idx & 63;
-            const int64_t n0 = (int64_t)(bid + u * G) * 16;
-            reduce_tile(red + u * W * 64, 64, l, W, n0, N, s_act,
-                        *reinterpret_cast<const float4*>(s_w + n0 + 4 * (l >> 4)), sh, M, l);
-        }
-    }
-}
-
-// Weight staging through LDS for the persistent variant.  A weight load
-// instruction in which each lane takes 16 bytes of a 16-row fragment in the
-// MFMA operand layout (lane -> row) touches 16 half cache lines; one in which 8
-// lanes cover a row's 128-byte chunk (8 rows per instruction) touches 8 whole
-// lines, and the memory pipeline streams the latter markedly faster at decode
-// sizes.  So each wave moves its chunks with whole-line direct-to-LDS loads
-// into a private ring of S 2 KB slots and reads its A fragments back from
-// there (no barrier: the wave that loads a slot is the only one reading it).
-// Within a slot row n holds its 16-byte pieces XOR-swizzled by row (skipping
-// one row bit), so the fragment reads are bank-conflict free.
 __device__ __forceinline__ int wswz(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 
 // Chunk `chunk` of tile rows n0..n0+15 into an LDS slot: instruction i covers
@@ -537,9 +241,9 @@ __device__ __forceinline__ void dma_wchunk(__amdgpu_buffer_rsrc_t rw, uint8_t* s
 {
     const uint32_t c = (uint32_t)chunk * kChunk;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)slot, 16, (int)(ok ? row_off0 + c : kOob), 0, 0,
-                                             FP8MM_SMALLM_CPOL);
+                                             kWeightCpol);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(slot + 1024), 16, (int)(ok ? row_off1 + c : kOob), 0,
-                                             0, FP8MM_SMALLM_CPOL);
+                                             0, kWeightCpol);
 }
 
 // The A fragment (row r, logical pieces g and g+4) of a staged chunk, and the
@@ -657,8 +361,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
     };
     [[maybe_unused]] auto fire = [&](const Pend& pd, int slot) {
         uint8_t* sl = ring + slot * SB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)sl, 16, (int)pd.w0, 0, 0, FP8MM_SMALLM_CPOL);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sl + 1024), 16, (int)pd.w1, 0, 0, FP8MM_SMALLM_CPOL);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)sl, 16, (int)pd.w0, 0, 0, kWeightCpol);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sl + 1024), 16, (int)pd.w1, 0, 0, kWeightCpol);
         if (XI >= 1)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sl + 2048), 16, (int)pd.x0, 0, 0, 0);
         if (XI >= 2)
@@ -779,7 +483,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
 int small_m_waves(int64_t K)
 {
     const int64_t nchunks = (K + kChunk - 1) / kChunk;
-    int64_t w = (nchunks + FP8MM_SMALLM_CPW - 1) / FP8MM_SMALLM_CPW;
+    int64_t w = (nchunks + kCpw - 1) / kCpw;
     if (w < 1) w = 1;
     if (w > kMaxWaves) w = kMaxWaves;
     return (int)w;
@@ -788,7 +492,7 @@ int small_m_waves(int64_t K)
 }  // namespace
 
 // The reduction buffer can exceed the default 64 KB dynamic-LDS limit (W = 16
-// waves x 4 M tiles x NT tiles); allow up to the 160 KB a gfx950 CU has.
+// waves x 4 M tiles); allow up to the 160 KB a gfx950 CU has.
 template <int MT>
 void allow_large_lds()
 {
@@ -798,53 +502,6 @@ void allow_large_lds()
         return true;
     }();
     (void)done;
-}
-
-// LDS bytes of the all-in-flight variant, or 0 if it does not apply.
-size_t xlds_bytes(int64_t M, int64_t K, int W)
-{
-    if (M > 16 || K % 1024 != 0 || K > (int64_t)kChunk * kXldsMaxCpw * W) return 0;
-    const size_t b = (size_t)((M * (K + 16) + 15) & ~(int64_t)15) + (size_t)W * kXldsNT * 64 * sizeof(v4f);
-    return b <= (size_t)FP8MM_SMALLM_XLDS_MAX ? b : 0;
-}
-
-template <int CPW>
-void launch_xlds(const dim3& grid, const dim3& block, size_t lds, hipStream_t stream, const uint8_t* xq,
-                 const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh, int M, int64_t N,
-                 int64_t K, int nchunks)
-{
-    static const bool attr = [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_xlds<CPW, kXldsNT>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        return true;
-    }();
-    (void)attr;
-    hipLaunchKernelGGL((k_gemm_small_m_xlds<CPW, kXldsNT>), grid, block, lds, stream, xq, wq, s_act, s_w, sh,
-                       M, N, K, nchunks);
-}
-
-// LDS bytes of the persistent variant (x_q rows + reduction buffers for
-// `tiles` tiles), or 0 if it does not apply.
-size_t persist_bytes(int64_t M, int64_t N, int64_t K, int W, int64_t tiles)
-{
-    if (!FP8MM_SMALLM_PERSIST || M > 16 || K % 1024 != 0 || N * K >= ((int64_t)1 << 31)) return 0;
-    const size_t b = (size_t)((M * (K + 16) + 15) & ~(int64_t)15) + (size_t)tiles * W * 64 * sizeof(v4f);
-    return b <= (size_t)160 * 1024 ? b : 0;
-}
-
-template <int CPW, int D, int WMAX, bool DEFER>
-void launch_persist(const dim3& grid, const dim3& block, size_t lds, hipStream_t stream, const uint8_t* xq,
-                    const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh, int M, int64_t N,
-                    int64_t K, int nchunks)
-{
-    static const bool attr = [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_persist<CPW, D, WMAX, DEFER>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        return true;
-    }();
-    (void)attr;
-    hipLaunchKernelGGL((k_gemm_small_m_persist<CPW, D, WMAX, DEFER>), grid, block, lds, stream, xq, wq, s_act, s_w, sh,
-                       M, N, K, nchunks);
 }
 
 template <int S, bool DEFER, int XI, bool BAL>
@@ -868,12 +525,12 @@ void launch_ring(const dim3& grid, const dim3& block, size_t lds, hipStream_t st
 bool try_ring(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh,
               int64_t M, int64_t N, int64_t K, int W, int nchunks, hipStream_t stream)
 {
-    if (!FP8MM_SMALLM_RING || M > 16 || K % 1024 != 0 || N * K >= ((int64_t)1 << 31)) return false;
+    if (M > 16 || K % 1024 != 0 || N * K >= ((int64_t)1 << 31)) return false;
     const int64_t G = N / 16 < num_cus() ? N / 16 : num_cus();
     const int64_t tiles_max = (N / 16 + G - 1) / G;      // whole tiles, or FR + 1 with the balanced last round
     // Balanced last round when whole tiles leave the busiest workgroup at least
     // 1.3x the average weight bytes.
-    const bool bal = FP8MM_SMALLM_BAL && 10 * tiles_max * G >= 13 * (N / 16);
+    const bool bal = 10 * tiles_max * G >= 13 * (N / 16);
     const size_t xb = (size_t)((M * (K + 16) + 15) & ~(int64_t)15);
     const size_t part = (size_t)W * 64 * sizeof(v4f);               // one tile's partials
     const size_t dpart = (size_t)W * (M <= 8 ? 32 : 64) * sizeof(v4f);   // ... as the deferred buffer keeps them
@@ -917,64 +574,9 @@ void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, cons
     const int W = small_m_waves(K);
     const int nchunks = (int)((K + kChunk - 1) / kChunk);
     if (try_ring(xq, wq, s_act, s_w, shards, M, N, K, W, nchunks, stream)) return;
-    const int64_t G = N / 16 < num_cus() ? N / 16 : num_cus();
-    const int64_t tiles_max = (N / 16 + G - 1) / G;            // tiles of the busiest workgroup
-    // (deferring needs registers too: only with up to 8 waves, 256 VGPRs each)
-    const size_t pl_defer = FP8MM_SMALLM_DEFER && W <= 8 ? persist_bytes(M, N, K, W, tiles_max) : 0;
-    const size_t pl = pl_defer ? pl_defer : persist_bytes(M, N, K, W, 2);
-    const bool defer = pl_defer != 0;
-    if (pl) {
-        // Ring depth: as many tiles in flight as the registers allow (<= 3).
-        // Up to 8 waves: 2 waves per SIMD, 256 VGPRs each; more: 4, 128 VGPRs.
-        const int cpw = (nchunks + W - 1) / W;
-        const dim3 grid((uint32_t)G), block(64 * W);
-        const int budget = (W <= 8 ? 256 : 128) - 72;
-        int d = budget / (cpw * 8);
-        d = d < 1 ? 1 : (d > 3 ? 3 : d);
-#define FP8MM_PERSIST_ARGS grid, block, pl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks
-#define FP8MM_PERSIST_DISPATCH(C, DF)                                                         \
-        if (W > 8) launch_persist<C, 1, 16, DF>(FP8MM_PERSIST_ARGS);                           \
-        else if (d == 1) launch_persist<C, 1, 8, DF>(FP8MM_PERSIST_ARGS);                      \
-        else if (d == 2) launch_persist<C, 2, 8, DF>(FP8MM_PERSIST_ARGS);                      \
-        else launch_persist<C, 3, 8, DF>(FP8MM_PERSIST_ARGS);
-#define FP8MM_PERSIST_CASE(C)                                                                 \
-    case C:                                                                                   \
-        if (defer) { FP8MM_PERSIST_DISPATCH(C, true) } else { FP8MM_PERSIST_DISPATCH(C, false) } \
-        return;
-        switch (cpw) {
-            FP8MM_PERSIST_CASE(1)
-            FP8MM_PERSIST_CASE(2)
-            FP8MM_PERSIST_CASE(3)
-            FP8MM_PERSIST_CASE(4)
-            FP8MM_PERSIST_CASE(5)
-            FP8MM_PERSIST_CASE(6)
-            FP8MM_PERSIST_CASE(7)
-            FP8MM_PERSIST_CASE(8)
-            FP8MM_PERSIST_CASE(9)
-        default: break;                                  // more chunks per wave: the kernels below
-        }
-#undef FP8MM_PERSIST_ARGS
-#undef FP8MM_PERSIST_DISPATCH
-#undef FP8MM_PERSIST_CASE
-    }
-    const size_t xl = xlds_bytes(M, K, W);
-    if (xl) {
-        const int cpw = (nchunks + W - 1) / W;
-        const dim3 grid((uint32_t)((N + 16 * kXldsNT - 1) / (16 * kXldsNT))), block(64 * W);
-        switch (cpw) {
-        case 1: launch_xlds<1>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
-        case 2: launch_xlds<2>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
-        case 3: launch_xlds<3>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
-        case 4: launch_xlds<4>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
-        case 5: launch_xlds<5>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
-        case 6: launch_xlds<6>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
-        case 7: launch_xlds<7>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
-        default: launch_xlds<8>(grid, block, xl, stream, xq, wq, s_act, s_w, shards, (int)M, N, K, nchunks); return;
-        }
-    }
     const int MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    const size_t lds = (size_t)W * kNT * MT * 64 * sizeof(v4f);
-    const dim3 grid((uint32_t)((N + 16 * kNT - 1) / (16 * kNT))), block(64 * W);
+    const size_t lds = (size_t)W * MT * 64 * sizeof(v4f);
+    const dim3 grid((uint32_t)((N + 15) / 16)), block(64 * W);
     if (lds > 64 * 1024) {
         if (MT == 1) allow_large_lds<1>();
         else if (MT == 2) allow_large_lds<2>();

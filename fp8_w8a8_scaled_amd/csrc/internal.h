@@ -36,51 +36,6 @@ void launch_quant_per_token(const uint16_t* x, int64_t ldx, const uint16_t* gamm
                             float* s_rows, int64_t M, int64_t K, hipStream_t stream);
 void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, float s_act,
                            uint8_t* xq, int64_t M, int64_t I, hipStream_t stream);
-// Table-based SiLU*mul quant: workgroups per CU, 16-byte pieces per thread
-// and step, next-step prefetch, non-temporal loads.
-#ifndef FP8MM_SILU_LUT_BPC
-#define FP8MM_SILU_LUT_BPC 1
-#endif
-#ifndef FP8MM_SILU_NP
-#define FP8MM_SILU_NP 2
-#endif
-#ifndef FP8MM_SILU_PF
-#define FP8MM_SILU_PF 0
-#endif
-#ifndef FP8MM_SILU_NT
-#define FP8MM_SILU_NT 1
-#endif
-bool silu_mul_uses_table(int64_t M, int64_t I, float s_act);
-// Table-based plain static quant (same bytes): from this many elements on,
-// workgroups per CU, 16-byte pieces per thread and step.
-#ifndef FP8MM_PLAIN_LUT_MIN_ELEMS
-#define FP8MM_PLAIN_LUT_MIN_ELEMS (1LL << 20)
-#endif
-#ifndef FP8MM_PLAIN_LUT_BPC
-#define FP8MM_PLAIN_LUT_BPC 2
-#endif
-#ifndef FP8MM_PLAIN_LUT_NP
-#define FP8MM_PLAIN_LUT_NP 2
-#endif
-// plain static quant with 4 values per thread below this many elements
-#ifndef FP8MM_PLAIN_HALF_MAX_ELEMS
-#define FP8MM_PLAIN_HALF_MAX_ELEMS ((1LL << 20) - 1)
-#endif
-// Table-based fused RMSNorm quant (the same bytes as the per-element kernel):
-// from this many rows on, groups of 256 threads (one row each) per workgroup,
-// workgroups per CU.
-#ifndef FP8MM_RMS_LUT_MIN_ROWS
-#define FP8MM_RMS_LUT_MIN_ROWS 1
-#endif
-#ifndef FP8MM_RMS_LUT_MIN_K
-#define FP8MM_RMS_LUT_MIN_K 2048          // shorter rows do not repay the table
-#endif
-#ifndef FP8MM_RMS_LUT_GROUPS
-#define FP8MM_RMS_LUT_GROUPS 2
-#endif
-#ifndef FP8MM_RMS_LUT_BPC
-#define FP8MM_RMS_LUT_BPC 2
-#endif
 void launch_act_scale_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, int64_t M,
                                int64_t I, float* s_act, float* partial, hipStream_t stream);
 

@@ -22,6 +22,18 @@ namespace {
 
 constexpr int kQuantThreads = kRmsRowThreads;
 
+// Launch choices of the table-based kernels (measured on MI355X; the bytes do
+// not depend on them).
+constexpr int kSiluLutPerCu = 1;                  // SiLU*mul quant: workgroups per CU
+constexpr int kSiluLutPieces = 2;                 // ... 16-byte pieces per thread and step
+constexpr int64_t kPlainLutMinElems = 1LL << 20;  // plain quant: table path from this many elements
+constexpr int kPlainLutPerCu = 2;
+constexpr int kPlainLutPieces = 2;
+constexpr int64_t kPlainHalfMaxElems = (1LL << 20) - 1;   // plain quant: 4 values per thread below this
+constexpr int64_t kRmsLutMinK = 2048;             // fused RMSNorm quant: shorter rows do not repay the table
+constexpr int kRmsLutGroups = 2;                  // ... 256-thread row groups per workgroup
+constexpr int kRmsLutPerCu = 2;                   // ... workgroups per CU
+
 // Fixed-order block reduction of a double (wave butterfly, then waves in order).
 __device__ double block_sum_f64(double v, double* lds)
 {
@@ -130,18 +142,6 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_rmsnorm(
 // in order), so r is bitwise the same.  A thread holds its pieces of the row
 // and of gamma in registers and loads its pieces of the group's next row
 // before the row's barrier.
-// Entries 1 .. kCodeBand of a band table: entry 1 + e holds the code of the
-// bf16 magnitude lo + e.  Adding 128 to a finite bf16 pattern doubles its
-// value, and every quotient here is an fp32 normal in [2^-11, 2^9), where the
-// rounded quotient doubles with it: fl32(h 2^k / s) = 2^k fl32(h / s).  So one
-// division per mantissa serves all 20 binades.  blockDim.x is a multiple of 128.
-__device__ __forceinline__ void fill_band_table(uint8_t* tab, uint32_t lo, float s_act)
-{
-    const float q0 = bf16_to_f32(lo + (threadIdx.x & 127u)) / s_act;
-    for (int e = threadIdx.x; e < (int)kCodeBand; e += blockDim.x)
-        tab[1 + e] = f32_to_e4m3_sat(q0 * __uint_as_float((127u + (uint32_t)(e >> 7)) << 23));
-}
-
 template <int G>
 struct RmsLutShared {
     uint8_t tab[kCodeBand + 2];        // [0]: below the band, [1 + i]: band entry i, [kCodeBand + 1]: above
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(G * kRmsRowThreads) void k_quant_rmsnorm_lut(
     }
     const uint32_t lo = code_band_lo(s_act);
     const int lo1 = (int)lo - 1;                         // table index of magnitude a: clamp(a - lo1)
-    fill_band_table(sh.tab, lo, s_act);
+    fill_band_table(sh.tab, lo, s_act, threadIdx.x, blockDim.x);
     if (threadIdx.x == 0) sh.tab[0] = 0u, sh.tab[kCodeBand + 1] = 0x7eu;
     const bool gamma_ok = __syncthreads_and(g_fin);       // also orders the table before its first read
 
@@ -539,22 +539,18 @@ __device__ __forceinline__ void silu_mul_quant_tables(const uint4 (&g)[NP], cons
 // under s_act (65,536 bytes, 5120 of them by division).  It then streams a
 // contiguous share of the [M, I] pieces, NP per thread per step (kSiluLutThreads
 // apart, so each load instruction of a wave covers 1 KB), stepping the row and
-// column instead of dividing; with PF the next step's loads are issued before
-// this step's arithmetic.  total = M * I / 8 < 2^31.
+// column instead of dividing.  total = M * I / 8 < 2^31.
 constexpr int kSiluLutThreads = 1024;
 
+// Non-temporal: the activation is read once.
 __device__ __forceinline__ uint4 load_piece(const uint16_t* p)
 {
-#if FP8MM_SILU_NT
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     return make_uint4(r.x, r.y, r.z, r.w);
-#else
-    return *reinterpret_cast<const uint4*>(p);
-#endif
 }
 
-template <int NP, bool PF>
+template <int NP>
 __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
     const uint16_t* __restrict__ gate, int64_t ldg, const uint16_t* __restrict__ up, int64_t ldu, float s_act,
     uint8_t* __restrict__ xq, uint32_t nv, uint32_t total, int64_t I)
@@ -607,20 +603,8 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
             v_[p] -= v_[p] >= nv ? nv : 0u;
         }
     };
-    if (PF) load_step(i, m, v, g, u);
     for (;;) {
-        uint32_t mn[NP], vn[NP];
-        uint4 gn[NP], un[NP];
-        const uint32_t in = i + kStep;
-        const bool more = in < end;
-        if (PF) {
-#pragma unroll
-            for (int p = 0; p < NP; ++p) mn[p] = m[p], vn[p] = v[p];
-            advance(mn, vn);
-            load_step(more ? in : i, more ? mn : m, more ? vn : v, gn, un);
-        } else {
-            load_step(i, m, v, g, u);
-        }
+        load_step(i, m, v, g, u);
         uint2 o[NP];
         silu_mul_quant_tables<NP>(g, u, stab, ctab, o);
         // a piece past `end` was loaded from piece 0's address, so its codes are
@@ -631,14 +615,9 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
             const bool ok = i + (uint32_t)p * kSiluLutThreads < end;
             *reinterpret_cast<uint2*>(xq + (int64_t)(ok ? m[p] : m[0]) * I + (ok ? v[p] : v[0]) * 8) = o[p];
         }
-        if (!more) break;
-        i = in;
-        if (PF) {
-#pragma unroll
-            for (int p = 0; p < NP; ++p) m[p] = mn[p], v[p] = vn[p], g[p] = gn[p], u[p] = un[p];
-        } else {
-            advance(m, v);
-        }
+        i += kStep;
+        if (i >= end) break;
+        advance(m, v);
     }
 }
 
@@ -650,6 +629,8 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
 // the share is loaded from the thread's first piece and stores that piece's
 // codes there again.  total = M * K / 8 < 2^31.
 constexpr int kPlainLutThreads = 1024;
+static_assert(kPlainLutThreads % 128 == 0, "fill_band_table: one mantissa per thread across the binades");
+static_assert(kRmsLutGroups * kRmsRowThreads % 128 == 0, "fill_band_table: one mantissa per thread across the binades");
 
 template <int NP>
 __global__ __launch_bounds__(kPlainLutThreads) void k_quant_plain_lut(
@@ -659,7 +640,7 @@ __global__ __launch_bounds__(kPlainLutThreads) void k_quant_plain_lut(
     __shared__ uint8_t tab[kCodeBand + 3];
     const uint32_t lo = code_band_lo(s_act);
     const int lo1 = (int)lo - 1;
-    fill_band_table(tab, lo, s_act);
+    fill_band_table(tab, lo, s_act, threadIdx.x, blockDim.x);
     if (threadIdx.x == 0) tab[0] = 0u, tab[kCodeBand + 1] = 0x7eu, tab[kCodeBand + 2] = 0x7eu;
     __syncthreads();
     constexpr uint32_t kStep = (uint32_t)NP * kPlainLutThreads;
@@ -784,10 +765,10 @@ void launch_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float e
                   uint8_t* xq, int64_t M, int64_t K, hipStream_t stream)
 {
     const int64_t ppt = ((K >> 3) + kRmsRowThreads - 1) / kRmsRowThreads;   // 16-byte pieces per thread
-    if (gamma && M >= FP8MM_RMS_LUT_MIN_ROWS && M < ((int64_t)1 << 30) && K >= FP8MM_RMS_LUT_MIN_K && ppt <= 4 &&
+    if (gamma && M < ((int64_t)1 << 30) && K >= kRmsLutMinK && ppt <= 4 &&
         code_table_ok(s_act)) {
-        constexpr int G = FP8MM_RMS_LUT_GROUPS;
-        const int64_t want = (M + G - 1) / G, cap = (int64_t)num_cus() * FP8MM_RMS_LUT_BPC;
+        constexpr int G = kRmsLutGroups;
+        const int64_t want = (M + G - 1) / G, cap = (int64_t)num_cus() * kRmsLutPerCu;
         const dim3 grid((uint32_t)(want < cap ? want : cap)), block(G * kRmsRowThreads);
         if (ppt <= 1)
             hipLaunchKernelGGL((k_quant_rmsnorm_lut<1, G>), grid, block, 0, stream, x, ldx, gamma, eps, s_act, xq, M, K);
@@ -800,12 +781,12 @@ void launch_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float e
     } else if (gamma) {
         hipLaunchKernelGGL(k_quant_rmsnorm, dim3((uint32_t)M), dim3(kQuantThreads), 0, stream,
                            x, ldx, gamma, eps, s_act, xq, K);
-    } else if (M * (K >> 3) >= FP8MM_PLAIN_LUT_MIN_ELEMS / 8 && M * (K >> 3) < ((int64_t)1 << 31) &&
+    } else if (M * (K >> 3) >= kPlainLutMinElems / 8 && M * (K >> 3) < ((int64_t)1 << 31) &&
                code_table_ok(s_act)) {
         const int64_t total = M * (K >> 3);
-        hipLaunchKernelGGL((k_quant_plain_lut<FP8MM_PLAIN_LUT_NP>), dim3((uint32_t)num_cus() * FP8MM_PLAIN_LUT_BPC),
+        hipLaunchKernelGGL((k_quant_plain_lut<kPlainLutPieces>), dim3((uint32_t)num_cus() * kPlainLutPerCu),
                            dim3(kPlainLutThreads), 0, stream, x, ldx, s_act, xq, (uint32_t)(K >> 3), (uint32_t)total, K);
-    } else if (M * K <= FP8MM_PLAIN_HALF_MAX_ELEMS) {
+    } else if (M * K <= kPlainHalfMaxElems) {
         const int64_t blocks = (M * (K >> 2) + kQuantThreads - 1) / kQuantThreads;
         hipLaunchKernelGGL(k_quant_plain_half, dim3((uint32_t)(blocks < 1 ? 1 : blocks)), dim3(kQuantThreads), 0,
                            stream, x, ldx, s_act, xq, M, K);
@@ -851,13 +832,19 @@ void launch_quant_per_token(const uint16_t* x, int64_t ldx, const uint16_t* gamm
         hipLaunchKernelGGL(k_quant_per_token, grid, block, 0, stream, x, ldx, gamma, eps, xq, s_rows, K);
 }
 
+static bool silu_mul_uses_table(int64_t M, int64_t I, float s_act)
+{
+    const int64_t total = M * (I >> 3);
+    return total >= FP8MM_SILU_TABLE_MIN_ELEMS / 8 && total < ((int64_t)1 << 31) && code_table_ok(s_act);
+}
+
 void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, float s_act,
                            uint8_t* xq, int64_t M, int64_t I, hipStream_t stream)
 {
     const int64_t total = M * (I >> 3);
     if (silu_mul_uses_table(M, I, s_act)) {
-        const int64_t grid = (int64_t)num_cus() * FP8MM_SILU_LUT_BPC;
-        hipLaunchKernelGGL((k_silu_mul_quant_lut<FP8MM_SILU_NP, FP8MM_SILU_PF != 0>), dim3((uint32_t)grid),
+        const int64_t grid = (int64_t)num_cus() * kSiluLutPerCu;
+        hipLaunchKernelGGL((k_silu_mul_quant_lut<kSiluLutPieces>), dim3((uint32_t)grid),
                            dim3(kSiluLutThreads), 0, stream, gate, ldg,
                            up, ldu, s_act, xq, (uint32_t)(I >> 3), (uint32_t)total, I);
     } else {
@@ -866,11 +853,6 @@ void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up
     }
 }
 
-bool silu_mul_uses_table(int64_t M, int64_t I, float s_act)
-{
-    const int64_t total = M * (I >> 3);
-    return total >= FP8MM_SILU_TABLE_MIN_ELEMS / 8 && total < ((int64_t)1 << 31) && code_table_ok(s_act);
-}
 
 void launch_act_scale_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, int64_t M,
                                int64_t I, float* s_act, float* partial, hipStream_t stream)

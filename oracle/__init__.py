@@ -62,6 +62,7 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
     L.oracle_f64_to_bf16.restype = ctypes.c_uint16
     L.oracle_f32_to_bf16.argtypes = [F32]
+    L.oracle_f64_to_bf16_array.argtypes = [P, I64, P]
     L.oracle_f32_to_bf16.restype = ctypes.c_uint16
     L.oracle_quant_act.argtypes = [P, I64, I64, I64, F32, P]
     L.oracle_rmsnorm.argtypes = [P, I64, P, F32, I64, I64, P]
@@ -109,6 +110,14 @@ def e4m3_encode(t) -> np.ndarray:
 
 def f64_to_bf16(d: float) -> int:
     return int(lib().oracle_f64_to_bf16(float(d)))
+
+
+def f64_to_bf16_array(d: np.ndarray) -> np.ndarray:
+    """bf16 bits (RNE, one rounding) of every double of d."""
+    a = _c(d, np.float64)
+    out = np.empty(a.shape, np.uint16)
+    lib().oracle_f64_to_bf16_array(_ptr(a), a.size, _ptr(out))
+    return out
 
 
 def f32_to_bf16(f: float) -> int:
@@ -245,6 +254,36 @@ def scaled_mm(xq: np.ndarray, wq: np.ndarray, s_act: float, s_w: np.ndarray, wan
     out = np.empty((M, N), np.uint16)
     v = np.empty((M, N), np.float64) if want_v else None
     lib().oracle_scaled_mm(_ptr(a), _ptr(b), float(s_act), _ptr(sw), M, N, K, _ptr(out), N, _ptr(v))
+    return (out, v) if want_v else out
+
+
+# Largest K for which every partial sum of the accumulation is exact in fp64:
+# each E4M3 value is a multiple of 2^-9 with magnitude <= 448, so a product is
+# a multiple of 2^-18 of magnitude <= 448^2, and a sum of K of them needs fewer
+# than 53 bits while K * 448^2 * 2^18 < 2^53.
+EXACT_K_MAX = int(2 ** 35 // (448 * 448))
+
+
+def scaled_mm_blas(xq: np.ndarray, wq: np.ndarray, s_act: float, s_w: np.ndarray, want_v: bool = False):
+    """The GEMM of ``scaled_mm`` with its accumulation taken by a library fp64
+    matmul (numpy / BLAS) on the decoded operands: the same definition,
+    acc[m, n] = sum_k dec(x_q[m, k]) dec(w_q[n, k]), for large shapes.  The
+    matmul may block, reorder and fuse as it likes: while K <= EXACT_K_MAX
+    every product and every partial sum is exact in fp64, so any order gives
+    the one exact sum.  The epilogue is scaled_mm's, (acc * s_act) * s_w[n] in
+    fp64 with one rounding to bf16."""
+    a = _c(xq, np.uint8)
+    b = _c(wq, np.uint8)
+    sw = _c(s_w, np.float32)
+    M, K = a.shape
+    N, K2 = b.shape
+    assert K == K2 and sw.shape == (N,)
+    assert K <= EXACT_K_MAX, "fp64 accumulation is exact only up to EXACT_K_MAX"
+    tab = e4m3_table()
+    v = np.matmul(tab[a], tab[b].T)              # exact sums, [M, N] fp64
+    v *= np.float64(np.float32(s_act))
+    v *= sw.astype(np.float64)[None, :]
+    out = f64_to_bf16_array(v)
     return (out, v) if want_v else out
 
 

@@ -134,6 +134,13 @@ uint16_t oracle_f64_to_bf16(double d)
 
 uint16_t oracle_f32_to_bf16(float f) { return oracle_f64_to_bf16((double)f); }
 
+/* oracle_f64_to_bf16 applied to each of n doubles. */
+void oracle_f64_to_bf16_array(const double* d, int64_t n, uint16_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_bf16(d[i]);
+}
+
 /* ------------------------------------------------------ activation quant --- */
 
 /* Plain static per-tensor quant: x_q = satRNE_E4M3( fl32(f32(x) / s_act) ).

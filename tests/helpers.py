@@ -70,3 +70,16 @@ def assert_within_tolerance(gpu_bits: np.ndarray, ref_bits: np.ndarray, v: np.nd
 def ulps_apart(gpu_bits: np.ndarray, ref_bits: np.ndarray) -> np.ndarray:
     """Distance in bf16 units at the reference's scale."""
     return np.abs(bf16_f64(gpu_bits) - bf16_f64(ref_bits)) / ulp_bf16(bf16_f64(ref_bits))
+
+
+def assert_within_tolerance_rows(gpu_bits: np.ndarray, ref_bits: np.ndarray, v: np.ndarray, what: str = "",
+                                 block: int = 256):
+    """assert_within_tolerance over row blocks (large outputs, bounded memory)."""
+    worst = 0.0
+    for r0 in range(0, ref_bits.shape[0], block):
+        worst = max(worst, assert_within_tolerance(gpu_bits[r0:r0 + block], ref_bits[r0:r0 + block],
+                                                   v[r0:r0 + block], f"{what} rows {r0}+"))
+    return worst
+
+
+BF16_NAN = 0x7FC0

@@ -58,6 +58,15 @@ extern "C" int code_table_build(float s) {
 extern "C" void codes_from_table(const unsigned short* h, long n, unsigned char* o) {
     for (long i = 0; i < n; ++i) o[i] = g_codes[h[i]];
 }
+extern "C" long band_table_mismatches(float s, int nthreads) {
+    if (!fp8mm::code_table_ok(s)) return -1;
+    const unsigned lo = fp8mm::code_band_lo(s);
+    static unsigned char tab[fp8mm::kCodeBand + 2];
+    for (int t = 0; t < nthreads; ++t) fp8mm::fill_band_table(tab, lo, s, t, nthreads);
+    long bad = 0;
+    for (unsigned e = 0; e < fp8mm::kCodeBand; ++e) bad += tab[1 + e] != fp8mm::code_table_entry(lo + e, lo, s);
+    return bad;
+}
 extern "C" void silu_mul_codes(const unsigned short* g, const unsigned short* u, long n, float s, unsigned char* o) {
     code_table_build(s);
     for (long i = 0; i < n; ++i)
@@ -82,6 +91,8 @@ def dev():
     lib.silu_both.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p]
     lib.silu_mul_codes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_float, ctypes.c_void_p]
     lib.bf_sel_mismatches_all.restype = ctypes.c_long
+    lib.band_table_mismatches.argtypes = [ctypes.c_float, ctypes.c_int]
+    lib.band_table_mismatches.restype = ctypes.c_long
     lib.code_table_build.argtypes = [ctypes.c_float]
     lib.codes_from_table.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p]
     lib.silu_lut_build()
@@ -199,3 +210,20 @@ def test_branch_free_bf16_rounding_equals_the_plain_one_on_every_fp32(dev):
     """f32_to_bf16_rne_sel (the select form the table kernel uses) against
     f32_to_bf16_rne on all 2^32 fp32 patterns."""
     assert dev.bf_sel_mismatches_all() == 0
+
+
+def test_band_table_fill_equals_per_entry_division(dev):
+    """fill_band_table (one division per mantissa, scaled by powers of two
+    across the 20 binades, the work split over nthreads) against
+    code_table_entry (one division per entry) over 3000 log-uniform scales in
+    [2^-100, 2^100], both edges and the decode / prefill scales, for the
+    thread counts the kernels launch with."""
+    g = np.random.Generator(np.random.PCG64(1234))
+    scales = np.exp2(g.uniform(-100.0, 100.0, 3000)).astype(np.float32)
+    scales = np.concatenate([scales, np.float32([2.0 ** -100, 2.0 ** 100, 1.0, 1.0 / 448.0, 0.0137,
+                                                 np.nextafter(np.float32(2.0 ** -100), np.float32(1.0)),
+                                                 np.nextafter(np.float32(2.0 ** 100), np.float32(0.0))])])
+    for n in (128, 512, 1024):
+        for s in scales:
+            assert dev.band_table_mismatches(float(s), n) == 0, (float(s), n)
+    assert dev.band_table_mismatches(2.0 ** -101, 128) == -1

@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 import workloads as wl
-from helpers import (assert_within_tolerance, bf16_dev, f32_dev, host_u16, host_u8, u8_dev)
+from helpers import (assert_within_tolerance, assert_within_tolerance_rows, bf16_dev, f32_dev, host_u16,
+                     host_u8, u8_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -271,11 +272,22 @@ def test_decode_mlp_merged_gate_up_and_down(fp8, M):
     assert_within_tolerance(got2, ref2, v2, f"down M={M}")
 
 
-def test_prefill_sampled_rows(fp8):
-    """Prefill chunk, M = 6576 (large-M arm): the whole GEMM on the GPU from the
-    oracle's quantized inputs, checked on sampled rows (tile edges, the ragged
-    tail, random rows) against the oracle; the GPU's own quantization of the
-    same inputs is checked bit-exact on the side."""
+def _nan_filled(shape, device="cuda"):
+    """A bf16 output buffer full of NaN: an element the kernel never writes stays
+    NaN and fails the finiteness check of the tolerance test."""
+    import torch
+    return torch.full(shape, float("nan"), dtype=torch.bfloat16, device=device)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_all_elements(fp8):
+    """Prefill chunk, M = 6576 (large-M arm: 26 x 136 tiles of gate_up, about
+    14 rounds of the persistent grid, and 35 x 20 of down): every element of the
+    merged gate_up [6576, 34816] and of down [6576, 5120] against the oracle,
+    into NaN-filled outputs.  The GPU's own quantization of the same inputs
+    (fused RMSNorm quant, plain quant, weight quant) is checked bit-exact on the
+    side."""
+    import torch
     M, K, N = 6576, 5120, 34816
     x = wl.activation_bf16(5, M, K, outliers=False)
     g = wl.gamma_bf16(5, K)
@@ -290,23 +302,47 @@ def test_prefill_sampled_rows(fp8):
                                                                   sw.view(np.uint32))
     del wq_gpu, sw_gpu
     assert fp8.select(M, N, K) == 1
-    outs = fp8.scaled_mm_merged(u8_dev(xq), u8_dev(wq), s1, f32_dev(sw), [17408, 17408])
+    outs = [_nan_filled((M, N // 2)), _nan_filled((M, N // 2))]
+    fp8.scaled_mm_merged(u8_dev(xq), u8_dev(wq), s1, f32_dev(sw), [N // 2, N // 2], outs=outs)
     _sync()
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 4095, 4096, 6399, 6400, 6527, 6528, 6575],
-                                     np.random.Generator(np.random.PCG64(3)).integers(0, M, 19)]))
-    got = np.concatenate([host_u16(o) for o in outs], axis=1)[rows]
-    ref, v = oracle.scaled_mm(xq[rows], wq, s1, sw, want_v=True)
-    assert_within_tolerance(got, ref, v, "prefill gate_up")
+    got = np.concatenate([host_u16(o) for o in outs], axis=1)
+    del outs
+    torch.cuda.empty_cache()
+    ref, v = oracle.scaled_mm_blas(xq, wq, s1, sw, want_v=True)
+    assert_within_tolerance_rows(got, ref, v, "prefill gate_up")
+    del got, ref, v, wq
     # down projection K = 17408
     xd = wl.activation_bf16(5, M, 17408, outliers=False, tensor=wl.T_DOWN_X)
     s2 = oracle.act_scale(xd)
     xq2 = oracle.quant_act(xd, s2)
     assert np.array_equal(host_u8(fp8.quant(bf16_dev(xd), s2)), xq2)
     wq2, sw2 = oracle.quant_weight(wl.weight_f32(5, 5120, 17408, tensor=wl.T_DOWN_W))
-    out2 = fp8.scaled_mm(u8_dev(xq2), u8_dev(wq2), s2, f32_dev(sw2))
+    out2 = _nan_filled((M, 5120))
+    fp8.scaled_mm(u8_dev(xq2), u8_dev(wq2), s2, f32_dev(sw2), out=out2)
     _sync()
-    ref2, v2 = oracle.scaled_mm(xq2[rows], wq2, s2, sw2, want_v=True)
-    assert_within_tolerance(host_u16(out2)[rows], ref2, v2, "prefill down")
+    ref2, v2 = oracle.scaled_mm_blas(xq2, wq2, s2, sw2, want_v=True)
+    assert_within_tolerance_rows(host_u16(out2), ref2, v2, "prefill down")
+
+
+# Shapes with more large-M tiles than the 256 CUs, so every workgroup of the
+# persistent grid walks more than one tile, with ragged M and N edges:
+#   4000 x 8176: 16 x 32 = 512 tiles of 256x256 (the launcher picks them: 2
+#                rounds against 3 rounds of 672 tiles of 256x192);
+#   2300 x 8176: 12 x 32 = 384 tiles of 256x192 (picked: 2 rounds of
+#                three-quarter tiles against 2 full rounds of 288 tiles).
+@pytest.mark.parametrize("M,N,K", [(4000, 8176, 1024), (2300, 8176, 1024), (6576, 5120, 2048)])
+def test_large_m_multi_round_all_elements(fp8, M, N, K):
+    g = np.random.Generator(np.random.PCG64(M + N + K))
+    xq = wl.random_codes(9, M, K, m=M)
+    wq = wl.random_codes(9, N, K, tensor=wl.T_W, m=N)
+    s_act = float(np.float32(0.0071))
+    sw = (g.random(N) * 1e-3 + 1e-4).astype(np.float32)
+    assert fp8.select(M, N, K) == 1
+    out = _nan_filled((M, N))
+    fp8.scaled_mm(u8_dev(xq), u8_dev(wq), s_act, f32_dev(sw), out=out)
+    _sync()
+    ref, v = oracle.scaled_mm_blas(xq, wq, s_act, sw, want_v=True)
+    assert_within_tolerance_rows(host_u16(out), ref, v, f"{M}x{N}x{K}")
 
 
 def test_decode_step_sweep_64_layers(fp8):
@@ -387,7 +423,9 @@ def test_both_arms_agree_with_oracle(fp8, M):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 16), (3, 48, 48), (17, 32, 272), (33, 64, 400), (65, 80, 144),
-                                   (129, 144, 1040), (257, 272, 2064), (300, 1040, 17408)])
+                                   (129, 144, 1040), (257, 272, 2064), (300, 1040, 17408),
+                                   # K % 1024 == 0 but x_q + partials + ring past the LDS: the generic kernel
+                                   (1, 33168, 32768), (12, 10240, 32768)])
 def test_ragged_shapes_both_arms(fp8, M, N, K):
     g = np.random.Generator(np.random.PCG64(M * 1000 + N + K))
     xq = wl.random_codes(9, M, K, m=M)

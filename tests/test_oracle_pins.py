@@ -189,6 +189,44 @@ def test_gemm_exact_accumulation_closed_form():
     assert np.array_equal(oracle.exact_acc(xq[:, perm], wq[:, perm]), acc)
 
 
+def test_blas_gemm_is_the_plain_gemm():
+    """scaled_mm_blas (library fp64 matmul on decoded codes) against the plain
+    loop of scaled_mm, bit for bit in the bf16 output and the fp64 v: on the
+    tiny workload, on random codes at K = 17408 with rows of +-448 (the largest
+    partial sums the bound allows for), on the hand-worked product, and under a
+    consistent K permutation.  An fp32 matmul, a transposed operand or a dropped
+    scale fails it."""
+    x = wl.activation_bf16(1, 4, 256, outliers=False)
+    s_act = oracle.act_scale(x)
+    xq = oracle.quant_act(x, s_act)
+    wq, sw = oracle.quant_weight(wl.weight_f32(1, 384, 256))
+    a, va = oracle.scaled_mm(xq, wq, s_act, sw, want_v=True)
+    b, vb = oracle.scaled_mm_blas(xq, wq, s_act, sw, want_v=True)
+    assert np.array_equal(a, b) and np.array_equal(va.view(np.uint64), vb.view(np.uint64))
+    g = np.random.Generator(np.random.PCG64(77))
+    M, N, K = 5, 48, 17408
+    xq = wl.FINITE_CODE_VALUES[g.integers(0, 254, (M, K))]
+    wq = wl.FINITE_CODE_VALUES[g.integers(0, 254, (N, K))]
+    xq[0], wq[0], wq[1] = 0x7E, 0x7E, 0xFE           # sums of +-448^2 K
+    xq[1, ::2] = 0x01                                # the smallest subnormal against the largest values
+    sw = (g.random(N) * 1e-3 + 1e-5).astype(np.float32)
+    s_act = float(np.float32(0.0123))
+    a, va = oracle.scaled_mm(xq, wq, s_act, sw, want_v=True)
+    b, vb = oracle.scaled_mm_blas(xq, wq, s_act, sw, want_v=True)
+    assert np.array_equal(a, b) and np.array_equal(va.view(np.uint64), vb.view(np.uint64))
+    assert vb[0, 0] == 448.0 * 448.0 * K * np.float64(np.float32(s_act)) * np.float64(sw[0])
+    perm = g.permutation(K)
+    assert np.array_equal(oracle.scaled_mm_blas(xq[:, perm], wq[:, perm], s_act, sw), b)
+    t = _golden("tiny_product.json")
+    xq = np.array([[int(c, 16) for c in t["x_q"]]], np.uint8)
+    wq = np.array([[int(c, 16) for c in r] for r in t["W_q"]], np.uint8)
+    out = oracle.scaled_mm_blas(xq, wq, float.fromhex(t["s_act"]),
+                                np.array([float.fromhex(v) for v in t["s_w"]], np.float32))
+    assert [hex(v) for v in out[0]] == t["out_bf16"]
+    # the bound behind the exactness: K * 448^2 in units of 2^-18 below 2^53
+    assert oracle.EXACT_K_MAX * 448 * 448 * 2 ** 18 < 2 ** 53 <= (oracle.EXACT_K_MAX + 1) * 448 * 448 * 2 ** 18
+
+
 def test_invariants_scale_zero_identity_sign_merge():
     g = np.random.Generator(np.random.PCG64(11))
     M, N, K = 5, 48, 512
