@@ -28,7 +28,8 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH, ESCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_FLOATS = 65536
 SMALL_M_MAX = 64
 THRESHOLD_MIN = 16
 MAX_SHARDS = 8
@@ -67,6 +68,7 @@ _strerror = _decl("fp8mm_strerror", [_I32], ctypes.c_char_p)
 _quant_weight = _decl("fp8_quant_weight", [_P, _I64, _I64, _P, _P, _P])
 _act_scale_ws = _decl("fp8_act_scale_workspace_bytes", [_I64, _I64], _SZ)
 _act_scale = _decl("fp8_act_scale", [_P, _I64, _P, _F32, _I64, _I64, _P, _P, _SZ, _P])
+_act_scale_noalloc = _decl("fp8_act_scale_noalloc", [_P, _I64, _P, _F32, _I64, _I64, _P, _P])
 _silu_mul_quant = _decl("fp8_silu_mul_quant", [_P, _I64, _P, _I64, _F32, _P, _I64, _I64, _P])
 _act_scale_silu_mul = _decl("fp8_act_scale_silu_mul", [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _SZ, _P])
 _qw_tensor_ws = _decl("fp8_quant_weight_per_tensor_workspace_bytes", [_I64, _I64], _SZ)
@@ -160,6 +162,25 @@ def act_scale(x: torch.Tensor, gamma: Optional[torch.Tensor] = None, eps: float 
     _check(_act_scale(_ptr(x), ldx, _ptr(gamma), float(eps), M, K, _ptr(s), _ptr(ws), ws.numel(), _stream(x)),
            "fp8_act_scale")
     return s
+
+
+def act_scale_noalloc(x: torch.Tensor, gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """act_scale without a workspace: the library's static per-GPU scratch holds
+    the partial maxima (calls that overlap on one GPU race).  ``out`` (device
+    f32 [1]) lets a caller that cannot allocate pass its own result buffer."""
+    _need(x.is_cuda and x.dtype == torch.bfloat16, "x must be a bf16 CUDA tensor")
+    ldx = _row_major(x, "x")
+    M, K = x.shape
+    if gamma is not None:
+        _need(gamma.is_cuda and gamma.dtype == torch.bfloat16 and gamma.is_contiguous() and gamma.numel() == K,
+              "gamma must be a contiguous bf16 CUDA tensor of K elements")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _need(out.is_cuda and out.dtype == torch.float32 and out.numel() >= 1, "out must be a device f32 tensor")
+    _check(_act_scale_noalloc(_ptr(x), ldx, _ptr(gamma), float(eps), M, K, _ptr(out), _stream(x)),
+           "fp8_act_scale_noalloc")
+    return out
 
 
 def _gate_up(gate: torch.Tensor, up: torch.Tensor):

@@ -269,6 +269,7 @@ const char* fp8mm_strerror(int status)
     case FP8MM_EUNSUPPORTED: return "unsupported shape or alignment (K%16, N%16, ld%8, 16-byte pointers)";
     case FP8MM_EWORKSPACE: return "workspace too small";
     case FP8MM_ELAUNCH: return "HIP kernel launch failed";
+    case FP8MM_ESCRATCH: return "input needs more scratch than the allocation-free entry point's static array holds";
     default: return "unknown status";
     }
 }
@@ -359,6 +360,21 @@ int fp8_act_scale(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float e
     if (!workspace || workspace_bytes < fp8_act_scale_workspace_bytes(M, K)) return FP8MM_EWORKSPACE;
     if (!aligned16(workspace)) return FP8MM_EUNSUPPORTED;
     fp8mm::launch_act_scale(x, ldx, gamma, eps, M, K, s_act, static_cast<float*>(workspace), stream);
+    return launch_status();
+}
+
+int fp8_act_scale_noalloc(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, int64_t M, int64_t K,
+                          float* s_act, hipStream_t stream)
+{
+    if (!x || !s_act || M < 0 || K < 0 || ldx < K) return FP8MM_EINVAL;
+    if (gamma && !(std::isfinite(eps) && eps >= 0.0f)) return FP8MM_EINVAL;
+    if (K % 16 != 0 || ldx % 8 != 0 || !aligned16(x) || (gamma && !aligned16(gamma))) return FP8MM_EUNSUPPORTED;
+    if (gamma && M > (int64_t)0x7fffffff) return FP8MM_EUNSUPPORTED;
+    if (M == 0 || K == 0) return FP8MM_EINVAL;   // no tensor to calibrate on
+    if (fp8mm::act_scale_partials(M, K, gamma != nullptr) > (size_t)FP8MM_NOALLOC_SCRATCH_FLOATS) return FP8MM_ESCRATCH;
+    float* partial = nullptr;
+    if (fp8mm::noalloc_scratch(&partial) != hipSuccess || !partial) return FP8MM_ELAUNCH;
+    fp8mm::launch_act_scale(x, ldx, gamma, eps, M, K, s_act, partial, stream);
     return launch_status();
 }
 

@@ -32,6 +32,9 @@ void launch_act_scale(const uint16_t* x, int64_t ldx, const uint16_t* gamma, flo
                       int64_t M, int64_t K, float* s_act, float* partial, hipStream_t stream);
 void launch_quant_weight(const float* w, int64_t N, int64_t K, uint8_t* wq, float* s_w,
                          hipStream_t stream);
+// The current device's copy of the static scratch array of the allocation-free
+// calibration (FP8MM_NOALLOC_SCRATCH_FLOATS floats), looked up once per device.
+hipError_t noalloc_scratch(float** ptr);
 void launch_quant_per_token(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, uint8_t* xq,
                             float* s_rows, int64_t M, int64_t K, hipStream_t stream);
 void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up, int64_t ldu, float s_act,

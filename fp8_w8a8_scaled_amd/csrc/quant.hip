@@ -11,6 +11,8 @@
 // All kernels are memory-bound streaming passes: 16-byte bf16 loads, 8-byte
 // E4M3 stores; LDS holds block reductions and the lookup tables that replace
 // the per-element division and encode.
+#include <mutex>
+
 #include "act_quant.h"
 #include "act_tables.h"
 #include "device_common.h"
@@ -861,6 +863,35 @@ void launch_act_scale_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t
     hipLaunchKernelGGL(k_absmax_silu_mul, dim3((uint32_t)np), dim3(kQuantThreads), 0, stream, gate, ldg, up, ldu, M,
                        I, partial);
     hipLaunchKernelGGL(k_absmax_final, dim3(1), dim3(kQuantThreads), 0, stream, partial, np, s_act);
+}
+
+// Scratch of fp8_act_scale_noalloc: the partial maxima of k_absmax_plain /
+// k_absmax_rmsnorm, read by k_absmax_final.  Each GPU holds its own copy at its
+// own address; host code uses the address hipGetSymbolAddress returns for the
+// current device, never the array's name (a host-side stand-in).
+static __device__ __align__(256) float scratch[FP8MM_NOALLOC_SCRATCH_FLOATS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(float** ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = static_cast<float*>(p);
+    }
+    *ptr = g_scratch[dev];
+    return hipSuccess;
 }
 
 void launch_quant_weight(const float* w, int64_t N, int64_t K, uint8_t* wq, float* s_w, hipStream_t stream)

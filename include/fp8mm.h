@@ -27,8 +27,10 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless marked "host".  The caller owns every
- *     buffer (inputs, outputs, weights, scales, workspaces); the library keeps
- *     no device allocation and never calls hipMalloc/hipFree.
+ *     buffer (inputs, outputs, weights, scales, workspaces); the library never
+ *     calls hipMalloc/hipFree.  Its only device memory of its own is the fixed
+ *     static scratch array of fp8_act_scale_noalloc (FP8MM_NOALLOC_SCRATCH_FLOATS
+ *     floats per GPU, held until the process ends).
  *   - Every GPU call is asynchronous on `stream` (0 = the null stream), never
  *     synchronizes and returns an int status (enum below).  No C++ exception
  *     crosses the ABI.
@@ -65,7 +67,8 @@ enum fp8mm_status {
     FP8MM_EINVAL = -1,
     FP8MM_EUNSUPPORTED = -2,
     FP8MM_EWORKSPACE = -3,
-    FP8MM_ELAUNCH = -4
+    FP8MM_ELAUNCH = -4,
+    FP8MM_ESCRATCH = -5
 };
 
 /* Largest M the small-M (memory-bound) kernel serves; the threshold may not
@@ -312,6 +315,22 @@ int fp8_act_scale(const uint16_t* x, int64_t ldx,
                   const uint16_t* gamma, float eps,
                   int64_t M, int64_t K, float* s_act,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* fp8_act_scale without a workspace, for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same *s_act bits, with the partial
+ * maxima kept in a static device array of FP8MM_NOALLOC_SCRATCH_FLOATS floats
+ * (one copy per GPU, held until the process ends).  The first call on a device
+ * looks up that device's copy (hipGetSymbolAddress); no call allocates.
+ * The scratch needs fp8_act_scale_workspace_bytes(M, K) / 4 floats (at most
+ * 4096 without gamma, M with gamma); more returns FP8MM_ESCRATCH before any
+ * launch.  Every call on one GPU shares its array (each call writes all the
+ * partials it reads, nothing needs clearing): calls that overlap on one GPU,
+ * on different streams or host threads, race and must not be issued. */
+#define FP8MM_NOALLOC_SCRATCH_FLOATS 65536
+int fp8_act_scale_noalloc(const uint16_t* x, int64_t ldx,
+                          const uint16_t* gamma, float eps,
+                          int64_t M, int64_t K, float* s_act, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Merged projections whose shards carry per-tensor scales (the q/k/v shards
