@@ -79,6 +79,7 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_quant_weight_per_tensor.argtypes = [P, I64, I64, P, P]
     L.oracle_requant_max_scale.argtypes = [P, P, P, ctypes.c_int, I64, P, P]
     L.oracle_num_threads.restype = ctypes.c_int
+    L.oracle_set_num_threads.argtypes = [ctypes.c_int]
     return L
 
 
@@ -326,3 +327,8 @@ def exact_acc(xq: np.ndarray, wq: np.ndarray) -> np.ndarray:
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the oracle's loops (results do not depend on it)."""
+    lib().oracle_set_num_threads(int(n))

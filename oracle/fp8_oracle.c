@@ -421,6 +421,17 @@ void oracle_exact_acc(const unsigned char* xq, const unsigned char* wq,
         }
 }
 
+/* Threads of the OpenMP loops above (the CPU baseline times 1 and all). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
