@@ -12,6 +12,7 @@ import glob
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -19,7 +20,7 @@ LIB = os.path.join(HERE, "libfp8mm.so")
 ROOT = os.path.dirname(HERE)
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
@@ -33,12 +34,23 @@ def sources() -> list[str]:
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every source to an object in parallel (one hipcc per file), then
+    link the shared library."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *sources(), "-o", tmp]
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(objdir, os.path.basename(f) + ".o") for f in srcs]
+    cmds = [[hipcc, *HIPCC_FLAGS, "-c", f, "-o", o] for f, o in zip(srcs, objs)]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
+        for rc in ex.map(lambda c: subprocess.call(c), cmds):
+            if rc != 0:
+                raise subprocess.CalledProcessError(rc, "hipcc")
+    tmp = LIB + ".tmp"
+    subprocess.check_call([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

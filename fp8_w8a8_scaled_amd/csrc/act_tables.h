@@ -117,6 +117,70 @@ __device__ __host__ __forceinline__ void fill_band_table(uint8_t* tab, uint32_t 
     }
 }
 
+// The 8 E4M3 codes of 8 bf16 values (one 16-byte piece, words w0..w3, value i
+// in bits 16 (i % 2) of word i / 2) under the band table `tab` of the plain
+// static quant: entry 0 below the band (a signed zero), entries 1 ..
+// kCodeBand the band (filled by fill_band_table), kCodeBand + 1 and + 2 the
+// saturated code; a NaN keeps its sign (0x7F | sign).  lo1 = code_band_lo - 1.
+__device__ __forceinline__ uint2 quant8_band(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                             const uint8_t* tab, int lo1)
+{
+    const uint32_t w[4] = {w0, w1, w2, w3};
+    uint32_t o[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        uint32_t c = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t a = (w[2 * q + (e >> 1)] >> ((e & 1) * 16)) & 0x7fffu;
+            const uint32_t t = tab[min(max((int)a - lo1, 0), (int)kCodeBand + 1)];
+            c |= (a > 0x7f80u ? 0x7fu : t) << (8 * e);
+        }
+        // the four sign bits: bit 15 and bit 31 of each pair of values
+        o[q] = c | (__builtin_amdgcn_perm(w[2 * q + 1], w[2 * q], 0x07050301u) & 0x80808080u);
+    }
+    return make_uint2(o[0], o[1]);
+}
+
+// The 8 E4M3 codes of the RMSNorm output y_b = bf16(fl32(fl32(x r) gamma)) of
+// one piece (x words w0..w3, gamma as fp32 gf[0..7]) under the band table
+// (entry 0 below the band, kCodeBand + 1 saturated).  Valid when r and gamma
+// are finite: |x r| <= sqrt(K), so y_b is finite or +-inf, never NaN, and its
+// code depends on its magnitude bits and sign only.  lo1 = code_band_lo - 1.
+__device__ __forceinline__ uint2 rms_codes8_band(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, const float* gf,
+                                                 float r, const uint8_t* tab, int lo1)
+{
+    const uint32_t w[4] = {w0, w1, w2, w3};
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        h[i] = pack_bf16x2(bf16_to_f32(w[i] & 0xffffu) * r * gf[2 * i], bf16_to_f32(w[i] >> 16) * r * gf[2 * i + 1]);
+    uint32_t o[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        uint32_t c = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int a = (int)((h[2 * q + (e >> 1)] >> ((e & 1) * 16)) & 0x7fffu);
+            c |= (uint32_t)tab[min(max(a - lo1, 0), (int)kCodeBand + 1)] << (8 * e);
+        }
+        // the four sign bits: bit 15 and bit 31 of each packed pair
+        o[q] = c | (__builtin_amdgcn_perm(h[2 * q + 1], h[2 * q], 0x07050301u) & 0x80808080u);
+    }
+    return make_uint2(o[0], o[1]);
+}
+
+// Bytes of a plain-quant band table: entries 0 .. kCodeBand + 2, padded.
+constexpr int kBandTableBytes = ((int)kCodeBand + 3 + 15) & ~15;
+
+// Fill a whole band table (entries 0, 1 .. kCodeBand, kCodeBand + 1, + 2) for
+// s_act, the share of thread `tid` of `nthreads` (a multiple of 128).
+__device__ __forceinline__ void fill_plain_band_table(uint8_t* tab, float s_act, int tid, int nthreads)
+{
+    fill_band_table(tab, code_band_lo(s_act), s_act, tid, nthreads);
+    if (tid == 0) tab[0] = 0u, tab[kCodeBand + 1] = 0x7eu, tab[kCodeBand + 2] = 0x7eu;
+}
+
 // fp32 -> bf16 bits, round to nearest even, NaN -> quiet NaN with its sign,
 // written without branches (same results as f32_to_bf16_rne).
 __device__ __host__ __forceinline__ uint32_t f32_to_bf16_rne_sel(float f)

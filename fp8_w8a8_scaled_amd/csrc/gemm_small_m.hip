@@ -213,12 +213,13 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 // (or do not exist) and are not stored.  The shard is that of n0 (one lookup
 // for the tile: a tile starting at a multiple of 16 lies in one shard), or
 // with lane_shard that of each 4-row group (such a group never straddles two
-// shards: shard starts are multiples of 16).
+// shards: shard starts are multiples of 16).  m_off: the first output row of
+// the MFMA B tile (16 for the second of two).
 __device__ __forceinline__ void reduce_tile(const v4f* red, int stride, int slot, int W, int64_t n0, int64_t nend,
                                             float s_act, const float4 sw, const ShardTable& sh, int M, int lane,
-                                            bool lane_shard = false)
+                                            bool lane_shard = false, int m_off = 0)
 {
-    const int m = lane & 15;
+    const int m = m_off + (lane & 15);
     const int64_t n = n0 + 4 * (lane >> 4);
     if (m >= M || n >= nend) return;
     v4f s = red[slot];
@@ -479,6 +480,268 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
     }
 }
 
+// ---------------------------------------------------------------------------
+// k_gemm_small_m_rx: the ring kernel's weight stream with the x_q B fragments
+// in registers.
+//
+// A wave works on the same chunks (w, w + W, ...) of every weight tile, so it
+// multiplies every tile by the same B fragments.  XM_RES loads them once,
+// before the weight stream starts, and keeps them in registers (CPW chunks x
+// MT B tiles x 8 VGPRs), so all of the LDS holds weight rings and partial
+// sums.  Where they would not fit (more than 5 chunks per wave, e.g. K =
+// 17408), XM_STREAM loads each chunk's fragments from L2 (x_q is at most 32 x
+// K bytes) together with that chunk's weight, into a register ring as deep as
+// the weight ring.
+// MT = 1 or 2 B tiles (M <= 16 or M <= 32).  The chunk -> wave assignment (W
+// depends on K only), the MFMA sequence and the fixed-order reduction are
+// those of the other kernels of this file, so for a given M every kernel
+// choice gives the same bits.
+constexpr int XM_RES = 0, XM_STREAM = 1;
+
+// The A fragment (row r, logical pieces g and g + 4) of a staged weight chunk.
+// The pointer is restrict-qualified: this read never touches a slot with
+// loads in flight (the explicit waits order it), which keeps the compiler from
+// waiting for every outstanding direct-to-LDS load first.
+__device__ __forceinline__ v8i slot_afrag(const uint8_t* __restrict__ slot, int r, int g)
+{
+    const uint8_t* ws = slot + r * kChunk;
+    return pack(*reinterpret_cast<const uint4*>(ws + wswz(r, g) * 16),
+                *reinterpret_cast<const uint4*>(ws + wswz(r, g + 4) * 16));
+}
+
+// B fragments of chunk `chunk` for the MT B tiles (rows mt*16 + r, bytes 16g
+// and 64 + 16g of the chunk); zeros for rows past M or a chunk that does not
+// exist (an offset past the end of the buffer).
+template <int MT>
+__device__ __forceinline__ void load_bfrag(v8i (&b)[MT], __amdgpu_buffer_rsrc_t rx, int chunk, bool cok, int r, int g,
+                                           int M, int64_t K)
+{
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + r;
+        const uint32_t o = cok && m < M ? (uint32_t)((int64_t)m * K + chunk * kChunk + g * 16) : kOob;
+        const u32x4_t lo = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)o, 0, 0);
+        const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(o + 64), 0, 0);
+        b[mt] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+}
+
+// Workgroup barrier for LDS data written by the waves' own stores: wait for
+// this wave's LDS stores (lgkmcnt), then s_barrier; the empty asm statements
+// keep the compiler from moving memory accesses across it.  __syncthreads()
+// (and any LDS fence) would also wait for every outstanding direct-to-LDS
+// load, i.e. drain the weight ring.
+__device__ __forceinline__ void lds_barrier()
+{
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(FP8MM_SM_LGKM0);
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// Partial sums of a finished tile into LDS (restrict: the partials area is
+// never a target of the in-flight direct-to-LDS loads).
+__device__ __forceinline__ void put_partial(v4f* __restrict__ dst, v4f v) { *dst = v; }
+
+template <int S, int MT, int XM, int CPW, bool BAL, bool DEFER>
+__global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act, const float* __restrict__ s_w,
+    ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw)
+{
+    static_assert(XM == XM_STREAM || CPW > 0, "resident fragments need a compile-time chunk count");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int ntiles = (int)(N >> 4);
+    const int FR = BAL ? ntiles / G : 0;                // >= 1 with BAL: G <= N / 16
+    const int R = FR * G * 16, ngr = BAL ? ((int)N - R) >> 2 : 0;
+    const int q0 = 4 * (int)((int64_t)ngr * bid / G), q1 = 4 * (int)((int64_t)ngr * (bid + 1) / G);
+    const int my_tiles = BAL ? FR + (q1 > q0 ? 1 : 0) : (ntiles - bid + G - 1) / G;
+    __builtin_assume(my_tiles >= 1);                    // G <= ntiles
+    const int tiles_max = BAL ? FR + (ngr > 0 ? 1 : 0) : (ntiles + G - 1) / G;
+    auto tile_rows = [&](int u, int& rt, int& re) {     // rows [rt, re) of tile u
+        if (!BAL || u < FR) {
+            rt = (bid + u * G) * 16;
+            re = rt + 16;
+        } else {
+            rt = R + q0;
+            re = R + q1;
+        }
+    };
+    const int cw = XM == XM_STREAM ? cpw : CPW;         // chunks per wave and tile
+    // LDS: [partials] [W rings of S 2 KB slots].  partials: [2][W][MT][64], or
+    // with DEFER [tiles_max][W][MT][mp] (reduced once, at the end; for M <= 8
+    // only the 32 lanes holding columns m < 8).
+    const int mp = MT == 1 && M <= 8 ? 32 : 64;
+    const int pslot = mp == 64 ? lane : (lane >> 4) * 8 + (lane & 7);
+    v4f* red = reinterpret_cast<v4f*>(smem);
+    const int64_t red_elems = DEFER ? (int64_t)tiles_max * W * MT * mp : (int64_t)2 * W * MT * 64;
+    uint8_t* ring = reinterpret_cast<uint8_t*>(red + red_elems) + wave * S * 2048;
+    const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
+    // this lane's two rows of a weight chunk (instruction i: row 8i + lane/8), logical piece
+    const int lrow = lane >> 3;
+    const uint32_t pieceoff0 = (uint32_t)(lrow * K + wswz(lrow, lane & 7) * 16);
+    const uint32_t pieceoff1 = (uint32_t)((lrow + 8) * K + wswz(lrow + 8, lane & 7) * 16);
+    const int total = my_tiles * cw;                    // this wave's chunks, tile-major
+    // Issue cursor: sequence position iq, its tile iu and chunk index ic, and
+    // the rows [irt, ire) of tile iu.  prep() returns the weight offsets of the
+    // chunk at the cursor (past the buffer, i.e. zeros, where nothing is loaded)
+    // and its chunk, and advances; fire() issues the weight loads into a slot.
+    int iq = 0, iu = 0, ic = 0, irt, ire;
+    tile_rows(0, irt, ire);
+    struct Pend {
+        uint32_t w0, w1;
+        int chunk;
+        bool ok;
+    };
+    auto prep = [&]() {
+        const int chunk = wave + ic * W;
+        const bool ok = iq < total && chunk < nchunks;
+        const uint32_t t0 = (uint32_t)((int64_t)irt * K) + (uint32_t)chunk * kChunk;
+        Pend pd;
+        pd.w0 = ok && irt + lrow < ire ? t0 + pieceoff0 : kOob;
+        pd.w1 = ok && irt + lrow + 8 < ire ? t0 + pieceoff1 : kOob;
+        pd.chunk = chunk;
+        pd.ok = ok;
+        ++iq;
+        if (++ic == cw) {
+            ic = 0;
+            ++iu;
+            tile_rows(iu, irt, ire);
+        }
+        return pd;
+    };
+    auto fire = [&](const Pend& pd, int slot) {
+        uint8_t* sl = ring + slot * 2048;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)sl, 16, (int)pd.w0, 0, 0, kWeightCpol);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sl + 1024), 16, (int)pd.w1, 0, 0, kWeightCpol);
+    };
+    auto a_frag = [&](int slot) { return slot_afrag(ring + slot * 2048, r, g); };
+
+    constexpr int NB = XM == XM_STREAM ? S : CPW;
+    v8i bx[NB][MT];
+    const __amdgpu_buffer_rsrc_t rx = weight_rsrc(xq, (int64_t)M * K);
+    if constexpr (XM == XM_RES) {
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) load_bfrag<MT>(bx[c], rx, wave + c * W, wave + c * W < nchunks, r, g, M, K);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const Pend pd = prep();
+        fire(pd, s);
+        if constexpr (XM == XM_STREAM) load_bfrag<MT>(bx[s], rx, pd.chunk, pd.ok, r, g, M, K);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // weight scales of tile u for this lane's four rows (tile-by-tile reduction
+    // only; loaded in the loop iteration that uses them, so the compiler can
+    // count the loads issued after them instead of waiting for all)
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
+    auto tile_sw = [&](int t) {
+        int rt, re;
+        tile_rows(t, rt, re);
+        const int n = rt + 4 * g;
+        const uint32_t o = t < my_tiles && n < re ? (uint32_t)n * 4 : kOob;
+        return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, 0, 0);
+    };
+    v4f acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    // end of tile u: keep its partials (DEFER) or reduce it now
+    auto tile_done = [&](int u, const u32x4_t& swu) {
+        if constexpr (DEFER) {
+            if (mp == 64 || (lane & 15) < 8)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) put_partial(red + ((u * W + wave) * MT + mt) * mp + pslot, acc[mt]);
+        } else {
+            v4f* rb = red + (u & 1) * W * MT * 64;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) put_partial(rb + (wave * MT + mt) * 64 + lane, acc[mt]);
+            lds_barrier();
+            int rt, re;
+            tile_rows(u, rt, re);
+            if (wave == 0) {
+                const float4 sw4 = make_float4(__uint_as_float(swu[0]), __uint_as_float(swu[1]),
+                                               __uint_as_float(swu[2]), __uint_as_float(swu[3]));
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    reduce_tile(rb + mt * 64, MT * 64, lane, W, rt, re, s_act, sw4, sh, M, lane, BAL && u >= FR,
+                                16 * mt);
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    };
+
+    if constexpr (XM == XM_STREAM) {
+        // Whole ring cycles: positions past `total` load zeros and add zeros, and
+        // a tile past my_tiles is not kept (an early exit from the cycle would
+        // join the loop's back edge with other load counts, and the compiler
+        // would then wait for every outstanding load).  DEFER only.
+        static_assert(XM != XM_STREAM || DEFER, "streamed fragments keep the scales out of the loop");
+        int c = 0, u = 0;
+        for (int j0 = 0; j0 < total; j0 += S) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const Pend nx = prep();                  // chunk j + S, into this slot once it is read
+                // chunk j's weight and fragments landed: the S-1 chunks after it may be in flight
+                __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT((2 + 2 * MT) * (S - 1)));
+                const v8i A = a_frag(s);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, bx[s][mt], acc[mt], 0, 0, 0, 0, 0,
+                                                                              0);
+                __builtin_amdgcn_s_waitcnt(FP8MM_SM_LGKM0);   // the slot's reads have returned
+                fire(nx, s);
+                load_bfrag<MT>(bx[s], rx, nx.chunk, nx.ok, r, g, M, K);
+                if (++c == cw) {
+                    if (u < my_tiles) tile_done(u, u32x4_t{0u, 0u, 0u, 0u});
+                    c = 0;
+                    ++u;
+                }
+            }
+        }
+    } else {
+        int slot = 0;
+        for (int u = 0; u < my_tiles; ++u) {
+            u32x4_t swu{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) {
+                const Pend nx = prep();
+                // chunk landed: only the S-1 chunks after it may be in flight
+                __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT(2 * (S - 1)));
+                const v8i A = a_frag(slot);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, bx[c][mt], acc[mt], 0, 0, 0, 0, 0,
+                                                                              0);
+                __builtin_amdgcn_s_waitcnt(FP8MM_SM_LGKM0);
+                fire(nx, slot);
+                if (!DEFER && c == 0) swu = tile_sw(u);  // this tile's scales, behind its first refill
+                slot = slot + 1 == S ? 0 : slot + 1;
+            }
+            tile_done(u, swu);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);                      // no load outlives the workgroup
+    if constexpr (DEFER) {                               // one barrier, then every wave reduces
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < my_tiles * MT * mp; idx += blockDim.x) {
+            const int uu = idx / (MT * mp), rem = idx - uu * MT * mp;
+            const int mt = rem / mp, ps = rem - mt * mp;
+            const int l = mp == 64 ? ps : (ps >> 3) * 16 + (ps & 7);
+            int n0, re;
+            tile_rows(uu, n0, re);
+            if (n0 + 4 * (l >> 4) >= re) continue;       // another workgroup's rows
+            reduce_tile(red + (uu * W * MT + mt) * mp, MT * mp, ps, W, n0, re, s_act,
+                        *reinterpret_cast<const float4*>(s_w + n0 + 4 * (l >> 4)), sh, M, l, BAL, 16 * mt);
+        }
+    }
+}
+
 // Waves per workgroup: a function of K only (it fixes the summation order).
 int small_m_waves(int64_t K)
 {
@@ -568,11 +831,115 @@ bool try_ring(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_
     return false;
 }
 
+// Mode, ring depth and reduction of the register-fragment kernel for a shape
+// it takes: fragments resident for 4..5 chunks per wave, streamed beyond that
+// (M > 16 only: at M <= 16 the ring kernel's LDS streaming is faster); the
+// deepest ring that fits, deferred reduction preferred.
+struct RxPlan {
+    int xm, mt, cpw, S;
+    bool bal, defer;
+    size_t lds;
+    unsigned G, W;
+};
+
+bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p)
+{
+    if (M < 1 || M > 32 || K % kChunk != 0 || N * K >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31)) return false;
+    const int W = small_m_waves(K);
+    const int nchunks = (int)(K / kChunk);
+    const int cpw = (nchunks + W - 1) / W;
+    const bool res = cpw >= 4 && cpw <= kCpw;
+    if (cpw < 4 || (!res && M <= 16)) return false;      // short rows, or streamed at M <= 16: the ring kernel
+    const int64_t G = N / 16 < num_cus() ? N / 16 : num_cus();
+    const int64_t tiles_max = (N / 16 + G - 1) / G;
+    p->bal = 10 * tiles_max * G >= 13 * (N / 16);
+    p->xm = res ? XM_RES : XM_STREAM;
+    p->mt = M <= 16 ? 1 : 2;
+    p->cpw = cpw;
+    p->G = (unsigned)G;
+    p->W = (unsigned)W;
+    const size_t mp = p->mt == 1 && M <= 8 ? 32 : 64;
+    auto bytes = [&](int S, bool df) {
+        return (df ? (size_t)tiles_max * W * p->mt * mp : (size_t)2 * W * p->mt * 64) * sizeof(v4f) +
+               (size_t)W * S * 2048;
+    };
+    static const struct { int S; bool df; } order[] = {{6, true}, {6, false}, {4, true}, {4, false}, {3, true},
+                                                       {3, false}, {2, true}, {2, false}};
+    for (const auto& o : order)
+        if (bytes(o.S, o.df) <= 160 * 1024 && (o.df || p->xm != XM_STREAM)) {
+            p->S = o.S;
+            p->defer = o.df;
+            p->lds = bytes(o.S, o.df);
+            return true;
+        }
+    return false;
+}
+
+#define FP8MM_RX_ARGS p, xq, wq, s_act, s_w, sh, M, N, K, nchunks, stream
+template <int S, int MT, int XM, int CPW, bool BAL, bool DEFER>
+void launch_rx(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
+               const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, hipStream_t stream)
+{
+    static const bool attr = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_rx<S, MT, XM, CPW, BAL, DEFER>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        return true;
+    }();
+    (void)attr;
+    hipLaunchKernelGGL((k_gemm_small_m_rx<S, MT, XM, CPW, BAL, DEFER>), dim3(p.G), dim3(64 * p.W), p.lds, stream, xq,
+                       wq, s_act, s_w, sh, M, N, K, nchunks, p.cpw);
+}
+
+template <int MT, int XM, int CPW, bool BAL>
+void dispatch_rx_sd(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
+                    const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, hipStream_t stream)
+{
+    constexpr bool kStream = XM == XM_STREAM;   // streamed fragments: deferred reduction only
+    if (p.S == 6 && p.defer) launch_rx<6, MT, XM, CPW, BAL, true>(FP8MM_RX_ARGS);
+    else if (p.S == 4 && p.defer) launch_rx<4, MT, XM, CPW, BAL, true>(FP8MM_RX_ARGS);
+    else if (p.S == 3 && p.defer) launch_rx<3, MT, XM, CPW, BAL, true>(FP8MM_RX_ARGS);
+    else if (p.S == 2 && p.defer) launch_rx<2, MT, XM, CPW, BAL, true>(FP8MM_RX_ARGS);
+    else if constexpr (!kStream) {
+        if (p.S == 6) launch_rx<6, MT, XM, CPW, BAL, false>(FP8MM_RX_ARGS);
+        else if (p.S == 4) launch_rx<4, MT, XM, CPW, BAL, false>(FP8MM_RX_ARGS);
+        else if (p.S == 3) launch_rx<3, MT, XM, CPW, BAL, false>(FP8MM_RX_ARGS);
+        else launch_rx<2, MT, XM, CPW, BAL, false>(FP8MM_RX_ARGS);
+    }
+}
+
+template <int MT, int XM, int CPW>
+void dispatch_rx(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
+                 const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, hipStream_t stream)
+{
+    if (p.bal) dispatch_rx_sd<MT, XM, CPW, true>(FP8MM_RX_ARGS);
+    else dispatch_rx_sd<MT, XM, CPW, false>(FP8MM_RX_ARGS);
+}
+
+// Launch the register-fragment kernel if it takes this shape.
+bool try_rx(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh, int64_t M64,
+            int64_t N, int64_t K, hipStream_t stream)
+{
+    RxPlan p;
+    if (!plan_rx(M64, N, K, &p)) return false;
+    const int M = (int)M64, nchunks = (int)(K / kChunk);
+    if (p.xm == XM_RES) {
+        if (p.mt == 1 && p.cpw == 4) dispatch_rx<1, XM_RES, 4>(FP8MM_RX_ARGS);
+        else if (p.mt == 1) dispatch_rx<1, XM_RES, 5>(FP8MM_RX_ARGS);
+        else if (p.cpw == 4) dispatch_rx<2, XM_RES, 4>(FP8MM_RX_ARGS);
+        else dispatch_rx<2, XM_RES, 5>(FP8MM_RX_ARGS);
+    } else {
+        dispatch_rx<2, XM_STREAM, 0>(FP8MM_RX_ARGS);
+    }
+    return true;
+}
+#undef FP8MM_RX_ARGS
+
 void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
                          const ShardTable& shards, int64_t M, int64_t N, int64_t K, hipStream_t stream)
 {
     const int W = small_m_waves(K);
     const int nchunks = (int)((K + kChunk - 1) / kChunk);
+    if (try_rx(xq, wq, s_act, s_w, shards, M, N, K, stream)) return;
     if (try_ring(xq, wq, s_act, s_w, shards, M, N, K, W, nchunks, stream)) return;
     const int MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     const size_t lds = (size_t)W * MT * 64 * sizeof(v4f);

@@ -228,25 +228,8 @@ __global__ __launch_bounds__(G * kRmsRowThreads) void k_quant_rmsnorm_lut(
 #pragma unroll
             for (int p = 0; p < PPT; ++p) {
                 const int v = t + p * kRmsRowThreads;
-                const uint32_t w[4] = {in[p].x, in[p].y, in[p].z, in[p].w};
-                uint32_t h[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    h[i] = pack_bf16x2(bf16_to_f32(w[i] & 0xffffu) * r * gf[p][2 * i],
-                                       bf16_to_f32(w[i] >> 16) * r * gf[p][2 * i + 1]);
-                uint32_t o[2];
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    uint32_t c = 0u;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int a = (int)((h[2 * q + (e >> 1)] >> ((e & 1) * 16)) & 0x7fffu);
-                        c |= (uint32_t)sh.tab[min(max(a - lo1, 0), (int)kCodeBand + 1)] << (8 * e);
-                    }
-                    // the four sign bits: bit 15 and bit 31 of each packed pair
-                    o[q] = c | (__builtin_amdgcn_perm(h[2 * q + 1], h[2 * q], 0x07050301u) & 0x80808080u);
-                }
-                if (v < nv) *reinterpret_cast<uint2*>(out + (int64_t)v * 8) = make_uint2(o[0], o[1]);
+                const uint2 o = rms_codes8_band(in[p].x, in[p].y, in[p].z, in[p].w, gf[p], r, sh.tab, lo1);
+                if (v < nv) *reinterpret_cast<uint2*>(out + (int64_t)v * 8) = o;
             }
         } else {
 #pragma unroll
@@ -639,11 +622,9 @@ __global__ __launch_bounds__(kPlainLutThreads) void k_quant_plain_lut(
     const uint16_t* __restrict__ x, int64_t ldx, float s_act, uint8_t* __restrict__ xq, uint32_t nv,
     uint32_t total, int64_t K)
 {
-    __shared__ uint8_t tab[kCodeBand + 3];
-    const uint32_t lo = code_band_lo(s_act);
-    const int lo1 = (int)lo - 1;
-    fill_band_table(tab, lo, s_act, threadIdx.x, blockDim.x);
-    if (threadIdx.x == 0) tab[0] = 0u, tab[kCodeBand + 1] = 0x7eu, tab[kCodeBand + 2] = 0x7eu;
+    __shared__ uint8_t tab[kBandTableBytes];
+    const int lo1 = (int)code_band_lo(s_act) - 1;
+    fill_plain_band_table(tab, s_act, threadIdx.x, blockDim.x);
     __syncthreads();
     constexpr uint32_t kStep = (uint32_t)NP * kPlainLutThreads;
     const uint32_t per = ((total + gridDim.x - 1) / gridDim.x + kStep - 1) / kStep * kStep;
@@ -672,23 +653,9 @@ __global__ __launch_bounds__(kPlainLutThreads) void k_quant_plain_lut(
             in[p] = make_uint4(r.x, r.y, r.z, r.w);
         }
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const uint32_t w[4] = {in[p].x, in[p].y, in[p].z, in[p].w};
-            uint32_t o[2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                uint32_t c = 0u;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t a = (w[2 * q + (e >> 1)] >> ((e & 1) * 16)) & 0x7fffu;
-                    const uint32_t t = tab[min(max((int)a - lo1, 0), (int)kCodeBand + 1)];
-                    c |= (a > 0x7f80u ? 0x7fu : t) << (8 * e);
-                }
-                // the four sign bits: bit 15 and bit 31 of each pair of values
-                o[q] = c | (__builtin_amdgcn_perm(w[2 * q + 1], w[2 * q], 0x07050301u) & 0x80808080u);
-            }
-            *reinterpret_cast<uint2*>(xq + (int64_t)mm[p] * K + vv[p] * 8) = make_uint2(o[0], o[1]);
-        }
+        for (int p = 0; p < NP; ++p)
+            *reinterpret_cast<uint2*>(xq + (int64_t)mm[p] * K + vv[p] * 8) =
+                quant8_band(in[p].x, in[p].y, in[p].z, in[p].w, tab, lo1);
         i += kStep;
         if (i >= end) break;
 #pragma unroll

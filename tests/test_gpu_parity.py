@@ -424,7 +424,7 @@ def test_both_arms_agree_with_oracle(fp8, M):
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 16), (3, 48, 48), (17, 32, 272), (33, 64, 400), (65, 80, 144),
                                    (129, 144, 1040), (257, 272, 2064), (300, 1040, 17408),
-                                   # K % 1024 == 0 but x_q + partials + ring past the LDS: the generic kernel
+                                   # K % 1024 == 0 but the ring kernel's LDS plan does not fit: the generic kernel
                                    (1, 33168, 32768), (12, 10240, 32768)])
 def test_ragged_shapes_both_arms(fp8, M, N, K):
     g = np.random.Generator(np.random.PCG64(M * 1000 + N + K))
