@@ -76,6 +76,7 @@ def _args():
     p.add_argument("--summarize-pmc", metavar="DIR")
     p.add_argument("--summarize-mfma", metavar="DIR")
     p.add_argument("--cpu-table", metavar="NAME", help="time the oracle on every workload -> profiles/NAME.md")
+    p.add_argument("--sweep-threshold", metavar="NAME", help="time both GEMM arms over M -> profiles/NAME.md (GPU)")
     p.add_argument("--pmc-driver", choices=["decode", "prefill", "prefill_f32", "prefill_mfma"],
                    help="run a known-size copy, then a few launches of one GEMM (for rocprofv3 --pmc)")
     p.add_argument("--meta-out", metavar="DIR")
@@ -587,6 +588,47 @@ def bench_sweep(fp8, layers, M, steps, warmup, wid=4):
     return res
 
 
+def sweep_threshold(fp8, name, cmd, steps=40):
+    """Both GEMM arms (forced) at M = 1 .. 128 on the decode-MLP shapes (gate_up
+    34816 x 5120, down 5120 x 17408), weights rotated past the Infinity Cache,
+    median of 10 graph replays; writes profiles/NAME.md with the crossover."""
+    import torch
+    import workloads as wl
+    shapes = (("gate_up", 34816, 5120), ("down", 5120, 17408))
+    Ms = (1, 2, 4, 8, 16, 24, 32, 40, 48, 64, 96, 128)
+    rows = []
+    for nm, N, K in shapes:
+        wq, sw = fp8.quant_weight(f32_dev(wl.weight_f32(3, N, K)))
+        copies = max(2, -(-2 * LLC_BYTES // (N * K)) + 1)
+        ws = [wq] + [wq.clone() for _ in range(copies - 1)]
+        for M in Ms:
+            xq = fp8.quant(bf16_dev(wl.activation_bf16(3, M, K, outliers=True)), 0.05)
+            out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            t = {}
+            for arm in (0, 1):
+                if arm == 0 and M > fp8.SMALL_M_MAX:
+                    t[arm] = None
+                    continue
+                t[arm] = timed(lambda i: fp8.scaled_mm(xq, ws[i % copies], 0.05, sw, out=out, arm=arm), steps, 3)[
+                    "median_ms"] * 1e3
+            rows.append((nm, M, N, K, t[0], t[1]))
+            print(f"threshold sweep {nm} M={M}: small {t[0]} large {t[1]}", flush=True)
+        del ws
+        torch.cuda.empty_cache()
+    lines = [f"# {name}", "", "Both arms of the dispatcher, forced (`fp8_scaled_mm_arm`), on the decode-MLP shapes; "
+             "weights rotated past the Infinity Cache; median of 10 replays of a graph of "
+             f"{steps} launches, microseconds per launch.", "", f"Command: `{cmd}`", "",
+             f"kernel_sources_sha256_16: {kernel_sources_hash()}", "",
+             "| GEMM | M | small-M arm us | large-M arm us | faster |", "|---|---|---|---|---|"]
+    for nm, M, N, K, a, b in rows:
+        faster = "small" if a is not None and a <= b else "large"
+        lines.append(f"| {nm} {N}x{K} | {M} | {'-' if a is None else f'{a:.2f}'} | {b:.2f} | {faster} |")
+    out = os.path.join(PROFILES, f"{name}.md")
+    os.makedirs(PROFILES, exist_ok=True)
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out, flush=True)
+
+
 def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -982,6 +1024,8 @@ def main():
     torch.cuda.set_device(0)
     if a.pmc_driver:
         return pmc_driver(fp8, a.pmc_driver, a.meta_out)
+    if a.sweep_threshold:
+        return sweep_threshold(fp8, a.sweep_threshold, a.cmd)
     decode = {M: bench_decode(fp8, M, a.steps, a.warmup) for M in sorted(set(wl.DECODE_PROJ.Ms) | {a.M})}
     head = decode[a.M]
     gemm_bytes = head["algorithmic_bytes_per_gemm"]

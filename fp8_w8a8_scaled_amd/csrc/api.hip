@@ -16,7 +16,9 @@
 
 namespace {
 
-// Default threshold: the largest M served by the small-M arm.
+// Default threshold: the largest M served by the small-M arm.  Measured on
+// MI355X for the decode-MLP gate_up (34816 x 5120): the small-M arm takes 37 us
+// at M = 32 against 65 us for the large-M arm, and 81 us at M = 40 against 66.
 constexpr int64_t kDefaultThreshold = 32;
 
 int64_t initial_threshold()
