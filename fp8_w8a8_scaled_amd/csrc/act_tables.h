@@ -20,42 +20,45 @@ __device__ __host__ __forceinline__ float silu_f64(float g)
     return (float)(d / (1.0 + exp(-d)));
 }
 
-// silu_f64 of every bf16 gate as s = fma(g, m, t) with the pair (m, t) read
-// from a table.  Outside a band of magnitudes s is exact in closed form:
+// silu_f64 of every bf16 gate as s = fma(g, m, t).  Outside a band of
+// magnitudes s is exact in closed form:
 //   |g| < 2^-25           s = g / 2  (g^2/4 is below half an fp32 ulp of g/2)
 //   g >= 109, +inf, +NaN  s = g      (exp(-g) < 2^-157)
 //   g <= -109, -inf, -NaN s = g * 0  (-0: |g| e^g is below half the least fp32
 //                                     subnormal; -inf / inf and NaN give NaN)
-// so the table holds, per sign, a below-band entry (0.5, -0), the band entries
-// (0, silu_f64(g)) for magnitudes [2^-25, 109) (bf16 patterns 0x3300 ..
-// 0x42D9), and an above-band entry ((1 or 0), -0).  fma(g, 0, t) = t exactly
-// (no band value is zero) and fma(g, m, -0) = g * m exactly.
+// so only the band entries silu_f64(g), for magnitudes [2^-25, 109) (bf16
+// patterns 0x3300 .. 0x42D9) of both signs, come from a table (t, with m = 0);
+// outside it t = -0 and m = 0.5 below the band, 1 above it for g > 0 and 0
+// above it for g < 0.  fma(g, 0, t) = t exactly (no band value is zero) and
+// fma(g, m, -0) = g * m exactly.
 constexpr uint32_t kSiluLo = 0x3300u, kSiluBand = 0x42DAu - 0x3300u;
-constexpr int kSiluHalf = (int)kSiluBand + 2;
-constexpr int kSiluTableSize = 2 * kSiluHalf;       // (m, t) pairs
+constexpr int kSiluTableSize = 2 * (int)kSiluBand;  // t values: positive band, then negative
 
-__device__ __host__ __forceinline__ float2 silu_table_entry(int j)
+__device__ __host__ __forceinline__ float silu_table_entry(int j)
 {
-    const uint32_t neg = j >= kSiluHalf ? 1u : 0u;
-    const int k = j - (int)neg * kSiluHalf;
-    if (k == 0) return make_float2(0.5f, -0.0f);
-    if (k == kSiluHalf - 1) return make_float2(neg ? 0.0f : 1.0f, -0.0f);
-    return make_float2(0.0f, silu_f64(bf16_to_f32((neg << 15) | (kSiluLo + (uint32_t)k - 1u))));
+    const uint32_t neg = j >= (int)kSiluBand ? 1u : 0u;
+    return silu_f64(bf16_to_f32((neg << 15) | (kSiluLo + (uint32_t)j - neg * kSiluBand)));
 }
 
+// Table index of gate bits b (clamped into the band; out-of-band gates do not
+// use the value read there).
 __device__ __host__ __forceinline__ uint32_t silu_table_index(uint32_t b)
 {
     const int d = (int)(b & 0x7fffu) - (int)kSiluLo;
-    const int k = d < -1 ? -1 : (d > (int)kSiluBand ? (int)kSiluBand : d);      // a med3
-    return (uint32_t)(k + 1) + (b >> 15) * (uint32_t)kSiluHalf;
+    const int k = d < 0 ? 0 : (d >= (int)kSiluBand ? (int)kSiluBand - 1 : d);   // a med3
+    return (uint32_t)k + (b >> 15) * kSiluBand;
 }
 
-__device__ __host__ __forceinline__ float silu_finish(uint32_t b, float2 mt)
+__device__ __host__ __forceinline__ float silu_finish(uint32_t b, float t_band)
 {
-    return __builtin_fmaf(bf16_to_f32(b), mt.x, mt.y);
+    const int d = (int)(b & 0x7fffu) - (int)kSiluLo;
+    const bool below = d < 0, above = d >= (int)kSiluBand;
+    const float m = below ? 0.5f : (above ? ((b >> 15) ? 0.0f : 1.0f) : 0.0f);
+    const float t = below || above ? -0.0f : t_band;
+    return __builtin_fmaf(bf16_to_f32(b), m, t);
 }
 
-__device__ __host__ __forceinline__ float silu_from_table(uint32_t b, const float2* tab)
+__device__ __host__ __forceinline__ float silu_from_table(uint32_t b, const float* tab)
 {
     return silu_finish(b, tab[silu_table_index(b)]);
 }

@@ -26,7 +26,7 @@ constexpr int kQuantThreads = kRmsRowThreads;
 
 // Launch choices of the table-based kernels (measured on MI355X; the bytes do
 // not depend on them).
-constexpr int kSiluLutPerCu = 1;                  // SiLU*mul quant: workgroups per CU
+constexpr int kSiluLutPerCu = 2;                  // SiLU*mul quant: workgroups per CU
 constexpr int kSiluLutPieces = 2;                 // ... 16-byte pieces per thread and step
 constexpr int64_t kPlainLutMinElems = 1LL << 20;  // plain quant: table path from this many elements
 constexpr int kPlainLutPerCu = 2;
@@ -481,15 +481,17 @@ __global__ __launch_bounds__(kQuantThreads) void k_silu_mul_quant(
 }
 
 // Table path for NP 16-byte pieces of gate and up: every SiLU table read is
-// issued before any is used, then every code table read, so one LDS latency
-// covers 8 * NP values; nothing branches.
+// issued before any is used, then the codes of the bf16 products come from the
+// band table of the plain quant (quant8_band: the codes of every bf16 value
+// under s_act, a NaN keeping its sign); nothing branches.
 template <int NP>
-__device__ __forceinline__ void silu_mul_quant_tables(const uint4 (&g)[NP], const uint4 (&u)[NP], const float2* stab,
-                                                      const uint8_t* ctab, uint2 (&out)[NP])
+__device__ __forceinline__ void silu_mul_quant_tables(const uint4 (&g)[NP], const uint4 (&u)[NP],
+                                                      const float* __restrict__ stab,
+                                                      const uint8_t* __restrict__ ctab, int lo1, uint2 (&out)[NP])
 {
     constexpr int E = 8 * NP;
-    uint32_t gb[E], hb[E], c[E];
-    float2 mt[E];
+    uint32_t gb[E], hb[E];
+    float t[E];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const uint32_t w[4] = {g[p].x, g[p].y, g[p].z, g[p].w};
@@ -497,7 +499,7 @@ __device__ __forceinline__ void silu_mul_quant_tables(const uint4 (&g)[NP], cons
         for (int i = 0; i < 8; ++i) gb[8 * p + i] = (w[i >> 1] >> ((i & 1) * 16)) & 0xffffu;
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) mt[e] = stab[silu_table_index(gb[e])];
+    for (int e = 0; e < E; ++e) t[e] = stab[silu_table_index(gb[e])];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const uint32_t w[4] = {u[p].x, u[p].y, u[p].z, u[p].w};
@@ -505,23 +507,19 @@ __device__ __forceinline__ void silu_mul_quant_tables(const uint4 (&g)[NP], cons
         for (int i = 0; i < 8; ++i) {
             const int e = 8 * p + i;
             const float uv = bf16_to_f32((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
-            hb[e] = f32_to_bf16_cvt(silu_finish(gb[e], mt[e]) * uv);
+            hb[e] = f32_to_bf16_cvt(silu_finish(gb[e], t[e]) * uv);
         }
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) c[e] = ctab[hb[e]];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        uint32_t o[2] = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i >> 2] |= c[8 * p + i] << ((i & 3) * 8);
-        out[p] = make_uint2(o[0], o[1]);
-    }
+    for (int p = 0; p < NP; ++p)
+        out[p] = quant8_band(hb[8 * p] | (hb[8 * p + 1] << 16), hb[8 * p + 2] | (hb[8 * p + 3] << 16),
+                             hb[8 * p + 4] | (hb[8 * p + 5] << 16), hb[8 * p + 6] | (hb[8 * p + 7] << 16), ctab, lo1);
 }
 
 // Many rows (prefill).  Each workgroup first fills two LDS tables: the SiLU
-// (m, t) pairs (8116 fp64 evaluations) and the E4M3 code of every bf16 value
-// under s_act (65,536 bytes, 5120 of them by division).  It then streams a
+// values of the band gates (8116 fp64 evaluations, 32 KB) and the band code
+// table of the plain quant under s_act (2.5 KB, one division per mantissa),
+// small enough for two 1024-thread workgroups per CU.  It then streams a
 // contiguous share of the [M, I] pieces, NP per thread per step (kSiluLutThreads
 // apart, so each load instruction of a wave covers 1 KB), stepping the row and
 // column instead of dividing.  total = M * I / 8 < 2^31.
@@ -540,18 +538,12 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
     const uint16_t* __restrict__ gate, int64_t ldg, const uint16_t* __restrict__ up, int64_t ldu, float s_act,
     uint8_t* __restrict__ xq, uint32_t nv, uint32_t total, int64_t I)
 {
-    __shared__ float2 stab[kSiluTableSize];
-    __shared__ uint32_t ctab4[16384];
-    const uint32_t lo = code_band_lo(s_act);
+    __shared__ float stab[kSiluTableSize];
+    __shared__ uint8_t ctab[kBandTableBytes];
     for (int j = threadIdx.x; j < kSiluTableSize; j += blockDim.x) stab[j] = silu_table_entry(j);
-    for (int j = threadIdx.x; j < 16384; j += blockDim.x) {
-        uint32_t w = 0u;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) w |= code_table_entry(4u * j + k, lo, s_act) << (8 * k);
-        ctab4[j] = w;
-    }
+    fill_plain_band_table(ctab, s_act, threadIdx.x, blockDim.x);
+    const int lo1 = (int)code_band_lo(s_act) - 1;
     __syncthreads();
-    const uint8_t* ctab = reinterpret_cast<const uint8_t*>(ctab4);
     // this workgroup's pieces: [begin, end), a multiple of kStep long
     constexpr uint32_t kStep = (uint32_t)NP * kSiluLutThreads;
     const uint32_t per = ((total + gridDim.x - 1) / gridDim.x + kStep - 1) / kStep * kStep;
@@ -591,7 +583,7 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
     for (;;) {
         load_step(i, m, v, g, u);
         uint2 o[NP];
-        silu_mul_quant_tables<NP>(g, u, stab, ctab, o);
+        silu_mul_quant_tables<NP>(g, u, stab, ctab, lo1, o);
         // a piece past `end` was loaded from piece 0's address, so its codes are
         // piece 0's: it stores them there again instead of branching (a branch
         // lets the compiler sink that piece's loads behind the other's store)
@@ -614,7 +606,8 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
 // the share is loaded from the thread's first piece and stores that piece's
 // codes there again.  total = M * K / 8 < 2^31.
 constexpr int kPlainLutThreads = 1024;
-static_assert(kPlainLutThreads % 128 == 0, "fill_band_table: one mantissa per thread across the binades");
+static_assert(kPlainLutThreads % 128 == 0 && kSiluLutThreads % 128 == 0,
+              "fill_band_table: one mantissa per thread across the binades");
 static_assert(kRmsLutGroups * kRmsRowThreads % 128 == 0, "fill_band_table: one mantissa per thread across the binades");
 
 template <int NP>

@@ -37,7 +37,7 @@ extern "C" long bf_sel_mismatches_all(void) {
     }
     return bad;
 }
-static float2 g_stab[fp8mm::kSiluTableSize];
+static float g_stab[fp8mm::kSiluTableSize];
 extern "C" int silu_lut_build(void) {
     for (int j = 0; j < fp8mm::kSiluTableSize; ++j) g_stab[j] = fp8mm::silu_table_entry(j);
     return fp8mm::kSiluTableSize;
