@@ -442,9 +442,10 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
             const int nl = (tid & 63) * 4;
             const int64_t n = n0 + nl;
             if (n < N) {
-                const int si = shard_of(sh, n);
-                float* col = static_cast<float*>(sh.out[si]) + (n - sh.start[si]);
-                const int64_t ldo = sh.ldo[si];
+                void* o;
+                int64_t ldo, st;
+                shard_fields(sh, n, o, ldo, st);
+                float* col = static_cast<float*>(o) + (n - st);
                 // rows ml = threadIdx/64 + 4 r: four LDS reads, then their stores
                 // (rows past M are read but not stored)
 #pragma unroll
@@ -491,9 +492,10 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
         const int nl = (tid & 31) * 8;
         const int64_t n = n0 + nl;
         if (n < N) {
-            const int si = shard_of(sh, n);
-            uint16_t* col = static_cast<uint16_t*>(sh.out[si]) + (n - sh.start[si]);
-            const int64_t ldo = sh.ldo[si];
+            void* o;
+            int64_t ldo, st;
+            shard_fields(sh, n, o, ldo, st);
+            uint16_t* col = static_cast<uint16_t*>(o) + (n - st);
             // rows ml = threadIdx/32 + 8 r: four LDS reads, then their stores
             // (rows past M are read but not stored)
 #pragma unroll

@@ -19,12 +19,15 @@
 //  * the W per-wave partial sums are reduced in LDS in a fixed order (no
 //    atomics, no workspace), then the scale epilogue and the store happen in
 //    registers.
-// Two kernels share that work split, so they give the same bits:
-//  * k_gemm_small_m_ring (M <= 16, K % 1024 == 0, every decode shape):
-//    persistent, one workgroup per CU walking its weight tiles; each wave
-//    streams its chunks with whole-line direct-to-LDS loads into a private
-//    ring of LDS slots, x_q staged in LDS once (or streamed with each chunk
-//    when it does not fit);
+// Three kernels share that work split, so they give the same bits:
+//  * k_gemm_small_m_rx (M <= 32, K % 128 == 0 with 4-5 chunks per wave, and
+//    M 17-32 beyond): persistent, one workgroup per CU walking its weight
+//    tiles; each wave streams its weight chunks with whole-line direct-to-LDS
+//    loads into a private ring of LDS slots and keeps its x_q B fragments in
+//    registers (loaded once, or with each chunk);
+//  * k_gemm_small_m_ring (M <= 16, K % 1024 == 0, the longer rows): the same
+//    stream, with x_q staged in LDS once (or streamed with each chunk when it
+//    does not fit);
 //  * k_gemm_small_m (anything else up to M = 64): one workgroup per tile, the
 //    fragments loaded straight into registers.
 // W and the chunk assignment depend on K only, so every column's summation
@@ -228,11 +231,20 @@ __device__ __forceinline__ void reduce_tile(const v4f* red, int stride, int slot
         s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
     }
     const float sa = row_scale(sh, m, s_act);
-    store_out4(sh, shard_of(sh, lane_shard ? n : n0), m, n, (s.x * sa) * sw.x, (s.y * sa) * sw.y, (s.z * sa) * sw.z,
-               (s.w * sa) * sw.w);
+    store_out4_any(sh, lane_shard ? n : n0, m, n, (s.x * sa) * sw.x, (s.y * sa) * sw.y, (s.z * sa) * sw.z,
+                   (s.w * sa) * sw.w);
 }
 
 __device__ __forceinline__ int wswz(int row, int piece) { return piece ^ ((row >> 1) & 7); }
+
+// The weight scales of rows n..n+3 through the buffer resource of s_w (a
+// buffer load, which the compiler cannot fold with an LDS read of the same
+// values into one flat load).
+__device__ __forceinline__ float4 tile_scales(__amdgpu_buffer_rsrc_t rs, int n)
+{
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, n * 4, 0, 0);
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
 
 // Chunk `chunk` of tile rows n0..n0+15 into an LDS slot: instruction i covers
 // rows 8i..8i+7; lane -> row 8i + lane/8, physical piece lane%8.  `ok` false:
@@ -287,7 +299,7 @@ __device__ __forceinline__ v4f chunk_mfma_x(const uint8_t* __restrict__ slot, in
 template <int S, bool DEFER, int XI, bool BAL>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act,
-    const float* __restrict__ s_w, ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw)
+    const float* __restrict__ s_w, ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw, int sw_lds)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int W = blockDim.x >> 6;
@@ -320,8 +332,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
     const int mp = M <= 8 ? 32 : 64;
     const int pslot = mp == 64 ? lane : (lane >> 4) * 8 + (lane & 7);
     v4f* red = reinterpret_cast<v4f*>(smem + xbytes);
-    uint8_t* ring = smem + xbytes + (DEFER ? (int64_t)tiles_max * W * mp : (int64_t)2 * W * 64) * sizeof(v4f) +
-                    wave * S * SB;
+    uint8_t* ring0 = smem + xbytes + (DEFER ? (int64_t)tiles_max * W * mp : (int64_t)2 * W * 64) * sizeof(v4f);
+    uint8_t* ring = ring0 + wave * S * SB;
+    float* swl = reinterpret_cast<float*>(ring0 + W * S * SB);   // DEFER, sw_lds: the tiles' weight scales
     const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
     const __amdgpu_buffer_rsrc_t rx = weight_rsrc(xq, M * K);
     // this lane's two rows of a chunk (instruction i: row 8i + lane/8), logical piece
@@ -385,6 +398,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
                                                      0, 0, 0);
     };
 
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
+    if (DEFER && sw_lds) {
+        // The weight scales of this workgroup's tiles into LDS, 16 per tile
+        // (zeros past a tile's rows), ahead of everything else: the final
+        // reduction reads them from LDS instead of waiting on memory (where
+        // the LDS has room for them).
+        for (int t0 = 4 * wave; t0 < tiles_max; t0 += 4 * W) {
+            const int t = t0 + (lane >> 4);
+            int rt, re;
+            tile_rows(t, rt, re);
+            const int n = rt + (lane & 15);
+            const uint32_t o = t < my_tiles && n < re ? (uint32_t)n * 4 : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(swl + t0 * 16), 4, (int)o, 0, 0, 0);
+        }
+    }
     if (XI == 0) {
         // x_q -> LDS first: each wave moves 64 consecutive 16-byte pieces (1 KB,
         // inside one row because K/16 is a multiple of 64) per instruction.
@@ -412,7 +440,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
     const uint8_t* xrow = xs + (r < M ? r : M - 1) * ldsx;
     const int xsr = XI == 1 ? (r < 8 ? r : 7) : r;      // streamed x_q: row of the slot's x part
     // weight scales of tile u for this lane's four rows (tile-by-tile reduction only)
-    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
     auto tile_sw = [&](int t) {
         int rt, re;
         tile_rows(t, rt, re);
@@ -474,8 +501,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
             int n0, re;
             tile_rows(uu, n0, re);
             if (n0 + 4 * (l >> 4) >= re) continue;       // another workgroup's rows
-            reduce_tile(red + uu * W * mp, mp, ps, W, n0, re, s_act,
-                        *reinterpret_cast<const float4*>(s_w + n0 + 4 * (l >> 4)), sh, M, l, BAL);
+            const float4 sw4 = sw_lds ? *reinterpret_cast<const float4*>(swl + uu * 16 + 4 * (l >> 4))
+                                      : tile_scales(rs, n0 + 4 * (l >> 4));
+            reduce_tile(red + uu * W * mp, mp, ps, W, n0, re, s_act, sw4, sh, M, l, BAL);
         }
     }
 }
@@ -546,7 +574,7 @@ __device__ __forceinline__ void put_partial(v4f* __restrict__ dst, v4f v) { *dst
 template <int S, int MT, int XM, int CPW, bool BAL, bool DEFER>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act, const float* __restrict__ s_w,
-    ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw)
+    ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw, int sw_lds)
 {
     static_assert(XM == XM_STREAM || CPW > 0, "resident fragments need a compile-time chunk count");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -571,14 +599,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
         }
     };
     const int cw = XM == XM_STREAM ? cpw : CPW;         // chunks per wave and tile
-    // LDS: [partials] [W rings of S 2 KB slots].  partials: [2][W][MT][64], or
-    // with DEFER [tiles_max][W][MT][mp] (reduced once, at the end; for M <= 8
-    // only the 32 lanes holding columns m < 8).
+    // LDS: [partials] [W rings of S 2 KB slots] [DEFER, sw_lds: weight scales].
+    // partials: [2][W][MT][64], or with DEFER [tiles_max][W][MT][mp] (reduced
+    // once, at the end; for M <= 8 only the 32 lanes holding columns m < 8).
     const int mp = MT == 1 && M <= 8 ? 32 : 64;
     const int pslot = mp == 64 ? lane : (lane >> 4) * 8 + (lane & 7);
     v4f* red = reinterpret_cast<v4f*>(smem);
     const int64_t red_elems = DEFER ? (int64_t)tiles_max * W * MT * mp : (int64_t)2 * W * MT * 64;
     uint8_t* ring = reinterpret_cast<uint8_t*>(red + red_elems) + wave * S * 2048;
+    float* swl = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(red + red_elems) + W * S * 2048);
     const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
     // this lane's two rows of a weight chunk (instruction i: row 8i + lane/8), logical piece
     const int lrow = lane >> 3;
@@ -620,6 +649,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     };
     auto a_frag = [&](int slot) { return slot_afrag(ring + slot * 2048, r, g); };
 
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
+    if (DEFER && sw_lds) {
+        // The weight scales of this workgroup's tiles into LDS, 16 per tile
+        // (zeros past a tile's rows), one 4-byte direct-to-LDS load per lane,
+        // issued ahead of the stream: the final reduction then reads them from
+        // LDS instead of waiting on memory after the last chunk (where the LDS
+        // has room for them).
+        for (int t0 = 4 * wave; t0 < tiles_max; t0 += 4 * W) {
+            const int t = t0 + (lane >> 4);
+            int rt, re;
+            tile_rows(t, rt, re);
+            const int n = rt + (lane & 15);
+            const uint32_t o = t < my_tiles && n < re ? (uint32_t)n * 4 : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(swl + t0 * 16), 4, (int)o, 0, 0, 0);
+        }
+    }
     constexpr int NB = XM == XM_STREAM ? S : CPW;
     v8i bx[NB][MT];
     const __amdgpu_buffer_rsrc_t rx = weight_rsrc(xq, (int64_t)M * K);
@@ -639,7 +684,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     // weight scales of tile u for this lane's four rows (tile-by-tile reduction
     // only; loaded in the loop iteration that uses them, so the compiler can
     // count the loads issued after them instead of waiting for all)
-    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
     auto tile_sw = [&](int t) {
         int rt, re;
         tile_rows(t, rt, re);
@@ -736,8 +780,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
             int n0, re;
             tile_rows(uu, n0, re);
             if (n0 + 4 * (l >> 4) >= re) continue;       // another workgroup's rows
-            reduce_tile(red + (uu * W * MT + mt) * mp, MT * mp, ps, W, n0, re, s_act,
-                        *reinterpret_cast<const float4*>(s_w + n0 + 4 * (l >> 4)), sh, M, l, BAL, 16 * mt);
+            const float4 sw4 = sw_lds ? *reinterpret_cast<const float4*>(swl + uu * 16 + 4 * (l >> 4))
+                                      : tile_scales(rs, n0 + 4 * (l >> 4));
+            reduce_tile(red + (uu * W * MT + mt) * mp, MT * mp, ps, W, n0, re, s_act, sw4, sh, M, l, BAL, 16 * mt);
         }
     }
 }
@@ -770,7 +815,7 @@ void allow_large_lds()
 template <int S, bool DEFER, int XI, bool BAL>
 void launch_ring(const dim3& grid, const dim3& block, size_t lds, hipStream_t stream, const uint8_t* xq,
                  const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh, int M, int64_t N, int64_t K,
-                 int nchunks, int cpw)
+                 int nchunks, int cpw, int sw_lds)
 {
     static const bool attr = [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_ring<S, DEFER, XI, BAL>),
@@ -779,7 +824,7 @@ void launch_ring(const dim3& grid, const dim3& block, size_t lds, hipStream_t st
     }();
     (void)attr;
     hipLaunchKernelGGL((k_gemm_small_m_ring<S, DEFER, XI, BAL>), grid, block, lds, stream, xq, wq, s_act, s_w, sh, M, N, K,
-                       nchunks, cpw);
+                       nchunks, cpw, sw_lds);
 }
 
 // The LDS-ring persistent kernel, if it applies (M <= 16, K % 1024 == 0,
@@ -803,14 +848,18 @@ bool try_ring(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_
     auto bytes = [&](int S, bool df, int xi) {
         return (xi ? 0 : xb) + (df ? tiles_max * dpart : 2 * part) + (size_t)W * S * (2048 + 1024 * xi);
     };
+    // with DEFER, the tiles' weight scales in LDS too where they fit
+    const size_t swb = (size_t)(tiles_max + 3) / 4 * 256;
 #define FP8MM_RING_TRY(S, DF, XI)                                                                      \
     if (bytes(S, DF, XI) <= 160 * 1024) {                                                              \
+        const int swl = DF && bytes(S, DF, XI) + swb <= 160 * 1024;                                    \
+        const size_t lds = bytes(S, DF, XI) + (swl ? swb : 0);                                         \
         if (bal)                                                                                       \
-            launch_ring<S, DF, XI, true>(grid, block, bytes(S, DF, XI), stream, xq, wq, s_act, s_w, sh, (int)M, N, K, \
-                                         nchunks, cpw);                                                \
+            launch_ring<S, DF, XI, true>(grid, block, lds, stream, xq, wq, s_act, s_w, sh, (int)M, N, K, nchunks, \
+                                         cpw, swl);                                                    \
         else                                                                                           \
-            launch_ring<S, DF, XI, false>(grid, block, bytes(S, DF, XI), stream, xq, wq, s_act, s_w, sh, (int)M, N, K, \
-                                          nchunks, cpw);                                               \
+            launch_ring<S, DF, XI, false>(grid, block, lds, stream, xq, wq, s_act, s_w, sh, (int)M, N, K, nchunks, \
+                                          cpw, swl);                                                   \
         return true;                                                                                   \
     }
     FP8MM_RING_TRY(6, true, 0)
@@ -837,7 +886,7 @@ bool try_ring(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_
 // deepest ring that fits, deferred reduction preferred.
 struct RxPlan {
     int xm, mt, cpw, S;
-    bool bal, defer;
+    bool bal, defer, sw_lds;
     size_t lds;
     unsigned G, W;
 };
@@ -867,9 +916,11 @@ bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p)
                                                        {3, false}, {2, true}, {2, false}};
     for (const auto& o : order)
         if (bytes(o.S, o.df) <= 160 * 1024 && (o.df || p->xm != XM_STREAM)) {
+            const size_t swb = (size_t)(tiles_max + 3) / 4 * 256;   // DEFER: the weight scales, where they fit
             p->S = o.S;
             p->defer = o.df;
-            p->lds = bytes(o.S, o.df);
+            p->sw_lds = o.df && bytes(o.S, o.df) + swb <= 160 * 1024;
+            p->lds = bytes(o.S, o.df) + (p->sw_lds ? swb : 0);
             return true;
         }
     return false;
@@ -887,7 +938,7 @@ void launch_rx(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float s_ac
     }();
     (void)attr;
     hipLaunchKernelGGL((k_gemm_small_m_rx<S, MT, XM, CPW, BAL, DEFER>), dim3(p.G), dim3(64 * p.W), p.lds, stream, xq,
-                       wq, s_act, s_w, sh, M, N, K, nchunks, p.cpw);
+                       wq, s_act, s_w, sh, M, N, K, nchunks, p.cpw, (int)p.sw_lds);
 }
 
 template <int MT, int XM, int CPW, bool BAL>
