@@ -32,12 +32,52 @@ __device__ __host__ __forceinline__ float silu_f64(float g)
 // above it for g < 0.  fma(g, 0, t) = t exactly (no band value is zero) and
 // fma(g, m, -0) = g * m exactly.
 constexpr uint32_t kSiluLo = 0x3300u, kSiluBand = 0x42DAu - 0x3300u;
-constexpr int kSiluTableSize = 2 * (int)kSiluBand;  // t values: positive band, then negative
+// Table layout: entry sign * kSiluSignStride + (|g| bits - kSiluLo).  The
+// stride is a power of two, so the gate's sign bit moves into the index with
+// one shift and mask.
+constexpr int kSiluSignStride = 4096;
+constexpr int kSiluTableSize = 2 * kSiluSignStride;
 
-__device__ __host__ __forceinline__ float silu_table_entry(int j)
+// exp(x) for |x| < 128, evaluated by the compiler to build the table below:
+// x = k ln2 + r with |r| <= ln2 / 2 (Cody-Waite reduction; the high part of
+// ln2 has trailing zero bits, so k ln2_hi is exact), exp(r) from its Taylor
+// series to degree 18 by Horner's rule (the truncation error is below 2^-60
+// of the result), times 2^k built from its exponent bits.  The host tests
+// compare every table entry with silu_f64 (the C library's exp).
+constexpr double silu_cx_exp(double x)
 {
-    const uint32_t neg = j >= (int)kSiluBand ? 1u : 0u;
-    return silu_f64(bf16_to_f32((neg << 15) | (kSiluLo + (uint32_t)j - neg * kSiluBand)));
+    constexpr double ln2_hi = 6.93147180369123816490e-01, ln2_lo = 1.90821492927058770002e-10;
+    const double kd = x * 1.44269504088896338700e+00;
+    const int k = (int)(kd < 0.0 ? kd - 0.5 : kd + 0.5);
+    const double r = (x - k * ln2_hi) - k * ln2_lo;
+    double c[19] = {};
+    c[0] = 1.0;
+    for (int n = 1; n < 19; ++n) c[n] = c[n - 1] / n;
+    double p = c[18];
+    for (int n = 17; n >= 0; --n) p = p * r + c[n];
+    return p * __builtin_bit_cast(double, (uint64_t)(1023 + k) << 52);
+}
+
+// silu_f64 of a band gate, at compile time.
+constexpr float silu_cx(uint32_t b)
+{
+    const double d = (double)__builtin_bit_cast(float, b << 16);
+    return (float)(d / (1.0 + silu_cx_exp(-d)));
+}
+
+struct SiluBandTable {
+    float t[kSiluTableSize];
+};
+
+// The band values of both signs (entries past the band in each half are 0 and
+// never read).
+constexpr SiluBandTable make_silu_band_table()
+{
+    SiluBandTable tab{};
+    for (int sg = 0; sg < 2; ++sg)
+        for (int j = 0; j < (int)kSiluBand; ++j)
+            tab.t[sg * kSiluSignStride + j] = silu_cx(((uint32_t)sg << 15) | (kSiluLo + (uint32_t)j));
+    return tab;
 }
 
 // Table index of gate bits b (clamped into the band; out-of-band gates do not
@@ -46,7 +86,7 @@ __device__ __host__ __forceinline__ uint32_t silu_table_index(uint32_t b)
 {
     const int d = (int)(b & 0x7fffu) - (int)kSiluLo;
     const int k = d < 0 ? 0 : (d >= (int)kSiluBand ? (int)kSiluBand - 1 : d);   // a med3
-    return (uint32_t)k + (b >> 15) * kSiluBand;
+    return (uint32_t)k + (b >> 15) * (uint32_t)kSiluSignStride;
 }
 
 __device__ __host__ __forceinline__ float silu_finish(uint32_t b, float t_band)
@@ -204,6 +244,113 @@ __device__ __host__ __forceinline__ uint32_t f32_to_bf16_cvt(float f)
 #else
     return f32_to_bf16_rne_sel(f);
 #endif
+}
+
+// Two fp32 -> packed bf16 bits (lo in bits 0-15), round to nearest even:
+// v_cvt_pk_bf16_f32 on the device, the integer form on the host.
+__device__ __host__ __forceinline__ uint32_t pack_bf16x2_hd(float lo, float hi)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return pack_bf16x2(lo, hi);
+#else
+    return f32_to_bf16_rne_sel(lo) | (f32_to_bf16_rne_sel(hi) << 16);
+#endif
+}
+
+// The sign bits of the four bf16 values in words w0 (values 0, 1) and w1
+// (values 2, 3) as bit 7 of bytes 0..3 (one byte permute on the device).
+__device__ __host__ __forceinline__ uint32_t sign_bytes4(uint32_t w0, uint32_t w1)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_perm(w1, w0, 0x07050301u) & 0x80808080u;
+#else
+    return ((w0 >> 8) & 0x80u) | ((w0 >> 16) & 0x8000u) | ((w1 << 8) & 0x800000u) | (w1 & 0x80000000u);
+#endif
+}
+
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __host__ __forceinline__ u16x2_t as_u16x2(uint32_t w) { return __builtin_bit_cast(u16x2_t, w); }
+__device__ __host__ __forceinline__ uint32_t as_u32(u16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __host__ __forceinline__ u16x2_t splat_u16x2(uint32_t v)
+{
+    return u16x2_t{(unsigned short)v, (unsigned short)v};
+}
+
+// E4M3 codes of h = bf16(fl32(silu(g) * u)) under s_act for the 8 gate and up
+// values of one 16-byte piece each (gate words gw, up words uw: value 2i in
+// the low half of word i), the common case only: every gate inside the SiLU
+// band (s = its table entry t) and no h a NaN.  Then h's code is the band
+// table's entry of its magnitude (below the band a zero, above it 448, inf
+// included) with h's sign.  Two values are handled per 32-bit word with
+// packed 16-bit integer operations.  Writes the 8 table values of the gates
+// (for the exact path) and returns false if some value is outside the common
+// case; the codes are then not valid.  stab: the SiLU band table;
+// ctab: the plain quant's band table; lo1 = code_band_lo(s_act) - 1.
+__device__ __host__ __forceinline__ bool silu_mul_codes8_fast(const uint32_t (&gw)[4], const uint32_t (&uw)[4],
+                                                              const float* stab, const uint8_t* ctab, uint32_t lo1,
+                                                              float (&t)[8], uint2& out)
+{
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // band offset |g| - kSiluLo of both halves; below the band it wraps past the band's end
+        const u16x2_t d = as_u16x2(gw[i] & 0x7fff7fffu) - splat_u16x2(kSiluLo);
+        const u16x2_t k = __builtin_elementwise_min(d, splat_u16x2(kSiluBand - 1u));
+        ok = ok && as_u32(k) == as_u32(d);
+        const uint32_t idx = as_u32(k) | ((gw[i] >> 3) & 0x10001000u);   // + sign * 4096
+        t[2 * i] = stab[idx & 0xffffu];
+        t[2 * i + 1] = stab[idx >> 16];
+    }
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        h[i] = pack_bf16x2_hd(t[2 * i] * __builtin_bit_cast(float, uw[i] << 16),
+                              t[2 * i + 1] * __builtin_bit_cast(float, uw[i] & 0xffff0000u));
+    uint32_t c[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        uint32_t cc = 0u;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const u16x2_t a = as_u16x2(h[2 * q + e] & 0x7fff7fffu);
+            ok = ok && as_u32(__builtin_elementwise_max(a, splat_u16x2(0x7f80u))) == 0x7f807f80u;   // no NaN
+            const u16x2_t j = __builtin_elementwise_min(__builtin_elementwise_sub_sat(a, splat_u16x2(lo1)),
+                                                        splat_u16x2(kCodeBand + 1u));
+            cc |= ((uint32_t)ctab[as_u32(j) & 0xffffu] | ((uint32_t)ctab[as_u32(j) >> 16] << 8)) << (16 * e);
+        }
+        c[q] = cc | sign_bytes4(h[2 * q], h[2 * q + 1]);
+    }
+    out = make_uint2(c[0], c[1]);
+    return ok;
+}
+
+// The same codes for any inputs, from the gates' table values t (as
+// silu_mul_codes8_fast wrote them): s = silu_finish(g, t) (the closed forms
+// outside the band), a NaN h encoded with its own sign.
+__device__ __host__ __forceinline__ uint2 silu_mul_codes8_exact(const uint32_t (&gw)[4], const uint32_t (&uw)[4],
+                                                                const float (&t)[8], const uint8_t* ctab,
+                                                                uint32_t lo1)
+{
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        h[i] = pack_bf16x2_hd(silu_finish(gw[i] & 0xffffu, t[2 * i]) * __builtin_bit_cast(float, uw[i] << 16),
+                              silu_finish(gw[i] >> 16, t[2 * i + 1]) * __builtin_bit_cast(float, uw[i] & 0xffff0000u));
+    uint32_t c[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        uint32_t cc = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t a = (h[2 * q + (e >> 1)] >> ((e & 1) * 16)) & 0x7fffu;
+            const int j = (int)a - (int)lo1;
+            const uint32_t code = ctab[j < 0 ? 0 : (j > (int)kCodeBand + 1 ? (int)kCodeBand + 1 : j)];
+            cc |= (a > 0x7f80u ? 0x7fu : code) << (8 * e);
+        }
+        c[q] = cc | sign_bytes4(h[2 * q], h[2 * q + 1]);
+    }
+    return make_uint2(c[0], c[1]);
 }
 
 }  // namespace fp8mm

@@ -480,49 +480,23 @@ __global__ __launch_bounds__(kQuantThreads) void k_silu_mul_quant(
     }
 }
 
-// Table path for NP 16-byte pieces of gate and up: every SiLU table read is
-// issued before any is used, then the codes of the bf16 products come from the
-// band table of the plain quant (quant8_band: the codes of every bf16 value
-// under s_act, a NaN keeping its sign); nothing branches.
-template <int NP>
-__device__ __forceinline__ void silu_mul_quant_tables(const uint4 (&g)[NP], const uint4 (&u)[NP],
-                                                      const float* __restrict__ stab,
-                                                      const uint8_t* __restrict__ ctab, int lo1, uint2 (&out)[NP])
-{
-    constexpr int E = 8 * NP;
-    uint32_t gb[E], hb[E];
-    float t[E];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const uint32_t w[4] = {g[p].x, g[p].y, g[p].z, g[p].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) gb[8 * p + i] = (w[i >> 1] >> ((i & 1) * 16)) & 0xffffu;
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) t[e] = stab[silu_table_index(gb[e])];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const uint32_t w[4] = {u[p].x, u[p].y, u[p].z, u[p].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int e = 8 * p + i;
-            const float uv = bf16_to_f32((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
-            hb[e] = f32_to_bf16_cvt(silu_finish(gb[e], t[e]) * uv);
-        }
-    }
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-        out[p] = quant8_band(hb[8 * p] | (hb[8 * p + 1] << 16), hb[8 * p + 2] | (hb[8 * p + 3] << 16),
-                             hb[8 * p + 4] | (hb[8 * p + 5] << 16), hb[8 * p + 6] | (hb[8 * p + 7] << 16), ctab, lo1);
-}
+// The SiLU band table (silu_f64 of every band gate, both signs), evaluated by
+// the compiler: each workgroup copies it into LDS instead of evaluating 8116
+// fp64 SiLUs.
+__device__ const SiluBandTable kSiluBandTableDev = make_silu_band_table();
 
-// Many rows (prefill).  Each workgroup first fills two LDS tables: the SiLU
-// values of the band gates (8116 fp64 evaluations, 32 KB) and the band code
-// table of the plain quant under s_act (2.5 KB, one division per mantissa),
-// small enough for two 1024-thread workgroups per CU.  It then streams a
-// contiguous share of the [M, I] pieces, NP per thread per step (kSiluLutThreads
-// apart, so each load instruction of a wave covers 1 KB), stepping the row and
-// column instead of dividing.  total = M * I / 8 < 2^31.
+// Many rows (prefill).  Each workgroup first copies the SiLU band table into
+// LDS (32 KB: two 16-byte direct-to-LDS loads per thread) and fills the band
+// code table of the plain quant under s_act (2.5 KB, one division per
+// mantissa), 35 KB in all: two 1024-thread workgroups per CU.  The grid then
+// sweeps the [M, I] pieces together, NP per thread per step (kSiluLutThreads
+// apart, so each load instruction of a wave covers 1 KB), with one step of
+// the whole grid between a thread's steps.  A piece past the end is loaded
+// from the thread's first piece of the step and stores that piece's codes
+// there again, so nothing branches around a load or a store.  Per piece the
+// common case (silu_mul_codes8_fast) runs first; a piece with a gate outside
+// the SiLU band or a NaN product takes the exact path.  total = M * I / 8 <
+// 2^31.
 constexpr int kSiluLutThreads = 1024;
 
 // Non-temporal: the activation is read once.
@@ -533,25 +507,33 @@ __device__ __forceinline__ uint4 load_piece(const uint16_t* p)
     return make_uint4(r.x, r.y, r.z, r.w);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int NP>
 __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
     const uint16_t* __restrict__ gate, int64_t ldg, const uint16_t* __restrict__ up, int64_t ldu, float s_act,
     uint8_t* __restrict__ xq, uint32_t nv, uint32_t total, int64_t I)
 {
-    __shared__ float stab[kSiluTableSize];
+    __shared__ __attribute__((aligned(16))) float stab[kSiluTableSize];
     __shared__ uint8_t ctab[kBandTableBytes];
-    for (int j = threadIdx.x; j < kSiluTableSize; j += blockDim.x) stab[j] = silu_table_entry(j);
+    {
+        // the SiLU table: 32 chunks of 1 KB, a wave's 64 lanes x 16 bytes each
+        const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<SiluBandTable*>(&kSiluBandTableDev), (short)0, (int)sizeof(SiluBandTable), 0x00020000);
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+        for (int c = wave; c < (int)(sizeof(SiluBandTable) / 1024); c += kSiluLutThreads / 64)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_void*)(reinterpret_cast<uint8_t*>(stab) + c * 1024), 16,
+                                                     c * 1024 + lane * 16, 0, 0, 0);
+    }
     fill_plain_band_table(ctab, s_act, threadIdx.x, blockDim.x);
-    const int lo1 = (int)code_band_lo(s_act) - 1;
-    __syncthreads();
-    // this workgroup's pieces: [begin, end), a multiple of kStep long
-    constexpr uint32_t kStep = (uint32_t)NP * kSiluLutThreads;
-    const uint32_t per = ((total + gridDim.x - 1) / gridDim.x + kStep - 1) / kStep * kStep;
-    const uint32_t begin = blockIdx.x * per;
-    const uint32_t end = begin + per < total ? begin + per : total;
-    uint32_t i = begin + threadIdx.x;
-    if (i >= end) return;
-    const uint32_t dm = kStep / nv, dv = kStep - dm * nv;     // one step = dm rows + dv pieces
+    const uint32_t lo1 = code_band_lo(s_act) - 1u;
+    __syncthreads();                                    // both tables in LDS
+    const uint32_t stride = gridDim.x * (uint32_t)(NP * kSiluLutThreads);
+    uint32_t i = blockIdx.x * (uint32_t)(NP * kSiluLutThreads) + threadIdx.x;
+    if (i >= total) return;
+    // the pieces' rows and columns, stepped instead of divided: piece
+    // ip + stride is dm rows and dv pieces further
+    const uint32_t dm = stride / nv, dv = stride - dm * nv;
     uint32_t m[NP], v[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
@@ -559,42 +541,34 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
         m[p] = ip / nv;
         v[p] = ip - m[p] * nv;
     }
-    // a piece at or past `end` is loaded from piece 0's address instead (a
-    // valid location), so no load needs a branch
-    uint4 g[NP], u[NP];
-    auto load_step = [&](uint32_t i_, const uint32_t (&m_)[NP], const uint32_t (&v_)[NP], uint4 (&g_)[NP],
-                         uint4 (&u_)[NP]) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const bool ok = i_ + (uint32_t)p * kSiluLutThreads < end;
-            const uint32_t mm = ok ? m_[p] : m_[0], vv = ok ? v_[p] : v_[0];
-            g_[p] = load_piece(gate + mm * ldg + vv * 8);
-            u_[p] = load_piece(up + mm * ldu + vv * 8);
-        }
-    };
-    auto advance = [&](uint32_t (&m_)[NP], uint32_t (&v_)[NP]) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            v_[p] += dv;
-            m_[p] += dm + (v_[p] >= nv ? 1u : 0u);
-            v_[p] -= v_[p] >= nv ? nv : 0u;
-        }
-    };
     for (;;) {
-        load_step(i, m, v, g, u);
-        uint2 o[NP];
-        silu_mul_quant_tables<NP>(g, u, stab, ctab, lo1, o);
-        // a piece past `end` was loaded from piece 0's address, so its codes are
-        // piece 0's: it stores them there again instead of branching (a branch
-        // lets the compiler sink that piece's loads behind the other's store)
+        uint4 g[NP], u[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            const bool ok = i + (uint32_t)p * kSiluLutThreads < end;
-            *reinterpret_cast<uint2*>(xq + (int64_t)(ok ? m[p] : m[0]) * I + (ok ? v[p] : v[0]) * 8) = o[p];
+            const bool in = i + (uint32_t)p * kSiluLutThreads < total;
+            const uint32_t mm = in ? m[p] : m[0], vv = in ? v[p] : v[0];
+            g[p] = load_piece(gate + mm * ldg + vv * 8);
+            u[p] = load_piece(up + mm * ldu + vv * 8);
         }
-        i += kStep;
-        if (i >= end) break;
-        advance(m, v);
+        __builtin_amdgcn_sched_barrier(0);              // every load of the step in flight before any use
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const bool in = i + (uint32_t)p * kSiluLutThreads < total;
+            const uint32_t gw[4] = {g[p].x, g[p].y, g[p].z, g[p].w};
+            const uint32_t uw[4] = {u[p].x, u[p].y, u[p].z, u[p].w};
+            float t[8];
+            uint2 o;
+            if (!silu_mul_codes8_fast(gw, uw, stab, ctab, lo1, t, o)) o = silu_mul_codes8_exact(gw, uw, t, ctab, lo1);
+            *reinterpret_cast<uint2*>(xq + (int64_t)(in ? m[p] : m[0]) * I + (in ? v[p] : v[0]) * 8) = o;
+        }
+        i += stride;
+        if (i >= total) break;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            v[p] += dv;
+            m[p] += dm + (v[p] >= nv ? 1u : 0u);
+            v[p] -= v[p] >= nv ? nv : 0u;
+        }
     }
 }
 

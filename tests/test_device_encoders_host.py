@@ -37,11 +37,9 @@ extern "C" long bf_sel_mismatches_all(void) {
     }
     return bad;
 }
-static float g_stab[fp8mm::kSiluTableSize];
-extern "C" int silu_lut_build(void) {
-    for (int j = 0; j < fp8mm::kSiluTableSize; ++j) g_stab[j] = fp8mm::silu_table_entry(j);
-    return fp8mm::kSiluTableSize;
-}
+static constexpr fp8mm::SiluBandTable g_tab = fp8mm::make_silu_band_table();
+static const float* g_stab = g_tab.t;
+extern "C" int silu_lut_build(void) { return fp8mm::kSiluTableSize; }
 extern "C" void silu_both(const unsigned short* b, long n, float* from_lut, float* direct) {
     for (long i = 0; i < n; ++i) {
         from_lut[i] = fp8mm::silu_from_table(b[i], g_stab);
@@ -72,6 +70,28 @@ extern "C" void silu_mul_codes(const unsigned short* g, const unsigned short* u,
     for (long i = 0; i < n; ++i)
         o[i] = g_codes[fp8mm::f32_to_bf16_cvt(fp8mm::silu_from_table(g[i], g_stab) * fp8mm::bf16_to_f32(u[i]))];
 }
+// The table kernel's per-piece logic (n a multiple of 8): the common-case
+// codes where silu_mul_codes8_fast accepts the piece (fast[i / 8] = 1), else
+// silu_mul_codes8_exact.
+extern "C" void silu_mul_codes_pieces(const unsigned short* g, const unsigned short* u, long n, float s,
+                                      unsigned char* o, unsigned char* fast) {
+    static unsigned char tab[fp8mm::kBandTableBytes];
+    const unsigned lo = fp8mm::code_band_lo(s);
+    for (int t = 0; t < 1024; ++t) fp8mm::fill_band_table(tab, lo, s, t, 1024);
+    tab[0] = 0u, tab[fp8mm::kCodeBand + 1] = 0x7eu, tab[fp8mm::kCodeBand + 2] = 0x7eu;
+    for (long i = 0; i < n; i += 8) {
+        uint32_t gw[4], uw[4];
+        for (int k = 0; k < 4; ++k) {
+            gw[k] = g[i + 2 * k] | ((uint32_t)g[i + 2 * k + 1] << 16);
+            uw[k] = u[i + 2 * k] | ((uint32_t)u[i + 2 * k + 1] << 16);
+        }
+        float t[8];
+        uint2 c;
+        fast[i / 8] = fp8mm::silu_mul_codes8_fast(gw, uw, g_stab, tab, lo - 1u, t, c);
+        if (!fast[i / 8]) c = fp8mm::silu_mul_codes8_exact(gw, uw, t, tab, lo - 1u);
+        for (int k = 0; k < 4; ++k) o[i + k] = (c.x >> (8 * k)) & 0xffu, o[i + 4 + k] = (c.y >> (8 * k)) & 0xffu;
+    }
+}
 """
 
 
@@ -90,6 +110,8 @@ def dev():
     lib.bf.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p]
     lib.silu_both.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p]
     lib.silu_mul_codes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_float, ctypes.c_void_p]
+    lib.silu_mul_codes_pieces.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_float,
+                                          ctypes.c_void_p, ctypes.c_void_p]
     lib.bf_sel_mismatches_all.restype = ctypes.c_long
     lib.band_table_mismatches.argtypes = [ctypes.c_float, ctypes.c_int]
     lib.band_table_mismatches.restype = ctypes.c_long
@@ -204,6 +226,36 @@ def test_silu_mul_quant_device_logic_matches_oracle(dev):
         assert np.array_equal(nan_w, (got & 0x7F) == 0x7F)
         bad = np.flatnonzero((got != want) & ~nan_w)
         assert bad.size == 0, [(hex(gate[i]), hex(up[i]), hex(got[i]), hex(want[i])) for i in bad[:8]]
+
+
+def test_silu_mul_piece_logic_matches_oracle(dev):
+    """The table kernel's per-piece logic (the common-case fast path with its
+    fallback to the exact path), run on the host, against the oracle: every
+    gate pattern times unit, random and every up pattern, and N(0, 2) gates
+    and ups, where every piece must take the fast path.  Pieces holding a gate
+    outside the SiLU band or a NaN product must not."""
+    every = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    rng = np.random.Generator(np.random.PCG64(12))
+    rnd_b = (rng.standard_normal(65536).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    nrm_g = ((rng.standard_normal(1 << 16) * 2).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    nrm_u = ((rng.standard_normal(1 << 16) * 2).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    gate = np.concatenate([every, every, every, rnd_b, nrm_g])
+    up = np.concatenate([np.full(65536, 0x3F80, np.uint16), rnd_b, every[::-1].copy(), every, nrm_u])
+    for s in (1.0, 0.37, 1.0 / 448.0):
+        got = np.empty(gate.size, np.uint8)
+        fast = np.empty(gate.size // 8, np.uint8)
+        dev.silu_mul_codes_pieces(gate.ctypes.data, up.ctypes.data, gate.size, s, got.ctypes.data, fast.ctypes.data)
+        want = oracle.silu_mul_quant(gate[None], up[None], np.float32(s))[0]
+        nan_w = (want & 0x7F) == 0x7F
+        assert np.array_equal(nan_w, (got & 0x7F) == 0x7F)
+        bad = np.flatnonzero((got != want) & ~nan_w)
+        assert bad.size == 0, [(hex(gate[i]), hex(up[i]), hex(got[i]), hex(want[i])) for i in bad[:8]]
+        # which pieces the fast path may take: every gate magnitude in the band, no NaN product
+        mag = (gate & 0x7FFF).reshape(-1, 8)
+        in_band = ((mag >= 0x3300) & (mag < 0x42DA)).all(axis=1)
+        no_nan = ~nan_w.reshape(-1, 8).any(axis=1)
+        assert np.array_equal(fast.astype(bool), in_band & no_nan)
+        assert fast[-(1 << 13):].all()                  # the N(0, 2) pieces
 
 
 def test_branch_free_bf16_rounding_equals_the_plain_one_on_every_fp32(dev):
