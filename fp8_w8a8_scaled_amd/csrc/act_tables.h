@@ -12,6 +12,18 @@
 
 namespace fp8mm {
 
+// Two 16-bit lanes of one 32-bit word (a pair of bf16 values): the packed
+// 16-bit integer operations of gfx9 (v_pk_sub_u16, v_pk_min_u16, ...).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __host__ __forceinline__ u16x2_t as_u16x2(uint32_t w) { return __builtin_bit_cast(u16x2_t, w); }
+__device__ __host__ __forceinline__ uint32_t as_u32(u16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __host__ __forceinline__ u16x2_t splat_u16x2(uint32_t v)
+{
+    return u16x2_t{(unsigned short)v, (unsigned short)v};
+}
+
+
 // SiLU of a gate value, s = fl32( g / (1 + exp(-g)) ) with the expression in
 // fp64 (the same reading as the RMSNorm scale: wide arithmetic, one rounding).
 __device__ __host__ __forceinline__ float silu_f64(float g)
@@ -185,6 +197,16 @@ __device__ __forceinline__ uint2 quant8_band(uint32_t w0, uint32_t w1, uint32_t 
     return make_uint2(o[0], o[1]);
 }
 
+// The band-table codes (without sign) of the two bf16 magnitudes in word h:
+// entry clamp(|h| - lo1, 0, kCodeBand + 1) each, as bytes 0 and 1.  For
+// values that are not NaN (a NaN takes the saturated entry).
+__device__ __host__ __forceinline__ uint32_t band_codes2(uint32_t h, const uint8_t* tab, uint32_t lo1)
+{
+    const u16x2_t j = __builtin_elementwise_min(__builtin_elementwise_sub_sat(as_u16x2(h & 0x7fff7fffu), splat_u16x2(lo1)),
+                                                splat_u16x2(kCodeBand + 1u));
+    return (uint32_t)tab[as_u32(j) & 0xffffu] | ((uint32_t)tab[as_u32(j) >> 16] << 8);
+}
+
 // The 8 E4M3 codes of the RMSNorm output y_b = bf16(fl32(fl32(x r) gamma)) of
 // one piece (x words w0..w3, gamma as fp32 gf[0..7]) under the band table
 // (entry 0 below the band, kCodeBand + 1 saturated).  Valid when r and gamma
@@ -200,16 +222,9 @@ __device__ __forceinline__ uint2 rms_codes8_band(uint32_t w0, uint32_t w1, uint3
         h[i] = pack_bf16x2(bf16_to_f32(w[i] & 0xffffu) * r * gf[2 * i], bf16_to_f32(w[i] >> 16) * r * gf[2 * i + 1]);
     uint32_t o[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        uint32_t c = 0u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int a = (int)((h[2 * q + (e >> 1)] >> ((e & 1) * 16)) & 0x7fffu);
-            c |= (uint32_t)tab[min(max(a - lo1, 0), (int)kCodeBand + 1)] << (8 * e);
-        }
-        // the four sign bits: bit 15 and bit 31 of each packed pair
-        o[q] = c | (__builtin_amdgcn_perm(h[2 * q + 1], h[2 * q], 0x07050301u) & 0x80808080u);
-    }
+    for (int q = 0; q < 2; ++q)                         // the four sign bits: bits 15 and 31 of each pair
+        o[q] = band_codes2(h[2 * q], tab, (uint32_t)lo1) | (band_codes2(h[2 * q + 1], tab, (uint32_t)lo1) << 16) |
+               (__builtin_amdgcn_perm(h[2 * q + 1], h[2 * q], 0x07050301u) & 0x80808080u);
     return make_uint2(o[0], o[1]);
 }
 
@@ -268,15 +283,6 @@ __device__ __host__ __forceinline__ uint32_t sign_bytes4(uint32_t w0, uint32_t w
 #endif
 }
 
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __host__ __forceinline__ u16x2_t as_u16x2(uint32_t w) { return __builtin_bit_cast(u16x2_t, w); }
-__device__ __host__ __forceinline__ uint32_t as_u32(u16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
-__device__ __host__ __forceinline__ u16x2_t splat_u16x2(uint32_t v)
-{
-    return u16x2_t{(unsigned short)v, (unsigned short)v};
-}
-
 // E4M3 codes of h = bf16(fl32(silu(g) * u)) under s_act for the 8 gate and up
 // values of one 16-byte piece each (gate words gw, up words uw: value 2i in
 // the low half of word i), the common case only: every gate inside the SiLU
@@ -315,9 +321,7 @@ __device__ __host__ __forceinline__ bool silu_mul_codes8_fast(const uint32_t (&g
         for (int e = 0; e < 2; ++e) {
             const u16x2_t a = as_u16x2(h[2 * q + e] & 0x7fff7fffu);
             ok = ok && as_u32(__builtin_elementwise_max(a, splat_u16x2(0x7f80u))) == 0x7f807f80u;   // no NaN
-            const u16x2_t j = __builtin_elementwise_min(__builtin_elementwise_sub_sat(a, splat_u16x2(lo1)),
-                                                        splat_u16x2(kCodeBand + 1u));
-            cc |= ((uint32_t)ctab[as_u32(j) & 0xffffu] | ((uint32_t)ctab[as_u32(j) >> 16] << 8)) << (16 * e);
+            cc |= band_codes2(h[2 * q + e], ctab, lo1) << (16 * e);
         }
         c[q] = cc | sign_bytes4(h[2 * q], h[2 * q + 1]);
     }

@@ -352,8 +352,9 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int nk = (int)(K / TK);
-    const int64_t k_last = (int64_t)(nk - 1) * TK;
-    auto kof = [&](int st) { const int64_t k = (int64_t)st * TK; return k < k_last ? k : k_last; };
+    // K offset of stage st; the stages past the end (the pipeline's trailing
+    // loads) load from past the end of the buffers: zeros, no memory traffic
+    auto kof = [&](int st) { return st < nk ? (int64_t)st * TK : (int64_t)0x80000000u; };
     RowOffsets<NJ> ro;
     // The lane index passes through an empty asm statement, so the offsets'
     // lane arithmetic is redone per tile rather than hoisted out of the tile
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     // Epilogue: scale, round to bf16, stage the TX x 256 tile in LDS (rows of
     // m, padded), then store rows with 16-byte, row-contiguous writes (an f32
     // output in two halves: a whole f32 tile would not fit in LDS).
-    __builtin_amdgcn_s_waitcnt(0);                     // retire the trailing (unused) stage loads
+    __builtin_amdgcn_s_waitcnt(0);                     // retire the trailing (zero) stage loads
     __syncthreads();                                   // every stage read by every wave
     // The same for the epilogue's thread-index arithmetic (row and column
     // indices, LDS addresses).

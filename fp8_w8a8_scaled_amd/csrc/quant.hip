@@ -24,6 +24,8 @@ namespace {
 
 constexpr int kQuantThreads = kRmsRowThreads;
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 // Launch choices of the table-based kernels (measured on MI355X; the bytes do
 // not depend on them).
 constexpr int kSiluLutPerCu = 2;                  // SiLU*mul quant: workgroups per CU
@@ -232,13 +234,13 @@ __global__ __launch_bounds__(G * kRmsRowThreads) void k_quant_rmsnorm_lut(
                 if (v < nv) *reinterpret_cast<uint2*>(out + (int64_t)v * 8) = o;
             }
         } else {
-#pragma unroll
-            for (int p = 0; p < PPT; ++p) {
-                const int v = t + p * kRmsRowThreads;
-                if (v < nv)
-                    *reinterpret_cast<uint2*>(out + (int64_t)v * 8) =
-                        rms_quant8(in[p], *reinterpret_cast<const uint4*>(gamma + (int64_t)v * 8), r, s_act);
-            }
+            // the per-element path: a compact loop that reads the row again
+            const uint16_t* row = x + m * ldx;
+#pragma unroll 1
+            for (int v = t; v < nv; v += kRmsRowThreads)
+                *reinterpret_cast<uint2*>(out + (int64_t)v * 8) =
+                    rms_quant8(*reinterpret_cast<const uint4*>(row + (int64_t)v * 8),
+                               *reinterpret_cast<const uint4*>(gamma + (int64_t)v * 8), r, s_act);
         }
     };
     const int64_t first = (int64_t)blockIdx.x * G;       // the workgroup runs while its first group has a row
@@ -488,7 +490,9 @@ __device__ const SiluBandTable kSiluBandTableDev = make_silu_band_table();
 // Many rows (prefill).  Each workgroup first copies the SiLU band table into
 // LDS (32 KB: two 16-byte direct-to-LDS loads per thread) and fills the band
 // code table of the plain quant under s_act (2.5 KB, one division per
-// mantissa), 35 KB in all: two 1024-thread workgroups per CU.  The grid then
+// mantissa), 35 KB in all: two 1024-thread workgroups per CU (fewer
+// workgroups when the pieces do not fill them), with its first step's loads
+// already in flight.  The grid then
 // sweeps the [M, I] pieces together, NP per thread per step (kSiluLutThreads
 // apart, so each load instruction of a wave covers 1 KB), with one step of
 // the whole grid between a thread's steps.  A piece past the end is loaded
@@ -507,8 +511,6 @@ __device__ __forceinline__ uint4 load_piece(const uint16_t* p)
     return make_uint4(r.x, r.y, r.z, r.w);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 template <int NP>
 __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
     const uint16_t* __restrict__ gate, int64_t ldg, const uint16_t* __restrict__ up, int64_t ldu, float s_act,
@@ -516,6 +518,30 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
 {
     __shared__ __attribute__((aligned(16))) float stab[kSiluTableSize];
     __shared__ uint8_t ctab[kBandTableBytes];
+    const uint32_t stride = gridDim.x * (uint32_t)(NP * kSiluLutThreads);
+    uint32_t i = blockIdx.x * (uint32_t)(NP * kSiluLutThreads) + threadIdx.x;
+    const bool live = i < total;
+    // the pieces' rows and columns, stepped instead of divided: piece
+    // ip + stride is dm rows and dv pieces further
+    const uint32_t dm = stride / nv, dv = stride - dm * nv;
+    uint32_t m[NP], v[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const uint32_t ip = live ? i + (uint32_t)p * kSiluLutThreads : 0u;
+        m[p] = ip / nv;
+        v[p] = ip - m[p] * nv;
+    }
+    uint4 g[NP], u[NP];
+    auto load_step = [&]() {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const bool in = i + (uint32_t)p * kSiluLutThreads < total;
+            const uint32_t mm = in ? m[p] : m[0], vv = in ? v[p] : v[0];
+            g[p] = load_piece(gate + mm * ldg + vv * 8);
+            u[p] = load_piece(up + mm * ldu + vv * 8);
+        }
+    };
+    load_step();                                        // the first step's loads fly while the tables are built
     {
         // the SiLU table: 32 chunks of 1 KB, a wave's 64 lanes x 16 bytes each
         const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
@@ -528,28 +554,8 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
     fill_plain_band_table(ctab, s_act, threadIdx.x, blockDim.x);
     const uint32_t lo1 = code_band_lo(s_act) - 1u;
     __syncthreads();                                    // both tables in LDS
-    const uint32_t stride = gridDim.x * (uint32_t)(NP * kSiluLutThreads);
-    uint32_t i = blockIdx.x * (uint32_t)(NP * kSiluLutThreads) + threadIdx.x;
-    if (i >= total) return;
-    // the pieces' rows and columns, stepped instead of divided: piece
-    // ip + stride is dm rows and dv pieces further
-    const uint32_t dm = stride / nv, dv = stride - dm * nv;
-    uint32_t m[NP], v[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const uint32_t ip = i + (uint32_t)p * kSiluLutThreads;
-        m[p] = ip / nv;
-        v[p] = ip - m[p] * nv;
-    }
+    if (!live) return;
     for (;;) {
-        uint4 g[NP], u[NP];
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const bool in = i + (uint32_t)p * kSiluLutThreads < total;
-            const uint32_t mm = in ? m[p] : m[0], vv = in ? v[p] : v[0];
-            g[p] = load_piece(gate + mm * ldg + vv * 8);
-            u[p] = load_piece(up + mm * ldu + vv * 8);
-        }
         __builtin_amdgcn_sched_barrier(0);              // every load of the step in flight before any use
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -569,15 +575,17 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
             m[p] += dm + (v[p] >= nv ? 1u : 0u);
             v[p] -= v[p] >= nv ? nv : 0u;
         }
+        load_step();
     }
 }
 
 // Plain static quant of many elements: the codes of quant8 from a 2563-byte
 // table of the band of magnitudes whose code needs the division (as in
 // k_quant_rmsnorm_lut; entry kCodeBand + 2 is unused padding), a NaN keeping
-// its sign.  Each workgroup fills the table, then streams a contiguous share of
-// the [M, K] pieces, NP per thread per step, without branches: a piece past
-// the share is loaded from the thread's first piece and stores that piece's
+// its sign.  Each workgroup issues its first step's loads, fills the table,
+// then the grid sweeps the [M, K] pieces together, NP per thread per step (one
+// grid step between a thread's steps), without branches: a piece past the end
+// is loaded from the thread's first piece of the step and stores that piece's
 // codes there again.  total = M * K / 8 < 2^31.
 constexpr int kPlainLutThreads = 1024;
 static_assert(kPlainLutThreads % 128 == 0 && kSiluLutThreads % 128 == 0,
@@ -590,47 +598,49 @@ __global__ __launch_bounds__(kPlainLutThreads) void k_quant_plain_lut(
     uint32_t total, int64_t K)
 {
     __shared__ uint8_t tab[kBandTableBytes];
-    const int lo1 = (int)code_band_lo(s_act) - 1;
-    fill_plain_band_table(tab, s_act, threadIdx.x, blockDim.x);
-    __syncthreads();
-    constexpr uint32_t kStep = (uint32_t)NP * kPlainLutThreads;
-    const uint32_t per = ((total + gridDim.x - 1) / gridDim.x + kStep - 1) / kStep * kStep;
-    const uint32_t begin = blockIdx.x * per;
-    const uint32_t end = begin + per < total ? begin + per : total;
-    uint32_t i = begin + threadIdx.x;
-    if (i >= end) return;
-    const uint32_t dm = kStep / nv, dv = kStep - dm * nv;      // one step = dm rows + dv pieces
+    const uint32_t stride = gridDim.x * (uint32_t)(NP * kPlainLutThreads);
+    uint32_t i = blockIdx.x * (uint32_t)(NP * kPlainLutThreads) + threadIdx.x;
+    const bool live = i < total;
+    const uint32_t dm = stride / nv, dv = stride - dm * nv;     // one grid step = dm rows + dv pieces
     uint32_t m[NP], v[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        const uint32_t ip = i + (uint32_t)p * kPlainLutThreads;
+        const uint32_t ip = live ? i + (uint32_t)p * kPlainLutThreads : 0u;
         m[p] = ip / nv;
         v[p] = ip - m[p] * nv;
     }
-    for (;;) {
-        uint4 in[NP];
-        uint32_t mm[NP], vv[NP];
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    uint4 in[NP];
+    auto load_step = [&]() {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            const bool ok = i + (uint32_t)p * kPlainLutThreads < end;
-            mm[p] = ok ? m[p] : m[0];
-            vv[p] = ok ? v[p] : v[0];
-            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-            const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + mm[p] * ldx + vv[p] * 8));
+            const bool in_range = i + (uint32_t)p * kPlainLutThreads < total;
+            const u32x4 r = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(x + (in_range ? m[p] : m[0]) * ldx + (in_range ? v[p] : v[0]) * 8));
             in[p] = make_uint4(r.x, r.y, r.z, r.w);
         }
+    };
+    load_step();                                        // the first step's loads fly while the table is built
+    const int lo1 = (int)code_band_lo(s_act) - 1;
+    fill_plain_band_table(tab, s_act, threadIdx.x, blockDim.x);
+    __syncthreads();
+    if (!live) return;
+    for (;;) {
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
-            *reinterpret_cast<uint2*>(xq + (int64_t)mm[p] * K + vv[p] * 8) =
+        for (int p = 0; p < NP; ++p) {
+            const bool in_range = i + (uint32_t)p * kPlainLutThreads < total;
+            *reinterpret_cast<uint2*>(xq + (int64_t)(in_range ? m[p] : m[0]) * K + (in_range ? v[p] : v[0]) * 8) =
                 quant8_band(in[p].x, in[p].y, in[p].z, in[p].w, tab, lo1);
-        i += kStep;
-        if (i >= end) break;
+        }
+        i += stride;
+        if (i >= total) break;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             v[p] += dv;
             m[p] += dm + (v[p] >= nv ? 1u : 0u);
             v[p] -= v[p] >= nv ? nv : 0u;
         }
+        load_step();
     }
 }
 
@@ -720,7 +730,9 @@ void launch_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float e
     } else if (M * (K >> 3) >= kPlainLutMinElems / 8 && M * (K >> 3) < ((int64_t)1 << 31) &&
                code_table_ok(s_act)) {
         const int64_t total = M * (K >> 3);
-        hipLaunchKernelGGL((k_quant_plain_lut<kPlainLutPieces>), dim3((uint32_t)num_cus() * kPlainLutPerCu),
+        const int64_t cap = (int64_t)num_cus() * kPlainLutPerCu;
+        const int64_t need = (total + kPlainLutPieces * kPlainLutThreads - 1) / (kPlainLutPieces * kPlainLutThreads);
+        hipLaunchKernelGGL((k_quant_plain_lut<kPlainLutPieces>), dim3((uint32_t)(need < cap ? need : cap)),
                            dim3(kPlainLutThreads), 0, stream, x, ldx, s_act, xq, (uint32_t)(K >> 3), (uint32_t)total, K);
     } else if (M * K <= kPlainHalfMaxElems) {
         const int64_t blocks = (M * (K >> 2) + kQuantThreads - 1) / kQuantThreads;
@@ -779,7 +791,10 @@ void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up
 {
     const int64_t total = M * (I >> 3);
     if (silu_mul_uses_table(M, I, s_act)) {
-        const int64_t grid = (int64_t)num_cus() * kSiluLutPerCu;
+        // up to two workgroups per CU, fewer when the pieces do not fill them
+        const int64_t cap = (int64_t)num_cus() * kSiluLutPerCu;
+        const int64_t need = (total + kSiluLutPieces * kSiluLutThreads - 1) / (kSiluLutPieces * kSiluLutThreads);
+        const int64_t grid = need < cap ? need : cap;
         hipLaunchKernelGGL((k_silu_mul_quant_lut<kSiluLutPieces>), dim3((uint32_t)grid),
                            dim3(kSiluLutThreads), 0, stream, gate, ldg,
                            up, ldu, s_act, xq, (uint32_t)(I >> 3), (uint32_t)total, I);

@@ -131,7 +131,7 @@ int fp8_quant_rmsnorm(const uint16_t* x, int64_t ldx,
  * per-workgroup tables of the same evaluations instead of evaluating them per
  * element; the bytes are the same.
  * ---------------------------------------------------------------------- */
-#define FP8MM_SILU_TABLE_MIN_ELEMS (1LL << 22)
+#define FP8MM_SILU_TABLE_MIN_ELEMS (1LL << 19)
 int fp8_silu_mul_quant(const uint16_t* gate, int64_t ldg,
                        const uint16_t* up, int64_t ldu,
                        float s_act, uint8_t* x_q,

@@ -102,29 +102,32 @@ def test_quant_strided_input_and_special_rows(fp8):
     assert list(got[4, :4]) == [0x7E, 0xFE, 0x7F, 0xFF]
 
 
+@pytest.mark.parametrize("M", [37, 130])
 @pytest.mark.parametrize("K", [256, 2064, 5120, 8192, 16384])
 @pytest.mark.parametrize("s_act", [1.0, 0.37, 2.0 ** -20, 2.0 ** 20, 2.0 ** -99, 2.0 ** 99, 2.0 ** -110])
-def test_rmsnorm_quant_wide_gamma_and_special_rows(fp8, K, s_act):
+def test_rmsnorm_quant_wide_gamma_and_special_rows(fp8, M, K, s_act):
     """gamma spans 2^-40 .. 2^41 with random signs, so y_b crosses both edges of
     the band of magnitudes whose code needs the division, under every scale.
-    2048 <= K <= 8192 with 2^-100 <= s_act <= 2^100 takes the code lookup, the rest the
-    per-element path; both must give the oracle's bytes.  Special rows: inf, NaN,
-    all zeros with eps = 0 (r = inf), a lone subnormal; then an infinite gamma."""
+    2048 <= K <= 8192 with 2^-100 <= s_act <= 2^100 takes the code lookup, the
+    rest the per-element path; all must give the oracle's bytes (130 rows: an
+    odd row count for the row groups, rows strided).  Special rows: inf, NaN,
+    all zeros with eps = 0 (r = inf), a lone subnormal; then an infinite
+    gamma."""
     rng = np.random.default_rng(4200 + K)
-    M = 37
     x = wl.to_bf16_bits((rng.standard_normal((M, K)) * np.where(rng.random((M, K)) < 0.01, 20.0, 1.0))
                         .astype(np.float32))
     g = wl.to_bf16_bits((rng.choice([-1.0, 1.0], K) * (1.0 + rng.random(K))
                          * np.exp2(rng.integers(-40, 41, K))).astype(np.float32))
-    got = host_u8(fp8.quant_rmsnorm(bf16_dev(x), bf16_dev(g), float(s_act), wl.EPS))
+    dev_x = (lambda a: _strided(a, K + 16)) if M > 64 else bf16_dev
+    got = host_u8(fp8.quant_rmsnorm(dev_x(x), bf16_dev(g), float(s_act), wl.EPS))
     assert np.array_equal(got, oracle.quant_rmsnorm(x, g, wl.EPS, s_act))
 
     x[3, 5], x[4, 9], x[6, 0] = 0x7F80, 0x7FC0, 0x0001      # inf, NaN, subnormal in a zero row
     x[5], x[6, 1:] = 0, 0
-    got = host_u8(fp8.quant_rmsnorm(bf16_dev(x), bf16_dev(g), float(s_act), 0.0))
+    got = host_u8(fp8.quant_rmsnorm(dev_x(x), bf16_dev(g), float(s_act), 0.0))
     _assert_codes_equal(got, oracle.quant_rmsnorm(x, g, 0.0, s_act), "special rows")
     g[7] = 0xFF80                                            # gamma = -inf: every row per element
-    got = host_u8(fp8.quant_rmsnorm(bf16_dev(x), bf16_dev(g), float(s_act), wl.EPS))
+    got = host_u8(fp8.quant_rmsnorm(dev_x(x), bf16_dev(g), float(s_act), wl.EPS))
     _assert_codes_equal(got, oracle.quant_rmsnorm(x, g, wl.EPS, s_act), "infinite gamma")
 
 
