@@ -524,7 +524,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
 // depends on K only), the MFMA sequence and the fixed-order reduction are
 // those of the other kernels of this file, so for a given M every kernel
 // choice gives the same bits.
-constexpr int XM_RES = 0, XM_STREAM = 1;
+// XM_LDS (M <= 8): the resident fragments come through LDS: one 1 KB
+// direct-to-LDS load per chunk (x_q rows 0..7) issued before the weight
+// stream, read into registers once the first chunk has landed.  Register
+// loads issued before the stream made the compiler wait for every
+// outstanding load (the whole first ring fill) before the first chunk.
+constexpr int XM_RES = 0, XM_STREAM = 1, XM_LDS = 2;
 
 // The A fragment (row r, logical pieces g and g + 4) of a staged weight chunk.
 // The pointer is restrict-qualified: this read never touches a slot with
@@ -535,6 +540,14 @@ __device__ __forceinline__ v8i slot_afrag(const uint8_t* __restrict__ slot, int 
     const uint8_t* ws = slot + r * kChunk;
     return pack(*reinterpret_cast<const uint4*>(ws + wswz(r, g) * 16),
                 *reinterpret_cast<const uint4*>(ws + wswz(r, g + 4) * 16));
+}
+
+// The B fragment (x_q row `row`, pieces g and g + 4) of a chunk staged in LDS
+// as 8 rows x 128 bytes (restrict, as slot_afrag).
+__device__ __forceinline__ v8i lds_bfrag(const uint8_t* __restrict__ base, int row, int g)
+{
+    return pack(*reinterpret_cast<const uint4*>(base + row * kChunk + g * 16),
+                *reinterpret_cast<const uint4*>(base + row * kChunk + (g + 4) * 16));
 }
 
 // B fragments of chunk `chunk` for the MT B tiles (rows mt*16 + r, bytes 16g
@@ -577,6 +590,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw, int sw_lds)
 {
     static_assert(XM == XM_STREAM || CPW > 0, "resident fragments need a compile-time chunk count");
+    static_assert(XM != XM_LDS || MT == 1, "fragments through LDS: M <= 8");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -599,7 +613,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
         }
     };
     const int cw = XM == XM_STREAM ? cpw : CPW;         // chunks per wave and tile
-    // LDS: [partials] [W rings of S 2 KB slots] [DEFER, sw_lds: weight scales].
+    // LDS: [partials] [W rings of S 2 KB slots] [XM_LDS: W x CPW x 1 KB of x_q]
+    // [DEFER, sw_lds: weight scales].
     // partials: [2][W][MT][64], or with DEFER [tiles_max][W][MT][mp] (reduced
     // once, at the end; for M <= 8 only the 32 lanes holding columns m < 8).
     const int mp = MT == 1 && M <= 8 ? 32 : 64;
@@ -607,7 +622,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     v4f* red = reinterpret_cast<v4f*>(smem);
     const int64_t red_elems = DEFER ? (int64_t)tiles_max * W * MT * mp : (int64_t)2 * W * MT * 64;
     uint8_t* ring = reinterpret_cast<uint8_t*>(red + red_elems) + wave * S * 2048;
-    float* swl = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(red + red_elems) + W * S * 2048);
+    uint8_t* bxl = reinterpret_cast<uint8_t*>(red + red_elems) + W * S * 2048;
+    float* swl = reinterpret_cast<float*>(bxl + (XM == XM_LDS ? W * CPW * 1024 : 0));
     const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
     // this lane's two rows of a weight chunk (instruction i: row 8i + lane/8), logical piece
     const int lrow = lane >> 3;
@@ -671,6 +687,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     if constexpr (XM == XM_RES) {
 #pragma unroll
         for (int c = 0; c < CPW; ++c) load_bfrag<MT>(bx[c], rx, wave + c * W, wave + c * W < nchunks, r, g, M, K);
+    } else if constexpr (XM == XM_LDS) {
+        // chunk c of this wave, x_q rows 0..7: lane -> row lane / 8, piece lane % 8
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            const int chunk = wave + c * W, xrow = lane >> 3;
+            const uint32_t o = chunk < nchunks && xrow < M
+                                   ? (uint32_t)(xrow * K + chunk * kChunk + (lane & 7) * 16) : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(bxl + (wave * CPW + c) * 1024), 16, (int)o, 0,
+                                                     0, 0);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -720,6 +746,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
         for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
     };
 
+    if constexpr (XM == XM_LDS) {
+        // the fragments landed (only the ring fill may be in flight); rows
+        // 8..15 of the B tile repeat rows 0..7 (their columns are never kept)
+        __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT(2 * S));
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) bx[c][0] = lds_bfrag(bxl + (wave * CPW + c) * 1024, r & 7, g);
+    }
     if constexpr (XM == XM_STREAM) {
         // Whole ring cycles: positions past `total` load zeros and add zeros, and
         // a tile past my_tiles is not kept (an early exit from the cycle would
@@ -917,10 +950,14 @@ bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p)
     for (const auto& o : order)
         if (bytes(o.S, o.df) <= 160 * 1024 && (o.df || p->xm != XM_STREAM)) {
             const size_t swb = (size_t)(tiles_max + 3) / 4 * 256;   // DEFER: the weight scales, where they fit
+            // M <= 8: the fragments through LDS where they fit beside this ring
+            const size_t xlb = (size_t)W * cpw * 1024;
+            if (res && M <= 8 && bytes(o.S, o.df) + xlb <= 160 * 1024) p->xm = XM_LDS;
+            const size_t base = bytes(o.S, o.df) + (p->xm == XM_LDS ? xlb : 0);
             p->S = o.S;
             p->defer = o.df;
-            p->sw_lds = o.df && bytes(o.S, o.df) + swb <= 160 * 1024;
-            p->lds = bytes(o.S, o.df) + (p->sw_lds ? swb : 0);
+            p->sw_lds = o.df && base + swb <= 160 * 1024;
+            p->lds = base + (p->sw_lds ? swb : 0);
             return true;
         }
     return false;
@@ -973,7 +1010,10 @@ bool try_rx(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
     RxPlan p;
     if (!plan_rx(M64, N, K, &p)) return false;
     const int M = (int)M64, nchunks = (int)(K / kChunk);
-    if (p.xm == XM_RES) {
+    if (p.xm == XM_LDS) {
+        if (p.cpw == 4) dispatch_rx<1, XM_LDS, 4>(FP8MM_RX_ARGS);
+        else dispatch_rx<1, XM_LDS, 5>(FP8MM_RX_ARGS);
+    } else if (p.xm == XM_RES) {
         if (p.mt == 1 && p.cpw == 4) dispatch_rx<1, XM_RES, 4>(FP8MM_RX_ARGS);
         else if (p.mt == 1) dispatch_rx<1, XM_RES, 5>(FP8MM_RX_ARGS);
         else if (p.cpw == 4) dispatch_rx<2, XM_RES, 4>(FP8MM_RX_ARGS);
