@@ -524,11 +524,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
 // depends on K only), the MFMA sequence and the fixed-order reduction are
 // those of the other kernels of this file, so for a given M every kernel
 // choice gives the same bits.
-// XM_LDS (M <= 8): the resident fragments come through LDS: one 1 KB
-// direct-to-LDS load per chunk (x_q rows 0..7) issued before the weight
-// stream, read into registers once the first chunk has landed.  Register
-// loads issued before the stream made the compiler wait for every
-// outstanding load (the whole first ring fill) before the first chunk.
+// XM_LDS (M <= 16): the resident fragments come through LDS: per chunk one
+// 1 KB direct-to-LDS load per 8 x_q rows (8 rows at M <= 8, else 16) issued
+// before the weight stream, read into registers once the first chunk has
+// landed.  Register loads issued before the stream made the compiler wait
+// for every outstanding load (the whole first ring fill) before the first
+// chunk.
 constexpr int XM_RES = 0, XM_STREAM = 1, XM_LDS = 2;
 
 // The A fragment (row r, logical pieces g and g + 4) of a staged weight chunk.
@@ -590,7 +591,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw, int sw_lds)
 {
     static_assert(XM == XM_STREAM || CPW > 0, "resident fragments need a compile-time chunk count");
-    static_assert(XM != XM_LDS || MT == 1, "fragments through LDS: M <= 8");
+    static_assert(XM != XM_LDS || MT == 1, "fragments through LDS: M <= 16");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -613,7 +614,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
         }
     };
     const int cw = XM == XM_STREAM ? cpw : CPW;         // chunks per wave and tile
-    // LDS: [partials] [W rings of S 2 KB slots] [XM_LDS: W x CPW x 1 KB of x_q]
+    // LDS: [partials] [W rings of S 2 KB slots] [XM_LDS: W x CPW chunks of xr x_q rows]
     // [DEFER, sw_lds: weight scales].
     // partials: [2][W][MT][64], or with DEFER [tiles_max][W][MT][mp] (reduced
     // once, at the end; for M <= 8 only the 32 lanes holding columns m < 8).
@@ -622,8 +623,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     v4f* red = reinterpret_cast<v4f*>(smem);
     const int64_t red_elems = DEFER ? (int64_t)tiles_max * W * MT * mp : (int64_t)2 * W * MT * 64;
     uint8_t* ring = reinterpret_cast<uint8_t*>(red + red_elems) + wave * S * 2048;
+    const int xr = M <= 8 ? 8 : 16;                     // XM_LDS: x_q rows staged per chunk
     uint8_t* bxl = reinterpret_cast<uint8_t*>(red + red_elems) + W * S * 2048;
-    float* swl = reinterpret_cast<float*>(bxl + (XM == XM_LDS ? W * CPW * 1024 : 0));
+    float* swl = reinterpret_cast<float*>(bxl + (XM == XM_LDS ? W * CPW * xr * kChunk : 0));
     const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
     // this lane's two rows of a weight chunk (instruction i: row 8i + lane/8), logical piece
     const int lrow = lane >> 3;
@@ -688,15 +690,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
 #pragma unroll
         for (int c = 0; c < CPW; ++c) load_bfrag<MT>(bx[c], rx, wave + c * W, wave + c * W < nchunks, r, g, M, K);
     } else if constexpr (XM == XM_LDS) {
-        // chunk c of this wave, x_q rows 0..7: lane -> row lane / 8, piece lane % 8
+        // chunk c of this wave, x_q rows 8h .. 8h + 7: lane -> row 8h + lane / 8, piece lane % 8
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            const int chunk = wave + c * W, xrow = lane >> 3;
-            const uint32_t o = chunk < nchunks && xrow < M
-                                   ? (uint32_t)(xrow * K + chunk * kChunk + (lane & 7) * 16) : kOob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(bxl + (wave * CPW + c) * 1024), 16, (int)o, 0,
-                                                     0, 0);
-        }
+        for (int c = 0; c < CPW; ++c)
+            for (int h = 0; h < xr / 8; ++h) {
+                const int chunk = wave + c * W, xrow = 8 * h + (lane >> 3);
+                const uint32_t o = chunk < nchunks && xrow < M
+                                       ? (uint32_t)(xrow * K + chunk * kChunk + (lane & 7) * 16) : kOob;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (lds_void*)(bxl + (wave * CPW + c) * xr * kChunk + h * 1024), 16, (int)o, 0, 0, 0);
+            }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -747,11 +750,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     };
 
     if constexpr (XM == XM_LDS) {
-        // the fragments landed (only the ring fill may be in flight); rows
-        // 8..15 of the B tile repeat rows 0..7 (their columns are never kept)
+        // the fragments landed (only the ring fill may be in flight); at
+        // M <= 8 rows 8..15 of the B tile repeat rows 0..7 (their columns are
+        // never kept)
         __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT(2 * S));
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) bx[c][0] = lds_bfrag(bxl + (wave * CPW + c) * 1024, r & 7, g);
+        for (int c = 0; c < CPW; ++c) bx[c][0] = lds_bfrag(bxl + (wave * CPW + c) * xr * kChunk, r & (xr - 1), g);
     }
     if constexpr (XM == XM_STREAM) {
         // Whole ring cycles: positions past `total` load zeros and add zeros, and
@@ -947,19 +951,22 @@ bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p)
     };
     static const struct { int S; bool df; } order[] = {{6, true}, {6, false}, {4, true}, {4, false}, {3, true},
                                                        {3, false}, {2, true}, {2, false}};
-    for (const auto& o : order)
-        if (bytes(o.S, o.df) <= 160 * 1024 && (o.df || p->xm != XM_STREAM)) {
-            const size_t swb = (size_t)(tiles_max + 3) / 4 * 256;   // DEFER: the weight scales, where they fit
-            // M <= 8: the fragments through LDS where they fit beside this ring
-            const size_t xlb = (size_t)W * cpw * 1024;
-            if (res && M <= 8 && bytes(o.S, o.df) + xlb <= 160 * 1024) p->xm = XM_LDS;
-            const size_t base = bytes(o.S, o.df) + (p->xm == XM_LDS ? xlb : 0);
-            p->S = o.S;
-            p->defer = o.df;
-            p->sw_lds = o.df && base + swb <= 160 * 1024;
-            p->lds = base + (p->sw_lds ? swb : 0);
-            return true;
-        }
+    // M <= 16 with resident fragments: through LDS (XM_LDS) where they fit
+    // beside some ring, even one shallower than the register path's (measured
+    // faster on every decode shape); else in registers
+    const size_t xl = res && M <= 16 ? (size_t)W * cpw * (M <= 8 ? 8 : 16) * kChunk : 0;
+    for (const size_t xlb : {xl, (size_t)0})
+        for (const auto& o : order)
+            if (bytes(o.S, o.df) + xlb <= 160 * 1024 && (o.df || p->xm != XM_STREAM)) {
+                const size_t swb = (size_t)(tiles_max + 3) / 4 * 256;   // DEFER: the weight scales, where they fit
+                const size_t base = bytes(o.S, o.df) + xlb;
+                if (xlb) p->xm = XM_LDS;
+                p->S = o.S;
+                p->defer = o.df;
+                p->sw_lds = o.df && base + swb <= 160 * 1024;
+                p->lds = base + (p->sw_lds ? swb : 0);
+                return true;
+            }
     return false;
 }
 

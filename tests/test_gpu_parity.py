@@ -427,6 +427,9 @@ def test_both_arms_agree_with_oracle(fp8, M):
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 16), (3, 48, 48), (17, 32, 272), (33, 64, 400), (65, 80, 144),
                                    (129, 144, 1040), (257, 272, 2064), (300, 1040, 17408),
+                                   # x_q fragments staged through LDS: 8 rows (M = 5) and 16 rows (M = 11, 13),
+                                   # with a balanced last round (4112 = 257 tiles) and 5 waves (K = 3072)
+                                   (5, 10240, 5120), (13, 4112, 5120), (11, 6144, 3072),
                                    # K % 1024 == 0 but the ring kernel's LDS plan does not fit: the generic kernel
                                    (1, 33168, 32768), (12, 10240, 32768)])
 def test_ragged_shapes_both_arms(fp8, M, N, K):
