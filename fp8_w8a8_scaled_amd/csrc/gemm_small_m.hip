@@ -217,10 +217,14 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 // for the tile: a tile starting at a multiple of 16 lies in one shard), or
 // with lane_shard that of each 4-row group (such a group never straddles two
 // shards: shard starts are multiples of 16).  m_off: the first output row of
-// the MFMA B tile (16 for the second of two).
-__device__ __forceinline__ void reduce_tile(const v4f* red, int stride, int slot, int W, int64_t n0, int64_t nend,
+// the MFMA B tile (16 for the second of two).  srl: the activation scales of
+// the output rows in LDS, or null (per-tensor s_act, or sh's per-row scales
+// read from memory).
+__device__ __forceinline__ void reduce_tile(const v4f* __restrict__ red, int stride, int slot, int W, int64_t n0,
+                                            int64_t nend,
                                             float s_act, const float4 sw, const ShardTable& sh, int M, int lane,
-                                            bool lane_shard = false, int m_off = 0)
+                                            bool lane_shard = false, int m_off = 0,
+                                            const float* __restrict__ srl = nullptr)
 {
     const int m = m_off + (lane & 15);
     const int64_t n = n0 + 4 * (lane >> 4);
@@ -230,7 +234,7 @@ __device__ __forceinline__ void reduce_tile(const v4f* red, int stride, int slot
         const v4f p = red[w * stride + slot];
         s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
     }
-    const float sa = row_scale(sh, m, s_act);
+    const float sa = srl ? srl[m] : row_scale(sh, m, s_act);
     store_out4_any(sh, lane_shard ? n : n0, m, n, (s.x * sa) * sw.x, (s.y * sa) * sw.y, (s.z * sa) * sw.z,
                    (s.w * sa) * sw.w);
 }
@@ -551,6 +555,9 @@ __device__ __forceinline__ v8i lds_bfrag(const uint8_t* __restrict__ base, int r
                 *reinterpret_cast<const uint4*>(base + row * kChunk + (g + 4) * 16));
 }
 
+// Four weight scales staged in LDS (restrict, as slot_afrag).
+__device__ __forceinline__ float4 lds_f4(const float* __restrict__ p) { return *reinterpret_cast<const float4*>(p); }
+
 // B fragments of chunk `chunk` for the MT B tiles (rows mt*16 + r, bytes 16g
 // and 64 + 16g of the chunk); zeros for rows past M or a chunk that does not
 // exist (an offset past the end of the buffer).
@@ -588,7 +595,7 @@ __device__ __forceinline__ void put_partial(v4f* __restrict__ dst, v4f v) { *dst
 template <int S, int MT, int XM, int CPW, bool BAL, bool DEFER>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act, const float* __restrict__ s_w,
-    ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw, int sw_lds)
+    ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw)
 {
     static_assert(XM == XM_STREAM || CPW > 0, "resident fragments need a compile-time chunk count");
     static_assert(XM != XM_LDS || MT == 1, "fragments through LDS: M <= 16");
@@ -615,7 +622,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     };
     const int cw = XM == XM_STREAM ? cpw : CPW;         // chunks per wave and tile
     // LDS: [partials] [W rings of S 2 KB slots] [XM_LDS: W x CPW chunks of xr x_q rows]
-    // [DEFER, sw_lds: weight scales].
+    // [activation scales of the 64 output rows] [weight scales of the
+    // workgroup's tiles, 16 per tile].
     // partials: [2][W][MT][64], or with DEFER [tiles_max][W][MT][mp] (reduced
     // once, at the end; for M <= 8 only the 32 lanes holding columns m < 8).
     const int mp = MT == 1 && M <= 8 ? 32 : 64;
@@ -625,7 +633,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     uint8_t* ring = reinterpret_cast<uint8_t*>(red + red_elems) + wave * S * 2048;
     const int xr = M <= 8 ? 8 : 16;                     // XM_LDS: x_q rows staged per chunk
     uint8_t* bxl = reinterpret_cast<uint8_t*>(red + red_elems) + W * S * 2048;
-    float* swl = reinterpret_cast<float*>(bxl + (XM == XM_LDS ? W * CPW * xr * kChunk : 0));
+    float* srl = reinterpret_cast<float*>(bxl + (XM == XM_LDS ? W * CPW * xr * kChunk : 0));
+    float* swl = srl + 64;
     const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
     // this lane's two rows of a weight chunk (instruction i: row 8i + lane/8), logical piece
     const int lrow = lane >> 3;
@@ -668,12 +677,23 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     auto a_frag = [&](int slot) { return slot_afrag(ring + slot * 2048, r, g); };
 
     const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
-    if (DEFER && sw_lds) {
+    // The activation scale of each output row into LDS: the per-row scales
+    // with one direct-to-LDS load (wave 0), else s_act.  A global load of them
+    // inside the stream would make the compiler drain the ring around it.
+    if (sh.s_rows) {
+        if (wave == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                weight_rsrc(reinterpret_cast<const uint8_t*>(sh.s_rows), (int64_t)M * 4), (lds_void*)srl, 4,
+                lane < M ? lane * 4 : (int)kOob, 0, 0, 0);
+    } else if (threadIdx.x < 64) {
+        srl[threadIdx.x] = s_act;
+    }
+    {
         // The weight scales of this workgroup's tiles into LDS, 16 per tile
         // (zeros past a tile's rows), one 4-byte direct-to-LDS load per lane,
-        // issued ahead of the stream: the final reduction then reads them from
-        // LDS instead of waiting on memory after the last chunk (where the LDS
-        // has room for them).
+        // issued ahead of the stream: the reductions then read them from LDS
+        // (a global load inside the stream made the compiler drain the ring
+        // around it).
         for (int t0 = 4 * wave; t0 < tiles_max; t0 += 4 * W) {
             const int t = t0 + (lane >> 4);
             int rt, re;
@@ -710,21 +730,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // weight scales of tile u for this lane's four rows (tile-by-tile reduction
-    // only; loaded in the loop iteration that uses them, so the compiler can
-    // count the loads issued after them instead of waiting for all)
-    auto tile_sw = [&](int t) {
-        int rt, re;
-        tile_rows(t, rt, re);
-        const int n = rt + 4 * g;
-        const uint32_t o = t < my_tiles && n < re ? (uint32_t)n * 4 : kOob;
-        return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, 0, 0);
-    };
     v4f acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
     // end of tile u: keep its partials (DEFER) or reduce it now
-    auto tile_done = [&](int u, const u32x4_t& swu) {
+    auto tile_done = [&](int u) {
         if constexpr (DEFER) {
             if (mp == 64 || (lane & 15) < 8)
 #pragma unroll
@@ -737,12 +747,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
             int rt, re;
             tile_rows(u, rt, re);
             if (wave == 0) {
-                const float4 sw4 = make_float4(__uint_as_float(swu[0]), __uint_as_float(swu[1]),
-                                               __uint_as_float(swu[2]), __uint_as_float(swu[3]));
+                const float4 sw4 = lds_f4(swl + u * 16 + 4 * g);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     reduce_tile(rb + mt * 64, MT * 64, lane, W, rt, re, s_act, sw4, sh, M, lane, BAL && u >= FR,
-                                16 * mt);
+                                16 * mt, srl);
             }
         }
 #pragma unroll
@@ -779,7 +788,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
                 fire(nx, s);
                 load_bfrag<MT>(bx[s], rx, nx.chunk, nx.ok, r, g, M, K);
                 if (++c == cw) {
-                    if (u < my_tiles) tile_done(u, u32x4_t{0u, 0u, 0u, 0u});
+                    if (u < my_tiles) tile_done(u);
                     c = 0;
                     ++u;
                 }
@@ -787,8 +796,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
         }
     } else {
         int slot = 0;
-        for (int u = 0; u < my_tiles; ++u) {
-            u32x4_t swu{0u, 0u, 0u, 0u};
+        auto tile_body = [&](int u) {
 #pragma unroll
             for (int c = 0; c < CPW; ++c) {
                 const Pend nx = prep();
@@ -801,11 +809,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
                                                                               0);
                 __builtin_amdgcn_s_waitcnt(FP8MM_SM_LGKM0);
                 fire(nx, slot);
-                if (!DEFER && c == 0) swu = tile_sw(u);  // this tile's scales, behind its first refill
                 slot = slot + 1 == S ? 0 : slot + 1;
             }
-            tile_done(u, swu);
+            tile_done(u);
+        };
+        // Register fragments: the first tile outside the loop.  Their first
+        // uses are then straight-line code, where the compiler counts the
+        // loads issued after them; at the head of a loop that uses them it
+        // waited for every outstanding load (the whole first ring fill).
+        int u0 = 0;
+        if constexpr (XM == XM_RES) {
+            tile_body(0);
+            u0 = 1;
         }
+        for (int u = u0; u < my_tiles; ++u) tile_body(u);
     }
     __builtin_amdgcn_s_waitcnt(0);                      // no load outlives the workgroup
     if constexpr (DEFER) {                               // one barrier, then every wave reduces
@@ -817,9 +834,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
             int n0, re;
             tile_rows(uu, n0, re);
             if (n0 + 4 * (l >> 4) >= re) continue;       // another workgroup's rows
-            const float4 sw4 = sw_lds ? *reinterpret_cast<const float4*>(swl + uu * 16 + 4 * (l >> 4))
-                                      : tile_scales(rs, n0 + 4 * (l >> 4));
-            reduce_tile(red + (uu * W * MT + mt) * mp, MT * mp, ps, W, n0, re, s_act, sw4, sh, M, l, BAL, 16 * mt);
+            reduce_tile(red + (uu * W * MT + mt) * mp, MT * mp, ps, W, n0, re, s_act, lds_f4(swl + uu * 16 + 4 * (l >> 4)),
+                        sh, M, l, BAL, 16 * mt, srl);
         }
     }
 }
@@ -923,7 +939,7 @@ bool try_ring(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_
 // deepest ring that fits, deferred reduction preferred.
 struct RxPlan {
     int xm, mt, cpw, S;
-    bool bal, defer, sw_lds;
+    bool bal, defer;
     size_t lds;
     unsigned G, W;
 };
@@ -955,16 +971,14 @@ bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p)
     // beside some ring, even one shallower than the register path's (measured
     // faster on every decode shape); else in registers
     const size_t xl = res && M <= 16 ? (size_t)W * cpw * (M <= 8 ? 8 : 16) * kChunk : 0;
+    const size_t swb = 256 + (size_t)(tiles_max + 3) / 4 * 256; // the rows' and the tiles' scales
     for (const size_t xlb : {xl, (size_t)0})
         for (const auto& o : order)
-            if (bytes(o.S, o.df) + xlb <= 160 * 1024 && (o.df || p->xm != XM_STREAM)) {
-                const size_t swb = (size_t)(tiles_max + 3) / 4 * 256;   // DEFER: the weight scales, where they fit
-                const size_t base = bytes(o.S, o.df) + xlb;
+            if (bytes(o.S, o.df) + xlb + swb <= 160 * 1024 && (o.df || p->xm != XM_STREAM)) {
                 if (xlb) p->xm = XM_LDS;
                 p->S = o.S;
                 p->defer = o.df;
-                p->sw_lds = o.df && base + swb <= 160 * 1024;
-                p->lds = base + (p->sw_lds ? swb : 0);
+                p->lds = bytes(o.S, o.df) + xlb + swb;
                 return true;
             }
     return false;
@@ -982,7 +996,7 @@ void launch_rx(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float s_ac
     }();
     (void)attr;
     hipLaunchKernelGGL((k_gemm_small_m_rx<S, MT, XM, CPW, BAL, DEFER>), dim3(p.G), dim3(64 * p.W), p.lds, stream, xq,
-                       wq, s_act, s_w, sh, M, N, K, nchunks, p.cpw, (int)p.sw_lds);
+                       wq, s_act, s_w, sh, M, N, K, nchunks, p.cpw);
 }
 
 template <int MT, int XM, int CPW, bool BAL>
