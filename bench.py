@@ -961,7 +961,7 @@ def pmc_driver(fp8, which, meta_dir):
         torch.cuda.synchronize()
         for i in range(3):
             fp8.scaled_mm(xq, copies[4 * i + 1], s_act, sw, out=out)
-        kernel = "k_gemm_small_m_ring"
+        kernel = "k_gemm_small_m_rx"
     elif which == "prefill_mfma":
         # the prefill gate_up and down GEMMs, 3 launches each, for the MFMA counters
         M, K, N, K2, N2 = 6576, 5120, 34816, 17408, 5120
@@ -1047,9 +1047,9 @@ def main():
                    "step": "static quant [M,K] + scaled GEMM via dispatcher (small-M arm), graph-replayed",
                    "timing": f"median over {REPLAYS} replays of a graph of {a.steps} steps",
                    "algorithmic_bytes_per_step": head["algorithmic_bytes_per_step"]},
-        "roofline": {"bound": "hbm", "kernel": "k_gemm_small_m_ring", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "k_gemm_small_m_rx", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": load_traffic(f"decode_gemm_M{a.M}_K5120_N10240_pmc", "k_gemm_small_m_ring"),
+                     "traffic": load_traffic(f"decode_gemm_M{a.M}_K5120_N10240_pmc", "k_gemm_small_m_rx"),
                      "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_us": head["gemm_us"],
                      "min_launch_us": head["gemm_min_us"],
                      "timing": f"median over {REPLAYS} replays of a graph of {a.steps} back-to-back launches"},
