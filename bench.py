@@ -87,7 +87,7 @@ def _args():
 
 # The sources each profiled kernel is compiled from (its own file and the
 # shared device header); a traffic figure is valid only for these bytes.
-KERNEL_SOURCES = {"k_gemm_small_m": ("gemm_small_m.hip", "device_common.h", "out_store.h", "internal.h"),
+KERNEL_SOURCES = {"k_gemm_small_m": ("gemm_small_m.hip", "act_tables.h", "device_common.h", "out_store.h", "internal.h"),
                   "k_gemm_large_m": ("gemm_large_m.hip", "device_common.h", "out_store.h", "internal.h"),
                   "k_silu_mul_quant": ("quant.hip", "device_common.h", "act_tables.h", "internal.h")}
 

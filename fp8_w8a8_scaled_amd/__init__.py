@@ -52,6 +52,9 @@ _quant_rmsnorm = _decl("fp8_quant_rmsnorm", [_P, _I64, _P, _F32, _F32, _P, _I64,
 _scaled_mm = _decl("fp8_scaled_mm", [_P, _P, _F32, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P])
 _scaled_mm_arm = _decl("fp8_scaled_mm_arm", [_P, _P, _F32, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _SZ, _P])
 _scaled_mm_merged = _decl("fp8_scaled_mm_merged", [_P, _P, _F32, _P, ctypes.POINTER(Shard), _I32, _I64, _I64, _P, _SZ, _P])
+_quant_scaled_mm_fused = _decl("fp8_quant_scaled_mm_fused", [_I64, _I64, _I64, _I64, _F32])
+_quant_scaled_mm_merged = _decl("fp8_quant_scaled_mm_merged",
+                                [_P, _I64, _F32, _P, _P, _P, ctypes.POINTER(Shard), _I32, _I64, _I64, _P, _SZ, _P])
 _quant_per_token = _decl("fp8_quant_per_token", [_P, _I64, _P, _F32, _P, _P, _I64, _I64, _P])
 _scaled_mm_per_token = _decl("fp8_scaled_mm_per_token", [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P])
 _scaled_mm_merged_per_token = _decl("fp8_scaled_mm_merged_per_token",
@@ -376,6 +379,50 @@ def scaled_mm_merged(x_q: torch.Tensor, w_q: torch.Tensor, s_act: float, s_w: to
     _check(fn(_ptr(x_q), _ptr(w_q), float(s_act), _ptr(s_w), arr, len(shard_sizes), M, K,
               _ptr(ws), wsb, _stream(x_q)), "fp8_scaled_mm_merged")
     return list(outs)
+
+
+def quant_scaled_mm_merged(x: torch.Tensor, s_act: float, w_q: torch.Tensor, s_w: torch.Tensor,
+                           shard_sizes: Sequence[int], outs: Optional[Sequence[torch.Tensor]] = None,
+                           x_q: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Static quant of bf16 x [M, K] and the merged GEMM on the codes, one
+    launch where the small-M kernel takes the shape (M <= 8): returns
+    (list of bf16 [M, n_i] outputs, x_q uint8 [M, K])."""
+    _need(x.is_cuda and x.dtype == torch.bfloat16, "x must be a bf16 CUDA tensor")
+    ldx = _row_major(x, "x")
+    M, K = x.shape
+    w_q = _codes(w_q, "w_q")
+    _need(w_q.is_cuda and w_q.dim() == 2 and w_q.shape[1] == K and w_q.is_contiguous(),
+          "w_q must be contiguous E4M3 codes [N, K]")
+    _need(s_w.is_cuda and s_w.dtype == torch.float32 and s_w.is_contiguous() and s_w.numel() == w_q.shape[0],
+          "s_w must be a contiguous f32 CUDA tensor of N elements")
+    _need(sum(shard_sizes) == w_q.shape[0], "shard sizes must sum to the weight rows")
+    _need(1 <= len(shard_sizes) <= MAX_SHARDS, f"1..{MAX_SHARDS} shards")
+    if x_q is None:
+        x_q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    x_q = _codes(x_q, "x_q")
+    _need(x_q.is_contiguous() and tuple(x_q.shape) == (M, K), "x_q must be contiguous uint8 [M, K]")
+    if outs is None:
+        outs = [torch.empty((M, n), dtype=torch.bfloat16, device=x.device) for n in shard_sizes]
+    arr = (Shard * len(shard_sizes))()
+    for i, (n, o) in enumerate(zip(shard_sizes, outs)):
+        _need(o.dtype == torch.bfloat16 and o.is_cuda and o.shape == (M, n), "shard outputs must be bf16 [M, n_i]")
+        arr[i] = Shard(int(n), o.data_ptr(), _row_major(o, "out"))
+    ws, wsb = _workspace(M, w_q.shape[0], K, x.device, workspace)
+    _check(_quant_scaled_mm_merged(_ptr(x), ldx, float(s_act), _ptr(x_q), _ptr(w_q), _ptr(s_w), arr,
+                                   len(shard_sizes), M, K, _ptr(ws), wsb, _stream(x)), "fp8_quant_scaled_mm_merged")
+    return list(outs), x_q
+
+
+def quant_scaled_mm_fused(M: int, N: int, K: int, ldx: Optional[int] = None, s_act: float = 1.0) -> bool:
+    """Whether quant_scaled_mm_merged runs as one launch for this shape."""
+    return bool(_quant_scaled_mm_fused(M, N, K, K if ldx is None else ldx, float(s_act)))
+
+
+def quant_scaled_mm(x: torch.Tensor, s_act: float, w_q: torch.Tensor, s_w: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, x_q: Optional[torch.Tensor] = None):
+    """Static quant of bf16 x and one projection: returns (bf16 [M, N], x_q)."""
+    outs, xq = quant_scaled_mm_merged(x, s_act, w_q, s_w, [w_q.shape[0]], None if out is None else [out], x_q)
+    return outs[0], xq
 
 
 # ------------------------------------------------------ per-token scales --

@@ -143,6 +143,20 @@ __device__ __host__ __forceinline__ uint32_t code_band_lo(float s_act)
     return (u + 0xffffu) >> 16;                    // round the magnitude up to bf16
 }
 
+// E4M3 code of a positive fp32 q in [2^-12, 2^10) (the quotients of a band
+// table), rounded to nearest even and saturating as f32_to_e4m3_sat does, with
+// no branches: below 2^-6 the subnormal grid m 2^-9 (q 2^9, an exact scaling,
+// rounded to the nearest even integer), else the fp32 mantissa rounded to 3
+// bits at bit 20 and rebiased, clamped to the largest finite code.
+__device__ __host__ __forceinline__ uint32_t e4m3_code_band(float q)
+{
+    uint32_t a;
+    __builtin_memcpy(&a, &q, 4);
+    const uint32_t cn = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+    const uint32_t cs = (uint32_t)__builtin_rintf(q * 512.0f);
+    return a < 0x3c800000u ? cs : (cn < 0x7eu ? cn : 0x7eu);
+}
+
 __device__ __host__ __forceinline__ uint32_t code_table_entry(uint32_t h, uint32_t lo, float s_act)
 {
     const uint32_t a = h & 0x7fffu, sg = (h >> 8) & 0x80u;
@@ -168,7 +182,7 @@ __device__ __host__ __forceinline__ void fill_band_table(uint8_t* tab, uint32_t 
         const uint32_t pw = (127u + (uint32_t)(e >> 7)) << 23;   // 2^(e / 128)
         float p2;
         __builtin_memcpy(&p2, &pw, 4);
-        tab[1 + e] = (uint8_t)f32_to_e4m3_sat(q0 * p2);
+        tab[1 + e] = (uint8_t)e4m3_code_band(q0 * p2);
     }
 }
 
@@ -195,6 +209,25 @@ __device__ __forceinline__ uint2 quant8_band(uint32_t w0, uint32_t w1, uint32_t 
         o[q] = c | (__builtin_amdgcn_perm(w[2 * q + 1], w[2 * q], 0x07050301u) & 0x80808080u);
     }
     return make_uint2(o[0], o[1]);
+}
+
+// The quotient a / s, a = |h| of a bf16 value, as the plain static quant
+// rounds it (fp32, to nearest even), without a division: r = fl32(1 / s), the
+// estimate q0 = fl32(a r), its remainder a - q0 s exact through one fused
+// multiply-add, and one correction fl32(q0 + rem r).  With r correctly
+// rounded and q0 within an ulp of a / s, that correction is the correctly
+// rounded quotient (Markstein's theorem on division by fused multiply-add,
+// valid while nothing overflows or underflows; exhaustively compared with the
+// division for every bf16 a and thousands of scales in [2^-100, 2^100]).
+// Magnitudes above F = fl32(448 s) are clamped to F first: their codes
+// saturate either way (the quotient of F stays below 464, which rounds to
+// 448), and no product overflows.  A NaN a compares false and stays NaN.
+// Quotients that underflow are below 2^-26 here (s >= 2^-100), code 0 either way.
+__device__ __host__ __forceinline__ float quant_quotient(float a, float s, float r, float F)
+{
+    const float c = a > F ? F : a;
+    const float q0 = c * r;
+    return __builtin_fmaf(__builtin_fmaf(-q0, s, c), r, q0);
 }
 
 // The band-table codes (without sign) of the two bf16 magnitudes in word h:

@@ -32,6 +32,7 @@
 //    fragments loaded straight into registers.
 // W and the chunk assignment depend on K only, so every column's summation
 // order is the same for a merged call and a per-shard call: bitwise identical.
+#include "act_tables.h"
 #include "device_common.h"
 #include "internal.h"
 #include "out_store.h"
@@ -534,7 +535,54 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
 // landed.  Register loads issued before the stream made the compiler wait
 // for every outstanding load (the whole first ring fill) before the first
 // chunk.
-constexpr int XM_RES = 0, XM_STREAM = 1, XM_LDS = 2;
+// XM_QLDS (M <= 8): XM_LDS with the fragments quantized in the kernel from the
+// bf16 activation (the static quant fused into the GEMM launch): each wave
+// loads the bf16 values of its own chunks interleaved with the ring fill, one
+// chunk ahead of the weights (activation c + 1 before weight chunk c), and
+// encodes each chunk inside the fill, where issuing stalls on the full memory
+// pipe anyway: quotients by multiply and fused multiply-add, codes by the
+// hardware conversion, no table and no barrier.  Each wave stages its own
+// codes in LDS (read back by the same wave only); workgroup 0 also stores them
+// (x_q).
+constexpr int XM_RES = 0, XM_STREAM = 1, XM_LDS = 2, XM_QLDS = 3;
+
+// The bf16 activation of a fused quant + GEMM launch (XM_QLDS): rows of ldx
+// elements, and where workgroup 0 stores its E4M3 codes ([M, K], contiguous).
+// rcp = fl32(1 / s_act), sat = fl32(448 s_act): the quotient's operands.
+struct XSrc {
+    const uint16_t* x;
+    int64_t ldx;
+    uint8_t* xq_out;
+    float rcp, sat;
+};
+
+// The 16 E4M3 codes of 16 bf16 values (words of a then b; value i in bits
+// 16 (i % 2) of word i / 2) under the plain static quant: quant_quotient of
+// each magnitude, encoded two at a time by the hardware conversion (rounding
+// to nearest even like the software encoder on every magnitude up to 464,
+// which bounds the quotients here), the sign from the bf16 sign bit.  A NaN
+// magnitude gives a NaN quotient, whose code has its 7 low bits set: 0x7F
+// after the mask, with the value's sign.
+__device__ __forceinline__ uint4 quant16_div(uint4 a, uint4 b, float s, float rcp, float sat)
+{
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t h = w[2 * k + (i >> 1)];
+            q[i] = quant_quotient(__builtin_fabsf(__builtin_bit_cast(float, i & 1 ? h & 0xffff0000u : h << 16)), s,
+                                  rcp, sat);
+        }
+        int c = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        c = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], c, true);
+        o[k] = ((uint32_t)c & 0x7f7f7f7fu) | (__builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x07050301u) & 0x80808080u);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 
 // The A fragment (row r, logical pieces g and g + 4) of a staged weight chunk.
 // The pointer is restrict-qualified: this read never touches a slot with
@@ -554,6 +602,10 @@ __device__ __forceinline__ v8i lds_bfrag(const uint8_t* __restrict__ base, int r
     return pack(*reinterpret_cast<const uint4*>(base + row * kChunk + g * 16),
                 *reinterpret_cast<const uint4*>(base + row * kChunk + (g + 4) * 16));
 }
+
+// 16 codes into the fragment staging area (restrict: this area is never a
+// target of the in-flight direct-to-LDS loads).
+__device__ __forceinline__ void put_codes(uint8_t* __restrict__ dst, uint4 q) { *reinterpret_cast<uint4*>(dst) = q; }
 
 // Four weight scales staged in LDS (restrict, as slot_afrag).
 __device__ __forceinline__ float4 lds_f4(const float* __restrict__ p) { return *reinterpret_cast<const float4*>(p); }
@@ -595,10 +647,11 @@ __device__ __forceinline__ void put_partial(v4f* __restrict__ dst, v4f v) { *dst
 template <int S, int MT, int XM, int CPW, bool BAL, bool DEFER>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act, const float* __restrict__ s_w,
-    ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw)
+    ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw, XSrc xs)
 {
     static_assert(XM == XM_STREAM || CPW > 0, "resident fragments need a compile-time chunk count");
-    static_assert(XM != XM_LDS || MT == 1, "fragments through LDS: M <= 16");
+    static_assert((XM != XM_LDS && XM != XM_QLDS) || MT == 1, "fragments through LDS: M <= 16");
+    constexpr bool kLds = XM == XM_LDS || XM == XM_QLDS;   // fragments staged in LDS
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -631,9 +684,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     v4f* red = reinterpret_cast<v4f*>(smem);
     const int64_t red_elems = DEFER ? (int64_t)tiles_max * W * MT * mp : (int64_t)2 * W * MT * 64;
     uint8_t* ring = reinterpret_cast<uint8_t*>(red + red_elems) + wave * S * 2048;
-    const int xr = M <= 8 ? 8 : 16;                     // XM_LDS: x_q rows staged per chunk
+    const int xr = M <= 8 ? 8 : 16;                     // XM_LDS, XM_QLDS (8): x_q rows staged per chunk
     uint8_t* bxl = reinterpret_cast<uint8_t*>(red + red_elems) + W * S * 2048;
-    float* srl = reinterpret_cast<float*>(bxl + (XM == XM_LDS ? W * CPW * xr * kChunk : 0));
+    float* srl = reinterpret_cast<float*>(bxl + (kLds ? W * CPW * xr * kChunk : 0));
     float* swl = srl + 64;
     const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
     // this lane's two rows of a weight chunk (instruction i: row 8i + lane/8), logical piece
@@ -675,6 +728,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sl + 1024), 16, (int)pd.w1, 0, 0, kWeightCpol);
     };
     auto a_frag = [&](int slot) { return slot_afrag(ring + slot * 2048, r, g); };
+
+    // XM_QLDS: this lane's bf16 values of each of the wave's chunks (x row
+    // lane / 8, values 16 (lane % 8) .. + 15; zeros past M or past the last
+    // chunk), loaded by load_xv inside the ring fill
+    [[maybe_unused]] uint4 xv[XM == XM_QLDS ? CPW : 1][2];
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t rxb =
+        weight_rsrc(reinterpret_cast<const uint8_t*>(xs.x), XM == XM_QLDS ? ((int64_t)(M - 1) * xs.ldx + K) * 2 : 0);
+    auto load_xv = [&](int c) {
+        const int chunk = wave + c * W, xrow = lane >> 3;
+        const uint32_t o = chunk < nchunks && xrow < M
+                               ? (uint32_t)((xrow * xs.ldx + chunk * kChunk + (lane & 7) * 16) * 2) : kOob;
+        const u32x4_t lo = __builtin_amdgcn_raw_buffer_load_b128(rxb, (int)o, 0, 0);
+        const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(rxb, (int)(o + 16), 0, 0);
+        xv[c][0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        xv[c][1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    };
 
     const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
     // The activation scale of each output row into LDS: the per-row scales
@@ -721,12 +790,46 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
                     rx, (lds_void*)(bxl + (wave * CPW + c) * xr * kChunk + h * 1024), 16, (int)o, 0, 0, 0);
             }
     }
+    // XM_QLDS: chunk c's codes into the wave's own staging area (read back
+    // by the same wave only), then into its fragment; workgroup 0 also stores
+    // them to x_q
+    auto quant_chunk = [&](int c) {
+        const uint4 q = quant16_div(xv[c][0], xv[c][1], s_act, xs.rcp, xs.sat);
+        put_codes(bxl + (wave * CPW + c) * 1024 + lane * 16, q);
+        const int chunk = wave + c * W, xrow = lane >> 3;
+        if (bid == 0 && xs.xq_out && chunk < nchunks && xrow < M)
+            *reinterpret_cast<uint4*>(xs.xq_out + (int64_t)xrow * K + chunk * kChunk + (lane & 7) * 16) = q;
+        __builtin_amdgcn_s_waitcnt(FP8MM_SM_LGKM0);
+        bx[c][0] = lds_bfrag(bxl + (wave * CPW + c) * 1024, r & 7, g);
+    };
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (XM == XM_QLDS) {
+        // Issuing the fill stalls on a full memory pipe for microseconds:
+        // chunk c is encoded there, two ring slots after its activation was
+        // requested, instead of in the first tile (the weights have landed
+        // by then, and the encoding would only add to the wait).
+        load_xv(0);
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const Pend pd = prep();
-        fire(pd, s);
-        if constexpr (XM == XM_STREAM) load_bfrag<MT>(bx[s], rx, pd.chunk, pd.ok, r, g, M, K);
+        for (int s = 0; s < S; ++s) {
+            if (s + 1 < CPW) load_xv(s + 1);
+            fire(prep(), s);
+            if (s >= 2 && s - 2 < CPW) {
+                __builtin_amdgcn_sched_barrier(0);
+                quant_chunk(s - 2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int c = S + 1; c < CPW; ++c) load_xv(c);
+#pragma unroll
+        for (int c = S - 2 > 0 ? S - 2 : 0; c < CPW; ++c) quant_chunk(c);
+    } else {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const Pend pd = prep();
+            fire(pd, s);
+            if constexpr (XM == XM_STREAM) load_bfrag<MT>(bx[s], rx, pd.chunk, pd.ok, r, g, M, K);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -971,7 +1074,7 @@ bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p)
     // beside some ring, even one shallower than the register path's (measured
     // faster on every decode shape); else in registers
     const size_t xl = res && M <= 16 ? (size_t)W * cpw * (M <= 8 ? 8 : 16) * kChunk : 0;
-    const size_t swb = 256 + (size_t)(tiles_max + 3) / 4 * 256; // the rows' and the tiles' scales
+    const size_t swb = 256 + (size_t)(tiles_max + 3) / 4 * 256;   // the rows' and the tiles' scales
     for (const size_t xlb : {xl, (size_t)0})
         for (const auto& o : order)
             if (bytes(o.S, o.df) + xlb + swb <= 160 * 1024 && (o.df || p->xm != XM_STREAM)) {
@@ -984,10 +1087,10 @@ bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p)
     return false;
 }
 
-#define FP8MM_RX_ARGS p, xq, wq, s_act, s_w, sh, M, N, K, nchunks, stream
+#define FP8MM_RX_ARGS p, xq, wq, s_act, s_w, sh, M, N, K, nchunks, xs, stream
 template <int S, int MT, int XM, int CPW, bool BAL, bool DEFER>
 void launch_rx(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
-               const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, hipStream_t stream)
+               const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, const XSrc& xs, hipStream_t stream)
 {
     static const bool attr = [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_rx<S, MT, XM, CPW, BAL, DEFER>),
@@ -996,12 +1099,13 @@ void launch_rx(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float s_ac
     }();
     (void)attr;
     hipLaunchKernelGGL((k_gemm_small_m_rx<S, MT, XM, CPW, BAL, DEFER>), dim3(p.G), dim3(64 * p.W), p.lds, stream, xq,
-                       wq, s_act, s_w, sh, M, N, K, nchunks, p.cpw);
+                       wq, s_act, s_w, sh, M, N, K, nchunks, p.cpw, xs);
 }
 
 template <int MT, int XM, int CPW, bool BAL>
 void dispatch_rx_sd(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
-                    const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, hipStream_t stream)
+                    const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, const XSrc& xs,
+                    hipStream_t stream)
 {
     constexpr bool kStream = XM == XM_STREAM;   // streamed fragments: deferred reduction only
     if (p.S == 6 && p.defer) launch_rx<6, MT, XM, CPW, BAL, true>(FP8MM_RX_ARGS);
@@ -1018,20 +1122,27 @@ void dispatch_rx_sd(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float
 
 template <int MT, int XM, int CPW>
 void dispatch_rx(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
-                 const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, hipStream_t stream)
+                 const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, const XSrc& xs, hipStream_t stream)
 {
     if (p.bal) dispatch_rx_sd<MT, XM, CPW, true>(FP8MM_RX_ARGS);
     else dispatch_rx_sd<MT, XM, CPW, false>(FP8MM_RX_ARGS);
 }
 
-// Launch the register-fragment kernel if it takes this shape.
+// Launch the register-fragment kernel if it takes this shape.  With xsrc, the
+// fused static quant: only the XM_QLDS plan (M <= 8, fragments staged in LDS),
+// else false.
 bool try_rx(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh, int64_t M64,
-            int64_t N, int64_t K, hipStream_t stream)
+            int64_t N, int64_t K, hipStream_t stream, const XSrc* xsrc = nullptr)
 {
     RxPlan p;
     if (!plan_rx(M64, N, K, &p)) return false;
     const int M = (int)M64, nchunks = (int)(K / kChunk);
-    if (p.xm == XM_LDS) {
+    const XSrc xs = xsrc ? *xsrc : XSrc{nullptr, 0, nullptr, 0.0f, 0.0f};
+    if (xsrc) {
+        if (p.xm != XM_LDS || M > 8) return false;
+        if (p.cpw == 4) dispatch_rx<1, XM_QLDS, 4>(FP8MM_RX_ARGS);
+        else dispatch_rx<1, XM_QLDS, 5>(FP8MM_RX_ARGS);
+    } else if (p.xm == XM_LDS) {
         if (p.cpw == 4) dispatch_rx<1, XM_LDS, 4>(FP8MM_RX_ARGS);
         else dispatch_rx<1, XM_LDS, 5>(FP8MM_RX_ARGS);
     } else if (p.xm == XM_RES) {
@@ -1045,6 +1156,25 @@ bool try_rx(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
     return true;
 }
 #undef FP8MM_RX_ARGS
+
+bool quant_gemm_small_m_fits(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act)
+{
+    // 32-bit buffer offsets into the activation; the plain quant's code table
+    if (M < 1 || M > 8 || ldx < K || !code_table_ok(s_act) || ((M - 1) * ldx + K) * 2 >= ((int64_t)1 << 31))
+        return false;
+    RxPlan p;
+    return plan_rx(M, N, K, &p) && p.xm == XM_LDS;
+}
+
+bool launch_quant_gemm_small_m(const uint16_t* x, int64_t ldx, uint8_t* xq_out, const uint8_t* wq, float s_act,
+                               const float* s_w, const ShardTable& shards, int64_t M, int64_t N, int64_t K,
+                               hipStream_t stream)
+{
+    if (!quant_gemm_small_m_fits(M, N, K, ldx, s_act)) return false;
+    // the quotient's operands, rounded once here (IEEE single on the host)
+    const XSrc xs{x, ldx, xq_out, 1.0f / s_act, 448.0f * s_act};
+    return try_rx(nullptr, wq, s_act, s_w, shards, M, N, K, stream, &xs);
+}
 
 void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
                          const ShardTable& shards, int64_t M, int64_t N, int64_t K, hipStream_t stream)

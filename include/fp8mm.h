@@ -188,7 +188,9 @@ int fp8_scaled_mm_arm(const uint8_t* x_q, const uint8_t* w_q,
  * w_q  : E4M3 [sum n_i, K]; s_w: f32 [sum n_i].
  * shards (HOST array, read during the call only): shard i covers weight rows
  *     [sum_{j<i} n_j, sum_{j<=i} n_j) and writes bf16 [M, n_i] to out_i with
- *     row stride ldo_i >= n_i.  n_i % 16 == 0.  1 <= num_shards <= 8.
+ *     row stride ldo_i >= n_i.  n_i % 16 == 0; an empty shard (n_i == 0)
+ *     is never written and its out_i and ldo_i are not checked.
+ *     1 <= num_shards <= 8.
  * Merge admission is the caller's: merge only shards whose input scales are
  * bitwise equal (fp8_scales_bitwise_equal); otherwise call fp8_scaled_mm per
  * shard.  Column n of shard i is bitwise equal to the same column of a
@@ -205,6 +207,37 @@ int fp8_scaled_mm_merged(const uint8_t* x_q, const uint8_t* w_q,
                          const fp8_shard_t* shards, int num_shards,
                          int64_t M, int64_t K,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Static quant and merged projection in one call: x_q = the codes of
+ * fp8_quant_rmsnorm(x, gamma = NULL, s_act), then fp8_scaled_mm_merged on
+ * them (the quantize-once follow-on of vllm.cpp #417, its ranked follow-ons:
+ * one launch instead of a quant launch per projection).  For 1 <= M <= 8 on
+ * the small-M arm, with 2^-100 <= s_act <= 2^100 and an LDS plan for the
+ * shape, ONE kernel does both: every workgroup encodes the activation rows
+ * it multiplies by (the correctly rounded fp32 quotient x / s_act from the
+ * reciprocal and fused multiply-adds, then the hardware E4M3 conversion) and
+ * workgroup 0 writes x_q.  Otherwise the two calls run back to back.  Either
+ * way x_q and the outputs are bitwise those of the two separate calls.
+ *
+ * x      : bf16 [M, K] (DEVICE), row stride ldx >= K (a multiple of 8),
+ *          16-byte aligned.
+ * s_act  : static per-tensor scale, finite > 0.
+ * x_q    : E4M3 [M, K] (DEVICE), contiguous, written; must not overlap x.
+ * w_q, s_w, shards, num_shards, workspace: as fp8_scaled_mm_merged.
+ * Errors: those of fp8_quant_rmsnorm and fp8_scaled_mm_merged; nothing is
+ * launched on an error.
+ * ---------------------------------------------------------------------- */
+int fp8_quant_scaled_mm_merged(const uint16_t* x, int64_t ldx, float s_act, uint8_t* x_q,
+                               const uint8_t* w_q, const float* s_w,
+                               const fp8_shard_t* shards, int num_shards,
+                               int64_t M, int64_t K,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* 1 if fp8_quant_scaled_mm_merged runs as one launch for an [M, K] activation
+ * of row stride ldx, N output columns in total and scale s_act; else 0 (also
+ * for arguments it would reject).  Host-only: launches nothing. */
+int fp8_quant_scaled_mm_fused(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act);
 
 /* ------------------------------------------------------------------------
  * F32-output variants (the A/B of vllm.cpp #417 Finding 1: an F32 output

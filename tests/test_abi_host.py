@@ -175,6 +175,44 @@ def test_merged_validation_fails_closed(fp8):
     assert call([Shard(17408, D, 16)]) == fp8.EINVAL             # ldo < n
 
 
+def test_quant_merged_validation_fails_closed(fp8):
+    """The one-launch static quant + merged GEMM checks the quant's and the
+    GEMM's arguments before launching anything."""
+    lib = fp8.raw_lib()
+    Shard = fp8.Shard
+    f = lib.fp8_quant_scaled_mm_merged
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.POINTER(Shard), ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    E, U = fp8.EINVAL, fp8.EUNSUPPORTED
+    good = (Shard * 2)(Shard(17408, D, 17408), Shard(17408, D + 0x1000000, 17408))
+
+    def call(x=A, ldx=5120, s=0.1, xq=B, M=8, K=5120, shards=good, n=2):
+        return f(x, ldx, s, xq, C, C + 0x100000, shards, n, M, K, None, 0, None)
+
+    assert call(M=0) == fp8.OK
+    assert call(x=None) == E
+    assert call(xq=None) == E
+    assert call(ldx=5000) == E                                  # ldx < K
+    assert call(s=0.0) == E
+    assert call(s=float("inf")) == E
+    assert call(ldx=5124) == U                                  # ldx % 8
+    assert call(K=5112 + 4, ldx=5120) == U                      # K % 16
+    assert call(x=A + 2) == U
+    assert call(xq=B + 8) == U
+    assert call(xq=A + 16) == E                                 # x_q overlaps x
+    assert call(n=0) == E
+    assert call(shards=(Shard * 1)(Shard(17400, D, 17408)), n=1) == U
+    assert call(shards=(Shard * 1)(Shard(17408, None, 17408)), n=1) == E
+    q = lib.fp8_quant_scaled_mm_fused
+    q.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_float]
+    assert q(9, 10240, 5120, 5120, 0.1) == 0                    # beyond the fused kernel's M
+    assert q(8, 10240, 5120, 5120, 2.0 ** -120) == 0            # outside the code table's range
+    assert q(8, 10240, 5120, 5000, 0.1) == 0                    # ldx < K
+    assert q(8, 10240, 5120, 5120, 0.0) == 0
+    assert q(0, 10240, 5120, 5120, 0.1) == 0
+
+
 def test_quant_validation_fails_closed(fp8):
     lib = fp8.raw_lib()
     f = lib.fp8_quant_rmsnorm

@@ -56,6 +56,34 @@ extern "C" int code_table_build(float s) {
 extern "C" void codes_from_table(const unsigned short* h, long n, unsigned char* o) {
     for (long i = 0; i < n; ++i) o[i] = g_codes[h[i]];
 }
+// The fused GEMM's encoder on the host: quant_quotient (multiply and fused
+// multiply-add instead of a division), the software encoder standing in for
+// the hardware conversion (the same codes on [0, 464], the quotients' range),
+// the NaN mask and the sign byte; against code_table_entry for every bf16.
+extern "C" long quotient_code_mismatches(float s) {
+    if (!fp8mm::code_table_ok(s)) return -1;
+    const unsigned lo = fp8mm::code_band_lo(s);
+    const float rcp = 1.0f / s, sat = 448.0f * s;
+    long bad = 0;
+    for (unsigned h = 0; h < 65536; ++h) {
+        const unsigned bits = (h << 16) & 0x7fffffffu;
+        float a;
+        __builtin_memcpy(&a, &bits, 4);
+        const float q = fp8mm::quant_quotient(a, s, rcp, sat);
+        const unsigned c = (fp8mm::f32_to_e4m3_sat(q) & 0x7fu) | ((h >> 8) & 0x80u);
+        bad += c != fp8mm::code_table_entry(h, lo, s);
+    }
+    return bad;
+}
+extern "C" long band_code_mismatches(void) {
+    long bad = 0;
+    for (unsigned u = 0x39800000u; u < 0x44800000u; ++u) {     // every fp32 in [2^-12, 2^10)
+        float f;
+        __builtin_memcpy(&f, &u, 4);
+        bad += fp8mm::e4m3_code_band(f) != fp8mm::f32_to_e4m3_sat(f);
+    }
+    return bad;
+}
 extern "C" long band_table_mismatches(float s, int nthreads) {
     if (!fp8mm::code_table_ok(s)) return -1;
     const unsigned lo = fp8mm::code_band_lo(s);
@@ -113,6 +141,9 @@ def dev():
     lib.silu_mul_codes_pieces.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_float,
                                           ctypes.c_void_p, ctypes.c_void_p]
     lib.bf_sel_mismatches_all.restype = ctypes.c_long
+    lib.band_code_mismatches.restype = ctypes.c_long
+    lib.quotient_code_mismatches.argtypes = [ctypes.c_float]
+    lib.quotient_code_mismatches.restype = ctypes.c_long
     lib.band_table_mismatches.argtypes = [ctypes.c_float, ctypes.c_int]
     lib.band_table_mismatches.restype = ctypes.c_long
     lib.code_table_build.argtypes = [ctypes.c_float]
@@ -275,7 +306,30 @@ def test_band_table_fill_equals_per_entry_division(dev):
     scales = np.concatenate([scales, np.float32([2.0 ** -100, 2.0 ** 100, 1.0, 1.0 / 448.0, 0.0137,
                                                  np.nextafter(np.float32(2.0 ** -100), np.float32(1.0)),
                                                  np.nextafter(np.float32(2.0 ** 100), np.float32(0.0))])])
-    for n in (128, 512, 1024):
+    for n in (128, 256, 512, 640, 768, 1024):
         for s in scales:
             assert dev.band_table_mismatches(float(s), n) == 0, (float(s), n)
     assert dev.band_table_mismatches(2.0 ** -101, 128) == -1
+
+
+def test_branch_free_band_encoder_equals_the_plain_one(dev):
+    """e4m3_code_band (the band table fill's encoder: a select between the
+    subnormal grid and the rounded mantissa) against f32_to_e4m3_sat on every
+    positive fp32 in [2^-12, 2^10), the range of a band table's quotients."""
+    assert dev.band_code_mismatches() == 0
+
+
+def test_division_free_quotient_codes_equal_the_plain_quant(dev):
+    """The fused quant + GEMM's encoder (quotient from the reciprocal and two
+    fused multiply-adds, magnitude clamped at 448 s, NaN kept by the mask,
+    sign from the bf16 bit) against the per-entry division, for every bf16
+    pattern, over 1500 log-uniform scales in [2^-100, 2^100], scales with
+    random low mantissa bits, both edges and the decode / prefill scales."""
+    g = np.random.Generator(np.random.PCG64(77))
+    scales = np.exp2(g.uniform(-100.0, 100.0, 1000)).astype(np.float32)
+    jitter = (scales.view(np.uint32) ^ g.integers(0, 1 << 12, scales.size, dtype=np.uint32)).view(np.float32)
+    scales = np.concatenate([scales, jitter[:500], np.float32([2.0 ** -100, 2.0 ** 100, 1.0, 1.0 / 448.0, 0.0137,
+                                                               3.0, 1.0 / 7.0, 448.0])])
+    scales = scales[(scales >= 2.0 ** -100) & (scales <= 2.0 ** 100)]
+    bad = [(float(s), n) for s in scales if (n := dev.quotient_code_mismatches(float(s))) != 0]
+    assert not bad, bad[:5]

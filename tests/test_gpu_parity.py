@@ -577,6 +577,93 @@ def test_merged_equals_split_bitwise(fp8, M):
         start += n
 
 
+# ------------------------------------- static quant fused into the GEMM ----
+
+def _quant_then_merged(fp8, xd, s_act, wd, swd, shards):
+    """The two-call path the fused entry must reproduce bit for bit."""
+    xq = fp8.quant(xd, s_act)
+    return [host_u16(o) for o in fp8.scaled_mm_merged(xq, wd, s_act, swd, shards)], host_u8(xq)
+
+
+def _check_fused(fp8, x, xd, s_act, wq, sw, shards, fused, what):
+    wd, swd = u8_dev(wq), f32_dev(sw)
+    M, K = x.shape
+    assert fp8.quant_scaled_mm_fused(M, sum(shards), K, xd.stride(0), s_act) == fused, what
+    want, want_q = _quant_then_merged(fp8, xd, s_act, wd, swd, shards)
+    assert np.array_equal(want_q, oracle.quant_act(x, np.float32(s_act))), what
+    for rep in range(2):                      # twice: the second call finds the first's x_q and outputs
+        outs, xq = fp8.quant_scaled_mm_merged(xd, s_act, wd, swd, shards)
+        assert np.array_equal(host_u8(xq), want_q), f"{what}: x_q (call {rep})"
+        for i, (o, w) in enumerate(zip(outs, want)):
+            assert np.array_equal(host_u16(o), w), f"{what}: shard {i} (call {rep})"
+    return want, want_q
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("K,shards", [(5120, [10240]), (5120, [17408, 17408]), (6144, [5120]),
+                                      (5120, [4096, 1024, 9216]), (2048, [4112, 1008]), (3072, [2048])])
+def test_fused_quant_merged_equals_quant_then_merged(fp8, M, K, shards):
+    """One launch (static quant in the small-M GEMM kernel) == quant, then the
+    merged GEMM: x_q and every shard's output bit for bit, and the outputs
+    within the oracle's tolerance."""
+    x = wl.activation_bf16(2, M, K, outliers=True)
+    s_act = oracle.act_scale(x)
+    wq, sw = oracle.quant_weight(wl.weight_f32(2, sum(shards), K))
+    want, xq = _check_fused(fp8, x, bf16_dev(x), float(s_act), wq, sw, shards, True, f"M={M} K={K}")
+    ref, v = oracle.scaled_mm(xq, wq, s_act, sw, want_v=True)
+    assert_within_tolerance(np.concatenate(want, axis=1), ref, v, f"fused M={M} K={K}")
+
+
+@pytest.mark.parametrize("s_act", [1.0, 1.0 / 7.0, 2.0 ** -99, 2.0 ** 99])
+def test_fused_quant_every_bf16_pattern(fp8, s_act):
+    """Every bf16 pattern (NaN, inf, subnormals, -0) as an 8 x 8192 activation,
+    rotated per row: the in-kernel encoder gives the plain quant's codes."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(8, 8192)
+    x = np.stack([np.roll(bits[i], 301 * i) for i in range(8)])
+    wq = wl.random_codes(5, 2048, 8192, tensor=wl.T_W)
+    sw = (np.random.Generator(np.random.PCG64(5)).random(2048) * 1e-3 + 1e-5).astype(np.float32)
+    for M in (8, 5):
+        _check_fused(fp8, x[:M], bf16_dev(x[:M]), s_act, wq, sw, [1024, 1024], True, f"patterns M={M}")
+
+
+def test_fused_quant_strided_activation(fp8):
+    M, K, ld = 3, 5120, 5136
+    x = wl.activation_bf16(3, M, K, outliers=True)
+    s_act = float(oracle.act_scale(x))
+    wq, sw = oracle.quant_weight(wl.weight_f32(3, 10240, K))
+    _check_fused(fp8, x, _strided(x, ld), s_act, wq, sw, [10240], True, "strided")
+
+
+@pytest.mark.parametrize("M,K,N,s_act", [(9, 5120, 10240, 0.01), (16, 5120, 10240, 0.01),
+                                         (8, 5120, 10240, 2.0 ** -120), (4, 17408, 5120, 0.01),
+                                         (2, 256, 384, 0.01), (40, 5120, 2048, 0.01)])
+def test_fused_quant_falls_back_to_two_launches(fp8, M, K, N, s_act):
+    """Shapes the fused kernel does not take (M > 8, a scale outside the code
+    table's range, rows too long or too short for its plan, the large-M arm)
+    run the quant and the GEMM as two launches, with the same results."""
+    x = wl.activation_bf16(4, M, K, outliers=True)
+    wq, sw = oracle.quant_weight(wl.weight_f32(4, N, K))
+    _check_fused(fp8, x, bf16_dev(x), s_act, wq, sw, [N], False, f"fallback M={M} K={K} N={N}")
+
+
+def test_fused_quant_empty_shapes(fp8):
+    import torch
+    K = 5120
+    wq, sw = oracle.quant_weight(wl.weight_f32(4, 64, K))
+    x = torch.zeros((0, K), dtype=torch.bfloat16, device="cuda")
+    outs, xq = fp8.quant_scaled_mm_merged(x, 0.1, u8_dev(wq), f32_dev(sw), [64])
+    assert xq.shape == (0, K) and outs[0].shape == (0, 64)
+    # no output columns: only the quant runs
+    xh = wl.activation_bf16(4, 2, K, outliers=True)
+    empty_w = torch.zeros((0, K), dtype=torch.uint8, device="cuda")
+    empty_s = torch.zeros((0,), dtype=torch.float32, device="cuda")
+    outs, xq = fp8.quant_scaled_mm_merged(bf16_dev(xh), 0.1, empty_w, empty_s, [0])
+    assert np.array_equal(host_u8(xq), oracle.quant_act(xh, np.float32(0.1)))
+    # an empty shard between two others, fused
+    wq, sw = oracle.quant_weight(wl.weight_f32(4, 2048, K))
+    _check_fused(fp8, xh, bf16_dev(xh), 0.1, wq, sw, [1024, 0, 1024], True, "empty middle shard")
+
+
 @pytest.mark.parametrize("M", [1, 2, 4])
 def test_run_to_run_and_graph_capture_bitwise(fp8, M):
     import torch
