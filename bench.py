@@ -1,23 +1,26 @@
 """Benchmark of the FP8 E4M3 W8A8 scaled-matmul layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--M 8] [--no-prefill] [--no-mlp] [--no-sweep] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--M 8] [--no-prefill] [--no-mlp] [--no-sweep] [--no-cpu-baseline] [--headline-only]
 
 Prints ONE JSON line.  The headline (`value`) is the decode projection (M = 8,
 K = 5120, N = 10240): a step is one pass of the layer's decode path over one
-batch -- static quant of the bf16 activation [M, 5120] to E4M3, then the scaled
+batch -- static quant of the bf16 activation [M, 5120] to E4M3 and the scaled
 GEMM against a 10240 x 5120 E4M3 weight with per-channel scales and a bf16
-output, the kernel picked by the M-threshold dispatcher (the small-M arm).
+output, the kernel picked by the M-threshold dispatcher (the small-M arm), in
+one launch (fp8_quant_scaled_mm_merged: the quant runs inside the GEMM kernel
+and still writes x_q).
 `value` is algorithmic bytes per step / step time in GB/s, with inputs resident
 in HBM; weight copies are rotated so that no step finds its weight in the
 256 MB Infinity Cache.  Steps are captured into a HIP graph of K steps and the
 graph is replayed; every time is the median over 10 timed replays (HIP events
 on the replay stream), per step.
 
-`roofline` is for the dominant kernel (the small-M GEMM): algorithmic bytes per
-launch over its median launch duration in a graph of K back-to-back GEMM
-launches on the same stream.  `traffic` comes from a rocprofv3 FETCH_SIZE /
-WRITE_SIZE summary committed under profiles/ (null if absent or if the kernel
-sources changed since it was taken).  `configs` holds every workload: the tiny
+`roofline` is for the step's kernel (the small-M GEMM with the quant inside:
+the step is one launch): algorithmic bytes per launch over its median launch
+duration in the graph of K back-to-back steps on the same stream.  The GEMM
+alone (x_q given) is reported beside it.  `traffic` comes from a rocprofv3
+FETCH_SIZE / WRITE_SIZE summary committed under profiles/ (null if absent or if
+the kernel sources changed since it was taken).  `configs` holds every workload: the tiny
 case (1), the decode projection at M = 1, 2, 4, 8 (2) and the decode MLP step
 at M = 1, 4, 8, 16, 32 (3), each with GB/s and the fraction of the 8 TB/s
 peak.  `prefill` reports the prefill chunk (config 5, M = 6576: fused
@@ -71,6 +74,8 @@ def _args():
     p.add_argument("--no-sweep", action="store_true", help="skip the 64-layer decode-step weight sweep")
     p.add_argument("--no-mlp", action="store_true", help="skip the decode-MLP entries")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--headline-only", action="store_true",
+                   help="only the headline decode workload at --M (for a kernel trace of just its launches)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--summarize-trace", metavar="DIR")
     p.add_argument("--summarize-pmc", metavar="DIR")
@@ -233,6 +238,9 @@ def bench_decode(fp8, M, steps, warmup):
     assert fp8.select(M, N, K) == 0
 
     def step(i):
+        fp8.quant_scaled_mm(xd, s_act, ws[i % copies], sw, out=out, x_q=xq)
+
+    def two_launches(i):
         fp8.quant(xd, s_act, out=xq)
         fp8.scaled_mm(xq, ws[i % copies], s_act, sw, out=out)
 
@@ -240,22 +248,28 @@ def bench_decode(fp8, M, steps, warmup):
         fp8.scaled_mm(xq, ws[i % copies], s_act, sw, out=out)
 
     st = timed(step, steps, warmup)
+    st2 = timed(two_launches, steps, warmup)
     gt = timed(gemm, steps, warmup)
-    step_bytes = gemm_bytes + quant_bytes
+    one = bool(fp8.quant_scaled_mm_fused(M, N, K, K, s_act))
+    # one launch reads x, writes x_q and never reads x_q back; two launches do
+    two_bytes = gemm_bytes + quant_bytes
+    step_bytes = two_bytes - M * K if one else two_bytes
     del ws
     torch.cuda.empty_cache()
     return {"workload": f"decode_proj_M{M}_K{K}_N{N}", "M": M, "K": K, "N": N, "weight_copies_rotated": copies,
-            "step_us": st["median_ms"] * 1e3, "step_min_us": st["min_ms"] * 1e3,
+            "step_us": st["median_ms"] * 1e3, "step_min_us": st["min_ms"] * 1e3, "step_one_launch": one,
             "step_GBs": _rate(step_bytes, st["median_ms"]), "step_frac": _rate(step_bytes, st["median_ms"]) / HBM_PEAK_GBS,
             "algorithmic_bytes_per_step": step_bytes,
+            "two_launches_us": st2["median_ms"] * 1e3, "two_launches_GBs": _rate(two_bytes, st2["median_ms"]),
             "gemm_us": gt["median_ms"] * 1e3, "gemm_min_us": gt["min_ms"] * 1e3,
             "gemm_GBs": _rate(gemm_bytes, gt["median_ms"]), "gemm_frac": _rate(gemm_bytes, gt["median_ms"]) / HBM_PEAK_GBS,
             "algorithmic_bytes_per_gemm": gemm_bytes}
 
 
 def bench_tiny(fp8, steps, warmup):
-    """Config 1, M = 4, K = 256, N = 384: static quant + GEMM.  About 100 KB
-    of operands, resident in L2: the time is launch latency, not bandwidth."""
+    """Config 1, M = 4, K = 256, N = 384: static quant + GEMM (through the
+    one-launch entry, which takes two launches at this K).  About 100 KB of
+    operands, resident in L2: the time is launch latency, not bandwidth."""
     import torch
     import workloads as wl
     M, K, N = 4, 256, 384
@@ -266,8 +280,7 @@ def bench_tiny(fp8, steps, warmup):
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
     def step(i):
-        fp8.quant(xd, s_act, out=xq)
-        fp8.scaled_mm(xq, wq, s_act, sw, out=out)
+        fp8.quant_scaled_mm(xd, s_act, wq, sw, out=out, x_q=xq)
 
     st = timed(step, steps, warmup)
     gt = timed(lambda i: fp8.scaled_mm(xq, wq, s_act, sw, out=out), steps, warmup)
@@ -530,11 +543,12 @@ def bench_sweep(fp8, layers, M, steps, warmup, wid=4):
     streams count x bytes from HBM (far past the Infinity Cache).  A step is,
     per layer and projection, the static quant of its bf16 input (fused
     RMSNorm quant for the projections a norm feeds: qkv(z) and gate_up; the
-    fused SiLU*mul quant of the gate_up output for down) and its GEMM, at M
-    tokens."""
+    fused SiLU*mul quant of the gate_up output for down; the plain quant
+    inside the GEMM's launch where the small-M kernel takes the shape) and its
+    GEMM, at M tokens."""
     import torch
     import workloads as wl
-    plan, src, step_bytes, gemm_bytes = [], {}, 0, 0
+    plan, src, step_bytes, gemm_bytes, launches = [], {}, 0, 0, 0
     for gi, (count, projs) in enumerate(layers):
         srcs = []
         for pi, p in enumerate(projs):
@@ -560,7 +574,10 @@ def bench_sweep(fp8, layers, M, steps, warmup, wid=4):
             for (p, x, gam, s, wq, sw, xq, outs) in srcs:
                 plan.append((p, x, gam, s, wq if li == 0 else wq.clone(), sw, xq, outs))
                 qb = 5 * M * p.K if isinstance(x, tuple) else 3 * M * p.K + (2 * p.K if gam is not None else 0)
-                step_bytes += p.N * p.K + 4 * p.N + M * p.K + 2 * M * p.N + qb
+                one = not isinstance(x, tuple) and gam is None and fp8.quant_scaled_mm_fused(M, p.N, p.K, p.K, s)
+                launches += 1 if one else 2
+                # one launch never reads x_q back
+                step_bytes += p.N * p.K + 4 * p.N + (0 if one else M * p.K) + 2 * M * p.N + qb
                 gemm_bytes += p.N * p.K + 4 * p.N + M * p.K + 2 * M * p.N
     torch.cuda.synchronize()
 
@@ -570,8 +587,9 @@ def bench_sweep(fp8, layers, M, steps, warmup, wid=4):
                 fp8.silu_mul_quant(x[0], x[1], s, out=xq)
             elif gam is not None:
                 fp8.quant_rmsnorm(x, gam, s, wl.EPS, out=xq)
-            else:
-                fp8.quant(x, s, out=xq)
+            else:                                        # plain quant: in the GEMM's launch where it fits
+                fp8.quant_scaled_mm_merged(x, s, wq, sw, list(p.shards or (p.N,)), outs=outs, x_q=xq)
+                continue
             if p.shards:
                 fp8.scaled_mm_merged(xq, wq, s, sw, list(p.shards), outs=outs)
             else:
@@ -587,7 +605,7 @@ def bench_sweep(fp8, layers, M, steps, warmup, wid=4):
     ms = timed(step, steps, warmup)["median_ms"]
     gms = timed(gemms, steps, warmup)["median_ms"]
     n_launch = len(plan)
-    res = {"layers": sum(c for c, _ in layers), "launches_per_step": 2 * n_launch, "gemm_launches": n_launch,
+    res = {"layers": sum(c for c, _ in layers), "launches_per_step": launches, "gemm_launches": n_launch,
            "weight_bytes": sum(p.N * p.K for (p, *_r) in plan), "ms_per_step": ms,
            "value": step_bytes / (ms * 1e-3) / 1e9, "unit": "GB/s",
            "gemm_only": {"ms": gms, "GBs": gemm_bytes / (gms * 1e-3) / 1e9}}
@@ -940,9 +958,10 @@ def summarize_mfma(d, name, cmd):
 def pmc_driver(fp8, which, meta_dir):
     """Launches profiled by the FETCH_SIZE / WRITE_SIZE passes: first one
     elementwise kernel that reads 256 MiB and writes 256 MiB (the calibration
-    copy: torch.neg on float32), then 3 launches of the decode GEMM (on 3
-    different weight copies, so each launch finds its weight cache-cold) or of
-    the prefill gate_up GEMM, on the bench's inputs."""
+    copy: torch.neg on float32), then 3 launches of the decode step (the GEMM
+    with the static quant inside, on 3 different weight copies, so each launch
+    finds its weight cache-cold) or of the prefill gate_up GEMM, on the bench's
+    inputs."""
     import torch
     import workloads as wl
     nbytes = 256 * 2 ** 20
@@ -956,11 +975,11 @@ def pmc_driver(fp8, which, meta_dir):
         s_act = float(fp8.act_scale(xd).item())
         wq, sw = fp8.quant_weight(f32_dev(wl.weight_f32(wl.DECODE_PROJ.wid, N, K)))
         copies = [wq] + [wq.clone() for _ in range(11)]
-        xq = fp8.quant(xd, s_act)
+        xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
         out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         torch.cuda.synchronize()
-        for i in range(3):
-            fp8.scaled_mm(xq, copies[4 * i + 1], s_act, sw, out=out)
+        for i in range(3):                          # the one-launch step: quant inside the GEMM
+            fp8.quant_scaled_mm(xd, s_act, copies[4 * i + 1], sw, out=out, x_q=xq)
         kernel = "k_gemm_small_m_rx"
     elif which == "prefill_mfma":
         # the prefill gate_up and down GEMMs, 3 launches each, for the MFMA counters
@@ -1004,6 +1023,8 @@ def pmc_driver(fp8, which, meta_dir):
         kernel = "k_gemm_large_m_tiled"
     torch.cuda.synchronize()
     alg = N * K + 4 * N + M * K + (4 if which == "prefill_f32" else 2) * M * N
+    if which == "decode":
+        alg += 2 * M * K                            # x read as bf16, x_q written (and not read back)
     os.makedirs(meta_dir, exist_ok=True)
     json.dump({"kernel": kernel, "copy_kernel": "elementwise_kernel", "copy_bytes": nbytes, "algorithmic_bytes": alg},
               open(os.path.join(meta_dir, "pmc_meta.json"), "w"))
@@ -1034,26 +1055,34 @@ def main():
         return pmc_driver(fp8, a.pmc_driver, a.meta_out)
     if a.sweep_threshold:
         return sweep_threshold(fp8, a.sweep_threshold, a.cmd)
-    decode = {M: bench_decode(fp8, M, a.steps, a.warmup) for M in sorted(set(wl.DECODE_PROJ.Ms) | {a.M})}
+    Ms = [a.M] if a.headline_only else sorted(set(wl.DECODE_PROJ.Ms) | {a.M})
+    decode = {M: bench_decode(fp8, M, a.steps, a.warmup) for M in Ms}
     head = decode[a.M]
-    gemm_bytes = head["algorithmic_bytes_per_gemm"]
-    achieved = head["gemm_GBs"]
+    assert head["step_one_launch"], "the headline step is one launch at this shape"
+    achieved = head["step_GBs"]
     line = {
         "metric": METRIC, "value": head["step_GBs"], "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": head["step_us"] * 1e-3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic (seeded, workloads/)",
         "config": {"workload": head["workload"], "M": a.M, "K": head["K"], "N": head["N"],
                    "weight_copies_rotated": head["weight_copies_rotated"],
-                   "step": "static quant [M,K] + scaled GEMM via dispatcher (small-M arm), graph-replayed",
+                   "step": "static quant [M,K] + scaled GEMM via dispatcher (small-M arm), one launch, graph-replayed",
                    "timing": f"median over {REPLAYS} replays of a graph of {a.steps} steps",
                    "algorithmic_bytes_per_step": head["algorithmic_bytes_per_step"]},
-        "roofline": {"bound": "hbm", "kernel": "k_gemm_small_m_rx", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": load_traffic(f"decode_gemm_M{a.M}_K5120_N10240_pmc", "k_gemm_small_m_rx"),
-                     "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_us": head["gemm_us"],
-                     "min_launch_us": head["gemm_min_us"],
-                     "timing": f"median over {REPLAYS} replays of a graph of {a.steps} back-to-back launches"},
+        "roofline": {"bound": "hbm", "kernel": "k_gemm_small_m_rx (static quant inside)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": load_traffic(f"decode_step_M{a.M}_K5120_N10240_pmc", "k_gemm_small_m_rx"),
+                     "algorithmic_bytes_per_launch": head["algorithmic_bytes_per_step"], "avg_launch_us": head["step_us"],
+                     "min_launch_us": head["step_min_us"],
+                     "timing": f"median over {REPLAYS} replays of a graph of {a.steps} back-to-back launches",
+                     "gemm_alone": {"avg_launch_us": head["gemm_us"], "achieved": head["gemm_GBs"],
+                                    "frac": head["gemm_frac"],
+                                    "algorithmic_bytes_per_launch": head["algorithmic_bytes_per_gemm"]}},
     }
+    if a.headline_only:
+        line["config"]["headline_only"] = True
+        print(json.dumps(line), flush=True)
+        return
     line["configs"] = {"1_tiny": bench_tiny(fp8, a.steps, a.warmup),
                        "2_decode_proj": {f"M{M}": r for M, r in decode.items()}}
     if not a.no_mlp:
