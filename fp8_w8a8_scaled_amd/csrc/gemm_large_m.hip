@@ -275,8 +275,10 @@ __device__ __forceinline__ uint4 frag_half(const uint8_t* __restrict__ st, int f
 // One sub-step: the MF MFMAs of `fc`; the first NF are each followed by the
 // two 16-byte reads of one fragment of the next sub-step (into `fn`), so the
 // reads have landed before the sub-step ends, and, when LD is set, the
-// stage's LOADS loads (into `fill`) are spread over all MF MFMAs.
-template <int NJ, bool LD>
+// stage's LOADS loads (into `fill`) are spread over all MF MFMAs.  With Z the
+// MFMAs start from zero (the tile's first sub-step): the accumulators need no
+// clearing (256 register writes per lane and tile).
+template <int NJ, bool LD, bool Z = false>
 __device__ __forceinline__ void substep(const uint8_t* __restrict__ frag_src, int sub_next, int lane, int wn, int wm,
                                         const Frags<NJ>& fc, Frags<NJ>& fn, v16f (&acc)[4][NJ], uint8_t* fill,
                                         uint32_t k, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx,
@@ -287,7 +289,8 @@ __device__ __forceinline__ void substep(const uint8_t* __restrict__ frag_src, in
 #pragma unroll
     for (int s = 0; s < C::MF; ++s) {
         const int i = s / NJ, j = s % NJ;
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fc.a[i], fc.b[j], Z ? v16f{} : acc[i][j], 0, 0, 0,
+                                                                    0, 0, 0);
         if (s < C::NF) {
             t[2 * s] = frag_half<NJ>(frag_src, s, 0, sub_next, lane, wn, wm);
             t[2 * s + 1] = frag_half<NJ>(frag_src, s, 1, sub_next, lane, wn, wm);
@@ -343,13 +346,7 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     const int tn = (t % in_group) / gsz;
     const int64_t m0 = (int64_t)tm * TX, n0 = (int64_t)tn * TW;
 
-    v16f acc[4][NJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    v16f acc[4][NJ];                                   // set by the first sub-step (Z)
 
     const int nk = (int)(K / TK);
     // K offset of stage st; the stages past the end (the pipeline's trailing
@@ -380,18 +377,21 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
 #pragma unroll
     for (int f = 0; f < NJ; ++f)
         fa.b[f] = pack(frag_half<NJ>(smem, 4 + f, 0, 0, lane, wn, wm), frag_half<NJ>(smem, 4 + f, 1, 0, lane, wn, wm));
-    for (int kt = 0; kt < nk; ++kt) {
+    // stage kt (kt < nk): sub-step 0 (its sub-step 1 fragments come from the
+    // same stage); boundary: stage kt+1 landed (the only stage in flight),
+    // stage kt fully read; sub-step 1: fragments of stage kt+1, and the loads
+    // of stage kt+2 into stage kt's buffer.  Stage 0 starts the accumulators.
+    auto stage = [&](int kt, auto first) {
         uint8_t* cur = smem + (kt & 1) * C::STAGE_BYTES;
         uint8_t* nxt = smem + ((kt + 1) & 1) * C::STAGE_BYTES;
-        // sub-step 0 of stage kt (its sub-step 1 fragments come from the same stage)
-        substep<NJ, false>(cur, 1, lane, wn, wm, fa, fb, acc, nullptr, 0u, rw, rx, ro, wave);
-        // boundary: stage kt+1 landed (the only stage in flight), stage kt fully read
+        substep<NJ, false, decltype(first)::value>(cur, 1, lane, wn, wm, fa, fb, acc, nullptr, 0u, rw, rx, ro, wave);
         __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_LGKM0_IMM(0));
         __builtin_amdgcn_s_barrier();
-        // sub-step 1 of stage kt: fragments of stage kt+1, and the loads of stage kt+2 into stage kt's buffer
         const int64_t k2 = kof(kt + 2);
         substep<NJ, true>(nxt, 0, lane, wn, wm, fb, fa, acc, cur, (uint32_t)k2, rw, rx, ro, wave);
-    }
+    };
+    stage(0, std::true_type{});
+    for (int kt = 1; kt < nk; ++kt) stage(kt, std::false_type{});
 
     // Epilogue: scale, round to bf16, stage the TX x 256 tile in LDS (rows of
     // m, padded), then store rows with 16-byte, row-contiguous writes (an f32

@@ -314,7 +314,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
     const int ntiles = (int)(N >> 4);
     const int FR = BAL ? ntiles / G : 0;                // >= 1 with BAL: G <= N / 16
     const int R = FR * G * 16, ngr = BAL ? ((int)N - R) >> 2 : 0;
-    const int q0 = 4 * (int)((int64_t)ngr * bid / G), q1 = 4 * (int)((int64_t)ngr * (bid + 1) / G);
+    // 32-bit: ngr (bid + 1) <= (N / 4) G < 2^30 (N < 2^24: N K < 2^31 here; G <= 256 CUs)
+    const int q0 = 4 * (int)((uint32_t)ngr * (uint32_t)bid / (uint32_t)G),
+              q1 = 4 * (int)((uint32_t)ngr * (uint32_t)(bid + 1) / (uint32_t)G);
     const int my_tiles = BAL ? FR + (q1 > q0 ? 1 : 0) : (ntiles - bid + G - 1) / G;
     __builtin_assume(my_tiles >= 1);                    // G <= ntiles
     const int tiles_max = BAL ? FR + (ngr > 0 ? 1 : 0) : (ntiles + G - 1) / G;
@@ -660,7 +662,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     const int ntiles = (int)(N >> 4);
     const int FR = BAL ? ntiles / G : 0;                // >= 1 with BAL: G <= N / 16
     const int R = FR * G * 16, ngr = BAL ? ((int)N - R) >> 2 : 0;
-    const int q0 = 4 * (int)((int64_t)ngr * bid / G), q1 = 4 * (int)((int64_t)ngr * (bid + 1) / G);
+    // 32-bit: ngr (bid + 1) <= (N / 4) G < 2^30 (N < 2^24: N K < 2^31 here; G <= 256 CUs)
+    const int q0 = 4 * (int)((uint32_t)ngr * (uint32_t)bid / (uint32_t)G),
+              q1 = 4 * (int)((uint32_t)ngr * (uint32_t)(bid + 1) / (uint32_t)G);
     const int my_tiles = BAL ? FR + (q1 > q0 ? 1 : 0) : (ntiles - bid + G - 1) / G;
     __builtin_assume(my_tiles >= 1);                    // G <= ntiles
     const int tiles_max = BAL ? FR + (ngr > 0 ? 1 : 0) : (ntiles + G - 1) / G;
