@@ -189,7 +189,9 @@ struct Cfg {
     static constexpr int C_ROW = TW * 2 + 16;                 // padded bf16 C row (one m), bytes
     static constexpr int C_ROW32 = TW * 4 + 16;               // padded f32 C row, bytes
     static constexpr int A = NSTAGE * STAGE_BYTES, B = TX * C_ROW, C = TX / 2 * C_ROW32;
-    static constexpr int LDS = A > B ? (A > C ? A : C) : (B > C ? B : C);
+    static constexpr int LDS_MAIN = A > B ? (A > C ? A : C) : (B > C ? B : C);
+    static constexpr int SW_OFF = LDS_MAIN;                   // the tile's TW weight scales (f32), after the rest
+    static constexpr int LDS = LDS_MAIN + TW * 4;
     static_assert(NF <= MF && LOADS <= 2 * MF, "reads and loads fit the sub-step's MFMA slots");
     static_assert((TX / 8) % 4 == 0 && (TX / 2 / 4) % 4 == 0, "epilogue rows per thread come in groups of 4");
     static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -338,6 +340,8 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     const int in_group = GM * num_n;
     // operand buffers: rows past N or M load zeros
     const __amdgpu_buffer_rsrc_t rw = operand_rsrc(wq, N * K), rx = operand_rsrc(xq, M * K);
+    const __amdgpu_buffer_rsrc_t rsw = operand_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
+    float* swl = reinterpret_cast<float*>(smem + C::SW_OFF);
     for (int u = bid >> 3; u < tiles_x; u += nbx) {
     const int t = start_x + u;
     const int first_m = (t / in_group) * GM;
@@ -380,18 +384,31 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     // stage kt (kt < nk): sub-step 0 (its sub-step 1 fragments come from the
     // same stage); boundary: stage kt+1 landed (the only stage in flight),
     // stage kt fully read; sub-step 1: fragments of stage kt+1, and the loads
-    // of stage kt+2 into stage kt's buffer.  Stage 0 starts the accumulators.
-    auto stage = [&](int kt, auto first) {
+    // of stage kt+2 into stage kt's buffer.  Stage 0 starts the accumulators;
+    // the last stage also fetches the tile's weight scales into LDS (one
+    // direct-to-LDS load per wave, past the boundary's wait: it lands during
+    // the last sub-step instead of in front of the epilogue).
+    auto stage = [&](int kt, auto first, auto last) {
         uint8_t* cur = smem + (kt & 1) * C::STAGE_BYTES;
         uint8_t* nxt = smem + ((kt + 1) & 1) * C::STAGE_BYTES;
         substep<NJ, false, decltype(first)::value>(cur, 1, lane, wn, wm, fa, fb, acc, nullptr, 0u, rw, rx, ro, wave);
         __builtin_amdgcn_s_waitcnt(FP8MM_VMCNT_LGKM0_IMM(0));
         __builtin_amdgcn_s_barrier();
+        if constexpr (decltype(last)::value) {
+            const int64_t n = n0 + wave * 64 + lane;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void_t*)(swl + wave * 64), 4,
+                                                     n < N ? (int)(n * 4) : (int)0x80000000u, 0, 0, 0);
+        }
         const int64_t k2 = kof(kt + 2);
         substep<NJ, true>(nxt, 0, lane, wn, wm, fb, fa, acc, cur, (uint32_t)k2, rw, rx, ro, wave);
     };
-    stage(0, std::true_type{});
-    for (int kt = 1; kt < nk; ++kt) stage(kt, std::false_type{});
+    if (nk == 1) {
+        stage(0, std::true_type{}, std::true_type{});
+    } else {
+        stage(0, std::true_type{}, std::false_type{});
+        for (int kt = 1; kt < nk - 1; ++kt) stage(kt, std::false_type{}, std::false_type{});
+        stage(nk - 1, std::false_type{}, std::true_type{});
+    }
 
     // Epilogue: scale, round to bf16, stage the TX x 256 tile in LDS (rows of
     // m, padded), then store rows with 16-byte, row-contiguous writes (an f32
@@ -406,14 +423,12 @@ __global__ __launch_bounds__(256) void k_gemm_large_m_tiled(
     const int ewn = (tid >> 6) & 1, ewm = tid >> 7;    // this wave's wn, wm
     // 32x32 C layout with W as A: lane l holds column l%32 (= m) and rows
     // 8*(v/4) + 4*(l/32) + v%4 (= n): four consecutive n per v/4.
-    float4 swv[4][4];                                  // all weight scales first, one wait
+    float4 swv[4][4];                                  // the weight scales, staged by the last stage (zeros past N)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t n = n0 + ewn * 128 + i * 32 + 8 * q + 4 * fh;
-            swv[i][q] = *reinterpret_cast<const float4*>(s_w + (n < N ? n : 0));
-        }
+        for (int q = 0; q < 4; ++q)
+            swv[i][q] = *reinterpret_cast<const float4*>(swl + ewn * 128 + i * 32 + 8 * q + 4 * fh);
     // The loops below run row group j outermost, so only one activation scale
     // (per-tensor, or this lane's row's) is live at a time.
     if (sh.f32) {

@@ -431,7 +431,9 @@ def test_both_arms_agree_with_oracle(fp8, M):
                                    # with a balanced last round (4112 = 257 tiles) and 5 waves (K = 3072)
                                    (5, 10240, 5120), (13, 4112, 5120), (11, 6144, 3072),
                                    # K % 1024 == 0 but the ring kernel's LDS plan does not fit: the generic kernel
-                                   (1, 33168, 32768), (12, 10240, 32768)])
+                                   (1, 33168, 32768), (12, 10240, 32768),
+                                   # large-M tiles with one K stage (first and last at once) and with two
+                                   (300, 528, 128), (520, 272, 256)])
 def test_ragged_shapes_both_arms(fp8, M, N, K):
     g = np.random.Generator(np.random.PCG64(M * 1000 + N + K))
     xq = wl.random_codes(9, M, K, m=M)
