@@ -19,12 +19,16 @@
 //  * the W per-wave partial sums are reduced in LDS in a fixed order (no
 //    atomics, no workspace), then the scale epilogue and the store happen in
 //    registers.
-// Three kernels share that work split, so they give the same bits:
+// Four kernels share that work split, so they give the same bits:
+//  * k_gemm_small_m_pair (M <= 32, rows longer than 5 chunks per wave, at
+//    most two tiles per workgroup): the two tiles' chunks in one slot, against
+//    fragments streamed with each chunk, so x_q is read once per workgroup;
 //  * k_gemm_small_m_rx (M <= 32, K % 128 == 0 with 4-5 chunks per wave, and
 //    M 17-32 beyond): persistent, one workgroup per CU walking its weight
 //    tiles; each wave streams its weight chunks with whole-line direct-to-LDS
 //    loads into a private ring of LDS slots and keeps its x_q B fragments in
-//    registers (loaded once, or with each chunk);
+//    registers (loaded once, or with each chunk); for M <= 8 it can also
+//    quantize the bf16 activation itself (the static quant in its launch);
 //  * k_gemm_small_m_ring (M <= 16, K % 1024 == 0, the longer rows): the same
 //    stream, with x_q staged in LDS once (or streamed with each chunk when it
 //    does not fit);
@@ -947,6 +951,137 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     }
 }
 
+// Two-tile kernel for long rows (more chunks per wave than stay resident: the
+// x_q fragments streamed from L2 with every chunk, MT B tiles of 16 rows) when
+// no workgroup has more than two tiles: both tiles' weight chunks travel in
+// one 4 KB ring slot and multiply the same fragments, so each workgroup reads
+// x_q once instead of once per tile (the balanced last round gives every
+// workgroup a whole tile and a few rows, and the fragments of those rows cost
+// as much as a whole tile's).  Chunks, their order per wave, the MFMAs and the
+// reduction are those of the other kernels: the same bits.  At the end each
+// wave writes its partial sums into its own ring area (its loads have all
+// landed) and the workgroup reduces them.
+template <int S, int MT, bool BAL>
+__global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_pair(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act, const float* __restrict__ s_w,
+    ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int ntiles = (int)(N >> 4);
+    // tile 0: rows bid*16 .. (BAL: FR = 1 whole tile per workgroup); tile 1:
+    // the balanced share of the leftover rows (BAL) or tile bid + G
+    const int R = BAL ? G * 16 : 0, ngr = BAL ? ((int)N - R) >> 2 : 0;
+    // 32-bit: ngr (bid + 1) <= (N / 4) G < 2^30 (N < 2^24: N K < 2^31 here; G <= 256 CUs)
+    const int q0 = 4 * (int)((uint32_t)ngr * (uint32_t)bid / (uint32_t)G),
+              q1 = 4 * (int)((uint32_t)ngr * (uint32_t)(bid + 1) / (uint32_t)G);
+    int rt[2], re[2];
+    rt[0] = bid * 16;
+    re[0] = rt[0] + 16;
+    if (BAL) {
+        rt[1] = R + q0;
+        re[1] = R + q1;
+    } else {
+        rt[1] = (bid + G) * 16;
+        re[1] = bid + G < ntiles ? rt[1] + 16 : rt[1];
+    }
+    const int my_tiles = re[1] > rt[1] ? 2 : 1;
+    // LDS: [W rings of S 4 KB slots (two tiles' chunks); at the end each wave's
+    // partial sums in its own ring area] [activation scales of 64 rows] [the
+    // two tiles' weight scales]
+    uint8_t* ring = smem + wave * S * 4096;
+    float* srl = reinterpret_cast<float*>(smem + W * S * 4096);
+    float* swl = srl + 64;
+    const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
+    const __amdgpu_buffer_rsrc_t rx = weight_rsrc(xq, (int64_t)M * K);
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
+    if (sh.s_rows) {
+        if (wave == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                weight_rsrc(reinterpret_cast<const uint8_t*>(sh.s_rows), (int64_t)M * 4), (lds_void*)srl, 4,
+                lane < M ? lane * 4 : (int)kOob, 0, 0, 0);
+    } else if (threadIdx.x < 64) {
+        srl[threadIdx.x] = s_act;
+    }
+    if (wave == 0) {
+        // the two tiles' 16 weight scales each (zeros past a tile's rows)
+        const int t = lane >> 4, n = rt[t & 1] + (lane & 15);
+        const uint32_t o = t < 2 && n < re[t & 1] ? (uint32_t)n * 4 : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)swl, 4, (int)o, 0, 0, 0);
+    }
+    // this lane's two rows of a tile's chunk (instruction i: row 8i + lane/8), logical piece
+    const int lrow = lane >> 3;
+    const uint32_t pieceoff0 = (uint32_t)(lrow * K + wswz(lrow, lane & 7) * 16);
+    const uint32_t pieceoff1 = (uint32_t)((lrow + 8) * K + wswz(lrow + 8, lane & 7) * 16);
+    // position i of this wave's stream: chunk wave + i W of both tiles, into a slot
+    auto fire = [&](int i, int slot) {
+        const int chunk = wave + i * W;
+        const bool ok = i < cpw && chunk < nchunks;
+        uint8_t* sl = ring + slot * 4096;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t t0 = (uint32_t)((int64_t)rt[t] * K) + (uint32_t)chunk * kChunk;
+            const uint32_t w0 = ok && rt[t] + lrow < re[t] ? t0 + pieceoff0 : kOob;
+            const uint32_t w1 = ok && rt[t] + lrow + 8 < re[t] ? t0 + pieceoff1 : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sl + t * 2048), 16, (int)w0, 0, 0, kWeightCpol);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sl + t * 2048 + 1024), 16, (int)w1, 0, 0,
+                                                     kWeightCpol);
+        }
+    };
+    v8i bx[S][MT];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        fire(s, s);
+        load_bfrag<MT>(bx[s], rx, wave + s * W, s < cpw && wave + s * W < nchunks, r, g, M, K);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    v4f acc[2][MT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    // whole ring cycles: positions past cpw load zeros and add zeros
+    for (int j0 = 0; j0 < cpw; j0 += S) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int nx = j0 + s + S;
+            // position j0 + s landed (4 weight + 2 MT fragment loads per position): the S - 1 after it may be in flight
+            __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT((4 + 2 * MT) * (S - 1)));
+            const v8i A0 = slot_afrag(ring + s * 4096, r, g);
+            const v8i A1 = slot_afrag(ring + s * 4096 + 2048, r, g);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                acc[0][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, bx[s][mt], acc[0][mt], 0, 0, 0, 0,
+                                                                             0, 0);
+                acc[1][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, bx[s][mt], acc[1][mt], 0, 0, 0, 0,
+                                                                             0, 0);
+            }
+            __builtin_amdgcn_s_waitcnt(FP8MM_SM_LGKM0);   // the slot's reads have returned
+            fire(nx, s);
+            load_bfrag<MT>(bx[s], rx, wave + nx * W, nx < cpw && wave + nx * W < nchunks, r, g, M, K);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);                      // no load outlives the workgroup; the ring area is free
+    v4f* mine = reinterpret_cast<v4f*>(ring);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) put_partial(mine + (t * MT + mt) * 64 + lane, acc[t][mt]);
+    __syncthreads();
+    const int stride = S * 4096 / (int)sizeof(v4f);     // v4f per wave's ring area
+    for (int idx = threadIdx.x; idx < my_tiles * MT * 64; idx += blockDim.x) {
+        const int t = idx / (MT * 64), rem = idx - t * MT * 64;
+        const int mt = rem / 64, l = rem - mt * 64;
+        if (rt[t] + 4 * (l >> 4) >= re[t]) continue;     // rows of another workgroup
+        reduce_tile(reinterpret_cast<const v4f*>(smem) + (t * MT + mt) * 64, stride, l, W, rt[t], re[t], s_act,
+                    lds_f4(swl + t * 16 + 4 * (l >> 4)), sh, M, l, t == 1 && BAL, 16 * mt, srl);
+    }
+}
+
 // Waves per workgroup: a function of K only (it fixes the summation order).
 int small_m_waves(int64_t K)
 {
@@ -1161,6 +1296,60 @@ bool try_rx(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
 }
 #undef FP8MM_RX_ARGS
 
+template <int S, int MT, bool BAL>
+void launch_pair(unsigned G, unsigned W, size_t lds, const uint8_t* xq, const uint8_t* wq, float s_act,
+                 const float* s_w, const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, int cpw,
+                 hipStream_t stream)
+{
+    static const bool attr = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_pair<S, MT, BAL>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        return true;
+    }();
+    (void)attr;
+    hipLaunchKernelGGL((k_gemm_small_m_pair<S, MT, BAL>), dim3(G), dim3(64 * W), lds, stream, xq, wq, s_act, s_w, sh,
+                       M, N, K, nchunks, cpw);
+}
+
+// The two-tile kernel, if it takes the shape: M <= 32, more chunks per wave
+// than stay resident (the fragments streamed), and at most two tiles per
+// workgroup (one whole tile and a balanced share of the rest, or two whole).
+// Measured against the kernels it replaces there (5120 x 17408, the decode
+// MLP's down projection): M = 32 42.4 -> 29.0 us, M = 16 23.6 -> 21.1 us,
+// M = 8 19.7 -> 19.2 us, M = 1 unchanged.
+bool try_pair(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh, int64_t M,
+              int64_t N, int64_t K, hipStream_t stream)
+{
+    if (M < 1 || M > 32 || K % kChunk != 0 || N * K >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31))
+        return false;
+    const int W = small_m_waves(K);
+    const int nchunks = (int)(K / kChunk);
+    const int cpw = (nchunks + W - 1) / W;
+    if (cpw <= kCpw) return false;                      // resident fragments: the register kernel
+    const int64_t ntiles = N / 16;
+    const int64_t G = ntiles < num_cus() ? ntiles : num_cus();
+    const int64_t tiles_max = (ntiles + G - 1) / G;
+    const bool bal = 10 * tiles_max * G >= 13 * ntiles;  // the register kernel's rule
+    if (bal ? ntiles / G != 1 : tiles_max != 2) return false;
+#define FP8MM_PAIR_LAUNCH(S, MT) \
+    (bal ? launch_pair<S, MT, true>((unsigned)G, (unsigned)W, lds, xq, wq, s_act, s_w, sh, (int)M, N, K, nchunks, cpw, stream) \
+         : launch_pair<S, MT, false>((unsigned)G, (unsigned)W, lds, xq, wq, s_act, s_w, sh, (int)M, N, K, nchunks, cpw, stream))
+    for (const int S : {3, 2}) {
+        const size_t lds = (size_t)W * S * 4096 + 512;
+        if (lds > 160 * 1024) continue;
+        if (M <= 16) {
+            if (S == 3) FP8MM_PAIR_LAUNCH(3, 1);
+            else FP8MM_PAIR_LAUNCH(2, 1);
+        } else {
+            if (S == 3) FP8MM_PAIR_LAUNCH(3, 2);
+            else FP8MM_PAIR_LAUNCH(2, 2);
+        }
+        return true;
+    }
+#undef FP8MM_PAIR_LAUNCH
+    return false;
+}
+
 bool quant_gemm_small_m_fits(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act)
 {
     // 32-bit buffer offsets into the activation; the plain quant's code table
@@ -1185,6 +1374,7 @@ void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, cons
 {
     const int W = small_m_waves(K);
     const int nchunks = (int)((K + kChunk - 1) / kChunk);
+    if (try_pair(xq, wq, s_act, s_w, shards, M, N, K, stream)) return;
     if (try_rx(xq, wq, s_act, s_w, shards, M, N, K, stream)) return;
     if (try_ring(xq, wq, s_act, s_w, shards, M, N, K, W, nchunks, stream)) return;
     const int MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);

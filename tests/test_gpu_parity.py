@@ -446,6 +446,29 @@ def test_ragged_shapes_both_arms(fp8, M, N, K):
         assert_within_tolerance(_run_arm(fp8, xq, wq, s_act, sw, arm), ref, v, f"{M}x{N}x{K} arm {arm}")
 
 
+@pytest.mark.parametrize("M,N,K,shards", [(32, 5120, 17408, [5120]), (17, 5120, 17408, [4112, 1008]),
+                                          (29, 6400, 17408, [6400]), (24, 4112, 12288, [2048, 16, 2048])])
+def test_two_tile_streamed_fragment_kernel(fp8, M, N, K, shards):
+    """M 17..32 with long rows and at most two tiles per workgroup (a whole
+    tile and a balanced share of the rest, or two whole tiles: 6400 rows): both
+    tiles' chunks multiply the same streamed fragments.  Within the oracle's
+    tolerance on every element, and merged == one call per shard bit for bit
+    (the single shards run other kernels: the same bits by construction)."""
+    xq = wl.random_codes(8, M, K, m=M)
+    wq = wl.random_codes(8, N, K, tensor=wl.T_W, m=N)
+    sw = (np.random.Generator(np.random.PCG64(N + K)).random(N) * 1e-3 + 1e-5).astype(np.float32)
+    s_act = 0.0093
+    xd, wd, swd = u8_dev(xq), u8_dev(wq), f32_dev(sw)
+    merged = [host_u16(o) for o in fp8.scaled_mm_merged(xd, wd, s_act, swd, shards)]
+    ref, v = oracle.scaled_mm(xq, wq, s_act, sw, want_v=True)
+    assert_within_tolerance(np.concatenate(merged, axis=1), ref, v, f"two-tile {M}x{N}x{K}")
+    start = 0
+    for n, mo in zip(shards, merged):
+        split = host_u16(fp8.scaled_mm(xd, wd[start:start + n], s_act, swd[start:start + n]))
+        assert np.array_equal(split, mo), f"shard at {start} differs"
+        start += n
+
+
 def test_strided_output_and_zero_m(fp8):
     import torch
     xq, wq, s_act, sw = _prepare(1, 4, 384, 256, outliers=False)
