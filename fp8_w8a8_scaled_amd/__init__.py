@@ -52,7 +52,10 @@ _quant_rmsnorm = _decl("fp8_quant_rmsnorm", [_P, _I64, _P, _F32, _F32, _P, _I64,
 _scaled_mm = _decl("fp8_scaled_mm", [_P, _P, _F32, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P])
 _scaled_mm_arm = _decl("fp8_scaled_mm_arm", [_P, _P, _F32, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _SZ, _P])
 _scaled_mm_merged = _decl("fp8_scaled_mm_merged", [_P, _P, _F32, _P, ctypes.POINTER(Shard), _I32, _I64, _I64, _P, _SZ, _P])
-_quant_scaled_mm_fused = _decl("fp8_quant_scaled_mm_fused", [_I64, _I64, _I64, _I64, _F32])
+_quant_scaled_mm_fused = _decl("fp8_quant_scaled_mm_fused", [_I64, _I64, _I64, _I64, _F32, _I32])
+_quant_rmsnorm_scaled_mm_merged = _decl("fp8_quant_rmsnorm_scaled_mm_merged",
+                                        [_P, _I64, _P, _F32, _F32, _P, _P, _P, ctypes.POINTER(Shard), _I32, _I64,
+                                         _I64, _P, _SZ, _P])
 _quant_scaled_mm_merged = _decl("fp8_quant_scaled_mm_merged",
                                 [_P, _I64, _F32, _P, _P, _P, ctypes.POINTER(Shard), _I32, _I64, _I64, _P, _SZ, _P])
 _quant_per_token = _decl("fp8_quant_per_token", [_P, _I64, _P, _F32, _P, _P, _I64, _I64, _P])
@@ -381,15 +384,20 @@ def scaled_mm_merged(x_q: torch.Tensor, w_q: torch.Tensor, s_act: float, s_w: to
     return list(outs)
 
 
-def quant_scaled_mm_merged(x: torch.Tensor, s_act: float, w_q: torch.Tensor, s_w: torch.Tensor,
-                           shard_sizes: Sequence[int], outs: Optional[Sequence[torch.Tensor]] = None,
-                           x_q: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
-    """Static quant of bf16 x [M, K] and the merged GEMM on the codes, one
-    launch where the small-M kernel takes the shape (M <= 8): returns
-    (list of bf16 [M, n_i] outputs, x_q uint8 [M, K])."""
+def quant_rmsnorm_scaled_mm_merged(x: torch.Tensor, gamma: Optional[torch.Tensor], s_act: float, eps: float,
+                                   w_q: torch.Tensor, s_w: torch.Tensor, shard_sizes: Sequence[int],
+                                   outs: Optional[Sequence[torch.Tensor]] = None, x_q: Optional[torch.Tensor] = None,
+                                   workspace: Optional[torch.Tensor] = None):
+    """Fused RMSNorm quant (gamma given) or plain static quant (gamma None) of
+    bf16 x [M, K] and the merged GEMM on the codes, one launch where the
+    small-M kernel takes the shape: returns (list of bf16 [M, n_i] outputs,
+    x_q uint8 [M, K])."""
     _need(x.is_cuda and x.dtype == torch.bfloat16, "x must be a bf16 CUDA tensor")
     ldx = _row_major(x, "x")
     M, K = x.shape
+    if gamma is not None:
+        _need(gamma.is_cuda and gamma.dtype == torch.bfloat16 and gamma.is_contiguous()
+              and gamma.numel() == K, "gamma must be a contiguous bf16 CUDA tensor of K elements")
     w_q = _codes(w_q, "w_q")
     _need(w_q.is_cuda and w_q.dim() == 2 and w_q.shape[1] == K and w_q.is_contiguous(),
           "w_q must be contiguous E4M3 codes [N, K]")
@@ -408,14 +416,30 @@ def quant_scaled_mm_merged(x: torch.Tensor, s_act: float, w_q: torch.Tensor, s_w
         _need(o.dtype == torch.bfloat16 and o.is_cuda and o.shape == (M, n), "shard outputs must be bf16 [M, n_i]")
         arr[i] = Shard(int(n), o.data_ptr(), _row_major(o, "out"))
     ws, wsb = _workspace(M, w_q.shape[0], K, x.device, workspace)
-    _check(_quant_scaled_mm_merged(_ptr(x), ldx, float(s_act), _ptr(x_q), _ptr(w_q), _ptr(s_w), arr,
-                                   len(shard_sizes), M, K, _ptr(ws), wsb, _stream(x)), "fp8_quant_scaled_mm_merged")
+    if gamma is None:
+        _check(_quant_scaled_mm_merged(_ptr(x), ldx, float(s_act), _ptr(x_q), _ptr(w_q), _ptr(s_w), arr,
+                                       len(shard_sizes), M, K, _ptr(ws), wsb, _stream(x)), "fp8_quant_scaled_mm_merged")
+    else:
+        _check(_quant_rmsnorm_scaled_mm_merged(_ptr(x), ldx, _ptr(gamma), float(eps), float(s_act), _ptr(x_q),
+                                               _ptr(w_q), _ptr(s_w), arr, len(shard_sizes), M, K, _ptr(ws), wsb,
+                                               _stream(x)), "fp8_quant_rmsnorm_scaled_mm_merged")
     return list(outs), x_q
 
 
-def quant_scaled_mm_fused(M: int, N: int, K: int, ldx: Optional[int] = None, s_act: float = 1.0) -> bool:
-    """Whether quant_scaled_mm_merged runs as one launch for this shape."""
-    return bool(_quant_scaled_mm_fused(M, N, K, K if ldx is None else ldx, float(s_act)))
+def quant_scaled_mm_merged(x: torch.Tensor, s_act: float, w_q: torch.Tensor, s_w: torch.Tensor,
+                           shard_sizes: Sequence[int], outs: Optional[Sequence[torch.Tensor]] = None,
+                           x_q: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Static quant of bf16 x [M, K] and the merged GEMM on the codes, one
+    launch where the small-M kernel takes the shape (M <= 8): returns (list of
+    bf16 [M, n_i] outputs, x_q uint8 [M, K])."""
+    return quant_rmsnorm_scaled_mm_merged(x, None, s_act, 0.0, w_q, s_w, shard_sizes, outs, x_q, workspace)
+
+
+def quant_scaled_mm_fused(M: int, N: int, K: int, ldx: Optional[int] = None, s_act: float = 1.0,
+                          rmsnorm: bool = False) -> bool:
+    """Whether quant_scaled_mm_merged (or, rmsnorm, quant_rmsnorm_scaled_mm_merged
+    with a gamma) runs as one launch for this shape."""
+    return bool(_quant_scaled_mm_fused(M, N, K, K if ldx is None else ldx, float(s_act), int(bool(rmsnorm))))
 
 
 def quant_scaled_mm(x: torch.Tensor, s_act: float, w_q: torch.Tensor, s_w: torch.Tensor,

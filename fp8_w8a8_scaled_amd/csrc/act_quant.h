@@ -19,15 +19,16 @@ namespace fp8mm {
 // order.  A kernel that computes the same r must take the same order.
 constexpr int kRmsRowThreads = 256;
 
-// ss + the squares of the 8 values of a piece, added in element order (each
-// square of a bf16 value is exact in fp64).
+// ss + the squares of the 8 values of a piece, added in element order.  The
+// square of a bf16 value (8 significant bits) is exact in fp64, so the fused
+// multiply-add rounds exactly as the product followed by the sum would.
 __device__ __forceinline__ double sumsq8(const uint4 in, double ss)
 {
     const uint32_t w[4] = {in.x, in.y, in.z, in.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const double f = (double)bf16_to_f32((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
-        ss += f * f;
+        ss = __builtin_fma(f, f, ss);
     }
     return ss;
 }

@@ -170,25 +170,29 @@ int fp8_scaled_mm_merged(const uint8_t* x_q, const uint8_t* w_q, float s_act, co
     return run_gemm(x_q, w_q, s_act, s_w, tab, num_shards, false, M, K, -1, workspace, workspace_bytes, stream);
 }
 
-int fp8_quant_scaled_mm_fused(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act)
+int fp8_quant_scaled_mm_fused(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act, int rmsnorm)
 {
     if (M < 1 || N < 1 || K < 1 || N % 16 != 0 || K % 16 != 0 || ldx < K || ldx % 8 != 0 || !good_scale(s_act))
         return 0;
-    return fp8_scaled_mm_select(M, N, K) == 0 && fp8mm::quant_gemm_small_m_fits(M, N, K, ldx, s_act) ? 1 : 0;
+    return fp8_scaled_mm_select(M, N, K) == 0 && fp8mm::quant_gemm_small_m_fits(M, N, K, ldx, s_act, rmsnorm != 0)
+               ? 1 : 0;
 }
 
-int fp8_quant_scaled_mm_merged(const uint16_t* x, int64_t ldx, float s_act, uint8_t* x_q,
-                               const uint8_t* w_q, const float* s_w, const fp8_shard_t* shards, int num_shards,
-                               int64_t M, int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream)
+int fp8_quant_rmsnorm_scaled_mm_merged(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, float s_act,
+                                       uint8_t* x_q, const uint8_t* w_q, const float* s_w,
+                                       const fp8_shard_t* shards, int num_shards, int64_t M, int64_t K,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (!shards || num_shards < 1 || num_shards > FP8MM_MAX_SHARDS) return FP8MM_EINVAL;
-    // the quant's arguments (as fp8_quant_rmsnorm without gamma)
+    // the quant's arguments (as fp8_quant_rmsnorm)
     if (M < 0 || K < 0 || ldx < K) return FP8MM_EINVAL;
     if (!good_scale(s_act)) return FP8MM_EINVAL;
+    if (gamma && !(std::isfinite(eps) && eps >= 0.0f)) return FP8MM_EINVAL;
     if (K % 16 != 0 || ldx % 8 != 0) return FP8MM_EUNSUPPORTED;
     if (M > 0 && K > 0) {
         if (!x || !x_q) return FP8MM_EINVAL;
-        if (!aligned16(x) || !aligned16(x_q)) return FP8MM_EUNSUPPORTED;
+        if (!aligned16(x) || !aligned16(x_q) || (gamma && !aligned16(gamma))) return FP8MM_EUNSUPPORTED;
+        if (gamma && M > (int64_t)0x7fffffff) return FP8MM_EUNSUPPORTED;
         const uintptr_t xb = reinterpret_cast<uintptr_t>(x), xe = xb + (uintptr_t)((M - 1) * ldx + K) * 2;
         const uintptr_t qb = reinterpret_cast<uintptr_t>(x_q), qe = qb + (uintptr_t)(M * K);
         if (qb < xe && xb < qe) return FP8MM_EINVAL;
@@ -202,14 +206,22 @@ int fp8_quant_scaled_mm_merged(const uint16_t* x, int64_t ldx, float s_act, uint
     if (rc != FP8MM_OK) return rc;
     if (workspace_bytes < fp8_scaled_mm_workspace_bytes(M, N, K)) return FP8MM_EWORKSPACE;
     if (M == 0 || K == 0) return FP8MM_OK;
-    if (fp8_quant_scaled_mm_fused(M, N, K, ldx, s_act) &&
-        fp8mm::launch_quant_gemm_small_m(x, ldx, x_q, w_q, s_act, s_w, st, M, N, K, stream))
+    if (fp8_quant_scaled_mm_fused(M, N, K, ldx, s_act, gamma != nullptr) &&
+        fp8mm::launch_quant_gemm_small_m(x, ldx, gamma, eps, x_q, w_q, s_act, s_w, st, M, N, K, stream))
         return launch_status();
-    fp8mm::launch_quant(x, ldx, nullptr, 0.0f, s_act, x_q, M, K, stream);
+    fp8mm::launch_quant(x, ldx, gamma, eps, s_act, x_q, M, K, stream);
     if (N == 0) return launch_status();
     const int qs = launch_status();
     if (qs != FP8MM_OK) return qs;
     return run_gemm(x_q, w_q, s_act, s_w, tab, num_shards, false, M, K, -1, workspace, workspace_bytes, stream);
+}
+
+int fp8_quant_scaled_mm_merged(const uint16_t* x, int64_t ldx, float s_act, uint8_t* x_q,
+                               const uint8_t* w_q, const float* s_w, const fp8_shard_t* shards, int num_shards,
+                               int64_t M, int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return fp8_quant_rmsnorm_scaled_mm_merged(x, ldx, nullptr, 0.0f, s_act, x_q, w_q, s_w, shards, num_shards, M, K,
+                                              workspace, workspace_bytes, stream);
 }
 
 int fp8_scaled_mm_f32(const uint8_t* x_q, const uint8_t* w_q, float s_act, const float* s_w,

@@ -36,6 +36,7 @@
 //    fragments loaded straight into registers.
 // W and the chunk assignment depend on K only, so every column's summation
 // order is the same for a merged call and a per-shard call: bitwise identical.
+#include "act_quant.h"
 #include "act_tables.h"
 #include "device_common.h"
 #include "internal.h"
@@ -550,16 +551,26 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_ring(
 // hardware conversion, no table and no barrier.  Each wave stages its own
 // codes in LDS (read back by the same wave only); workgroup 0 also stores them
 // (x_q).
-constexpr int XM_RES = 0, XM_STREAM = 1, XM_LDS = 2, XM_QLDS = 3;
+// XM_QRMS (M <= 8, 8 waves: K of 4608..5120): XM_QLDS for the fused RMSNorm
+// quant.  r of each row takes the standalone kernel's summation order: its
+// thread t holds pieces t, t + 256, ... (8 values each), which are all in one
+// lane here (chunk c's pieces 16c .. 16c + 15 sit in wave c % 8, and 256
+// pieces are 16 chunks apart), so each lane sums its 4 threads' squares,
+// stages them in LDS (one barrier), and wave m does row m's 4 xor butterflies
+// and adds the 4 sums in order (a second barrier) before any chunk is encoded.
+constexpr int XM_RES = 0, XM_STREAM = 1, XM_LDS = 2, XM_QLDS = 3, XM_QRMS = 4;
 
 // The bf16 activation of a fused quant + GEMM launch (XM_QLDS): rows of ldx
 // elements, and where workgroup 0 stores its E4M3 codes ([M, K], contiguous).
-// rcp = fl32(1 / s_act), sat = fl32(448 s_act): the quotient's operands.
+// rcp = fl32(1 / s_act), sat = fl32(448 s_act): the quotient's operands;
+// gamma (bf16 [K]) and eps for XM_QRMS.
 struct XSrc {
     const uint16_t* x;
     int64_t ldx;
     uint8_t* xq_out;
     float rcp, sat;
+    const uint16_t* gamma;
+    float eps;
 };
 
 // The 16 E4M3 codes of 16 bf16 values (words of a then b; value i in bits
@@ -609,6 +620,14 @@ __device__ __forceinline__ v8i lds_bfrag(const uint8_t* __restrict__ base, int r
                 *reinterpret_cast<const uint4*>(base + row * kChunk + (g + 4) * 16));
 }
 
+// Staged values of the fused RMSNorm's row sums (restrict: these LDS areas are
+// never targets of the in-flight direct-to-LDS loads, so the compiler need not
+// wait for them).
+__device__ __forceinline__ void lds_put_f64(double* __restrict__ p, double v) { *p = v; }
+__device__ __forceinline__ double lds_get_f64(const double* __restrict__ p) { return *p; }
+__device__ __forceinline__ void lds_put_f32(float* __restrict__ p, float v) { *p = v; }
+__device__ __forceinline__ float lds_get_f32(const float* __restrict__ p) { return *p; }
+
 // 16 codes into the fragment staging area (restrict: this area is never a
 // target of the in-flight direct-to-LDS loads).
 __device__ __forceinline__ void put_codes(uint8_t* __restrict__ dst, uint4 q) { *reinterpret_cast<uint4*>(dst) = q; }
@@ -650,14 +669,17 @@ __device__ __forceinline__ void lds_barrier()
 // never a target of the in-flight direct-to-LDS loads).
 __device__ __forceinline__ void put_partial(v4f* __restrict__ dst, v4f v) { *dst = v; }
 
+// (XM_QRMS runs 8 waves: its bound leaves each lane 256 registers, which the
+// activation, gamma and fragments of 5 chunks need.)
 template <int S, int MT, int XM, int CPW, bool BAL, bool DEFER>
-__global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
+__global__ __launch_bounds__(XM == XM_QRMS ? 64 * 8 : 64 * kMaxWaves) void k_gemm_small_m_rx(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act, const float* __restrict__ s_w,
     ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw, XSrc xs)
 {
     static_assert(XM == XM_STREAM || CPW > 0, "resident fragments need a compile-time chunk count");
-    static_assert((XM != XM_LDS && XM != XM_QLDS) || MT == 1, "fragments through LDS: M <= 16");
-    constexpr bool kLds = XM == XM_LDS || XM == XM_QLDS;   // fragments staged in LDS
+    static_assert((XM != XM_LDS && XM != XM_QLDS && XM != XM_QRMS) || MT == 1, "fragments through LDS: M <= 16");
+    constexpr bool kQ = XM == XM_QLDS || XM == XM_QRMS;   // the activation quantized in the kernel
+    constexpr bool kLds = XM == XM_LDS || kQ;            // fragments staged in LDS
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -740,9 +762,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     // XM_QLDS: this lane's bf16 values of each of the wave's chunks (x row
     // lane / 8, values 16 (lane % 8) .. + 15; zeros past M or past the last
     // chunk), loaded by load_xv inside the ring fill
-    [[maybe_unused]] uint4 xv[XM == XM_QLDS ? CPW : 1][2];
+    [[maybe_unused]] uint4 xv[kQ ? CPW : 1][2];
     [[maybe_unused]] const __amdgpu_buffer_rsrc_t rxb =
-        weight_rsrc(reinterpret_cast<const uint8_t*>(xs.x), XM == XM_QLDS ? ((int64_t)(M - 1) * xs.ldx + K) * 2 : 0);
+        weight_rsrc(reinterpret_cast<const uint8_t*>(xs.x), kQ ? ((int64_t)(M - 1) * xs.ldx + K) * 2 : 0);
     auto load_xv = [&](int c) {
         const int chunk = wave + c * W, xrow = lane >> 3;
         const uint32_t o = chunk < nchunks && xrow < M
@@ -752,6 +774,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
         xv[c][0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         xv[c][1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     };
+    // XM_QRMS: gamma of this lane's 16 columns of each chunk (the same for the
+    // 8 rows), and each row's r (LDS, after the swl scales)
+    [[maybe_unused]] uint4 gv[XM == XM_QRMS ? CPW : 1][2];
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t rgb =
+        weight_rsrc(reinterpret_cast<const uint8_t*>(xs.gamma), XM == XM_QRMS ? K * 2 : 0);
+    auto load_g = [&](int c) {
+        const int chunk = wave + c * W;
+        const uint32_t o = chunk < nchunks ? (uint32_t)((chunk * kChunk + (lane & 7) * 16) * 2) : kOob;
+        const u32x4_t lo = __builtin_amdgcn_raw_buffer_load_b128(rgb, (int)o, 0, 0);
+        const u32x4_t hi = __builtin_amdgcn_raw_buffer_load_b128(rgb, (int)(o + 16), 0, 0);
+        gv[c][0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        gv[c][1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    };
+    float* rrow = swl + (tiles_max + 3) / 4 * 64;       // XM_QRMS: r of rows 0..7
 
     const __amdgpu_buffer_rsrc_t rs = weight_rsrc(reinterpret_cast<const uint8_t*>(s_w), N * 4);
     // The activation scale of each output row into LDS: the per-row scales
@@ -802,7 +838,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
     // by the same wave only), then into its fragment; workgroup 0 also stores
     // them to x_q
     auto quant_chunk = [&](int c) {
-        const uint4 q = quant16_div(xv[c][0], xv[c][1], s_act, xs.rcp, xs.sat);
+        uint4 a = xv[c][0], b = xv[c][1];
+        if constexpr (XM == XM_QRMS) {
+            // y = bf16(fl32(fl32(x r) gamma)), the values the plain quant then takes
+            const float rr = lds_get_f32(rrow + (lane >> 3));
+            const uint32_t xw[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            const uint32_t gw[8] = {gv[c][0].x, gv[c][0].y, gv[c][0].z, gv[c][0].w,
+                                    gv[c][1].x, gv[c][1].y, gv[c][1].z, gv[c][1].w};
+            uint32_t yw[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                yw[i] = pack_bf16x2((bf16_to_f32(xw[i] & 0xffffu) * rr) * bf16_to_f32(gw[i] & 0xffffu),
+                                    (bf16_to_f32(xw[i] >> 16) * rr) * bf16_to_f32(gw[i] >> 16));
+            a = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+            b = make_uint4(yw[4], yw[5], yw[6], yw[7]);
+        }
+        const uint4 q = quant16_div(a, b, s_act, xs.rcp, xs.sat);
         put_codes(bxl + (wave * CPW + c) * 1024 + lane * 16, q);
         const int chunk = wave + c * W, xrow = lane >> 3;
         if (bid == 0 && xs.xq_out && chunk < nchunks && xrow < M)
@@ -811,7 +862,58 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_rx(
         bx[c][0] = lds_bfrag(bxl + (wave * CPW + c) * 1024, r & 7, g);
     };
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (XM == XM_QLDS) {
+    if constexpr (XM == XM_QRMS) {
+        // activation and gamma first, two ring slots, then r (two barriers),
+        // then the rest of the fill with the chunks encoded between its slots
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) load_xv(c);
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) load_g(c);
+        constexpr int S0 = S < 2 ? S : 2;
+#pragma unroll
+        for (int s = 0; s < S0; ++s) fire(prep(), s);
+        __builtin_amdgcn_sched_barrier(0);              // every load above issued before the sums wait for any
+        // this lane's 4 threads of the standalone order (W = 8): t = 16 (wave +
+        // 8 gg) + 2 (lane % 8) + h holds the chunks at positions gg, gg + 2, ...
+        double ss[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            ss[c & 1][0] = sumsq8(xv[c][0], ss[c & 1][0]);
+            ss[c & 1][1] = sumsq8(xv[c][1], ss[c & 1][1]);
+        }
+        double* part = reinterpret_cast<double*>(bxl);  // [8 rows][256 threads], free until the encoding
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                lds_put_f64(part + (lane >> 3) * kRmsRowThreads + 16 * (wave + 8 * gg) + 2 * (lane & 7) + h, ss[gg][h]);
+        lds_barrier();
+        if (wave < M) {
+            double tot = 0.0;                            // the 4 wave sums in order, each an xor butterfly
+#pragma unroll
+            for (int k = 0; k < kRmsRowThreads / 64; ++k) {
+                double v = lds_get_f64(part + wave * kRmsRowThreads + 64 * k + lane);
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+                tot += v;
+            }
+            if (lane == 0) lds_put_f32(rrow + wave, rms_inv(tot, K, xs.eps));
+        } else if (lane == 0) {
+            lds_put_f32(rrow + wave, 0.0f);              // rows past M: never kept
+        }
+        lds_barrier();
+#pragma unroll
+        for (int s = S0; s < S; ++s) {
+            fire(prep(), s);
+            if (s - S0 < CPW) {
+                __builtin_amdgcn_sched_barrier(0);
+                quant_chunk(s - S0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int c = S - S0; c < CPW; ++c) quant_chunk(c);
+    } else if constexpr (XM == XM_QLDS) {
         // Issuing the fill stalls on a full memory pipe for microseconds:
         // chunk c is encoded there, two ring slots after its activation was
         // requested, instead of in the first tile (the weights have landed
@@ -1186,7 +1288,7 @@ struct RxPlan {
     unsigned G, W;
 };
 
-bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p)
+bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p, size_t extra = 0)
 {
     if (M < 1 || M > 32 || K % kChunk != 0 || N * K >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31)) return false;
     const int W = small_m_waves(K);
@@ -1213,7 +1315,7 @@ bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p)
     // beside some ring, even one shallower than the register path's (measured
     // faster on every decode shape); else in registers
     const size_t xl = res && M <= 16 ? (size_t)W * cpw * (M <= 8 ? 8 : 16) * kChunk : 0;
-    const size_t swb = 256 + (size_t)(tiles_max + 3) / 4 * 256;   // the rows' and the tiles' scales
+    const size_t swb = 256 + (size_t)(tiles_max + 3) / 4 * 256 + extra;   // the rows' and the tiles' scales
     for (const size_t xlb : {xl, (size_t)0})
         for (const auto& o : order)
             if (bytes(o.S, o.df) + xlb + swb <= 160 * 1024 && (o.df || p->xm != XM_STREAM)) {
@@ -1274,10 +1376,14 @@ bool try_rx(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
             int64_t N, int64_t K, hipStream_t stream, const XSrc* xsrc = nullptr)
 {
     RxPlan p;
-    if (!plan_rx(M64, N, K, &p)) return false;
+    const bool rms = xsrc && xsrc->gamma;
+    if (!plan_rx(M64, N, K, &p, rms ? 32 : 0)) return false;   // XM_QRMS: the rows' r after the scales
     const int M = (int)M64, nchunks = (int)(K / kChunk);
-    const XSrc xs = xsrc ? *xsrc : XSrc{nullptr, 0, nullptr, 0.0f, 0.0f};
-    if (xsrc) {
+    const XSrc xs = xsrc ? *xsrc : XSrc{nullptr, 0, nullptr, 0.0f, 0.0f, nullptr, 0.0f};
+    if (rms) {
+        if (p.xm != XM_LDS || M > 8 || p.W != 8 || p.cpw != 5) return false;
+        dispatch_rx<1, XM_QRMS, 5>(FP8MM_RX_ARGS);
+    } else if (xsrc) {
         if (p.xm != XM_LDS || M > 8) return false;
         if (p.cpw == 4) dispatch_rx<1, XM_QLDS, 4>(FP8MM_RX_ARGS);
         else dispatch_rx<1, XM_QLDS, 5>(FP8MM_RX_ARGS);
@@ -1350,22 +1456,24 @@ bool try_pair(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_
     return false;
 }
 
-bool quant_gemm_small_m_fits(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act)
+bool quant_gemm_small_m_fits(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act, bool rmsnorm)
 {
-    // 32-bit buffer offsets into the activation; the plain quant's code table
+    // 32-bit buffer offsets into the activation; the range where the
+    // quotient by multiply and fused multiply-add is exact
     if (M < 1 || M > 8 || ldx < K || !code_table_ok(s_act) || ((M - 1) * ldx + K) * 2 >= ((int64_t)1 << 31))
         return false;
     RxPlan p;
-    return plan_rx(M, N, K, &p) && p.xm == XM_LDS;
+    if (!plan_rx(M, N, K, &p, rmsnorm ? 32 : 0) || p.xm != XM_LDS) return false;
+    return !rmsnorm || (p.W == 8 && p.cpw == 5);         // the RMSNorm's summation order needs 8 waves
 }
 
-bool launch_quant_gemm_small_m(const uint16_t* x, int64_t ldx, uint8_t* xq_out, const uint8_t* wq, float s_act,
-                               const float* s_w, const ShardTable& shards, int64_t M, int64_t N, int64_t K,
-                               hipStream_t stream)
+bool launch_quant_gemm_small_m(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, uint8_t* xq_out,
+                               const uint8_t* wq, float s_act, const float* s_w, const ShardTable& shards, int64_t M,
+                               int64_t N, int64_t K, hipStream_t stream)
 {
-    if (!quant_gemm_small_m_fits(M, N, K, ldx, s_act)) return false;
+    if (!quant_gemm_small_m_fits(M, N, K, ldx, s_act, gamma != nullptr)) return false;
     // the quotient's operands, rounded once here (IEEE single on the host)
-    const XSrc xs{x, ldx, xq_out, 1.0f / s_act, 448.0f * s_act};
+    const XSrc xs{x, ldx, xq_out, 1.0f / s_act, 448.0f * s_act, gamma, eps};
     return try_rx(nullptr, wq, s_act, s_w, shards, M, N, K, stream, &xs);
 }
 

@@ -61,15 +61,16 @@ void launch_requant_max_scale(const uint8_t* in, uint8_t* out, const ShardScales
 void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
                          const ShardTable& shards, int64_t M, int64_t N, int64_t K,
                          hipStream_t stream);
-// The static quant of bf16 x fused into the small-M GEMM (one launch; x_q
-// also written).  Returns false, launching nothing, where the fused kernel
-// does not take the shape (M > 8, scale outside the code table's range, or
-// no LDS plan): the caller then quantizes and multiplies separately.
-// Whether launch_quant_gemm_small_m takes this shape (the host-side plan only).
-bool quant_gemm_small_m_fits(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act);
-bool launch_quant_gemm_small_m(const uint16_t* x, int64_t ldx, uint8_t* xq_out, const uint8_t* wq, float s_act,
-                               const float* s_w, const ShardTable& shards, int64_t M, int64_t N, int64_t K,
-                               hipStream_t stream);
+// The static quant of bf16 x (with gamma: the fused RMSNorm quant) inside
+// the small-M GEMM (one launch; x_q also written).  Returns false, launching
+// nothing, where the fused kernel does not take the shape (M > 8, a scale
+// outside 2^-100..2^100, no LDS plan; with gamma also W != 8): the caller then
+// quantizes and multiplies separately.  quant_gemm_small_m_fits: whether it
+// takes the shape (the host-side plan only).
+bool quant_gemm_small_m_fits(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act, bool rmsnorm);
+bool launch_quant_gemm_small_m(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, uint8_t* xq_out,
+                               const uint8_t* wq, float s_act, const float* s_w, const ShardTable& shards, int64_t M,
+                               int64_t N, int64_t K, hipStream_t stream);
 
 // gemm_large_m.hip: compute units of the current device (cached).
 int num_cus();

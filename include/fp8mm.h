@@ -234,10 +234,26 @@ int fp8_quant_scaled_mm_merged(const uint16_t* x, int64_t ldx, float s_act, uint
                                int64_t M, int64_t K,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* 1 if fp8_quant_scaled_mm_merged runs as one launch for an [M, K] activation
- * of row stride ldx, N output columns in total and scale s_act; else 0 (also
- * for arguments it would reject).  Host-only: launches nothing. */
-int fp8_quant_scaled_mm_fused(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act);
+/* The same with the fused RMSNorm quant: x_q = fp8_quant_rmsnorm(x, gamma,
+ * eps, s_act), then fp8_scaled_mm_merged (gamma == NULL: exactly
+ * fp8_quant_scaled_mm_merged).  One kernel where the plain form takes one and
+ * the rows are 36..40 chunks of 128 (K of 4608..5120: 8 waves, whose chunks
+ * hold each of the standalone kernel's 256 summing threads in one lane, so the
+ * row sums keep its order): the workgroups compute each row's r, then encode.
+ * x_q and the outputs are bitwise those of the two separate calls.
+ * gamma: bf16 [K] (DEVICE), 16-byte aligned, or NULL; eps finite >= 0.
+ * Errors: those of fp8_quant_rmsnorm and fp8_scaled_mm_merged. */
+int fp8_quant_rmsnorm_scaled_mm_merged(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
+                                       float s_act, uint8_t* x_q, const uint8_t* w_q, const float* s_w,
+                                       const fp8_shard_t* shards, int num_shards, int64_t M, int64_t K,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* 1 if fp8_quant_scaled_mm_merged (rmsnorm = 0) or
+ * fp8_quant_rmsnorm_scaled_mm_merged with a gamma (rmsnorm != 0) runs as one
+ * launch for an [M, K] activation of row stride ldx, N output columns in total
+ * and scale s_act; else 0 (also for arguments it would reject).  Host-only:
+ * launches nothing. */
+int fp8_quant_scaled_mm_fused(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act, int rmsnorm);
 
 /* ------------------------------------------------------------------------
  * F32-output variants (the A/B of vllm.cpp #417 Finding 1: an F32 output

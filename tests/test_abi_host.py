@@ -205,12 +205,28 @@ def test_quant_merged_validation_fails_closed(fp8):
     assert call(shards=(Shard * 1)(Shard(17400, D, 17408)), n=1) == U
     assert call(shards=(Shard * 1)(Shard(17408, None, 17408)), n=1) == E
     q = lib.fp8_quant_scaled_mm_fused
-    q.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_float]
-    assert q(9, 10240, 5120, 5120, 0.1) == 0                    # beyond the fused kernel's M
-    assert q(8, 10240, 5120, 5120, 2.0 ** -120) == 0            # outside the code table's range
-    assert q(8, 10240, 5120, 5000, 0.1) == 0                    # ldx < K
-    assert q(8, 10240, 5120, 5120, 0.0) == 0
-    assert q(0, 10240, 5120, 5120, 0.1) == 0
+    q.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_float, ctypes.c_int]
+    for rms in (0, 1):
+        assert q(9, 10240, 5120, 5120, 0.1, rms) == 0           # beyond the fused kernel's M
+        assert q(8, 10240, 5120, 5120, 2.0 ** -120, rms) == 0   # outside the quotient's exact range
+        assert q(8, 10240, 5120, 5000, 0.1, rms) == 0           # ldx < K
+        assert q(8, 10240, 5120, 5120, 0.0, rms) == 0
+        assert q(0, 10240, 5120, 5120, 0.1, rms) == 0
+    # the fused RMSNorm quant: its own argument checks, before any launch
+    h = lib.fp8_quant_rmsnorm_scaled_mm_merged
+    h.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(Shard), ctypes.c_int, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+
+    def rcall(gamma=D + 0x2000000, eps=1e-6, M=8, xq=B):
+        return h(A, 5120, gamma, eps, 0.1, xq, C, C + 0x100000, good, 2, M, 5120, None, 0, None)
+
+    assert rcall(M=0) == fp8.OK
+    assert rcall(eps=float("nan")) == E
+    assert rcall(eps=-1.0) == E
+    assert rcall(gamma=D + 0x2000000 + 2) == U
+    assert rcall(xq=A + 16) == E                                 # x_q overlaps x
+    assert rcall(gamma=None, eps=float("nan"), M=0) == fp8.OK   # no gamma: eps unused
 
 
 def test_quant_validation_fails_closed(fp8):

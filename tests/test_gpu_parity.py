@@ -671,6 +671,75 @@ def test_fused_quant_falls_back_to_two_launches(fp8, M, K, N, s_act):
     _check_fused(fp8, x, bf16_dev(x), s_act, wq, sw, [N], False, f"fallback M={M} K={K} N={N}")
 
 
+def _check_fused_rms(fp8, x, xd, g, eps, s_act, wq, sw, shards, fused, what):
+    """Fused RMSNorm quant + merged GEMM against fp8_quant_rmsnorm then the
+    merged GEMM: x_q and every output bit for bit (twice), x_q against the oracle."""
+    wd, swd, gd = u8_dev(wq), f32_dev(sw), bf16_dev(g)
+    M, K = x.shape
+    assert fp8.quant_scaled_mm_fused(M, sum(shards), K, xd.stride(0), s_act, rmsnorm=True) == fused, what
+    xq = fp8.quant_rmsnorm(xd, gd, s_act, eps)
+    want_q = host_u8(xq)
+    assert np.array_equal(want_q, oracle.quant_rmsnorm(x, g, eps, np.float32(s_act))), what
+    want = [host_u16(o) for o in fp8.scaled_mm_merged(xq, wd, s_act, swd, shards)]
+    for rep in range(2):
+        outs, xq2 = fp8.quant_rmsnorm_scaled_mm_merged(xd, gd, s_act, eps, wd, swd, shards)
+        assert np.array_equal(host_u8(xq2), want_q), f"{what}: x_q (call {rep})"
+        for i, (o, w) in enumerate(zip(outs, want)):
+            assert np.array_equal(host_u16(o), w), f"{what}: shard {i} (call {rep})"
+    return want, want_q
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("K,shards", [(5120, [17408, 17408]), (5120, [12288]), (5120, [12288, 1024, 1024]),
+                                      (4608, [5120])])
+def test_fused_rmsnorm_quant_merged_equals_two_calls(fp8, M, K, shards):
+    """The RMSNorm quant in the GEMM's launch (8 waves, rows of 36..40
+    chunks): the standalone kernel's bytes and the two calls' outputs, bit for
+    bit, and the outputs within the oracle's tolerance."""
+    x = wl.activation_bf16(3, M, K, outliers=True)
+    g = wl.gamma_bf16(3, K)
+    s_act = float(oracle.act_scale(x, g, wl.EPS))
+    wq, sw = oracle.quant_weight(wl.weight_f32(3, sum(shards), K))
+    want, xq = _check_fused_rms(fp8, x, bf16_dev(x), g, wl.EPS, s_act, wq, sw, shards, True, f"rms M={M} K={K}")
+    ref, v = oracle.scaled_mm(xq, wq, np.float32(s_act), sw, want_v=True)
+    assert_within_tolerance(np.concatenate(want, axis=1), ref, v, f"fused rms M={M} K={K}")
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.0])
+def test_fused_rmsnorm_quant_special_rows(fp8, eps):
+    """Zero rows (r = 1 / sqrt(eps), or inf at eps = 0: 0 * inf is NaN), -0,
+    subnormal, +-max, inf and NaN values, gamma with zeros, extremes and a NaN,
+    a strided activation: the same bytes as the standalone RMSNorm quant."""
+    M, K, ld = 8, 5120, 5136
+    x = wl.activation_bf16(3, M, K, outliers=True)
+    x[1] = 0
+    x[2] = 0x8000
+    x[3, :5] = np.array([0x0001, 0x8001, 0x7F7F, 0xFF7F, 0x0080], np.uint16)
+    x[4, 7] = 0x7F80                                   # +inf: r = 0
+    x[5, 100] = 0x7FC0                                 # NaN: r NaN
+    x[6] = (x[6].astype(np.uint32) & 0x80FF).astype(np.uint16) | 0x0100   # tiny values
+    g = wl.gamma_bf16(3, K)
+    g[:3] = np.array([0x0000, 0x7F7F, 0x0001], np.uint16)
+    g2 = g.copy()
+    g2[11] = 0x7FC0                                    # NaN in gamma: that column NaN in every row
+    s_act = 0.0137
+    wq, sw = oracle.quant_weight(wl.weight_f32(3, 12288, K))
+    for gg, nm in ((g, "gamma"), (g2, "NaN gamma")):
+        _check_fused_rms(fp8, x, _strided(x, ld), gg, eps, s_act, wq, sw, [12288], True, f"{nm} eps={eps}")
+
+
+@pytest.mark.parametrize("M,K,N,s_act", [(9, 5120, 12288, 0.01), (8, 4096, 12288, 0.01), (8, 6144, 5120, 0.01),
+                                         (8, 5120, 12288, 2.0 ** -120), (40, 5120, 2048, 0.01)])
+def test_fused_rmsnorm_quant_falls_back(fp8, M, K, N, s_act):
+    """Shapes the fused RMSNorm path does not take (M > 8, rows whose wave
+    count is not 8, a scale outside the exact quotient's range, the large-M
+    arm): two launches, the same bytes."""
+    x = wl.activation_bf16(4, M, K, outliers=True)
+    g = wl.gamma_bf16(4, K)
+    wq, sw = oracle.quant_weight(wl.weight_f32(4, N, K))
+    _check_fused_rms(fp8, x, bf16_dev(x), g, wl.EPS, s_act, wq, sw, [N], False, f"rms fallback M={M} K={K}")
+
+
 def test_fused_quant_empty_shapes(fp8):
     import torch
     K = 5120
