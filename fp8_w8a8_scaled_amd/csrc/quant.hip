@@ -432,19 +432,23 @@ __global__ __launch_bounds__(kQuantThreads) void k_absmax_final(
 
 // ---- SiLU*mul -> E4M3 (the MLP activation feeding the down projection) -----
 
-// h_b = bf16(fl32(s * u)) (bits), s = silu(g) from `silu` (silu_f64 itself, or
-// its table), for the 8 gate / up values of one 16-byte load each.
+// h_b = bf16(fl32(s * u)) (bits) for one gate / up pair of bf16 bits, with
+// s = silu(g) from `silu` (silu_f64 itself, or its table).
+template <class Silu>
+__device__ __forceinline__ uint32_t silu_mul1(uint32_t g, uint32_t u, Silu silu)
+{
+    return f32_to_bf16_rne(silu(g) * bf16_to_f32(u));
+}
+
+// silu_mul1 of the 8 gate / up values of one 16-byte load each.
 template <class Silu>
 __device__ __forceinline__ void silu_mul8(const uint4 g, const uint4 u, uint32_t hb[8], Silu silu)
 {
     const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
     const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float sg = silu((gw[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
-        const float uv = bf16_to_f32((uw[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
-        hb[i] = f32_to_bf16_rne(sg * uv);
-    }
+    for (int i = 0; i < 8; ++i)
+        hb[i] = silu_mul1((gw[i >> 1] >> ((i & 1) * 16)) & 0xffffu, (uw[i >> 1] >> ((i & 1) * 16)) & 0xffffu, silu);
 }
 
 struct SiluDirect {
@@ -456,29 +460,24 @@ struct CodeDirect {
     __device__ uint32_t operator()(uint32_t hb) const { return quant_value(bf16_to_f32(hb), s_act); }
 };
 
-template <class Silu, class Code>
-__device__ __forceinline__ uint2 silu_mul_quant8(const uint4 g, const uint4 u, Silu silu, Code code)
-{
-    uint32_t hb[8];
-    silu_mul8(g, u, hb, silu);
-    uint32_t o[2] = {0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j >> 2] |= code(hb[j]) << ((j & 3) * 8);
-    return make_uint2(o[0], o[1]);
-}
-
-// Few rows (decode): silu in fp64 and the IEEE division per element.
+// Few rows (decode): silu in fp64 and the IEEE division per element.  Each
+// thread takes two elements (4-byte loads, a 2-byte store), so a decode step's
+// M x I (8 x 17408: 70K threads) still spreads over every CU and each wave's
+// serial fp64 work stays short.
 __global__ __launch_bounds__(kQuantThreads) void k_silu_mul_quant(
     const uint16_t* __restrict__ gate, int64_t ldg, const uint16_t* __restrict__ up, int64_t ldu, float s_act,
     uint8_t* __restrict__ xq, int64_t M, int64_t I)
 {
-    const int64_t nv = I >> 3, total = M * nv;
+    const int64_t np = I >> 1, total = M * np;
+    const CodeDirect code{s_act};
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t m = i / nv, v = i - m * nv;
-        const uint4 g = *reinterpret_cast<const uint4*>(gate + m * ldg + v * 8);
-        const uint4 u = *reinterpret_cast<const uint4*>(up + m * ldu + v * 8);
-        *reinterpret_cast<uint2*>(xq + m * I + v * 8) = silu_mul_quant8(g, u, SiluDirect{}, CodeDirect{s_act});
+        const int64_t m = i / np, v = i - m * np;
+        const uint32_t g = *reinterpret_cast<const uint32_t*>(gate + m * ldg + v * 2);
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(up + m * ldu + v * 2);
+        const uint32_t lo = code(silu_mul1(g & 0xffffu, u & 0xffffu, SiluDirect{}));
+        const uint32_t hi = code(silu_mul1(g >> 16, u >> 16, SiluDirect{}));
+        *reinterpret_cast<uint16_t*>(xq + m * I + v * 2) = (uint16_t)(lo | (hi << 8));
     }
 }
 
@@ -799,8 +798,10 @@ void launch_silu_mul_quant(const uint16_t* gate, int64_t ldg, const uint16_t* up
                            dim3(kSiluLutThreads), 0, stream, gate, ldg,
                            up, ldu, s_act, xq, (uint32_t)(I >> 3), (uint32_t)total, I);
     } else {
-        hipLaunchKernelGGL(k_silu_mul_quant, dim3((uint32_t)plain_grid(M, I)), dim3(kQuantThreads), 0, stream, gate,
-                           ldg, up, ldu, s_act, xq, M, I);
+        // two elements per thread, at most 4096 workgroups (grid-stride beyond)
+        const int64_t blocks = (M * (I >> 1) + kQuantThreads - 1) / kQuantThreads;
+        hipLaunchKernelGGL(k_silu_mul_quant, dim3((uint32_t)(blocks < 4096 ? blocks : 4096)), dim3(kQuantThreads),
+                           0, stream, gate, ldg, up, ldu, s_act, xq, M, I);
     }
 }
 
