@@ -5,7 +5,10 @@
 // Both tables exist because the quantities are functions of one bf16 value:
 // SiLU of a bf16 gate, and the E4M3 code of a bf16 activation h under a fixed
 // static scale.  Building them costs a few thousand evaluations per
-// workgroup; the per-element path then needs one LDS read each.
+// workgroup; the per-element path then needs one LDS read each.  Where that
+// fill does not pay (few rows per workgroup, or a GEMM's own launch), the code
+// comes from the table-free encoder here instead: the exact quotient by
+// multiply and fused multiply-add, then the hardware E4M3 conversion.
 #pragma once
 
 #include "device_common.h"
@@ -230,6 +233,28 @@ __device__ __host__ __forceinline__ float quant_quotient(float a, float s, float
     return __builtin_fmaf(__builtin_fmaf(-q0, s, c), r, q0);
 }
 
+// The 4 E4M3 codes (bytes 0..3) of the bf16 values in words w0 (values 0, 1)
+// and w1 (values 2, 3) under the static quant, without a table: quant_quotient
+// of each magnitude (rcp = fl32(1 / s), sat = fl32(448 s)), encoded two at a
+// time by gfx950's conversion to E4M3 (round to nearest even like the
+// software encoder on every magnitude up to 464, which bounds the quotients
+// here), the signs from the bf16 sign bits.  A NaN gives a NaN quotient, whose
+// code has its 7 low bits set: 0x7F after the mask, with the value's sign;
+// inf takes sat and saturates.  Valid for 2^-100 <= s <= 2^100.
+__device__ __forceinline__ uint32_t quant4_cvt(uint32_t w0, uint32_t w1, float s, float rcp, float sat)
+{
+    float q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t h = i < 2 ? w0 : w1;
+        q[i] = quant_quotient(__builtin_fabsf(__builtin_bit_cast(float, i & 1 ? h & 0xffff0000u : h << 16)), s, rcp,
+                              sat);
+    }
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], c, true);
+    return ((uint32_t)c & 0x7f7f7f7fu) | (__builtin_amdgcn_perm(w1, w0, 0x07050301u) & 0x80808080u);
+}
+
 // The band-table codes (without sign) of the two bf16 magnitudes in word h:
 // entry clamp(|h| - lo1, 0, kCodeBand + 1) each, as bytes 0 and 1.  For
 // values that are not NaN (a NaN takes the saturated entry).
@@ -241,24 +266,17 @@ __device__ __host__ __forceinline__ uint32_t band_codes2(uint32_t h, const uint8
 }
 
 // The 8 E4M3 codes of the RMSNorm output y_b = bf16(fl32(fl32(x r) gamma)) of
-// one piece (x words w0..w3, gamma as fp32 gf[0..7]) under the band table
-// (entry 0 below the band, kCodeBand + 1 saturated).  Valid when r and gamma
-// are finite: |x r| <= sqrt(K), so y_b is finite or +-inf, never NaN, and its
-// code depends on its magnitude bits and sign only.  lo1 = code_band_lo - 1.
-__device__ __forceinline__ uint2 rms_codes8_band(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, const float* gf,
-                                                 float r, const uint8_t* tab, int lo1)
+// one piece (x words w0..w3, gamma as fp32 gf[0..7]) by quant4_cvt, for any r
+// and gamma (a NaN y_b takes 0x7F with its sign, +-inf saturates).
+__device__ __forceinline__ uint2 rms_codes8_cvt(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, const float* gf,
+                                                float r, float s, float rcp, float sat)
 {
     const uint32_t w[4] = {w0, w1, w2, w3};
     uint32_t h[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         h[i] = pack_bf16x2(bf16_to_f32(w[i] & 0xffffu) * r * gf[2 * i], bf16_to_f32(w[i] >> 16) * r * gf[2 * i + 1]);
-    uint32_t o[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)                         // the four sign bits: bits 15 and 31 of each pair
-        o[q] = band_codes2(h[2 * q], tab, (uint32_t)lo1) | (band_codes2(h[2 * q + 1], tab, (uint32_t)lo1) << 16) |
-               (__builtin_amdgcn_perm(h[2 * q + 1], h[2 * q], 0x07050301u) & 0x80808080u);
-    return make_uint2(o[0], o[1]);
+    return make_uint2(quant4_cvt(h[0], h[1], s, rcp, sat), quant4_cvt(h[2], h[3], s, rcp, sat));
 }
 
 // Bytes of a plain-quant band table: entries 0 .. kCodeBand + 2, padded.

@@ -574,30 +574,12 @@ struct XSrc {
 };
 
 // The 16 E4M3 codes of 16 bf16 values (words of a then b; value i in bits
-// 16 (i % 2) of word i / 2) under the plain static quant: quant_quotient of
-// each magnitude, encoded two at a time by the hardware conversion (rounding
-// to nearest even like the software encoder on every magnitude up to 464,
-// which bounds the quotients here), the sign from the bf16 sign bit.  A NaN
-// magnitude gives a NaN quotient, whose code has its 7 low bits set: 0x7F
-// after the mask, with the value's sign.
+// 16 (i % 2) of word i / 2) under the plain static quant, four at a time by
+// quant4_cvt (exact quotients, the hardware conversion, no table).
 __device__ __forceinline__ uint4 quant16_div(uint4 a, uint4 b, float s, float rcp, float sat)
 {
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float q[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t h = w[2 * k + (i >> 1)];
-            q[i] = quant_quotient(__builtin_fabsf(__builtin_bit_cast(float, i & 1 ? h & 0xffff0000u : h << 16)), s,
-                                  rcp, sat);
-        }
-        int c = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-        c = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], c, true);
-        o[k] = ((uint32_t)c & 0x7f7f7f7fu) | (__builtin_amdgcn_perm(w[2 * k + 1], w[2 * k], 0x07050301u) & 0x80808080u);
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
+    return make_uint4(quant4_cvt(a.x, a.y, s, rcp, sat), quant4_cvt(a.z, a.w, s, rcp, sat),
+                      quant4_cvt(b.x, b.y, s, rcp, sat), quant4_cvt(b.z, b.w, s, rcp, sat));
 }
 
 

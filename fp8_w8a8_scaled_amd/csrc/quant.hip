@@ -34,9 +34,8 @@ constexpr int64_t kPlainLutMinElems = 1LL << 20;  // plain quant: table path fro
 constexpr int kPlainLutPerCu = 2;
 constexpr int kPlainLutPieces = 2;
 constexpr int64_t kPlainHalfMaxElems = (1LL << 20) - 1;   // plain quant: 4 values per thread below this
-constexpr int64_t kRmsLutMinK = 2048;             // fused RMSNorm quant: shorter rows do not repay the table
-constexpr int kRmsLutGroups = 2;                  // ... 256-thread row groups per workgroup
-constexpr int kRmsLutPerCu = 2;                   // ... workgroups per CU
+constexpr int kRmsRowsGroups = 2;                 // fused RMSNorm quant: 256-thread row groups per workgroup
+constexpr int kRmsRowsPerCu = 2;                  // ... workgroups per CU
 
 // Fixed-order block reduction of a double (wave butterfly, then waves in order).
 __device__ double block_sum_f64(double v, double* lds)
@@ -131,14 +130,10 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_rmsnorm(
 }
 
 // The same bytes as k_quant_rmsnorm with the division and the encode replaced
-// by a lookup (K <= 2048 * PPT, 2^-100 <= s_act <= 2^100).  Once r and gamma
-// are finite, no y can be a NaN: |x * r| <= sqrt(K), so y is finite or
-// overflows to +-inf.  The code of y then depends only on the magnitude bits a
-// of y_b and its sign: a below code_band_lo(s_act) gives a signed zero, a at or
-// past lo + kCodeBand (inf included) the saturated code, and the kCodeBand
-// magnitudes between are looked up in a workgroup table filled once with the
-// exact division.  Rows with a non-finite value or r, or a non-finite gamma,
-// take the per-element path.
+// by rms_codes8_cvt (exact quotients by multiply and fused multiply-add, the
+// hardware E4M3 conversion; K <= 2048 * PPT, 2^-100 <= s_act <= 2^100, with
+// rcp = fl32(1 / s_act) and sat = fl32(448 s_act) from the host).  Every
+// value, inf and NaN included, takes the same path: no table, no fallback.
 //
 // A workgroup is G groups of 256 threads, persistent over rows: each group
 // takes one row at a time and sums its squares in k_quant_rmsnorm's order
@@ -147,8 +142,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_rmsnorm(
 // and of gamma in registers and loads its pieces of the group's next row
 // before the row's barrier.
 template <int G>
-struct RmsLutShared {
-    uint8_t tab[kCodeBand + 2];        // [0]: below the band, [1 + i]: band entry i, [kCodeBand + 1]: above
+struct RmsRowsShared {
     double part[2][G][kRmsRowThreads / 64];
 };
 
@@ -174,11 +168,11 @@ __device__ __forceinline__ void load_row_pieces(const uint16_t* __restrict__ x, 
 }
 
 template <int PPT, int G>
-__global__ __launch_bounds__(G * kRmsRowThreads) void k_quant_rmsnorm_lut(
+__global__ __launch_bounds__(G * kRmsRowThreads) void k_quant_rmsnorm_rows(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma, float eps,
-    float s_act, uint8_t* __restrict__ xq, int64_t M, int64_t K)
+    float s_act, float rcp, float sat, uint8_t* __restrict__ xq, int64_t M, int64_t K)
 {
-    __shared__ RmsLutShared<G> sh;
+    __shared__ RmsRowsShared<G> sh;
     const int grp = threadIdx.x / kRmsRowThreads, t = threadIdx.x % kRmsRowThreads;
     const int wave = t >> 6, lane = t & 63;
     const int nv = (int)(K >> 3);
@@ -189,26 +183,16 @@ __global__ __launch_bounds__(G * kRmsRowThreads) void k_quant_rmsnorm_lut(
     uint4 buf[2][PPT];
     load_row_pieces<PPT>(x, ldx, (int)m, M, K, t, buf[0]);
 
-    // gamma as fp32, fixed per thread; the lookup needs all of it finite
+    // gamma as fp32, fixed per thread
     float gf[PPT][8];
-    bool g_fin = true;
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
         const int v = t + p * kRmsRowThreads;
         const uint4 g = v < nv ? *reinterpret_cast<const uint4*>(gamma + (int64_t)v * 8) : make_uint4(0u, 0u, 0u, 0u);
         const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t b = (gw[i >> 1] >> ((i & 1) * 16)) & 0xffffu;
-            gf[p][i] = bf16_to_f32(b);
-            g_fin = g_fin && (b & 0x7fffu) < 0x7f80u;
-        }
+        for (int i = 0; i < 8; ++i) gf[p][i] = bf16_to_f32((gw[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
     }
-    const uint32_t lo = code_band_lo(s_act);
-    const int lo1 = (int)lo - 1;                         // table index of magnitude a: clamp(a - lo1)
-    fill_band_table(sh.tab, lo, s_act, threadIdx.x, blockDim.x);
-    if (threadIdx.x == 0) sh.tab[0] = 0u, sh.tab[kCodeBand + 1] = 0x7eu;
-    const bool gamma_ok = __syncthreads_and(g_fin);       // also orders the table before its first read
 
     // one row of the group: `in` holds it, `nx` receives the group's next row
     auto row_step = [&](const uint4 (&in)[PPT], uint4 (&nx)[PPT], int it) {
@@ -226,21 +210,11 @@ __global__ __launch_bounds__(G * kRmsRowThreads) void k_quant_rmsnorm_lut(
         const float r = rms_inv(tot, K, eps);
         uint8_t* out = xq + m * K;
         if (m >= M) return;
-        if (gamma_ok && __builtin_isfinite(tot) && __builtin_isfinite(r)) {
 #pragma unroll
-            for (int p = 0; p < PPT; ++p) {
-                const int v = t + p * kRmsRowThreads;
-                const uint2 o = rms_codes8_band(in[p].x, in[p].y, in[p].z, in[p].w, gf[p], r, sh.tab, lo1);
-                if (v < nv) *reinterpret_cast<uint2*>(out + (int64_t)v * 8) = o;
-            }
-        } else {
-            // the per-element path: a compact loop that reads the row again
-            const uint16_t* row = x + m * ldx;
-#pragma unroll 1
-            for (int v = t; v < nv; v += kRmsRowThreads)
-                *reinterpret_cast<uint2*>(out + (int64_t)v * 8) =
-                    rms_quant8(*reinterpret_cast<const uint4*>(row + (int64_t)v * 8),
-                               *reinterpret_cast<const uint4*>(gamma + (int64_t)v * 8), r, s_act);
+        for (int p = 0; p < PPT; ++p) {
+            const int v = t + p * kRmsRowThreads;
+            const uint2 o = rms_codes8_cvt(in[p].x, in[p].y, in[p].z, in[p].w, gf[p], r, s_act, rcp, sat);
+            if (v < nv) *reinterpret_cast<uint2*>(out + (int64_t)v * 8) = o;
         }
     };
     const int64_t first = (int64_t)blockIdx.x * G;       // the workgroup runs while its first group has a row
@@ -579,8 +553,8 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
 }
 
 // Plain static quant of many elements: the codes of quant8 from a 2563-byte
-// table of the band of magnitudes whose code needs the division (as in
-// k_quant_rmsnorm_lut; entry kCodeBand + 2 is unused padding), a NaN keeping
+// table of the band of magnitudes whose code needs the division (entry
+// kCodeBand + 2 is unused padding), a NaN keeping
 // its sign.  Each workgroup issues its first step's loads, fills the table,
 // then the grid sweeps the [M, K] pieces together, NP per thread per step (one
 // grid step between a thread's steps), without branches: a piece past the end
@@ -589,7 +563,6 @@ __global__ __launch_bounds__(kSiluLutThreads) void k_silu_mul_quant_lut(
 constexpr int kPlainLutThreads = 1024;
 static_assert(kPlainLutThreads % 128 == 0 && kSiluLutThreads % 128 == 0,
               "fill_band_table: one mantissa per thread across the binades");
-static_assert(kRmsLutGroups * kRmsRowThreads % 128 == 0, "fill_band_table: one mantissa per thread across the binades");
 
 template <int NP>
 __global__ __launch_bounds__(kPlainLutThreads) void k_quant_plain_lut(
@@ -710,19 +683,19 @@ void launch_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float e
                   uint8_t* xq, int64_t M, int64_t K, hipStream_t stream)
 {
     const int64_t ppt = ((K >> 3) + kRmsRowThreads - 1) / kRmsRowThreads;   // 16-byte pieces per thread
-    if (gamma && M < ((int64_t)1 << 30) && K >= kRmsLutMinK && ppt <= 4 &&
-        code_table_ok(s_act)) {
-        constexpr int G = kRmsLutGroups;
-        const int64_t want = (M + G - 1) / G, cap = (int64_t)num_cus() * kRmsLutPerCu;
+    if (gamma && M < ((int64_t)1 << 30) && ppt <= 4 && code_table_ok(s_act)) {
+        constexpr int G = kRmsRowsGroups;
+        const int64_t want = (M + G - 1) / G, cap = (int64_t)num_cus() * kRmsRowsPerCu;
         const dim3 grid((uint32_t)(want < cap ? want : cap)), block(G * kRmsRowThreads);
-        if (ppt <= 1)
-            hipLaunchKernelGGL((k_quant_rmsnorm_lut<1, G>), grid, block, 0, stream, x, ldx, gamma, eps, s_act, xq, M, K);
-        else if (ppt <= 2)
-            hipLaunchKernelGGL((k_quant_rmsnorm_lut<2, G>), grid, block, 0, stream, x, ldx, gamma, eps, s_act, xq, M, K);
-        else if (ppt <= 3)
-            hipLaunchKernelGGL((k_quant_rmsnorm_lut<3, G>), grid, block, 0, stream, x, ldx, gamma, eps, s_act, xq, M, K);
-        else
-            hipLaunchKernelGGL((k_quant_rmsnorm_lut<4, G>), grid, block, 0, stream, x, ldx, gamma, eps, s_act, xq, M, K);
+        const float rcp = 1.0f / s_act, sat = 448.0f * s_act;     // the quotient's operands, rounded once
+#define FP8MM_RMS_ROWS(PPT)                                                                                    \
+    hipLaunchKernelGGL((k_quant_rmsnorm_rows<PPT, G>), grid, block, 0, stream, x, ldx, gamma, eps, s_act, rcp, sat, \
+                       xq, M, K)
+        if (ppt <= 1) FP8MM_RMS_ROWS(1);
+        else if (ppt <= 2) FP8MM_RMS_ROWS(2);
+        else if (ppt <= 3) FP8MM_RMS_ROWS(3);
+        else FP8MM_RMS_ROWS(4);
+#undef FP8MM_RMS_ROWS
     } else if (gamma) {
         hipLaunchKernelGGL(k_quant_rmsnorm, dim3((uint32_t)M), dim3(kQuantThreads), 0, stream,
                            x, ldx, gamma, eps, s_act, xq, K);

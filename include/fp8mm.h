@@ -98,8 +98,10 @@ enum fp8mm_status {
  * gamma : bf16 [K] or NULL.
  * s_act : static per-tensor scale, finite and > 0 (FP8MM_EINVAL otherwise).
  * x_q   : E4M3 [M, K], contiguous (row stride K); must not overlap x.
- * With 2^-100 <= s_act <= 2^100, the fused form for 2048 <= K <= 8192 and the plain
- * form from 2^20 elements on take each code from a per-workgroup table of the
+ * With 2^-100 <= s_act <= 2^100, the fused form for K <= 8192 computes each
+ * quotient by multiply and fused multiply-add (exact: the same quotient as the
+ * division) and encodes it with the hardware conversion, and the plain form
+ * from 2^20 elements on takes each code from a per-workgroup table of the
  * same divisions (a NaN keeps the per-element rule); the bytes are the same.
  * ---------------------------------------------------------------------- */
 int fp8_quant_rmsnorm(const uint16_t* x, int64_t ldx,
