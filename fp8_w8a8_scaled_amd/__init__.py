@@ -58,6 +58,10 @@ _quant_rmsnorm_scaled_mm_merged = _decl("fp8_quant_rmsnorm_scaled_mm_merged",
                                          _I64, _P, _SZ, _P])
 _quant_scaled_mm_merged = _decl("fp8_quant_scaled_mm_merged",
                                 [_P, _I64, _F32, _P, _P, _P, ctypes.POINTER(Shard), _I32, _I64, _I64, _P, _SZ, _P])
+_gate_up_silu_quant = _decl("fp8_gate_up_silu_quant",
+                            [_P, _I64, _P, _F32, _F32, _P, _P, _P, _F32, _P, _I64, _I64, _I64, _P])
+_gate_up_silu_quant_fused = _decl("fp8_gate_up_silu_quant_fused", [_I64, _I64, _I64, _I64, _F32, _F32, _I32])
+_interleave_gate_up = _decl("fp8_interleave_gate_up", [_P, _P, _P, _P, _I64, _I64, _P])
 _quant_per_token = _decl("fp8_quant_per_token", [_P, _I64, _P, _F32, _P, _P, _I64, _I64, _P])
 _scaled_mm_per_token = _decl("fp8_scaled_mm_per_token", [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P])
 _scaled_mm_merged_per_token = _decl("fp8_scaled_mm_merged_per_token",
@@ -447,6 +451,80 @@ def quant_scaled_mm(x: torch.Tensor, s_act: float, w_q: torch.Tensor, s_w: torch
     """Static quant of bf16 x and one projection: returns (bf16 [M, N], x_q)."""
     outs, xq = quant_scaled_mm_merged(x, s_act, w_q, s_w, [w_q.shape[0]], None if out is None else [out], x_q)
     return outs[0], xq
+
+
+# ------------------------------------- gate_up with the SiLU*mul epilogue --
+
+def interleave_gate_up(w_q: torch.Tensor, s_w: torch.Tensor):
+    """Load-time layout of a merged gate_up weight [W_gate; W_up] (uint8 [2I, K],
+    f32 [2I]) for gate_up_silu_quant: 8 gate rows, then the up rows of the same
+    8 columns, per 16-row tile.  Returns (w_il, s_il)."""
+    w_q = _codes(w_q, "w_q")
+    _need(w_q.is_cuda and w_q.dim() == 2 and w_q.is_contiguous() and w_q.shape[0] % 2 == 0,
+          "w_q must be contiguous E4M3 codes [2I, K]")
+    _need(s_w.is_cuda and s_w.dtype == torch.float32 and s_w.is_contiguous() and s_w.numel() == w_q.shape[0],
+          "s_w must be a contiguous f32 CUDA tensor of 2I elements")
+    N, K = w_q.shape
+    w_il = torch.empty_like(w_q)
+    s_il = torch.empty_like(s_w)
+    _check(_interleave_gate_up(_ptr(w_q), _ptr(s_w), _ptr(w_il), _ptr(s_il), N // 2, K, _stream(w_q)),
+           "fp8_interleave_gate_up")
+    return w_il, s_il
+
+
+def gate_up_silu_quant_fused(M: int, I: int, K: int, s_act: float, s_down: float, quant: int = 0,
+                             ldx: Optional[int] = None) -> bool:
+    """Whether gate_up_silu_quant takes the shape: quant 0 (x_q given), 1 (plain
+    static quant of x in the launch), 2 (fused RMSNorm quant)."""
+    return bool(_gate_up_silu_quant_fused(M, I, K, K if ldx is None else ldx, float(s_act), float(s_down),
+                                          int(quant)))
+
+
+def gate_up_silu_quant(w_il: torch.Tensor, s_il: torch.Tensor, s_act: float, s_down: float,
+                       x_q: Optional[torch.Tensor] = None, x: Optional[torch.Tensor] = None,
+                       gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                       out: Optional[torch.Tensor] = None, x_q_out: Optional[torch.Tensor] = None):
+    """The merged gate_up projection on the interleaved weight with the SiLU*mul
+    -> E4M3 quant (scale s_down) as its epilogue, one launch: returns h_q uint8
+    [M, I].  Input: the codes x_q [M, K], or bf16 x [M, K] quantized in the
+    launch (with gamma: the fused RMSNorm quant; x_q_out, if given, receives
+    the codes).  Raises Fp8mmError (EUNSUPPORTED) where the launch does not
+    take the shape (gate_up_silu_quant_fused)."""
+    w_il = _codes(w_il, "w_il")
+    _need(w_il.is_cuda and w_il.dim() == 2 and w_il.is_contiguous(), "w_il must be contiguous E4M3 codes [2I, K]")
+    _need(s_il.is_cuda and s_il.dtype == torch.float32 and s_il.is_contiguous() and s_il.numel() == w_il.shape[0],
+          "s_il must be a contiguous f32 CUDA tensor of 2I elements")
+    N, K = w_il.shape
+    I = N // 2
+    if x is not None:
+        _need(x_q is None, "give x_q or x, not both")
+        _need(x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2 and x.shape[1] == K,
+              "x must be a bf16 CUDA tensor [M, K]")
+        ldx = _row_major(x, "x")
+        M = x.shape[0]
+        if gamma is not None:
+            _need(gamma.is_cuda and gamma.dtype == torch.bfloat16 and gamma.is_contiguous()
+                  and gamma.numel() == K, "gamma must be a contiguous bf16 CUDA tensor of K elements")
+        xq = None
+        if x_q_out is not None:
+            xq = _codes(x_q_out, "x_q_out")
+            _need(xq.is_contiguous() and tuple(xq.shape) == (M, K), "x_q_out must be contiguous uint8 [M, K]")
+        dev = x.device
+    else:
+        _need(x_q is not None and gamma is None, "x_q (codes) or x (bf16) is needed; gamma only with x")
+        xq = _codes(x_q, "x_q")
+        _need(xq.is_cuda and xq.is_contiguous() and xq.dim() == 2 and xq.shape[1] == K,
+              "x_q must be contiguous E4M3 codes [M, K]")
+        M, ldx = xq.shape[0], K
+        dev = xq.device
+    if out is None:
+        out = torch.empty((M, I), dtype=torch.uint8, device=dev)
+    out = _codes(out, "out")
+    _need(out.is_contiguous() and tuple(out.shape) == (M, I), "out must be contiguous uint8 [M, I]")
+    _check(_gate_up_silu_quant(_ptr(x), ldx, _ptr(gamma), float(eps), float(s_act), _ptr(xq), _ptr(w_il),
+                               _ptr(s_il), float(s_down), _ptr(out), M, I, K, _stream(w_il)),
+           "fp8_gate_up_silu_quant")
+    return out
 
 
 # ------------------------------------------------------ per-token scales --

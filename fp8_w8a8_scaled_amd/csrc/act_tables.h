@@ -255,6 +255,15 @@ __device__ __forceinline__ uint32_t quant4_cvt(uint32_t w0, uint32_t w1, float s
     return ((uint32_t)c & 0x7f7f7f7fu) | (__builtin_amdgcn_perm(w1, w0, 0x07050301u) & 0x80808080u);
 }
 
+// quant4_cvt of the two bf16 values of one word: codes in bytes 0 and 1.
+__device__ __forceinline__ uint32_t quant2_cvt(uint32_t w, float s, float rcp, float sat)
+{
+    const float q0 = quant_quotient(__builtin_fabsf(__builtin_bit_cast(float, w << 16)), s, rcp, sat);
+    const float q1 = quant_quotient(__builtin_fabsf(__builtin_bit_cast(float, w & 0xffff0000u)), s, rcp, sat);
+    const int c = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+    return ((uint32_t)c & 0x7f7fu) | (__builtin_amdgcn_perm(0u, w, 0x0c0c0301u) & 0x8080u);
+}
+
 // The band-table codes (without sign) of the two bf16 magnitudes in word h:
 // entry clamp(|h| - lo1, 0, kCodeBand + 1) each, as bytes 0 and 1.  For
 // values that are not NaN (a NaN takes the saturated entry).

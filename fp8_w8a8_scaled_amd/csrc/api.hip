@@ -400,6 +400,65 @@ int fp8_act_scale_silu_mul(const uint16_t* gate, int64_t ldg, const uint16_t* up
     return launch_status();
 }
 
+int fp8_interleave_gate_up(const uint8_t* w_q, const float* s_w, uint8_t* w_il, float* s_il, int64_t I, int64_t K,
+                           hipStream_t stream)
+{
+    if (I < 0 || K < 0) return FP8MM_EINVAL;
+    if (I % 16 != 0 || K % 16 != 0) return FP8MM_EUNSUPPORTED;
+    if (I == 0) return FP8MM_OK;
+    if (K == 0) return FP8MM_EUNSUPPORTED;
+    if (!w_q || !s_w || !w_il || !s_il) return FP8MM_EINVAL;
+    if (!aligned16(w_q) || !aligned16(w_il) || !aligned16(s_w) || !aligned16(s_il)) return FP8MM_EUNSUPPORTED;
+    if (I > ((int64_t)1 << 40) / K) return FP8MM_EUNSUPPORTED;
+    const size_t wb = (size_t)(2 * I * K), sb = (size_t)(2 * I) * 4;
+    if (overlaps(w_il, wb, w_q, wb) || overlaps(w_il, wb, s_w, sb) || overlaps(s_il, sb, w_q, wb) ||
+        overlaps(s_il, sb, s_w, sb) || overlaps(s_il, sb, w_il, wb))
+        return FP8MM_EINVAL;
+    fp8mm::launch_interleave_gate_up(w_q, s_w, w_il, s_il, I, K, stream);
+    return launch_status();
+}
+
+int fp8_gate_up_silu_quant_fused(int64_t M, int64_t I, int64_t K, int64_t ldx, float s_act, float s_down, int quant)
+{
+    if (M < 1 || I < 1 || K < 1 || I % 16 != 0 || K % 16 != 0 || quant < 0 || quant > 2 || !good_scale(s_act) ||
+        !good_scale(s_down))
+        return 0;
+    if (quant && (ldx < K || ldx % 8 != 0)) return 0;
+    return fp8_scaled_mm_select(M, 2 * I, K) == 0 && fp8mm::gate_up_silu_fits(M, I, K, ldx, s_act, s_down, quant)
+               ? 1 : 0;
+}
+
+int fp8_gate_up_silu_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, float s_act,
+                           uint8_t* x_q, const uint8_t* w_il, const float* s_il, float s_down, uint8_t* h_q,
+                           int64_t M, int64_t I, int64_t K, hipStream_t stream)
+{
+    if (M < 0 || I < 0 || K < 0) return FP8MM_EINVAL;
+    if (!good_scale(s_act) || !good_scale(s_down)) return FP8MM_EINVAL;
+    if (gamma && (!x || !(std::isfinite(eps) && eps >= 0.0f))) return FP8MM_EINVAL;
+    if (x && ldx < K) return FP8MM_EINVAL;
+    if (I % 16 != 0 || K % 16 != 0 || (x && ldx % 8 != 0)) return FP8MM_EUNSUPPORTED;
+    if (M == 0 || I == 0) return FP8MM_OK;
+    if (K == 0) return FP8MM_EUNSUPPORTED;
+    if (!w_il || !s_il || !h_q || (!x && !x_q)) return FP8MM_EINVAL;
+    if (!aligned16(w_il) || !aligned16(s_il) || !aligned16(h_q) || (x_q && !aligned16(x_q)) || (x && !aligned16(x)) ||
+        (gamma && !aligned16(gamma)))
+        return FP8MM_EUNSUPPORTED;
+    // h_q is written, and x_q too when the quant runs in the launch
+    const size_t hb = (size_t)(M * I), qb = (size_t)(M * K), wb = (size_t)(2 * I * K), sb = (size_t)(2 * I) * 4;
+    const size_t xb = x ? (size_t)((M - 1) * ldx + K) * 2 : 0;
+    if (overlaps(h_q, hb, w_il, wb) || overlaps(h_q, hb, s_il, sb) || (x_q && overlaps(h_q, hb, x_q, qb)) ||
+        (x && overlaps(h_q, hb, x, xb)) || (gamma && overlaps(h_q, hb, gamma, (size_t)K * 2)))
+        return FP8MM_EINVAL;
+    if (x && x_q && (overlaps(x_q, qb, x, xb) || overlaps(x_q, qb, w_il, wb) || overlaps(x_q, qb, s_il, sb) ||
+                     (gamma && overlaps(x_q, qb, gamma, (size_t)K * 2))))
+        return FP8MM_EINVAL;
+    const int quant = x ? (gamma ? 2 : 1) : 0;
+    if (!fp8_gate_up_silu_quant_fused(M, I, K, ldx, s_act, s_down, quant)) return FP8MM_EUNSUPPORTED;
+    if (!fp8mm::launch_gate_up_silu(x, ldx, gamma, eps, x_q, w_il, s_act, s_il, M, I, K, s_down, h_q, stream))
+        return FP8MM_EUNSUPPORTED;
+    return launch_status();
+}
+
 size_t fp8_act_scale_workspace_bytes(int64_t M, int64_t K)
 {
     if (M <= 0 || K <= 0) return 0;

@@ -573,6 +573,18 @@ struct XSrc {
     float eps;
 };
 
+// The SiLU*mul -> E4M3 epilogue of a gate_up launch.  The weight rows come
+// interleaved: 16-row tile t holds gate rows 8t .. 8t + 7, then the up rows of
+// the same 8 columns.  Instead of the bf16 gate_up output the kernel stores
+// h_q[m, j] = E4M3 code of fl32(h / s) for h = bf16(fl32(silu(g) u)), with g
+// and u the bf16 values the gate_up output would hold: E4M3 [M, I],
+// contiguous.  rcp = fl32(1 / s), sat = fl32(448 s).
+struct SiluOut {
+    uint8_t* hq;
+    int64_t I;
+    float s, rcp, sat;
+};
+
 // The 16 E4M3 codes of 16 bf16 values (words of a then b; value i in bits
 // 16 (i % 2) of word i / 2) under the plain static quant, four at a time by
 // quant4_cvt (exact quotients, the hardware conversion, no table).
@@ -634,6 +646,52 @@ __device__ __forceinline__ void load_bfrag(v8i (&b)[MT], __amdgpu_buffer_rsrc_t 
     }
 }
 
+// reduce_tile for the SiLU*mul epilogue (a whole tile of the interleaved
+// gate_up weight, activation scales in LDS): every lane sums its W partials
+// in wave order, scales its 4 columns and rounds them to bf16 as the gate_up
+// output would hold them.  Lanes l and l + 32 hold the gate and the up values
+// of the same 4 columns of one row and swap them; lane l < 32 then takes
+// columns 0, 1 and lane l + 32 columns 2, 3, and where the B tile has at most
+// 8 live rows (lanes with l % 16 >= 8 idle) a second swap leaves one column
+// per lane.  Each column: h = bf16(fl32(silu(g) u)) with silu in fp64, as in
+// the standalone SiLU*mul kernel, and its E4M3 code under so.s.  Every lane
+// takes part in the swaps.
+__device__ __forceinline__ void reduce_tile_silu(const v4f* __restrict__ red, int stride, int slot, int W, int64_t n0,
+                                                 const float4 sw, int M, int lane, int m_off,
+                                                 const float* __restrict__ srl, const SiluOut& so)
+{
+    const int r = lane & 15;
+    v4f s = red[slot];
+    for (int w = 1; w < W; ++w) {
+        const v4f p = red[w * stride + slot];
+        s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+    }
+    const float sa = srl[m_off + r];
+    const uint32_t v0 = f32_to_bf16_rne((s.x * sa) * sw.x) | (f32_to_bf16_rne((s.y * sa) * sw.y) << 16);
+    const uint32_t v1 = f32_to_bf16_rne((s.z * sa) * sw.z) | (f32_to_bf16_rne((s.w * sa) * sw.w) << 16);
+    const uint32_t o0 = (uint32_t)__shfl_xor((int)v0, 32, 64), o1 = (uint32_t)__shfl_xor((int)v1, 32, 64);
+    const bool hi = lane >= 32;
+    const uint32_t gw = hi ? o1 : v0, uw = hi ? v1 : o0;   // columns 2 hi, 2 hi + 1: gate, up
+    // h_q column of this lane's first value
+    const int64_t j = (n0 >> 1) + 4 * ((lane >> 4) & 1) + 2 * (hi ? 1 : 0);
+    if (M - m_off <= 8) {
+        // rows 0..7 only: lane l + 8 takes the second column of lane l's pair
+        const uint32_t g2 = (uint32_t)__shfl_xor((int)gw, 8, 64), u2 = (uint32_t)__shfl_xor((int)uw, 8, 64);
+        const bool second = (lane & 8) != 0;
+        const int m = m_off + (lane & 7);
+        if (m >= M) return;
+        const uint32_t gb = second ? g2 >> 16 : gw & 0xffffu, ub = second ? u2 >> 16 : uw & 0xffffu;
+        const uint32_t h = f32_to_bf16_rne(silu_f64(bf16_to_f32(gb)) * bf16_to_f32(ub));
+        so.hq[(int64_t)m * so.I + j + (second ? 1 : 0)] = (uint8_t)quant2_cvt(h, so.s, so.rcp, so.sat);
+    } else {
+        const int m = m_off + r;
+        if (m >= M) return;
+        const uint32_t h = f32_to_bf16_rne(silu_f64(bf16_to_f32(gw & 0xffffu)) * bf16_to_f32(uw & 0xffffu)) |
+                           (f32_to_bf16_rne(silu_f64(bf16_to_f32(gw >> 16)) * bf16_to_f32(uw >> 16)) << 16);
+        *reinterpret_cast<uint16_t*>(so.hq + (int64_t)m * so.I + j) = (uint16_t)quant2_cvt(h, so.s, so.rcp, so.sat);
+    }
+}
+
 // Workgroup barrier for LDS data written by the waves' own stores: wait for
 // this wave's LDS stores (lgkmcnt), then s_barrier; the empty asm statements
 // keep the compiler from moving memory accesses across it.  __syncthreads()
@@ -651,14 +709,16 @@ __device__ __forceinline__ void lds_barrier()
 // never a target of the in-flight direct-to-LDS loads).
 __device__ __forceinline__ void put_partial(v4f* __restrict__ dst, v4f v) { *dst = v; }
 
-// (XM_QRMS runs 8 waves: its bound leaves each lane 256 registers, which the
-// activation, gamma and fragments of 5 chunks need.)
-template <int S, int MT, int XM, int CPW, bool BAL, bool DEFER>
-__global__ __launch_bounds__(XM == XM_QRMS ? 64 * 8 : 64 * kMaxWaves) void k_gemm_small_m_rx(
+// (XM_QRMS and the SiLU*mul epilogue run at most 8 waves: the bound leaves
+// each lane 256 registers, which the activation, gamma and fragments of 5
+// chunks, or 2 B tiles' fragments and the epilogue's fp64 work, need.)
+template <int S, int MT, int XM, int CPW, bool BAL, bool DEFER, bool SILU>
+__global__ __launch_bounds__(XM == XM_QRMS || SILU ? 64 * 8 : 64 * kMaxWaves) void k_gemm_small_m_rx(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act, const float* __restrict__ s_w,
-    ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw, XSrc xs)
+    ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw, XSrc xs, SiluOut so)
 {
     static_assert(XM == XM_STREAM || CPW > 0, "resident fragments need a compile-time chunk count");
+    static_assert(!SILU || (!BAL && !DEFER), "the SiLU*mul epilogue: whole tiles, reduced one at a time");
     static_assert((XM != XM_LDS && XM != XM_QLDS && XM != XM_QRMS) || MT == 1, "fragments through LDS: M <= 16");
     constexpr bool kQ = XM == XM_QLDS || XM == XM_QRMS;   // the activation quantized in the kernel
     constexpr bool kLds = XM == XM_LDS || kQ;            // fragments staged in LDS
@@ -941,12 +1001,17 @@ __global__ __launch_bounds__(XM == XM_QRMS ? 64 * 8 : 64 * kMaxWaves) void k_gem
             lds_barrier();
             int rt, re;
             tile_rows(u, rt, re);
-            if (wave == 0) {
+            // the SiLU*mul epilogue's fp64 work goes round the waves, one tile each
+            if (wave == (SILU ? u % W : 0)) {
                 const float4 sw4 = lds_f4(swl + u * 16 + 4 * g);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    reduce_tile(rb + mt * 64, MT * 64, lane, W, rt, re, s_act, sw4, sh, M, lane, BAL && u >= FR,
-                                16 * mt, srl);
+                for (int mt = 0; mt < MT; ++mt) {
+                    if constexpr (SILU)
+                        reduce_tile_silu(rb + mt * 64, MT * 64, lane, W, rt, sw4, M, lane, 16 * mt, srl, so);
+                    else
+                        reduce_tile(rb + mt * 64, MT * 64, lane, W, rt, re, s_act, sw4, sh, M, lane, BAL && u >= FR,
+                                    16 * mt, srl);
+                }
             }
         }
 #pragma unroll
@@ -1270,7 +1335,7 @@ struct RxPlan {
     unsigned G, W;
 };
 
-bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p, size_t extra = 0)
+bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p, size_t extra = 0, bool no_defer = false)
 {
     if (M < 1 || M > 32 || K % kChunk != 0 || N * K >= ((int64_t)1 << 31) || M * K >= ((int64_t)1 << 31)) return false;
     const int W = small_m_waves(K);
@@ -1300,7 +1365,7 @@ bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p, size_t extra = 0)
     const size_t swb = 256 + (size_t)(tiles_max + 3) / 4 * 256 + extra;   // the rows' and the tiles' scales
     for (const size_t xlb : {xl, (size_t)0})
         for (const auto& o : order)
-            if (bytes(o.S, o.df) + xlb + swb <= 160 * 1024 && (o.df || p->xm != XM_STREAM)) {
+            if (bytes(o.S, o.df) + xlb + swb <= 160 * 1024 && (o.df || p->xm != XM_STREAM) && !(o.df && no_defer)) {
                 if (xlb) p->xm = XM_LDS;
                 p->S = o.S;
                 p->defer = o.df;
@@ -1310,25 +1375,26 @@ bool plan_rx(int64_t M, int64_t N, int64_t K, RxPlan* p, size_t extra = 0)
     return false;
 }
 
-#define FP8MM_RX_ARGS p, xq, wq, s_act, s_w, sh, M, N, K, nchunks, xs, stream
-template <int S, int MT, int XM, int CPW, bool BAL, bool DEFER>
+#define FP8MM_RX_ARGS p, xq, wq, s_act, s_w, sh, M, N, K, nchunks, xs, so, stream
+template <int S, int MT, int XM, int CPW, bool BAL, bool DEFER, bool SILU = false>
 void launch_rx(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
-               const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, const XSrc& xs, hipStream_t stream)
+               const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, const XSrc& xs, const SiluOut& so,
+               hipStream_t stream)
 {
     static const bool attr = [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_rx<S, MT, XM, CPW, BAL, DEFER>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_rx<S, MT, XM, CPW, BAL, DEFER, SILU>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         return true;
     }();
     (void)attr;
-    hipLaunchKernelGGL((k_gemm_small_m_rx<S, MT, XM, CPW, BAL, DEFER>), dim3(p.G), dim3(64 * p.W), p.lds, stream, xq,
-                       wq, s_act, s_w, sh, M, N, K, nchunks, p.cpw, xs);
+    hipLaunchKernelGGL((k_gemm_small_m_rx<S, MT, XM, CPW, BAL, DEFER, SILU>), dim3(p.G), dim3(64 * p.W), p.lds, stream,
+                       xq, wq, s_act, s_w, sh, M, N, K, nchunks, p.cpw, xs, so);
 }
 
 template <int MT, int XM, int CPW, bool BAL>
 void dispatch_rx_sd(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
                     const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, const XSrc& xs,
-                    hipStream_t stream)
+                    const SiluOut& so, hipStream_t stream)
 {
     constexpr bool kStream = XM == XM_STREAM;   // streamed fragments: deferred reduction only
     if (p.S == 6 && p.defer) launch_rx<6, MT, XM, CPW, BAL, true>(FP8MM_RX_ARGS);
@@ -1345,23 +1411,36 @@ void dispatch_rx_sd(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float
 
 template <int MT, int XM, int CPW>
 void dispatch_rx(const RxPlan& p, const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
-                 const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, const XSrc& xs, hipStream_t stream)
+                 const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, const XSrc& xs, const SiluOut& so,
+                 hipStream_t stream)
 {
-    if (p.bal) dispatch_rx_sd<MT, XM, CPW, true>(FP8MM_RX_ARGS);
-    else dispatch_rx_sd<MT, XM, CPW, false>(FP8MM_RX_ARGS);
+    if (so.hq) {                                         // the SiLU*mul epilogue: whole tiles, no deferral
+        if constexpr (XM != XM_STREAM) {                 // (streamed fragments need the deferral)
+            if (p.S == 6) launch_rx<6, MT, XM, CPW, false, false, true>(FP8MM_RX_ARGS);
+            else if (p.S == 4) launch_rx<4, MT, XM, CPW, false, false, true>(FP8MM_RX_ARGS);
+            else if (p.S == 3) launch_rx<3, MT, XM, CPW, false, false, true>(FP8MM_RX_ARGS);
+            else launch_rx<2, MT, XM, CPW, false, false, true>(FP8MM_RX_ARGS);
+        }
+    } else if (p.bal) {
+        dispatch_rx_sd<MT, XM, CPW, true>(FP8MM_RX_ARGS);
+    } else {
+        dispatch_rx_sd<MT, XM, CPW, false>(FP8MM_RX_ARGS);
+    }
 }
 
 // Launch the register-fragment kernel if it takes this shape.  With xsrc, the
 // fused static quant: only the XM_QLDS plan (M <= 8, fragments staged in LDS),
 // else false.
 bool try_rx(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w, const ShardTable& sh, int64_t M64,
-            int64_t N, int64_t K, hipStream_t stream, const XSrc* xsrc = nullptr)
+            int64_t N, int64_t K, hipStream_t stream, const XSrc* xsrc = nullptr, const SiluOut* silu = nullptr)
 {
     RxPlan p;
     const bool rms = xsrc && xsrc->gamma;
-    if (!plan_rx(M64, N, K, &p, rms ? 32 : 0)) return false;   // XM_QRMS: the rows' r after the scales
+    // XM_QRMS: the rows' r after the scales; the SiLU*mul epilogue: whole tiles
+    if (!plan_rx(M64, N, K, &p, rms ? 32 : 0, silu != nullptr) || (silu && p.bal)) return false;
     const int M = (int)M64, nchunks = (int)(K / kChunk);
     const XSrc xs = xsrc ? *xsrc : XSrc{nullptr, 0, nullptr, 0.0f, 0.0f, nullptr, 0.0f};
+    const SiluOut so = silu ? *silu : SiluOut{nullptr, 0, 0.0f, 0.0f, 0.0f};
     if (rms) {
         if (p.xm != XM_LDS || M > 8 || p.W != 8 || p.cpw != 5) return false;
         dispatch_rx<1, XM_QRMS, 5>(FP8MM_RX_ARGS);
@@ -1457,6 +1536,39 @@ bool launch_quant_gemm_small_m(const uint16_t* x, int64_t ldx, const uint16_t* g
     // the quotient's operands, rounded once here (IEEE single on the host)
     const XSrc xs{x, ldx, xq_out, 1.0f / s_act, 448.0f * s_act, gamma, eps};
     return try_rx(nullptr, wq, s_act, s_w, shards, M, N, K, stream, &xs);
+}
+
+bool gate_up_silu_fits(int64_t M, int64_t I, int64_t K, int64_t ldx, float s_act, float s_down, int quant)
+{
+    if (M < 1 || M > 32 || I < 8 || I % 8 != 0 || !code_table_ok(s_down)) return false;
+    // with the quant in the launch: as quant_gemm_small_m_fits
+    if (quant && (M > 8 || ldx < K || !code_table_ok(s_act) || ((M - 1) * ldx + K) * 2 >= ((int64_t)1 << 31)))
+        return false;
+    RxPlan p;
+    if (!plan_rx(M, 2 * I, K, &p, quant == 2 ? 32 : 0, true) || p.bal || p.W > 8) return false;
+    if (quant && p.xm != XM_LDS) return false;
+    return quant != 2 || (p.W == 8 && p.cpw == 5);
+}
+
+bool launch_gate_up_silu(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, uint8_t* xq,
+                         const uint8_t* wq, float s_act, const float* s_w, int64_t M, int64_t I, int64_t K,
+                         float s_down, uint8_t* hq, hipStream_t stream)
+{
+    const int quant = x ? (gamma ? 2 : 1) : 0;
+    if (!gate_up_silu_fits(M, I, K, ldx, s_act, s_down, quant)) return false;
+    // one shard over the interleaved rows; the epilogue stores h_q instead
+    ShardTable sh{};
+    sh.num = 1;
+    sh.start[1] = 2 * I;
+    sh.out[0] = hq;
+    sh.ldo[0] = I;
+    // the quotients' operands, rounded once here (IEEE single on the host)
+    const SiluOut so{hq, I, s_down, 1.0f / s_down, 448.0f * s_down};
+    if (quant) {
+        const XSrc xs{x, ldx, xq, 1.0f / s_act, 448.0f * s_act, gamma, eps};
+        return try_rx(nullptr, wq, s_act, s_w, sh, M, 2 * I, K, stream, &xs, &so);
+    }
+    return try_rx(xq, wq, s_act, s_w, sh, M, 2 * I, K, stream, nullptr, &so);
 }
 
 void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,

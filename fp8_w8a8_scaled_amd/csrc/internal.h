@@ -68,6 +68,18 @@ void launch_gemm_small_m(const uint8_t* xq, const uint8_t* wq, float s_act, cons
 // quantizes and multiplies separately.  quant_gemm_small_m_fits: whether it
 // takes the shape (the host-side plan only).
 bool quant_gemm_small_m_fits(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act, bool rmsnorm);
+// The gate_up launch with the SiLU*mul -> E4M3 quant as its epilogue (weight
+// rows interleaved 8 gate / 8 up per 16-row tile, N = 2I; h_q E4M3 [M, I]).
+// quant: 0 = x_q given (x NULL), 1 = plain static quant of x in the launch,
+// 2 = fused RMSNorm quant (gamma); x_q is then written when not NULL.
+// gate_up_silu_fits: whether the launch takes the shape (else
+// launch_gate_up_silu returns false and launches nothing).
+bool gate_up_silu_fits(int64_t M, int64_t I, int64_t K, int64_t ldx, float s_act, float s_down, int quant);
+bool launch_gate_up_silu(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, uint8_t* xq,
+                         const uint8_t* wq, float s_act, const float* s_w, int64_t M, int64_t I, int64_t K,
+                         float s_down, uint8_t* hq, hipStream_t stream);
+void launch_interleave_gate_up(const uint8_t* wq, const float* s_w, uint8_t* w_il, float* s_il, int64_t I,
+                               int64_t K, hipStream_t stream);
 bool launch_quant_gemm_small_m(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, uint8_t* xq_out,
                                const uint8_t* wq, float s_act, const float* s_w, const ShardTable& shards, int64_t M,
                                int64_t N, int64_t K, hipStream_t stream);

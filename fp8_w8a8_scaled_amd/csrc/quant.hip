@@ -670,6 +670,25 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_weight(
     }
 }
 
+// Load-time layout of a merged gate_up weight for the SiLU*mul epilogue: row
+// 16t + i of w_il is gate row 8t + i (i < 8) or up row 8t + i - 8 (rows I +
+// 8t + i - 8 of the merged [gate; up] weight), and s_il follows the rows.
+// One thread per 16-byte piece.
+__global__ __launch_bounds__(kQuantThreads) void k_interleave_gate_up(
+    const uint8_t* __restrict__ wq, const float* __restrict__ s_w, uint8_t* __restrict__ w_il,
+    float* __restrict__ s_il, int64_t I, int64_t K)
+{
+    const int64_t nv = K >> 4, total = 2 * I * nv;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = i / nv, v = i - row * nv;
+        const int64_t t = row >> 4, k = row & 15;
+        const int64_t src = k < 8 ? 8 * t + k : I + 8 * t + (k - 8);
+        *reinterpret_cast<uint4*>(w_il + row * K + v * 16) = *reinterpret_cast<const uint4*>(wq + src * K + v * 16);
+        if (v == 0) s_il[row] = s_w[src];
+    }
+}
+
 int64_t plain_grid(int64_t M, int64_t K)
 {
     const int64_t total = M * (K >> 3);
@@ -820,6 +839,14 @@ hipError_t noalloc_scratch(float** ptr)
 void launch_quant_weight(const float* w, int64_t N, int64_t K, uint8_t* wq, float* s_w, hipStream_t stream)
 {
     hipLaunchKernelGGL(k_quant_weight, dim3((uint32_t)N), dim3(kQuantThreads), 0, stream, w, K, wq, s_w);
+}
+
+void launch_interleave_gate_up(const uint8_t* wq, const float* s_w, uint8_t* w_il, float* s_il, int64_t I,
+                               int64_t K, hipStream_t stream)
+{
+    const int64_t blocks = (2 * I * (K >> 4) + kQuantThreads - 1) / kQuantThreads;
+    hipLaunchKernelGGL(k_interleave_gate_up, dim3((uint32_t)(blocks < 4096 ? blocks : 4096)), dim3(kQuantThreads), 0,
+                       stream, wq, s_w, w_il, s_il, I, K);
 }
 
 }  // namespace fp8mm

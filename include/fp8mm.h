@@ -258,6 +258,55 @@ int fp8_quant_rmsnorm_scaled_mm_merged(const uint16_t* x, int64_t ldx, const uin
 int fp8_quant_scaled_mm_fused(int64_t M, int64_t N, int64_t K, int64_t ldx, float s_act, int rmsnorm);
 
 /* ------------------------------------------------------------------------
+ * Merged gate_up projection with the SiLU*mul -> FP8 quant as its epilogue
+ * (the gate/up pair of the tower, vllm.cpp #252 "SETTLED BY PAIRED TRACE";
+ * quantize once for the next GEMM, vllm.cpp #417, ranked follow-ons): for the
+ * decode MLP, one launch computes
+ *     h_q = fp8_silu_mul_quant(gate, up, s_down)
+ * of [gate | up] = fp8_scaled_mm_merged(x_q, [W_gate; W_up], s_act, s_w)
+ * without writing the bf16 gate_up output; with x != NULL the activation
+ * quant runs in the same launch as in fp8_quant_rmsnorm_scaled_mm_merged
+ * (gamma != NULL: the fused RMSNorm quant).  h_q (and x_q when written) are
+ * bitwise those of the separate calls on the merged weight.
+ *
+ * The weight comes in the layout fp8_interleave_gate_up writes: each 16-row
+ * tile holds 8 gate rows, then the up rows of the same 8 columns, so one
+ * workgroup owns both halves of every column it reduces.
+ *
+ * x, ldx, gamma, eps: as fp8_quant_rmsnorm_scaled_mm_merged, or x == NULL
+ *          (and gamma == NULL): x_q is the input.
+ * s_act  : static scale of x_q, finite > 0.
+ * x_q    : E4M3 [M, K] (DEVICE), contiguous: the input when x == NULL, else
+ *          written when not NULL.
+ * w_il   : E4M3 [2I, K] (DEVICE), interleaved; s_il: f32 [2I], interleaved.
+ * s_down : static scale of h_q (the down projection's input), finite > 0.
+ * h_q    : E4M3 [M, I] (DEVICE), contiguous, written; overlaps no input.
+ * I % 16 == 0, K % 16 == 0, 16-byte aligned pointers.  FP8MM_EUNSUPPORTED
+ * (nothing launched) unless fp8_gate_up_silu_quant_fused accepts the call:
+ * the caller then runs the separate calls on the merged weight.
+ * ---------------------------------------------------------------------- */
+int fp8_gate_up_silu_quant(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps, float s_act,
+                           uint8_t* x_q, const uint8_t* w_il, const float* s_il, float s_down, uint8_t* h_q,
+                           int64_t M, int64_t I, int64_t K, hipStream_t stream);
+
+/* 1 if fp8_gate_up_silu_quant takes an [M, K] activation (row stride ldx),
+ * I gate columns and the scales s_act, s_down, with quant = 0 (x_q given),
+ * 1 (plain static quant of x) or 2 (fused RMSNorm quant); else 0.  It needs
+ * the small-M arm (fp8_scaled_mm_select(M, 2I, K) == 0), M <= 32 (M <= 8 with
+ * the quant in the launch), 2^-100 <= s_down <= 2^100 (and s_act with the
+ * quant), and a plan of whole 16-row tiles per workgroup.  Host-only. */
+int fp8_gate_up_silu_quant_fused(int64_t M, int64_t I, int64_t K, int64_t ldx, float s_act, float s_down, int quant);
+
+/* Load-time layout for fp8_gate_up_silu_quant: from the merged gate_up
+ * weight w_q = [W_gate; W_up] (E4M3 [2I, K]) and its scales s_w (f32 [2I]),
+ * row 16t + i of w_il is gate row 8t + i for i < 8 and up row 8t + i - 8
+ * (merged row I + 8t + i - 8) for i >= 8; s_il follows the rows.  A copy:
+ * outputs must not overlap inputs.  I % 16 == 0, K % 16 == 0, 16-byte
+ * aligned pointers. */
+int fp8_interleave_gate_up(const uint8_t* w_q, const float* s_w, uint8_t* w_il, float* s_il, int64_t I, int64_t K,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * F32-output variants (the A/B of vllm.cpp #417 Finding 1: an F32 output
  * doubles the bytes of the largest activation buffers against the model's
  * bf16).  Same kernels, same arithmetic and kernel choice; the epilogue stores

@@ -290,6 +290,76 @@ def test_silu_mul_validation_fails_closed(fp8):
     assert g(A, L, A + 2 * I, L, 8, I, C, D + 8, ws, None) == U
 
 
+def test_gate_up_silu_validation_fails_closed(fp8):
+    """The gate_up launch with the SiLU*mul epilogue, its plan query and the
+    weight interleave check their arguments before launching anything; a shape
+    outside the fused plans is FP8MM_EUNSUPPORTED (the caller then runs the
+    separate calls)."""
+    lib = fp8.raw_lib()
+    P, I64, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    f = lib.fp8_gate_up_silu_quant
+    f.argtypes = [P, I64, P, F32, F32, P, P, P, F32, P, I64, I64, I64, P]
+    E, U = fp8.EINVAL, fp8.EUNSUPPORTED
+
+    def call(x=None, ldx=5120, gamma=None, eps=1e-6, s=0.1, xq=B, w=C, sw=C + 0xC000000, sd=0.05, hq=D, M=8,
+             I=17408, K=5120):
+        return f(x, ldx, gamma, eps, s, xq, w, sw, sd, hq, M, I, K, None)
+
+    assert call(M=0) == fp8.OK
+    assert call(I=0) == fp8.OK
+    assert call(M=-1) == E
+    assert call(s=0.0) == E
+    assert call(sd=float("nan")) == E
+    assert call(gamma=A) == E                                    # gamma without x
+    assert call(x=A, gamma=A + 0x1000000, eps=-1.0) == E
+    assert call(x=A, ldx=5000) == E                              # ldx < K
+    assert call(I=17400) == U                                    # I % 16
+    assert call(K=5112) == U                                     # K % 16
+    assert call(x=A, ldx=5124) == U                              # ldx % 8
+    assert call(K=0) == U
+    assert call(w=None) == E
+    assert call(hq=None) == E
+    assert call(xq=None) == E                                    # neither x nor x_q
+    assert call(hq=D + 8) == U
+    assert call(sw=C + 0xC000000 + 4) == U
+    assert call(x=A + 2) == U
+    assert call(hq=C + 16) == E                                  # h_q overlaps the weight
+    assert call(hq=B + 64) == E                                  # h_q overlaps x_q
+    assert call(x=A, xq=A + 16) == E                             # x_q (written) overlaps x
+    assert call(M=33) == U                                       # the large-M arm (threshold 32)
+    assert call(x=A, M=9) == U                                   # the quant in the launch: M <= 8
+    assert call(sd=2.0 ** -120) == U                             # outside the quotient's exact range
+    q = lib.fp8_gate_up_silu_quant_fused
+    q.argtypes = [I64, I64, I64, I64, F32, F32, ctypes.c_int]
+    assert q(33, 17408, 5120, 5120, 0.1, 0.05, 0) == 0
+    assert q(9, 17408, 5120, 5120, 0.1, 0.05, 1) == 0
+    assert q(9, 17408, 5120, 5120, 0.1, 0.05, 2) == 0
+    assert q(8, 17408, 5120, 5120, 0.1, 2.0 ** -120, 0) == 0
+    assert q(8, 17408, 5120, 5120, 2.0 ** -120, 0.05, 1) == 0
+    assert q(8, 17400, 5120, 5120, 0.1, 0.05, 0) == 0
+    assert q(8, 17408, 5120, 5120, 0.1, 0.05, 3) == 0
+    assert q(8, 17408, 5120, 5000, 0.1, 0.05, 2) == 0
+    assert q(0, 17408, 5120, 5120, 0.1, 0.05, 0) == 0
+    g = lib.fp8_interleave_gate_up
+    g.argtypes = [P, P, P, P, I64, I64, P]
+
+    def icall(w=A, sw=B, wil=C, sil=D, I=17408, K=5120):
+        return g(w, sw, wil, sil, I, K, None)
+
+    assert icall(I=0) == fp8.OK
+    assert icall(I=-16) == E
+    assert icall(I=17400) == U
+    assert icall(K=5112) == U
+    assert icall(K=0) == U
+    assert icall(w=None) == E
+    assert icall(sil=None) == E
+    assert icall(wil=C + 8) == U
+    assert icall(sw=B + 4) == U
+    assert icall(wil=A + 16) == E                                # w_il overlaps w_q
+    assert icall(sil=B + 16) == E                                # s_il overlaps s_w
+    assert icall(sil=C + 64) == E                                # s_il overlaps w_il
+
+
 def test_f32_output_validation_fails_closed(fp8):
     lib = fp8.raw_lib()
     f = lib.fp8_scaled_mm_f32
