@@ -1110,11 +1110,19 @@ __global__ __launch_bounds__(XM == XM_QRMS || SILU ? 64 * 8 : 64 * kMaxWaves) vo
 // reduction are those of the other kernels: the same bits.  At the end each
 // wave writes its partial sums into its own ring area (its loads have all
 // landed) and the workgroup reduces them.
-template <int S, int MT, bool BAL>
+// SHORT (balanced, at most 8 rows in every workgroup's second tile): that
+// tile's chunk takes 1 KB of the slot (rows 0..7, one load), so a slot is
+// 3 KB and a third slot fits in LDS.  Its A fragment rows 8..15 then read
+// whatever follows (the next slot, or the 1 KB of padding after the rings):
+// they only reach output rows past the tile's end, which are never stored.
+template <int S, int MT, bool BAL, bool SHORT>
 __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_pair(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ wq, float s_act, const float* __restrict__ s_w,
     ShardTable sh, int M, int64_t N, int64_t K, int nchunks, int cpw)
 {
+    static_assert(!SHORT || BAL, "a short second tile is a balanced share");
+    constexpr int SB = SHORT ? 3072 : 4096;             // slot bytes
+    constexpr int NW = SHORT ? 3 : 4;                   // weight loads per position
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int W = blockDim.x >> 6;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1138,11 +1146,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_pair(
         re[1] = bid + G < ntiles ? rt[1] + 16 : rt[1];
     }
     const int my_tiles = re[1] > rt[1] ? 2 : 1;
-    // LDS: [W rings of S 4 KB slots (two tiles' chunks); at the end each wave's
-    // partial sums in its own ring area] [activation scales of 64 rows] [the
-    // two tiles' weight scales]
-    uint8_t* ring = smem + wave * S * 4096;
-    float* srl = reinterpret_cast<float*>(smem + W * S * 4096);
+    // LDS: [W rings of S slots of SB bytes (two tiles' chunks); at the end each
+    // wave's partial sums in its own ring area] [SHORT: 1 KB of padding]
+    // [activation scales of 64 rows] [the two tiles' weight scales]
+    uint8_t* ring = smem + wave * S * SB;
+    float* srl = reinterpret_cast<float*>(smem + W * S * SB + (SHORT ? 1024 : 0));
     float* swl = srl + 64;
     const __amdgpu_buffer_rsrc_t rw = weight_rsrc(wq, N * K);
     const __amdgpu_buffer_rsrc_t rx = weight_rsrc(xq, (int64_t)M * K);
@@ -1169,15 +1177,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_pair(
     auto fire = [&](int i, int slot) {
         const int chunk = wave + i * W;
         const bool ok = i < cpw && chunk < nchunks;
-        uint8_t* sl = ring + slot * 4096;
+        uint8_t* sl = ring + slot * SB;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint32_t t0 = (uint32_t)((int64_t)rt[t] * K) + (uint32_t)chunk * kChunk;
             const uint32_t w0 = ok && rt[t] + lrow < re[t] ? t0 + pieceoff0 : kOob;
             const uint32_t w1 = ok && rt[t] + lrow + 8 < re[t] ? t0 + pieceoff1 : kOob;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sl + t * 2048), 16, (int)w0, 0, 0, kWeightCpol);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sl + t * 2048 + 1024), 16, (int)w1, 0, 0,
-                                                     kWeightCpol);
+            if (!SHORT || t == 0)                        // SHORT: rows 8..15 of the second tile are never loaded
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sl + t * 2048 + 1024), 16, (int)w1, 0, 0,
+                                                         kWeightCpol);
         }
     };
     v8i bx[S][MT];
@@ -1198,10 +1207,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_pair(
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const int nx = j0 + s + S;
-            // position j0 + s landed (4 weight + 2 MT fragment loads per position): the S - 1 after it may be in flight
-            __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT((4 + 2 * MT) * (S - 1)));
-            const v8i A0 = slot_afrag(ring + s * 4096, r, g);
-            const v8i A1 = slot_afrag(ring + s * 4096 + 2048, r, g);
+            // position j0 + s landed (NW weight + 2 MT fragment loads per position): the S - 1 after it may be in flight
+            __builtin_amdgcn_s_waitcnt(FP8MM_SM_VMCNT((NW + 2 * MT) * (S - 1)));
+            const v8i A0 = slot_afrag(ring + s * SB, r, g);
+            const v8i A1 = slot_afrag(ring + s * SB + 2048, r, g);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 acc[0][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, bx[s][mt], acc[0][mt], 0, 0, 0, 0,
@@ -1221,7 +1230,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_gemm_small_m_pair(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) put_partial(mine + (t * MT + mt) * 64 + lane, acc[t][mt]);
     __syncthreads();
-    const int stride = S * 4096 / (int)sizeof(v4f);     // v4f per wave's ring area
+    const int stride = S * SB / (int)sizeof(v4f);       // v4f per wave's ring area
     for (int idx = threadIdx.x; idx < my_tiles * MT * 64; idx += blockDim.x) {
         const int t = idx / (MT * 64), rem = idx - t * MT * 64;
         const int mt = rem / 64, l = rem - mt * 64;
@@ -1463,19 +1472,19 @@ bool try_rx(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_w,
 }
 #undef FP8MM_RX_ARGS
 
-template <int S, int MT, bool BAL>
+template <int S, int MT, bool BAL, bool SHORT = false>
 void launch_pair(unsigned G, unsigned W, size_t lds, const uint8_t* xq, const uint8_t* wq, float s_act,
                  const float* s_w, const ShardTable& sh, int M, int64_t N, int64_t K, int nchunks, int cpw,
                  hipStream_t stream)
 {
     static const bool attr = [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_pair<S, MT, BAL>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_small_m_pair<S, MT, BAL, SHORT>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         return true;
     }();
     (void)attr;
-    hipLaunchKernelGGL((k_gemm_small_m_pair<S, MT, BAL>), dim3(G), dim3(64 * W), lds, stream, xq, wq, s_act, s_w, sh,
-                       M, N, K, nchunks, cpw);
+    hipLaunchKernelGGL((k_gemm_small_m_pair<S, MT, BAL, SHORT>), dim3(G), dim3(64 * W), lds, stream, xq, wq, s_act,
+                       s_w, sh, M, N, K, nchunks, cpw);
 }
 
 // The two-tile kernel, if it takes the shape: M <= 32, more chunks per wave
@@ -1501,6 +1510,18 @@ bool try_pair(const uint8_t* xq, const uint8_t* wq, float s_act, const float* s_
 #define FP8MM_PAIR_LAUNCH(S, MT) \
     (bal ? launch_pair<S, MT, true>((unsigned)G, (unsigned)W, lds, xq, wq, s_act, s_w, sh, (int)M, N, K, nchunks, cpw, stream) \
          : launch_pair<S, MT, false>((unsigned)G, (unsigned)W, lds, xq, wq, s_act, s_w, sh, (int)M, N, K, nchunks, cpw, stream))
+    // a short second tile (every balanced share <= 8 rows: ceil(share groups / G) <= 2): 3 KB slots, 3 of them
+    const int64_t ngr = (N - G * 16) / 4;
+    if (bal && (ngr + G - 1) / G <= 2 && (size_t)W * 3 * 3072 + 1024 + 512 <= 160 * 1024) {
+        const size_t lds = (size_t)W * 3 * 3072 + 1024 + 512;
+        if (M <= 16)
+            launch_pair<3, 1, true, true>((unsigned)G, (unsigned)W, lds, xq, wq, s_act, s_w, sh, (int)M, N, K, nchunks,
+                                          cpw, stream);
+        else
+            launch_pair<3, 2, true, true>((unsigned)G, (unsigned)W, lds, xq, wq, s_act, s_w, sh, (int)M, N, K, nchunks,
+                                          cpw, stream);
+        return true;
+    }
     for (const int S : {3, 2}) {
         const size_t lds = (size_t)W * S * 4096 + 512;
         if (lds > 160 * 1024) continue;

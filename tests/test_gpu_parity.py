@@ -447,13 +447,17 @@ def test_ragged_shapes_both_arms(fp8, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,shards", [(32, 5120, 17408, [5120]), (17, 5120, 17408, [4112, 1008]),
-                                          (29, 6400, 17408, [6400]), (24, 4112, 12288, [2048, 16, 2048])])
+                                          (29, 6400, 17408, [6400]), (24, 4112, 12288, [2048, 16, 2048]),
+                                          (8, 5120, 17408, [5120]), (1, 5120, 17408, [2560, 2560]),
+                                          (8, 6240, 17408, [6240]), (32, 6240, 17408, [3120, 3120])])
 def test_two_tile_streamed_fragment_kernel(fp8, M, N, K, shards):
-    """M 17..32 with long rows and at most two tiles per workgroup (a whole
-    tile and a balanced share of the rest, or two whole tiles: 6400 rows): both
-    tiles' chunks multiply the same streamed fragments.  Within the oracle's
-    tolerance on every element, and merged == one call per shard bit for bit
-    (the single shards run other kernels: the same bits by construction)."""
+    """Long rows and at most two tiles per workgroup (a whole tile and a
+    balanced share of the rest, or two whole tiles: 6400 rows): both tiles'
+    chunks multiply the same streamed fragments.  Shares of at most 8 rows
+    (5120, 4112 rows on 256 CUs) take 3 KB ring slots, larger ones (6240: up
+    to 12 rows) 4 KB slots.  Within the oracle's tolerance on every element,
+    and merged == one call per shard bit for bit (the single shards run other
+    kernels: the same bits by construction)."""
     xq = wl.random_codes(8, M, K, m=M)
     wq = wl.random_codes(8, N, K, tensor=wl.T_W, m=N)
     sw = (np.random.Generator(np.random.PCG64(N + K)).random(N) * 1e-3 + 1e-5).astype(np.float32)
