@@ -379,6 +379,196 @@ def bench_mlp(fp8, Ms, steps, warmup):
                     "down, graph-replayed; the separate calls beside it", **res}
 
 
+def bench_prefill(fp8, steps, warmup):
+    import torch
+    import workloads as wl
+
+    M, K1, N1, K2, N2 = 6576, 5120, 34816, 17408, 5120
+    wid = wl.PREFILL.wid
+    x = wl.activation_bf16(wid, M, K1, outliers=False)
+    g = wl.gamma_bf16(wid, K1)
+    xd, gd = bf16_dev(x), bf16_dev(g)
+    s1 = float(fp8.act_scale(xd, gd, wl.EPS).item())
+    wq1, sw1 = fp8.quant_weight(f32_dev(wl.weight_f32(wid, N1, K1)))
+    wq2, sw2 = fp8.quant_weight(f32_dev(wl.weight_f32(wid, N2, K2, tensor=wl.T_DOWN_W)))
+    xq1 = torch.empty((M, K1), dtype=torch.uint8, device="cuda")
+    xq2 = torch.empty((M, K2), dtype=torch.uint8, device="cuda")
+    gate = torch.empty((M, N1 // 2), dtype=torch.bfloat16, device="cuda")
+    up = torch.empty((M, N1 // 2), dtype=torch.bfloat16, device="cuda")
+    down = torch.empty((M, N2), dtype=torch.bfloat16, device="cuda")
+    assert fp8.select(M, N1, K1) == 1
+    flops1, flops2 = 2 * M * N1 * K1, 2 * M * N2 * K2
+    # the down projection's static scale, calibrated on this input's activation
+    fp8.quant_rmsnorm(xd, gd, s1, wl.EPS, out=xq1)
+    fp8.scaled_mm_merged(xq1, wq1, s1, sw1, [N1 // 2, N1 // 2], outs=[gate, up])
+    s2 = float(fp8.act_scale_silu_mul(gate, up).item())
+
+    def step(i):
+        fp8.quant_rmsnorm(xd, gd, s1, wl.EPS, out=xq1)
+        fp8.scaled_mm_merged(xq1, wq1, s1, sw1, [N1 // 2, N1 // 2], outs=[gate, up])
+        fp8.silu_mul_quant(gate, up, s2, out=xq2)
+        fp8.scaled_mm(xq2, wq2, s2, sw2, out=down)
+
+    ms = timed(step, steps, warmup)["median_ms"]
+    # The GEMMs alone: weight copies rotated past the Infinity Cache (2 x 178 MB
+    # for gate_up, 3 x 89 MB for down), as inside the step, where the other
+    # kernels' traffic evicts them; back-to-back launches of one weight would
+    # find part of it cached.
+    ws1 = [wq1, wq1.clone()]
+    ws2 = [wq2, wq2.clone(), wq2.clone()]
+    gu_ms, gu_each = graph_time_ms(lambda i: fp8.scaled_mm_merged(xq1, ws1[i % 2], s1, sw1, [N1 // 2, N1 // 2],
+                                                                  outs=[gate, up]), steps, warmup, replays=REPLAYS)
+    gu_ms = replay_stats(gu_each)["median_us"] * 1e-3
+    dn_ms, dn_each = graph_time_ms(lambda i: fp8.scaled_mm(xq2, ws2[i % 3], s2, sw2, out=down), steps, warmup,
+                                   replays=REPLAYS)
+    dn_ms = replay_stats(dn_each)["median_us"] * 1e-3
+    # A/B: the same merged gate_up launch with F32 outputs (twice the output bytes)
+    gate32 = torch.empty((M, N1 // 2), dtype=torch.float32, device="cuda")
+    up32 = torch.empty((M, N1 // 2), dtype=torch.float32, device="cuda")
+    gu32_ms = timed(lambda i: fp8.scaled_mm_merged(xq1, ws1[i % 2], s1, sw1, [N1 // 2, N1 // 2],
+                                                   outs=[gate32, up32]), steps, warmup)["median_ms"]
+    del gate32, up32
+    del ws1, ws2
+    torch.cuda.empty_cache()
+    sq_ms = timed(lambda i: fp8.silu_mul_quant(gate, up, s2, out=xq2), steps, warmup)["median_ms"]
+    sq_bytes = 5 * M * K2
+    # the step's fused RMSNorm quant alone, and the plain static quant of a bf16
+    # [M, 17408] down-projection input (the gate half stands in for it)
+    rq_ms = timed(lambda i: fp8.quant_rmsnorm(xd, gd, s1, wl.EPS, out=xq1), steps, warmup)["median_ms"]
+    pq_ms = timed(lambda i: fp8.quant(gate, s2, out=xq2), steps, warmup)["median_ms"]
+    ach = flops1 / (gu_ms * 1e-3) / 1e12
+    return {
+        "workload": f"prefill_M{M}_gateup_K{K1}_N{N1}_down_K{K2}_N{N2}",
+        "value": (flops1 + flops2) / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_step": ms,
+        "step": "fused RMSNorm quant + merged gate_up GEMM + fused SiLU*mul quant + down GEMM (large-M arm), "
+                "graph-replayed",
+        "gemm_tflops": {"gate_up": ach, "down": flops2 / (dn_ms * 1e-3) / 1e12},
+        "gemm_frac": {"gate_up": ach / FP8_PEAK_TFLOPS, "down": flops2 / (dn_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS},
+        "gemm_us": {"gate_up": gu_ms * 1e3, "down": dn_ms * 1e3},
+        "down_further_replays": replay_stats(dn_each),
+        "silu_mul_quant": {"us": sq_ms * 1e3, "GBs": sq_bytes / (sq_ms * 1e-3) / 1e9},
+        "quant_rmsnorm": {"us": rq_ms * 1e3, "GBs": (3 * M * K1 + 2 * K1) / (rq_ms * 1e-3) / 1e9},
+        "plain_quant_M6576_K17408": {"us": pq_ms * 1e3, "GBs": 3 * M * K2 / (pq_ms * 1e-3) / 1e9},
+        "f32_out_ab": {"gate_up_bf16_us": gu_ms * 1e3, "gate_up_f32_us": gu32_ms * 1e3,
+                       "out_bytes_bf16": 2 * M * N1, "out_bytes_f32": 4 * M * N1,
+                       "f32_over_bf16_time": gu32_ms / gu_ms,
+                       "traffic_bf16": load_traffic("prefill_gateup_M6576_K5120_N34816_pmc", "k_gemm_large_m_tiled"),
+                       "traffic_f32": load_traffic("prefill_gateup_f32out_M6576_K5120_N34816_pmc",
+                                                   "k_gemm_large_m_tiled")},
+        "roofline": {"bound": "mfma", "kernel": "k_gemm_large_m_tiled (gate_up)", "achieved": ach,
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / FP8_PEAK_TFLOPS,
+                     "traffic": load_traffic("prefill_gateup_M6576_K5120_N34816_pmc", "k_gemm_large_m_tiled"),
+                     "mfma_counters": load_mfma("prefill_mfma_M6576", "k_gemm_large_m_tiled"),
+                     "algorithmic_flops_per_launch": flops1, "avg_launch_us": gu_ms * 1e3,
+                     "further_replays": replay_stats(gu_each)},
+    }
+
+
+def bench_per_token(fp8, M, steps, warmup):
+    """Per-token dynamic scales beside the per-tensor numbers: the decode step
+    (per-token quant [M,5120] + GEMM 10240x5120 with per-row scales, weights
+    rotated as in the main line) and the prefill gate_up (per-token fused
+    RMSNorm quant [6576,5120] + merged gate_up with per-row scales)."""
+    import torch
+    import workloads as wl
+    K, N = 5120, 10240
+    xd = bf16_dev(wl.activation_bf16(wl.DECODE_PROJ.wid, M, K, outliers=True))
+    wq, sw = fp8.quant_weight(f32_dev(wl.weight_f32(wl.DECODE_PROJ.wid, N, K)))
+    copies = max(2, -(-2 * LLC_BYTES // (N * K)) + 1)
+    ws = [wq] + [wq.clone() for _ in range(copies - 1)]
+    xq, sr = fp8.quant_per_token(xd)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        fp8.quant_per_token(xd, out=xq, scales=sr)
+        fp8.scaled_mm_per_token(xq, ws[i % copies], sr, sw, out=out)
+
+    ms = timed(step, steps, warmup)["median_ms"]
+    gms = timed(lambda i: fp8.scaled_mm_per_token(xq, ws[i % copies], sr, sw, out=out), steps, warmup)["median_ms"]
+    step_bytes = N * K + 4 * N + M * K + 2 * M * N + 3 * M * K + 4 * M
+    del ws
+    Mp, N1 = 6576, 34816
+    wid = wl.PREFILL.wid
+    xp = bf16_dev(wl.activation_bf16(wid, Mp, K, outliers=False))
+    gp = bf16_dev(wl.gamma_bf16(wid, K))
+    wq1, sw1 = fp8.quant_weight(f32_dev(wl.weight_f32(wid, N1, K)))
+    xq1, sr1 = fp8.quant_per_token(xp, gp, wl.EPS)
+    outs = [torch.empty((Mp, N1 // 2), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    pq_ms = graph_time_ms(lambda i: fp8.quant_per_token(xp, gp, wl.EPS, out=xq1, scales=sr1), 10, 2)
+    pg_ms = graph_time_ms(lambda i: fp8.scaled_mm_merged_per_token(xq1, wq1, sr1, sw1, [N1 // 2, N1 // 2],
+                                                                   outs=outs), 10, 2)
+    return {"decode_step": {"workload": f"decode_proj_M{M}_K{K}_N{N}", "us": ms * 1e3,
+                            "GBs": step_bytes / (ms * 1e-3) / 1e9, "gemm_us": gms * 1e3},
+            "prefill": {"quant_rmsnorm_per_token_us": pq_ms * 1e3,
+                        "gate_up_us": pg_ms * 1e3, "gate_up_TFLOPs": 2 * Mp * N1 * K / (pg_ms * 1e-3) / 1e12}}
+
+
+def bench_merge_policies(fp8, M, steps, warmup):
+    """Attention q/k/v (12288 | 1024 | 1024 rows, K=5120) whose shards carry
+    per-tensor weight scales and mismatched static input scales, at decode M:
+    the exact policy (merge declined: quant + GEMM per shard, 6 launches)
+    against the max-scale policy (one quant at the largest input scale, weights
+    requantized to the largest weight scale, one merged GEMM: 2 launches), with
+    the accuracy the max-scale merge gives up, measured against the exact split
+    outputs.  Weights rotate as in the main line."""
+    import numpy as np
+    import torch
+    import workloads as wl
+    shards, K = (12288, 1024, 1024), 5120
+    x = wl.activation_bf16(4, M, K, outliers=True)
+    xd = bf16_dev(x)
+    s_cal = float(fp8.act_scale(xd).item())
+    s_in = [float(np.float32(s_cal * f)) for f in (1.0, 1.5, 0.75)]
+    wqs, sws = [], []
+    for i, n in enumerate(shards):
+        w = wl.weight_f32(4, n, K, tensor=wl.T_SHARD0 + i) * np.float32((1.0, 0.5, 2.0)[i])
+        wq, s = fp8.quant_weight_per_tensor(f32_dev(w))
+        wqs.append(wq)
+        sws.append(float(s.item()))
+    merge, _ = fp8.merge_admit(s_in, fp8.MERGE_EXACT)
+    assert not merge
+    _, s_mx = fp8.merge_admit(s_in, fp8.MERGE_MAX_SCALE)
+    w_cat = torch.cat(wqs)
+    w_mx, sw_mx, _ = fp8.requant_max_scale(w_cat, shards, sws)
+    N = sum(shards)
+    copies = max(2, -(-2 * LLC_BYTES // (N * K)) + 1)
+    split_w = [[w] + [w.clone() for _ in range(copies - 1)] for w in wqs]
+    split_sw = [torch.full((n,), s, dtype=torch.float32, device="cuda") for n, s in zip(shards, sws)]
+    merged_w = [w_mx] + [w_mx.clone() for _ in range(copies - 1)]
+    xq_s = [torch.empty((M, K), dtype=torch.uint8, device="cuda") for _ in shards]
+    xq_m = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    out_s = [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for n in shards]
+    out_m = [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for n in shards]
+
+    def split(i):
+        for j in range(len(shards)):
+            fp8.quant(xd, s_in[j], out=xq_s[j])
+            fp8.scaled_mm(xq_s[j], split_w[j][i % copies], s_in[j], split_sw[j], out=out_s[j])
+
+    def merged(i):
+        fp8.quant(xd, s_mx, out=xq_m)
+        fp8.scaled_mm_merged(xq_m, merged_w[i % copies], s_mx, sw_mx, list(shards), outs=out_m)
+
+    split_ms = timed(split, steps, warmup)["median_ms"]
+    merged_ms = timed(merged, steps, warmup)["median_ms"]
+    split(0)
+    merged(0)
+    torch.cuda.synchronize()
+    ex = torch.cat(out_s, dim=1).float().cpu().numpy().astype(np.float64)
+    mx = torch.cat(out_m, dim=1).float().cpu().numpy().astype(np.float64)
+    row = np.sqrt((ex * ex).sum(axis=1, keepdims=True))
+    rel = np.abs(mx - ex) / row
+    wbytes = N * K
+    return {"workload": f"attn_qkv_M{M}_K{K}_N{N}_shards_12288_1024_1024",
+            "split_exact_us": split_ms * 1e3, "split_launches": 6,
+            "merged_max_scale_us": merged_ms * 1e3, "merged_launches": 2,
+            "split_over_merged_time": split_ms / merged_ms,
+            "weight_GBs": {"split": wbytes / (split_ms * 1e-3) / 1e9, "merged": wbytes / (merged_ms * 1e-3) / 1e9},
+            "max_scale_error_vs_exact": {"max_abs_over_row_norm": float(rel.max()),
+                                         "mean_abs_over_row_norm": float(rel.mean())},
+            "input_scales": s_in, "weight_scales": sws}
+
+
 def bench_sweep(fp8, layers, M, steps, warmup, wid=4):
     """Decode-step weight sweep: `layers` = ((count, projections), ...).  The
     distinct projections of each layer group get their own seeded weights
