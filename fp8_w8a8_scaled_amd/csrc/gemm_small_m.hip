@@ -21,14 +21,17 @@
 //    registers.
 // Four kernels share that work split, so they give the same bits:
 //  * k_gemm_small_m_pair (M <= 32, rows longer than 5 chunks per wave, at
-//    most two tiles per workgroup): the two tiles' chunks in one slot, against
-//    fragments streamed with each chunk, so x_q is read once per workgroup;
+//    most two tiles per workgroup): the two tiles' chunks in one slot (3 KB
+//    when the second tile is a share of at most 8 rows), against fragments
+//    streamed with each chunk, so x_q is read once per workgroup;
 //  * k_gemm_small_m_rx (M <= 32, K % 128 == 0 with 4-5 chunks per wave, and
 //    M 17-32 beyond): persistent, one workgroup per CU walking its weight
 //    tiles; each wave streams its weight chunks with whole-line direct-to-LDS
 //    loads into a private ring of LDS slots and keeps its x_q B fragments in
 //    registers (loaded once, or with each chunk); for M <= 8 it can also
-//    quantize the bf16 activation itself (the static quant in its launch);
+//    quantize the bf16 activation itself (the static or the fused RMSNorm
+//    quant in its launch), and on an interleaved gate_up weight it can end
+//    with the SiLU*mul -> E4M3 quant instead of the bf16 store;
 //  * k_gemm_small_m_ring (M <= 16, K % 1024 == 0, the longer rows): the same
 //    stream, with x_q staged in LDS once (or streamed with each chunk when it
 //    does not fit);

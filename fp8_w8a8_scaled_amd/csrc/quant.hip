@@ -10,7 +10,10 @@
 //
 // All kernels are memory-bound streaming passes: 16-byte bf16 loads, 8-byte
 // E4M3 stores; LDS holds block reductions and the lookup tables that replace
-// the per-element division and encode.
+// the per-element division and encode (the fused RMSNorm quant instead takes
+// the exact quotient by multiply and fused multiply-add and the hardware E4M3
+// conversion).  Also here: the load-time interleave of a gate_up weight for
+// the SiLU*mul epilogue of the small-M GEMM.
 #include <mutex>
 
 #include "act_quant.h"
