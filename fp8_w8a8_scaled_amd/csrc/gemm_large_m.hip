@@ -154,7 +154,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_large_m(
 // with row-contiguous 16-byte stores.
 // Rows past M or N load a clamped (real) row and are never stored.
 // ---------------------------------------------------------------------------
-constexpr int kGroupM = 8;                   // x_q row-tiles per tile group (L2 sharing)
+// x_q row-tiles per tile group (L2 sharing).  A round of an XCD's 32
+// workgroups then spans GM x_q panels and 32 / GM weight panels, fewest near
+// GM = sqrt(32); measured at prefill M (same bits): GM = 8 924 / 467 us
+// (gate_up / down), 4-6 901-915 / 445-454 us, 12 972 / 474 us.
+constexpr int kGroupM = 6;
 
 // The C tile stores are non-temporal.  The workgroups finish their tiles at
 // about the same time, and the C tiles they write (4 MB per XCD per round)
