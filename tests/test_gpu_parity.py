@@ -108,7 +108,8 @@ def test_quant_strided_input_and_special_rows(fp8):
 def test_rmsnorm_quant_wide_gamma_and_special_rows(fp8, M, K, s_act):
     """gamma spans 2^-40 .. 2^41 with random signs, so y_b crosses both edges of
     the band of magnitudes whose code needs the division, under every scale.
-    2048 <= K <= 8192 with 2^-100 <= s_act <= 2^100 takes the code lookup, the
+    K <= 8192 with 2^-100 <= s_act <= 2^100 takes the row-group kernel (exact
+    quotient by multiply and fused multiply-add, hardware conversion), the
     rest the per-element path; all must give the oracle's bytes (130 rows: an
     odd row count for the row groups, rows strided).  Special rows: inf, NaN,
     all zeros with eps = 0 (r = inf), a lone subnormal; then an infinite
