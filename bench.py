@@ -915,8 +915,8 @@ def summarize_trace(d, name, cmd):
 
 def summarize_pmc(d, name, cmd):
     """FETCH_SIZE / WRITE_SIZE per dispatch of the target kernel, scaled by the
-    same counters on the plain copy the driver runs first (an elementwise
-    read-N-bytes / write-N-bytes kernel of known size)."""
+    same counters on the plain copy that `--pmc-driver` runs first (an
+    elementwise read-N-bytes / write-N-bytes kernel of known size)."""
     per = {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
