@@ -496,12 +496,13 @@ def _f32_bits_to_bf16_rne(a):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 10240, 5120), (8, 10240, 5120), (16, 384, 256), (17, 32, 272),
-                                   (65, 80, 144), (300, 1040, 5120), (600, 544, 1088)])
+                                   (65, 80, 144), (300, 1040, 5120), (600, 544, 1088), (8, 5120, 17408),
+                                   (32, 5120, 17408)])
 def test_f32_output_rounds_to_the_bf16_output(fp8, M, N, K):
     """The F32 variant stores the same scaled fp32 value the bf16 variant
     rounds: bf16_RNE(f32 out) equals the bf16 out bit for bit, on both arms
-    (M <= 64: small-M; larger M: large-M), and the f32 values meet the
-    oracle's tolerance."""
+    (M <= 64: small-M, the two-tile kernel at K = 17408; larger M: large-M),
+    and the f32 values meet the oracle's tolerance."""
     xq, wq, s_act, sw = _prepare(2, M, N, K, outliers=True)
     xd, wd, swd = u8_dev(xq), u8_dev(wq), f32_dev(sw)
     o16 = host_u16(fp8.scaled_mm(xd, wd, s_act, swd))
@@ -551,8 +552,8 @@ def test_per_token_quant_bit_exact(fp8, wid, M, K, rms):
     assert np.array_equal(host_u8(q), q_ref), f"{int((host_u8(q) != q_ref).sum())} codes differ"
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 10240, 5120), (8, 10240, 5120), (8, 5120, 17408), (33, 64, 400),
-                                   (300, 1040, 5120)])
+@pytest.mark.parametrize("M,N,K", [(1, 10240, 5120), (8, 10240, 5120), (8, 5120, 17408), (32, 5120, 17408),
+                                   (33, 64, 400), (300, 1040, 5120)])
 def test_per_token_gemm_against_oracle(fp8, M, N, K):
     """Per-row scales in the epilogue, on both arms; with every row scale equal
     the result is the per-tensor GEMM bit for bit."""
