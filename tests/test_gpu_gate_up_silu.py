@@ -126,3 +126,48 @@ def test_gate_up_silu_outside_the_fused_plans(fp8):
     assert int((out != 0xA5).sum().item()) == 0
     assert not fp8.gate_up_silu_quant_fused(40, 17408, 5120, s_act, 0.05, 0)
     assert not fp8.gate_up_silu_quant_fused(9, 17408, 5120, s_act, 0.05, 1)
+
+
+def test_decode_mlp_under_graph_capture(fp8):
+    """The decode MLP as two launches (gate_up with the RMSNorm quant inside and
+    the SiLU*mul quant as its epilogue, then down) captured in a HIP graph and
+    replayed several times, with eager work between replays: every replay
+    gives the eager bytes."""
+    import torch
+    M, I, K = 8, 17408, 5120
+    x = wl.activation_bf16(3, M, K, outliers=True)
+    g = wl.gamma_bf16(3, K)
+    xd, gd = bf16_dev(x), bf16_dev(g)
+    s_act = float(oracle.act_scale(x, g, wl.EPS))
+    wq, sw = oracle.quant_weight(wl.weight_f32(3, 2 * I, K))
+    wd, swd = u8_dev(wq), f32_dev(sw)
+    w2, sw2 = oracle.quant_weight(wl.weight_f32(3, 5120, I, tensor=wl.T_DOWN_W))
+    w2d, sw2d = u8_dev(w2), f32_dev(sw2)
+    w_il, s_il = fp8.interleave_gate_up(wd, swd)
+    xq = fp8.quant_rmsnorm(xd, gd, s_act, wl.EPS)
+    gate, up = fp8.scaled_mm_merged(xq, wd, s_act, swd, [I, I])
+    s_down = float(fp8.act_scale_silu_mul(gate, up).item())
+    assert fp8.gate_up_silu_quant_fused(M, I, K, s_act, s_down, 2)
+    hq_e = fp8.gate_up_silu_quant(w_il, s_il, s_act, s_down, x=xd, gamma=gd, eps=wl.EPS)
+    out_e = fp8.scaled_mm(hq_e, w2d, s_down, sw2d)
+    want_h, want_o = host_u8(hq_e), host_u16(out_e)
+    hq_g, out_g = torch.empty_like(hq_e), torch.empty_like(out_e)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        fp8.gate_up_silu_quant(w_il, s_il, s_act, s_down, x=xd, gamma=gd, eps=wl.EPS, out=hq_g)
+        fp8.scaled_mm(hq_g, w2d, s_down, sw2d, out=out_g)
+    torch.cuda.current_stream().wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fp8.gate_up_silu_quant(w_il, s_il, s_act, s_down, x=xd, gamma=gd, eps=wl.EPS, out=hq_g)
+        fp8.scaled_mm(hq_g, w2d, s_down, sw2d, out=out_g)
+    for i in range(4):
+        hq_g.fill_(0)
+        out_g.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u8(hq_g), want_h), f"replay {i}: h_q"
+        assert np.array_equal(host_u16(out_g), want_o), f"replay {i}: down output"
+        _ = fp8.gate_up_silu_quant(w_il, s_il, s_act, s_down, x_q=xq)   # eager work between replays
+        torch.cuda.synchronize()
