@@ -92,19 +92,40 @@ def _args():
 
 # The sources each profiled kernel is compiled from (its own file and the
 # shared device header); a traffic figure is valid only for these bytes.
-KERNEL_SOURCES = {"k_gemm_small_m": ("gemm_small_m.hip", "act_tables.h", "device_common.h", "out_store.h", "internal.h"),
-                  "k_gemm_large_m": ("gemm_large_m.hip", "device_common.h", "out_store.h", "internal.h"),
-                  "k_silu_mul_quant": ("quant.hip", "device_common.h", "act_tables.h", "internal.h")}
+# The source file each kernel (matched by name prefix) is compiled from; the
+# headers it includes are followed from there.
+KERNEL_SOURCES = {"k_gemm_small_m": "gemm_small_m.hip", "k_gemm_large_m": "gemm_large_m.hip",
+                  "k_silu_mul_quant": "quant.hip"}
+
+
+def kernel_files(kernel: str) -> list[str]:
+    """The source `kernel` is built from, then every header it includes through
+    quoted #include lines, transitively (paths relative to the kernel sources,
+    sorted)."""
+    key = next(k for k in KERNEL_SOURCES if kernel.startswith(k))
+    root = KERNEL_SOURCES[key]
+    seen, todo = set(), [root]
+    while todo:
+        rel = todo.pop()
+        if rel in seen:
+            continue
+        seen.add(rel)
+        base = os.path.dirname(rel)
+        with open(os.path.join(CSRC, rel)) as fh:
+            for line in fh:
+                m = re.match(r'\s*#\s*include\s+"([^"]+)"', line)
+                if m:
+                    todo.append(os.path.normpath(os.path.join(base, m.group(1))))
+    return [root] + sorted(seen - {root})
 
 
 def kernel_sources_hash(kernel: str | None = None) -> str:
-    """sha256 (16 hex digits) of every kernel source, or of those `kernel` is
-    built from (matched by name prefix)."""
+    """sha256 (16 hex digits) of every kernel source, or of the files `kernel`
+    is built from (kernel_files)."""
     if kernel is None:
         files = sorted(glob.glob(os.path.join(CSRC, "*")))
     else:
-        key = next(k for k in KERNEL_SOURCES if kernel.startswith(k))
-        files = [os.path.join(CSRC, f) for f in KERNEL_SOURCES[key]]
+        files = [os.path.join(CSRC, f) for f in kernel_files(kernel)]
     h = hashlib.sha256()
     for f in files:
         with open(f, "rb") as fh:
@@ -939,7 +960,7 @@ def summarize_pmc(d, name, cmd):
              f"`{target}`, calibrated on a plain copy of {meta['copy_bytes']} bytes "
              f"(`{copy_k}`, read {meta['copy_bytes']} and written {meta['copy_bytes']}).", "",
              f"Commands: `{cmd}`", "", f"kernel_source_sha256_16: {kernel_sources_hash(target)} "
-             f"({', '.join(KERNEL_SOURCES[next(k for k in KERNEL_SOURCES if target.startswith(k))])})", "",
+             f"({', '.join(kernel_files(target))})", "",
              "| counter | KiB per launch | copy KiB | scale = copy bytes / copy KiB·1024 | bytes per launch |",
              "|---|---|---|---|---|"]
     for cname, (kib, ck, fac, b, n) in res.items():
@@ -1002,7 +1023,7 @@ def summarize_mfma(d, name, cmd):
              "of gate_up (M=6576, N=34816, K=5120) and down (M=6576, N=5120, K=17408), means per launch.", "",
              f"Command: `{cmd}`", "",
              f"kernel_source_sha256_16: {kernel_sources_hash(target)} "
-             f"({', '.join(KERNEL_SOURCES[next(k for k in KERNEL_SOURCES if target.startswith(k))])})", "",
+             f"({', '.join(kernel_files(target))})", "",
              "Normalisation: executed FP8 flops = SQ_INSTS_VALU_MFMA_MOPS_F8 x 512 (the counter counts F8 add/mul ops "
              "/ 512), against 2 M N K; MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs) / "
              f"(GRBM_GUI_ACTIVE per XCD x {meta['simds']} SIMDs), rocprofv3's MfmaUtil; GRBM_GUI_ACTIVE is reported "
