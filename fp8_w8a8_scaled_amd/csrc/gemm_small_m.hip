@@ -963,10 +963,26 @@ __global__ __launch_bounds__(XM == XM_QRMS || SILU ? 64 * 8 : 64 * kMaxWaves) vo
         // chunk c is encoded there, two ring slots after its activation was
         // requested, instead of in the first tile (the weights have landed
         // by then, and the encoding would only add to the wait).
-        load_xv(0);
+        if (M > 4) {
+            // Past 4 rows the 32 workgroups of an XCD asking for the same
+            // activation lines at once cost more than the interleaving saves:
+            // every activation load goes first, the wave's chunks in an order
+            // rotated by the workgroup's place within its XCD (workgroups go
+            // round-robin over the 8 XCDs).  Each unrolled order keeps the
+            // register indices compile-time constants.
+            const int rot = (int)((blockIdx.x >> 3) % CPW);
+#pragma unroll
+            for (int rr = 0; rr < CPW; ++rr)
+                if (rr == rot) {
+#pragma unroll
+                    for (int c = 0; c < CPW; ++c) load_xv((c + rr) % CPW);
+                }
+        } else {
+            load_xv(0);
+        }
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            if (s + 1 < CPW) load_xv(s + 1);
+            if (M <= 4 && s + 1 < CPW) load_xv(s + 1);
             fire(prep(), s);
             if (s >= 2 && s - 2 < CPW) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -974,8 +990,9 @@ __global__ __launch_bounds__(XM == XM_QRMS || SILU ? 64 * 8 : 64 * kMaxWaves) vo
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        if (M <= 4)
 #pragma unroll
-        for (int c = S + 1; c < CPW; ++c) load_xv(c);
+            for (int c = S + 1; c < CPW; ++c) load_xv(c);
 #pragma unroll
         for (int c = S - 2 > 0 ? S - 2 : 0; c < CPW; ++c) quant_chunk(c);
     } else {
