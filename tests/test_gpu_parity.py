@@ -630,7 +630,9 @@ def _check_fused(fp8, x, xd, s_act, wq, sw, shards, fused, what):
     return want, want_q
 
 
-@pytest.mark.parametrize("M", [1, 3, 8])
+# M = 4 is the last row count with the activation loads interleaved with the
+# weight fill, 5 the first with every load first in a rotated chunk order
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 8])
 @pytest.mark.parametrize("K,shards", [(5120, [10240]), (5120, [17408, 17408]), (6144, [5120]),
                                       (5120, [4096, 1024, 9216]), (2048, [4112, 1008]), (3072, [2048])])
 def test_fused_quant_merged_equals_quant_then_merged(fp8, M, K, shards):
